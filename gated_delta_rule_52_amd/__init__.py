@@ -1,0 +1,14 @@
+"""Kimi Delta Attention (KDA) on MI355X (gfx950): chunkwise prefill and
+recurrent decode as hand-written HIP kernels behind a C ABI (include/kda.h).
+
+The Python layer only marshals arguments: torch tensors supply device memory
+and the current HIP stream; every step of the operator runs in libkda.so.
+"""
+__all__ = ["chunk_fwd", "recurrent_step", "KdaError", "chunk_fwd_workspace_bytes"]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import ops
+        return getattr(ops, name)
+    raise AttributeError(name)

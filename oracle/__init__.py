@@ -1,0 +1,115 @@
+"""fp64 CPU oracle for the Kimi Delta Attention (KDA) operator.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
+benchmark's CPU-baseline leg are the only callers.  Nothing here is used by,
+or uses, the HIP path.
+
+* ``forward``: the token-by-token fp64 recurrence (C, OpenMP), see
+  ``kda_oracle.c`` for the definition it follows.
+* ``reference``: independent numpy special cases and the fp64 chunked form.
+
+Parity status: every function here is pinned by ``tests/test_oracle.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc (fp64, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O3", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-fno-fast-math", "-ffp-contract=off", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        i64, dp, fp = ctypes.c_int64, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_float)
+        lib.kda_oracle_forward.restype = ctypes.c_int
+        lib.kda_oracle_forward.argtypes = [
+            i64, ctypes.POINTER(ctypes.c_int64), i64, i64, i64,
+            fp, fp, fp, fp, fp, dp, ctypes.c_double,
+            ctypes.POINTER(ctypes.c_int32), i64, dp, dp, ctypes.c_int]
+        lib.kda_oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().kda_oracle_max_threads())
+
+
+def _f32(x):
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _ptr(a, t):
+    return a.ctypes.data_as(ctypes.POINTER(t)) if a is not None else None
+
+
+def forward(q, k, v, g, beta, h0=None, cu_seqlens=None, scale: float = 1.0,
+            heads: Optional[Sequence[int]] = None, nthreads: int = 0,
+            want_state: bool = True):
+    """fp64 token recurrence.
+
+    q, k, g: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H] (any float
+    dtype, taken as float32 exact values); h0: [N, H, dk, dv] or None;
+    cu_seqlens: [N+1] offsets into the flattened B*T token axis, or None for
+    B fixed-length sequences.  Returns (o [B, T, nh, dv], hT [N, nh, dk, dv])
+    in float64 for the requested heads (all heads by default).  h0 is taken
+    in float64 so a state can be chained between calls without rounding.
+    """
+    lib = _load()
+    q, k, v, g, beta = map(_f32, (q, k, v, g, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens is None:
+        cu = np.arange(B + 1, dtype=np.int64) * T
+    else:
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    hs = np.arange(H, dtype=np.int32) if heads is None else np.ascontiguousarray(heads, dtype=np.int32)
+    nh = len(hs)
+    o = np.zeros((B, T, nh, dv), dtype=np.float64)
+    hT = np.zeros((N, nh, dk, dv), dtype=np.float64) if want_state else None
+    h0a = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
+    rc = lib.kda_oracle_forward(
+        N, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, dk, dv,
+        _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
+        _ptr(g, ctypes.c_float), _ptr(beta, ctypes.c_float), _ptr(h0a, ctypes.c_double),
+        float(scale), hs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), nh,
+        _ptr(o, ctypes.c_double), _ptr(hT, ctypes.c_double), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_forward failed with code {rc}")
+    return o, hT
+
+
+def decode_step(q, k, v, g, beta, state, scale: float = 1.0, nthreads: int = 0):
+    """One recurrent step for N independent sequences.
+
+    q, k, g: [N, H, dk]; v: [N, H, dv]; beta: [N, H]; state: [N, H, dk, dv].
+    A decode step is the recurrence over a sequence of length one, so this
+    runs ``forward`` with N one-token sequences.  Returns (o [N, H, dv],
+    new_state [N, H, dk, dv]) in float64.
+    """
+    N = q.shape[0]
+    cu = np.arange(N + 1, dtype=np.int64)
+    o, hT = forward(q[None], k[None], v[None], g[None], beta[None], h0=state,
+                    cu_seqlens=cu, scale=scale, nthreads=nthreads)
+    return o[0], hT

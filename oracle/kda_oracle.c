@@ -1,0 +1,136 @@
+/*
+ * kda_oracle.c - plain, slow, fp64 CPU oracle for the Kimi Delta Attention
+ * (KDA) operator.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP path.
+ *
+ * What it computes (Kimi Linear review notes, research-notes-dl6.pages.dev,
+ * section "Method / from Linear Attention to KDA", the KDA recurrence and
+ * its read-then-write reading): for every sequence n and head h,
+ * independently, starting from S_0 = h0[n,h] (zeros if absent),
+ *
+ *     alpha_t = exp(g_t)                      (per key channel)
+ *     S~      = Diag(alpha_t) S_{t-1}         (decay first ...)
+ *     S_t     = S~ + beta_t k_t (v_t - S~^T k_t)^T   (... then the delta write)
+ *     o_t     = scale * S_t^T q_t             (read after this token's write)
+ *
+ * and the final state S_T.  The same page's code-verification table states
+ * that the public naive recurrence multiplies by exp(g) first and then writes
+ * beta k (v - k^T S); this is that order.  `scale` is 1 in the pages' formula.
+ *
+ * Arithmetic is fp64 throughout; inputs arrive as float32 arrays holding the
+ * exact values the GPU receives (bf16 values are exactly representable in
+ * float32) and are widened to double before use.
+ *
+ * Layout: tokens are packed along one axis; q, k, g are [T_total, H, dk],
+ * v is [T_total, H, dv], beta is [T_total, H], sequence n owns tokens
+ * [cu[n], cu[n+1]).  Only the heads listed in `heads` (nh of them) are
+ * computed; outputs are [T_total, nh, dv] and [N, nh, dk, dv], in that order
+ * of heads.  h0, when given, is a double array [N, H, dk, dv] (all heads), so
+ * that a state can be chained from one call to the next without rounding.
+ *
+ * Parallelism: OpenMP over the independent (sequence, head) pairs.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int kda_oracle_forward(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk,
+                       int64_t dv, const float *q, const float *k, const float *v,
+                       const float *g, const float *beta, const double *h0,
+                       double scale, const int32_t *heads, int64_t nh, double *o,
+                       double *hT, int nthreads)
+{
+    if (n_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0 || nh <= 0)
+        return 1;
+    for (int64_t n = 0; n < n_seqs; ++n)
+        if (cu[n + 1] < cu[n])
+            return 2;
+    for (int64_t j = 0; j < nh; ++j)
+        if (heads[j] < 0 || heads[j] >= H)
+            return 3;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int64_t units = n_seqs * nh;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < units; ++u) {
+        int64_t n = u / nh, hj = u % nh, h = heads[hj];
+        double *S = (double *)malloc(sizeof(double) * (size_t)(dk * dv));
+        double *kv = (double *)malloc(sizeof(double) * (size_t)(dk + dk + dv + dv));
+        if (!S || !kv) {
+            free(S);
+            free(kv);
+#pragma omp atomic write
+            err = 4;
+            continue;
+        }
+        double *kt = kv, *qt = kv + dk, *vt = kv + 2 * dk, *p = kv + 2 * dk + dv;
+        /* S_0 */
+        for (int64_t i = 0; i < dk * dv; ++i)
+            S[i] = h0 ? h0[((n * H + h) * dk) * dv + i] : 0.0;
+        for (int64_t t = cu[n]; t < cu[n + 1]; ++t) {
+            const int64_t base_k = (t * H + h) * dk, base_v = (t * H + h) * dv;
+            for (int64_t i = 0; i < dk; ++i) {
+                kt[i] = (double)k[base_k + i];
+                qt[i] = (double)q[base_k + i];
+            }
+            for (int64_t j = 0; j < dv; ++j)
+                vt[j] = (double)v[base_v + j];
+            const double b = (double)beta[t * H + h];
+            /* S~ = Diag(exp(g_t)) S_{t-1} */
+            for (int64_t i = 0; i < dk; ++i) {
+                const double a = exp((double)g[base_k + i]);
+                for (int64_t j = 0; j < dv; ++j)
+                    S[i * dv + j] *= a;
+            }
+            /* p = S~^T k_t */
+            for (int64_t j = 0; j < dv; ++j)
+                p[j] = 0.0;
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j)
+                    p[j] += S[i * dv + j] * kt[i];
+            /* S_t = S~ + beta k (v - p)^T */
+            for (int64_t i = 0; i < dk; ++i) {
+                const double bk = b * kt[i];
+                for (int64_t j = 0; j < dv; ++j)
+                    S[i * dv + j] += bk * (vt[j] - p[j]);
+            }
+            /* o_t = scale * S_t^T q_t */
+            double *ot = o + (t * nh + hj) * dv;
+            for (int64_t j = 0; j < dv; ++j)
+                ot[j] = 0.0;
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j)
+                    ot[j] += S[i * dv + j] * qt[i];
+            for (int64_t j = 0; j < dv; ++j)
+                ot[j] *= scale;
+        }
+        if (hT)
+            memcpy(hT + ((n * nh + hj) * dk) * dv, S, sizeof(double) * (size_t)(dk * dv));
+        free(S);
+        free(kv);
+    }
+    return err;
+}
+
+int kda_oracle_version(void) { return 1; }
+
+int kda_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
