@@ -1,0 +1,190 @@
+// kda_api.cpp - host entry points of the C ABI declared in include/kda.h.
+//
+// Every argument is validated here, before anything is enqueued, so that a
+// bad call returns a status code and launches nothing.  The kernels never
+// allocate; the caller's stream carries all work.
+#include "kda.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kda_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kda_status fail(kda_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+kda_status fail(kda_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+bool valid_dtype(kda_dtype d) { return d == KDA_DTYPE_BF16 || d == KDA_DTYPE_FP32; }
+size_t dsize(kda_dtype d) { return d == KDA_DTYPE_BF16 ? 2 : 4; }
+bool valid_dim(int32_t d) { return d == 64 || d == 128; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void *p, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return {a, a + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+kda_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return KDA_OK;
+    return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Checks shared by kda_chunk_fwd and kda_chunk_fwd_workspace_bytes.
+kda_status check_chunk_sizes(const kda_chunk_fwd_args *a) {
+    if (!a) return fail(KDA_ERR_NULL_POINTER, "args is NULL");
+    if (a->struct_size != sizeof(kda_chunk_fwd_args))
+        return fail(KDA_ERR_BAD_STRUCT, "struct_size %u != %zu", a->struct_size, sizeof(kda_chunk_fwd_args));
+    if (a->B < 0 || a->T < 0 || a->H <= 0 || a->num_seqs < 0)
+        return fail(KDA_ERR_BAD_SHAPE, "B=%d T=%d H=%d num_seqs=%d", a->B, a->T, a->H, a->num_seqs);
+    if (!valid_dim(a->dk) || !valid_dim(a->dv))
+        return fail(KDA_ERR_UNSUPPORTED, "dk=%d dv=%d (supported: 64, 128)", a->dk, a->dv);
+    if (!valid_dtype(a->in_dtype) || !valid_dtype(a->out_dtype))
+        return fail(KDA_ERR_UNSUPPORTED, "in_dtype=%d out_dtype=%d", a->in_dtype, a->out_dtype);
+    if (a->chunk_size != 64 && a->chunk_size != 32 && a->chunk_size != 16)
+        return fail(KDA_ERR_UNSUPPORTED, "chunk_size=%d (supported: 16, 32, 64)", a->chunk_size);
+    if (!std::isfinite(a->scale)) return fail(KDA_ERR_BAD_SHAPE, "scale is not finite");
+    if (a->cu_seqlens) {
+        if (a->B != 1) return fail(KDA_ERR_BAD_SHAPE, "packed variable-length input needs B == 1 (B=%d)", a->B);
+    } else if (a->num_seqs != a->B) {
+        return fail(KDA_ERR_BAD_SHAPE, "num_seqs=%d must equal B=%d without cu_seqlens", a->num_seqs, a->B);
+    }
+    const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
+    if (tokens * a->H * (a->dk > a->dv ? a->dk : a->dv) > (int64_t{1} << 40))
+        return fail(KDA_ERR_BAD_SHAPE, "problem too large");
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL_POINTER: return "null pointer";
+        case KDA_ERR_BAD_SHAPE: return "bad shape";
+        case KDA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case KDA_ERR_BAD_STRUCT: return "argument struct size mismatch";
+        case KDA_ERR_HIP: return "HIP error";
+        case KDA_ERR_ALIAS: return "output overlaps an input";
+    }
+    return "unknown status";
+}
+
+const char *kda_last_error(void) { return g_last_error.c_str(); }
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_fwd_args *a) {
+    if (check_chunk_sizes(a) != KDA_OK) return static_cast<size_t>(-1);
+    return kda::chunk_workspace_bytes(a->B, a->T, a->H, a->dk, a->dv, a->num_seqs, a->chunk_size,
+                                      a->cu_seqlens != nullptr);
+}
+
+kda_status kda_chunk_fwd(const kda_chunk_fwd_args *a) {
+    g_last_error.clear();
+    kda_status st = check_chunk_sizes(a);
+    if (st != KDA_OK) return st;
+    const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
+    const int N = a->num_seqs;
+    if (tokens > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o))
+        return fail(KDA_ERR_NULL_POINTER, "q, k, v, g, beta and o are required");
+    if (a->cu_seqlens == nullptr && a->B > 0 && N > 0 && tokens == 0 && !a->final_state)
+        return KDA_OK;
+    const size_t need = kda::chunk_workspace_bytes(a->B, a->T, a->H, a->dk, a->dv, N, a->chunk_size,
+                                                   a->cu_seqlens != nullptr);
+    if (a->workspace_bytes < need || (need > 0 && !a->workspace))
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", a->workspace_bytes, need);
+    // The output must not overlap any input.
+    const size_t th = static_cast<size_t>(tokens) * a->H;
+    const size_t in_sz = dsize(a->in_dtype);
+    const Range ro = range_of(a->o, th * a->dv * dsize(a->out_dtype));
+    const Range ins[] = {range_of(a->q, th * a->dk * in_sz), range_of(a->k, th * a->dk * in_sz),
+                         range_of(a->v, th * a->dv * in_sz), range_of(a->g, th * a->dk * 4),
+                         range_of(a->beta, th * in_sz)};
+    const size_t sbytes = static_cast<size_t>(N) * a->H * a->dk * a->dv * 4;
+    for (const Range &r : ins)
+        if (overlap(ro, r)) return fail(KDA_ERR_ALIAS, "o overlaps an input");
+    if (a->final_state) {
+        const Range rf = range_of(a->final_state, sbytes);
+        for (const Range &r : ins)
+            if (overlap(rf, r)) return fail(KDA_ERR_ALIAS, "final_state overlaps an input");
+        if (overlap(rf, ro)) return fail(KDA_ERR_ALIAS, "final_state overlaps o");
+        if (a->initial_state && a->initial_state != a->final_state &&
+            overlap(rf, range_of(a->initial_state, sbytes)))
+            return fail(KDA_ERR_ALIAS, "final_state partially overlaps initial_state");
+    }
+    if (N == 0 || (tokens == 0 && !a->final_state)) return KDA_OK;
+
+    kda::ChunkLaunch L{};
+    L.q = a->q; L.k = a->k; L.v = a->v; L.g = a->g; L.beta = a->beta;
+    L.h0 = a->initial_state; L.hT = a->final_state; L.o = a->o;
+    L.cu_seqlens = a->cu_seqlens;
+    L.B = a->B; L.T = a->T; L.H = a->H; L.dk = a->dk; L.dv = a->dv; L.N = N;
+    L.chunk = a->chunk_size; L.scale = a->scale;
+    L.in_bf16 = a->in_dtype == KDA_DTYPE_BF16;
+    L.out_bf16 = a->out_dtype == KDA_DTYPE_BF16;
+    L.workspace = a->workspace; L.workspace_bytes = a->workspace_bytes;
+    L.stream = static_cast<hipStream_t>(a->stream);
+    return hip_status(kda::launch_chunk(L), "kda_chunk_fwd launch");
+}
+
+kda_status kda_recurrent_step(const kda_recurrent_step_args *a) {
+    g_last_error.clear();
+    if (!a) return fail(KDA_ERR_NULL_POINTER, "args is NULL");
+    if (a->struct_size != sizeof(kda_recurrent_step_args))
+        return fail(KDA_ERR_BAD_STRUCT, "struct_size %u != %zu", a->struct_size, sizeof(kda_recurrent_step_args));
+    if (a->N < 0 || a->H <= 0) return fail(KDA_ERR_BAD_SHAPE, "N=%d H=%d", a->N, a->H);
+    if (!valid_dim(a->dk) || !valid_dim(a->dv))
+        return fail(KDA_ERR_UNSUPPORTED, "dk=%d dv=%d (supported: 64, 128)", a->dk, a->dv);
+    if (!valid_dtype(a->in_dtype) || !valid_dtype(a->out_dtype))
+        return fail(KDA_ERR_UNSUPPORTED, "in_dtype=%d out_dtype=%d", a->in_dtype, a->out_dtype);
+    if (!std::isfinite(a->scale)) return fail(KDA_ERR_BAD_SHAPE, "scale is not finite");
+    if (a->N == 0) return KDA_OK;
+    if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o || !a->final_state)
+        return fail(KDA_ERR_NULL_POINTER, "q, k, v, g, beta, o and final_state are required");
+    const size_t nh = static_cast<size_t>(a->N) * a->H, in_sz = dsize(a->in_dtype);
+    const size_t sbytes = nh * a->dk * a->dv * 4;
+    const Range ro = range_of(a->o, nh * a->dv * dsize(a->out_dtype));
+    const Range rf = range_of(a->final_state, sbytes);
+    const Range ins[] = {range_of(a->q, nh * a->dk * in_sz), range_of(a->k, nh * a->dk * in_sz),
+                         range_of(a->v, nh * a->dv * in_sz), range_of(a->g, nh * a->dk * 4),
+                         range_of(a->beta, nh * in_sz)};
+    for (const Range &r : ins)
+        if (overlap(ro, r) || overlap(rf, r)) return fail(KDA_ERR_ALIAS, "an output overlaps an input");
+    if (overlap(ro, rf)) return fail(KDA_ERR_ALIAS, "o overlaps final_state");
+    if (a->initial_state && a->initial_state != a->final_state &&
+        overlap(rf, range_of(a->initial_state, sbytes)))
+        return fail(KDA_ERR_ALIAS, "final_state partially overlaps initial_state");
+
+    kda::RecurrentLaunch L{};
+    L.q = a->q; L.k = a->k; L.v = a->v; L.g = a->g; L.beta = a->beta;
+    L.h0 = a->initial_state; L.hT = a->final_state; L.o = a->o;
+    L.cu_seqlens = nullptr;
+    L.N = a->N; L.T = 1; L.H = a->H; L.dk = a->dk; L.dv = a->dv; L.scale = a->scale;
+    L.in_bf16 = a->in_dtype == KDA_DTYPE_BF16;
+    L.out_bf16 = a->out_dtype == KDA_DTYPE_BF16;
+    L.multi_token = false;
+    L.stream = static_cast<hipStream_t>(a->stream);
+    return hip_status(kda::launch_recurrent(L), "kda_recurrent_step launch");
+}
+
+}  // extern "C"

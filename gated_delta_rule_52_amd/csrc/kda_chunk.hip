@@ -1,0 +1,321 @@
+// kda_chunk.hip - chunkwise-parallel KDA prefill for gfx950, fp32 matrix cores.
+//
+// The sequence is cut into chunks of C tokens (Kimi Linear review notes,
+// section "Chunkwise Algorithm", C = 64); only the fp32 state S crosses chunk
+// boundaries.  Inside a chunk with rows r = 0..L-1 and entering state S
+// (jxzklqfsx.com article, hardware-efficient chunkwise algorithm: WY
+// representation, UT transform by row-wise forward substitution, inter-chunk
+// recurrence with intra-chunk parallel output; the chunk equations below are
+// derived from the recurrence and pinned against it by chunk-size invariance):
+//
+//   G_r      = g_0 + ... + g_r                  chunk-local log decay (a1);
+//                                               gamma^{i->r} = exp(G_r - G_i)
+//   A_kk[r,i]= beta_r sum_c k_r k_i exp(G_r-G_i), i <  r   (a2, decayed K K^T)
+//   A_qk[r,i]= scale  sum_c q_r k_i exp(G_r-G_i), i <= r   (a2, decayed Q K^T)
+//   T        = (I + A_kk)^{-1}                   UT transform (a3)
+//   V_new    = T (beta * (V - (e^G * K) S))      = U - W S with the WY factors
+//                                               U = T beta V, W = T beta e^G K (a4, a5)
+//   O        = scale (e^G * Q) S + A_qk V_new    inter + intra output (a6)
+//   S       <- e^{G_L} * S + (e^{G_L - G} * K)^T V_new       (a5)
+//
+// The two decayed Gram blocks are formed per 16-row block a with reference
+// row ref = 16a - 1 (G_{-1} = 0): row factors exp(G_r - G_ref) <= 1 and
+// column factors exp(G_ref - G_i), which are <= 1 left of the block and at
+// most exp(range of 16 rows) inside it.  If some 16-row block decays by more
+// than exp(-80) in a channel, its diagonal block is recomputed pair by pair
+// (exp(G_r - G_i) directly), so no factor ever overflows fp32.
+//
+// Work split: one workgroup (4 waves) per (sequence, head, 32-column dv
+// slice), walking the sequence's chunks in order.  All products run on
+// v_mfma_f32_16x16x4f32 with fp32 operands staged in LDS.  This kernel is
+// the exact-fp32 path (fp32 inputs) and the reference for the bf16 path.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+constexpr float kMaxBlockDecay = 80.0f;  // exp(80) is far below FLT_MAX
+
+template <int DK, int C, int BV, bool InBf16, bool OutBf16>
+__global__ void __launch_bounds__(256, 1)
+chunk_fp32_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
+                  const void *__restrict__ v_, const float *__restrict__ g,
+                  const void *__restrict__ beta_, const float *h0, float *hT,
+                  void *__restrict__ o_, const int32_t *__restrict__ cu_seqlens,
+                  int T, int H, int DV, float scale) {
+    using In = Elem<InBf16>;
+    using Out = Elem<OutBf16>;
+    const typename In::T *q = static_cast<const typename In::T *>(q_);
+    const typename In::T *k = static_cast<const typename In::T *>(k_);
+    const typename In::T *v = static_cast<const typename In::T *>(v_);
+    const typename In::T *beta = static_cast<const typename In::T *>(beta_);
+    typename Out::T *o = static_cast<typename Out::T *>(o_);
+
+    constexpr int NB = C / 16;        // 16-row blocks per chunk
+    constexpr int DKP = DK + 1;       // padded row strides (bank spread)
+    constexpr int CP = C + 1;
+    constexpr int BVP = BV + 1;
+    constexpr int NCT = BV / 16;      // 16-column tiles in the slice
+    static_assert(C % 16 == 0 && C <= 64 && BV % 16 == 0 && DK % 16 == 0, "tiling");
+
+    __shared__ float sG[C * DKP];     // G (cumulative log decay)
+    __shared__ float sK[C * DKP];     // k
+    __shared__ float sQ[C * DKP];     // q
+    __shared__ float sA[C * CP];      // beta-scaled A_kk (strictly lower), then T in place
+    __shared__ float sAq[C * CP];     // scale-scaled A_qk (lower incl. diagonal)
+    __shared__ float sS[DK * BVP];    // state slice, [dk][dv]
+    __shared__ float sX[C * BVP];     // beta (V - e^G K S), then V_new
+    __shared__ float sBeta[C];
+    __shared__ int sRange[NB];        // float bits of each block's largest decay
+
+    const int slice = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lk = lane >> 4;   // MFMA row/col lane, k lane
+    const int j0 = slice * BV;
+
+    int64_t t0, t1;
+    if (cu_seqlens) {
+        t0 = cu_seqlens[n];
+        t1 = cu_seqlens[n + 1];
+        if (t1 < t0) t1 = t0;
+    } else {
+        t0 = static_cast<int64_t>(n) * T;
+        t1 = t0 + T;
+    }
+    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * DV;
+
+    // ---- initial state slice -> LDS
+    for (int e = tid; e < DK * BV; e += 256) {
+        const int i = e / BV, j = e % BV;
+        sS[i * BVP + j] = h0 ? h0[sbase + static_cast<int64_t>(i) * DV + j0 + j] : 0.f;
+    }
+
+    for (int64_t c0 = t0; c0 < t1; c0 += C) {
+        const int L = static_cast<int>(t1 - c0 < C ? t1 - c0 : C);
+        // ---- a1: load the chunk, chunk-local cumulative log decay
+        if (tid < NB) sRange[tid] = 0;
+        for (int e = tid; e < C * DK; e += 256) {
+            const int r = e / DK, c = e % DK;
+            const int64_t gi = ((c0 + r) * H + h) * DK + c;
+            const bool ok = r < L;
+            sK[r * DKP + c] = ok ? In::load(k, gi) : 0.f;
+            sQ[r * DKP + c] = ok ? In::load(q, gi) : 0.f;
+        }
+        if (tid < C) sBeta[tid] = tid < L ? In::load(beta, (c0 + tid) * H + h) : 0.f;
+        for (int c = tid; c < DK; c += 256) {
+            float acc = 0.f;
+            for (int r = 0; r < C; ++r) {
+                if (r < L) acc += g[((c0 + r) * H + h) * DK + c];
+                sG[r * DKP + c] = acc;
+            }
+        }
+        __syncthreads();
+        for (int c = tid; c < DK; c += 256) {
+#pragma unroll
+            for (int a = 0; a < NB; ++a) {
+                const float gref = a ? sG[(16 * a - 1) * DKP + c] : 0.f;
+                const float rng = gref - sG[(16 * a + 15) * DKP + c];
+                atomicMax(&sRange[a], __float_as_int(fmaxf(rng, 0.f)));
+            }
+        }
+        __syncthreads();
+
+        // ---- a2: A_kk and A_qk, one (row block, column block) tile pair per step
+        for (int p = wave; p < NB * (NB + 1) / 2; p += 4) {
+            int a = 0, rem = p;
+            while (rem > a) { rem -= a + 1; ++a; }
+            const int b = rem;  // b <= a
+            const int r = 16 * a + lr, i = 16 * b + lr;
+            f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < DK / 4; ++s) {
+                const int c = 4 * s + lk;
+                const float gref = a ? sG[(16 * a - 1) * DKP + c] : 0.f;
+                const float xf = __expf(sG[r * DKP + c] - gref);
+                const float kc = sK[i * DKP + c] * __expf(fminf(gref - sG[i * DKP + c], kMaxBlockDecay));
+                akk = mfma4(sK[r * DKP + c] * xf, kc, akk);
+                aqk = mfma4(sQ[r * DKP + c] * xf, kc, aqk);
+            }
+            const bool exact = (a == b) && __int_as_float(sRange[a]) > kMaxBlockDecay;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int rr = 16 * a + 4 * lk + jj, ii = 16 * b + lr;
+                float vk = akk[jj], vq = aqk[jj];
+                if (exact) {  // pair-by-pair decay for a block that decays too fast
+                    vk = 0.f;
+                    vq = 0.f;
+                    for (int c = 0; c < DK; ++c) {
+                        const float d = __expf(sG[rr * DKP + c] - sG[ii * DKP + c]);
+                        vk += sK[rr * DKP + c] * sK[ii * DKP + c] * d;
+                        vq += sQ[rr * DKP + c] * sK[ii * DKP + c] * d;
+                    }
+                }
+                sA[rr * CP + ii] = ii < rr ? sBeta[rr] * vk : 0.f;
+                sAq[rr * CP + ii] = ii <= rr ? scale * vq : 0.f;
+            }
+        }
+        // upper tiles are zero
+        for (int e = tid; e < C * C; e += 256) {
+            const int r = e / C, i = e % C;
+            if ((i >> 4) > (r >> 4)) {
+                sA[r * CP + i] = 0.f;
+                sAq[r * CP + i] = 0.f;
+            }
+        }
+        __syncthreads();
+
+        // ---- a3: T = (I + A_kk)^{-1} by forward substitution, in place, one
+        // column per lane of wave 0: row r reads A[r][i] (i < r) and rows of T
+        // above it; the lanes reconverge before row r is overwritten, so every
+        // read of row r sees A and every read of an earlier row sees T.
+        if (tid < C) {
+            const int jcol = tid;
+            for (int r = 0; r < C; ++r) {
+                float acc = (r == jcol) ? 1.f : 0.f;
+                for (int i = jcol; i < r; ++i) acc -= sA[r * CP + i] * sA[i * CP + jcol];
+                sA[r * CP + jcol] = acc;
+            }
+        }
+        // ---- a5 (first half): X = beta (V - (e^G K) S), Y = (e^G Q) S; wave = row block
+        f32x4 accX[NCT], accY[NCT];
+#pragma unroll
+        for (int t = 0; t < NCT; ++t) {
+            accX[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accY[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        const bool rowblk = wave < NB;
+        if (rowblk) {
+            const int r = 16 * wave + lr;
+            for (int s = 0; s < DK / 4; ++s) {
+                const int c = 4 * s + lk;
+                const float e = __expf(sG[r * DKP + c]);
+                const float ak = sK[r * DKP + c] * e, aq = sQ[r * DKP + c] * e;
+#pragma unroll
+                for (int t = 0; t < NCT; ++t) {
+                    const float bs = sS[c * BVP + 16 * t + lr];
+                    accX[t] = mfma4(ak, bs, accX[t]);
+                    accY[t] = mfma4(aq, bs, accY[t]);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < NCT; ++t) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int rr = 16 * wave + 4 * lk + jj, j = 16 * t + lr;
+                    const float vv = rr < L ? In::load(v, ((c0 + rr) * H + h) * static_cast<int64_t>(DV) + j0 + j) : 0.f;
+                    sX[rr * BVP + j] = sBeta[rr] * (vv - accX[t][jj]);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- a4/a5: V_new = T X (T unit lower triangular)
+        f32x4 accV[NCT];
+#pragma unroll
+        for (int t = 0; t < NCT; ++t) accV[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (rowblk) {
+            const int r = 16 * wave + lr;
+            for (int s = 0; s < 4 * (wave + 1); ++s) {
+                const int i = 4 * s + lk;
+                const float at = sA[r * CP + i];
+#pragma unroll
+                for (int t = 0; t < NCT; ++t) accV[t] = mfma4(at, sX[i * BVP + 16 * t + lr], accV[t]);
+            }
+        }
+        __syncthreads();
+        if (rowblk) {
+#pragma unroll
+            for (int t = 0; t < NCT; ++t)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) sX[(16 * wave + 4 * lk + jj) * BVP + 16 * t + lr] = accV[t][jj];
+        }
+        __syncthreads();
+
+        // ---- a6: O = scale Y + A_qk V_new
+        if (rowblk) {
+            const int r = 16 * wave + lr;
+#pragma unroll
+            for (int t = 0; t < NCT; ++t) accY[t] *= scale;
+            for (int s = 0; s < 4 * (wave + 1); ++s) {
+                const int i = 4 * s + lk;
+                const float aq = sAq[r * CP + i];
+#pragma unroll
+                for (int t = 0; t < NCT; ++t) accY[t] = mfma4(aq, sX[i * BVP + 16 * t + lr], accY[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < NCT; ++t)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int rr = 16 * wave + 4 * lk + jj;
+                    if (rr < L) Out::store(o, ((c0 + rr) * H + h) * static_cast<int64_t>(DV) + j0 + 16 * t + lr, accY[t][jj]);
+                }
+        }
+
+        // ---- a5: S <- e^{G_L} S + (e^{G_L - G} K)^T V_new ; 16-row dk tiles over waves
+        for (int rt = wave; rt < DK / 16; rt += 4) {
+            const int ic = 16 * rt + lr;  // dk index of this lane's A row
+            const float gl = sG[(C - 1) * DKP + ic];
+            f32x4 acc[NCT];
+#pragma unroll
+            for (int t = 0; t < NCT; ++t)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int ir = 16 * rt + 4 * lk + jj;
+                    acc[t][jj] = __expf(sG[(C - 1) * DKP + ir]) * sS[ir * BVP + 16 * t + lr];
+                }
+            for (int s = 0; s < C / 4; ++s) {
+                const int rr = 4 * s + lk;
+                const float ak = sK[rr * DKP + ic] * __expf(gl - sG[rr * DKP + ic]);
+#pragma unroll
+                for (int t = 0; t < NCT; ++t) acc[t] = mfma4(ak, sX[rr * BVP + 16 * t + lr], acc[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < NCT; ++t)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) sS[(16 * rt + 4 * lk + jj) * BVP + 16 * t + lr] = acc[t][jj];
+        }
+        __syncthreads();
+    }
+
+    if (hT) {
+        for (int e = tid; e < DK * BV; e += 256) {
+            const int i = e / BV, j = e % BV;
+            hT[sbase + static_cast<int64_t>(i) * DV + j0 + j] = sS[i * BVP + j];
+        }
+    }
+}
+
+size_t chunk_workspace_bytes(int, int, int, int, int, int, int, bool) { return 0; }
+
+template <int DK, int C>
+static hipError_t launch_chunk_dk(const ChunkLaunch &L) {
+    constexpr int BV = 32;
+    dim3 grid(L.dv / BV, L.H, L.N), block(256);
+#define KDA_CHUNK(IB, OB)                                                                             \
+    hipLaunchKernelGGL((chunk_fp32_kernel<DK, C, BV, IB, OB>), grid, block, 0, L.stream, L.q, L.k, L.v, \
+                       L.g, L.beta, L.h0, L.hT, L.o, L.cu_seqlens, L.T, L.H, L.dv, L.scale)
+    if (L.in_bf16 && L.out_bf16) KDA_CHUNK(true, true);
+    else if (L.in_bf16) KDA_CHUNK(true, false);
+    else if (L.out_bf16) KDA_CHUNK(false, true);
+    else KDA_CHUNK(false, false);
+#undef KDA_CHUNK
+    return hipGetLastError();
+}
+
+template <int DK>
+static hipError_t launch_chunk_c(const ChunkLaunch &L) {
+    if (L.chunk == 64) return launch_chunk_dk<DK, 64>(L);
+    if (L.chunk == 32) return launch_chunk_dk<DK, 32>(L);
+    return launch_chunk_dk<DK, 16>(L);
+}
+
+hipError_t launch_chunk(const ChunkLaunch &L) {
+    return L.dk == 128 ? launch_chunk_c<128>(L) : launch_chunk_c<64>(L);
+}
+
+}  // namespace kda

@@ -1,0 +1,70 @@
+// kda_device.h - device helpers shared by the KDA kernels (gfx950 / CDNA4).
+//
+// bf16 <-> fp32 conversion (bf16 is the upper half of an IEEE binary32, so
+// widening is a shift and narrowing rounds to nearest, ties to even), typed
+// loads for the two input dtypes, and wave64 reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even narrowing; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Element loads/stores for a tensor whose dtype is a template parameter:
+// IsBf16 == true means uint16_t storage holding bf16, false means float.
+template <bool IsBf16>
+struct Elem;
+
+template <>
+struct Elem<true> {
+    using T = uint16_t;
+    __device__ __forceinline__ static float load(const T *p, int64_t i) { return bf16_to_f32(p[i]); }
+    __device__ __forceinline__ static void store(T *p, int64_t i, float x) { p[i] = f32_to_bf16(x); }
+    // four consecutive elements (8-byte aligned)
+    __device__ __forceinline__ static float4 load4(const T *p, int64_t i) {
+        const uint2 w = *reinterpret_cast<const uint2 *>(p + i);
+        return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                           __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+    }
+    __device__ __forceinline__ static void store4(T *p, int64_t i, float4 x) {
+        uint2 w;
+        w.x = static_cast<uint32_t>(f32_to_bf16(x.x)) | (static_cast<uint32_t>(f32_to_bf16(x.y)) << 16);
+        w.y = static_cast<uint32_t>(f32_to_bf16(x.z)) | (static_cast<uint32_t>(f32_to_bf16(x.w)) << 16);
+        *reinterpret_cast<uint2 *>(p + i) = w;
+    }
+};
+
+template <>
+struct Elem<false> {
+    using T = float;
+    __device__ __forceinline__ static float load(const T *p, int64_t i) { return p[i]; }
+    __device__ __forceinline__ static void store(T *p, int64_t i, float x) { p[i] = x; }
+    __device__ __forceinline__ static float4 load4(const T *p, int64_t i) {
+        return *reinterpret_cast<const float4 *>(p + i);
+    }
+    __device__ __forceinline__ static void store4(T *p, int64_t i, float4 x) {
+        *reinterpret_cast<float4 *>(p + i) = x;
+    }
+};
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+    return x;
+}
+
+}  // namespace kda

@@ -21,7 +21,8 @@ device is lossless and the oracle sees exactly what the GPU sees.
 
 Draw order for one generator: [sequence lengths], q, k, v, beta-logits,
 g-logits, h0.  For the decode workload the state is drawn first, then per
-step q, k, v, beta-logits, g-logits.
+step q, k, v, beta-logits, g-logits; a long decode run cycles through a pool
+of such per-step batches.
 """
 from __future__ import annotations
 
@@ -32,7 +33,7 @@ import numpy as np
 
 __all__ = [
     "KdaInputs", "bf16_round", "l2_normalise", "softplus", "sigmoid",
-    "make_prefill", "make_decode_state", "decode_steps", "WORKLOADS",
+    "make_prefill", "make_decode_state", "decode_steps", "decode_step_pool", "WORKLOADS",
     "make_workload",
 ]
 
@@ -40,16 +41,19 @@ __all__ = [
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); return float32."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    b = x.view(np.uint32).astype(np.uint64)
-    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
-    return (b.astype(np.uint32) << 16).view(np.float32)
+    b = x.view(np.uint32)
+    r = (b >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += b                       # wraps only for NaN payloads
+    r &= np.uint32(0xFFFF0000)
+    return r.view(np.float32)
 
 
 def l2_normalise(x: np.ndarray) -> np.ndarray:
     """Normalise the last axis to unit L2 norm in float32."""
     x = x.astype(np.float32, copy=False)
-    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True, dtype=np.float32))
-    return (x / n).astype(np.float32)
+    n = np.sqrt(np.einsum("...i,...i->...", x, x))[..., None]
+    return np.divide(x, n, dtype=np.float32)
 
 
 def softplus(x: np.ndarray) -> np.ndarray:
@@ -184,6 +188,16 @@ def decode_steps(rng, steps: int, N: int, H: int, dk: int, dv: int,
                    g=(-f32(gscale) * softplus(gl)).astype(f32))
 
 
+def decode_step_pool(rng, pool: int, N: int, H: int, dk: int, dv: int,
+                     in_dtype: str = "bf16", gscale: float = 1.0) -> dict:
+    """Draw ``pool`` token batches for the decode workload, stacked on a
+    leading axis: q, k, g [pool,N,H,dk]; v [pool,N,H,dv]; beta [pool,N,H].
+    Step s of a long decode run uses batch s % pool (each step still reads
+    its own copy at its own device offset)."""
+    steps = list(decode_steps(rng, pool, N, H, dk, dv, in_dtype, gscale))
+    return {k: np.stack([s[k] for s in steps]) for k in steps[0]}
+
+
 # The five workloads: shapes and recipes of the Kimi Linear operator sweep
 # (batch 1, 16 heads, head dim 128) plus a small fp32 case, a decode batch and
 # a packed variable-length batch.
@@ -195,7 +209,7 @@ WORKLOADS = {
     "prefill_64k": dict(kind="prefill", seed=2, B=1, T=65536, H=16, dk=128, dv=128,
                         in_dtype="bf16", gscale=1.0, h0_std=0.02),
     "decode_256x16": dict(kind="decode", seed=3, N=256, H=16, dk=128, dv=128,
-                          in_dtype="bf16", gscale=1.0, steps=1024, state_std=0.02),
+                          in_dtype="bf16", gscale=1.0, steps=1024, pool=32, state_std=0.02),
     "varlen_8seq": dict(kind="prefill", seed=4, B=1, T=None, H=32, dk=128, dv=128,
                         in_dtype="bf16", gscale=0.01, h0_std=0.02,
                         lengths_range=(1024, 32768), n_seqs=8),

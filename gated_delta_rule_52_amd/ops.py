@@ -1,0 +1,157 @@
+"""Torch-facing wrappers of the KDA C ABI.
+
+torch supplies device memory and the current HIP stream; every step of the
+operator runs in libkda.so.  Shapes and dtypes follow include/kda.h.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import KdaError  # noqa: F401  (re-exported)
+
+_DT = {torch.bfloat16: _lib.KDA_DTYPE_BF16, torch.float32: _lib.KDA_DTYPE_FP32}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _fill_chunk_args(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, scale,
+                     chunk_size, workspace=None, workspace_bytes=0):
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    a = _lib.ChunkFwdArgs()
+    a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+    a.initial_state, a.final_state, a.o = _ptr(initial_state), _ptr(final_state), _ptr(o)
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.B, a.T, a.H, a.dk, a.dv, a.num_seqs = B, T, H, dk, dv, N
+    a.scale = float(scale)
+    a.in_dtype = _DT[q.dtype]
+    a.out_dtype = _DT[o.dtype]
+    a.chunk_size = int(chunk_size)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = int(workspace_bytes)
+    a.stream = _stream(q.device)
+    return a
+
+
+def chunk_fwd_workspace_bytes(q, v, cu_seqlens=None, chunk_size: int = 64) -> int:
+    B, T, H, dk = q.shape
+    a = _lib.ChunkFwdArgs()
+    a.B, a.T, a.H, a.dk, a.dv = B, T, H, dk, v.shape[-1]
+    a.num_seqs = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.scale, a.in_dtype, a.out_dtype, a.chunk_size = 1.0, _DT[q.dtype], _DT[q.dtype], chunk_size
+    n = _lib.chunk_workspace_raw(a)
+    if n == 2 ** 64 - 1:
+        _lib.check(_lib.STATUS_CODE["KDA_ERR_BAD_SHAPE"])
+    return int(n)
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+              beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, scale: float = 1.0,
+              chunk_size: int = 64, out_dtype: Optional[torch.dtype] = None,
+              output_final_state: bool = True, final_state: Optional[torch.Tensor] = None,
+              o: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise KDA prefill.  Returns (o [B,T,H,dv], final_state [N,H,dk,dv] or None).
+
+    q, k: [B,T,H,dk] (bf16 or fp32); v: [B,T,H,dv]; g: [B,T,H,dk] fp32 (log
+    decay); beta: [B,T,H]; initial_state: [N,H,dk,dv] fp32 or None;
+    cu_seqlens: int32 [N+1] device tensor for packed variable-length input
+    (B == 1).  ``final_state`` may be given (it may be ``initial_state`` for an
+    in-place update); otherwise one is allocated when ``output_final_state``.
+    """
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported input dtype {dt}")
+    _need(q, "q", (B, T, H, dk), dt)
+    _need(k, "k", (B, T, H, dk), dt)
+    _need(v, "v", (B, T, H, dv), dt)
+    _need(g, "g", (B, T, H, dk), torch.float32)
+    _need(beta, "beta", (B, T, H), dt)
+    N = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32)
+        N = cu_seqlens.numel() - 1
+    if initial_state is not None:
+        _need(initial_state, "initial_state", (N, H, dk, dv), torch.float32)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif final_state is not None:
+        _need(final_state, "final_state", (N, H, dk, dv), torch.float32)
+    od = out_dtype or dt
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=od, device=q.device)
+    else:
+        _need(o, "o", (B, T, H, dv), od)
+    ws = chunk_fwd_workspace_bytes(q, v, cu_seqlens, chunk_size)
+    if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
+        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+    a = _fill_chunk_args(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, scale,
+                         chunk_size, workspace, ws if ws > 0 else 0)
+    _lib.check(_lib.chunk_fwd_raw(a))
+    return o, final_state
+
+
+def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                   beta: torch.Tensor, state: Optional[torch.Tensor],
+                   final_state: Optional[torch.Tensor] = None, scale: float = 1.0,
+                   out_dtype: Optional[torch.dtype] = None,
+                   o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step for N sequences.  q, k, g: [N,H,dk]; v: [N,H,dv];
+    beta: [N,H]; state: [N,H,dk,dv] fp32 (or None for zeros).  The new state
+    is written to ``final_state`` (default: ``state`` itself, in place).
+    Returns o [N,H,dv]."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported input dtype {dt}")
+    _need(q, "q", (N, H, dk), dt)
+    _need(k, "k", (N, H, dk), dt)
+    _need(v, "v", (N, H, dv), dt)
+    _need(g, "g", (N, H, dk), torch.float32)
+    _need(beta, "beta", (N, H), dt)
+    if state is not None:
+        _need(state, "state", (N, H, dk, dv), torch.float32)
+    if final_state is None:
+        if state is None:
+            raise ValueError("final_state is required when state is None")
+        final_state = state
+    _need(final_state, "final_state", (N, H, dk, dv), torch.float32)
+    od = out_dtype or dt
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=od, device=q.device)
+    a = _lib.RecurrentStepArgs()
+    a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+    a.initial_state, a.final_state, a.o = _ptr(state), _ptr(final_state), _ptr(o)
+    a.N, a.H, a.dk, a.dv = N, H, dk, dv
+    a.scale = float(scale)
+    a.in_dtype = _DT[dt]
+    a.out_dtype = _DT[od]
+    a.stream = _stream(q.device)
+    _lib.check(_lib.recurrent_step_raw(a))
+    return o

@@ -1,0 +1,167 @@
+/*
+ * kda.h - C ABI of the Kimi Delta Attention (KDA) operator for MI355X (gfx950).
+ *
+ * The operator (Kimi Linear review notes, research-notes-dl6.pages.dev,
+ * section "Method / from Linear Attention to KDA", the KDA recurrence):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = scale * S_t^T q_t,      alpha_t = exp(g_t) in [0,1]^dk,
+ *
+ * computed per sequence and head, with a dk x dv fp32 state S per (sequence,
+ * head).  The same page's "Training and Inference" section routes long
+ * prompts to the chunkwise kernel and single decode steps to the fused
+ * recurrent kernel, with the recurrent state cached between calls; both are
+ * exported here.  `scale` is 1 in the pages' formula.
+ *
+ * General conventions for every entry point:
+ *  - Every tensor pointer is a DEVICE pointer to contiguous row-major memory
+ *    with the layout given below, aligned to 16 bytes.  The caller owns all
+ *    memory, including the workspace; the library never allocates, frees,
+ *    synchronises or keeps a pointer after the call returns.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *    the default stream).  The call returns after enqueueing.
+ *  - Arguments are validated on the host before anything is enqueued; on
+ *    any error nothing is launched and a status other than KDA_OK is
+ *    returned (no exception crosses the ABI).  kda_last_error() then gives a
+ *    thread-local message.  Values inside tensors are not validated: g <= 0
+ *    (alpha <= 1), finite inputs and a non-decreasing cu_seqlens are
+ *    preconditions, and violating them gives unspecified numbers (never an
+ *    out-of-bounds access: every index the kernels form is clamped to the
+ *    sizes passed here).
+ *  - Results are deterministic (no atomics in any reduction): the same
+ *    inputs give the same bits on every run.
+ *  - Functions are thread-safe; concurrent calls on different streams are
+ *    independent.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+    KDA_DTYPE_BF16 = 0, /* bfloat16, round-to-nearest-even on output */
+    KDA_DTYPE_FP32 = 1
+} kda_dtype;
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
+    KDA_ERR_BAD_SHAPE = 2,           /* a size is negative or inconsistent */
+    KDA_ERR_UNSUPPORTED = 3,         /* dk/dv/dtype/chunk size not supported */
+    KDA_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes below what is required */
+    KDA_ERR_BAD_STRUCT = 5,          /* struct_size does not match this library */
+    KDA_ERR_HIP = 6,                 /* a HIP launch failed; see kda_last_error() */
+    KDA_ERR_ALIAS = 7                /* the output overlaps an input */
+} kda_status;
+
+/*
+ * Chunkwise-parallel prefill (Kimi Linear review notes, section "Chunkwise
+ * Algorithm"; jxzklqfsx.com article, section on the hardware-efficient
+ * chunkwise algorithm): the sequence is cut into chunks of `chunk_size`
+ * tokens that never straddle two sequences; inside a chunk the decayed
+ * K K^T and Q K^T blocks, the UT-transform inverse and the WY factors are
+ * formed in parallel, and only the fp32 state crosses chunk boundaries.
+ *
+ * Shapes (N = number of sequences):
+ *   q, k : [B, T, H, dk]  in_dtype
+ *   v    : [B, T, H, dv]  in_dtype
+ *   g    : [B, T, H, dk]  fp32, log of the per-channel forget gate (alpha = exp(g))
+ *   beta : [B, T, H]      in_dtype, the per-token, per-head write strength
+ *   initial_state : [N, H, dk, dv] fp32, or NULL for zeros
+ *   final_state   : [N, H, dk, dv] fp32, or NULL to skip; may equal initial_state
+ *                   (each state slice is read before it is written)
+ *   o    : [B, T, H, dv]  out_dtype; must not overlap any input
+ *   cu_seqlens : NULL for B fixed-length sequences of T tokens (N = B), or a
+ *                DEVICE int32 array [N+1] of token offsets for packed
+ *                variable-length input (then B must be 1, cu_seqlens[0] = 0,
+ *                cu_seqlens[N] = T, non-decreasing; empty sequences allowed,
+ *                their final state equals their initial state).
+ *   dk, dv : 64 or 128 (dk may differ from dv).
+ *   chunk_size : 64 (16 and 32 are accepted as well).
+ *   workspace : device scratch of at least kda_chunk_fwd_workspace_bytes()
+ *               bytes (may be NULL when that is 0); its contents on entry
+ *               are ignored and on exit are unspecified.  Two calls in
+ *               flight at once must not share a workspace.
+ */
+typedef struct {
+    uint32_t struct_size; /* = sizeof(kda_chunk_fwd_args) */
+    const void *q;
+    const void *k;
+    const void *v;
+    const float *g;
+    const void *beta;
+    const float *initial_state;
+    float *final_state;
+    void *o;
+    const int32_t *cu_seqlens;
+    int32_t B, T, H, dk, dv, num_seqs; /* num_seqs = N (must equal B when cu_seqlens is NULL) */
+    float scale;
+    kda_dtype in_dtype;  /* dtype of q, k, v, beta */
+    kda_dtype out_dtype; /* dtype of o */
+    int32_t chunk_size;
+    void *workspace;
+    size_t workspace_bytes;
+    void *stream; /* hipStream_t */
+} kda_chunk_fwd_args;
+
+/* Bytes of workspace kda_chunk_fwd needs for these arguments (host-only, no
+ * HIP call, only the size fields are read).  Returns (size_t)-1 when the
+ * arguments are invalid. */
+size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_fwd_args *args);
+
+kda_status kda_chunk_fwd(const kda_chunk_fwd_args *args);
+
+/*
+ * One recurrent decode step for N independent sequences (Kimi Linear review
+ * notes, section "Training and Inference": the fused recurrent kernel serves
+ * single steps and keeps the fixed-size recurrent state in the cache).
+ * Per (n, h): S~ = Diag(exp(g)) S;  S' = S~ + beta k (v - S~^T k)^T;
+ * o = scale * S'^T q.  Each state slice is read once and written once.
+ *
+ * Shapes:
+ *   q, k : [N, H, dk] in_dtype;  v : [N, H, dv] in_dtype;  g : [N, H, dk] fp32
+ *   beta : [N, H] in_dtype
+ *   initial_state : [N, H, dk, dv] fp32, or NULL for zeros
+ *   final_state   : [N, H, dk, dv] fp32, required; may equal initial_state
+ *                   (in-place update of the cached state)
+ *   o : [N, H, dv] out_dtype
+ *   dk, dv : 64 or 128.
+ */
+typedef struct {
+    uint32_t struct_size; /* = sizeof(kda_recurrent_step_args) */
+    const void *q;
+    const void *k;
+    const void *v;
+    const float *g;
+    const void *beta;
+    const float *initial_state;
+    float *final_state;
+    void *o;
+    int32_t N, H, dk, dv;
+    float scale;
+    kda_dtype in_dtype;
+    kda_dtype out_dtype;
+    void *stream; /* hipStream_t */
+} kda_recurrent_step_args;
+
+kda_status kda_recurrent_step(const kda_recurrent_step_args *args);
+
+/* Static text for a status code. */
+const char *kda_status_string(kda_status s);
+/* Thread-local text describing the last failure on this thread ("" if none). */
+const char *kda_last_error(void);
+/* KDA_ABI_VERSION of the loaded library. */
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

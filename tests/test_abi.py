@@ -1,0 +1,116 @@
+"""CPU tests of the C ABI: the library loads, exports every function that
+include/kda.h declares, and rejects bad arguments with the documented status
+codes before anything is launched (no GPU is touched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_52_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 32          # distinct fake device addresses: only compared, never used
+S = _lib.STATUS_CODE
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[\w\s\*]+?\b(kda_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_function_is_exported():
+    lib = _lib.load()
+    decl = header_functions()
+    assert decl == sorted(_lib.EXPORTS)
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert lib.kda_abi_version() == 1
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for code in range(8):
+        assert lib.kda_status_string(code).decode() not in ("", "unknown status")
+    assert lib.kda_status_string(99).decode() == "unknown status"
+
+
+def chunk_args(**kw):
+    a = _lib.ChunkFwdArgs()
+    base = dict(q=FAKE, k=2 * FAKE, v=3 * FAKE, g=4 * FAKE, beta=5 * FAKE, o=6 * FAKE,
+                initial_state=None, final_state=7 * FAKE, cu_seqlens=None,
+                B=1, T=128, H=2, dk=128, dv=128, num_seqs=1, scale=1.0,
+                in_dtype=_lib.KDA_DTYPE_BF16, out_dtype=_lib.KDA_DTYPE_FP32, chunk_size=64)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=96), "KDA_ERR_UNSUPPORTED"),
+    (dict(dv=256), "KDA_ERR_UNSUPPORTED"),
+    (dict(in_dtype=7), "KDA_ERR_UNSUPPORTED"),
+    (dict(chunk_size=48), "KDA_ERR_UNSUPPORTED"),
+    (dict(H=0), "KDA_ERR_BAD_SHAPE"),
+    (dict(T=-1), "KDA_ERR_BAD_SHAPE"),
+    (dict(num_seqs=2), "KDA_ERR_BAD_SHAPE"),
+    (dict(B=2, num_seqs=2, cu_seqlens=8 * FAKE), "KDA_ERR_BAD_SHAPE"),
+    (dict(scale=float("nan")), "KDA_ERR_BAD_SHAPE"),
+    (dict(q=None), "KDA_ERR_NULL_POINTER"),
+    (dict(o=None), "KDA_ERR_NULL_POINTER"),
+    (dict(o=FAKE + 64), "KDA_ERR_ALIAS"),
+    (dict(final_state=3 * FAKE + 8), "KDA_ERR_ALIAS"),
+    (dict(initial_state=7 * FAKE + 4096), "KDA_ERR_ALIAS"),
+])
+def test_chunk_fwd_rejects(kw, status):
+    rc = _lib.chunk_fwd_raw(chunk_args(**kw))
+    assert rc == S[status], (_lib.STATUS.get(rc), _lib.load().kda_last_error())
+    assert _lib.load().kda_last_error().decode() != ""
+
+
+def test_chunk_struct_size_is_checked():
+    a = chunk_args()
+    a.struct_size = ctypes.sizeof(_lib.ChunkFwdArgs) - 8
+    assert _lib.load().kda_chunk_fwd(ctypes.byref(a)) == S["KDA_ERR_BAD_STRUCT"]
+    assert _lib.load().kda_chunk_fwd(None) == S["KDA_ERR_NULL_POINTER"]
+
+
+def test_workspace_query():
+    assert _lib.chunk_workspace_raw(chunk_args(dk=7)) == 2 ** 64 - 1
+    n = _lib.chunk_workspace_raw(chunk_args(T=65536, H=16))
+    assert 0 <= n < 2 ** 40
+
+
+def step_args(**kw):
+    a = _lib.RecurrentStepArgs()
+    base = dict(q=FAKE, k=2 * FAKE, v=3 * FAKE, g=4 * FAKE, beta=5 * FAKE, o=6 * FAKE,
+                initial_state=7 * FAKE, final_state=7 * FAKE, N=4, H=2, dk=128, dv=128, scale=1.0,
+                in_dtype=_lib.KDA_DTYPE_BF16, out_dtype=_lib.KDA_DTYPE_FP32)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=32), "KDA_ERR_UNSUPPORTED"),
+    (dict(out_dtype=5), "KDA_ERR_UNSUPPORTED"),
+    (dict(N=-1), "KDA_ERR_BAD_SHAPE"),
+    (dict(H=0), "KDA_ERR_BAD_SHAPE"),
+    (dict(final_state=None), "KDA_ERR_NULL_POINTER"),
+    (dict(beta=None), "KDA_ERR_NULL_POINTER"),
+    (dict(o=5 * FAKE), "KDA_ERR_ALIAS"),
+    (dict(final_state=FAKE), "KDA_ERR_ALIAS"),
+    (dict(initial_state=7 * FAKE + 256), "KDA_ERR_ALIAS"),
+])
+def test_recurrent_step_rejects(kw, status):
+    rc = _lib.recurrent_step_raw(step_args(**kw))
+    assert rc == S[status], (_lib.STATUS.get(rc), _lib.load().kda_last_error())
+
+
+def test_empty_problems_are_no_ops():
+    # nothing to do: returns before any HIP call
+    assert _lib.recurrent_step_raw(step_args(N=0)) == 0
+    assert _lib.chunk_fwd_raw(chunk_args(B=0, num_seqs=0)) == 0
