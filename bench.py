@@ -1,0 +1,195 @@
+"""Benchmark: KDA chunkwise prefill (B=1, H=16, dk=dv=128, T=65536) and the
+recurrent decode step (256 sequences x 16 heads, 1024 steps) on one MI355X.
+
+One step = one kda_chunk_fwd over the whole 64K-token batch (every prefill
+stage: cumulative decay, decayed Gram blocks, UT inverse, WY factors, state
+propagation, output).  Inputs are drawn on the host, copied to HBM once, and
+are resident when timing starts.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+METRIC = "KDA prefill tokens/s (H=16,d=128,T=64K) + decode step us/token, % roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_alg_bytes(B, T, H, dk, dv, N, in_bytes=2, out_bytes=2, h0=True, hT=True):
+    """Algorithmic HBM bytes of one prefill: every input read once, every
+    output written once, no intermediates."""
+    th = B * T * H
+    per_th = (2 * dk + dv + 1) * in_bytes + dk * 4 + dv * out_bytes
+    return th * per_th + (int(h0) + int(hT)) * N * H * dk * dv * 4
+
+
+def decode_alg_bytes(N, H, dk, dv, in_bytes=2, out_bytes=2):
+    nh = N * H
+    return nh * (2 * dk * dv * 4 + (2 * dk + dv + 1) * in_bytes + dk * 4 + dv * out_bytes)
+
+
+def time_prefill(args):
+    import torch
+    import gated_delta_rule_52_amd as kda
+    from gated_delta_rule_52_amd.inputs import make_workload
+    x = make_workload("prefill_64k")
+    log(f"prefill_64k drawn: B={x.B} T={x.T} H={x.H} dk={x.dk} dv={x.dv}")
+    dev = "cuda:0"
+    bf, f32 = torch.bfloat16, torch.float32
+    t = lambda a, dt: torch.from_numpy(a).to(dev).to(dt)
+    q, k, v, beta = t(x.q, bf), t(x.k, bf), t(x.v, bf), t(x.beta, bf)
+    g, h0 = t(x.g, f32), t(x.h0, f32)
+    hT = torch.empty_like(h0)
+    o = torch.empty((x.B, x.T, x.H, x.dv), dtype=bf, device=dev)
+    step = lambda: kda.chunk_fwd(q, k, v, g, beta, initial_state=h0, final_state=hT, o=o,
+                                 out_dtype=bf)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"prefill: {ms:.3f} ms/step (events), wall {1e3 * wall / args.steps:.3f} ms/step")
+    nbytes = prefill_alg_bytes(x.B, x.T, x.H, x.dk, x.dv, x.N)
+    return x, ms, nbytes
+
+
+def time_decode(args):
+    import torch
+    from gated_delta_rule_52_amd import _lib
+    from gated_delta_rule_52_amd.inputs import WORKLOADS, make_decode_state, decode_step_pool
+    w = WORKLOADS["decode_256x16"]
+    N, H, dk, dv, steps, pool = w["N"], w["H"], w["dk"], w["dv"], w["steps"], w["pool"]
+    rng, S0 = make_decode_state(w["seed"], N, H, dk, dv, std=w["state_std"])
+    P = decode_step_pool(rng, pool, N, H, dk, dv, in_dtype=w["in_dtype"], gscale=w["gscale"])
+    dev = "cuda:0"
+    bf, f32 = torch.bfloat16, torch.float32
+    # every step reads its own inputs at its own offset
+    idx = torch.arange(steps) % pool
+    q = torch.from_numpy(P["q"]).to(dev).to(bf)[idx].contiguous()
+    k = torch.from_numpy(P["k"]).to(dev).to(bf)[idx].contiguous()
+    v = torch.from_numpy(P["v"]).to(dev).to(bf)[idx].contiguous()
+    g = torch.from_numpy(P["g"]).to(dev)[idx].contiguous()
+    beta = torch.from_numpy(P["beta"]).to(dev).to(bf)[idx].contiguous()
+    S = torch.from_numpy(S0).to(dev)
+    o = torch.empty((steps, N, H, dv), dtype=bf, device=dev)
+    lib = _lib.load()
+    stream = torch.cuda.current_stream()
+    argv = []
+    for s in range(steps):
+        a = _lib.RecurrentStepArgs()
+        a.struct_size = ctypes.sizeof(_lib.RecurrentStepArgs)
+        a.q, a.k, a.v = q[s].data_ptr(), k[s].data_ptr(), v[s].data_ptr()
+        a.g, a.beta = g[s].data_ptr(), beta[s].data_ptr()
+        a.initial_state = a.final_state = S.data_ptr()
+        a.o = o[s].data_ptr()
+        a.N, a.H, a.dk, a.dv, a.scale = N, H, dk, dv, 1.0
+        a.in_dtype = a.out_dtype = _lib.KDA_DTYPE_BF16
+        a.stream = stream.cuda_stream
+        argv.append(ctypes.byref(a))
+        argv.append(a)
+    refs = argv[0::2]
+
+    def run_all():
+        for r in refs:
+            rc = lib.kda_recurrent_step(r)
+            if rc:
+                _lib.check(rc)
+
+    run_all()  # warm-up pass (advances the state; timing does not depend on values)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run_all()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / steps
+    log(f"decode: {us:.2f} us/step over {steps} steps")
+    return dict(N=N, H=H, dk=dk, dv=dv, steps=steps, us=us, nbytes=decode_alg_bytes(N, H, dk, dv))
+
+
+def cpu_baseline(x):
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    units = x.N * x.H
+    threads = min(cores, units)
+    t0 = time.perf_counter()
+    oracle.forward(x.q, x.k, x.v, x.g, x.beta, h0=x.h0.astype(np.float64), nthreads=threads,
+                   want_state=True)
+    dt = time.perf_counter() - t0
+    log(f"oracle: {dt:.2f} s on {threads} threads")
+    return dict(value=x.B * x.T / dt, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"whole prefill_64k workload ({x.H} heads x {x.T} tokens, fp64 token "
+                       f"recurrence), {dt:.2f} s wall")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the operator's heads and sequences shard with no exchange, see the design notes",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    x, ms, nbytes = time_prefill(args)
+    tok_s = x.B * x.T / (ms * 1e-3)
+    ach = nbytes / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": "prefill_64k", "B": x.B, "T": x.T, "H": x.H, "dk": x.dk, "dv": x.dv,
+                   "in_dtype": "bf16", "out_dtype": "bf16", "chunk": 64, "initial_state": True},
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                     "alg_bytes_per_launch": nbytes, "kernel": "kda_chunk_fwd (one launch per step)"},
+    }
+    if not args.no_decode:
+        d = time_decode(args)
+        dach = d["nbytes"] / (d["us"] * 1e-6) / 1e9
+        rec["decode"] = {
+            "workload": "decode_256x16", "us_per_step": d["us"],
+            "us_per_token_step": d["us"], "us_per_token_amortized": d["us"] / d["N"],
+            "tokens_per_s": d["N"] / (d["us"] * 1e-6),
+            "steps": d["steps"],
+            "roofline": {"bound": "hbm", "achieved": dach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dach / HBM_PEAK_GBS, "alg_bytes_per_launch": d["nbytes"]},
+        }
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
