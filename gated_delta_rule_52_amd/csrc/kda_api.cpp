@@ -107,12 +107,6 @@ kda_status kda_chunk_fwd(const kda_chunk_fwd_args *a) {
     const int N = a->num_seqs;
     if (tokens > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o))
         return fail(KDA_ERR_NULL_POINTER, "q, k, v, g, beta and o are required");
-    if (a->cu_seqlens == nullptr && a->B > 0 && N > 0 && tokens == 0 && !a->final_state)
-        return KDA_OK;
-    const size_t need = kda::chunk_workspace_bytes(a->B, a->T, a->H, a->dk, a->dv, N, a->chunk_size,
-                                                   a->cu_seqlens != nullptr);
-    if (a->workspace_bytes < need || (need > 0 && !a->workspace))
-        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", a->workspace_bytes, need);
     // The output must not overlap any input.
     const size_t th = static_cast<size_t>(tokens) * a->H;
     const size_t in_sz = dsize(a->in_dtype);
@@ -133,6 +127,21 @@ kda_status kda_chunk_fwd(const kda_chunk_fwd_args *a) {
             return fail(KDA_ERR_ALIAS, "final_state partially overlaps initial_state");
     }
     if (N == 0 || (tokens == 0 && !a->final_state)) return KDA_OK;
+    if (N > 65535 || a->H > 65535) return fail(KDA_ERR_UNSUPPORTED, "N=%d H=%d (at most 65535 each)", N, a->H);
+    const size_t need = kda::chunk_workspace_bytes(a->B, a->T, a->H, a->dk, a->dv, N, a->chunk_size,
+                                                   a->cu_seqlens != nullptr);
+    if (a->workspace_bytes < need || (need > 0 && !a->workspace))
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", a->workspace_bytes, need);
+    if (a->workspace) {
+        const Range rw = range_of(a->workspace, need);
+        for (const Range &r : ins)
+            if (overlap(rw, r)) return fail(KDA_ERR_ALIAS, "workspace overlaps an input");
+        if (overlap(rw, ro)) return fail(KDA_ERR_ALIAS, "workspace overlaps o");
+        if (a->final_state && overlap(rw, range_of(a->final_state, sbytes)))
+            return fail(KDA_ERR_ALIAS, "workspace overlaps final_state");
+        if (a->initial_state && overlap(rw, range_of(a->initial_state, sbytes)))
+            return fail(KDA_ERR_ALIAS, "workspace overlaps initial_state");
+    }
 
     kda::ChunkLaunch L{};
     L.q = a->q; L.k = a->k; L.v = a->v; L.g = a->g; L.beta = a->beta;

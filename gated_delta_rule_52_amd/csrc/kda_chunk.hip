@@ -25,10 +25,13 @@
 // than exp(-80) in a channel, its diagonal block is recomputed pair by pair
 // (exp(G_r - G_i) directly), so no factor ever overflows fp32.
 //
-// Work split: one workgroup (4 waves) per (sequence, head, 32-column dv
-// slice), walking the sequence's chunks in order.  All products run on
-// v_mfma_f32_16x16x4f32 with fp32 operands staged in LDS.  This kernel is
-// the exact-fp32 path (fp32 inputs) and the reference for the bf16 path.
+// Work split: one workgroup (4 waves) per (segment, head, 32-column slice),
+// walking the segment's chunks in order.  All products run on
+// v_mfma_f32_16x16x4f32 with fp32 operands staged in LDS.  This is the
+// exact-fp32 path (fp32 inputs).  The same kernel serves the two parallel
+// passes of the segmented prefill (see kda_segments.hip): kLocal computes a
+// segment's local state H (zero start) and its transition P (identity start,
+// v = 0); kOut replays the segment from its true entering state and writes o.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -42,13 +45,12 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 
 constexpr float kMaxBlockDecay = 80.0f;  // exp(80) is far below FLT_MAX
 
-template <int DK, int C, int BV, bool InBf16, bool OutBf16>
+template <int DK, int C, int BV, bool InBf16, bool OutBf16, int MODE>
 __global__ void __launch_bounds__(256, 1)
 chunk_fp32_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
                   const void *__restrict__ v_, const float *__restrict__ g,
-                  const void *__restrict__ beta_, const float *h0, float *hT,
-                  void *__restrict__ o_, const int32_t *__restrict__ cu_seqlens,
-                  int T, int H, int DV, float scale) {
+                  const void *__restrict__ beta_, float *hT, void *__restrict__ o_,
+                  SegmentView sv, int H, int DV, float scale) {
     using In = Elem<InBf16>;
     using Out = Elem<OutBf16>;
     const typename In::T *q = static_cast<const typename In::T *>(q_);
@@ -74,26 +76,32 @@ chunk_fp32_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
     __shared__ float sBeta[C];
     __shared__ int sRange[NB];        // float bits of each block's largest decay
 
-    const int slice = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
+    const int slice = blockIdx.x, seg = blockIdx.y, h = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lk = lane >> 4;   // MFMA row/col lane, k lane
-    const int j0 = slice * BV;
+    if (seg >= sv.count()) return;
+    const int4 sd = sv.table[seg];
+    const int n = sd.x;
+    const bool last = sd.w & kSegLast;
+    if (MODE == kLocal && last) return;         // a last segment's P, H are never used
+    const int64_t t0 = sd.y, t1 = sd.z;
+    // kLocal: slices [0, DV/BV) are columns of H, the rest columns of P (dk x dk)
+    const bool pcols = MODE == kLocal && slice >= DV / BV;
+    const int j0 = (pcols ? slice - DV / BV : slice) * BV;
+    const int ld = pcols ? DK : DV;             // row stride of the state being built
 
-    int64_t t0, t1;
-    if (cu_seqlens) {
-        t0 = cu_seqlens[n];
-        t1 = cu_seqlens[n + 1];
-        if (t1 < t0) t1 = t0;
+    // ---- entering state slice -> LDS
+    if (MODE == kOut) {
+        const float *src = sv.sin + (static_cast<int64_t>(seg) * H + h) * DK * DV;
+        for (int e = tid; e < DK * BV; e += 256) {
+            const int i = e / BV, j = e % BV;
+            sS[i * BVP + j] = src[static_cast<int64_t>(i) * DV + j0 + j];
+        }
     } else {
-        t0 = static_cast<int64_t>(n) * T;
-        t1 = t0 + T;
-    }
-    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * DV;
-
-    // ---- initial state slice -> LDS
-    for (int e = tid; e < DK * BV; e += 256) {
-        const int i = e / BV, j = e % BV;
-        sS[i * BVP + j] = h0 ? h0[sbase + static_cast<int64_t>(i) * DV + j0 + j] : 0.f;
+        for (int e = tid; e < DK * BV; e += 256) {
+            const int i = e / BV, j = e % BV;
+            sS[i * BVP + j] = (pcols && i == j0 + j) ? 1.f : 0.f;
+        }
     }
 
     for (int64_t c0 = t0; c0 < t1; c0 += C) {
@@ -108,11 +116,28 @@ chunk_fp32_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
             sQ[r * DKP + c] = ok ? In::load(q, gi) : 0.f;
         }
         if (tid < C) sBeta[tid] = tid < L ? In::load(beta, (c0 + tid) * H + h) : 0.f;
-        for (int c = tid; c < DK; c += 256) {
+        {   // a1: per channel, 256/DK threads each scan C*DK/256 consecutive rows
+            constexpr int PARTS = 256 / DK, RP = C / PARTS;
+            const int c = tid % DK, part = tid / DK;
+            float gv[RP];
+#pragma unroll
+            for (int m = 0; m < RP; ++m) {
+                const int r = part * RP + m;
+                gv[m] = r < L ? g[((c0 + r) * H + h) * DK + c] : 0.f;
+            }
             float acc = 0.f;
-            for (int r = 0; r < C; ++r) {
-                if (r < L) acc += g[((c0 + r) * H + h) * DK + c];
-                sG[r * DKP + c] = acc;
+#pragma unroll
+            for (int m = 0; m < RP; ++m) {
+                acc += gv[m];
+                sG[(part * RP + m) * DKP + c] = acc;
+            }
+            __syncthreads();
+            float off = 0.f;
+            for (int pp = 0; pp < part; ++pp) off += sG[((pp + 1) * RP - 1) * DKP + c];
+            __syncthreads();
+            if (part > 0) {
+#pragma unroll
+                for (int m = 0; m < RP; ++m) sG[(part * RP + m) * DKP + c] += off;
             }
         }
         __syncthreads();
@@ -173,12 +198,21 @@ chunk_fp32_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
         // column per lane of wave 0: row r reads A[r][i] (i < r) and rows of T
         // above it; the lanes reconverge before row r is overwritten, so every
         // read of row r sees A and every read of an earlier row sees T.
+        // Entries above the diagonal of T are 0, so the sum may run over all
+        // i < r; every lane then runs the same loop.
         if (tid < C) {
             const int jcol = tid;
             for (int r = 0; r < C; ++r) {
-                float acc = (r == jcol) ? 1.f : 0.f;
-                for (int i = jcol; i < r; ++i) acc -= sA[r * CP + i] * sA[i * CP + jcol];
-                sA[r * CP + jcol] = acc;
+                float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+                int i = 0;
+                for (; i + 4 <= r; i += 4) {
+                    a0 += sA[r * CP + i] * sA[i * CP + jcol];
+                    a1 += sA[r * CP + i + 1] * sA[(i + 1) * CP + jcol];
+                    a2 += sA[r * CP + i + 2] * sA[(i + 2) * CP + jcol];
+                    a3 += sA[r * CP + i + 3] * sA[(i + 3) * CP + jcol];
+                }
+                for (; i < r; ++i) a0 += sA[r * CP + i] * sA[i * CP + jcol];
+                sA[r * CP + jcol] = ((r == jcol) ? 1.f : 0.f) - ((a0 + a1) + (a2 + a3));
             }
         }
         // ---- a5 (first half): X = beta (V - (e^G K) S), Y = (e^G Q) S; wave = row block
@@ -207,7 +241,9 @@ chunk_fp32_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int rr = 16 * wave + 4 * lk + jj, j = 16 * t + lr;
-                    const float vv = rr < L ? In::load(v, ((c0 + rr) * H + h) * static_cast<int64_t>(DV) + j0 + j) : 0.f;
+                    const float vv = (rr < L && !pcols)
+                                         ? In::load(v, ((c0 + rr) * H + h) * static_cast<int64_t>(DV) + j0 + j)
+                                         : 0.f;
                     sX[rr * BVP + j] = sBeta[rr] * (vv - accX[t][jj]);
                 }
             }
@@ -237,7 +273,7 @@ chunk_fp32_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
         __syncthreads();
 
         // ---- a6: O = scale Y + A_qk V_new
-        if (rowblk) {
+        if (MODE == kOut && rowblk) {
             const int r = 16 * wave + lr;
 #pragma unroll
             for (int t = 0; t < NCT; ++t) accY[t] *= scale;
@@ -282,40 +318,49 @@ chunk_fp32_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
         __syncthreads();
     }
 
-    if (hT) {
+    float *dst = nullptr;
+    if (MODE == kOut) {
+        if (last && hT) dst = hT + (static_cast<int64_t>(n) * H + h) * DK * DV;
+    } else {
+        dst = (pcols ? sv.P : sv.Hs) + (static_cast<int64_t>(seg) * H + h) * DK * ld;
+    }
+    if (dst) {
         for (int e = tid; e < DK * BV; e += 256) {
             const int i = e / BV, j = e % BV;
-            hT[sbase + static_cast<int64_t>(i) * DV + j0 + j] = sS[i * BVP + j];
+            dst[static_cast<int64_t>(i) * ld + j0 + j] = sS[i * BVP + j];
         }
     }
 }
 
-size_t chunk_workspace_bytes(int, int, int, int, int, int, int, bool) { return 0; }
-
-template <int DK, int C>
-static hipError_t launch_chunk_dk(const ChunkLaunch &L) {
+template <int DK, int C, int MODE>
+static void launch_fp32_dk(const ChunkLaunch &L, const SegmentView &sv, int max_segs) {
     constexpr int BV = 32;
-    dim3 grid(L.dv / BV, L.H, L.N), block(256);
-#define KDA_CHUNK(IB, OB)                                                                             \
-    hipLaunchKernelGGL((chunk_fp32_kernel<DK, C, BV, IB, OB>), grid, block, 0, L.stream, L.q, L.k, L.v, \
-                       L.g, L.beta, L.h0, L.hT, L.o, L.cu_seqlens, L.T, L.H, L.dv, L.scale)
+    const int slices = MODE == kOut ? L.dv / BV : (L.dv + DK) / BV;
+    dim3 grid(slices, max_segs, L.H), block(256);
+#define KDA_CHUNK(IB, OB)                                                                               \
+    hipLaunchKernelGGL((chunk_fp32_kernel<DK, C, BV, IB, OB, MODE>), grid, block, 0, L.stream, L.q, L.k, \
+                       L.v, L.g, L.beta, L.hT, L.o, sv, L.H, L.dv, L.scale)
     if (L.in_bf16 && L.out_bf16) KDA_CHUNK(true, true);
     else if (L.in_bf16) KDA_CHUNK(true, false);
     else if (L.out_bf16) KDA_CHUNK(false, true);
     else KDA_CHUNK(false, false);
 #undef KDA_CHUNK
-    return hipGetLastError();
 }
 
-template <int DK>
-static hipError_t launch_chunk_c(const ChunkLaunch &L) {
-    if (L.chunk == 64) return launch_chunk_dk<DK, 64>(L);
-    if (L.chunk == 32) return launch_chunk_dk<DK, 32>(L);
-    return launch_chunk_dk<DK, 16>(L);
+template <int MODE>
+void launch_fp32_pass(const ChunkLaunch &L, const SegmentView &sv, int max_segs) {
+    if (L.dk == 128) {
+        if (L.chunk == 64) launch_fp32_dk<128, 64, MODE>(L, sv, max_segs);
+        else if (L.chunk == 32) launch_fp32_dk<128, 32, MODE>(L, sv, max_segs);
+        else launch_fp32_dk<128, 16, MODE>(L, sv, max_segs);
+    } else {
+        if (L.chunk == 64) launch_fp32_dk<64, 64, MODE>(L, sv, max_segs);
+        else if (L.chunk == 32) launch_fp32_dk<64, 32, MODE>(L, sv, max_segs);
+        else launch_fp32_dk<64, 16, MODE>(L, sv, max_segs);
+    }
 }
 
-hipError_t launch_chunk(const ChunkLaunch &L) {
-    return L.dk == 128 ? launch_chunk_c<128>(L) : launch_chunk_c<64>(L);
-}
+template void launch_fp32_pass<kLocal>(const ChunkLaunch &, const SegmentView &, int);
+template void launch_fp32_pass<kOut>(const ChunkLaunch &, const SegmentView &, int);
 
 }  // namespace kda

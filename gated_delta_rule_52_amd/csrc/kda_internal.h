@@ -48,4 +48,31 @@ struct ChunkLaunch {
 size_t chunk_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int chunk, bool varlen);
 hipError_t launch_chunk(const ChunkLaunch &L);
 
+// ---- segmented prefill (kda_segments.hip)
+//
+// Sequences are cut into segments of whole chunks.  Pass 1 (kLocal) gives
+// every segment but the last of each sequence its local state H (zero start)
+// and transition P (identity start, v = 0), so that leaving state =
+// P * entering state + H.  The combine pass chains these per sequence from
+// the initial state and stores each segment's entering state; pass 2 (kOut)
+// replays every segment from its entering state and writes o (and, for the
+// last segment, the final state).
+constexpr int kLocal = 0;
+constexpr int kOut = 1;
+constexpr int kSegLast = 1;
+constexpr int kSegFirst = 2;
+
+struct SegmentView {
+    const int4 *table;      // [max_segs] {sequence, first token, end token, flags}
+    const int32_t *seq_seg; // [N + 1] first segment of each sequence; [N] = count
+    int N;
+    float *P;               // [max_segs, H, dk, dk]
+    float *Hs;              // [max_segs, H, dk, dv]
+    float *sin;             // [max_segs, H, dk, dv] entering states
+    __device__ __forceinline__ int count() const { return seq_seg[N]; }
+};
+
+template <int MODE>
+void launch_fp32_pass(const ChunkLaunch &L, const SegmentView &sv, int max_segs);
+
 }  // namespace kda

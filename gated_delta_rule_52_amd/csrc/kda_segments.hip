@@ -1,0 +1,212 @@
+// kda_segments.hip - segmented chunkwise prefill: the chunk table, the
+// combine pass, and the host orchestration of the passes.
+//
+// Only the fp32 state crosses chunk boundaries (Kimi Linear review notes,
+// section "Chunkwise Algorithm"), and the state map of a run of chunks is
+// affine: leaving = P * entering + H, with P the product of the chunks'
+// transitions (dk x dk) and H the state reached from zero.  This lets the
+// long, serial chunk chain of a sequence be cut into segments that run in
+// parallel on all compute units:
+//
+//   table   : cut every sequence into segments of whole chunks, chunks never
+//             straddling two sequences (packed variable length);
+//   pass 1  : per (segment, head), in parallel: H and P of the segment;
+//   combine : per (sequence, head, dv slice), serial over its segments:
+//             entering(s+1) = P_s entering(s) + H_s, from the initial state;
+//   pass 2  : per (segment, head), in parallel: replay from the entering
+//             state, write o and (last segment) the final state.
+//
+// All passes run on the caller's stream; nothing is allocated.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kTargetUnits = 512;  // segments x heads wanted for two waves of workgroups
+
+struct Plan {
+    int seg_len;    // tokens per segment (a multiple of the chunk size)
+    int max_segs;   // bound on the number of segments
+    size_t off_table, off_seq, off_P, off_H, off_S, bytes;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t{255}; }
+
+Plan make_plan(int B, int T, int H, int dk, int dv, int N, int chunk, bool varlen) {
+    Plan p{};
+    const int64_t tokens = varlen ? T : static_cast<int64_t>(B) * T;
+    const int64_t chunks = varlen ? (tokens + chunk - 1) / chunk + N
+                                  : static_cast<int64_t>(B) * ((T + chunk - 1) / chunk);
+    int64_t per = (chunks * H + kTargetUnits - 1) / kTargetUnits;
+    if (per < 1) per = 1;
+    if (per > 64) per = 64;
+    p.seg_len = static_cast<int>(per) * chunk;
+    p.max_segs = varlen ? static_cast<int>((tokens + p.seg_len - 1) / p.seg_len + N)
+                        : B * ((T + p.seg_len - 1) / p.seg_len);
+    if (p.max_segs < 1) p.max_segs = 1;
+    const size_t ms = static_cast<size_t>(p.max_segs);
+    size_t o = 0;
+    p.off_table = o; o = align256(o + ms * sizeof(int4));
+    p.off_seq = o;   o = align256(o + (static_cast<size_t>(N) + 1) * sizeof(int32_t));
+    p.off_P = o;     o = align256(o + ms * H * dk * dk * sizeof(float));
+    p.off_H = o;     o = align256(o + ms * H * dk * dv * sizeof(float));
+    p.off_S = o;     o = align256(o + ms * H * dk * dv * sizeof(float));
+    p.bytes = o;
+    return p;
+}
+
+// a7: the segment table.  Each thread owns a contiguous range of sequences;
+// one block-wide exclusive scan of the per-thread segment counts gives every
+// sequence its first segment.
+__global__ void __launch_bounds__(256)
+build_segments_kernel(const int32_t *__restrict__ cu_seqlens, int T, int N, int seg_len,
+                      int4 *__restrict__ table, int32_t *__restrict__ seq_seg) {
+    __shared__ int s_cnt[256];
+    const int tid = threadIdx.x;
+    const int per = (N + 255) / 256;
+    const int n0 = tid * per, n1 = min(N, n0 + per);
+    auto bounds = [&](int n, int64_t &a, int64_t &b) {
+        if (cu_seqlens) {
+            a = cu_seqlens[n];
+            b = cu_seqlens[n + 1];
+            if (b < a) b = a;
+        } else {
+            a = static_cast<int64_t>(n) * T;
+            b = a + T;
+        }
+    };
+    int cnt = 0;
+    for (int n = n0; n < n1; ++n) {
+        int64_t a, b;
+        bounds(n, a, b);
+        cnt += static_cast<int>((b - a + seg_len - 1) / seg_len);
+    }
+    s_cnt[tid] = cnt;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int i = 0; i < 256; ++i) {
+            const int c = s_cnt[i];
+            s_cnt[i] = run;
+            run += c;
+        }
+        seq_seg[N] = run;
+    }
+    __syncthreads();
+    int idx = s_cnt[tid];
+    for (int n = n0; n < n1; ++n) {
+        int64_t a, b;
+        bounds(n, a, b);
+        seq_seg[n] = idx;
+        const int ns = static_cast<int>((b - a + seg_len - 1) / seg_len);
+        for (int s = 0; s < ns; ++s) {
+            const int64_t t0 = a + static_cast<int64_t>(s) * seg_len;
+            const int64_t t1 = t0 + seg_len < b ? t0 + seg_len : b;
+            const int flags = (s == ns - 1 ? kSegLast : 0) | (s == 0 ? kSegFirst : 0);
+            table[idx++] = make_int4(n, static_cast<int>(t0), static_cast<int>(t1), flags);
+        }
+    }
+}
+
+// Combine: per (sequence, head, 16-column slice of dv), walk the segments in
+// order, store each entering state and advance it by  S <- P_s S + H_s.
+// P_s (dk x dk fp32) is staged in LDS; the next one is fetched into registers
+// while the current product runs.  fp32 FMA throughout.
+template <int DK>
+__global__ void __launch_bounds__(256, 1)
+combine_kernel(SegmentView sv, const float *h0, float *hT, int H, int DV) {
+    constexpr int BV = 16, DKP = DK + 1, RG = 256 / BV, ROWS = DK / RG;
+    constexpr int PV4 = DK * DK / 4 / 256;   // float4 loads per thread for one P
+    __shared__ float sP[DK * DKP];
+    __shared__ float sS[DK * BV];
+    const int slice = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
+    const int tid = threadIdx.x, j = tid % BV, ig = tid / BV;
+    const int j0 = slice * BV;
+    const int first = sv.seq_seg[n], end = sv.seq_seg[n + 1];
+    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * DV;
+
+    float s[ROWS];
+#pragma unroll
+    for (int u = 0; u < ROWS; ++u) {
+        const int i = ig + RG * u;
+        s[u] = h0 ? h0[sbase + static_cast<int64_t>(i) * DV + j0 + j] : 0.f;
+    }
+    if (first == end) {  // empty sequence: the final state is the initial state
+        if (hT)
+#pragma unroll
+            for (int u = 0; u < ROWS; ++u) hT[sbase + static_cast<int64_t>(ig + RG * u) * DV + j0 + j] = s[u];
+        return;
+    }
+    float4 pn[PV4];
+    auto fetch = [&](int seg) {
+        const float4 *src = reinterpret_cast<const float4 *>(sv.P + (static_cast<int64_t>(seg) * H + h) * DK * DK);
+#pragma unroll
+        for (int m = 0; m < PV4; ++m) pn[m] = src[tid + 256 * m];
+    };
+    if (first + 1 < end) fetch(first);
+    for (int seg = first; seg < end; ++seg) {
+        float *sin = sv.sin + (static_cast<int64_t>(seg) * H + h) * DK * DV;
+#pragma unroll
+        for (int u = 0; u < ROWS; ++u) sin[static_cast<int64_t>(ig + RG * u) * DV + j0 + j] = s[u];
+        if (seg + 1 == end) break;
+        __syncthreads();  // previous product finished with sP and sS
+#pragma unroll
+        for (int m = 0; m < PV4; ++m) {
+            const int e = 4 * (tid + 256 * m), r = e / DK, c = e % DK;
+            sP[r * DKP + c] = pn[m].x;
+            sP[r * DKP + c + 1] = pn[m].y;
+            sP[r * DKP + c + 2] = pn[m].z;
+            sP[r * DKP + c + 3] = pn[m].w;
+        }
+#pragma unroll
+        for (int u = 0; u < ROWS; ++u) sS[(ig + RG * u) * BV + j] = s[u];
+        __syncthreads();
+        if (seg + 2 < end) fetch(seg + 1);
+        const float *hs = sv.Hs + (static_cast<int64_t>(seg) * H + h) * DK * DV;
+#pragma unroll
+        for (int u = 0; u < ROWS; ++u) {
+            const int i = ig + RG * u;
+            float a0 = 0.f, a1 = 0.f;
+            for (int m = 0; m < DK; m += 2) {
+                a0 += sP[i * DKP + m] * sS[m * BV + j];
+                a1 += sP[i * DKP + m + 1] * sS[(m + 1) * BV + j];
+            }
+            s[u] = (a0 + a1) + hs[static_cast<int64_t>(i) * DV + j0 + j];
+        }
+    }
+}
+
+}  // namespace
+
+size_t chunk_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int chunk, bool varlen) {
+    return make_plan(B, T, H, dk, dv, N, chunk, varlen).bytes;
+}
+
+hipError_t launch_chunk(const ChunkLaunch &L) {
+    const bool varlen = L.cu_seqlens != nullptr;
+    const Plan p = make_plan(L.B, L.T, L.H, L.dk, L.dv, L.N, L.chunk, varlen);
+    char *ws = static_cast<char *>(L.workspace);
+    SegmentView sv;
+    sv.table = reinterpret_cast<const int4 *>(ws + p.off_table);
+    sv.seq_seg = reinterpret_cast<const int32_t *>(ws + p.off_seq);
+    sv.N = L.N;
+    sv.P = reinterpret_cast<float *>(ws + p.off_P);
+    sv.Hs = reinterpret_cast<float *>(ws + p.off_H);
+    sv.sin = reinterpret_cast<float *>(ws + p.off_S);
+
+    hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(256), 0, L.stream, L.cu_seqlens, L.T, L.N,
+                       p.seg_len, reinterpret_cast<int4 *>(ws + p.off_table),
+                       reinterpret_cast<int32_t *>(ws + p.off_seq));
+    launch_fp32_pass<kLocal>(L, sv, p.max_segs);
+    dim3 cgrid(L.dv / 16, L.H, L.N);
+    if (L.dk == 128)
+        hipLaunchKernelGGL(combine_kernel<128>, cgrid, dim3(256), 0, L.stream, sv, L.h0, L.hT, L.H, L.dv);
+    else
+        hipLaunchKernelGGL(combine_kernel<64>, cgrid, dim3(256), 0, L.stream, sv, L.h0, L.hT, L.H, L.dv);
+    launch_fp32_pass<kOut>(L, sv, p.max_segs);
+    return hipGetLastError();
+}
+
+}  // namespace kda
