@@ -75,4 +75,9 @@ struct SegmentView {
 template <int MODE>
 void launch_fp32_pass(const ChunkLaunch &L, const SegmentView &sv, int max_segs);
 
+// fp16/bf16 matrix-core passes (kda_chunk_f16.hip): bf16 inputs, dk = dv = 128, chunk 64
+bool f16_pass_supported(const ChunkLaunch &L);
+template <int MODE>
+void launch_f16_pass(const ChunkLaunch &L, const SegmentView &sv, int max_segs);
+
 }  // namespace kda

@@ -199,13 +199,16 @@ hipError_t launch_chunk(const ChunkLaunch &L) {
     hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(256), 0, L.stream, L.cu_seqlens, L.T, L.N,
                        p.seg_len, reinterpret_cast<int4 *>(ws + p.off_table),
                        reinterpret_cast<int32_t *>(ws + p.off_seq));
-    launch_fp32_pass<kLocal>(L, sv, p.max_segs);
+    const bool fast = f16_pass_supported(L);
+    if (fast) launch_f16_pass<kLocal>(L, sv, p.max_segs);
+    else launch_fp32_pass<kLocal>(L, sv, p.max_segs);
     dim3 cgrid(L.dv / 16, L.H, L.N);
     if (L.dk == 128)
         hipLaunchKernelGGL(combine_kernel<128>, cgrid, dim3(256), 0, L.stream, sv, L.h0, L.hT, L.H, L.dv);
     else
         hipLaunchKernelGGL(combine_kernel<64>, cgrid, dim3(256), 0, L.stream, sv, L.h0, L.hT, L.H, L.dv);
-    launch_fp32_pass<kOut>(L, sv, p.max_segs);
+    if (fast) launch_f16_pass<kOut>(L, sv, p.max_segs);
+    else launch_fp32_pass<kOut>(L, sv, p.max_segs);
     return hipGetLastError();
 }
 

@@ -170,18 +170,20 @@ def test_extreme_gates(kda):
     check_prefill(kda, x)
 
 
-def test_single_token_prefill_equals_decode(kda):
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_single_token_prefill_equals_decode(kda, dt):
     import torch
-    x = make_prefill(54, 4, 1, 3, 128, 128, h0_std=0.3, name="t1")
+    x = make_prefill(54, 4, 1, 3, 128, 128, in_dtype=dt, h0_std=0.3, name="t1")
     o, hT = run_prefill(kda, x)
     d = upload(x)
     S = d["h0"].clone()
     od = kda.recurrent_step(d["q"][:, 0], d["k"][:, 0], d["v"][:, 0], d["g"][:, 0], d["beta"][:, 0], S,
                             out_dtype=torch.float32)
     torch.cuda.synchronize()
+    tol = TOL_FP32 if dt == "fp32" else TOL_BF16
     a, b = o[:, 0].cpu().numpy(), od.cpu().numpy()
-    assert np.linalg.norm(a - b) / np.linalg.norm(b) < 1e-5
-    assert np.linalg.norm(hT.cpu().numpy() - S.cpu().numpy()) / np.linalg.norm(S.cpu().numpy()) < 1e-5
+    assert np.linalg.norm(a - b) / np.linalg.norm(b) < tol
+    assert np.linalg.norm(hT.cpu().numpy() - S.cpu().numpy()) / np.linalg.norm(S.cpu().numpy()) < tol
 
 
 def test_prefill_equals_decode_steps(kda):
@@ -201,11 +203,14 @@ def test_prefill_equals_decode_steps(kda):
     assert e < TOL_BF16 and es < TOL_BF16
 
 
-def test_state_in_place_and_split(kda):
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_state_in_place_and_split(kda, dt):
     """final_state may alias initial_state; two halves chained through the
-    state equal one run."""
+    state equal one run (to rounding: the bf16 path rounds its matrix-core
+    operands per chunk, so a different cut rounds differently)."""
     import torch
-    x = make_prefill(56, 1, 300, 2, 128, 128, h0_std=0.3, name="split")
+    x = make_prefill(56, 1, 300, 2, 128, 128, in_dtype=dt, h0_std=0.3, name="split")
+    tol = TOL_FP32 if dt == "fp32" else TOL_BF16
     d = upload(x)
     o_full, h_full = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["h0"],
                                    out_dtype=torch.float32)
@@ -222,10 +227,10 @@ def test_state_in_place_and_split(kda):
     e = (o2 - o_full).norm().item() / o_full.norm().item()
     es = (S - h_full).norm().item() / h_full.norm().item()
     say(f"  split vs full: o={e:.3e} state={es:.3e}")
-    assert e < 1e-5 and es < 1e-5
+    assert e < tol and es < tol
     o_ref, h_ref = oracle_forward(x, [0, 1])
     eo, ess = slice_errors(o2.cpu().numpy(), S.cpu().numpy(), o_ref, h_ref, x, [0, 1])
-    assert eo <= TOL_BF16 and ess <= TOL_BF16
+    assert eo <= tol and ess <= tol
 
 
 def test_bf16_output_is_rounded_fp32_output_and_deterministic(kda):
