@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_chunk.hip", "kda_segments.hip", "kda_chunk_f16.hip"]
+SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_chunk.hip", "kda_segments.hip", "kda_prep.hip",
+           "kda_scan.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -96,7 +96,7 @@ int kda_abi_version(void) { return KDA_ABI_VERSION; }
 size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_fwd_args *a) {
     if (check_chunk_sizes(a) != KDA_OK) return static_cast<size_t>(-1);
     return kda::chunk_workspace_bytes(a->B, a->T, a->H, a->dk, a->dv, a->num_seqs, a->chunk_size,
-                                      a->cu_seqlens != nullptr);
+                                      a->cu_seqlens != nullptr, a->in_dtype == KDA_DTYPE_BF16);
 }
 
 kda_status kda_chunk_fwd(const kda_chunk_fwd_args *a) {
@@ -129,7 +129,7 @@ kda_status kda_chunk_fwd(const kda_chunk_fwd_args *a) {
     if (N == 0 || (tokens == 0 && !a->final_state)) return KDA_OK;
     if (N > 65535 || a->H > 65535) return fail(KDA_ERR_UNSUPPORTED, "N=%d H=%d (at most 65535 each)", N, a->H);
     const size_t need = kda::chunk_workspace_bytes(a->B, a->T, a->H, a->dk, a->dv, N, a->chunk_size,
-                                                   a->cu_seqlens != nullptr);
+                                                   a->cu_seqlens != nullptr, a->in_dtype == KDA_DTYPE_BF16);
     if (a->workspace_bytes < need || (need > 0 && !a->workspace))
         return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", a->workspace_bytes, need);
     if (a->workspace) {

@@ -45,7 +45,7 @@ struct ChunkLaunch {
     hipStream_t stream;
 };
 
-size_t chunk_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int chunk, bool varlen);
+size_t chunk_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int chunk, bool varlen, bool in_bf16);
 hipError_t launch_chunk(const ChunkLaunch &L);
 
 // ---- segmented prefill (kda_segments.hip)
@@ -75,9 +75,13 @@ struct SegmentView {
 template <int MODE>
 void launch_fp32_pass(const ChunkLaunch &L, const SegmentView &sv, int max_segs);
 
-// fp16/bf16 matrix-core passes (kda_chunk_f16.hip): bf16 inputs, dk = dv = 128, chunk 64
-bool f16_pass_supported(const ChunkLaunch &L);
+// fp16/bf16 matrix-core path (bf16 inputs, dk = dv = 128, chunk 64): a
+// parallel prep kernel writes one operand pack per chunk and head
+// (kda_prep.hip); the local and output passes stream them (kda_scan.hip).
+bool f16_path_supported(bool in_bf16, int dk, int dv, int chunk);
+size_t pack_bytes();  // bytes of one operand pack
+void launch_prep(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, void *packs);
 template <int MODE>
-void launch_f16_pass(const ChunkLaunch &L, const SegmentView &sv, int max_segs);
+void launch_scan(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, const void *packs);
 
 }  // namespace kda

@@ -1,0 +1,167 @@
+// kda_mfma.h - helpers shared by the fp16/bf16 matrix-core prefill kernels
+// (kda_prep.hip, kda_scan.hip) for gfx950: MFMA wrappers, power-of-two
+// scaling, packed conversions, cross-lane moves, buffer-resource accesses and
+// the layout of the per-chunk operand pack that the two kernels exchange.
+#pragma once
+
+#include "kda_device.h"
+
+namespace kda {
+namespace mc {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef int i4 __attribute__((ext_vector_type(4)));
+typedef int i2 __attribute__((ext_vector_type(2)));
+typedef unsigned u2 __attribute__((ext_vector_type(2)));
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+
+constexpr int DK = 128, DV = 128, C = 64;
+
+__device__ __forceinline__ f4 mma32(h8 a, h8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mma16(h4 a, h4 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mmab(b8 a, b8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
+
+// 2^e as a float (|e| < 127)
+__device__ __forceinline__ float pow2(int e) { return __int_as_float((e + 127) << 23); }
+
+// Exponent e with m * 2^-e in [0.5, 1) for m > 0 (0 for m == 0 or denormal m).
+__device__ __forceinline__ int exp_of(float m) {
+    const int b = (__float_as_int(m) >> 23) & 0xff;
+    return b == 0 ? 0 : b - 126;
+}
+
+__device__ __forceinline__ uint32_t hbits(_Float16 x) { return __builtin_bit_cast(uint16_t, x); }
+__device__ __forceinline__ uint32_t bbits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+    return hbits(static_cast<_Float16>(a)) | (hbits(static_cast<_Float16>(b)) << 16);
+}
+__device__ __forceinline__ h4 to_h4(f4 v, float s) {
+    return h4{static_cast<_Float16>(v[0] * s), static_cast<_Float16>(v[1] * s),
+              static_cast<_Float16>(v[2] * s), static_cast<_Float16>(v[3] * s)};
+}
+// bf16 high and low parts of two values, each pair packed in one word
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    const __bf16 ha = static_cast<__bf16>(a), hb = static_cast<__bf16>(b);
+    hi = bbits(ha) | (bbits(hb) << 16);
+    lo = bbits(static_cast<__bf16>(a - static_cast<float>(ha))) |
+         (bbits(static_cast<__bf16>(b - static_cast<float>(hb))) << 16);
+}
+// the two bf16 values packed in a word, widened
+__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ int bperm(int src_lane, uint32_t v) {
+    return __builtin_amdgcn_ds_bpermute(src_lane << 2, static_cast<int>(v));
+}
+
+// Two vertically stacked 16x16 accumulator tiles (rows 0-15 in f0, 16-31 in
+// f1; lane = 16*g + n holds rows 4g..4g+3 of column n) -> the B operand of a
+// 16x16x32 product (lane = 16*g + n holds rows 8g..8g+7 of column n), scaled
+// by s and rounded to fp16.  Pure cross-lane movement, no LDS storage.
+__device__ __forceinline__ h8 acc_to_b32(f4 f0, f4 f1, float s, int lane) {
+    const int g = lane >> 4, n = lane & 15;
+    const uint32_t p0a = pack_h2(f0[0] * s, f0[1] * s), p0b = pack_h2(f0[2] * s, f0[3] * s);
+    const uint32_t p1a = pack_h2(f1[0] * s, f1[1] * s), p1b = pack_h2(f1[2] * s, f1[3] * s);
+    const int s0 = ((g & 1) << 5) | n, s1 = s0 + 16;
+    const bool hi = g >= 2;
+    // every lane takes part in every permute (a permute reading an inactive
+    // lane returns garbage), then each lane keeps the tile it needs
+    const int a0 = bperm(s0, p0a), a1 = bperm(s0, p1a);
+    const int b0 = bperm(s0, p0b), b1 = bperm(s0, p1b);
+    const int c0 = bperm(s1, p0a), c1 = bperm(s1, p1a);
+    const int e0 = bperm(s1, p0b), e1 = bperm(s1, p1b);
+    const int d0 = hi ? a1 : a0, d1 = hi ? b1 : b0, d2 = hi ? c1 : c0, d3 = hi ? e1 : e0;
+    return __builtin_bit_cast(h8, (i4{d0, d1, d2, d3}));
+}
+
+// Maximum over the wave, returned wave-uniform: butterfly within each half
+// of the wave by swizzles (the pattern is an immediate, so no lane-index
+// registers), then the two halves' results read as scalars.
+template <int XorMask>
+__device__ __forceinline__ float swz_xor(float x) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (XorMask << 10) | 0x1f));
+}
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, swz_xor<16>(x));
+    x = fmaxf(x, swz_xor<8>(x));
+    x = fmaxf(x, swz_xor<4>(x));
+    x = fmaxf(x, swz_xor<2>(x));
+    x = fmaxf(x, swz_xor<1>(x));
+    const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    return fmaxf(lo, hi);
+}
+
+// Buffer resource over [base, base + bytes): raw buffer accesses at or past
+// the end read as zero and their stores are dropped.  Offsets are 32-bit
+// bytes from a wave-uniform base, so ragged tails need no masking and no
+// per-lane 64-bit address has to live across a loop.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+__device__ __forceinline__ uint32_t ld32(rsrc_t r, uint32_t off, int soff = 0) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), soff, 0);
+}
+__device__ __forceinline__ uint32_t ld16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, 0);
+}
+__device__ __forceinline__ u2 ld64(rsrc_t r, uint32_t off, int soff = 0) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), soff, 0);
+}
+__device__ __forceinline__ void st32(rsrc_t r, uint32_t v, uint32_t off, int soff = 0) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, static_cast<int>(off), soff, 0);
+}
+__device__ __forceinline__ void st64(rsrc_t r, u2 v, uint32_t off, int soff = 0) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, static_cast<int>(off), soff, 0);
+}
+__device__ __forceinline__ void st128(rsrc_t r, u4 v, uint32_t off, int soff = 0) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(off), soff, 0);
+}
+
+// ---- per-chunk operand pack (one per chunk and head, written by the prep
+// kernel, streamed by the scan kernels).  Every fp16 matrix carries a
+// power-of-two scale: stored = true value * 2^-e.  The 16-byte units of a
+// row are XOR-swizzled by the row's low three bits, so the pack can be
+// copied into LDS as a straight line and read there without bank conflicts.
+//
+//   [0, 512)        gamma: exp(G_last) per channel, fp32
+//   [512, 1024)     header: int exponents e_w, e_q, e_k, e_u, e_a
+//   W   [64][128]   T beta (e^G k)            A operand of W S
+//   KT  [128][64]   (e^{G_last - G} k)^T      A operand of the state update
+//   Q   [64][128]   scale e^G q               A operand of Q S
+//   A   [10][16][16] blocks (a, b), b <= a, of the decayed scale q k^T
+//   U   [8][4][64][4] T beta v in accumulator order: [16-column tile][row
+//                   block][lane][row within lane]
+constexpr int kPkGamma = 0;
+constexpr int kPkHdr = 512;
+constexpr int kPkW = 1024;
+constexpr int kPkKT = kPkW + C * DK * 2;
+constexpr int kPkQ = kPkKT + DK * C * 2;
+constexpr int kPkA = kPkQ + C * DK * 2;
+constexpr int kPkU = kPkA + 10 * 16 * 16 * 2;
+constexpr int kPkBytes = kPkU + C * DV * 2;
+constexpr int kPkLocal = kPkQ;   // bytes the local pass copies to LDS
+constexpr int kPkOut = kPkU;     // bytes the output pass copies to LDS
+static_assert(kPkLocal % 1024 == 0 && kPkOut % 1024 == 0, "whole 1 KiB wave copies");
+enum { kHdrW = 0, kHdrQ = 1, kHdrK = 2, kHdrU = 3, kHdrA = 4 };
+
+// byte offset of the 16-byte unit u of row r in a swizzled matrix whose rows
+// are `row_bytes` long
+__device__ __forceinline__ int swz(int r, int u, int row_bytes) {
+    return r * row_bytes + ((u ^ (r & 7)) << 4);
+}
+
+}  // namespace mc
+}  // namespace kda

@@ -10,6 +10,8 @@
 //
 //   table   : cut every sequence into segments of whole chunks, chunks never
 //             straddling two sequences (packed variable length);
+//   prep    : (matrix-core path) per (chunk, head), in parallel: everything
+//             in a chunk that does not depend on the entering state;
 //   pass 1  : per (segment, head), in parallel: H and P of the segment;
 //   combine : per (sequence, head, dv slice), serial over its segments:
 //             entering(s+1) = P_s entering(s) + H_s, from the initial state;
@@ -27,14 +29,16 @@ namespace {
 constexpr int kTargetUnits = 512;  // segments x heads wanted for two waves of workgroups
 
 struct Plan {
-    int seg_len;    // tokens per segment (a multiple of the chunk size)
+    int per;        // chunks per segment
+    int seg_len;    // tokens per segment (per * chunk)
     int max_segs;   // bound on the number of segments
-    size_t off_table, off_seq, off_P, off_H, off_S, bytes;
+    bool packs;     // matrix-core path: one operand pack per chunk and head
+    size_t off_table, off_seq, off_P, off_H, off_S, off_pack, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t{255}; }
 
-Plan make_plan(int B, int T, int H, int dk, int dv, int N, int chunk, bool varlen) {
+Plan make_plan(int B, int T, int H, int dk, int dv, int N, int chunk, bool varlen, bool in_bf16) {
     Plan p{};
     const int64_t tokens = varlen ? T : static_cast<int64_t>(B) * T;
     const int64_t chunks = varlen ? (tokens + chunk - 1) / chunk + N
@@ -42,10 +46,14 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int N, int chunk, bool varle
     int64_t per = (chunks * H + kTargetUnits - 1) / kTargetUnits;
     if (per < 1) per = 1;
     if (per > 64) per = 64;
-    p.seg_len = static_cast<int>(per) * chunk;
+    p.per = static_cast<int>(per);
+    p.seg_len = p.per * chunk;
     p.max_segs = varlen ? static_cast<int>((tokens + p.seg_len - 1) / p.seg_len + N)
                         : B * ((T + p.seg_len - 1) / p.seg_len);
     if (p.max_segs < 1) p.max_segs = 1;
+    // the matrix-core kernels address a segment's tokens with 32-bit byte offsets
+    p.packs = f16_path_supported(in_bf16, dk, dv, chunk) &&
+              static_cast<int64_t>(p.seg_len) * H * dk * sizeof(float) < (int64_t{1} << 31);
     const size_t ms = static_cast<size_t>(p.max_segs);
     size_t o = 0;
     p.off_table = o; o = align256(o + ms * sizeof(int4));
@@ -53,6 +61,7 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int N, int chunk, bool varle
     p.off_P = o;     o = align256(o + ms * H * dk * dk * sizeof(float));
     p.off_H = o;     o = align256(o + ms * H * dk * dv * sizeof(float));
     p.off_S = o;     o = align256(o + ms * H * dk * dv * sizeof(float));
+    p.off_pack = o;  o = align256(o + (p.packs ? ms * p.per * H * pack_bytes() : 0));
     p.bytes = o;
     return p;
 }
@@ -180,13 +189,13 @@ combine_kernel(SegmentView sv, const float *h0, float *hT, int H, int DV) {
 
 }  // namespace
 
-size_t chunk_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int chunk, bool varlen) {
-    return make_plan(B, T, H, dk, dv, N, chunk, varlen).bytes;
+size_t chunk_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int chunk, bool varlen, bool in_bf16) {
+    return make_plan(B, T, H, dk, dv, N, chunk, varlen, in_bf16).bytes;
 }
 
 hipError_t launch_chunk(const ChunkLaunch &L) {
     const bool varlen = L.cu_seqlens != nullptr;
-    const Plan p = make_plan(L.B, L.T, L.H, L.dk, L.dv, L.N, L.chunk, varlen);
+    const Plan p = make_plan(L.B, L.T, L.H, L.dk, L.dv, L.N, L.chunk, varlen, L.in_bf16);
     char *ws = static_cast<char *>(L.workspace);
     SegmentView sv;
     sv.table = reinterpret_cast<const int4 *>(ws + p.off_table);
@@ -199,15 +208,19 @@ hipError_t launch_chunk(const ChunkLaunch &L) {
     hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(256), 0, L.stream, L.cu_seqlens, L.T, L.N,
                        p.seg_len, reinterpret_cast<int4 *>(ws + p.off_table),
                        reinterpret_cast<int32_t *>(ws + p.off_seq));
-    const bool fast = f16_pass_supported(L);
-    if (fast) launch_f16_pass<kLocal>(L, sv, p.max_segs);
-    else launch_fp32_pass<kLocal>(L, sv, p.max_segs);
+    void *packs = ws + p.off_pack;
+    if (p.packs) {
+        launch_prep(L, sv, p.max_segs, p.per, packs);
+        launch_scan<kLocal>(L, sv, p.max_segs, p.per, packs);
+    } else {
+        launch_fp32_pass<kLocal>(L, sv, p.max_segs);
+    }
     dim3 cgrid(L.dv / 16, L.H, L.N);
     if (L.dk == 128)
         hipLaunchKernelGGL(combine_kernel<128>, cgrid, dim3(256), 0, L.stream, sv, L.h0, L.hT, L.H, L.dv);
     else
         hipLaunchKernelGGL(combine_kernel<64>, cgrid, dim3(256), 0, L.stream, sv, L.h0, L.hT, L.H, L.dv);
-    if (fast) launch_f16_pass<kOut>(L, sv, p.max_segs);
+    if (p.packs) launch_scan<kOut>(L, sv, p.max_segs, p.per, packs);
     else launch_fp32_pass<kOut>(L, sv, p.max_segs);
     return hipGetLastError();
 }
