@@ -187,6 +187,96 @@ combine_kernel(SegmentView sv, const float *h0, float *hT, int H, int DV) {
     }
 }
 
+// Combine on fp32 matrix cores (dk = 128): per (sequence, head, 16-column
+// slice of dv), entering(s+1) = P_s entering(s) + H_s, serial over the
+// sequence's segments.  P_s is staged in LDS (row stride padded to 132
+// floats: conflict-free 16-byte reads) and read as the A operand of
+// v_mfma_f32_16x16x4f32; the slice of the state lives in LDS transposed
+// ([column][row]), from which every wave reads it whole as the B operand.
+// Wave w produces row tiles 2w and 2w + 1.  The contraction index of a
+// product runs over (tile t, lane group g, jj) as k = 16 t + 4 g + jj, which
+// is the accumulator layout, so results feed the next step without
+// reshuffling.  The next P and H are fetched into registers while the
+// current product runs.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCP = 132;  // padded row stride of P in LDS (floats)
+
+__global__ void __launch_bounds__(256, 1)
+combine_mfma_kernel(SegmentView sv, const float *h0, float *hT, int H, int DV) {
+    constexpr int DK = 128, PV4 = DK * DK / 4 / 256;  // float4 loads per thread for one P
+    __shared__ __attribute__((aligned(16))) float sP[DK * kCP];
+    __shared__ __attribute__((aligned(16))) float sS[16 * kCP];
+    const int slice = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, m = lane & 15;
+    const int j0 = 16 * slice;
+    const int first = sv.seq_seg[n], end = sv.seq_seg[n + 1];
+    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * DV;
+
+    // entering state of the first segment: thread (row tid / 2, 8 columns)
+    {
+        const int r = tid >> 1, c8 = 8 * (tid & 1);
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = h0 ? h0[sbase + static_cast<int64_t>(r) * DV + j0 + c8 + e] : 0.f;
+        if (first == end) {  // empty sequence: the final state is the initial state
+            if (hT)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) hT[sbase + static_cast<int64_t>(r) * DV + j0 + c8 + e] = x[e];
+            return;
+        }
+        float *sin = sv.sin + (static_cast<int64_t>(first) * H + h) * DK * DV;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            sin[static_cast<int64_t>(r) * DV + j0 + c8 + e] = x[e];
+            sS[(c8 + e) * kCP + r] = x[e];
+        }
+    }
+    float4 pn[PV4];
+    f32x4 hn[2];
+    auto fetch = [&](int seg) {
+        const float4 *src = reinterpret_cast<const float4 *>(sv.P + (static_cast<int64_t>(seg) * H + h) * DK * DK);
+#pragma unroll
+        for (int u = 0; u < PV4; ++u) pn[u] = src[tid + 256 * u];
+        const float *hs = sv.Hs + (static_cast<int64_t>(seg) * H + h) * DK * DV;
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                hn[ii][jj] = hs[static_cast<int64_t>(16 * (2 * wave + ii) + 4 * g + jj) * DV + j0 + m];
+    };
+    if (first + 1 < end) fetch(first);
+    for (int seg = first; seg + 1 < end; ++seg) {
+#pragma unroll
+        for (int u = 0; u < PV4; ++u) {
+            const int e = 4 * (tid + 256 * u), r = e / DK, c = e % DK;
+            *reinterpret_cast<float4 *>(&sP[r * kCP + c]) = pn[u];
+        }
+        f32x4 acc[2] = {hn[0], hn[1]};
+        __syncthreads();  // P_s and entering(s) in LDS
+        if (seg + 2 < end) fetch(seg + 1);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const f32x4 b = *reinterpret_cast<const f32x4 *>(&sS[m * kCP + 16 * t + 4 * g]);
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(&sP[(16 * (2 * wave + ii) + m) * kCP + 16 * t + 4 * g]);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) acc[ii] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[jj], b[jj], acc[ii], 0, 0, 0);
+            }
+        }
+        __syncthreads();  // all reads of sP and sS done
+        float *sin = sv.sin + (static_cast<int64_t>(seg + 1) * H + h) * DK * DV;
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            const int r0 = 16 * (2 * wave + ii) + 4 * g;
+            *reinterpret_cast<f32x4 *>(&sS[m * kCP + r0]) = acc[ii];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) sin[static_cast<int64_t>(r0 + jj) * DV + j0 + m] = acc[ii][jj];
+        }
+    }
+}
+
 }  // namespace
 
 size_t chunk_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int chunk, bool varlen, bool in_bf16) {
@@ -217,7 +307,7 @@ hipError_t launch_chunk(const ChunkLaunch &L) {
     }
     dim3 cgrid(L.dv / 16, L.H, L.N);
     if (L.dk == 128)
-        hipLaunchKernelGGL(combine_kernel<128>, cgrid, dim3(256), 0, L.stream, sv, L.h0, L.hT, L.H, L.dv);
+        hipLaunchKernelGGL(combine_mfma_kernel, cgrid, dim3(256), 0, L.stream, sv, L.h0, L.hT, L.H, L.dv);
     else
         hipLaunchKernelGGL(combine_kernel<64>, cgrid, dim3(256), 0, L.stream, sv, L.h0, L.hT, L.H, L.dv);
     if (p.packs) launch_scan<kOut>(L, sv, p.max_segs, p.per, packs);
