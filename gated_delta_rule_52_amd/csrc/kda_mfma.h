@@ -132,9 +132,10 @@ __device__ __forceinline__ void st128(rsrc_t r, u4 v, uint32_t off, int soff = 0
 
 // ---- per-chunk operand pack (one per chunk and head, written by the prep
 // kernel, streamed by the scan kernels).  Every fp16 matrix carries a
-// power-of-two scale: stored = true value * 2^-e.  The 16-byte units of a
-// row are XOR-swizzled by the row's low three bits, so the pack can be
-// copied into LDS as a straight line and read there without bank conflicts.
+// power-of-two scale: stored = true value * 2^-e.  The pack is copied into
+// LDS as a straight line; the 16-byte units of the matrices are XOR-swizzled
+// by row so that the scan's 8-byte operand reads (16x16x16 MFMA A operands:
+// lane = 16 g + n reads row n, columns 4g .. 4g + 3) hit distinct banks.
 //
 //   [0, 512)        gamma: exp(G_last) per channel, fp32
 //   [512, 1024)     header: int exponents e_w, e_q, e_k, e_u, e_a
@@ -142,8 +143,8 @@ __device__ __forceinline__ void st128(rsrc_t r, u4 v, uint32_t off, int soff = 0
 //   KT  [128][64]   (e^{G_last - G} k)^T      A operand of the state update
 //   Q   [64][128]   scale e^G q               A operand of Q S
 //   A   [10][16][16] blocks (a, b), b <= a, of the decayed scale q k^T
-//   U   [8][4][64][4] T beta v in accumulator order: [16-column tile][row
-//                   block][lane][row within lane]
+//   U   T beta v in accumulator order: [16-column tile][row-block pair]
+//                   [lane][row block a, a + 1][row within lane]
 constexpr int kPkGamma = 0;
 constexpr int kPkHdr = 512;
 constexpr int kPkW = 1024;
@@ -157,10 +158,16 @@ constexpr int kPkOut = kPkU;     // bytes the output pass copies to LDS
 static_assert(kPkLocal % 1024 == 0 && kPkOut % 1024 == 0, "whole 1 KiB wave copies");
 enum { kHdrW = 0, kHdrQ = 1, kHdrK = 2, kHdrU = 3, kHdrA = 4 };
 
-// byte offset of the 16-byte unit u of row r in a swizzled matrix whose rows
-// are `row_bytes` long
-__device__ __forceinline__ int swz(int r, int u, int row_bytes) {
-    return r * row_bytes + ((u ^ (r & 7)) << 4);
+// byte offset of 16-byte unit u of row r: W and Q ([64][128] fp16, 16 units a row)
+__device__ __forceinline__ int swz_w(int r, int u) { return r * 256 + ((u ^ (r & 15)) << 4); }
+// ... KT ([128][64] fp16, 8 units a row; rows 2i and 2i + 1 share a pattern
+// but sit 128 bytes apart)
+__device__ __forceinline__ int swz_kt(int r, int u) { return r * 128 + ((u ^ ((r >> 1) & 7)) << 4); }
+// byte offset of 8-byte unit v (columns 4v .. 4v + 3) of row r of A block p
+__device__ __forceinline__ int a_off(int p, int r, int v) { return p * 512 + r * 32 + ((v ^ ((r >> 2) & 2)) << 3); }
+// byte offset of the 8 bytes of U (tile ct, row block a) that lane `lane` holds
+__device__ __forceinline__ int u_off(int ct, int a, int lane) {
+    return ((ct * 2 + (a >> 1)) * 64 + lane) * 16 + (a & 1) * 8;
 }
 
 }  // namespace mc

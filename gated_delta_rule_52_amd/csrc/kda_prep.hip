@@ -38,7 +38,6 @@ constexpr int HC = DK / 2;  // channels per half of dk
 constexpr int HP = HC + 8;  // row stride (halves) of the half-dk Gram operand tiles
 constexpr int KP = DK + 8;  // row stride (halves) of [row][dk] tiles
 constexpr int GP = DK + 4;  // row stride (floats) of [row][dk] fp32 tiles
-constexpr int RP = C + 8;   // row stride (halves) of [dk][row] tiles
 constexpr int BP = 16 + 8;  // row stride of 16x16 half blocks
 constexpr float kMaxChunkDecay = 80.0f;
 constexpr int NJOB = 20;    // Gram tile jobs: 10 A_kk block pairs, then 10 A_qk
@@ -55,8 +54,6 @@ struct alignas(16) PrepSmem {
         } g;
         struct {  // fp16 operands
             _Float16 ek[C * KP];   // k e^G 2^-ek; later W, swizzled [64][128]
-            _Float16 qs[C * KP];   // scale q e^G 2^-eq      [row][dk]
-            _Float16 kd[DK * RP];  // k e^{G_L - G} 2^-ek    [dk][row]
         } s;
         float gx[C * GP];          // G, for the exact path
     } op;
@@ -326,7 +323,16 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     }
     __syncthreads();  // (4) Gram results in LDS; operand area free
 
-    // ============ a3: diagonal blocks of T; fp16 operands to LDS ============
+    // ============ a3: diagonal blocks of T; e^G k to LDS, Q and KT to the pack ============
+    // the solve's v values, in accumulator layout, fetched ahead
+    uint32_t vpre[2][4][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                vpre[t][a][jj] = ld16(rs_v, 2 * ((16 * a + 4 * g4 + jj) * tok_stride + 16 * (2 * wave + t) + n16));
     float tcol[16];
     if (wave == 0) {  // lane 16a + j owns column j of T_aa = (I + A_aa)^{-1}
         const int a = g4, j = n16;
@@ -349,17 +355,18 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
+        // Q: the channel pair (hh HC + 2cq, +1) of row r is 4 bytes of 16-byte unit hh*8 + cq/4
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const int r = 8 * rq8 + m;
             *reinterpret_cast<uint32_t *>(&sm.op.s.ek[r * KP + hh * HC + 2 * cq]) = ekp[hh][m];
-            *reinterpret_cast<uint32_t *>(&sm.op.s.qs[r * KP + hh * HC + 2 * cq]) = qsp[hh][m];
+            st32(rs_p, qsp[hh][m], kPkQ + swz_w(r, hh * 8 + (cq >> 2)) + 4 * (cq & 3));
         }
+        // KT: eight consecutive rows of one channel are one 16-byte unit
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {  // eight consecutive rows of one channel: one 16-byte store
-            const i4 w = {static_cast<int>(kdp[hh][e][0]), static_cast<int>(kdp[hh][e][1]),
-                          static_cast<int>(kdp[hh][e][2]), static_cast<int>(kdp[hh][e][3])};
-            *reinterpret_cast<i4 *>(&sm.op.s.kd[(hh * HC + 2 * cq + e) * RP + 8 * rq8]) = w;
+        for (int e = 0; e < 2; ++e) {
+            const u4 w = {kdp[hh][e][0], kdp[hh][e][1], kdp[hh][e][2], kdp[hh][e][3]};
+            st128(rs_p, w, kPkKT + swz_kt(hh * HC + 2 * cq + e, rq8));
         }
     }
     __syncthreads();  // (5)
@@ -391,7 +398,7 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 for (int jj = 0; jj < 4; ++jj) {
                     const int rr = 16 * a + 4 * g4 + jj;
                     const float x = kind == 0 ? static_cast<float>(sm.op.s.ek[rr * KP + col])
-                                              : lo_f(ld16(rs_v, 2 * (rr * tok_stride + col))) * svs;
+                                              : lo_f(vpre[t][a][jj]) * svs;
                     xp[jj] = sm.beta[rr] * x;
                 }
                 f4 accs = zero4();
@@ -439,12 +446,12 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int rr = 16 * a + 4 * g4 + jj;
-                    *reinterpret_cast<_Float16 *>(wst + swz(rr, col >> 3, 2 * DK) + 2 * (col & 7)) =
+                    *reinterpret_cast<_Float16 *>(wst + swz_w(rr, col >> 3) + 2 * (col & 7)) =
                         static_cast<_Float16>(Wr[t][a][jj] * swv);
                 }
                 // U straight to the pack, in accumulator order
                 const h4 uh = to_h4(Ur[t][a], suv);
-                st64(rs_p, __builtin_bit_cast(u2, uh), kPkU + ((ct * 4 + a) * kWave + lane) * 8);
+                st64(rs_p, __builtin_bit_cast(u2, uh), kPkU + u_off(ct, a, lane));
             }
         }
     }
@@ -452,24 +459,16 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     // ---- the rest of the pack, 16-byte units, consecutive threads on consecutive units
     {
         const char *wst = reinterpret_cast<const char *>(sm.op.s.ek);
-        const char *qst = reinterpret_cast<const char *>(sm.op.s.qs);
-        const char *kst = reinterpret_cast<const char *>(sm.op.s.kd);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int u = tid + NT * i;  // 0 .. 1023
             st128(rs_p, *reinterpret_cast<const u4 *>(wst + 16 * u), kPkW + 16 * u);
-            {   // KT: row r = channel (8 units per row)
-                const int r = u >> 3, p = u & 7, cl = p ^ (r & 7);
-                st128(rs_p, *reinterpret_cast<const u4 *>(kst + r * RP * 2 + 16 * cl), kPkKT + 16 * u);
-            }
-            {   // Q: row r = chunk row (16 units per row)
-                const int r = u >> 4, p = u & 15, cl = p ^ (r & 7);
-                st128(rs_p, *reinterpret_cast<const u4 *>(qst + r * KP * 2 + 16 * cl), kPkQ + 16 * u);
-            }
         }
         for (int u = tid; u < 10 * 16 * 2; u += NT) {  // A_qk blocks, rows of 32 bytes
-            const int p = u >> 5, row = (u >> 1) & 15, half = u & 1;
-            st128(rs_p, *reinterpret_cast<const u4 *>(&sm.aqk[p][row * BP + 8 * half]), kPkA + 16 * u);
+            // 16-byte half `half` of a stored row holds the row's logical half
+            // half ^ (row >= 8) (the 8-byte units of a_off, pairwise)
+            const int p = u >> 5, row = (u >> 1) & 15, half = u & 1, lh = half ^ (row >> 3);
+            st128(rs_p, *reinterpret_cast<const u4 *>(&sm.aqk[p][row * BP + 8 * lh]), kPkA + 16 * u);
         }
         if (tid < DK / 4)
             st128(rs_p, *reinterpret_cast<const u4 *>(&sm.gam[4 * tid]), kPkGamma + 16 * tid);

@@ -8,15 +8,23 @@
 //   V_new = U - X                       (U = T beta v)
 //   o     = (scale e^G q) S + A_qk V_new                     (a6, output pass)
 //   S    <- gamma * S + (e^{G_last - G} k)^T V_new           (a5)
-// The pack is copied HBM -> LDS by global_load_lds (no registers), U goes
-// straight to registers in accumulator order.  Each wave owns 32 state
-// columns; its state and V_new are rounded to fp16 for the products with a
-// power-of-two scale of its own (from the wave's maxima), so the waves never
-// exchange anything but the pack in LDS.
 //
-// Modes: kLocal (grid 2 x segments: an H workgroup, zero start, and a P
-// workgroup, identity start with v = 0, so that leaving = P entering + H)
-// and kOut (replay from the entering state, write o and the final state).
+// Streaming: the pack is copied HBM -> LDS by global_load_lds (no
+// registers) into one of two buffers while the other one is in use, so the
+// copy of chunk j + 1 overlaps the products of chunk j and a chunk costs one
+// barrier; U goes straight to registers in accumulator order, also one chunk
+// ahead.  Each wave owns 32 state columns (two 16-column tiles, processed
+// together so every A operand fragment is read from LDS once per wave).  All
+// products are 16x16x16, whose B operand layout is the accumulator layout:
+// the state and V_new feed them without any cross-lane movement.  They are
+// rounded to fp16 with power-of-two scales of the wave's own (from its
+// maxima), so waves share nothing but the pack.  o is staged in LDS per wave
+// and written with 16-byte stores.
+//
+// Modes: kLocal, 8 waves: waves 0-3 build H (the dv columns, zero start) and
+// waves 4-7 build P (the dk x dk transition: identity start, v = 0), so that
+// leaving = P entering + H; kOut, 4 waves: replay from the entering state,
+// write o and, for a sequence's last segment, the final state.
 #include "kda_internal.h"
 #include "kda_mfma.h"
 
@@ -24,23 +32,32 @@ namespace kda {
 namespace mc {
 namespace {
 
-constexpr int NW = 4, NT = NW * kWave;
-constexpr int NCT = 2;  // 16-column state tiles per wave
-
 typedef const void __attribute__((address_space(1))) *gptr_t;
 typedef void __attribute__((address_space(3))) *lptr_t;
 
+template <int MODE>
+struct ScanCfg {
+    static constexpr int NW = MODE == kOut ? 4 : 8;
+    static constexpr int NT = NW * kWave;
+    static constexpr int kBytes = MODE == kOut ? kPkOut : kPkLocal;  // pack bytes staged in LDS
+};
+
 template <int MODE, bool OutBf16>
-__global__ void __launch_bounds__(NT, 2)
+__global__ void __launch_bounds__(ScanCfg<MODE>::NT, 1)
 chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__restrict__ o_, SegmentView sv,
                   int H) {
     constexpr bool kOutPass = MODE == kOut;
-    constexpr int kBytes = kOutPass ? kPkOut : kPkLocal;
-    __shared__ __attribute__((aligned(16))) char lds[kBytes];
+    constexpr int NW = ScanCfg<MODE>::NW, kBytes = ScanCfg<MODE>::kBytes;
+    // two pack buffers as separate objects, so that the compiler can tell a
+    // copy into one from reads of the other and does not wait for the copy
+    __shared__ __attribute__((aligned(16))) char lds0[kBytes];
+    __shared__ __attribute__((aligned(16))) char lds1[kBytes];
+    // o of a chunk, per wave: 64 rows x 32 columns, rows padded by 16 bytes
+    // (the four row groups of an accumulator tile land on different banks)
+    constexpr int kStageRow = 32 * (OutBf16 ? 2 : 4) + 16;
+    __shared__ __attribute__((aligned(16))) char ostage[kOutPass ? NW : 1][kOutPass ? 64 * kStageRow : 16];
 
-    const int seg = kOutPass ? blockIdx.x : (blockIdx.x >> 1);
-    const bool pcols = !kOutPass && (blockIdx.x & 1);
-    const int h = blockIdx.y;
+    const int seg = blockIdx.x, h = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
@@ -51,19 +68,21 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     if (!kOutPass && last) return;
     const int64_t t0 = sd.y, t1 = sd.z;
     const int nch = static_cast<int>((t1 - t0 + C - 1) / C);
-    const int col0 = 32 * wave;  // this wave's state columns
+    const bool pcols = !kOutPass && wave >= 4;  // this wave builds P
+    const int ctile0 = 2 * (wave & 3);           // this wave's first 16-column tile
+    const int col0 = 16 * ctile0;
 
     // a state tile element (16 rt + 4 g4 + jj, col0 + 16 ct + n16) of a
     // row-major 128 x 128 fp32 matrix: one per-lane byte offset plus a constant
     const uint32_t st_lane = 4 * (4 * g4 * 128 + col0 + n16);
     auto st_off = [](int rt, int ct, int jj) { return 4 * ((16 * rt + jj) * 128 + 16 * ct); };
-    f4 acc[8][NCT];
+    f4 acc[8][2];
     if (kOutPass) {
         const rsrc_t rs = make_rsrc(sv.sin + (static_cast<int64_t>(seg) * H + h) * DK * DV, 4 * DK * DV);
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
                     acc[rt][ct][jj] = __uint_as_float(ld32(rs, st_lane, st_off(rt, ct, jj)));
@@ -71,7 +90,7 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
                     acc[rt][ct][jj] = (pcols && 16 * rt + 4 * g4 + jj == col0 + 16 * ct + n16) ? 1.f : 0.f;
@@ -80,7 +99,7 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
+        for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) smax = fmaxf(smax, fabsf(acc[rt][ct][jj]));
     smax = wave_max(smax);
@@ -93,122 +112,169 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     constexpr int ob = OutBf16 ? 2 : 4;
     const rsrc_t rs_o = make_rsrc(static_cast<char *>(o_) + seg_base * ob, kOutPass ? ob * seg_elems : 0);
 
-    for (int j = 0; j < nch; ++j) {
+    // chunk j's pack -> dst and its U -> registers
+    auto fetch = [&](int j, char *dst, u4 (&ur)[2][2]) {
         const char *pack = packs + (static_cast<int64_t>(seg * per + j) * H + h) * kPkBytes;
-        // pack -> LDS, 1 KiB per wave instruction
         for (int u = wave; u < kBytes / 1024; u += NW)
-            __builtin_amdgcn_global_load_lds((gptr_t)(pack + 1024 * u + 16 * lane), (lptr_t)(lds + 1024 * u), 16, 0, 0);
-        // U, accumulator order, for this wave's two column tiles
-        u2 ur[NCT][4] = {};
+            __builtin_amdgcn_global_load_lds((gptr_t)(pack + 1024 * u + 16 * lane), (lptr_t)(dst + 1024 * u), 16, 0, 0);
         if (!pcols) {
             const rsrc_t rs_p = make_rsrc(pack, kPkBytes);
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-                for (int a = 0; a < 4; ++a)
-                    ur[ct][a] = ld64(rs_p, kPkU + 8 * lane, (((2 * wave + ct) * 4 + a) * kWave) * 8);
+                for (int pr = 0; pr < 2; ++pr)
+                    ur[ct][pr] = __builtin_amdgcn_raw_buffer_load_b128(rs_p, kPkU + 16 * lane,
+                                                                       u_off(ctile0 + ct, 2 * pr, 0), 0);
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // (1) pack in LDS
+    };
+    u4 ur_cur[2][2] = {}, ur_nxt[2][2] = {};
+    fetch(0, lds0, ur_nxt);
 
-        const int *hdr = reinterpret_cast<const int *>(lds + kPkHdr);
+    // one chunk: its pack is in L, the next one's goes to Lnext
+    auto step = [&](int j, const char *L, char *Lnext) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // chunk j in L; every wave is done with chunk j - 1
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) ur_cur[ct][pr] = ur_nxt[ct][pr];
+        if (j + 1 < nch) fetch(j + 1, Lnext, ur_nxt);
+
+        const int *hdr = reinterpret_cast<const int *>(L + kPkHdr);
         const int ew = hdr[kHdrW], ek = hdr[kHdrK];
-        const float *gam = reinterpret_cast<const float *>(lds + kPkGamma);
+        const float *gam = reinterpret_cast<const float *>(L + kPkGamma);
         const int es = exp_of(smax);  // this wave's state, stored below 1
         const float ss = pow2(-es), unx = pow2(ew + es);
-        float smax_new = 0.f;
+        // lane (g4, n16) reads row n16, columns 4 g4 .. 4 g4 + 3 of a 16x16 A block:
+        // 8 bytes at unit 2 blk + g4 / 2, half g4 % 2
+        const int hsel = 8 * (g4 & 1), usel = g4 >> 1;
+
+        // The accumulator layout of a 16-row state tile is the B operand
+        // layout of a 16x16x16 product: the state feeds products as is.
+        h4 sh[2][8];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const int col = col0 + 16 * ct + n16;
-            h8 sb[4];
+        for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) sb[s] = acc_to_b32(acc[2 * s][ct], acc[2 * s + 1][ct], ss, lane);
-            // X = W S, Y = Q S
-            f4 X[4], Y[4];
+            for (int rt = 0; rt < 8; ++rt) sh[ct][rt] = to_h4(acc[rt][ct], ss);
+        // X = W S, Y = Q S
+        f4 X[2][4], Y[2][4];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                X[a] = zero4();
-                Y[a] = zero4();
+                X[ct][a] = zero4();
+                Y[ct][a] = zero4();
             }
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+        for (int rt = 0; rt < 8; ++rt) {
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const h8 wa = *reinterpret_cast<const h8 *>(lds + kPkW + swz(16 * a + n16, 4 * s + g4, 2 * DK));
-                    X[a] = mma32(wa, sb[s], X[a]);
-                    if (kOutPass) {
-                        const h8 qa = *reinterpret_cast<const h8 *>(lds + kPkQ + swz(16 * a + n16, 4 * s + g4, 2 * DK));
-                        Y[a] = mma32(qa, sb[s], Y[a]);
-                    }
+            for (int a = 0; a < 4; ++a) {
+                const h4 wa = *reinterpret_cast<const h4 *>(L + kPkW + swz_w(16 * a + n16, 2 * rt + usel) + hsel);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) X[ct][a] = mma16(wa, sh[ct][rt], X[ct][a]);
+                if (kOutPass) {
+                    const h4 qa = *reinterpret_cast<const h4 *>(L + kPkQ + swz_w(16 * a + n16, 2 * rt + usel) + hsel);
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) Y[ct][a] = mma16(qa, sh[ct][rt], Y[ct][a]);
                 }
             }
-            // V_new = U - X (fp32), then its own fp16 scale
-            f4 Vn[4];
-            float mv = 0.f;
-            {
-                const float unu = pcols ? 0.f : pow2(hdr[kHdrU]);
+        }
+        // V_new = U - X (fp32), then an fp16 scale of its own per tile
+        f4 Vn[2][4];
+        h4 Vh[2][4];
+        int evn[2];
+        {
+            const float unu = pow2(hdr[kHdrU]);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                float mv = 0.f;
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
-                    const h4 uh = __builtin_bit_cast(h4, ur[ct][a]);
+                    const u4 w = ur_cur[ct][a >> 1];
+                    const h4 uh = __builtin_bit_cast(h4, (a & 1) ? u2{w[2], w[3]} : u2{w[0], w[1]});
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const float uval = pcols ? 0.f : static_cast<float>(uh[jj]) * unu;
-                        Vn[a][jj] = uval - X[a][jj] * unx;
-                        mv = fmaxf(mv, fabsf(Vn[a][jj]));
+                        Vn[ct][a][jj] = uval - X[ct][a][jj] * unx;
+                        mv = fmaxf(mv, fabsf(Vn[ct][a][jj]));
                     }
                 }
-            }
-            const int evn = exp_of(wave_max(mv));
-            const float svn = pow2(-evn);
-            // a6: o = Q S + A_qk V_new
-            if (kOutPass) {
-                const float unq = pow2(hdr[kHdrQ] + es), una = pow2(hdr[kHdrA] + evn);
-                h4 Vh[4];
+                evn[ct] = exp_of(wave_max(mv));
+                const float svn = pow2(-evn[ct]);
 #pragma unroll
-                for (int a = 0; a < 4; ++a) Vh[a] = to_h4(Vn[a], svn);
+                for (int a = 0; a < 4; ++a) Vh[ct][a] = to_h4(Vn[ct][a], svn);
+            }
+        }
+        // a6: o = Q S + A_qk V_new, staged per wave in LDS, then 16-byte stores
+        if (kOutPass) {
+            const float unq = pow2(hdr[kHdrQ] + es);
+            char *st = ostage[wave];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const float una = pow2(hdr[kHdrA] + evn[ct]);
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
                     f4 oi = zero4();
 #pragma unroll
                     for (int b = 0; b <= a; ++b) {
-                        const h4 aq = *reinterpret_cast<const h4 *>(lds + kPkA + (a * (a + 1) / 2 + b) * 512 +
-                                                                    n16 * 32 + g4 * 8);
-                        oi = mma16(aq, Vh[b], oi);
+                        const h4 aq = *reinterpret_cast<const h4 *>(L + kPkA + a_off(a * (a + 1) / 2 + b, n16, g4));
+                        oi = mma16(aq, Vh[ct][b], oi);
                     }
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
-                        const int rr = 16 * a + 4 * g4 + jj;
-                        const float val = Y[a][jj] * unq + oi[jj] * una;
-                        const uint32_t e = (static_cast<uint32_t>(C * j + rr)) * tok_stride + col;
+                        const int rr = 16 * a + 4 * g4 + jj, cc = 16 * ct + n16;
+                        const float val = Y[ct][a][jj] * unq + oi[jj] * una;
                         if constexpr (OutBf16)
-                            __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(f32_to_bf16(val)), rs_o,
-                                                                  static_cast<int>(2 * e), 0, 0);
+                            *reinterpret_cast<__bf16 *>(st + rr * kStageRow + 2 * cc) = static_cast<__bf16>(val);
                         else
-                            st32(rs_o, __float_as_uint(val), 4 * e);
+                            *reinterpret_cast<float *>(st + rr * kStageRow + 4 * cc) = val;
                     }
                 }
             }
-            // a5: S <- gamma S + KT V_new
-            const h8 vb0 = acc_to_b32(Vn[0], Vn[1], svn, lane), vb1 = acc_to_b32(Vn[2], Vn[3], svn, lane);
-            const float down = pow2(-(ek + evn)), up = pow2(ek + evn);
+            // 64 rows x 32 columns of this wave: 16-byte units, rows past the
+            // segment end dropped by the buffer range
+            constexpr int kUnitsPerRow = 32 * ob / 16;
 #pragma unroll
-            for (int rt = 0; rt < 8; ++rt) {
-                const f4 gm = *reinterpret_cast<const f4 *>(gam + 16 * rt + 4 * g4);
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) acc[rt][ct][jj] *= gm[jj] * down;
-                const h8 k0 = *reinterpret_cast<const h8 *>(lds + kPkKT + swz(16 * rt + n16, g4, 2 * C));
-                const h8 k1 = *reinterpret_cast<const h8 *>(lds + kPkKT + swz(16 * rt + n16, 4 + g4, 2 * C));
-                acc[rt][ct] = mma32(k0, vb0, acc[rt][ct]);
-                acc[rt][ct] = mma32(k1, vb1, acc[rt][ct]);
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    acc[rt][ct][jj] *= up;
-                    smax_new = fmaxf(smax_new, fabsf(acc[rt][ct][jj]));
-                }
+            for (int k = 0; k < 64 * kUnitsPerRow / kWave; ++k) {
+                const int i = lane + kWave * k, rr = i / kUnitsPerRow, un = i % kUnitsPerRow;
+                const u4 w = *reinterpret_cast<const u4 *>(st + rr * kStageRow + 16 * un);
+                st128(rs_o, w, ob * ((static_cast<uint32_t>(C * j + rr)) * tok_stride + col0) + 16 * un);
             }
         }
+        // a5: S <- gamma S + KT V_new
+        float down[2], up[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            down[ct] = pow2(-(ek + evn[ct]));
+            up[ct] = pow2(ek + evn[ct]);
+        }
+        float smax_new = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) {
+            const f4 gm = *reinterpret_cast<const f4 *>(gam + 16 * rt + 4 * g4);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) acc[rt][ct][jj] *= gm[jj] * down[ct];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const h4 kt = *reinterpret_cast<const h4 *>(L + kPkKT + swz_kt(16 * rt + n16, 2 * a + usel) + hsel);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = mma16(kt, Vh[ct][a], acc[rt][ct]);
+            }
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    acc[rt][ct][jj] *= up[ct];
+                    smax_new = fmaxf(smax_new, fabsf(acc[rt][ct][jj]));
+                }
+        }
         smax = wave_max(smax_new);
-        __syncthreads();  // (2) LDS is refilled by the next chunk
+    };
+    for (int j = 0; j < nch; j += 2) {
+        step(j, lds0, lds1);
+        if (j + 1 < nch) step(j + 1, lds1, lds0);
     }
 
     // ---- leaving state (DK = DV: H and P are both 128 x 128)
@@ -223,7 +289,7 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
                     st32(rs, __float_as_uint(acc[rt][ct][jj]), st_lane, st_off(rt, ct, jj));
@@ -235,7 +301,7 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
 
 template <int MODE>
 void launch_scan(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, const void *packs) {
-    dim3 grid(MODE == kOut ? max_segs : 2 * max_segs, L.H), block(mc::NT);
+    dim3 grid(max_segs, L.H), block(mc::ScanCfg<MODE>::NT);
     const char *pk = static_cast<const char *>(packs);
     if (L.out_bf16)
         hipLaunchKernelGGL((mc::chunk_scan_kernel<MODE, true>), grid, block, 0, L.stream, pk, per, L.hT, L.o, sv, L.H);
