@@ -69,6 +69,8 @@ struct SegmentView {
     float *P;               // [max_segs, H, dk, dk]
     float *Hs;              // [max_segs, H, dk, dv]
     float *sin;             // [max_segs, H, dk, dv] entering states
+    int *xlist;             // chunks (pack numbers) the matrix-core prep hands to its exact path
+    int *xcount;            // their count (zeroed by the segment-table kernel)
     __device__ __forceinline__ int count() const { return seq_seg[N]; }
 };
 

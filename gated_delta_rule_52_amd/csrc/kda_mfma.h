@@ -42,19 +42,36 @@ __device__ __forceinline__ int exp_of(float m) {
 
 __device__ __forceinline__ uint32_t hbits(_Float16 x) { return __builtin_bit_cast(uint16_t, x); }
 __device__ __forceinline__ uint32_t bbits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
+typedef float fl2 __attribute__((ext_vector_type(2)));
+typedef _Float16 hf2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+// two floats -> packed fp16 pair (round to nearest even), one instruction
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-    return hbits(static_cast<_Float16>(a)) | (hbits(static_cast<_Float16>(b)) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((fl2{a, b}), hf2));
 }
 __device__ __forceinline__ h4 to_h4(f4 v, float s) {
-    return h4{static_cast<_Float16>(v[0] * s), static_cast<_Float16>(v[1] * s),
-              static_cast<_Float16>(v[2] * s), static_cast<_Float16>(v[3] * s)};
+    const hf2 lo = __builtin_convertvector((fl2{v[0] * s, v[1] * s}), hf2);
+    const hf2 hi = __builtin_convertvector((fl2{v[2] * s, v[3] * s}), hf2);
+    return h4{lo[0], lo[1], hi[0], hi[1]};
 }
 // bf16 high and low parts of two values, each pair packed in one word
+// (hi = round(x), lo = round(x - hi): ~16 significant bits together)
 __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
-    const __bf16 ha = static_cast<__bf16>(a), hb = static_cast<__bf16>(b);
-    hi = bbits(ha) | (bbits(hb) << 16);
-    lo = bbits(static_cast<__bf16>(a - static_cast<float>(ha))) |
-         (bbits(static_cast<__bf16>(b - static_cast<float>(hb))) << 16);
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((fl2{a, b}), bf2));
+    const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xffff0000u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((fl2{a - ha, b - hb}), bf2));
+}
+// running maximum of |x| over packed bf16 pairs, as 16-bit integers (the
+// order of non-negative floats is the order of their bit patterns)
+__device__ __forceinline__ uint32_t absmax2(uint32_t acc, uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, acc),
+                                                                  __builtin_bit_cast(us2, w & 0x7fff7fffu)));
+}
+// the larger of the two halves of absmax2's result, as a float
+__device__ __forceinline__ float absmax2_value(uint32_t acc) {
+    const uint32_t m = (acc & 0xffffu) > (acc >> 16) ? (acc & 0xffffu) : (acc >> 16);
+    return __uint_as_float(m << 16);
 }
 // the two bf16 values packed in a word, widened
 __device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }

@@ -79,17 +79,19 @@ __device__ __forceinline__ int offdiag_index(int a, int b) {  // b < a
     return a * (a - 1) / 2 + b;
 }
 
-// Grid: (segments x chunks per segment, heads).  Workgroup (seg * per + j, h)
-// prepares chunk j of segment seg for head h into pack number
-// (seg * per + j) * H + h.
-__global__ void __launch_bounds__(NT, 2)
-chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                  const uint16_t *__restrict__ v, const float *__restrict__ g,
-                  const uint16_t *__restrict__ beta, SegmentView sv, int per, int H, float scale,
-                  char *__restrict__ packs) {
-    __shared__ PrepSmem sm;
-    const int seg = blockIdx.x / per, jc = blockIdx.x - seg * per;
-    const int h = blockIdx.y;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// One chunk: chunk bx % per of segment bx / per, head h, into pack number
+// bx * H + h.  EXACT = false is the matrix-core path; a chunk whose decay
+// exceeds exp(-kMaxChunkDecay) in some channel is not written there but
+// appended to the exact list, and EXACT = true redoes it with the pair-by-pair
+// Gram blocks.  Returns early (whole workgroup) for chunks past the segment end.
+template <bool EXACT>
+__device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const uint16_t *__restrict__ q,
+                                           const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+                                           const float *__restrict__ g, const uint16_t *__restrict__ beta,
+                                           const SegmentView &sv, int per, int H, float scale, char *packs) {
+    const int seg = bx / per, jc = bx - seg * per;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
@@ -110,7 +112,7 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     const rsrc_t rs_q = make_rsrc(q + base, 2 * elems);
     const rsrc_t rs_v = make_rsrc(v + base, 2 * elems);
     const rsrc_t rs_g = make_rsrc(g + base, 4 * elems);
-    char *pack = packs + (static_cast<int64_t>(blockIdx.x) * H + h) * kPkBytes;
+    char *pack = packs + (static_cast<int64_t>(bx) * H + h) * kPkBytes;
     const rsrc_t rs_p = make_rsrc(pack, kPkBytes);
     const uint32_t key_lane = 8 * rq8 * tok_stride + 2 * cq;
 
@@ -121,7 +123,7 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     float G[2][8][2];  // [half][row][channel]
     uint32_t rk[2][8], rq[2][8];
     {
-        float mk = 0.f, mq = 0.f, mv = 0.f;
+        uint32_t mk2 = 0u, mq2 = 0u, mv2 = 0u;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             float r0 = 0.f, r1 = 0.f;
@@ -136,17 +138,17 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 r1 += __uint_as_float(gg[1]);
                 G[hh][m][0] = r0;
                 G[hh][m][1] = r1;
-                mk = fmaxf(mk, fmaxf(fabsf(lo_f(rk[hh][m])), fabsf(hi_f(rk[hh][m]))));
-                mq = fmaxf(mq, fmaxf(fabsf(lo_f(rq[hh][m])), fabsf(hi_f(rq[hh][m]))));
-                mv = fmaxf(mv, fmaxf(fabsf(lo_f(vv)), fabsf(hi_f(vv))));
+                mk2 = absmax2(mk2, rk[hh][m]);
+                mq2 = absmax2(mq2, rq[hh][m]);
+                mv2 = absmax2(mv2, vv);
             }
             sm.part[rq8][hh * HC + 2 * cq] = r0;
             sm.part[rq8][hh * HC + 2 * cq + 1] = r1;
         }
         if (tid < C) sm.beta[tid] = tid < L ? bf16_to_f32(beta[(c0 + tid) * H + h]) : 0.f;
-        mk = wave_max(mk);
-        mq = wave_max(mq);
-        mv = wave_max(mv);
+        const float mk = wave_max(absmax2_value(mk2));
+        const float mq = wave_max(absmax2_value(mq2));
+        const float mv = wave_max(absmax2_value(mv2));
         if (lane == 0) {
             atomicMax(&sm.imax[0], __float_as_int(mk));
             atomicMax(&sm.imax[1], __float_as_int(mq * fabsf(scale)));
@@ -180,7 +182,12 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     const int ev = exp_of(__int_as_float(sm.imax[2])) - 5;  // U's solve runs below 2^5
     const float sk = pow2(-ek), sq = pow2(-eq) * scale, svs = pow2(-ev);
     __syncthreads();  // (2) flag settled
-    const bool exact_path = sm.imax[5] != 0;
+    if constexpr (!EXACT) {
+        if (sm.imax[5] != 0) {  // beyond the factored form's range: exact kernel
+            if (tid == 0) sv.xlist[atomicAdd(sv.xcount, 1)] = bx * H + h;
+            return;
+        }
+    }
 
     // ============ a2: Gram tiles, one half of dk at a time ============
     f4 tacc[JPW];
@@ -189,33 +196,40 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     uint32_t ekp[2][8], qsp[2][8], kdp[2][2][4];  // fp16 operand pairs
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-        float em[2], emi[2];  // e^{m}, e^{-m}, m = G_L / 2
+        // per channel: m log2(e) with m = G_L / 2, and e^m times the fp16 scales
+        float mlg[2], em_sk[2], em_sq[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            em[e] = __expf(0.5f * GL[hh][e]);
-            emi[e] = __expf(-0.5f * GL[hh][e]);
+            mlg[e] = 0.5f * kLog2e * GL[hh][e];
+            const float em = __builtin_amdgcn_exp2f(mlg[e]);
+            em_sk[e] = em * sk;
+            em_sq[e] = em * sq;
         }
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const int r = 8 * rq8 + m;
             const float kk[2] = {lo_f(rk[hh][m]), hi_f(rk[hh][m])};
             const float qq[2] = {lo_f(rq[hh][m]), hi_f(rq[hh][m])};
-            float ekv[2], qsv[2], kdv[2], rkv[2], rqv[2], ckv[2];
+            float ekv[2], qsv[2], kdv[2], ra[2], rb[2], rc[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const float Gm = G[hh][m][e];
-                const float E = __expf(Gm);
-                ekv[e] = kk[e] * E * sk;
-                qsv[e] = qq[e] * E * sq;
-                if (!exact_path) {
-                    const float Ec = __expf(-Gm) * em[e];  // e^{m - G}
-                    rkv[e] = ekv[e] * emi[e];
-                    rqv[e] = qsv[e] * emi[e];
-                    ckv[e] = kk[e] * Ec * sk;
-                    kdv[e] = ckv[e] * em[e];               // e^{G_L - G}, G_L = 2m
+                if constexpr (!EXACT) {
+                    // row factor e^{G - m}, column factor e^{m - G}, both within e^{+-40}
+                    const float t = fmaf(Gm, kLog2e, -mlg[e]);
+                    const float rf = __builtin_amdgcn_exp2f(t), cf = __builtin_amdgcn_exp2f(-t);
+                    ra[e] = kk[e] * rf;          // Gram row operand k e^{G - m} (unscaled)
+                    rb[e] = qq[e] * rf;          // ... q e^{G - m}
+                    rc[e] = kk[e] * cf;          // Gram column operand k e^{m - G}
+                    ekv[e] = ra[e] * em_sk[e];   // k e^G 2^-ek
+                    qsv[e] = rb[e] * em_sq[e];   // scale q e^G 2^-eq
+                    kdv[e] = rc[e] * em_sk[e];   // k e^{G_L - G} 2^-ek, G_L = 2m
                 } else {
-                    rkv[e] = rqv[e] = ckv[e] = 0.f;
+                    const float E = __expf(Gm);
+                    ekv[e] = kk[e] * E * sk;
+                    qsv[e] = qq[e] * E * sq;
                     kdv[e] = kk[e] * __expf(GL[hh][e] - Gm) * sk;
+                    ra[e] = rb[e] = rc[e] = 0.f;
                 }
             }
             ekp[hh][m] = pack_h2(ekv[0], ekv[1]);
@@ -225,20 +239,20 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 const uint32_t hb = hbits(static_cast<_Float16>(kdv[e]));
                 kdp[hh][e][m >> 1] = (m & 1) ? (kdp[hh][e][m >> 1] | (hb << 16)) : hb;
             }
-            if (!exact_path) {
+            if constexpr (!EXACT) {
                 uint32_t hi, lo;
-                split2(rkv[0], rkv[1], hi, lo);
+                split2(ra[0], ra[1], hi, lo);
                 *reinterpret_cast<uint32_t *>(&sm.op.g.rkh[r * HP + 2 * cq]) = hi;
                 *reinterpret_cast<uint32_t *>(&sm.op.g.rkl[r * HP + 2 * cq]) = lo;
-                split2(ckv[0], ckv[1], hi, lo);
+                split2(rc[0], rc[1], hi, lo);
                 *reinterpret_cast<uint32_t *>(&sm.op.g.ckh[r * HP + 2 * cq]) = hi;
                 *reinterpret_cast<uint32_t *>(&sm.op.g.ckl[r * HP + 2 * cq]) = lo;
-                split2(rqv[0], rqv[1], hi, lo);
+                split2(rb[0], rb[1], hi, lo);
                 *reinterpret_cast<uint32_t *>(&sm.op.g.rqh[r * HP + 2 * cq]) = hi;
                 *reinterpret_cast<uint32_t *>(&sm.op.g.rql[r * HP + 2 * cq]) = lo;
             }
         }
-        if (!exact_path) {
+        if constexpr (!EXACT) {
             __syncthreads();  // (3a) this half's operands in LDS
 #pragma unroll
             for (int u = 0; u < JPW; ++u) {
@@ -264,7 +278,8 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
             __syncthreads();  // (3b) this half's operands consumed
         }
     }
-    if (!exact_path) {
+    if constexpr (!EXACT) {
+        const float skk = sk * sk, sqk = sq * sk;  // stored A_kk x 2^-2ek, A_qk x 2^-(eq + ek)
 #pragma unroll
         for (int u = 0; u < JPW; ++u) {
             const int j = wave + NW * u;
@@ -275,17 +290,17 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int rl4 = 4 * g4 + jj, rr = 16 * a + rl4, ii = 16 * b + n16;
-                if (!isq) {
+                if (!isq) {  // A_kk = beta k k^T (decayed), true scale
                     const float vk = ii < rr ? sm.beta[rr] * tacc[u][jj] : 0.f;
-                    if (a == b) sm.ad[a][rl4][n16] = vk * pow2(2 * ek);
-                    else sm.akk[offdiag_index(a, b)][rl4 * BP + n16] = static_cast<_Float16>(vk);
-                } else {
-                    sm.aqk[p][rl4 * BP + n16] = static_cast<_Float16>(ii <= rr ? tacc[u][jj] : 0.f);
+                    if (a == b) sm.ad[a][rl4][n16] = vk;
+                    else sm.akk[offdiag_index(a, b)][rl4 * BP + n16] = static_cast<_Float16>(vk * skk);
+                } else {     // A_qk = scale q k^T (decayed)
+                    sm.aqk[p][rl4 * BP + n16] = static_cast<_Float16>(ii <= rr ? tacc[u][jj] * sqk : 0.f);
                 }
             }
         }
     } else {
-        // exact path: A entries pair by pair from exp(G_r - G_i), fp32
+        // exact path: A entries pair by pair from exp(G_r - G_i), fp32 (compiled for EXACT only)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -483,6 +498,31 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     }
 }
 
+// fast path: one workgroup per chunk and head; grid (segments x per, heads)
+__global__ void __launch_bounds__(NT, 2)
+chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                  const uint16_t *__restrict__ v, const float *__restrict__ g,
+                  const uint16_t *__restrict__ beta, SegmentView sv, int per, int H, float scale,
+                  char *__restrict__ packs) {
+    __shared__ PrepSmem sm;
+    prep_chunk<false>(sm, blockIdx.x, blockIdx.y, q, k, v, g, beta, sv, per, H, scale, packs);
+}
+
+// exact path over the chunks the fast path listed (usually none)
+__global__ void __launch_bounds__(NT, 2)
+chunk_prep_exact_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                        const uint16_t *__restrict__ v, const float *__restrict__ g,
+                        const uint16_t *__restrict__ beta, SegmentView sv, int per, int H, float scale,
+                        char *__restrict__ packs) {
+    __shared__ PrepSmem sm;
+    const int n = *sv.xcount;
+    for (int i = blockIdx.x; i < n; i += gridDim.x) {
+        const int id = sv.xlist[i];
+        __syncthreads();  // the previous chunk's last LDS reads are done
+        prep_chunk<true>(sm, id / H, id % H, q, k, v, g, beta, sv, per, H, scale, packs);
+    }
+}
+
 }  // namespace
 }  // namespace mc
 
@@ -493,10 +533,13 @@ bool f16_path_supported(bool in_bf16, int dk, int dv, int chunk) {
 size_t pack_bytes() { return mc::kPkBytes; }
 
 void launch_prep(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, void *packs) {
-    dim3 grid(max_segs * per, L.H), block(mc::NT);
-    hipLaunchKernelGGL(mc::chunk_prep_kernel, grid, block, 0, L.stream, static_cast<const uint16_t *>(L.q),
-                       static_cast<const uint16_t *>(L.k), static_cast<const uint16_t *>(L.v), L.g,
-                       static_cast<const uint16_t *>(L.beta), sv, per, L.H, L.scale, static_cast<char *>(packs));
+    const uint16_t *q = static_cast<const uint16_t *>(L.q), *k = static_cast<const uint16_t *>(L.k);
+    const uint16_t *v = static_cast<const uint16_t *>(L.v), *b = static_cast<const uint16_t *>(L.beta);
+    char *pk = static_cast<char *>(packs);
+    hipLaunchKernelGGL(mc::chunk_prep_kernel, dim3(max_segs * per, L.H), dim3(mc::NT), 0, L.stream, q, k, v, L.g, b,
+                       sv, per, L.H, L.scale, pk);
+    hipLaunchKernelGGL(mc::chunk_prep_exact_kernel, dim3(256), dim3(mc::NT), 0, L.stream, q, k, v, L.g, b, sv, per,
+                       L.H, L.scale, pk);
 }
 
 }  // namespace kda

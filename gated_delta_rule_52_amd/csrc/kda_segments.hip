@@ -33,7 +33,7 @@ struct Plan {
     int seg_len;    // tokens per segment (per * chunk)
     int max_segs;   // bound on the number of segments
     bool packs;     // matrix-core path: one operand pack per chunk and head
-    size_t off_table, off_seq, off_P, off_H, off_S, off_pack, bytes;
+    size_t off_table, off_seq, off_P, off_H, off_S, off_pack, off_xlist, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t{255}; }
@@ -62,6 +62,7 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int N, int chunk, bool varle
     p.off_H = o;     o = align256(o + ms * H * dk * dv * sizeof(float));
     p.off_S = o;     o = align256(o + ms * H * dk * dv * sizeof(float));
     p.off_pack = o;  o = align256(o + (p.packs ? ms * p.per * H * pack_bytes() : 0));
+    p.off_xlist = o; o = align256(o + (p.packs ? (ms * p.per * H + 1) * sizeof(int) : 0));
     p.bytes = o;
     return p;
 }
@@ -71,9 +72,10 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int N, int chunk, bool varle
 // sequence its first segment.
 __global__ void __launch_bounds__(256)
 build_segments_kernel(const int32_t *__restrict__ cu_seqlens, int T, int N, int seg_len,
-                      int4 *__restrict__ table, int32_t *__restrict__ seq_seg) {
+                      int4 *__restrict__ table, int32_t *__restrict__ seq_seg, int *xcount) {
     __shared__ int s_cnt[256];
     const int tid = threadIdx.x;
+    if (tid == 0 && xcount) *xcount = 0;
     const int per = (N + 255) / 256;
     const int n0 = tid * per, n1 = min(N, n0 + per);
     auto bounds = [&](int n, int64_t &a, int64_t &b) {
@@ -294,10 +296,12 @@ hipError_t launch_chunk(const ChunkLaunch &L) {
     sv.P = reinterpret_cast<float *>(ws + p.off_P);
     sv.Hs = reinterpret_cast<float *>(ws + p.off_H);
     sv.sin = reinterpret_cast<float *>(ws + p.off_S);
+    sv.xcount = p.packs ? reinterpret_cast<int *>(ws + p.off_xlist) : nullptr;
+    sv.xlist = p.packs ? sv.xcount + 1 : nullptr;
 
     hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(256), 0, L.stream, L.cu_seqlens, L.T, L.N,
                        p.seg_len, reinterpret_cast<int4 *>(ws + p.off_table),
-                       reinterpret_cast<int32_t *>(ws + p.off_seq));
+                       reinterpret_cast<int32_t *>(ws + p.off_seq), sv.xcount);
     void *packs = ws + p.off_pack;
     if (p.packs) {
         launch_prep(L, sv, p.max_segs, p.per, packs);
