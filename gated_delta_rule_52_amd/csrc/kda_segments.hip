@@ -26,7 +26,7 @@ namespace kda {
 
 namespace {
 
-constexpr int kTargetUnits = 512;  // segments x heads wanted for two waves of workgroups
+constexpr int kTargetUnits = 256;  // segments x heads: one long segment per compute unit and pass
 
 struct Plan {
     int per;        // chunks per segment
