@@ -31,8 +31,11 @@ __device__ __forceinline__ f4 mmab(b8 a, b8 b, f4 c) {
 }
 __device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
 
-// 2^e as a float (|e| < 127)
-__device__ __forceinline__ float pow2(int e) { return __int_as_float((e + 127) << 23); }
+// 2^e as a float, saturating: 0 below the normal range (a true underflow of
+// the scaled quantity), 2^127 above it
+__device__ __forceinline__ float pow2(int e) {
+    return e < -126 ? 0.f : __int_as_float((min(e, 127) + 127) << 23);
+}
 
 // Exponent e with m * 2^-e in [0.5, 1) for m > 0 (0 for m == 0 or denormal m).
 __device__ __forceinline__ int exp_of(float m) {

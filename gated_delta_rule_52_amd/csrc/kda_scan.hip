@@ -13,18 +13,17 @@
 // registers) into one of two buffers while the other one is in use, so the
 // copy of chunk j + 1 overlaps the products of chunk j and a chunk costs one
 // barrier; U goes straight to registers in accumulator order, also one chunk
-// ahead.  Each wave owns 32 state columns (two 16-column tiles, processed
-// together so every A operand fragment is read from LDS once per wave).  All
+// ahead.  Each wave owns one 16-column tile of the state.  All
 // products are 16x16x16, whose B operand layout is the accumulator layout:
 // the state and V_new feed them without any cross-lane movement.  They are
 // rounded to fp16 with power-of-two scales of the wave's own (from its
 // maxima), so waves share nothing but the pack.  o is staged in LDS per wave
 // and written with 16-byte stores.
 //
-// Modes: kLocal, 8 waves: waves 0-3 build H (the dv columns, zero start) and
-// waves 4-7 build P (the dk x dk transition: identity start, v = 0), so that
-// leaving = P entering + H; kOut, 4 waves: replay from the entering state,
-// write o and, for a sequence's last segment, the final state.
+// Modes: kLocal, 16 waves: waves 0-7 build H (the dv columns, zero start)
+// and waves 8-15 build P (the dk x dk transition: identity start, v = 0), so
+// that leaving = P entering + H; kOut, 8 waves: replay from the entering
+// state, write o and, for a sequence's last segment, the final state.
 #include "kda_internal.h"
 #include "kda_mfma.h"
 
@@ -37,7 +36,9 @@ typedef void __attribute__((address_space(3))) *lptr_t;
 
 template <int MODE>
 struct ScanCfg {
-    static constexpr int NW = MODE == kOut ? 4 : 8;
+    static constexpr int NCT = 1;                    // 16-column state tiles per wave
+    static constexpr int NWH = 8 / NCT;              // waves per 128 columns
+    static constexpr int NW = MODE == kOut ? NWH : 2 * NWH;
     static constexpr int NT = NW * kWave;
     static constexpr int kBytes = MODE == kOut ? kPkOut : kPkLocal;  // pack bytes staged in LDS
 };
@@ -47,14 +48,15 @@ __global__ void __launch_bounds__(ScanCfg<MODE>::NT, 1)
 chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__restrict__ o_, SegmentView sv,
                   int H) {
     constexpr bool kOutPass = MODE == kOut;
-    constexpr int NW = ScanCfg<MODE>::NW, kBytes = ScanCfg<MODE>::kBytes;
+    constexpr int NW = ScanCfg<MODE>::NW, NWH = ScanCfg<MODE>::NWH, NCT = ScanCfg<MODE>::NCT;
+    constexpr int kBytes = ScanCfg<MODE>::kBytes;
     // two pack buffers as separate objects, so that the compiler can tell a
     // copy into one from reads of the other and does not wait for the copy
     __shared__ __attribute__((aligned(16))) char lds0[kBytes];
     __shared__ __attribute__((aligned(16))) char lds1[kBytes];
-    // o of a chunk, per wave: 64 rows x 32 columns, rows padded by 16 bytes
+    // o of a chunk, per wave: 64 rows x its columns, rows padded by 16 bytes
     // (the four row groups of an accumulator tile land on different banks)
-    constexpr int kStageRow = 32 * (OutBf16 ? 2 : 4) + 16;
+    constexpr int kStageRow = 16 * NCT * (OutBf16 ? 2 : 4) + 16;
     __shared__ __attribute__((aligned(16))) char ostage[kOutPass ? NW : 1][kOutPass ? 64 * kStageRow : 16];
 
     const int seg = blockIdx.x, h = blockIdx.y;
@@ -68,21 +70,21 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     if (!kOutPass && last) return;
     const int64_t t0 = sd.y, t1 = sd.z;
     const int nch = static_cast<int>((t1 - t0 + C - 1) / C);
-    const bool pcols = !kOutPass && wave >= 4;  // this wave builds P
-    const int ctile0 = 2 * (wave & 3);           // this wave's first 16-column tile
+    const bool pcols = !kOutPass && wave >= NWH;  // this wave builds P
+    const int ctile0 = NCT * (wave % NWH);         // this wave's first 16-column tile
     const int col0 = 16 * ctile0;
 
     // a state tile element (16 rt + 4 g4 + jj, col0 + 16 ct + n16) of a
     // row-major 128 x 128 fp32 matrix: one per-lane byte offset plus a constant
     const uint32_t st_lane = 4 * (4 * g4 * 128 + col0 + n16);
     auto st_off = [](int rt, int ct, int jj) { return 4 * ((16 * rt + jj) * 128 + 16 * ct); };
-    f4 acc[8][2];
+    f4 acc[8][NCT];
     if (kOutPass) {
         const rsrc_t rs = make_rsrc(sv.sin + (static_cast<int64_t>(seg) * H + h) * DK * DV, 4 * DK * DV);
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
                     acc[rt][ct][jj] = __uint_as_float(ld32(rs, st_lane, st_off(rt, ct, jj)));
@@ -90,19 +92,26 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
                     acc[rt][ct][jj] = (pcols && 16 * rt + 4 * g4 + jj == col0 + 16 * ct + n16) ? 1.f : 0.f;
     }
-    float smax = 0.f;
+    // acc[.][ct] holds the state times 2^-fr[ct]: a power-of-two frame that
+    // follows the scale of each chunk's update, so that the update's product
+    // lands in the accumulators without rescaling; smax[ct] = max |acc|
+    int fr[NCT];
+    float smax[NCT];
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
+    for (int ct = 0; ct < NCT; ++ct) {
+        fr[ct] = 0;
+        float m = 0.f;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) smax = fmaxf(smax, fabsf(acc[rt][ct][jj]));
-    smax = wave_max(smax);
+            for (int jj = 0; jj < 4; ++jj) m = fmaxf(m, fabsf(acc[rt][ct][jj]));
+        smax[ct] = wave_max(m);
+    }
 
     // o of the segment's tokens: element (t, c) at (t - t0) H DV + c from the
     // segment base; rows past the segment end are dropped
@@ -113,53 +122,50 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     const rsrc_t rs_o = make_rsrc(static_cast<char *>(o_) + seg_base * ob, kOutPass ? ob * seg_elems : 0);
 
     // chunk j's pack -> dst and its U -> registers
-    auto fetch = [&](int j, char *dst, u4 (&ur)[2][2]) {
+    auto fetch = [&](int j, char *dst, u4 (&ur)[NCT][2]) {
         const char *pack = packs + (static_cast<int64_t>(seg * per + j) * H + h) * kPkBytes;
         for (int u = wave; u < kBytes / 1024; u += NW)
             __builtin_amdgcn_global_load_lds((gptr_t)(pack + 1024 * u + 16 * lane), (lptr_t)(dst + 1024 * u), 16, 0, 0);
         if (!pcols) {
             const rsrc_t rs_p = make_rsrc(pack, kPkBytes);
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int pr = 0; pr < 2; ++pr)
                     ur[ct][pr] = __builtin_amdgcn_raw_buffer_load_b128(rs_p, kPkU + 16 * lane,
                                                                        u_off(ctile0 + ct, 2 * pr, 0), 0);
         }
     };
-    u4 ur_cur[2][2] = {}, ur_nxt[2][2] = {};
-    fetch(0, lds0, ur_nxt);
+    u4 urA[NCT][2] = {}, urB[NCT][2] = {};  // U of the chunk in use / of the next one (zero for P)
+    fetch(0, lds0, urA);
 
     // one chunk: its pack is in L, the next one's goes to Lnext
-    auto step = [&](int j, const char *L, char *Lnext) {
+    auto step = [&](int j, const char *L, char *Lnext, const u4 (&ur_cur)[NCT][2], u4 (&ur_nxt)[NCT][2]) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // chunk j in L; every wave is done with chunk j - 1
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int pr = 0; pr < 2; ++pr) ur_cur[ct][pr] = ur_nxt[ct][pr];
         if (j + 1 < nch) fetch(j + 1, Lnext, ur_nxt);
 
         const int *hdr = reinterpret_cast<const int *>(L + kPkHdr);
         const int ew = hdr[kHdrW], ek = hdr[kHdrK];
         const float *gam = reinterpret_cast<const float *>(L + kPkGamma);
-        const int es = exp_of(smax);  // this wave's state, stored below 1
-        const float ss = pow2(-es), unx = pow2(ew + es);
+        int es[NCT];  // the state in fp16 as S 2^-(es + fr), below 1
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) es[ct] = exp_of(smax[ct]);
         // lane (g4, n16) reads row n16, columns 4 g4 .. 4 g4 + 3 of a 16x16 A block:
         // 8 bytes at unit 2 blk + g4 / 2, half g4 % 2
         const int hsel = 8 * (g4 & 1), usel = g4 >> 1;
 
         // The accumulator layout of a 16-row state tile is the B operand
         // layout of a 16x16x16 product: the state feeds products as is.
-        h4 sh[2][8];
+        h4 sh[NCT][8];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int rt = 0; rt < 8; ++rt) sh[ct][rt] = to_h4(acc[rt][ct], ss);
+            for (int rt = 0; rt < 8; ++rt) sh[ct][rt] = to_h4(acc[rt][ct], pow2(-es[ct]));
         // X = W S, Y = Q S
-        f4 X[2][4], Y[2][4];
+        f4 X[NCT][4], Y[NCT][4];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 X[ct][a] = zero4();
@@ -171,22 +177,23 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
             for (int a = 0; a < 4; ++a) {
                 const h4 wa = *reinterpret_cast<const h4 *>(L + kPkW + swz_w(16 * a + n16, 2 * rt + usel) + hsel);
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) X[ct][a] = mma16(wa, sh[ct][rt], X[ct][a]);
+                for (int ct = 0; ct < NCT; ++ct) X[ct][a] = mma16(wa, sh[ct][rt], X[ct][a]);
                 if (kOutPass) {
                     const h4 qa = *reinterpret_cast<const h4 *>(L + kPkQ + swz_w(16 * a + n16, 2 * rt + usel) + hsel);
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) Y[ct][a] = mma16(qa, sh[ct][rt], Y[ct][a]);
+                    for (int ct = 0; ct < NCT; ++ct) Y[ct][a] = mma16(qa, sh[ct][rt], Y[ct][a]);
                 }
             }
         }
         // V_new = U - X (fp32), then an fp16 scale of its own per tile
-        f4 Vn[2][4];
-        h4 Vh[2][4];
-        int evn[2];
+        f4 Vn[NCT][4];
+        h4 Vh[NCT][4];
+        int evn[NCT];
         {
             const float unu = pow2(hdr[kHdrU]);
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
+            for (int ct = 0; ct < NCT; ++ct) {
+                const float unx = pow2(ew + es[ct] + fr[ct]);
                 float mv = 0.f;
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
@@ -194,8 +201,7 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
                     const h4 uh = __builtin_bit_cast(h4, (a & 1) ? u2{w[2], w[3]} : u2{w[0], w[1]});
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
-                        const float uval = pcols ? 0.f : static_cast<float>(uh[jj]) * unu;
-                        Vn[ct][a][jj] = uval - X[ct][a][jj] * unx;
+                        Vn[ct][a][jj] = static_cast<float>(uh[jj]) * unu - X[ct][a][jj] * unx;
                         mv = fmaxf(mv, fabsf(Vn[ct][a][jj]));
                     }
                 }
@@ -207,11 +213,10 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
         }
         // a6: o = Q S + A_qk V_new, staged per wave in LDS, then 16-byte stores
         if (kOutPass) {
-            const float unq = pow2(hdr[kHdrQ] + es);
             char *st = ostage[wave];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const float una = pow2(hdr[kHdrA] + evn[ct]);
+            for (int ct = 0; ct < NCT; ++ct) {
+                const float unq = pow2(hdr[kHdrQ] + es[ct] + fr[ct]), una = pow2(hdr[kHdrA] + evn[ct]);
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
                     f4 oi = zero4();
@@ -231,9 +236,9 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
                     }
                 }
             }
-            // 64 rows x 32 columns of this wave: 16-byte units, rows past the
+            // 64 rows x this wave's columns: 16-byte units, rows past the
             // segment end dropped by the buffer range
-            constexpr int kUnitsPerRow = 32 * ob / 16;
+            constexpr int kUnitsPerRow = 16 * NCT * ob / 16;
 #pragma unroll
             for (int k = 0; k < 64 * kUnitsPerRow / kWave; ++k) {
                 const int i = lane + kWave * k, rr = i / kUnitsPerRow, un = i % kUnitsPerRow;
@@ -241,40 +246,39 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
                 st128(rs_o, w, ob * ((static_cast<uint32_t>(C * j + rr)) * tok_stride + col0) + 16 * un);
             }
         }
-        // a5: S <- gamma S + KT V_new
-        float down[2], up[2];
+        // a5: S <- gamma S + KT V_new, in the new frame fr' = ek + evn, where
+        // the product KT_h V_h = KT V 2^-(ek + evn) needs no scaling
+        float gsc[NCT];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            down[ct] = pow2(-(ek + evn[ct]));
-            up[ct] = pow2(ek + evn[ct]);
+        for (int ct = 0; ct < NCT; ++ct) {
+            gsc[ct] = pow2(fr[ct] - (ek + evn[ct]));
+            fr[ct] = ek + evn[ct];
         }
-        float smax_new = 0.f;
+        float mx[NCT] = {};
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) {
             const f4 gm = *reinterpret_cast<const f4 *>(gam + 16 * rt + 4 * g4);
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) acc[rt][ct][jj] *= gm[jj] * down[ct];
+                for (int jj = 0; jj < 4; ++jj) acc[rt][ct][jj] *= gm[jj] * gsc[ct];
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const h4 kt = *reinterpret_cast<const h4 *>(L + kPkKT + swz_kt(16 * rt + n16, 2 * a + usel) + hsel);
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = mma16(kt, Vh[ct][a], acc[rt][ct]);
+                for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = mma16(kt, Vh[ct][a], acc[rt][ct]);
             }
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    acc[rt][ct][jj] *= up[ct];
-                    smax_new = fmaxf(smax_new, fabsf(acc[rt][ct][jj]));
-                }
+                for (int jj = 0; jj < 4; ++jj) mx[ct] = fmaxf(mx[ct], fabsf(acc[rt][ct][jj]));
         }
-        smax = wave_max(smax_new);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) smax[ct] = wave_max(mx[ct]);
     };
     for (int j = 0; j < nch; j += 2) {
-        step(j, lds0, lds1);
-        if (j + 1 < nch) step(j + 1, lds1, lds0);
+        step(j, lds0, lds1, urA, urB);
+        if (j + 1 < nch) step(j + 1, lds1, lds0, urB, urA);
     }
 
     // ---- leaving state (DK = DV: H and P are both 128 x 128)
@@ -289,10 +293,10 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
-                    st32(rs, __float_as_uint(acc[rt][ct][jj]), st_lane, st_off(rt, ct, jj));
+                    st32(rs, __float_as_uint(acc[rt][ct][jj] * pow2(fr[ct])), st_lane, st_off(rt, ct, jj));
     }
 }
 

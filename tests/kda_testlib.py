@@ -43,6 +43,9 @@ def slice_errors(o_gpu, hT_gpu, o_ref, hT_ref, x, heads):
     listed heads only."""
     o_gpu = np.asarray(o_gpu, dtype=np.float64).reshape(-1, o_gpu.shape[2], o_gpu.shape[3])
     o_ref = np.asarray(o_ref, dtype=np.float64).reshape(-1, o_ref.shape[2], o_ref.shape[3])
+    # a non-finite result is an infinite error (max() would drop a NaN)
+    if not np.isfinite(o_gpu).all() or (hT_gpu is not None and not np.isfinite(np.asarray(hT_gpu)).all()):
+        return float("inf"), float("inf")
     eo, es = 0.0, 0.0
     for n, (a, b) in enumerate(x.seq_bounds()):
         for j, h in enumerate(heads):
