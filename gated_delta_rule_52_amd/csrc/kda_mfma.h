@@ -159,9 +159,9 @@ __device__ __forceinline__ void st128(rsrc_t r, u4 v, uint32_t off, int soff = 0
 //
 //   [0, 512)        gamma: exp(G_last) per channel, fp32
 //   [512, 1024)     header: int exponents e_w, e_q, e_k, e_u, e_a
-//   W   [64][128]   T beta (e^G k)            A operand of W S
-//   KT  [128][64]   (e^{G_last - G} k)^T      A operand of the state update
-//   Q   [64][128]   scale e^G q               A operand of Q S
+//   W   [64][128]   T beta (e^G k)            A operand of W S       (w_col)
+//   KT  [128][64]   (e^{G_last - G} k)^T      A operand of the update (kt_col)
+//   Q   [64][128]   scale e^G q               A operand of Q S       (w_col)
 //   A   [10][16][16] blocks (a, b), b <= a, of the decayed scale q k^T
 //   U   T beta v in accumulator order: [16-column tile][row-block pair]
 //                   [lane][row block a, a + 1][row within lane]
@@ -178,13 +178,32 @@ constexpr int kPkOut = kPkU;     // bytes the output pass copies to LDS
 static_assert(kPkLocal % 1024 == 0 && kPkOut % 1024 == 0, "whole 1 KiB wave copies");
 enum { kHdrW = 0, kHdrQ = 1, kHdrK = 2, kHdrU = 3, kHdrA = 4 };
 
-// byte offset of 16-byte unit u of row r: W and Q ([64][128] fp16, 16 units a row)
-__device__ __forceinline__ int swz_w(int r, int u) { return r * 256 + ((u ^ (r & 15)) << 4); }
-// ... KT ([128][64] fp16, 8 units a row; rows 2i and 2i + 1 share a pattern
-// but sit 128 bytes apart)
-__device__ __forceinline__ int swz_kt(int r, int u) { return r * 128 + ((u ^ ((r >> 1) & 7)) << 4); }
-// byte offset of 8-byte unit v (columns 4v .. 4v + 3) of row r of A block p
-__device__ __forceinline__ int a_off(int p, int r, int v) { return p * 512 + r * 32 + ((v ^ ((r >> 2) & 2)) << 3); }
+// W, Q ([64][128] fp16) and KT ([128][64] fp16) are read as A operands of
+// 16x16x32 products whose contraction index is permuted: in step p, lane
+// (g, n) supplies rows 16 (2p) + 4g .. +3 and 16 (2p + 1) + 4g .. +3 of the B
+// matrix (exactly what its accumulators hold, so B needs no cross-lane
+// movement), and the A operand the matching columns.  The pack therefore
+// stores, in 16-byte unit 4p + g of a row, the columns 32p + 4g .. +3 and
+// 32p + 16 + 4g .. +3 (one b128 read per lane and step).  Units are
+// XOR-swizzled by row so that the 16 rows a read touches hit distinct banks.
+// byte offset of column c of row r
+__device__ __forceinline__ int w_col(int r, int c) {   // W, Q: 16 units a row
+    const int u = 4 * (c >> 5) + ((c >> 2) & 3);
+    return r * 256 + ((u ^ (r & 15)) << 4) + (((c >> 4) & 1) << 3) + ((c & 3) << 1);
+}
+__device__ __forceinline__ int kt_col(int r, int c) {  // KT: 8 units a row, rows 2i, 2i+1 128 bytes apart
+    const int u = 4 * (c >> 5) + ((c >> 2) & 3);
+    return r * 128 + ((u ^ ((r >> 1) & 7)) << 4) + (((c >> 4) & 1) << 3) + ((c & 3) << 1);
+}
+// byte offset of the 16-byte A operand unit (step p, lane group g) of row r
+__device__ __forceinline__ int w_unit(int r, int p, int g) { return r * 256 + (((4 * p + g) ^ (r & 15)) << 4); }
+__device__ __forceinline__ int kt_unit(int r, int p, int g) { return r * 128 + (((4 * p + g) ^ ((r >> 1) & 7)) << 4); }
+// A block p, row r, 8-byte unit v (columns 4v .. 4v + 3); the two 8-byte
+// units of each 16-byte half are exchanged in odd blocks (reads of two
+// blocks that the compiler fuses then fall on complementary banks)
+__device__ __forceinline__ int a_off(int p, int r, int v) {
+    return p * 512 + r * 32 + ((v ^ ((r >> 2) & 2) ^ (p & 1)) << 3);
+}
 // byte offset of the 8 bytes of U (tile ct, row block a) that lane `lane` holds
 __device__ __forceinline__ int u_off(int ct, int a, int lane) {
     return ((ct * 2 + (a >> 1)) * 64 + lane) * 16 + (a & 1) * 8;

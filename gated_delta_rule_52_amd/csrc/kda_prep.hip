@@ -375,13 +375,16 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
         for (int m = 0; m < 8; ++m) {
             const int r = 8 * rq8 + m;
             *reinterpret_cast<uint32_t *>(&sm.op.s.ek[r * KP + hh * HC + 2 * cq]) = ekp[hh][m];
-            st32(rs_p, qsp[hh][m], kPkQ + swz_w(r, hh * 8 + (cq >> 2)) + 4 * (cq & 3));
+            st32(rs_p, qsp[hh][m], kPkQ + w_col(r, hh * HC + 2 * cq));
         }
-        // KT: eight consecutive rows of one channel are one 16-byte unit
+        // KT: four consecutive rows of one channel are 8 contiguous bytes
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const u4 w = {kdp[hh][e][0], kdp[hh][e][1], kdp[hh][e][2], kdp[hh][e][3]};
-            st128(rs_p, w, kPkKT + swz_kt(hh * HC + 2 * cq + e, rq8));
+            // rows 8 rq8 + 4t .. +3 of channel c: 8 bytes each
+            const int c = hh * HC + 2 * cq + e;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                st64(rs_p, u2{kdp[hh][e][2 * t], kdp[hh][e][2 * t + 1]}, kPkKT + kt_col(c, 8 * rq8 + 4 * t));
         }
     }
     __syncthreads();  // (5)
@@ -461,7 +464,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int rr = 16 * a + 4 * g4 + jj;
-                    *reinterpret_cast<_Float16 *>(wst + swz_w(rr, col >> 3) + 2 * (col & 7)) =
+                    *reinterpret_cast<_Float16 *>(wst + w_col(rr, col)) =
                         static_cast<_Float16>(Wr[t][a][jj] * swv);
                 }
                 // U straight to the pack, in accumulator order
@@ -481,9 +484,11 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
         }
         for (int u = tid; u < 10 * 16 * 2; u += NT) {  // A_qk blocks, rows of 32 bytes
             // 16-byte half `half` of a stored row holds the row's logical half
-            // half ^ (row >= 8) (the 8-byte units of a_off, pairwise)
+            // half ^ (row >= 8), its two 8-byte units exchanged in odd blocks
             const int p = u >> 5, row = (u >> 1) & 15, half = u & 1, lh = half ^ (row >> 3);
-            st128(rs_p, *reinterpret_cast<const u4 *>(&sm.aqk[p][row * BP + 8 * lh]), kPkA + 16 * u);
+            u4 w = *reinterpret_cast<const u4 *>(&sm.aqk[p][row * BP + 8 * lh]);
+            if (p & 1) w = u4{w[2], w[3], w[0], w[1]};
+            st128(rs_p, w, kPkA + 16 * u);
         }
         if (tid < DK / 4)
             st128(rs_p, *reinterpret_cast<const u4 *>(&sm.gam[4 * tid]), kPkGamma + 16 * tid);

@@ -13,9 +13,9 @@
 // registers) into one of two buffers while the other one is in use, so the
 // copy of chunk j + 1 overlaps the products of chunk j and a chunk costs one
 // barrier; U goes straight to registers in accumulator order, also one chunk
-// ahead.  Each wave owns one 16-column tile of the state.  All
-// products are 16x16x16, whose B operand layout is the accumulator layout:
-// the state and V_new feed them without any cross-lane movement.  They are
+// ahead.  Each wave owns one 16-column tile of the state.  The state and
+// V_new feed the 16x16x32 products straight from the accumulator layout
+// (permuted contraction index, see w_col).  They are
 // rounded to fp16 with power-of-two scales of the wave's own (from its
 // maxima), so waves share nothing but the pack.  o is staged in LDS per wave
 // and written with 16-byte stores.
@@ -151,17 +151,19 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
         int es[NCT];  // the state in fp16 as S 2^-(es + fr), below 1
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) es[ct] = exp_of(smax[ct]);
-        // lane (g4, n16) reads row n16, columns 4 g4 .. 4 g4 + 3 of a 16x16 A block:
-        // 8 bytes at unit 2 blk + g4 / 2, half g4 % 2
-        const int hsel = 8 * (g4 & 1), usel = g4 >> 1;
-
-        // The accumulator layout of a 16-row state tile is the B operand
-        // layout of a 16x16x16 product: the state feeds products as is.
-        h4 sh[NCT][8];
+        // The accumulator layout of two 16-row state tiles is the B operand
+        // layout of a 16x16x32 product with a permuted contraction index (see
+        // w_col): the state feeds products as is.
+        h8 sb[NCT][4];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
+        for (int ct = 0; ct < NCT; ++ct) {
+            const float s = pow2(-es[ct]);
 #pragma unroll
-            for (int rt = 0; rt < 8; ++rt) sh[ct][rt] = to_h4(acc[rt][ct], pow2(-es[ct]));
+            for (int p = 0; p < 4; ++p) {
+                const h4 lo = to_h4(acc[2 * p][ct], s), hi = to_h4(acc[2 * p + 1][ct], s);
+                sb[ct][p] = h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+        }
         // X = W S, Y = Q S
         f4 X[NCT][4], Y[NCT][4];
 #pragma unroll
@@ -172,16 +174,16 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
                 Y[ct][a] = zero4();
             }
 #pragma unroll
-        for (int rt = 0; rt < 8; ++rt) {
+        for (int p = 0; p < 4; ++p) {
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const h4 wa = *reinterpret_cast<const h4 *>(L + kPkW + swz_w(16 * a + n16, 2 * rt + usel) + hsel);
+                const h8 wa = *reinterpret_cast<const h8 *>(L + kPkW + w_unit(16 * a + n16, p, g4));
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) X[ct][a] = mma16(wa, sh[ct][rt], X[ct][a]);
+                for (int ct = 0; ct < NCT; ++ct) X[ct][a] = mma32(wa, sb[ct][p], X[ct][a]);
                 if (kOutPass) {
-                    const h4 qa = *reinterpret_cast<const h4 *>(L + kPkQ + swz_w(16 * a + n16, 2 * rt + usel) + hsel);
+                    const h8 qa = *reinterpret_cast<const h8 *>(L + kPkQ + w_unit(16 * a + n16, p, g4));
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) Y[ct][a] = mma16(qa, sh[ct][rt], Y[ct][a]);
+                    for (int ct = 0; ct < NCT; ++ct) Y[ct][a] = mma32(qa, sb[ct][p], Y[ct][a]);
                 }
             }
         }
@@ -255,6 +257,14 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
             fr[ct] = ek + evn[ct];
         }
         float mx[NCT] = {};
+        h8 vb[NCT][2];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const h4 lo = Vh[ct][2 * p], hi = Vh[ct][2 * p + 1];
+                vb[ct][p] = h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) {
             const f4 gm = *reinterpret_cast<const f4 *>(gam + 16 * rt + 4 * g4);
@@ -263,10 +273,10 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) acc[rt][ct][jj] *= gm[jj] * gsc[ct];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const h4 kt = *reinterpret_cast<const h4 *>(L + kPkKT + swz_kt(16 * rt + n16, 2 * a + usel) + hsel);
+            for (int p = 0; p < 2; ++p) {
+                const h8 kt = *reinterpret_cast<const h8 *>(L + kPkKT + kt_unit(16 * rt + n16, p, g4));
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = mma16(kt, Vh[ct][a], acc[rt][ct]);
+                for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = mma32(kt, vb[ct][p], acc[rt][ct]);
             }
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
