@@ -35,7 +35,12 @@ namespace {
 
 constexpr int NW = 4, NT = NW * kWave;
 constexpr int HC = DK / 2;  // channels per half of dk
-constexpr int HP = HC + 8;  // row stride (halves) of the half-dk Gram operand tiles
+// Gram operand tiles of one half of dk: [64 rows][64 channels] bf16, 128-byte
+// rows whose 16-byte units are XOR-swizzled by (row / 2) mod 8: a 16-byte read
+// of 16 consecutive rows (one MFMA operand) then touches every bank once
+__device__ __forceinline__ int g_off(int r, int ch) {  // in halves
+    return r * HC + ((((ch >> 3) ^ ((r >> 1) & 7)) << 3) | (ch & 7));
+}
 constexpr int KP = DK + 8;  // row stride (halves) of [row][dk] tiles
 constexpr int GP = DK + 4;  // row stride (floats) of [row][dk] fp32 tiles
 constexpr int BP = 16 + 8;  // row stride of 16x16 half blocks
@@ -48,9 +53,9 @@ struct alignas(16) PrepSmem {
     // per-thread base plus an immediate offset below 64 KiB.
     union alignas(16) {
         struct {  // Gram operands of one half of dk, bf16 high/low parts, [row][channel]
-            uint16_t rkh[C * HP], rkl[C * HP];   // k_r e^{G_r - m} 2^-ek
-            uint16_t rqh[C * HP], rql[C * HP];   // scale q_r e^{G_r - m} 2^-eq
-            uint16_t ckh[C * HP], ckl[C * HP];   // k_i e^{m - G_i} 2^-ek
+            uint16_t rkh[C * HC], rkl[C * HC];   // k_r e^{G_r - m}  (g_off layout)
+            uint16_t rqh[C * HC], rql[C * HC];   // q_r e^{G_r - m}
+            uint16_t ckh[C * HC], ckl[C * HC];   // k_i e^{m - G_i}
         } g;
         struct {  // fp16 operands
             _Float16 ek[C * KP];   // k e^G 2^-ek; later W, swizzled [64][128]
@@ -242,14 +247,14 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
             if constexpr (!EXACT) {
                 uint32_t hi, lo;
                 split2(ra[0], ra[1], hi, lo);
-                *reinterpret_cast<uint32_t *>(&sm.op.g.rkh[r * HP + 2 * cq]) = hi;
-                *reinterpret_cast<uint32_t *>(&sm.op.g.rkl[r * HP + 2 * cq]) = lo;
+                *reinterpret_cast<uint32_t *>(&sm.op.g.rkh[g_off(r, 2 * cq)]) = hi;
+                *reinterpret_cast<uint32_t *>(&sm.op.g.rkl[g_off(r, 2 * cq)]) = lo;
                 split2(rc[0], rc[1], hi, lo);
-                *reinterpret_cast<uint32_t *>(&sm.op.g.ckh[r * HP + 2 * cq]) = hi;
-                *reinterpret_cast<uint32_t *>(&sm.op.g.ckl[r * HP + 2 * cq]) = lo;
+                *reinterpret_cast<uint32_t *>(&sm.op.g.ckh[g_off(r, 2 * cq)]) = hi;
+                *reinterpret_cast<uint32_t *>(&sm.op.g.ckl[g_off(r, 2 * cq)]) = lo;
                 split2(rb[0], rb[1], hi, lo);
-                *reinterpret_cast<uint32_t *>(&sm.op.g.rqh[r * HP + 2 * cq]) = hi;
-                *reinterpret_cast<uint32_t *>(&sm.op.g.rql[r * HP + 2 * cq]) = lo;
+                *reinterpret_cast<uint32_t *>(&sm.op.g.rqh[g_off(r, 2 * cq)]) = hi;
+                *reinterpret_cast<uint32_t *>(&sm.op.g.rql[g_off(r, 2 * cq)]) = lo;
             }
         }
         if constexpr (!EXACT) {
@@ -264,8 +269,8 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
                 const uint16_t *rl = isq ? sm.op.g.rql : sm.op.g.rkl;
 #pragma unroll
                 for (int s = 0; s < HC / 32; ++s) {
-                    const int ra = (16 * a + n16) * HP + 32 * s + 8 * g4;
-                    const int cb = (16 * b + n16) * HP + 32 * s + 8 * g4;
+                    const int ra = g_off(16 * a + n16, 32 * s + 8 * g4);
+                    const int cb = g_off(16 * b + n16, 32 * s + 8 * g4);
                     const b8 xh = *reinterpret_cast<const b8 *>(rh + ra);
                     const b8 xl = *reinterpret_cast<const b8 *>(rl + ra);
                     const b8 yh = *reinterpret_cast<const b8 *>(sm.op.g.ckh + cb);
