@@ -1,17 +1,24 @@
 """Benchmark: KDA chunkwise prefill (B=1, H=16, dk=dv=128, T=65536) and the
 recurrent decode step (256 sequences x 16 heads, 1024 steps) on one MI355X.
 
-One step = one kda_chunk_fwd over the whole 64K-token batch (every prefill
-stage: cumulative decay, decayed Gram blocks, UT inverse, WY factors, state
-propagation, output).  Inputs are drawn on the host, copied to HBM once, and
-are resident when timing starts.  Prints ONE JSON line.
+One step = one kda_chunk_fwd over the whole 64K-token batch: every stage of
+the prefill (cumulative decay, decayed Gram blocks, UT inverse, WY factors,
+inter-chunk state propagation, output) runs inside that call.  Inputs are
+drawn on the host, copied to HBM once, and are resident when timing starts.
+Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+                    [--calibrate-copy]
+
+--calibrate-copy adds, before the timed region, one elementwise copy kernel
+of a known size (256 MiB read + 256 MiB written): its FETCH_SIZE / WRITE_SIZE
+counters give the scale for the operator's measured HBM traffic.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -24,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 METRIC = "KDA prefill tokens/s (H=16,d=128,T=64K) + decode step us/token, % roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fwd_prefill_64k_traffic.md")
 
 
 def log(*a):
@@ -43,6 +51,38 @@ def decode_alg_bytes(N, H, dk, dv, in_bytes=2, out_bytes=2):
     return nh * (2 * dk * dv * 4 + (2 * dk + dv + 1) * in_bytes + dk * 4 + dv * out_bytes)
 
 
+def source_digest():
+    """sha256 over the HIP/C++ sources: a stored traffic measurement is only
+    reported while the kernels it was taken on are unchanged."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_52_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per kda_chunk_fwd call from the committed counter summary,
+    or None when it was taken on different kernel sources."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ":" in line:
+            key, val = line[2:].split(":", 1)
+            fields[key.strip()] = val.strip().strip("`")
+    if fields.get("source_sha256") != source_digest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
 def time_prefill(args):
     import torch
     import gated_delta_rule_52_amd as kda
@@ -56,25 +96,37 @@ def time_prefill(args):
     g, h0 = t(x.g, f32), t(x.h0, f32)
     hT = torch.empty_like(h0)
     o = torch.empty((x.B, x.T, x.H, x.dv), dtype=bf, device=dev)
+    ws = torch.empty(kda.chunk_fwd_workspace_bytes(q, v), dtype=torch.uint8, device=dev)
     step = lambda: kda.chunk_fwd(q, k, v, g, beta, initial_state=h0, final_state=hT, o=o,
-                                 out_dtype=bf)
+                                 out_dtype=bf, workspace=ws)
+    if args.calibrate_copy:
+        # an elementwise kernel (not a runtime blit) so the counters see it
+        a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        log("calibration copy (neg kernel): 268435456 B read, 268435456 B written")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # the library launches on torch's current stream: events there bracket every kernel of a call
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         step()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms = e0.elapsed_time(e1) / args.steps
-    log(f"prefill: {ms:.3f} ms/step (events), wall {1e3 * wall / args.steps:.3f} ms/step")
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    ms = float(ev[0].elapsed_time(ev[-1]) / args.steps)
+    log(f"prefill: {ms:.3f} ms/step (events), median {np.median(per):.3f}, p10 {np.percentile(per, 10):.3f}, "
+        f"p90 {np.percentile(per, 90):.3f}, wall {1e3 * wall / args.steps:.3f} ms/step")
     nbytes = prefill_alg_bytes(x.B, x.T, x.H, x.dk, x.dv, x.N)
-    return x, ms, nbytes
+    return x, ms, per, nbytes
 
 
 def time_decode(args):
@@ -132,6 +184,8 @@ def time_decode(args):
 
 
 def cpu_baseline(x):
+    """The fp64 token-recurrence oracle on the host cores, over the whole
+    prefill_64k workload (16 heads x 65,536 tokens: a few seconds)."""
     import oracle
     cores = len(os.sched_getaffinity(0))
     units = x.N * x.H
@@ -143,7 +197,7 @@ def cpu_baseline(x):
     log(f"oracle: {dt:.2f} s on {threads} threads")
     return dict(value=x.B * x.T / dt, unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"whole prefill_64k workload ({x.H} heads x {x.T} tokens, fp64 token "
-                       f"recurrence), {dt:.2f} s wall")
+                       f"recurrence, OpenMP over heads), {dt:.2f} s wall")
 
 
 def main():
@@ -153,6 +207,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -161,19 +216,25 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    x, ms, nbytes = time_prefill(args)
+    x, ms, per, nbytes = time_prefill(args)
     tok_s = x.B * x.T / (ms * 1e-3)
     ach = nbytes / (ms * 1e-3) / 1e9
+    traffic = stored_traffic()
     rec = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp32", "data": "synthetic",
+        "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "prefill_64k", "B": x.B, "T": x.T, "H": x.H, "dk": x.dk, "dv": x.dv,
-                   "in_dtype": "bf16", "out_dtype": "bf16", "chunk": 64, "initial_state": True},
+                   "in_dtype": "bf16", "out_dtype": "bf16", "chunk": 64, "initial_state": True,
+                   "final_state": True},
+        "ms_median": float(np.median(per)), "ms_p10": float(np.percentile(per, 10)),
+        "ms_p90": float(np.percentile(per, 90)),
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": None,
-                     "alg_bytes_per_launch": nbytes, "kernel": "kda_chunk_fwd (one launch per step)"},
+                     "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
+                     "alg_bytes_per_launch": nbytes,
+                     "kernel": "kda_chunk_fwd: one call = segment table, prep, local scan, "
+                               "combine, output scan (timed together on the library's stream)"},
     }
     if not args.no_decode:
         d = time_decode(args)
