@@ -50,28 +50,30 @@ constexpr int JPW = NJOB / NW;
 
 struct alignas(16) PrepSmem {
     // The operand area comes first: every per-row access to it is one
-    // per-thread base plus an immediate offset below 64 KiB.
+    // per-thread base plus an immediate offset below 64 KiB.  The Gram
+    // operands are dead once the Gram blocks are formed, and everything
+    // after them lives in the same bytes.
     union alignas(16) {
         struct {  // Gram operands of one half of dk, bf16 high/low parts, [row][channel]
             uint16_t rkh[C * HC], rkl[C * HC];   // k_r e^{G_r - m}  (g_off layout)
             uint16_t rqh[C * HC], rql[C * HC];   // q_r e^{G_r - m}
             uint16_t ckh[C * HC], ckl[C * HC];   // k_i e^{m - G_i}
         } g;
-        struct {  // fp16 operands
-            _Float16 ek[C * KP];   // k e^G 2^-ek; later W, swizzled [64][128]
+        struct {
+            _Float16 ek[C * KP];                   // k e^G 2^-ek; later W, swizzled [64][128]
+            float ad[4][16][17];                   // diagonal blocks of A_kk (fp32, true scale)
+            alignas(16) _Float16 akk[6][16 * BP];  // off-diagonal blocks of A_kk, x 2^-2ek
+            alignas(16) _Float16 aqk[10][16 * BP]; // blocks of A_qk (incl. scale), x 2^-(eq+ek)
+            alignas(16) _Float16 tinv[4][16 * BP]; // diagonal blocks of T, x 2^-et
         } s;
-        float gx[C * GP];          // G, for the exact path
     } op;
     float part[8][DK];                     // column sums of g per group of eight rows
     float beta[C];
     alignas(16) float gam[DK];             // exp(G_last) per channel
     int imax[8];                           // |k|, |scale q|, |v|, -, |T|, exact flag, |W|, |U|
-    float ad[4][16][17];                   // diagonal blocks of A_kk (fp32, true scale)
-    alignas(16) _Float16 akk[6][16 * BP];  // off-diagonal blocks of A_kk, x 2^-2ek
-    alignas(16) _Float16 aqk[10][16 * BP]; // blocks of A_qk (incl. scale), x 2^-(eq+ek)
-    alignas(16) _Float16 tinv[4][16 * BP]; // diagonal blocks of T, x 2^-et
 };
-static_assert(sizeof(PrepSmem) <= 80 * 1024, "two workgroups per compute unit");
+// three workgroups per compute unit (160 KiB of LDS, 512-byte allocation granules)
+static_assert(3 * ((sizeof(PrepSmem) + 511) / 512 * 512) <= 160 * 1024, "three workgroups per compute unit");
 
 // block-pair index p -> (a, b), b <= a, in the order (0,0),(1,0),(1,1),(2,0)...
 __device__ __forceinline__ void pair_ab(int p, int &a, int &b) {
@@ -92,7 +94,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // appended to the exact list, and EXACT = true redoes it with the pair-by-pair
 // Gram blocks.  Returns early (whole workgroup) for chunks past the segment end.
 template <bool EXACT>
-__device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const uint16_t *__restrict__ q,
+__device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int h, const uint16_t *__restrict__ q,
                                            const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
                                            const float *__restrict__ g, const uint16_t *__restrict__ beta,
                                            const SegmentView &sv, int per, int H, float scale, char *packs) {
@@ -128,7 +130,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
     float G[2][8][2];  // [half][row][channel]
     uint32_t rk[2][8], rq[2][8];
     {
-        uint32_t mk2 = 0u, mq2 = 0u, mv2 = 0u;
+        uint32_t mk2 = 0u, mq2 = 0u;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             float r0 = 0.f, r1 = 0.f;
@@ -138,14 +140,12 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
                 const u2 gg = ld64(rs_g, 4 * e);
                 rk[hh][m] = ld32(rs_k, 2 * e);
                 rq[hh][m] = ld32(rs_q, 2 * e);
-                const uint32_t vv = ld32(rs_v, 2 * e);
                 r0 += __uint_as_float(gg[0]);
                 r1 += __uint_as_float(gg[1]);
                 G[hh][m][0] = r0;
                 G[hh][m][1] = r1;
                 mk2 = absmax2(mk2, rk[hh][m]);
                 mq2 = absmax2(mq2, rq[hh][m]);
-                mv2 = absmax2(mv2, vv);
             }
             sm.part[rq8][hh * HC + 2 * cq] = r0;
             sm.part[rq8][hh * HC + 2 * cq + 1] = r1;
@@ -153,11 +153,9 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
         if (tid < C) sm.beta[tid] = tid < L ? bf16_to_f32(beta[(c0 + tid) * H + h]) : 0.f;
         const float mk = wave_max(absmax2_value(mk2));
         const float mq = wave_max(absmax2_value(mq2));
-        const float mv = wave_max(absmax2_value(mv2));
         if (lane == 0) {
             atomicMax(&sm.imax[0], __float_as_int(mk));
             atomicMax(&sm.imax[1], __float_as_int(mq * fabsf(scale)));
-            atomicMax(&sm.imax[2], __float_as_int(mv));
         }
     }
     __syncthreads();  // (1)
@@ -184,8 +182,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
         }
     const int ek = exp_of(__int_as_float(sm.imax[0]));
     const int eq = exp_of(__int_as_float(sm.imax[1]));
-    const int ev = exp_of(__int_as_float(sm.imax[2])) - 5;  // U's solve runs below 2^5
-    const float sk = pow2(-ek), sq = pow2(-eq) * scale, svs = pow2(-ev);
+    const float sk = pow2(-ek), sq = pow2(-eq) * scale;
     __syncthreads();  // (2) flag settled
     if constexpr (!EXACT) {
         if (sm.imax[5] != 0) {  // beyond the factored form's range: exact kernel
@@ -198,7 +195,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
     f4 tacc[JPW];
 #pragma unroll
     for (int u = 0; u < JPW; ++u) tacc[u] = zero4();
-    uint32_t ekp[2][8], qsp[2][8], kdp[2][2][4];  // fp16 operand pairs
+    uint32_t ekp[2][8];  // fp16 operand pairs of e^G k, kept for the W solve
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         // per channel: m log2(e) with m = G_L / 2, and e^m times the fp16 scales
@@ -210,6 +207,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
             em_sk[e] = em * sk;
             em_sq[e] = em * sq;
         }
+        uint32_t kdp[2][4];  // rows of e^{G_L - G} k, two per 32 bits, per channel
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const int r = 8 * rq8 + m;
@@ -238,11 +236,12 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
                 }
             }
             ekp[hh][m] = pack_h2(ekv[0], ekv[1]);
-            qsp[hh][m] = pack_h2(qsv[0], qsv[1]);
+            // Q: the channel pair (hh HC + 2cq, +1) of row r is 4 bytes of a 16-byte unit
+            st32(rs_p, pack_h2(qsv[0], qsv[1]), kPkQ + w_col(r, hh * HC + 2 * cq));
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const uint32_t hb = hbits(static_cast<_Float16>(kdv[e]));
-                kdp[hh][e][m >> 1] = (m & 1) ? (kdp[hh][e][m >> 1] | (hb << 16)) : hb;
+                kdp[e][m >> 1] = (m & 1) ? (kdp[e][m >> 1] | (hb << 16)) : hb;
             }
             if constexpr (!EXACT) {
                 uint32_t hi, lo;
@@ -257,6 +256,12 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
                 *reinterpret_cast<uint32_t *>(&sm.op.g.rql[g_off(r, 2 * cq)]) = lo;
             }
         }
+        // KT: four consecutive rows of one channel are 8 contiguous bytes
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                st64(rs_p, u2{kdp[e][2 * t], kdp[e][2 * t + 1]}, kPkKT + kt_col(hh * HC + 2 * cq + e, 8 * rq8 + 4 * t));
         if constexpr (!EXACT) {
             __syncthreads();  // (3a) this half's operands in LDS
 #pragma unroll
@@ -297,10 +302,10 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
                 const int rl4 = 4 * g4 + jj, rr = 16 * a + rl4, ii = 16 * b + n16;
                 if (!isq) {  // A_kk = beta k k^T (decayed), true scale
                     const float vk = ii < rr ? sm.beta[rr] * tacc[u][jj] : 0.f;
-                    if (a == b) sm.ad[a][rl4][n16] = vk;
-                    else sm.akk[offdiag_index(a, b)][rl4 * BP + n16] = static_cast<_Float16>(vk * skk);
+                    if (a == b) sm.op.s.ad[a][rl4][n16] = vk;
+                    else sm.op.s.akk[offdiag_index(a, b)][rl4 * BP + n16] = static_cast<_Float16>(vk * skk);
                 } else {     // A_qk = scale q k^T (decayed)
-                    sm.aqk[p][rl4 * BP + n16] = static_cast<_Float16>(ii <= rr ? tacc[u][jj] * sqk : 0.f);
+                    sm.op.s.aqk[p][rl4 * BP + n16] = static_cast<_Float16>(ii <= rr ? tacc[u][jj] * sqk : 0.f);
                 }
             }
         }
@@ -310,8 +315,8 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
-                sm.op.gx[(8 * rq8 + m) * GP + hh * HC + 2 * cq] = G[hh][m][0];
-                sm.op.gx[(8 * rq8 + m) * GP + hh * HC + 2 * cq + 1] = G[hh][m][1];
+                gx[(8 * rq8 + m) * GP + hh * HC + 2 * cq] = G[hh][m][0];
+                gx[(8 * rq8 + m) * GP + hh * HC + 2 * cq + 1] = G[hh][m][1];
             }
         __syncthreads();
         for (int pr = tid; pr < C * C; pr += NT) {
@@ -321,7 +326,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
             if (rr < L) {
                 const int64_t br = ((c0 + rr) * H + h) * DK, bi = ((c0 + ii) * H + h) * DK;
                 for (int c = 0; c < DK; ++c) {
-                    const float d = __expf(sm.op.gx[rr * GP + c] - sm.op.gx[ii * GP + c]);
+                    const float d = __expf(gx[rr * GP + c] - gx[ii * GP + c]);
                     const float kk = bf16_to_f32(k[bi + c]) * d;
                     vk += bf16_to_f32(k[br + c]) * kk;
                     vq += bf16_to_f32(q[br + c]) * kk;
@@ -329,15 +334,15 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
             }
             const int a = rr >> 4, b = ii >> 4, rl4 = rr & 15, cl = ii & 15;
             const float ak = ii < rr ? sm.beta[rr] * vk : 0.f;
-            if (a == b) sm.ad[a][rl4][cl] = ak;
-            else sm.akk[offdiag_index(a, b)][rl4 * BP + cl] = static_cast<_Float16>(ak * sk * sk);
-            sm.aqk[a * (a + 1) / 2 + b][rl4 * BP + cl] = static_cast<_Float16>(vq * sk * sq);
+            if (a == b) sm.op.s.ad[a][rl4][cl] = ak;
+            else sm.op.s.akk[offdiag_index(a, b)][rl4 * BP + cl] = static_cast<_Float16>(ak * sk * sk);
+            sm.op.s.aqk[a * (a + 1) / 2 + b][rl4 * BP + cl] = static_cast<_Float16>(vq * sk * sq);
         }
         for (int pr = tid; pr < 4 * 256; pr += NT) {  // upper halves of the diagonal blocks
             const int a = pr >> 8, rl4 = (pr >> 4) & 15, cl = pr & 15;
             if (cl > rl4) {
-                sm.ad[a][rl4][cl] = 0.f;
-                sm.aqk[a * (a + 1) / 2 + a][rl4 * BP + cl] = static_cast<_Float16>(0.f);
+                sm.op.s.ad[a][rl4][cl] = 0.f;
+                sm.op.s.aqk[a * (a + 1) / 2 + a][rl4 * BP + cl] = static_cast<_Float16>(0.f);
             }
         }
     }
@@ -361,10 +366,10 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
             float s0 = (r == j) ? 1.f : 0.f, s1 = 0.f;
 #pragma unroll
             for (int i = 0; i + 1 < r; i += 2) {
-                s0 -= sm.ad[a][r][i] * tcol[i];
-                s1 -= sm.ad[a][r][i + 1] * tcol[i + 1];
+                s0 -= sm.op.s.ad[a][r][i] * tcol[i];
+                s1 -= sm.op.s.ad[a][r][i + 1] * tcol[i + 1];
             }
-            if (r & 1) s0 -= sm.ad[a][r][r - 1] * tcol[r - 1];
+            if (r & 1) s0 -= sm.op.s.ad[a][r][r - 1] * tcol[r - 1];
             tcol[r] = s0 + s1;
         }
         float tm = 0.f;
@@ -374,30 +379,29 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
         if (lane == 0) sm.imax[4] = __float_as_int(tm);
     }
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        // Q: the channel pair (hh HC + 2cq, +1) of row r is 4 bytes of 16-byte unit hh*8 + cq/4
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int r = 8 * rq8 + m;
-            *reinterpret_cast<uint32_t *>(&sm.op.s.ek[r * KP + hh * HC + 2 * cq]) = ekp[hh][m];
-            st32(rs_p, qsp[hh][m], kPkQ + w_col(r, hh * HC + 2 * cq));
-        }
-        // KT: four consecutive rows of one channel are 8 contiguous bytes
+        for (int m = 0; m < 8; ++m)
+            *reinterpret_cast<uint32_t *>(&sm.op.s.ek[(8 * rq8 + m) * KP + hh * HC + 2 * cq]) = ekp[hh][m];
+    {   // |v| maximum, from the prefetched values (bf16 magnitudes order as integers)
+        uint32_t mv = 0u;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            // rows 8 rq8 + 4t .. +3 of channel c: 8 bytes each
-            const int c = hh * HC + 2 * cq + e;
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-                st64(rs_p, u2{kdp[hh][e][2 * t], kdp[hh][e][2 * t + 1]}, kPkKT + kt_col(c, 8 * rq8 + 4 * t));
-        }
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) mv = max(mv, vpre[t][a][jj] & 0x7fffu);
+        const float mvf = wave_max(__uint_as_float(mv << 16));
+        if (lane == 0) atomicMax(&sm.imax[2], __float_as_int(mvf));
     }
     __syncthreads();  // (5)
     const int et = exp_of(__int_as_float(sm.imax[4]));
+    const int ev = exp_of(__int_as_float(sm.imax[2])) - 5;  // U's solve runs below 2^5
+    const float svs = pow2(-ev);
     if (wave == 0) {
         const float st = pow2(-et);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sm.tinv[g4][r * BP + n16] = static_cast<_Float16>(tcol[r] * st);
+        for (int r = 0; r < 16; ++r) sm.op.s.tinv[g4][r * BP + n16] = static_cast<_Float16>(tcol[r] * st);
     }
     __syncthreads();  // (6)
 
@@ -427,13 +431,13 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
                 f4 accs = zero4();
 #pragma unroll
                 for (int b = 0; b < a; ++b) {
-                    const h4 aab = *reinterpret_cast<const h4 *>(&sm.akk[offdiag_index(a, b)][n16 * BP + 4 * g4]);
+                    const h4 aab = *reinterpret_cast<const h4 *>(&sm.op.s.akk[offdiag_index(a, b)][n16 * BP + 4 * g4]);
                     accs = mma16(aab, Vh[b], accs);
                 }
                 f4 yv;
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) yv[jj] = xp[jj] - accs[jj] * uns;
-                const h4 ta = *reinterpret_cast<const h4 *>(&sm.tinv[a][n16 * BP + 4 * g4]);
+                const h4 ta = *reinterpret_cast<const h4 *>(&sm.op.s.tinv[a][n16 * BP + 4 * g4]);
                 f4 va = mma16(ta, to_h4(yv, 1.f), zero4());
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) va[jj] *= unt;
@@ -491,7 +495,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
             // 16-byte half `half` of a stored row holds the row's logical half
             // half ^ (row >= 8), its two 8-byte units exchanged in odd blocks
             const int p = u >> 5, row = (u >> 1) & 15, half = u & 1, lh = half ^ (row >> 3);
-            u4 w = *reinterpret_cast<const u4 *>(&sm.aqk[p][row * BP + 8 * lh]);
+            u4 w = *reinterpret_cast<const u4 *>(&sm.op.s.aqk[p][row * BP + 8 * lh]);
             if (p & 1) w = u4{w[2], w[3], w[0], w[1]};
             st128(rs_p, w, kPkA + 16 * u);
         }
@@ -509,27 +513,28 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, int bx, int h, const ui
 }
 
 // fast path: one workgroup per chunk and head; grid (segments x per, heads)
-__global__ void __launch_bounds__(NT, 2)
+__global__ void __launch_bounds__(NT, 3)
 chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                   const uint16_t *__restrict__ v, const float *__restrict__ g,
                   const uint16_t *__restrict__ beta, SegmentView sv, int per, int H, float scale,
                   char *__restrict__ packs) {
     __shared__ PrepSmem sm;
-    prep_chunk<false>(sm, blockIdx.x, blockIdx.y, q, k, v, g, beta, sv, per, H, scale, packs);
+    prep_chunk<false>(sm, nullptr, blockIdx.x, blockIdx.y, q, k, v, g, beta, sv, per, H, scale, packs);
 }
 
 // exact path over the chunks the fast path listed (usually none)
-__global__ void __launch_bounds__(NT, 2)
+__global__ void __launch_bounds__(NT, 1)
 chunk_prep_exact_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                         const uint16_t *__restrict__ v, const float *__restrict__ g,
                         const uint16_t *__restrict__ beta, SegmentView sv, int per, int H, float scale,
                         char *__restrict__ packs) {
     __shared__ PrepSmem sm;
+    __shared__ float gx[C * GP];  // G of the chunk, for the pair-by-pair Gram entries
     const int n = *sv.xcount;
     for (int i = blockIdx.x; i < n; i += gridDim.x) {
         const int id = sv.xlist[i];
         __syncthreads();  // the previous chunk's last LDS reads are done
-        prep_chunk<true>(sm, id / H, id % H, q, k, v, g, beta, sv, per, H, scale, packs);
+        prep_chunk<true>(sm, gx, id / H, id % H, q, k, v, g, beta, sv, per, H, scale, packs);
     }
 }
 

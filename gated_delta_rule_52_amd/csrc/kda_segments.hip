@@ -191,24 +191,26 @@ combine_kernel(SegmentView sv, const float *h0, float *hT, int H, int DV) {
 
 // Combine on fp32 matrix cores (dk = 128): per (sequence, head, 16-column
 // slice of dv), entering(s+1) = P_s entering(s) + H_s, serial over the
-// sequence's segments.  P_s is staged in LDS (row stride padded to 132
-// floats: conflict-free 16-byte reads) and read as the A operand of
-// v_mfma_f32_16x16x4f32; the slice of the state lives in LDS transposed
-// ([column][row]), from which every wave reads it whole as the B operand.
-// Wave w produces row tiles 2w and 2w + 1.  The contraction index of a
-// product runs over (tile t, lane group g, jj) as k = 16 t + 4 g + jj, which
-// is the accumulator layout, so results feed the next step without
-// reshuffling.  The next P and H are fetched into registers while the
-// current product runs.
+// sequence's segments.  Wave w produces row tiles 2w and 2w + 1 with
+// v_mfma_f32_16x16x4f32.  The contraction index of a product runs over
+// (tile t, lane group g, jj) as k = 16 t + 4 g + jj, so that
+// * lane (m, g) takes its A operands for row r straight from HBM as eight
+//   16-byte pieces P[r][16 t + 4 g .. + 3] (no LDS), fetched two segments
+//   ahead into a register ring;
+// * the B operand, the state slice, is read from LDS kept transposed
+//   ([column][row]), and the accumulator layout of a result is exactly that
+//   layout, so each step writes its result back without reshuffling.
+// The state slice alternates between two LDS buffers: one barrier per step.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-constexpr int kCP = 132;  // padded row stride of P in LDS (floats)
+constexpr int kCP = 132;  // padded row stride of the transposed state (floats)
 
 __global__ void __launch_bounds__(256, 1)
 combine_mfma_kernel(SegmentView sv, const float *h0, float *hT, int H, int DV) {
-    constexpr int DK = 128, PV4 = DK * DK / 4 / 256;  // float4 loads per thread for one P
-    __shared__ __attribute__((aligned(16))) float sP[DK * kCP];
-    __shared__ __attribute__((aligned(16))) float sS[16 * kCP];
-    const int slice = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
+    constexpr int DK = 128;
+    __shared__ __attribute__((aligned(16))) float sS[2][16 * kCP];
+    // grid (H, dv / 16, N): the eight slices of head h are workgroups h + H i, all on XCD h mod 8
+    // when H is a multiple of 8, so P_s is read from HBM once per head and then hits in that L2
+    const int h = blockIdx.x, slice = blockIdx.y, n = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, m = lane & 15;
     const int j0 = 16 * slice;
@@ -231,52 +233,64 @@ combine_mfma_kernel(SegmentView sv, const float *h0, float *hT, int H, int DV) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             sin[static_cast<int64_t>(r) * DV + j0 + c8 + e] = x[e];
-            sS[(c8 + e) * kCP + r] = x[e];
+            sS[0][(c8 + e) * kCP + r] = x[e];
         }
     }
-    float4 pn[PV4];
-    f32x4 hn[2];
-    auto fetch = [&](int seg) {
-        const float4 *src = reinterpret_cast<const float4 *>(sv.P + (static_cast<int64_t>(seg) * H + h) * DK * DK);
-#pragma unroll
-        for (int u = 0; u < PV4; ++u) pn[u] = src[tid + 256 * u];
+    const int nsteps = end - first - 1;  // segments whose leaving state is some segment's entering state
+    if (nsteps <= 0) return;
+
+    // operands of one step: P rows 16 (2 wave + ii) + m at columns 16 t + 4 g, and H at the accumulator positions
+    auto fetch = [&](int seg, f32x4 (&pa)[2][8], f32x4 (&hb)[2]) {
+        const float *src = sv.P + (static_cast<int64_t>(seg) * H + h) * DK * DK;
         const float *hs = sv.Hs + (static_cast<int64_t>(seg) * H + h) * DK * DV;
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii)
+        for (int ii = 0; ii < 2; ++ii) {
+            const int r = 16 * (2 * wave + ii) + m;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) pa[ii][t] = *reinterpret_cast<const f32x4 *>(src + r * DK + 16 * t + 4 * g);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-                hn[ii][jj] = hs[static_cast<int64_t>(16 * (2 * wave + ii) + 4 * g + jj) * DV + j0 + m];
-    };
-    if (first + 1 < end) fetch(first);
-    for (int seg = first; seg + 1 < end; ++seg) {
-#pragma unroll
-        for (int u = 0; u < PV4; ++u) {
-            const int e = 4 * (tid + 256 * u), r = e / DK, c = e % DK;
-            *reinterpret_cast<float4 *>(&sP[r * kCP + c]) = pn[u];
+                hb[ii][jj] = hs[static_cast<int64_t>(16 * (2 * wave + ii) + 4 * g + jj) * DV + j0 + m];
         }
-        f32x4 acc[2] = {hn[0], hn[1]};
-        __syncthreads();  // P_s and entering(s) in LDS
-        if (seg + 2 < end) fetch(seg + 1);
+    };
+    // one step: entering(seg + 1) from entering(seg) in sS[b], into sS[b ^ 1]
+    auto step = [&](int seg, int b, const f32x4 (&pa)[2][8], const f32x4 (&hb)[2]) {
+        __syncthreads();  // entering(seg) complete in sS[b]; sS[b ^ 1] no longer read
+        f32x4 acc[2] = {hb[0], hb[1]};
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const f32x4 b = *reinterpret_cast<const f32x4 *>(&sS[m * kCP + 16 * t + 4 * g]);
+            const f32x4 bv = *reinterpret_cast<const f32x4 *>(&sS[b][m * kCP + 16 * t + 4 * g]);
 #pragma unroll
-            for (int ii = 0; ii < 2; ++ii) {
-                const f32x4 a = *reinterpret_cast<const f32x4 *>(&sP[(16 * (2 * wave + ii) + m) * kCP + 16 * t + 4 * g]);
+            for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) acc[ii] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[jj], b[jj], acc[ii], 0, 0, 0);
-            }
+                for (int ii = 0; ii < 2; ++ii)
+                    acc[ii] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[ii][t][jj], bv[jj], acc[ii], 0, 0, 0);
         }
-        __syncthreads();  // all reads of sP and sS done
         float *sin = sv.sin + (static_cast<int64_t>(seg + 1) * H + h) * DK * DV;
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
             const int r0 = 16 * (2 * wave + ii) + 4 * g;
-            *reinterpret_cast<f32x4 *>(&sS[m * kCP + r0]) = acc[ii];
+            *reinterpret_cast<f32x4 *>(&sS[b ^ 1][m * kCP + r0]) = acc[ii];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) sin[static_cast<int64_t>(r0 + jj) * DV + j0 + m] = acc[ii][jj];
         }
+    };
+    // Two segments' operands in flight.  The fetches are unconditional (past the
+    // last step they repeat its segment) so that every path through the loop
+    // has the same memory operations and the wait for a buffer leaves the
+    // other one in flight.
+    const int last_seg = end - 2;
+    f32x4 pA[2][8], pB[2][8], hA[2], hB[2];
+    fetch(first, pA, hA);
+    fetch(min(first + 1, last_seg), pB, hB);
+    int i = 0;
+    for (; i + 1 < nsteps; i += 2) {
+        step(first + i, 0, pA, hA);
+        fetch(min(first + i + 2, last_seg), pA, hA);
+        step(first + i + 1, 1, pB, hB);
+        fetch(min(first + i + 3, last_seg), pB, hB);
     }
+    if (i < nsteps) step(first + i, 0, pA, hA);
 }
 
 }  // namespace
@@ -309,11 +323,12 @@ hipError_t launch_chunk(const ChunkLaunch &L) {
     } else {
         launch_fp32_pass<kLocal>(L, sv, p.max_segs);
     }
-    dim3 cgrid(L.dv / 16, L.H, L.N);
-    if (L.dk == 128)
-        hipLaunchKernelGGL(combine_mfma_kernel, cgrid, dim3(256), 0, L.stream, sv, L.h0, L.hT, L.H, L.dv);
+    if (L.dk == 128)  // heads fastest: a head's slices share one XCD (workgroups go round-robin over XCDs)
+        hipLaunchKernelGGL(combine_mfma_kernel, dim3(L.H, L.dv / 16, L.N), dim3(256), 0, L.stream, sv, L.h0, L.hT,
+                           L.H, L.dv);
     else
-        hipLaunchKernelGGL(combine_kernel<64>, cgrid, dim3(256), 0, L.stream, sv, L.h0, L.hT, L.H, L.dv);
+        hipLaunchKernelGGL(combine_kernel<64>, dim3(L.dv / 16, L.H, L.N), dim3(256), 0, L.stream, sv, L.h0, L.hT,
+                           L.H, L.dv);
     if (p.packs) launch_scan<kOut>(L, sv, p.max_segs, p.per, packs);
     else launch_fp32_pass<kOut>(L, sv, p.max_segs);
     return hipGetLastError();
