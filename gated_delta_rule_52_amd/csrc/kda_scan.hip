@@ -97,20 +97,26 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
                 for (int jj = 0; jj < 4; ++jj)
                     acc[rt][ct][jj] = (pcols && 16 * rt + 4 * g4 + jj == col0 + 16 * ct + n16) ? 1.f : 0.f;
     }
-    // acc[.][ct] holds the state times 2^-fr[ct]: a power-of-two frame that
-    // follows the scale of each chunk's update, so that the update's product
-    // lands in the accumulators without rescaling; smax[ct] = max |acc|
+    // acc[.][ct] holds the state times 2^-fr[ct], a power-of-two frame of the
+    // wave's own, kept so that |acc| stays below 96: the state then feeds the
+    // fp16 products as is.  smax[ct] = max |acc|.
     int fr[NCT];
     float smax[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-        fr[ct] = 0;
         float m = 0.f;
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) m = fmaxf(m, fabsf(acc[rt][ct][jj]));
-        smax[ct] = wave_max(m);
+        m = wave_max(m);
+        fr[ct] = m > 0.f ? exp_of(m) : 0;  // entering state below 1 in its frame
+        const float s = pow2(-fr[ct]);
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) acc[rt][ct][jj] *= s;
+        smax[ct] = m * s;
     }
 
     // o of the segment's tokens: element (t, c) at (t - t0) H DV + c from the
@@ -148,22 +154,17 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
         const int *hdr = reinterpret_cast<const int *>(L + kPkHdr);
         const int ew = hdr[kHdrW], ek = hdr[kHdrK];
         const float *gam = reinterpret_cast<const float *>(L + kPkGamma);
-        int es[NCT];  // the state in fp16 as S 2^-(es + fr), below 1
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) es[ct] = exp_of(smax[ct]);
         // The accumulator layout of two 16-row state tiles is the B operand
         // layout of a 16x16x32 product with a permuted contraction index (see
-        // w_col): the state feeds products as is.
+        // w_col), and |acc| < 96: the state feeds products as is, in fp16.
         h8 sb[NCT][4];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const float s = pow2(-es[ct]);
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                const h4 lo = to_h4(acc[2 * p][ct], s), hi = to_h4(acc[2 * p + 1][ct], s);
+                const h4 lo = to_h4(acc[2 * p][ct], 1.f), hi = to_h4(acc[2 * p + 1][ct], 1.f);
                 sb[ct][p] = h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
-        }
         // X = W S, Y = Q S
         f4 X[NCT][4], Y[NCT][4];
 #pragma unroll
@@ -187,28 +188,45 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
                 }
             }
         }
-        // V_new = U - X (fp32), then an fp16 scale of its own per tile
+        // V_new = U - X (fp32; U = 0 for P), then the frame of the new state:
+        // kept when the update fits it (V_new 2^(ek - fr) within [2^-11, 1])
+        // and the state sits in [2^-6, 32], otherwise moved to the larger of
+        // the update's and the state's scales.  Then |KT_h V_h| <= 64 and
+        // |acc| stays below 96.
         f4 Vn[NCT][4];
         h4 Vh[NCT][4];
-        int evn[NCT];
+        int frn[NCT];
         {
             const float unu = pow2(hdr[kHdrU]);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const float unx = pow2(ew + es[ct] + fr[ct]);
+                const float unx = pow2(ew + fr[ct]);
                 float mv = 0.f;
+                if (pcols) {
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const u4 w = ur_cur[ct][a >> 1];
-                    const h4 uh = __builtin_bit_cast(h4, (a & 1) ? u2{w[2], w[3]} : u2{w[0], w[1]});
+                    for (int a = 0; a < 4; ++a)
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        Vn[ct][a][jj] = static_cast<float>(uh[jj]) * unu - X[ct][a][jj] * unx;
-                        mv = fmaxf(mv, fabsf(Vn[ct][a][jj]));
+                        for (int jj = 0; jj < 4; ++jj) {
+                            Vn[ct][a][jj] = X[ct][a][jj] * -unx;
+                            mv = fmaxf(mv, fabsf(Vn[ct][a][jj]));
+                        }
+                } else {
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const u4 w = ur_cur[ct][a >> 1];
+                        const h4 uh = __builtin_bit_cast(h4, (a & 1) ? u2{w[2], w[3]} : u2{w[0], w[1]});
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            Vn[ct][a][jj] = static_cast<float>(uh[jj]) * unu - X[ct][a][jj] * unx;
+                            mv = fmaxf(mv, fabsf(Vn[ct][a][jj]));
+                        }
                     }
                 }
-                evn[ct] = exp_of(wave_max(mv));
-                const float svn = pow2(-evn[ct]);
+                const int eu = ek + exp_of(wave_max(mv));  // |V_new| 2^ek < 2^eu
+                const float sm = smax[ct];
+                const bool keep = eu <= fr[ct] && fr[ct] <= eu + 10 && sm <= 32.f && sm >= 0.015625f;
+                frn[ct] = keep ? fr[ct] : max(eu, sm > 0.f ? fr[ct] + exp_of(sm) : eu);
+                const float svn = pow2(ek - frn[ct]);  // V_h = V_new 2^(ek - frn)
 #pragma unroll
                 for (int a = 0; a < 4; ++a) Vh[ct][a] = to_h4(Vn[ct][a], svn);
             }
@@ -218,7 +236,7 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
             char *st = ostage[wave];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const float unq = pow2(hdr[kHdrQ] + es[ct] + fr[ct]), una = pow2(hdr[kHdrA] + evn[ct]);
+                const float unq = pow2(hdr[kHdrQ] + fr[ct]), una = pow2(hdr[kHdrA] + frn[ct] - ek);
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
                     f4 oi = zero4();
@@ -248,13 +266,27 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
                 st128(rs_o, w, ob * ((static_cast<uint32_t>(C * j + rr)) * tok_stride + col0) + 16 * un);
             }
         }
-        // a5: S <- gamma S + KT V_new, in the new frame fr' = ek + evn, where
-        // the product KT_h V_h = KT V 2^-(ek + evn) needs no scaling
-        float gsc[NCT];
+        // a5: S <- gamma S + KT V_new in the frame frn, where the product
+        // KT_h V_h = KT V_new 2^-frn needs no scaling
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            gsc[ct] = pow2(fr[ct] - (ek + evn[ct]));
-            fr[ct] = ek + evn[ct];
+            if (frn[ct] == fr[ct]) {
+#pragma unroll
+                for (int rt = 0; rt < 8; ++rt) {
+                    const f4 gm = *reinterpret_cast<const f4 *>(gam + 16 * rt + 4 * g4);
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) acc[rt][ct][jj] *= gm[jj];
+                }
+            } else {
+                const float gsc = pow2(fr[ct] - frn[ct]);
+#pragma unroll
+                for (int rt = 0; rt < 8; ++rt) {
+                    const f4 gm = *reinterpret_cast<const f4 *>(gam + 16 * rt + 4 * g4);
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) acc[rt][ct][jj] *= gm[jj] * gsc;
+                }
+                fr[ct] = frn[ct];
+            }
         }
         float mx[NCT] = {};
         h8 vb[NCT][2];
@@ -267,11 +299,6 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
             }
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) {
-            const f4 gm = *reinterpret_cast<const f4 *>(gam + 16 * rt + 4 * g4);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) acc[rt][ct][jj] *= gm[jj] * gsc[ct];
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
                 const h8 kt = *reinterpret_cast<const h8 *>(L + kPkKT + kt_unit(16 * rt + n16, p, g4));
