@@ -153,16 +153,17 @@ __device__ __forceinline__ void st128(rsrc_t r, u4 v, uint32_t off, int soff = 0
 // ---- per-chunk operand pack (one per chunk and head, written by the prep
 // kernel, streamed by the scan kernels).  Every fp16 matrix carries a
 // power-of-two scale: stored = true value * 2^-e.  The pack is copied into
-// LDS as a straight line; the 16-byte units of the matrices are XOR-swizzled
-// by row so that the scan's 8-byte operand reads (16x16x16 MFMA A operands:
-// lane = 16 g + n reads row n, columns 4g .. 4g + 3) hit distinct banks.
+// LDS as a straight line; the 16-byte units of W, KT and Q are XOR-swizzled
+// by row so that the scan's operand reads hit distinct banks, and the A
+// blocks are stored in the order their 8-byte operand reads go.
 //
 //   [0, 512)        gamma: exp(G_last) per channel, fp32
 //   [512, 1024)     header: int exponents e_w, e_q, e_k, e_u, e_a
 //   W   [64][128]   T beta (e^G k)            A operand of W S       (w_col)
 //   KT  [128][64]   (e^{G_last - G} k)^T      A operand of the update (kt_col)
 //   Q   [64][128]   scale e^G q               A operand of Q S       (w_col)
-//   A   [10][16][16] blocks (a, b), b <= a, of the decayed scale q k^T
+//   A   [10][64][4]  blocks (a, b), b <= a, of the decayed scale q k^T, each in
+//                   lane order: lane 16 g + n holds row n, columns 4g .. 4g + 3
 //   U   T beta v in accumulator order: [16-column tile][row-block pair]
 //                   [lane][row block a, a + 1][row within lane]
 constexpr int kPkGamma = 0;
@@ -198,12 +199,6 @@ __device__ __forceinline__ int kt_col(int r, int c) {  // KT: 8 units a row, row
 // byte offset of the 16-byte A operand unit (step p, lane group g) of row r
 __device__ __forceinline__ int w_unit(int r, int p, int g) { return r * 256 + (((4 * p + g) ^ (r & 15)) << 4); }
 __device__ __forceinline__ int kt_unit(int r, int p, int g) { return r * 128 + (((4 * p + g) ^ ((r >> 1) & 7)) << 4); }
-// A block p, row r, 8-byte unit v (columns 4v .. 4v + 3); the two 8-byte
-// units of each 16-byte half are exchanged in odd blocks (reads of two
-// blocks that the compiler fuses then fall on complementary banks)
-__device__ __forceinline__ int a_off(int p, int r, int v) {
-    return p * 512 + r * 32 + ((v ^ ((r >> 2) & 2) ^ (p & 1)) << 3);
-}
 // byte offset of the 8 bytes of U (tile ct, row block a) that lane `lane` holds
 __device__ __forceinline__ int u_off(int ct, int a, int lane) {
     return ((ct * 2 + (a >> 1)) * 64 + lane) * 16 + (a & 1) * 8;

@@ -44,6 +44,15 @@ __device__ __forceinline__ int g_off(int r, int ch) {  // in halves
 constexpr int KP = DK + 8;  // row stride (halves) of [row][dk] tiles
 constexpr int GP = DK + 4;  // row stride (floats) of [row][dk] fp32 tiles
 constexpr int BP = 16 + 8;  // row stride of 16x16 half blocks
+// Blocks of A in "lane order": lane 16 g + n of a 16x16x16 product's A
+// operand holds row n, columns 4 g .. 4 g + 3, as 4 consecutive halves at
+// 8 lane.  The Gram products are formed transposed (column operand first),
+// so that their accumulators hold exactly these values.
+__device__ __forceinline__ int lane_pos(int row, int col) { return 4 * (row + 16 * (col >> 2)) + (col & 3); }
+// fp32 diagonal blocks of A_kk: rows of 20 floats (16-byte aligned), blocks
+// 324 floats apart (the four blocks a lane group reads fall on different banks)
+constexpr int kAdRow = 20, kAdBlock = 16 * kAdRow + 4;
+__device__ __forceinline__ int ad_off(int a, int r, int c) { return a * kAdBlock + r * kAdRow + c; }
 constexpr float kMaxChunkDecay = 80.0f;
 constexpr int NJOB = 20;    // Gram tile jobs: 10 A_kk block pairs, then 10 A_qk
 constexpr int JPW = NJOB / NW;
@@ -61,10 +70,10 @@ struct alignas(16) PrepSmem {
         } g;
         struct {
             _Float16 ek[C * KP];                   // k e^G 2^-ek; later W, swizzled [64][128]
-            float ad[4][16][17];                   // diagonal blocks of A_kk (fp32, true scale)
-            alignas(16) _Float16 akk[6][16 * BP];  // off-diagonal blocks of A_kk, x 2^-2ek
-            alignas(16) _Float16 aqk[10][16 * BP]; // blocks of A_qk (incl. scale), x 2^-(eq+ek)
-            alignas(16) _Float16 tinv[4][16 * BP]; // diagonal blocks of T, x 2^-et
+            alignas(16) float ad[4 * kAdBlock];     // diagonal blocks of A_kk (fp32, true scale), ad_off
+            alignas(16) _Float16 akk[6][64 * 4];    // off-diagonal blocks of A_kk, x 2^-2ek, in lane order
+            alignas(16) _Float16 aqk[10][64 * 4];   // blocks of A_qk (incl. scale), x 2^-(eq+ek), in lane order
+            alignas(16) _Float16 tinv[4][16 * BP];  // diagonal blocks of T, x 2^-et
         } s;
     } op;
     float part[8][DK];                     // column sums of g per group of eight rows
@@ -159,31 +168,33 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int 
         }
     }
     __syncthreads();  // (1)
+    if (tid < DK) {  // channel tid: exclusive prefix over the row groups; part[0] takes the total
+        float run = 0.f;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const float x = sm.part[p][tid];
+            if (p > 0) sm.part[p][tid] = run;
+            run += x;
+        }
+        sm.part[0][tid] = run;
+        sm.gam[tid] = __expf(run);
+        if (run < -kMaxChunkDecay) atomicOr(&sm.imax[5], 1);
+    }
+    const int ek = exp_of(__int_as_float(sm.imax[0]));
+    const int eq = exp_of(__int_as_float(sm.imax[1]));
+    const float sk = pow2(-ek), sq = pow2(-eq) * scale;
+    __syncthreads();  // (2) prefixes and flag settled
     float GL[2][2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int c = hh * HC + 2 * cq + e;
-            float off = 0.f, tot = 0.f;
-#pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                const float x = sm.part[p][c];
-                off += p < rq8 ? x : 0.f;
-                tot += x;
-            }
+            const float off = rq8 == 0 ? 0.f : sm.part[rq8][c];
 #pragma unroll
             for (int m = 0; m < 8; ++m) G[hh][m][e] += off;
-            GL[hh][e] = tot;
-            if (rq8 == 0) {
-                sm.gam[c] = __expf(tot);
-                if (tot < -kMaxChunkDecay) atomicOr(&sm.imax[5], 1);
-            }
+            GL[hh][e] = sm.part[0][c];
         }
-    const int ek = exp_of(__int_as_float(sm.imax[0]));
-    const int eq = exp_of(__int_as_float(sm.imax[1]));
-    const float sk = pow2(-ek), sq = pow2(-eq) * scale;
-    __syncthreads();  // (2) flag settled
     if constexpr (!EXACT) {
         if (sm.imax[5] != 0) {  // beyond the factored form's range: exact kernel
             if (tid == 0) sv.xlist[atomicAdd(sv.xcount, 1)] = bx * H + h;
@@ -280,9 +291,10 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int 
                     const b8 xl = *reinterpret_cast<const b8 *>(rl + ra);
                     const b8 yh = *reinterpret_cast<const b8 *>(sm.op.g.ckh + cb);
                     const b8 yl = *reinterpret_cast<const b8 *>(sm.op.g.ckl + cb);
-                    tacc[u] = mmab(xh, yh, tacc[u]);
-                    tacc[u] = mmab(xh, yl, tacc[u]);
-                    tacc[u] = mmab(xl, yh, tacc[u]);
+                    // transposed: accumulator (4 g4 + jj, n16) = entry (16 a + n16, 16 b + 4 g4 + jj)
+                    tacc[u] = mmab(yh, xh, tacc[u]);
+                    tacc[u] = mmab(yl, xh, tacc[u]);
+                    tacc[u] = mmab(yh, xl, tacc[u]);
                 }
             }
             __syncthreads();  // (3b) this half's operands consumed
@@ -297,16 +309,18 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int 
             const int p = isq ? j - 10 : j;
             int a, b;
             pair_ab(p, a, b);
+            // this lane's entries: row 16 a + n16, columns 16 b + 4 g4 + jj
+            f4 v = tacc[u];
+            if (!isq) {  // A_kk = beta k k^T (decayed), strictly lower
+                const float br = sm.beta[16 * a + n16];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int rl4 = 4 * g4 + jj, rr = 16 * a + rl4, ii = 16 * b + n16;
-                if (!isq) {  // A_kk = beta k k^T (decayed), true scale
-                    const float vk = ii < rr ? sm.beta[rr] * tacc[u][jj] : 0.f;
-                    if (a == b) sm.op.s.ad[a][rl4][n16] = vk;
-                    else sm.op.s.akk[offdiag_index(a, b)][rl4 * BP + n16] = static_cast<_Float16>(vk * skk);
-                } else {     // A_qk = scale q k^T (decayed)
-                    sm.op.s.aqk[p][rl4 * BP + n16] = static_cast<_Float16>(ii <= rr ? tacc[u][jj] * sqk : 0.f);
-                }
+                for (int jj = 0; jj < 4; ++jj) v[jj] = (a > b || 4 * g4 + jj < n16) ? br * v[jj] : 0.f;
+                if (a == b) *reinterpret_cast<f4 *>(&sm.op.s.ad[ad_off(a, n16, 4 * g4)]) = v;
+                else *reinterpret_cast<h4 *>(&sm.op.s.akk[offdiag_index(a, b)][4 * lane]) = to_h4(v, skk);
+            } else {     // A_qk = scale q k^T (decayed), lower
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) v[jj] = (a > b || 4 * g4 + jj <= n16) ? v[jj] : 0.f;
+                *reinterpret_cast<h4 *>(&sm.op.s.aqk[p][4 * lane]) = to_h4(v, sqk);
             }
         }
     } else {
@@ -334,15 +348,15 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int 
             }
             const int a = rr >> 4, b = ii >> 4, rl4 = rr & 15, cl = ii & 15;
             const float ak = ii < rr ? sm.beta[rr] * vk : 0.f;
-            if (a == b) sm.op.s.ad[a][rl4][cl] = ak;
-            else sm.op.s.akk[offdiag_index(a, b)][rl4 * BP + cl] = static_cast<_Float16>(ak * sk * sk);
-            sm.op.s.aqk[a * (a + 1) / 2 + b][rl4 * BP + cl] = static_cast<_Float16>(vq * sk * sq);
+            if (a == b) sm.op.s.ad[ad_off(a, rl4, cl)] = ak;
+            else sm.op.s.akk[offdiag_index(a, b)][lane_pos(rl4, cl)] = static_cast<_Float16>(ak * sk * sk);
+            sm.op.s.aqk[a * (a + 1) / 2 + b][lane_pos(rl4, cl)] = static_cast<_Float16>(vq * sk * sq);
         }
         for (int pr = tid; pr < 4 * 256; pr += NT) {  // upper halves of the diagonal blocks
             const int a = pr >> 8, rl4 = (pr >> 4) & 15, cl = pr & 15;
             if (cl > rl4) {
-                sm.op.s.ad[a][rl4][cl] = 0.f;
-                sm.op.s.aqk[a * (a + 1) / 2 + a][rl4 * BP + cl] = static_cast<_Float16>(0.f);
+                sm.op.s.ad[ad_off(a, rl4, cl)] = 0.f;
+                sm.op.s.aqk[a * (a + 1) / 2 + a][lane_pos(rl4, cl)] = static_cast<_Float16>(0.f);
             }
         }
     }
@@ -366,10 +380,10 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int 
             float s0 = (r == j) ? 1.f : 0.f, s1 = 0.f;
 #pragma unroll
             for (int i = 0; i + 1 < r; i += 2) {
-                s0 -= sm.op.s.ad[a][r][i] * tcol[i];
-                s1 -= sm.op.s.ad[a][r][i + 1] * tcol[i + 1];
+                s0 -= sm.op.s.ad[ad_off(a, r, i)] * tcol[i];
+                s1 -= sm.op.s.ad[ad_off(a, r, i + 1)] * tcol[i + 1];
             }
-            if (r & 1) s0 -= sm.op.s.ad[a][r][r - 1] * tcol[r - 1];
+            if (r & 1) s0 -= sm.op.s.ad[ad_off(a, r, r - 1)] * tcol[r - 1];
             tcol[r] = s0 + s1;
         }
         float tm = 0.f;
@@ -409,7 +423,9 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int 
     // wave w: column tiles 2w, 2w + 1 of both.  W is formed in the 2^-ek
     // frame of the stored e^G k, U in the 2^-ev frame.  Per row block a:
     //   Y_a = X_a - sum_{b<a} A_ab V_b,  V_a = T_aa Y_a.
-    const float uns = pow2(2 * ek), unt = pow2(et);
+    // V_a below is T_aa Y_a without T's 2^et: the products with it take the
+    // factor in uns, the stored W and U and their maxima in their scales
+    const float unt = pow2(et), uns = pow2(2 * ek) * unt;
     f4 Wr[2][4], Ur[2][4];
     float mw = 0.f, mu = 0.f;
 #pragma unroll
@@ -431,16 +447,14 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int 
                 f4 accs = zero4();
 #pragma unroll
                 for (int b = 0; b < a; ++b) {
-                    const h4 aab = *reinterpret_cast<const h4 *>(&sm.op.s.akk[offdiag_index(a, b)][n16 * BP + 4 * g4]);
+                    const h4 aab = *reinterpret_cast<const h4 *>(&sm.op.s.akk[offdiag_index(a, b)][4 * lane]);
                     accs = mma16(aab, Vh[b], accs);
                 }
                 f4 yv;
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) yv[jj] = xp[jj] - accs[jj] * uns;
                 const h4 ta = *reinterpret_cast<const h4 *>(&sm.op.s.tinv[a][n16 * BP + 4 * g4]);
-                f4 va = mma16(ta, to_h4(yv, 1.f), zero4());
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) va[jj] *= unt;
+                const f4 va = mma16(ta, to_h4(yv, 1.f), zero4());
                 Vh[a] = to_h4(va, 1.f);
                 if (kind == 0) {
                     Wr[t][a] = va;
@@ -454,8 +468,8 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int 
             }
         }
     }
-    mw = wave_max(mw);
-    mu = wave_max(mu);
+    mw = wave_max(mw) * unt;
+    mu = wave_max(mu) * unt;
     if (lane == 0) {
         atomicMax(&sm.imax[6], __float_as_int(mw));
         atomicMax(&sm.imax[7], __float_as_int(mu));
@@ -463,7 +477,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int 
     __syncthreads();  // (7) all reads of e^G k done; its area takes W
     const int ew = exp_of(__int_as_float(sm.imax[6])), eu = exp_of(__int_as_float(sm.imax[7]));
     {
-        const float swv = pow2(-ew), suv = pow2(-eu);
+        const float swv = pow2(-ew) * unt, suv = pow2(-eu) * unt;
         char *wst = reinterpret_cast<char *>(sm.op.s.ek);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -491,14 +505,9 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int 
             const int u = tid + NT * i;  // 0 .. 1023
             st128(rs_p, *reinterpret_cast<const u4 *>(wst + 16 * u), kPkW + 16 * u);
         }
-        for (int u = tid; u < 10 * 16 * 2; u += NT) {  // A_qk blocks, rows of 32 bytes
-            // 16-byte half `half` of a stored row holds the row's logical half
-            // half ^ (row >= 8), its two 8-byte units exchanged in odd blocks
-            const int p = u >> 5, row = (u >> 1) & 15, half = u & 1, lh = half ^ (row >> 3);
-            u4 w = *reinterpret_cast<const u4 *>(&sm.op.s.aqk[p][row * BP + 8 * lh]);
-            if (p & 1) w = u4{w[2], w[3], w[0], w[1]};
-            st128(rs_p, w, kPkA + 16 * u);
-        }
+        for (int u = tid; u < 10 * 64 * 8 / 16; u += NT)  // A_qk blocks, already in lane order
+            st128(rs_p, *reinterpret_cast<const u4 *>(reinterpret_cast<const char *>(sm.op.s.aqk) + 16 * u),
+                  kPkA + 16 * u);
         if (tid < DK / 4)
             st128(rs_p, *reinterpret_cast<const u4 *>(&sm.gam[4 * tid]), kPkGamma + 16 * tid);
         if (tid == 0) {

@@ -242,7 +242,7 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
                     f4 oi = zero4();
 #pragma unroll
                     for (int b = 0; b <= a; ++b) {
-                        const h4 aq = *reinterpret_cast<const h4 *>(L + kPkA + a_off(a * (a + 1) / 2 + b, n16, g4));
+                        const h4 aq = *reinterpret_cast<const h4 *>(L + kPkA + 512 * (a * (a + 1) / 2 + b) + 8 * lane);
                         oi = mma16(aq, Vh[ct][b], oi);
                     }
 #pragma unroll
