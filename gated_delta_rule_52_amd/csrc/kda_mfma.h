@@ -104,22 +104,23 @@ __device__ __forceinline__ h8 acc_to_b32(f4 f0, f4 f1, float s, int lane) {
     return __builtin_bit_cast(h8, (i4{d0, d1, d2, d3}));
 }
 
-// Maximum over the wave, returned wave-uniform: butterfly within each half
-// of the wave by swizzles (the pattern is an immediate, so no lane-index
-// registers), then the two halves' results read as scalars.
-template <int XorMask>
-__device__ __forceinline__ float swz_xor(float x) {
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (XorMask << 10) | 0x1f));
+// Maximum over the wave of non-negative values, returned wave-uniform, by
+// DPP moves on the VALU (no trip through the LDS pipe): shifts within each
+// row of 16 lanes leave the row maximum in its lane 15, two row broadcasts
+// carry it into lane 63.  Lanes a move reads from outside its row range
+// contribute 0, which never raises a maximum of non-negative values.
+template <int Ctrl>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xf, 0xf, true));
 }
 __device__ __forceinline__ float wave_max(float x) {
-    x = fmaxf(x, swz_xor<16>(x));
-    x = fmaxf(x, swz_xor<8>(x));
-    x = fmaxf(x, swz_xor<4>(x));
-    x = fmaxf(x, swz_xor<2>(x));
-    x = fmaxf(x, swz_xor<1>(x));
-    const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
-    const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
-    return fmaxf(lo, hi);
+    x = fmaxf(x, dpp_move<0x111>(x));  // row_shr:1
+    x = fmaxf(x, dpp_move<0x112>(x));  // row_shr:2
+    x = fmaxf(x, dpp_move<0x114>(x));  // row_shr:4
+    x = fmaxf(x, dpp_move<0x118>(x));  // row_shr:8
+    x = fmaxf(x, dpp_move<0x142>(x));  // row_bcast:15
+    x = fmaxf(x, dpp_move<0x143>(x));  // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
 // Buffer resource over [base, base + bytes): raw buffer accesses at or past
