@@ -183,6 +183,28 @@ def time_decode(args):
     return dict(N=N, H=H, dk=dk, dv=dv, steps=steps, us=us, nbytes=decode_alg_bytes(N, H, dk, dv))
 
 
+def copy_ceiling():
+    """HBM bandwidth a plain elementwise kernel reaches on this GPU: 1 GiB read
+    and 1 GiB written per launch (torch's neg kernel), best of 10 launches."""
+    import torch
+    a = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        torch.neg(a, out=b)
+    best = float("inf")
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.neg(a, out=b)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    gbs = 2 * a.numel() * 4 / (best * 1e-3) / 1e9
+    log(f"copy ceiling: {gbs:.0f} GB/s")
+    del a, b
+    return gbs
+
+
 def cpu_baseline(x):
     """The fp64 token-recurrence oracle on the host cores, over the whole
     prefill_64k workload (16 heads x 65,536 tokens: a few seconds)."""
@@ -217,6 +239,7 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     x, ms, per, nbytes = time_prefill(args)
+    copy_gbs = copy_ceiling()
     tok_s = x.B * x.T / (ms * 1e-3)
     ach = nbytes / (ms * 1e-3) / 1e9
     traffic = stored_traffic()
@@ -232,6 +255,7 @@ def main():
         "ms_p90": float(np.percentile(per, 90)),
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
+                     "measured_copy_gbs": copy_gbs, "frac_of_measured_copy": ach / copy_gbs,
                      "alg_bytes_per_launch": nbytes,
                      "kernel": "kda_chunk_fwd: one call = segment table, prep, local scan, "
                                "combine, output scan (timed together on the library's stream)"},
@@ -245,7 +269,8 @@ def main():
             "tokens_per_s": d["N"] / (d["us"] * 1e-6),
             "steps": d["steps"],
             "roofline": {"bound": "hbm", "achieved": dach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": dach / HBM_PEAK_GBS, "alg_bytes_per_launch": d["nbytes"]},
+                         "frac": dach / HBM_PEAK_GBS, "alg_bytes_per_launch": d["nbytes"],
+                         "measured_copy_gbs": copy_gbs, "frac_of_measured_copy": dach / copy_gbs},
         }
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(x)
