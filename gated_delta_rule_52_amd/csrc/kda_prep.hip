@@ -75,14 +75,14 @@ struct alignas(16) PrepSmem {
             alignas(16) _Float16 aqk[10][64 * 4];   // blocks of A_qk (incl. scale), x 2^-(eq+ek), in lane order
             alignas(16) _Float16 tinv[4][16 * BP];  // diagonal blocks of T, x 2^-et
         } s;
+        float part[8][DK];  // column sums of g per group of eight rows (dead before the Gram operands)
     } op;
-    float part[8][DK];                     // column sums of g per group of eight rows
     float beta[C];
     alignas(16) float gam[DK];             // exp(G_last) per channel
     int imax[8];                           // |k|, |scale q|, |v|, -, |T|, exact flag, |W|, |U|
 };
-// three workgroups per compute unit (160 KiB of LDS, 512-byte allocation granules)
-static_assert(3 * ((sizeof(PrepSmem) + 511) / 512 * 512) <= 160 * 1024, "three workgroups per compute unit");
+// three workgroups per compute unit (160 KiB of LDS), with room for coarse allocation granules
+static_assert(3 * (sizeof(PrepSmem) + 2048) <= 160 * 1024, "three workgroups per compute unit");
 
 // block-pair index p -> (a, b), b <= a, in the order (0,0),(1,0),(1,1),(2,0)...
 __device__ __forceinline__ void pair_ab(int p, int &a, int &b) {
@@ -156,8 +156,8 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int 
                 mk2 = absmax2(mk2, rk[hh][m]);
                 mq2 = absmax2(mq2, rq[hh][m]);
             }
-            sm.part[rq8][hh * HC + 2 * cq] = r0;
-            sm.part[rq8][hh * HC + 2 * cq + 1] = r1;
+            sm.op.part[rq8][hh * HC + 2 * cq] = r0;
+            sm.op.part[rq8][hh * HC + 2 * cq + 1] = r1;
         }
         if (tid < C) sm.beta[tid] = tid < L ? bf16_to_f32(beta[(c0 + tid) * H + h]) : 0.f;
         const float mk = wave_max(absmax2_value(mk2));
@@ -172,11 +172,11 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int 
         float run = 0.f;
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
-            const float x = sm.part[p][tid];
-            if (p > 0) sm.part[p][tid] = run;
+            const float x = sm.op.part[p][tid];
+            if (p > 0) sm.op.part[p][tid] = run;
             run += x;
         }
-        sm.part[0][tid] = run;
+        sm.op.part[0][tid] = run;
         sm.gam[tid] = __expf(run);
         if (run < -kMaxChunkDecay) atomicOr(&sm.imax[5], 1);
     }
@@ -190,11 +190,12 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int 
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int c = hh * HC + 2 * cq + e;
-            const float off = rq8 == 0 ? 0.f : sm.part[rq8][c];
+            const float off = rq8 == 0 ? 0.f : sm.op.part[rq8][c];
 #pragma unroll
             for (int m = 0; m < 8; ++m) G[hh][m][e] += off;
-            GL[hh][e] = sm.part[0][c];
+            GL[hh][e] = sm.op.part[0][c];
         }
+    __syncthreads();  // (2b) the sums are read before the operand area takes the Gram operands
     if constexpr (!EXACT) {
         if (sm.imax[5] != 0) {  // beyond the factored form's range: exact kernel
             if (tid == 0) sv.xlist[atomicAdd(sv.xcount, 1)] = bx * H + h;
