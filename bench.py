@@ -150,24 +150,27 @@ def time_decode(args):
     o = torch.empty((steps, N, H, dv), dtype=bf, device=dev)
     lib = _lib.load()
     stream = torch.cuda.current_stream()
-    argv = []
-    for s in range(steps):
-        a = _lib.RecurrentStepArgs()
-        a.struct_size = ctypes.sizeof(_lib.RecurrentStepArgs)
-        a.q, a.k, a.v = q[s].data_ptr(), k[s].data_ptr(), v[s].data_ptr()
-        a.g, a.beta = g[s].data_ptr(), beta[s].data_ptr()
-        a.initial_state = a.final_state = S.data_ptr()
-        a.o = o[s].data_ptr()
-        a.N, a.H, a.dk, a.dv, a.scale = N, H, dk, dv, 1.0
-        a.in_dtype = a.out_dtype = _lib.KDA_DTYPE_BF16
-        a.stream = stream.cuda_stream
-        argv.append(ctypes.byref(a))
-        argv.append(a)
-    refs = argv[0::2]
 
-    def run_all():
-        for r in refs:
-            rc = lib.kda_recurrent_step(r)
+    def make_args(strm):
+        keep = []
+        for s in range(steps):
+            a = _lib.RecurrentStepArgs()
+            a.struct_size = ctypes.sizeof(_lib.RecurrentStepArgs)
+            a.q, a.k, a.v = q[s].data_ptr(), k[s].data_ptr(), v[s].data_ptr()
+            a.g, a.beta = g[s].data_ptr(), beta[s].data_ptr()
+            a.initial_state = a.final_state = S.data_ptr()
+            a.o = o[s].data_ptr()
+            a.N, a.H, a.dk, a.dv, a.scale = N, H, dk, dv, 1.0
+            a.in_dtype = a.out_dtype = _lib.KDA_DTYPE_BF16
+            a.stream = strm.cuda_stream
+            keep.append(a)
+        return keep
+
+    refs = make_args(stream)
+
+    def run_all(args=refs):
+        for a in args:
+            rc = lib.kda_recurrent_step(ctypes.byref(a))
             if rc:
                 _lib.check(rc)
 
@@ -180,7 +183,22 @@ def time_decode(args):
     torch.cuda.synchronize()
     us = 1e3 * e0.elapsed_time(e1) / steps
     log(f"decode: {us:.2f} us/step over {steps} steps")
-    return dict(N=N, H=H, dk=dk, dv=dv, steps=steps, us=us, nbytes=decode_alg_bytes(N, H, dk, dv))
+    # the same steps captured once into a HIP graph and replayed
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.graph(graph, stream=side):
+        run_all(make_args(torch.cuda.current_stream()))
+    graph.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_graph = 1e3 * e0.elapsed_time(e1) / steps
+    log(f"decode under a graph: {us_graph:.2f} us/step")
+    return dict(N=N, H=H, dk=dk, dv=dv, steps=steps, us=us, us_graph=us_graph,
+                nbytes=decode_alg_bytes(N, H, dk, dv))
 
 
 def copy_ceiling():
@@ -264,7 +282,7 @@ def main():
         d = time_decode(args)
         dach = d["nbytes"] / (d["us"] * 1e-6) / 1e9
         rec["decode"] = {
-            "workload": "decode_256x16", "us_per_step": d["us"],
+            "workload": "decode_256x16", "us_per_step": d["us"], "us_per_step_graph": d["us_graph"],
             "us_per_token_step": d["us"], "us_per_token_amortized": d["us"] / d["N"],
             "tokens_per_s": d["N"] / (d["us"] * 1e-6),
             "steps": d["steps"],
