@@ -201,6 +201,49 @@ def time_decode(args):
                 nbytes=decode_alg_bytes(N, H, dk, dv))
 
 
+def append_alg_bytes(N, T, H, dk, dv, in_bytes=2, out_bytes=2):
+    nh = N * H
+    return nh * (2 * dk * dv * 4 + T * ((2 * dk + dv + 1) * in_bytes + dk * 4 + dv * out_bytes))
+
+
+def time_append(args):
+    """Short appends: 256 sequences x 16 heads each take 64 new tokens from a
+    cached state; the fused recurrent path and the chunkwise path side by side."""
+    import torch
+    import gated_delta_rule_52_amd as kda
+    from gated_delta_rule_52_amd.inputs import make_workload
+    x = make_workload("append_256x16x64")
+    dev = "cuda:0"
+    bf, f32 = torch.bfloat16, torch.float32
+    t = lambda a, dt: torch.from_numpy(a).to(dev).to(dt)
+    q, k, v, beta = t(x.q, bf), t(x.k, bf), t(x.v, bf), t(x.beta, bf)
+    g, h0 = t(x.g, f32), t(x.h0, f32)
+    hT = torch.empty_like(h0)
+    o = torch.empty((x.B, x.T, x.H, x.dv), dtype=bf, device=dev)
+    ws = torch.empty(kda.chunk_fwd_workspace_bytes(q, v), dtype=torch.uint8, device=dev)
+    paths = {
+        "recurrent_fwd": lambda: kda.recurrent_fwd(q, k, v, g, beta, initial_state=h0, final_state=hT, o=o,
+                                                   out_dtype=bf),
+        "chunk_fwd": lambda: kda.chunk_fwd(q, k, v, g, beta, initial_state=h0, final_state=hT, o=o,
+                                           out_dtype=bf, workspace=ws),
+    }
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fn in paths.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = 1e3 * e0.elapsed_time(e1) / 10
+        log(f"append_256x16x64 {name}: {res[name]:.1f} us per call")
+    return x, res, append_alg_bytes(x.B, x.T, x.H, x.dk, x.dv)
+
+
 def copy_ceiling():
     """HBM bandwidth a plain elementwise kernel reaches on this GPU: 1 GiB read
     and 1 GiB written per launch (torch's neg kernel), best of 10 launches."""
@@ -289,6 +332,17 @@ def main():
             "roofline": {"bound": "hbm", "achieved": dach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": dach / HBM_PEAK_GBS, "alg_bytes_per_launch": d["nbytes"],
                          "measured_copy_gbs": copy_gbs, "frac_of_measured_copy": dach / copy_gbs},
+        }
+    if not args.no_decode:
+        xa, ra, abytes = time_append(args)
+        best = min(ra, key=ra.get)
+        aach = abytes / (ra[best] * 1e-6) / 1e9
+        rec["append"] = {
+            "workload": "append_256x16x64", "N": xa.B, "T": xa.T, "H": xa.H,
+            "us_per_call": {k: v for k, v in ra.items()}, "path": best,
+            "tokens_per_s": xa.B * xa.T / (ra[best] * 1e-6),
+            "roofline": {"bound": "hbm", "achieved": aach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": aach / HBM_PEAK_GBS, "alg_bytes_per_launch": abytes},
         }
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(x)

@@ -21,7 +21,7 @@ STATUS = {
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 # Every function declared in include/kda.h.
-EXPORTS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step",
+EXPORTS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_fwd", "kda_recurrent_step",
            "kda_status_string", "kda_last_error", "kda_abi_version")
 
 vp = ctypes.c_void_p
@@ -76,6 +76,8 @@ def load():
         lib.kda_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(ChunkFwdArgs)]
         lib.kda_chunk_fwd.restype = ctypes.c_int
         lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(ChunkFwdArgs)]
+        lib.kda_recurrent_fwd.restype = ctypes.c_int
+        lib.kda_recurrent_fwd.argtypes = [ctypes.POINTER(ChunkFwdArgs)]
         lib.kda_recurrent_step.restype = ctypes.c_int
         lib.kda_recurrent_step.argtypes = [ctypes.POINTER(RecurrentStepArgs)]
         lib.kda_status_string.restype = ctypes.c_char_p
@@ -101,6 +103,11 @@ def chunk_fwd_raw(args: ChunkFwdArgs) -> int:
 def chunk_workspace_raw(args: ChunkFwdArgs) -> int:
     args.struct_size = ctypes.sizeof(ChunkFwdArgs)
     return load().kda_chunk_fwd_workspace_bytes(ctypes.byref(args))
+
+
+def recurrent_fwd_raw(args: ChunkFwdArgs) -> int:
+    args.struct_size = ctypes.sizeof(ChunkFwdArgs)
+    return load().kda_recurrent_fwd(ctypes.byref(args))
 
 
 def recurrent_step_raw(args: RecurrentStepArgs) -> int:

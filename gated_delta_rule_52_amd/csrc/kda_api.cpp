@@ -71,6 +71,35 @@ kda_status check_chunk_sizes(const kda_chunk_fwd_args *a) {
     return KDA_OK;
 }
 
+// Checks of the prefill-style arguments that kda_chunk_fwd and
+// kda_recurrent_fwd share: pointers, output aliasing, sizes.
+kda_status check_prefill_buffers(const kda_chunk_fwd_args *a) {
+    const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
+    const int N = a->num_seqs;
+    if (tokens > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o))
+        return fail(KDA_ERR_NULL_POINTER, "q, k, v, g, beta and o are required");
+    const size_t th = static_cast<size_t>(tokens) * a->H;
+    const size_t in_sz = dsize(a->in_dtype);
+    const Range ro = range_of(a->o, th * a->dv * dsize(a->out_dtype));
+    const Range ins[] = {range_of(a->q, th * a->dk * in_sz), range_of(a->k, th * a->dk * in_sz),
+                         range_of(a->v, th * a->dv * in_sz), range_of(a->g, th * a->dk * 4),
+                         range_of(a->beta, th * in_sz)};
+    const size_t sbytes = static_cast<size_t>(N) * a->H * a->dk * a->dv * 4;
+    for (const Range &r : ins)
+        if (overlap(ro, r)) return fail(KDA_ERR_ALIAS, "o overlaps an input");
+    if (a->final_state) {
+        const Range rf = range_of(a->final_state, sbytes);
+        for (const Range &r : ins)
+            if (overlap(rf, r)) return fail(KDA_ERR_ALIAS, "final_state overlaps an input");
+        if (overlap(rf, ro)) return fail(KDA_ERR_ALIAS, "final_state overlaps o");
+        if (a->initial_state && a->initial_state != a->final_state &&
+            overlap(rf, range_of(a->initial_state, sbytes)))
+            return fail(KDA_ERR_ALIAS, "final_state partially overlaps initial_state");
+    }
+    if (N > 65535 || a->H > 65535) return fail(KDA_ERR_UNSUPPORTED, "N=%d H=%d (at most 65535 each)", N, a->H);
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,11 +132,12 @@ kda_status kda_chunk_fwd(const kda_chunk_fwd_args *a) {
     g_last_error.clear();
     kda_status st = check_chunk_sizes(a);
     if (st != KDA_OK) return st;
+    st = check_prefill_buffers(a);
+    if (st != KDA_OK) return st;
     const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
     const int N = a->num_seqs;
-    if (tokens > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o))
-        return fail(KDA_ERR_NULL_POINTER, "q, k, v, g, beta and o are required");
-    // The output must not overlap any input.
+    if (N == 0 || (tokens == 0 && !a->final_state)) return KDA_OK;
+    // the workspace must not overlap any input or output
     const size_t th = static_cast<size_t>(tokens) * a->H;
     const size_t in_sz = dsize(a->in_dtype);
     const Range ro = range_of(a->o, th * a->dv * dsize(a->out_dtype));
@@ -115,19 +145,6 @@ kda_status kda_chunk_fwd(const kda_chunk_fwd_args *a) {
                          range_of(a->v, th * a->dv * in_sz), range_of(a->g, th * a->dk * 4),
                          range_of(a->beta, th * in_sz)};
     const size_t sbytes = static_cast<size_t>(N) * a->H * a->dk * a->dv * 4;
-    for (const Range &r : ins)
-        if (overlap(ro, r)) return fail(KDA_ERR_ALIAS, "o overlaps an input");
-    if (a->final_state) {
-        const Range rf = range_of(a->final_state, sbytes);
-        for (const Range &r : ins)
-            if (overlap(rf, r)) return fail(KDA_ERR_ALIAS, "final_state overlaps an input");
-        if (overlap(rf, ro)) return fail(KDA_ERR_ALIAS, "final_state overlaps o");
-        if (a->initial_state && a->initial_state != a->final_state &&
-            overlap(rf, range_of(a->initial_state, sbytes)))
-            return fail(KDA_ERR_ALIAS, "final_state partially overlaps initial_state");
-    }
-    if (N == 0 || (tokens == 0 && !a->final_state)) return KDA_OK;
-    if (N > 65535 || a->H > 65535) return fail(KDA_ERR_UNSUPPORTED, "N=%d H=%d (at most 65535 each)", N, a->H);
     const size_t need = kda::chunk_workspace_bytes(a->B, a->T, a->H, a->dk, a->dv, N, a->chunk_size,
                                                    a->cu_seqlens != nullptr, a->in_dtype == KDA_DTYPE_BF16);
     if (a->workspace_bytes < need || (need > 0 && !a->workspace))
@@ -154,6 +171,38 @@ kda_status kda_chunk_fwd(const kda_chunk_fwd_args *a) {
     L.workspace = a->workspace; L.workspace_bytes = a->workspace_bytes;
     L.stream = static_cast<hipStream_t>(a->stream);
     return hip_status(kda::launch_chunk(L), "kda_chunk_fwd launch");
+}
+
+kda_status kda_recurrent_fwd(const kda_chunk_fwd_args *a) {
+    g_last_error.clear();
+    if (!a) return fail(KDA_ERR_NULL_POINTER, "args is NULL");
+    if (a->struct_size != sizeof(kda_chunk_fwd_args))
+        return fail(KDA_ERR_BAD_STRUCT, "struct_size %u != %zu", a->struct_size, sizeof(kda_chunk_fwd_args));
+    if (a->B < 0 || a->T < 0 || a->H <= 0 || a->num_seqs < 0)
+        return fail(KDA_ERR_BAD_SHAPE, "B=%d T=%d H=%d num_seqs=%d", a->B, a->T, a->H, a->num_seqs);
+    if (!valid_dim(a->dk) || !valid_dim(a->dv))
+        return fail(KDA_ERR_UNSUPPORTED, "dk=%d dv=%d (supported: 64, 128)", a->dk, a->dv);
+    if (!valid_dtype(a->in_dtype) || !valid_dtype(a->out_dtype))
+        return fail(KDA_ERR_UNSUPPORTED, "in_dtype=%d out_dtype=%d", a->in_dtype, a->out_dtype);
+    if (!std::isfinite(a->scale)) return fail(KDA_ERR_BAD_SHAPE, "scale is not finite");
+    if (a->cu_seqlens ? a->B != 1 : a->num_seqs != a->B)
+        return fail(KDA_ERR_BAD_SHAPE, "num_seqs=%d with B=%d (%s)", a->num_seqs, a->B,
+                    a->cu_seqlens ? "packed input needs B = 1" : "num_seqs must equal B");
+    kda_status st = check_prefill_buffers(a);
+    if (st != KDA_OK) return st;
+    const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
+    if (a->num_seqs == 0 || (tokens == 0 && !a->final_state)) return KDA_OK;
+
+    kda::RecurrentLaunch L{};
+    L.q = a->q; L.k = a->k; L.v = a->v; L.g = a->g; L.beta = a->beta;
+    L.h0 = a->initial_state; L.hT = a->final_state; L.o = a->o;
+    L.cu_seqlens = a->cu_seqlens;
+    L.N = a->num_seqs; L.T = a->T; L.H = a->H; L.dk = a->dk; L.dv = a->dv; L.scale = a->scale;
+    L.in_bf16 = a->in_dtype == KDA_DTYPE_BF16;
+    L.out_bf16 = a->out_dtype == KDA_DTYPE_BF16;
+    L.multi_token = true;
+    L.stream = static_cast<hipStream_t>(a->stream);
+    return hip_status(kda::launch_recurrent(L), "kda_recurrent_fwd launch");
 }
 
 kda_status kda_recurrent_step(const kda_recurrent_step_args *a) {

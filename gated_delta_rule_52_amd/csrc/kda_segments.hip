@@ -44,8 +44,15 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int N, int chunk, bool varle
     const int64_t chunks = varlen ? (tokens + chunk - 1) / chunk + N
                                   : static_cast<int64_t>(B) * ((T + chunk - 1) / chunk);
     int64_t per = (chunks * H + kTargetUnits - 1) / kTargetUnits;
-    if (per < 1) per = 1;
     if (per > 64) per = 64;
+    // Segments never span two sequences, so a segment longer than the
+    // sequences only pads the pack array (and the prep grid) with empty
+    // slots: cap it at the sequence length, or for packed input at the
+    // average sequence length (the lengths themselves live on the device).
+    const int64_t seq_chunks = varlen ? (tokens + static_cast<int64_t>(chunk) * N - 1) / (static_cast<int64_t>(chunk) * (N > 0 ? N : 1))
+                                      : (T + chunk - 1) / chunk;
+    if (per > seq_chunks) per = seq_chunks;
+    if (per < 1) per = 1;
     p.per = static_cast<int>(per);
     p.seg_len = p.per * chunk;
     p.max_segs = varlen ? static_cast<int>((tokens + p.seg_len - 1) / p.seg_len + N)

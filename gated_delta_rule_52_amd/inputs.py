@@ -210,6 +210,8 @@ WORKLOADS = {
                         in_dtype="bf16", gscale=1.0, h0_std=0.02),
     "decode_256x16": dict(kind="decode", seed=3, N=256, H=16, dk=128, dv=128,
                           in_dtype="bf16", gscale=1.0, steps=1024, pool=32, state_std=0.02),
+    "append_256x16x64": dict(kind="prefill", seed=5, B=256, T=64, H=16, dk=128, dv=128,
+                             in_dtype="bf16", gscale=1.0, h0_std=0.02),
     "varlen_8seq": dict(kind="prefill", seed=4, B=1, T=None, H=32, dk=128, dv=128,
                         in_dtype="bf16", gscale=0.01, h0_std=0.02,
                         lengths_range=(1024, 32768), n_seqs=8),

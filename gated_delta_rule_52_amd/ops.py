@@ -116,6 +116,45 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     return o, final_state
 
 
+def recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                  cu_seqlens: Optional[torch.Tensor] = None, scale: float = 1.0,
+                  out_dtype: Optional[torch.dtype] = None, output_final_state: bool = True,
+                  final_state: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Token-by-token fused recurrent forward for short segments (at most a few
+    dozen tokens per sequence): the same arguments, shapes and results as
+    ``chunk_fwd`` (no chunk size, no workspace).  Returns (o, final_state)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported input dtype {dt}")
+    _need(q, "q", (B, T, H, dk), dt)
+    _need(k, "k", (B, T, H, dk), dt)
+    _need(v, "v", (B, T, H, dv), dt)
+    _need(g, "g", (B, T, H, dk), torch.float32)
+    _need(beta, "beta", (B, T, H), dt)
+    N = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32)
+        N = cu_seqlens.numel() - 1
+    if initial_state is not None:
+        _need(initial_state, "initial_state", (N, H, dk, dv), torch.float32)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif final_state is not None:
+        _need(final_state, "final_state", (N, H, dk, dv), torch.float32)
+    od = out_dtype or dt
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=od, device=q.device)
+    else:
+        _need(o, "o", (B, T, H, dv), od)
+    a = _fill_chunk_args(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, scale, 64)
+    _lib.check(_lib.recurrent_fwd_raw(a))
+    return o, final_state
+
+
 def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                    beta: torch.Tensor, state: Optional[torch.Tensor],
                    final_state: Optional[torch.Tensor] = None, scale: float = 1.0,

@@ -119,6 +119,23 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_fwd_args *args);
 kda_status kda_chunk_fwd(const kda_chunk_fwd_args *args);
 
 /*
+ * Multi-token fused recurrent forward (Kimi Linear review notes, section
+ * "Training and Inference": segments of at most 64 tokens, as well as single
+ * decode steps, go to the fused recurrent kernel, which keeps the recurrent
+ * state in registers for the whole segment).  The same recurrence as
+ * kda_chunk_fwd, computed token by token in order: per (sequence, head,
+ * 32-column slice of dv) one workgroup reads its state slice once, applies
+ * every token of the sequence, and writes the slice once.  Meant for short
+ * appends (speculative decoding, chunked prompt appends); kda_chunk_fwd is the
+ * faster choice once sequences are long.
+ *
+ * Arguments, shapes, dtypes, aliasing rules and errors are those of
+ * kda_chunk_fwd; chunk_size, workspace and workspace_bytes are ignored (no
+ * workspace is used).
+ */
+kda_status kda_recurrent_fwd(const kda_chunk_fwd_args *args);
+
+/*
  * One recurrent decode step for N independent sequences (Kimi Linear review
  * notes, section "Training and Inference": the fused recurrent kernel serves
  * single steps and keeps the fixed-size recurrent state in the cache).

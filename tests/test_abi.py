@@ -70,6 +70,24 @@ def test_chunk_fwd_rejects(kw, status):
     assert _lib.load().kda_last_error().decode() != ""
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=96), "KDA_ERR_UNSUPPORTED"),
+    (dict(out_dtype=7), "KDA_ERR_UNSUPPORTED"),
+    (dict(H=0), "KDA_ERR_BAD_SHAPE"),
+    (dict(num_seqs=2), "KDA_ERR_BAD_SHAPE"),
+    (dict(B=2, num_seqs=2, cu_seqlens=8 * FAKE), "KDA_ERR_BAD_SHAPE"),
+    (dict(scale=float("inf")), "KDA_ERR_BAD_SHAPE"),
+    (dict(v=None), "KDA_ERR_NULL_POINTER"),
+    (dict(o=2 * FAKE + 8), "KDA_ERR_ALIAS"),
+    (dict(final_state=6 * FAKE + 8), "KDA_ERR_ALIAS"),
+])
+def test_recurrent_fwd_rejects(kw, status):
+    # the same argument rules as kda_chunk_fwd; chunk_size and workspace are ignored
+    rc = _lib.recurrent_fwd_raw(chunk_args(chunk_size=48, **kw))
+    assert rc == S[status], (_lib.STATUS.get(rc), _lib.load().kda_last_error())
+    assert _lib.load().kda_last_error().decode() != ""
+
+
 def test_chunk_struct_size_is_checked():
     a = chunk_args()
     a.struct_size = ctypes.sizeof(_lib.ChunkFwdArgs) - 8
@@ -114,3 +132,4 @@ def test_empty_problems_are_no_ops():
     # nothing to do: returns before any HIP call
     assert _lib.recurrent_step_raw(step_args(N=0)) == 0
     assert _lib.chunk_fwd_raw(chunk_args(B=0, num_seqs=0)) == 0
+    assert _lib.recurrent_fwd_raw(chunk_args(B=0, num_seqs=0)) == 0
