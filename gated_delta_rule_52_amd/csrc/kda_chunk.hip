@@ -92,10 +92,10 @@ chunk_fp32_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
 
     // ---- entering state slice -> LDS
     if (MODE == kOut) {
-        const float *src = sv.sin + (static_cast<int64_t>(seg) * H + h) * DK * DV;
+        const float *src = sv.entering(seg, sd, h, H, DK, DV);
         for (int e = tid; e < DK * BV; e += 256) {
             const int i = e / BV, j = e % BV;
-            sS[i * BVP + j] = src[static_cast<int64_t>(i) * DV + j0 + j];
+            sS[i * BVP + j] = src ? src[static_cast<int64_t>(i) * DV + j0 + j] : 0.f;
         }
     } else {
         for (int e = tid; e < DK * BV; e += 256) {

@@ -68,10 +68,21 @@ struct SegmentView {
     int N;
     float *P;               // [max_segs, H, dk, dk]
     float *Hs;              // [max_segs, H, dk, dv]
-    float *sin;             // [max_segs, H, dk, dv] entering states
+    float *sin;             // [max_segs, H, dk, dv] entering states (not filled for one-segment sequences)
+    const float *h0;        // [N, H, dk, dv] initial states (null: zero)
     int *xlist;             // chunks (pack numbers) the matrix-core prep hands to its exact path
     int *xcount;            // their count (zeroed by the segment-table kernel)
     __device__ __forceinline__ int count() const { return seq_seg[N]; }
+    // the entering state of segment seg = {sequence, first token, end token, flags} at head h, row-major
+    // dk x dv; null stands for the zero state.  A sequence of one segment enters with its initial state,
+    // read in place: the workgroup that reads it is the one that later writes the final state, which may
+    // alias it.  Longer sequences read a copy, because their last segment may finish before the first
+    // has read its entering state.
+    __device__ __forceinline__ const float *entering(int seg, int4 sd, int h, int H, int DK, int DV) const {
+        if ((sd.w & (kSegFirst | kSegLast)) == (kSegFirst | kSegLast))
+            return h0 ? h0 + (static_cast<int64_t>(sd.x) * H + h) * DK * DV : nullptr;
+        return sin + (static_cast<int64_t>(seg) * H + h) * DK * DV;
+    }
 };
 
 template <int MODE>

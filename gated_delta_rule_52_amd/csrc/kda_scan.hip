@@ -80,7 +80,9 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     auto st_off = [](int rt, int ct, int jj) { return 4 * ((16 * rt + jj) * 128 + 16 * ct); };
     f4 acc[8][NCT];
     if (kOutPass) {
-        const rsrc_t rs = make_rsrc(sv.sin + (static_cast<int64_t>(seg) * H + h) * DK * DV, 4 * DK * DV);
+        // a zero-sized resource reads zeros: the zero initial state
+        const float *src = sv.entering(seg, sd, h, H, DK, DV);
+        const rsrc_t rs = make_rsrc(src, src ? 4 * DK * DV : 0);
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll

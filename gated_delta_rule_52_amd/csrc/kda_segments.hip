@@ -130,6 +130,8 @@ build_segments_kernel(const int32_t *__restrict__ cu_seqlens, int T, int N, int 
 
 // Combine: per (sequence, head, 16-column slice of dv), walk the segments in
 // order, store each entering state and advance it by  S <- P_s S + H_s.
+// Sequences of one segment are skipped: their output pass reads the initial
+// state itself.
 // P_s (dk x dk fp32) is staged in LDS; the next one is fetched into registers
 // while the current product runs.  fp32 FMA throughout.
 template <int DK>
@@ -143,6 +145,7 @@ combine_kernel(SegmentView sv, const float *h0, float *hT, int H, int DV) {
     const int tid = threadIdx.x, j = tid % BV, ig = tid / BV;
     const int j0 = slice * BV;
     const int first = sv.seq_seg[n], end = sv.seq_seg[n + 1];
+    if (end - first == 1) return;  // one segment: nothing to carry
     const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * DV;
 
     float s[ROWS];
@@ -222,6 +225,8 @@ combine_mfma_kernel(SegmentView sv, const float *h0, float *hT, int H, int DV) {
     const int g = lane >> 4, m = lane & 15;
     const int j0 = 16 * slice;
     const int first = sv.seq_seg[n], end = sv.seq_seg[n + 1];
+    const int nsteps = end - first - 1;  // segments whose leaving state is some segment's entering state
+    if (nsteps == 0) return;             // one segment: nothing to carry
     const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * DV;
 
     // entering state of the first segment: thread (row tid / 2, 8 columns)
@@ -243,8 +248,6 @@ combine_mfma_kernel(SegmentView sv, const float *h0, float *hT, int H, int DV) {
             sS[0][(c8 + e) * kCP + r] = x[e];
         }
     }
-    const int nsteps = end - first - 1;  // segments whose leaving state is some segment's entering state
-    if (nsteps <= 0) return;
 
     // operands of one step: P rows 16 (2 wave + ii) + m at columns 16 t + 4 g, and H at the accumulator positions
     auto fetch = [&](int seg, f32x4 (&pa)[2][8], f32x4 (&hb)[2]) {
@@ -317,6 +320,7 @@ hipError_t launch_chunk(const ChunkLaunch &L) {
     sv.P = reinterpret_cast<float *>(ws + p.off_P);
     sv.Hs = reinterpret_cast<float *>(ws + p.off_H);
     sv.sin = reinterpret_cast<float *>(ws + p.off_S);
+    sv.h0 = L.h0;
     sv.xcount = p.packs ? reinterpret_cast<int *>(ws + p.off_xlist) : nullptr;
     sv.xlist = p.packs ? sv.xcount + 1 : nullptr;
 
