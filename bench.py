@@ -7,7 +7,7 @@ inter-chunk state propagation, output) runs inside that call.  Inputs are
 drawn on the host, copied to HBM once, and are resident when timing starts.
 Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-append] [--no-cpu]
                     [--calibrate-copy]
 
 --calibrate-copy adds, before the timed region, one elementwise copy kernel
@@ -288,7 +288,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode and append lines")
+    ap.add_argument("--no-append", action="store_true", help="skip the append line")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -333,7 +334,7 @@ def main():
                          "frac": dach / HBM_PEAK_GBS, "alg_bytes_per_launch": d["nbytes"],
                          "measured_copy_gbs": copy_gbs, "frac_of_measured_copy": dach / copy_gbs},
         }
-    if not args.no_decode:
+    if not (args.no_decode or args.no_append):
         xa, ra, abytes = time_append(args)
         best = min(ra, key=ra.get)
         aach = abytes / (ra[best] * 1e-6) / 1e9
