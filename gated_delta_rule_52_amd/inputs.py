@@ -15,6 +15,12 @@ alpha = exp(g); L2-normalised queries and keys):
   long-retention workload), softplus(x) = log1p(exp(-|x|)) + max(x, 0);
 * optional initial state h0 ~ N(0, 0.02^2) (standard deviation 0.02).
 
+With ``fused=True`` the same draws are returned before the last two steps,
+for kernels that apply them themselves: q and k are left unnormalised
+(bf16-rounded N(0, 1) draws) and ``g`` holds the gate logits z ~ N(0, 1),
+the log-gate being -gscale * softplus(z).  ``transforms()`` names what the
+consumer must then apply.
+
 bf16 inputs are rounded once, round-to-nearest-even, and returned as float32
 arrays that hold the exact bf16 values, so converting them to bf16 on the
 device is lossless and the oracle sees exactly what the GPU sees.
@@ -84,6 +90,14 @@ class KdaInputs:
     in_dtype: str
     name: str = ""
     meta: dict = field(default_factory=dict)
+    fused: bool = False  # q, k unnormalised and g = gate logits (see module docstring)
+
+    def transforms(self) -> dict:
+        """Input transforms the consumer applies: none, or for ``fused``
+        inputs the in-kernel L2 norm and the softplus gate with its scale."""
+        if not self.fused:
+            return dict(qk_l2norm=False, gate_logits=False, gate_scale=1.0)
+        return dict(qk_l2norm=True, gate_logits=True, gate_scale=float(self.meta["gscale"]))
 
     @property
     def B(self) -> int:
@@ -126,7 +140,7 @@ def make_prefill(seed: int, B: int, T: int, H: int, dk: int, dv: int,
                  h0_std: Optional[float] = None,
                  seqlens: Optional[np.ndarray] = None,
                  lengths_range: Optional[tuple] = None, n_seqs: int = 0,
-                 name: str = "") -> KdaInputs:
+                 name: str = "", fused: bool = False) -> KdaInputs:
     """Draw one prefill problem.
 
     For packed variable-length input either pass ``seqlens`` or
@@ -153,14 +167,14 @@ def make_prefill(seed: int, B: int, T: int, H: int, dk: int, dv: int,
     h0 = None
     if h0_std is not None:
         h0 = (h0_std * rng.standard_normal((N, H, dk, dv), dtype=f32)).astype(f32)
-    q = _maybe_bf16(l2_normalise(q), in_dtype)
-    k = _maybe_bf16(l2_normalise(k), in_dtype)
+    q = _maybe_bf16(q if fused else l2_normalise(q), in_dtype)
+    k = _maybe_bf16(k if fused else l2_normalise(k), in_dtype)
     v = _maybe_bf16(v, in_dtype)
     beta = _maybe_bf16(sigmoid(bl), in_dtype)
-    g = (-np.float32(gscale) * softplus(gl)).astype(f32)
+    g = gl if fused else (-np.float32(gscale) * softplus(gl)).astype(f32)
     return KdaInputs(q=q, k=k, v=v, g=g, beta=beta, h0=h0, cu_seqlens=cu,
                      in_dtype=in_dtype, name=name,
-                     meta=dict(seed=seed, gscale=gscale, h0_std=h0_std))
+                     meta=dict(seed=seed, gscale=gscale, h0_std=h0_std), fused=fused)
 
 
 def make_decode_state(seed: int, N: int, H: int, dk: int, dv: int,
@@ -172,8 +186,9 @@ def make_decode_state(seed: int, N: int, H: int, dk: int, dv: int,
 
 
 def decode_steps(rng, steps: int, N: int, H: int, dk: int, dv: int,
-                 in_dtype: str = "bf16", gscale: float = 1.0) -> Iterator[dict]:
-    """Yield one token per sequence per step: q, k, g [N,H,dk]; v [N,H,dv]; beta [N,H]."""
+                 in_dtype: str = "bf16", gscale: float = 1.0, fused: bool = False) -> Iterator[dict]:
+    """Yield one token per sequence per step: q, k, g [N,H,dk]; v [N,H,dv]; beta [N,H].
+    ``fused`` as for make_prefill: q, k unnormalised and g the gate logits."""
     f32 = np.float32
     for _ in range(steps):
         q = rng.standard_normal((N, H, dk), dtype=f32)
@@ -181,20 +196,20 @@ def decode_steps(rng, steps: int, N: int, H: int, dk: int, dv: int,
         v = rng.standard_normal((N, H, dv), dtype=f32)
         bl = rng.standard_normal((N, H), dtype=f32)
         gl = rng.standard_normal((N, H, dk), dtype=f32)
-        yield dict(q=_maybe_bf16(l2_normalise(q), in_dtype),
-                   k=_maybe_bf16(l2_normalise(k), in_dtype),
+        yield dict(q=_maybe_bf16(q if fused else l2_normalise(q), in_dtype),
+                   k=_maybe_bf16(k if fused else l2_normalise(k), in_dtype),
                    v=_maybe_bf16(v, in_dtype),
                    beta=_maybe_bf16(sigmoid(bl), in_dtype),
-                   g=(-f32(gscale) * softplus(gl)).astype(f32))
+                   g=gl if fused else (-f32(gscale) * softplus(gl)).astype(f32))
 
 
 def decode_step_pool(rng, pool: int, N: int, H: int, dk: int, dv: int,
-                     in_dtype: str = "bf16", gscale: float = 1.0) -> dict:
+                     in_dtype: str = "bf16", gscale: float = 1.0, fused: bool = False) -> dict:
     """Draw ``pool`` token batches for the decode workload, stacked on a
     leading axis: q, k, g [pool,N,H,dk]; v [pool,N,H,dv]; beta [pool,N,H].
     Step s of a long decode run uses batch s % pool (each step still reads
     its own copy at its own device offset)."""
-    steps = list(decode_steps(rng, pool, N, H, dk, dv, in_dtype, gscale))
+    steps = list(decode_steps(rng, pool, N, H, dk, dv, in_dtype, gscale, fused))
     return {k: np.stack([s[k] for s in steps]) for k in steps[0]}
 
 
@@ -208,6 +223,9 @@ WORKLOADS = {
                        in_dtype="bf16", gscale=1.0, h0_std=None),
     "prefill_64k": dict(kind="prefill", seed=2, B=1, T=65536, H=16, dk=128, dv=128,
                         in_dtype="bf16", gscale=1.0, h0_std=0.02),
+    # the same problem handed over before the L2 norm and the gate activation
+    "prefill_64k_fused": dict(kind="prefill", seed=2, B=1, T=65536, H=16, dk=128, dv=128,
+                              in_dtype="bf16", gscale=1.0, h0_std=0.02, fused=True),
     "decode_256x16": dict(kind="decode", seed=3, N=256, H=16, dk=128, dv=128,
                           in_dtype="bf16", gscale=1.0, steps=1024, pool=32, state_std=0.02),
     "append_256x16x64": dict(kind="prefill", seed=5, B=256, T=64, H=16, dk=128, dv=128,

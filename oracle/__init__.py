@@ -45,7 +45,8 @@ def _load():
         lib.kda_oracle_forward.argtypes = [
             i64, ctypes.POINTER(ctypes.c_int64), i64, i64, i64,
             fp, fp, fp, fp, fp, dp, ctypes.c_double,
-            ctypes.POINTER(ctypes.c_int32), i64, dp, dp, ctypes.c_int]
+            ctypes.POINTER(ctypes.c_int32), i64, dp, dp, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_double]
         lib.kda_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -65,7 +66,8 @@ def _ptr(a, t):
 
 def forward(q, k, v, g, beta, h0=None, cu_seqlens=None, scale: float = 1.0,
             heads: Optional[Sequence[int]] = None, nthreads: int = 0,
-            want_state: bool = True):
+            want_state: bool = True, qk_l2norm: bool = False,
+            gate_logits: bool = False, gate_scale: float = 1.0):
     """fp64 token recurrence.
 
     q, k, g: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H] (any float
@@ -74,6 +76,10 @@ def forward(q, k, v, g, beta, h0=None, cu_seqlens=None, scale: float = 1.0,
     B fixed-length sequences.  Returns (o [B, T, nh, dv], hT [N, nh, dk, dv])
     in float64 for the requested heads (all heads by default).  h0 is taken
     in float64 so a state can be chained between calls without rounding.
+
+    qk_l2norm: q and k are L2-normalised per token and head first
+    (x / sqrt(sum x^2 + 1e-6)).  gate_logits: g holds logits z and the
+    log-gate is -gate_scale * softplus(z).  Both in fp64, see kda_oracle.c.
     """
     lib = _load()
     q, k, v, g, beta = map(_f32, (q, k, v, g, beta))
@@ -94,13 +100,14 @@ def forward(q, k, v, g, beta, h0=None, cu_seqlens=None, scale: float = 1.0,
         _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
         _ptr(g, ctypes.c_float), _ptr(beta, ctypes.c_float), _ptr(h0a, ctypes.c_double),
         float(scale), hs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), nh,
-        _ptr(o, ctypes.c_double), _ptr(hT, ctypes.c_double), int(nthreads))
+        _ptr(o, ctypes.c_double), _ptr(hT, ctypes.c_double), int(nthreads),
+        int(bool(qk_l2norm)), int(bool(gate_logits)), float(gate_scale))
     if rc != 0:
         raise RuntimeError(f"kda_oracle_forward failed with code {rc}")
     return o, hT
 
 
-def decode_step(q, k, v, g, beta, state, scale: float = 1.0, nthreads: int = 0):
+def decode_step(q, k, v, g, beta, state, scale: float = 1.0, nthreads: int = 0, **transforms):
     """One recurrent step for N independent sequences.
 
     q, k, g: [N, H, dk]; v: [N, H, dv]; beta: [N, H]; state: [N, H, dk, dv].
@@ -111,5 +118,5 @@ def decode_step(q, k, v, g, beta, state, scale: float = 1.0, nthreads: int = 0):
     N = q.shape[0]
     cu = np.arange(N + 1, dtype=np.int64)
     o, hT = forward(q[None], k[None], v[None], g[None], beta[None], h0=state,
-                    cu_seqlens=cu, scale=scale, nthreads=nthreads)
+                    cu_seqlens=cu, scale=scale, nthreads=nthreads, **transforms)
     return o[0], hT

@@ -20,6 +20,16 @@
  * that the public naive recurrence multiplies by exp(g) first and then writes
  * beta k (v - k^T S); this is that order.  `scale` is 1 in the pages' formula.
  *
+ * Two optional input transforms, which the kernels can fuse (the pages'
+ * parameterization table has the Q/K L2 normalization done inside the KDA
+ * kernel, and their test list names a fused gate), are applied per token
+ * before the recurrence:
+ *  - qk_l2norm: q_t and k_t are divided by sqrt(sum_i x_i^2 + eps) over the
+ *    key channels, eps = 1e-6 (the pages give no eps; this is the reading);
+ *  - gate_logits: g holds logits z and the log-gate is
+ *    g_t = -gate_scale * softplus(z_t), softplus(z) = log(1 + exp(z)), the
+ *    form of the synthetic gate recipe.
+ *
  * Arithmetic is fp64 throughout; inputs arrive as float32 arrays holding the
  * exact values the GPU receives (bf16 values are exactly representable in
  * float32) and are widened to double before use.
@@ -41,11 +51,28 @@
 #include <omp.h>
 #endif
 
+#define KDA_ORACLE_L2_EPS 1e-6
+
+/* log(1 + exp(z)) without overflow: for z > 0 it is z + log(1 + exp(-z)) */
+static double softplus(double z) { return z > 0.0 ? z + log1p(exp(-z)) : log1p(exp(z)); }
+
+/* x <- x / sqrt(sum x^2 + eps) */
+static void l2_normalise(double *x, int64_t n)
+{
+    double ss = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        ss += x[i] * x[i];
+    const double inv = 1.0 / sqrt(ss + KDA_ORACLE_L2_EPS);
+    for (int64_t i = 0; i < n; ++i)
+        x[i] *= inv;
+}
+
 int kda_oracle_forward(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk,
                        int64_t dv, const float *q, const float *k, const float *v,
                        const float *g, const float *beta, const double *h0,
                        double scale, const int32_t *heads, int64_t nh, double *o,
-                       double *hT, int nthreads)
+                       double *hT, int nthreads, int qk_l2norm, int gate_logits,
+                       double gate_scale)
 {
     if (n_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0 || nh <= 0)
         return 1;
@@ -85,12 +112,18 @@ int kda_oracle_forward(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk,
                 kt[i] = (double)k[base_k + i];
                 qt[i] = (double)q[base_k + i];
             }
+            if (qk_l2norm) {
+                l2_normalise(kt, dk);
+                l2_normalise(qt, dk);
+            }
             for (int64_t j = 0; j < dv; ++j)
                 vt[j] = (double)v[base_v + j];
             const double b = (double)beta[t * H + h];
             /* S~ = Diag(exp(g_t)) S_{t-1} */
             for (int64_t i = 0; i < dk; ++i) {
-                const double a = exp((double)g[base_k + i]);
+                const double gi = gate_logits ? -gate_scale * softplus((double)g[base_k + i])
+                                              : (double)g[base_k + i];
+                const double a = exp(gi);
                 for (int64_t j = 0; j < dv; ++j)
                     S[i * dv + j] *= a;
             }
@@ -124,7 +157,7 @@ int kda_oracle_forward(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk,
     return err;
 }
 
-int kda_oracle_version(void) { return 1; }
+int kda_oracle_version(void) { return 2; }
 
 int kda_oracle_max_threads(void)
 {
