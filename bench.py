@@ -7,7 +7,7 @@ inter-chunk state propagation, output) runs inside that call.  Inputs are
 drawn on the host, copied to HBM once, and are resident when timing starts.
 Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-append] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-append] [--no-fused] [--no-cpu]
                     [--calibrate-copy]
 
 --calibrate-copy adds, before the timed region, one elementwise copy kernel
@@ -83,12 +83,16 @@ def stored_traffic():
         return None
 
 
-def time_prefill(args):
+def time_prefill(args, name="prefill_64k", calibrate=False):
+    """Time kda_chunk_fwd on a named workload; ``prefill_64k_fused`` is the same
+    problem handed over before the L2 norm and the gate activation, which the
+    kernels then apply (the input transforms)."""
     import torch
     import gated_delta_rule_52_amd as kda
     from gated_delta_rule_52_amd.inputs import make_workload
-    x = make_workload("prefill_64k")
-    log(f"prefill_64k drawn: B={x.B} T={x.T} H={x.H} dk={x.dk} dv={x.dv}")
+    x = make_workload(name)
+    tr = x.transforms()
+    log(f"{name} drawn: B={x.B} T={x.T} H={x.H} dk={x.dk} dv={x.dv} transforms={tr}")
     dev = "cuda:0"
     bf, f32 = torch.bfloat16, torch.float32
     t = lambda a, dt: torch.from_numpy(a).to(dev).to(dt)
@@ -98,8 +102,8 @@ def time_prefill(args):
     o = torch.empty((x.B, x.T, x.H, x.dv), dtype=bf, device=dev)
     ws = torch.empty(kda.chunk_fwd_workspace_bytes(q, v), dtype=torch.uint8, device=dev)
     step = lambda: kda.chunk_fwd(q, k, v, g, beta, initial_state=h0, final_state=hT, o=o,
-                                 out_dtype=bf, workspace=ws)
-    if args.calibrate_copy:
+                                 out_dtype=bf, workspace=ws, **tr)
+    if calibrate:
         # an elementwise kernel (not a runtime blit) so the counters see it
         a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
@@ -123,7 +127,7 @@ def time_prefill(args):
     wall = time.perf_counter() - w0
     per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
     ms = float(ev[0].elapsed_time(ev[-1]) / args.steps)
-    log(f"prefill: {ms:.3f} ms/step (events), median {np.median(per):.3f}, p10 {np.percentile(per, 10):.3f}, "
+    log(f"{'prefill' if name == 'prefill_64k' else name}: {ms:.3f} ms/step (events), median {np.median(per):.3f}, p10 {np.percentile(per, 10):.3f}, "
         f"p90 {np.percentile(per, 90):.3f}, wall {1e3 * wall / args.steps:.3f} ms/step")
     nbytes = prefill_alg_bytes(x.B, x.T, x.H, x.dk, x.dv, x.N)
     return x, ms, per, nbytes
@@ -290,6 +294,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode and append lines")
     ap.add_argument("--no-append", action="store_true", help="skip the append line")
+    ap.add_argument("--no-fused", action="store_true", help="skip the fused input-transform line")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -300,7 +305,7 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    x, ms, per, nbytes = time_prefill(args)
+    x, ms, per, nbytes = time_prefill(args, calibrate=args.calibrate_copy)
     copy_gbs = copy_ceiling()
     tok_s = x.B * x.T / (ms * 1e-3)
     ach = nbytes / (ms * 1e-3) / 1e9
@@ -344,6 +349,16 @@ def main():
             "tokens_per_s": xa.B * xa.T / (ra[best] * 1e-6),
             "roofline": {"bound": "hbm", "achieved": aach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": aach / HBM_PEAK_GBS, "alg_bytes_per_launch": abytes},
+        }
+    if not args.no_fused:
+        xf, msf, perf, fbytes = time_prefill(args, "prefill_64k_fused")
+        fach = fbytes / (msf * 1e-3) / 1e9
+        rec["fused"] = {
+            "workload": "prefill_64k_fused", "transforms": xf.transforms(),
+            "ms_per_step": msf, "ms_median": float(np.median(perf)),
+            "tokens_per_s": xf.B * xf.T / (msf * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": fach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": fach / HBM_PEAK_GBS, "alg_bytes_per_launch": fbytes},
         }
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(x)

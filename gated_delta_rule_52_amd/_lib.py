@@ -13,6 +13,8 @@ LIB_PATH = os.path.join(HERE, "libkda.so")
 
 KDA_DTYPE_BF16 = 0
 KDA_DTYPE_FP32 = 1
+KDA_FLAG_QK_L2NORM = 1
+KDA_FLAG_GATE_SOFTPLUS = 2
 
 STATUS = {
     0: "KDA_OK", 1: "KDA_ERR_NULL_POINTER", 2: "KDA_ERR_BAD_SHAPE", 3: "KDA_ERR_UNSUPPORTED",
@@ -39,6 +41,7 @@ class ChunkFwdArgs(ctypes.Structure):
         ("chunk_size", ctypes.c_int32),
         ("workspace", vp), ("workspace_bytes", ctypes.c_size_t),
         ("stream", vp),
+        ("flags", ctypes.c_uint32), ("gate_scale", ctypes.c_float),
     ]
 
 
@@ -51,6 +54,7 @@ class RecurrentStepArgs(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
         ("stream", vp),
+        ("flags", ctypes.c_uint32), ("gate_scale", ctypes.c_float),
     ]
 
 

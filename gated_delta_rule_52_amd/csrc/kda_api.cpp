@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <cstddef>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -46,11 +47,40 @@ kda_status hip_status(hipError_t e, const char *what) {
     return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Checks shared by kda_chunk_fwd and kda_chunk_fwd_workspace_bytes.
-kda_status check_chunk_sizes(const kda_chunk_fwd_args *a) {
+// Copies the caller's struct into `out`: the struct of this ABI version, or
+// that of version 1, which ends before `flags` (then no input transform).
+// Checks the size and the transform fields.
+template <class Args>
+kda_status read_args(const Args *a, Args &out) {
     if (!a) return fail(KDA_ERR_NULL_POINTER, "args is NULL");
-    if (a->struct_size != sizeof(kda_chunk_fwd_args))
-        return fail(KDA_ERR_BAD_STRUCT, "struct_size %u != %zu", a->struct_size, sizeof(kda_chunk_fwd_args));
+    const size_t v1 = offsetof(Args, flags);
+    if (a->struct_size != sizeof(Args) && a->struct_size != v1)
+        return fail(KDA_ERR_BAD_STRUCT, "struct_size %u (expected %zu, or %zu for ABI version 1)", a->struct_size,
+                    sizeof(Args), v1);
+    std::memset(&out, 0, sizeof out);
+    std::memcpy(&out, a, a->struct_size);
+    if (a->struct_size == v1) {
+        out.flags = 0;
+        out.gate_scale = 1.f;
+    }
+    if (out.flags & ~(KDA_FLAG_QK_L2NORM | KDA_FLAG_GATE_SOFTPLUS))
+        return fail(KDA_ERR_UNSUPPORTED, "unknown flags 0x%x", out.flags);
+    if ((out.flags & KDA_FLAG_GATE_SOFTPLUS) && !(std::isfinite(out.gate_scale) && out.gate_scale >= 0.f))
+        return fail(KDA_ERR_BAD_SHAPE, "gate_scale must be finite and >= 0");
+    return KDA_OK;
+}
+
+template <class Args>
+kda::InputXform xform_of(const Args *a) {
+    kda::InputXform x{};
+    x.qk_l2norm = (a->flags & KDA_FLAG_QK_L2NORM) != 0;
+    x.gate_softplus = (a->flags & KDA_FLAG_GATE_SOFTPLUS) != 0;
+    x.gate_scale = a->gate_scale;
+    return x;
+}
+
+// Checks shared by kda_chunk_fwd and kda_chunk_fwd_workspace_bytes (on a struct read by read_args).
+kda_status check_chunk_sizes(const kda_chunk_fwd_args *a) {
     if (a->B < 0 || a->T < 0 || a->H <= 0 || a->num_seqs < 0)
         return fail(KDA_ERR_BAD_SHAPE, "B=%d T=%d H=%d num_seqs=%d", a->B, a->T, a->H, a->num_seqs);
     if (!valid_dim(a->dk) || !valid_dim(a->dv))
@@ -122,15 +152,21 @@ const char *kda_last_error(void) { return g_last_error.c_str(); }
 
 int kda_abi_version(void) { return KDA_ABI_VERSION; }
 
-size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_fwd_args *a) {
-    if (check_chunk_sizes(a) != KDA_OK) return static_cast<size_t>(-1);
+size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_fwd_args *user) {
+    kda_chunk_fwd_args args;
+    if (read_args(user, args) != KDA_OK || check_chunk_sizes(&args) != KDA_OK) return static_cast<size_t>(-1);
+    const kda_chunk_fwd_args *a = &args;
     return kda::chunk_workspace_bytes(a->B, a->T, a->H, a->dk, a->dv, a->num_seqs, a->chunk_size,
                                       a->cu_seqlens != nullptr, a->in_dtype == KDA_DTYPE_BF16);
 }
 
-kda_status kda_chunk_fwd(const kda_chunk_fwd_args *a) {
+kda_status kda_chunk_fwd(const kda_chunk_fwd_args *user) {
     g_last_error.clear();
-    kda_status st = check_chunk_sizes(a);
+    kda_chunk_fwd_args args;
+    kda_status st = read_args(user, args);
+    if (st != KDA_OK) return st;
+    const kda_chunk_fwd_args *a = &args;
+    st = check_chunk_sizes(a);
     if (st != KDA_OK) return st;
     st = check_prefill_buffers(a);
     if (st != KDA_OK) return st;
@@ -168,16 +204,18 @@ kda_status kda_chunk_fwd(const kda_chunk_fwd_args *a) {
     L.chunk = a->chunk_size; L.scale = a->scale;
     L.in_bf16 = a->in_dtype == KDA_DTYPE_BF16;
     L.out_bf16 = a->out_dtype == KDA_DTYPE_BF16;
+    L.xf = xform_of(a);
     L.workspace = a->workspace; L.workspace_bytes = a->workspace_bytes;
     L.stream = static_cast<hipStream_t>(a->stream);
     return hip_status(kda::launch_chunk(L), "kda_chunk_fwd launch");
 }
 
-kda_status kda_recurrent_fwd(const kda_chunk_fwd_args *a) {
+kda_status kda_recurrent_fwd(const kda_chunk_fwd_args *user) {
     g_last_error.clear();
-    if (!a) return fail(KDA_ERR_NULL_POINTER, "args is NULL");
-    if (a->struct_size != sizeof(kda_chunk_fwd_args))
-        return fail(KDA_ERR_BAD_STRUCT, "struct_size %u != %zu", a->struct_size, sizeof(kda_chunk_fwd_args));
+    kda_chunk_fwd_args args;
+    kda_status st = read_args(user, args);
+    if (st != KDA_OK) return st;
+    const kda_chunk_fwd_args *a = &args;
     if (a->B < 0 || a->T < 0 || a->H <= 0 || a->num_seqs < 0)
         return fail(KDA_ERR_BAD_SHAPE, "B=%d T=%d H=%d num_seqs=%d", a->B, a->T, a->H, a->num_seqs);
     if (!valid_dim(a->dk) || !valid_dim(a->dv))
@@ -188,7 +226,7 @@ kda_status kda_recurrent_fwd(const kda_chunk_fwd_args *a) {
     if (a->cu_seqlens ? a->B != 1 : a->num_seqs != a->B)
         return fail(KDA_ERR_BAD_SHAPE, "num_seqs=%d with B=%d (%s)", a->num_seqs, a->B,
                     a->cu_seqlens ? "packed input needs B = 1" : "num_seqs must equal B");
-    kda_status st = check_prefill_buffers(a);
+    st = check_prefill_buffers(a);
     if (st != KDA_OK) return st;
     const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
     if (a->num_seqs == 0 || (tokens == 0 && !a->final_state)) return KDA_OK;
@@ -201,15 +239,17 @@ kda_status kda_recurrent_fwd(const kda_chunk_fwd_args *a) {
     L.in_bf16 = a->in_dtype == KDA_DTYPE_BF16;
     L.out_bf16 = a->out_dtype == KDA_DTYPE_BF16;
     L.multi_token = true;
+    L.xf = xform_of(a);
     L.stream = static_cast<hipStream_t>(a->stream);
     return hip_status(kda::launch_recurrent(L), "kda_recurrent_fwd launch");
 }
 
-kda_status kda_recurrent_step(const kda_recurrent_step_args *a) {
+kda_status kda_recurrent_step(const kda_recurrent_step_args *user) {
     g_last_error.clear();
-    if (!a) return fail(KDA_ERR_NULL_POINTER, "args is NULL");
-    if (a->struct_size != sizeof(kda_recurrent_step_args))
-        return fail(KDA_ERR_BAD_STRUCT, "struct_size %u != %zu", a->struct_size, sizeof(kda_recurrent_step_args));
+    kda_recurrent_step_args args;
+    const kda_status st = read_args(user, args);
+    if (st != KDA_OK) return st;
+    const kda_recurrent_step_args *a = &args;
     if (a->N < 0 || a->H <= 0) return fail(KDA_ERR_BAD_SHAPE, "N=%d H=%d", a->N, a->H);
     if (!valid_dim(a->dk) || !valid_dim(a->dv))
         return fail(KDA_ERR_UNSUPPORTED, "dk=%d dv=%d (supported: 64, 128)", a->dk, a->dv);
@@ -241,6 +281,7 @@ kda_status kda_recurrent_step(const kda_recurrent_step_args *a) {
     L.in_bf16 = a->in_dtype == KDA_DTYPE_BF16;
     L.out_bf16 = a->out_dtype == KDA_DTYPE_BF16;
     L.multi_token = false;
+    L.xf = xform_of(a);
     L.stream = static_cast<hipStream_t>(a->stream);
     return hip_status(kda::launch_recurrent(L), "kda_recurrent_step launch");
 }

@@ -32,6 +32,9 @@
 // passes of the segmented prefill (see kda_segments.hip): kLocal computes a
 // segment's local state H (zero start) and its transition P (identity start,
 // v = 0); kOut replays the segment from its true entering state and writes o.
+// The optional input transforms act as the chunk is loaded: the gate logit
+// becomes the log-gate before the cumulative sum, and the k and q rows are
+// L2-normalised in LDS before any product reads them.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -45,12 +48,39 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 
 constexpr float kMaxBlockDecay = 80.0f;  // exp(80) is far below FLT_MAX
 
+// Divide each of the C rows of k and q in LDS (row stride DKP) by its L2 norm
+// over the DK channels (plus kL2Eps); 256 / C consecutive threads share a row.
+template <int C, int DK, int DKP>
+__device__ __forceinline__ void l2norm_rows(float *sK, float *sQ, int tid) {
+    constexpr int TPR = 256 / C, CPT = DK / TPR;
+    static_assert(kWave % TPR == 0 && DK % TPR == 0, "a row's threads sit in one wave");
+    const int r = tid / TPR, part = tid % TPR;
+    float kk = 0.f, qq = 0.f;
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+        const float a = sK[r * DKP + part + TPR * m], b = sQ[r * DKP + part + TPR * m];
+        kk += a * a;
+        qq += b * b;
+    }
+#pragma unroll
+    for (int msk = 1; msk < TPR; msk <<= 1) {
+        kk += __shfl_xor(kk, msk, kWave);
+        qq += __shfl_xor(qq, msk, kWave);
+    }
+    const float ik = rsqrtf(kk + kL2Eps), iq = rsqrtf(qq + kL2Eps);
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+        sK[r * DKP + part + TPR * m] *= ik;
+        sQ[r * DKP + part + TPR * m] *= iq;
+    }
+}
+
 template <int DK, int C, int BV, bool InBf16, bool OutBf16, int MODE>
 __global__ void __launch_bounds__(256, 1)
 chunk_fp32_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
                   const void *__restrict__ v_, const float *__restrict__ g,
                   const void *__restrict__ beta_, float *hT, void *__restrict__ o_,
-                  SegmentView sv, int H, int DV, float scale) {
+                  SegmentView sv, int H, int DV, float scale, InputXform ix) {
     using In = Elem<InBf16>;
     using Out = Elem<OutBf16>;
     const typename In::T *q = static_cast<const typename In::T *>(q_);
@@ -123,7 +153,7 @@ chunk_fp32_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
 #pragma unroll
             for (int m = 0; m < RP; ++m) {
                 const int r = part * RP + m;
-                gv[m] = r < L ? g[((c0 + r) * H + h) * DK + c] : 0.f;
+                gv[m] = r < L ? ix.log_gate(g[((c0 + r) * H + h) * DK + c]) : 0.f;
             }
             float acc = 0.f;
 #pragma unroll
@@ -141,6 +171,8 @@ chunk_fp32_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
             }
         }
         __syncthreads();
+        // k, q rows normalised; the barrier after the decay ranges orders this before the products
+        if (ix.qk_l2norm) l2norm_rows<C, DK, DKP>(sK, sQ, tid);
         for (int c = tid; c < DK; c += 256) {
 #pragma unroll
             for (int a = 0; a < NB; ++a) {
@@ -339,7 +371,7 @@ static void launch_fp32_dk(const ChunkLaunch &L, const SegmentView &sv, int max_
     dim3 grid(slices, max_segs, L.H), block(256);
 #define KDA_CHUNK(IB, OB)                                                                               \
     hipLaunchKernelGGL((chunk_fp32_kernel<DK, C, BV, IB, OB, MODE>), grid, block, 0, L.stream, L.q, L.k, \
-                       L.v, L.g, L.beta, L.hT, L.o, sv, L.H, L.dv, L.scale)
+                       L.v, L.g, L.beta, L.hT, L.o, sv, L.H, L.dv, L.scale, L.xf)
     if (L.in_bf16 && L.out_bf16) KDA_CHUNK(true, true);
     else if (L.in_bf16) KDA_CHUNK(true, false);
     else if (L.out_bf16) KDA_CHUNK(false, true);

@@ -8,6 +8,23 @@
 
 namespace kda {
 
+// Optional per-token input transforms (KDA_FLAG_* in kda.h), handed to the
+// kernels by value.
+constexpr float kL2Eps = 1e-6f;  // the L2 norm's epsilon, KDA_L2NORM_EPS
+struct InputXform {
+    bool qk_l2norm;      // q, k divided by sqrt(sum x^2 + kL2Eps) over dk
+    bool gate_softplus;  // g holds logits z; log-gate = -gate_scale softplus(z)
+    float gate_scale;
+    bool any() const { return qk_l2norm || gate_softplus; }
+    // The log-gate for input value g.  softplus(z) = log(1 + e^z) is taken as
+    // max(z, log(1 + e^min(z, 15))): above 15 softplus(z) - z < 3.1e-7, and
+    // below it the only loss is 1 + e^z rounding, an absolute error under
+    // 6e-8 in the log-gate, i.e. a relative error of that size in alpha.
+    __device__ __forceinline__ float log_gate(float g) const {
+        return gate_softplus ? -gate_scale * fmaxf(g, __logf(1.f + __expf(fminf(g, 15.f)))) : g;
+    }
+};
+
 // Token-by-token kernel: decode step (T = 1, N = number of sequences) or a
 // loop over the tokens of each sequence.
 struct RecurrentLaunch {
@@ -22,6 +39,7 @@ struct RecurrentLaunch {
     float scale;
     bool in_bf16, out_bf16;
     bool multi_token;           // split dv into narrow slices for long loops
+    InputXform xf;
     hipStream_t stream;
 };
 
@@ -40,6 +58,7 @@ struct ChunkLaunch {
     int chunk;
     float scale;
     bool in_bf16, out_bf16;
+    InputXform xf;
     void *workspace;
     size_t workspace_bytes;
     hipStream_t stream;

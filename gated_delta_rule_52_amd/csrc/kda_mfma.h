@@ -122,6 +122,19 @@ __device__ __forceinline__ float wave_max(float x) {
     x = fmaxf(x, dpp_move<0x143>(x));  // row_bcast:31
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
+// Sum over each half-wave (lanes 0-31 and 32-63 separately), the result in
+// every lane: butterflies over lane bits 0-3 as DPP moves (quad permutes
+// [1,0,3,2] and [2,3,0,1]; half-row and row mirrors, which pair the two
+// quads of an 8-lane group and the two 8-lane groups of a row once every lane
+// of each holds its group's sum), then bit 4 by a swizzle (xor mask 16 in the
+// 32-lane bit mode).
+__device__ __forceinline__ float half_wave_sum(float x) {
+    x += dpp_move<0xB1>(x);
+    x += dpp_move<0x4E>(x);
+    x += dpp_move<0x141>(x);
+    x += dpp_move<0x140>(x);
+    return x + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
 
 // Buffer resource over [base, base + bytes): raw buffer accesses at or past
 // the end read as zero and their stores are dropped.  Offsets are 32-bit

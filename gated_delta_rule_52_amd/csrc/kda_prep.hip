@@ -26,6 +26,11 @@
 //   pair-by-pair fp32 path instead.
 // * Everything stored is fp16 with a power-of-two scale per chunk and
 //   matrix, chosen from the matrix's maximum, so fp16's range never binds.
+//
+// The optional input transforms (XF instantiation) act on the values as they
+// arrive: the gate logit becomes the log-gate before the cumulative sum, and
+// each row's 1/|k| and 1/|q| (reduced over the 32 lanes that hold the row)
+// scale k and q before any product or maximum is formed.
 #include "kda_internal.h"
 #include "kda_mfma.h"
 
@@ -102,11 +107,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 // exceeds exp(-kMaxChunkDecay) in some channel is not written there but
 // appended to the exact list, and EXACT = true redoes it with the pair-by-pair
 // Gram blocks.  Returns early (whole workgroup) for chunks past the segment end.
-template <bool EXACT>
-__device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int h, const uint16_t *__restrict__ q,
-                                           const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-                                           const float *__restrict__ g, const uint16_t *__restrict__ beta,
-                                           const SegmentView &sv, int per, int H, float scale, char *packs) {
+template <bool EXACT, bool XF>
+__device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, int bx, int h,
+                                           const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                           const uint16_t *__restrict__ v, const float *__restrict__ g,
+                                           const uint16_t *__restrict__ beta, const SegmentView &sv, int per,
+                                           int H, float scale, char *packs, const InputXform ix) {
     const int seg = bx / per, jc = bx - seg * per;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -138,6 +144,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int 
     // ============ a1: raw inputs to registers, maxima, chunk-local cumulative decay ============
     float G[2][8][2];  // [half][row][channel]
     uint32_t rk[2][8], rq[2][8];
+    float nk[8], nq[8];  // XF: 1/|k| and 1/|q| of each of this thread's rows (1 without the L2 norm)
     {
         uint32_t mk2 = 0u, mq2 = 0u;
 #pragma unroll
@@ -149,19 +156,61 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int 
                 const u2 gg = ld64(rs_g, 4 * e);
                 rk[hh][m] = ld32(rs_k, 2 * e);
                 rq[hh][m] = ld32(rs_q, 2 * e);
-                r0 += __uint_as_float(gg[0]);
-                r1 += __uint_as_float(gg[1]);
+                float g0 = __uint_as_float(gg[0]), g1 = __uint_as_float(gg[1]);
+                if constexpr (XF) {  // rows past the chunk end stay 0: they must not decay G_last
+                    const bool real = 8 * rq8 + m < L;
+                    g0 = real ? ix.log_gate(g0) : 0.f;
+                    g1 = real ? ix.log_gate(g1) : 0.f;
+                }
+                r0 += g0;
+                r1 += g1;
                 G[hh][m][0] = r0;
                 G[hh][m][1] = r1;
-                mk2 = absmax2(mk2, rk[hh][m]);
-                mq2 = absmax2(mq2, rq[hh][m]);
+                if constexpr (!XF) {
+                    mk2 = absmax2(mk2, rk[hh][m]);
+                    mq2 = absmax2(mq2, rq[hh][m]);
+                }
             }
             sm.op.part[rq8][hh * HC + 2 * cq] = r0;
             sm.op.part[rq8][hh * HC + 2 * cq + 1] = r1;
         }
         if (tid < C) sm.beta[tid] = tid < L ? bf16_to_f32(beta[(c0 + tid) * H + h]) : 0.f;
-        const float mk = wave_max(absmax2_value(mk2));
-        const float mq = wave_max(absmax2_value(mq2));
+        float mk, mq;
+        if constexpr (XF) {
+            // a row's 128 channels sit in the 32 lanes of one half-wave, four per lane
+            float ak = 0.f, aq = 0.f;  // largest |k|/|k_row|, |q|/|q_row| of this thread
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                float sk2 = 0.f, sq2 = 0.f, xk = 0.f, xq = 0.f;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const float k0 = lo_f(rk[hh][m]), k1 = hi_f(rk[hh][m]);
+                    const float q0 = lo_f(rq[hh][m]), q1 = hi_f(rq[hh][m]);
+                    sk2 += k0 * k0 + k1 * k1;
+                    sq2 += q0 * q0 + q1 * q1;
+                    xk = fmaxf(xk, fmaxf(fabsf(k0), fabsf(k1)));
+                    xq = fmaxf(xq, fmaxf(fabsf(q0), fabsf(q1)));
+                }
+                nk[m] = nq[m] = 1.f;
+                if (ix.qk_l2norm) {
+                    nk[m] = rsqrtf(half_wave_sum(sk2) + kL2Eps);
+                    nq[m] = rsqrtf(half_wave_sum(sq2) + kL2Eps);
+                }
+                ak = fmaxf(ak, xk * nk[m]);
+                aq = fmaxf(aq, xq * nq[m]);
+                if constexpr (EXACT) {
+                    if (cq == 0) {
+                        nx[8 * rq8 + m] = nk[m];
+                        nx[C + 8 * rq8 + m] = nq[m];
+                    }
+                }
+            }
+            mk = wave_max(ak);
+            mq = wave_max(aq);
+        } else {
+            mk = wave_max(absmax2_value(mk2));
+            mq = wave_max(absmax2_value(mq2));
+        }
         if (lane == 0) {
             atomicMax(&sm.imax[0], __float_as_int(mk));
             atomicMax(&sm.imax[1], __float_as_int(mq * fabsf(scale)));
@@ -223,8 +272,14 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int 
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const int r = 8 * rq8 + m;
-            const float kk[2] = {lo_f(rk[hh][m]), hi_f(rk[hh][m])};
-            const float qq[2] = {lo_f(rq[hh][m]), hi_f(rq[hh][m])};
+            float kk[2] = {lo_f(rk[hh][m]), hi_f(rk[hh][m])};
+            float qq[2] = {lo_f(rq[hh][m]), hi_f(rq[hh][m])};
+            if constexpr (XF) {
+                kk[0] *= nk[m];
+                kk[1] *= nk[m];
+                qq[0] *= nq[m];
+                qq[1] *= nq[m];
+            }
             float ekv[2], qsv[2], kdv[2], ra[2], rb[2], rc[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
@@ -346,6 +401,10 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int 
                     vk += bf16_to_f32(k[br + c]) * kk;
                     vq += bf16_to_f32(q[br + c]) * kk;
                 }
+            }
+            if constexpr (XF) {  // the rows' L2 norms (1 without the transform)
+                vk *= nx[rr] * nx[ii];
+                vq *= nx[C + rr] * nx[ii];
             }
             const int a = rr >> 4, b = ii >> 4, rl4 = rr & 15, cl = ii & 15;
             const float ak = ii < rr ? sm.beta[rr] * vk : 0.f;
@@ -522,29 +581,34 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, int bx, int 
     }
 }
 
-// fast path: one workgroup per chunk and head; grid (segments x per, heads)
+// fast path: one workgroup per chunk and head; grid (segments x per, heads).
+// XF: with the input transforms.
+template <bool XF>
 __global__ void __launch_bounds__(NT, 3)
 chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                   const uint16_t *__restrict__ v, const float *__restrict__ g,
                   const uint16_t *__restrict__ beta, SegmentView sv, int per, int H, float scale,
-                  char *__restrict__ packs) {
+                  char *__restrict__ packs, InputXform ix) {
     __shared__ PrepSmem sm;
-    prep_chunk<false>(sm, nullptr, blockIdx.x, blockIdx.y, q, k, v, g, beta, sv, per, H, scale, packs);
+    prep_chunk<false, XF>(sm, nullptr, nullptr, blockIdx.x, blockIdx.y, q, k, v, g, beta, sv, per, H, scale, packs,
+                          ix);
 }
 
 // exact path over the chunks the fast path listed (usually none)
+template <bool XF>
 __global__ void __launch_bounds__(NT, 1)
 chunk_prep_exact_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                         const uint16_t *__restrict__ v, const float *__restrict__ g,
                         const uint16_t *__restrict__ beta, SegmentView sv, int per, int H, float scale,
-                        char *__restrict__ packs) {
+                        char *__restrict__ packs, InputXform ix) {
     __shared__ PrepSmem sm;
     __shared__ float gx[C * GP];  // G of the chunk, for the pair-by-pair Gram entries
+    __shared__ float nx[2 * C];   // XF: 1/|k| and 1/|q| of each row
     const int n = *sv.xcount;
     for (int i = blockIdx.x; i < n; i += gridDim.x) {
         const int id = sv.xlist[i];
         __syncthreads();  // the previous chunk's last LDS reads are done
-        prep_chunk<true>(sm, gx, id / H, id % H, q, k, v, g, beta, sv, per, H, scale, packs);
+        prep_chunk<true, XF>(sm, gx, nx, id / H, id % H, q, k, v, g, beta, sv, per, H, scale, packs, ix);
     }
 }
 
@@ -561,10 +625,17 @@ void launch_prep(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int 
     const uint16_t *q = static_cast<const uint16_t *>(L.q), *k = static_cast<const uint16_t *>(L.k);
     const uint16_t *v = static_cast<const uint16_t *>(L.v), *b = static_cast<const uint16_t *>(L.beta);
     char *pk = static_cast<char *>(packs);
-    hipLaunchKernelGGL(mc::chunk_prep_kernel, dim3(max_segs * per, L.H), dim3(mc::NT), 0, L.stream, q, k, v, L.g, b,
-                       sv, per, L.H, L.scale, pk);
-    hipLaunchKernelGGL(mc::chunk_prep_exact_kernel, dim3(256), dim3(mc::NT), 0, L.stream, q, k, v, L.g, b, sv, per,
-                       L.H, L.scale, pk);
+    if (L.xf.any()) {
+        hipLaunchKernelGGL(mc::chunk_prep_kernel<true>, dim3(max_segs * per, L.H), dim3(mc::NT), 0, L.stream, q, k, v,
+                           L.g, b, sv, per, L.H, L.scale, pk, L.xf);
+        hipLaunchKernelGGL(mc::chunk_prep_exact_kernel<true>, dim3(256), dim3(mc::NT), 0, L.stream, q, k, v, L.g, b,
+                           sv, per, L.H, L.scale, pk, L.xf);
+    } else {
+        hipLaunchKernelGGL(mc::chunk_prep_kernel<false>, dim3(max_segs * per, L.H), dim3(mc::NT), 0, L.stream, q, k,
+                           v, L.g, b, sv, per, L.H, L.scale, pk, L.xf);
+        hipLaunchKernelGGL(mc::chunk_prep_exact_kernel<false>, dim3(256), dim3(mc::NT), 0, L.stream, q, k, v, L.g, b,
+                           sv, per, L.H, L.scale, pk, L.xf);
+    }
 }
 
 }  // namespace kda

@@ -12,7 +12,11 @@
 //     o  = scale (r + beta (k.q) (v - p))      = scale S^T q after the write
 //
 // so the state is read from HBM once and written once per call, whatever the
-// number of tokens.  The state is dk x dv, row-major with dv contiguous:
+// number of tokens.  With the optional input transforms the gate is formed
+// from its logit as each token is staged, and the L2 norms of q and k are
+// reduced beside k.q and folded into p, r, k.q and the write (all linear in
+// k or q), so the normalised vectors are never stored.
+// The state is dk x dv, row-major with dv contiguous:
 // thread (rg, cg) owns columns [4cg, 4cg+4) of rows rg, rg+RG, ..., so one
 // wave's float4 loads cover whole 512-byte rows (fully coalesced).
 #include "kda_device.h"
@@ -26,7 +30,7 @@ recurrent_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
                  const void *__restrict__ v_, const float *__restrict__ g,
                  const void *__restrict__ beta_, const float *h0, float *hT,
                  void *__restrict__ o_, const int32_t *__restrict__ cu_seqlens,
-                 int T, int H, int DV, float scale) {
+                 int T, int H, int DV, float scale, InputXform xf) {
     using In = Elem<InBf16>;
     using Out = Elem<OutBf16>;
     const typename In::T *q = static_cast<const typename In::T *>(q_);
@@ -78,7 +82,7 @@ recurrent_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
         for (int i = tid; i < DK; i += NT) {
             s_kqa[b][0][i] = In::load(k, tk + i);
             s_kqa[b][1][i] = In::load(q, tk + i);
-            s_kqa[b][2][i] = __expf(g[tk + i]);
+            s_kqa[b][2][i] = __expf(xf.log_gate(g[tk + i]));
         }
         if (tid == 0) s_beta[b] = In::load(beta, t * H + h);
         const float4 vv = In::load4(v, tv + col);
@@ -109,10 +113,23 @@ recurrent_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
                 s_red[b][wave][1][cg * 4 + c] = r[c];
             }
         }
-        // k . q, reduced inside every wave (no extra barrier)
-        float kq = 0.f;
-        for (int i = lane; i < DK; i += kWave) kq += s_kqa[b][0][i] * s_kqa[b][1][i];
-        kq = wave_sum(kq);
+        // k . q (and |k|^2, |q|^2 when normalising), reduced inside every wave (no extra barrier)
+        float kq = 0.f, ik = 1.f, iq = 1.f;
+        if (xf.qk_l2norm) {
+            float kk = 0.f, qq = 0.f;
+            for (int i = lane; i < DK; i += kWave) {
+                const float a = s_kqa[b][0][i], c = s_kqa[b][1][i];
+                kq += a * c;
+                kk += a * a;
+                qq += c * c;
+            }
+            ik = rsqrtf(wave_sum(kk) + kL2Eps);
+            iq = rsqrtf(wave_sum(qq) + kL2Eps);
+            kq = wave_sum(kq) * ik * iq;
+        } else {
+            for (int i = lane; i < DK; i += kWave) kq += s_kqa[b][0][i] * s_kqa[b][1][i];
+            kq = wave_sum(kq);
+        }
         __syncthreads();
 
 #pragma unroll
@@ -123,11 +140,12 @@ recurrent_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
                 ps += s_red[b][w][0][cg * 4 + c];
                 rs += s_red[b][w][1][cg * 4 + c];
             }
-            p[c] = ps;
-            r[c] = rs;
+            p[c] = ps * ik;  // S~^T k with k normalised
+            r[c] = rs * iq;
         }
         (void)RG_PER_WAVE;
         const float bt = s_beta[b];
+        const float btk = bt * ik;  // the write's beta k, normalised
         const float d0 = vv.x - p[0], d1 = vv.y - p[1], d2 = vv.z - p[2], d3 = vv.w - p[3];
         if (rg == 0) {
             const float bkq = bt * kq;
@@ -137,7 +155,7 @@ recurrent_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
         }
 #pragma unroll
         for (int m = 0; m < ROWS; ++m) {
-            const float bk = bt * s_kqa[b][0][rg + m * RG];
+            const float bk = btk * s_kqa[b][0][rg + m * RG];
             s[m].x += bk * d0; s[m].y += bk * d1; s[m].z += bk * d2; s[m].w += bk * d3;
         }
     }
@@ -156,7 +174,7 @@ static hipError_t launch_rec_dk(const RecurrentLaunch &L) {
     dim3 grid(L.dv / BV, L.H, L.N), block(256);
 #define KDA_REC(IB, OB)                                                                       \
     hipLaunchKernelGGL((recurrent_kernel<DK, BV, IB, OB>), grid, block, 0, L.stream, L.q, L.k, \
-                       L.v, L.g, L.beta, L.h0, L.hT, L.o, L.cu_seqlens, L.T, L.H, L.dv, L.scale)
+                       L.v, L.g, L.beta, L.h0, L.hT, L.o, L.cu_seqlens, L.T, L.H, L.dv, L.scale, L.xf)
     if (L.in_bf16 && L.out_bf16) KDA_REC(true, true);
     else if (L.in_bf16) KDA_REC(true, false);
     else if (L.out_bf16) KDA_REC(false, true);

@@ -34,8 +34,12 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _flags(qk_l2norm: bool, gate_logits: bool) -> int:
+    return (_lib.KDA_FLAG_QK_L2NORM if qk_l2norm else 0) | (_lib.KDA_FLAG_GATE_SOFTPLUS if gate_logits else 0)
+
+
 def _fill_chunk_args(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, scale,
-                     chunk_size, workspace=None, workspace_bytes=0):
+                     chunk_size, workspace=None, workspace_bytes=0, flags=0, gate_scale=1.0):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
@@ -51,6 +55,8 @@ def _fill_chunk_args(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens
     a.workspace = _ptr(workspace)
     a.workspace_bytes = int(workspace_bytes)
     a.stream = _stream(q.device)
+    a.flags = int(flags)
+    a.gate_scale = float(gate_scale)
     return a
 
 
@@ -72,7 +78,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               cu_seqlens: Optional[torch.Tensor] = None, scale: float = 1.0,
               chunk_size: int = 64, out_dtype: Optional[torch.dtype] = None,
               output_final_state: bool = True, final_state: Optional[torch.Tensor] = None,
-              o: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+              o: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+              qk_l2norm: bool = False, gate_logits: bool = False, gate_scale: float = 1.0
               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise KDA prefill.  Returns (o [B,T,H,dv], final_state [N,H,dk,dv] or None).
 
@@ -81,6 +88,11 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     cu_seqlens: int32 [N+1] device tensor for packed variable-length input
     (B == 1).  ``final_state`` may be given (it may be ``initial_state`` for an
     in-place update); otherwise one is allocated when ``output_final_state``.
+
+    Input transforms done inside the kernels: ``qk_l2norm`` divides each
+    token's q and k by its L2 norm (plus 1e-6 under the root); with
+    ``gate_logits`` g holds logits z and the log-gate is
+    -gate_scale * softplus(z).
     """
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -111,7 +123,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
     a = _fill_chunk_args(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, scale,
-                         chunk_size, workspace, ws if ws > 0 else 0)
+                         chunk_size, workspace, ws if ws > 0 else 0, _flags(qk_l2norm, gate_logits), gate_scale)
     _lib.check(_lib.chunk_fwd_raw(a))
     return o, final_state
 
@@ -120,11 +132,12 @@ def recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
                   cu_seqlens: Optional[torch.Tensor] = None, scale: float = 1.0,
                   out_dtype: Optional[torch.dtype] = None, output_final_state: bool = True,
-                  final_state: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None
+                  final_state: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
+                  qk_l2norm: bool = False, gate_logits: bool = False, gate_scale: float = 1.0
                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Token-by-token fused recurrent forward for short segments (at most a few
-    dozen tokens per sequence): the same arguments, shapes and results as
-    ``chunk_fwd`` (no chunk size, no workspace).  Returns (o, final_state)."""
+    dozen tokens per sequence): the same arguments, shapes, input transforms and
+    results as ``chunk_fwd`` (no chunk size, no workspace).  Returns (o, final_state)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
@@ -150,7 +163,8 @@ def recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         o = torch.empty((B, T, H, dv), dtype=od, device=q.device)
     else:
         _need(o, "o", (B, T, H, dv), od)
-    a = _fill_chunk_args(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, scale, 64)
+    a = _fill_chunk_args(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, scale, 64,
+                         flags=_flags(qk_l2norm, gate_logits), gate_scale=gate_scale)
     _lib.check(_lib.recurrent_fwd_raw(a))
     return o, final_state
 
@@ -159,11 +173,12 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
                    beta: torch.Tensor, state: Optional[torch.Tensor],
                    final_state: Optional[torch.Tensor] = None, scale: float = 1.0,
                    out_dtype: Optional[torch.dtype] = None,
-                   o: Optional[torch.Tensor] = None) -> torch.Tensor:
+                   o: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
+                   gate_logits: bool = False, gate_scale: float = 1.0) -> torch.Tensor:
     """One decode step for N sequences.  q, k, g: [N,H,dk]; v: [N,H,dv];
     beta: [N,H]; state: [N,H,dk,dv] fp32 (or None for zeros).  The new state
     is written to ``final_state`` (default: ``state`` itself, in place).
-    Returns o [N,H,dv]."""
+    Input transforms as in ``chunk_fwd``.  Returns o [N,H,dv]."""
     N, H, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
@@ -192,5 +207,7 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
     a.in_dtype = _DT[dt]
     a.out_dtype = _DT[od]
     a.stream = _stream(q.device)
+    a.flags = _flags(qk_l2norm, gate_logits)
+    a.gate_scale = float(gate_scale)
     _lib.check(_lib.recurrent_step_raw(a))
     return o

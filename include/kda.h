@@ -43,7 +43,28 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
+
+/*
+ * Optional input transforms, applied inside the kernels to every token before
+ * the recurrence (`flags` of both argument structs; 0 applies none).  The
+ * Kimi Linear review notes' parameterization table has the Q/K L2
+ * normalization fused into the KDA kernel, and the public tests it lists
+ * cover a fused gate (section "Code Verification").
+ *
+ * KDA_FLAG_QK_L2NORM: q_t and k_t are divided by sqrt(sum_i x_i^2 + 1e-6)
+ *   over their dk channels, per token and head, in fp32 (the pages give no
+ *   epsilon; 1e-6 is this library's).
+ * KDA_FLAG_GATE_SOFTPLUS: g holds gate logits z and the log-gate used is
+ *   -gate_scale * softplus(z), softplus(z) = log(1 + exp(z)), so that
+ *   alpha = (1 + e^z)^-gate_scale.  gate_scale must be finite and >= 0.
+ *
+ * Structs of ABI version 1 (struct_size equal to the offset of `flags`) are
+ * still accepted and apply no transform.
+ */
+#define KDA_FLAG_QK_L2NORM 1u
+#define KDA_FLAG_GATE_SOFTPLUS 2u
+#define KDA_L2NORM_EPS 1e-6f
 
 typedef enum {
     KDA_DTYPE_BF16 = 0, /* bfloat16, round-to-nearest-even on output */
@@ -72,7 +93,8 @@ typedef enum {
  * Shapes (N = number of sequences):
  *   q, k : [B, T, H, dk]  in_dtype
  *   v    : [B, T, H, dv]  in_dtype
- *   g    : [B, T, H, dk]  fp32, log of the per-channel forget gate (alpha = exp(g))
+ *   g    : [B, T, H, dk]  fp32, log of the per-channel forget gate (alpha = exp(g)),
+ *                         or gate logits with KDA_FLAG_GATE_SOFTPLUS
  *   beta : [B, T, H]      in_dtype, the per-token, per-head write strength
  *   initial_state : [N, H, dk, dv] fp32, or NULL for zeros
  *   final_state   : [N, H, dk, dv] fp32, or NULL to skip; may equal initial_state
@@ -108,7 +130,9 @@ typedef struct {
     int32_t chunk_size;
     void *workspace;
     size_t workspace_bytes;
-    void *stream; /* hipStream_t */
+    void *stream;     /* hipStream_t */
+    uint32_t flags;   /* KDA_FLAG_* input transforms (ABI version 2) */
+    float gate_scale; /* used with KDA_FLAG_GATE_SOFTPLUS */
 } kda_chunk_fwd_args;
 
 /* Bytes of workspace kda_chunk_fwd needs for these arguments (host-only, no
@@ -144,6 +168,7 @@ kda_status kda_recurrent_fwd(const kda_chunk_fwd_args *args);
  *
  * Shapes:
  *   q, k : [N, H, dk] in_dtype;  v : [N, H, dv] in_dtype;  g : [N, H, dk] fp32
+ *          (log-gate, or gate logits with KDA_FLAG_GATE_SOFTPLUS)
  *   beta : [N, H] in_dtype
  *   initial_state : [N, H, dk, dv] fp32, or NULL for zeros
  *   final_state   : [N, H, dk, dv] fp32, required; may equal initial_state
@@ -165,7 +190,9 @@ typedef struct {
     float scale;
     kda_dtype in_dtype;
     kda_dtype out_dtype;
-    void *stream; /* hipStream_t */
+    void *stream;     /* hipStream_t */
+    uint32_t flags;   /* KDA_FLAG_* input transforms (ABI version 2) */
+    float gate_scale; /* used with KDA_FLAG_GATE_SOFTPLUS */
 } kda_recurrent_step_args;
 
 kda_status kda_recurrent_step(const kda_recurrent_step_args *args);

@@ -26,7 +26,7 @@ def test_every_declared_function_is_exported():
     assert decl == sorted(_lib.EXPORTS)
     for name in decl:
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
 
 
 def test_status_strings():
@@ -63,6 +63,9 @@ def chunk_args(**kw):
     (dict(o=FAKE + 64), "KDA_ERR_ALIAS"),
     (dict(final_state=3 * FAKE + 8), "KDA_ERR_ALIAS"),
     (dict(initial_state=7 * FAKE + 4096), "KDA_ERR_ALIAS"),
+    (dict(flags=4), "KDA_ERR_UNSUPPORTED"),
+    (dict(flags=_lib.KDA_FLAG_GATE_SOFTPLUS, gate_scale=-1.0), "KDA_ERR_BAD_SHAPE"),
+    (dict(flags=_lib.KDA_FLAG_GATE_SOFTPLUS, gate_scale=float("nan")), "KDA_ERR_BAD_SHAPE"),
 ])
 def test_chunk_fwd_rejects(kw, status):
     rc = _lib.chunk_fwd_raw(chunk_args(**kw))
@@ -80,6 +83,8 @@ def test_chunk_fwd_rejects(kw, status):
     (dict(v=None), "KDA_ERR_NULL_POINTER"),
     (dict(o=2 * FAKE + 8), "KDA_ERR_ALIAS"),
     (dict(final_state=6 * FAKE + 8), "KDA_ERR_ALIAS"),
+    (dict(flags=8), "KDA_ERR_UNSUPPORTED"),
+    (dict(flags=3, gate_scale=float("inf")), "KDA_ERR_BAD_SHAPE"),
 ])
 def test_recurrent_fwd_rejects(kw, status):
     # the same argument rules as kda_chunk_fwd; chunk_size and workspace are ignored
@@ -90,9 +95,31 @@ def test_recurrent_fwd_rejects(kw, status):
 
 def test_chunk_struct_size_is_checked():
     a = chunk_args()
-    a.struct_size = ctypes.sizeof(_lib.ChunkFwdArgs) - 8
+    a.struct_size = ctypes.sizeof(_lib.ChunkFwdArgs) - 4
     assert _lib.load().kda_chunk_fwd(ctypes.byref(a)) == S["KDA_ERR_BAD_STRUCT"]
     assert _lib.load().kda_chunk_fwd(None) == S["KDA_ERR_NULL_POINTER"]
+
+
+def test_version_1_structs_are_accepted_without_transforms():
+    """A struct that ends before `flags` (ABI version 1) is read without the
+    fields after it: invalid values there are never looked at."""
+    lib = _lib.load()
+    v1 = _lib.ChunkFwdArgs.flags.offset
+    a = chunk_args(B=0, num_seqs=0, flags=0xff, gate_scale=-1.0)
+    a.struct_size = v1
+    assert lib.kda_chunk_fwd(ctypes.byref(a)) == 0
+    assert lib.kda_recurrent_fwd(ctypes.byref(a)) == 0
+    a.struct_size = ctypes.sizeof(_lib.ChunkFwdArgs)
+    assert lib.kda_chunk_fwd(ctypes.byref(a)) == S["KDA_ERR_UNSUPPORTED"]
+    r = step_args(N=0, flags=0xff, gate_scale=-1.0)
+    r.struct_size = _lib.RecurrentStepArgs.flags.offset
+    assert lib.kda_recurrent_step(ctypes.byref(r)) == 0
+    r.struct_size = ctypes.sizeof(_lib.RecurrentStepArgs)
+    assert lib.kda_recurrent_step(ctypes.byref(r)) == S["KDA_ERR_UNSUPPORTED"]
+    # the workspace query reads the same way
+    w = chunk_args(T=4096, flags=0xff)
+    w.struct_size = v1
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(w)) == _lib.chunk_workspace_raw(chunk_args(T=4096))
 
 
 def test_workspace_query():
@@ -122,6 +149,8 @@ def step_args(**kw):
     (dict(o=5 * FAKE), "KDA_ERR_ALIAS"),
     (dict(final_state=FAKE), "KDA_ERR_ALIAS"),
     (dict(initial_state=7 * FAKE + 256), "KDA_ERR_ALIAS"),
+    (dict(flags=16), "KDA_ERR_UNSUPPORTED"),
+    (dict(flags=_lib.KDA_FLAG_GATE_SOFTPLUS, gate_scale=-0.5), "KDA_ERR_BAD_SHAPE"),
 ])
 def test_recurrent_step_rejects(kw, status):
     rc = _lib.recurrent_step_raw(step_args(**kw))

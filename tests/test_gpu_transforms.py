@@ -1,0 +1,106 @@
+"""GPU parity of the fused input transforms against the fp64 oracle.
+
+Inputs come before the last two steps of the synthetic recipe (``fused=True``):
+q and k unnormalised, g the gate logits.  The kernels apply the per-token L2
+norm of q and k and the log-gate -gate_scale * softplus(z) themselves; the
+oracle applies the same transforms in fp64.  Same metric and tolerances as
+the other parity tests (per (sequence, head) slice, 2e-3 for bf16 inputs,
+1e-5 for fp32).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gated_delta_rule_52_amd.inputs import decode_step_pool, make_decode_state, make_prefill
+from kda_testlib import TOL_BF16, TOL_FP32, dev, say, slice_errors, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import gated_delta_rule_52_amd as m
+    from gated_delta_rule_52_amd import _lib
+    _lib.load()
+    return m
+
+
+def oracle_fused(x, heads):
+    return oracle.forward(x.q, x.k, x.v, x.g, x.beta, h0=None if x.h0 is None else x.h0.astype(np.float64),
+                          cu_seqlens=x.cu_seqlens, heads=heads, **x.transforms())
+
+
+def check(kda, x, path="chunk"):
+    import torch
+    tol = TOL_FP32 if x.in_dtype == "fp32" else TOL_BF16
+    heads = list(range(x.H))
+    say(f"case {x.name} ({path}): B={x.B} T={x.T} H={x.H} dk={x.dk} dv={x.dv} N={x.N} "
+        f"dtype={x.in_dtype} transforms={x.transforms()}")
+    d = upload(x)
+    fn = kda.chunk_fwd if path == "chunk" else kda.recurrent_fwd
+    o, hT = fn(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["h0"], cu_seqlens=d["cu"],
+               out_dtype=torch.float32, **x.transforms())
+    torch.cuda.synchronize()
+    o_ref, h_ref = oracle_fused(x, heads)
+    eo, es = slice_errors(o.cpu().numpy(), hT.cpu().numpy(), o_ref, h_ref, x, heads)
+    say(f"  max slice rel err: o={eo:.3e} state={es:.3e} (tol {tol:g})")
+    assert eo <= tol and es <= tol, (eo, es)
+
+
+def test_bf16_matrix_core_path(kda):
+    """dk = dv = 128, bf16: the matrix-core prep with the transforms, several
+    chunks and a ragged tail, two sequences."""
+    check(kda, make_prefill(110, 2, 200, 3, 128, 128, h0_std=0.3, fused=True, name="fused_bf16"))
+
+
+def test_bf16_exact_chunks(kda):
+    """gate_scale 3: chunks decay past e^-80, so the pair-by-pair prep path
+    runs with the transforms too."""
+    check(kda, make_prefill(111, 1, 160, 2, 128, 128, gscale=3.0, h0_std=0.3, fused=True, name="fused_exact"))
+
+
+@pytest.mark.parametrize("dk,dv,dt", [(64, 64, "fp32"), (128, 128, "fp32"), (64, 128, "bf16")])
+def test_fp32_path(kda, dk, dv, dt):
+    check(kda, make_prefill(112, 1, 150, 2, dk, dv, in_dtype=dt, h0_std=0.3, fused=True,
+                            name=f"fused_{dk}x{dv}_{dt}"))
+
+
+def test_varlen_long_retention(kda):
+    x = make_prefill(113, 1, 0, 2, 128, 128, gscale=0.01, h0_std=0.02, fused=True,
+                     seqlens=[300, 0, 1, 64, 129], name="fused_varlen")
+    check(kda, x)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_recurrent_fwd(kda, dt):
+    check(kda, make_prefill(114, 2, 40, 2, 128, 128, in_dtype=dt, h0_std=0.3, fused=True,
+                            name=f"fused_rec_{dt}"), path="recurrent")
+
+
+@pytest.mark.parametrize("dk,dv,dt", [(128, 128, "bf16"), (64, 128, "fp32")])
+def test_decode_steps(kda, dk, dv, dt):
+    """Eight in-place decode steps with the transforms against the oracle's
+    steps (state chained in fp64)."""
+    import torch
+    N, H, steps, gs = 6, 3, 8, 0.5
+    rng, S0 = make_decode_state(115, N, H, dk, dv, std=0.3)
+    P = decode_step_pool(rng, steps, N, H, dk, dv, in_dtype=dt, fused=True)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    tol = TOL_FP32 if dt == "fp32" else TOL_BF16
+    S = dev(S0, torch.float32)
+    ref = S0.astype(np.float64)
+    worst = 0.0
+    for t in range(steps):
+        o = kda.recurrent_step(dev(P["q"][t], tdt), dev(P["k"][t], tdt), dev(P["v"][t], tdt),
+                               dev(P["g"][t], torch.float32), dev(P["beta"][t], tdt), S,
+                               out_dtype=torch.float32, qk_l2norm=True, gate_logits=True, gate_scale=gs)
+        o_ref, ref = oracle.decode_step(P["q"][t], P["k"][t], P["v"][t], P["g"][t], P["beta"][t], ref,
+                                        qk_l2norm=True, gate_logits=True, gate_scale=gs)
+        torch.cuda.synchronize()
+        eo = np.linalg.norm(o.cpu().numpy() - o_ref) / np.linalg.norm(o_ref)
+        es = np.linalg.norm(S.cpu().numpy() - ref) / np.linalg.norm(ref)
+        worst = max(worst, eo, es)
+    say(f"case decode transforms dk={dk} dv={dv} {dt}: worst rel err over {steps} steps {worst:.3e} (tol {tol:g})")
+    assert worst <= tol
