@@ -21,6 +21,9 @@ for kernels that apply them themselves: q and k are left unnormalised
 the log-gate being -gscale * softplus(z).  ``transforms()`` names what the
 consumer must then apply.
 
+With ``scalar_gate=True`` the gate logits are drawn per token and head only
+([B, T, H]): one forget rate for every key channel, Gated DeltaNet's gate.
+
 bf16 inputs are rounded once, round-to-nearest-even, and returned as float32
 arrays that hold the exact bf16 values, so converting them to bf16 on the
 device is lossless and the oracle sees exactly what the GPU sees.
@@ -91,13 +94,15 @@ class KdaInputs:
     name: str = ""
     meta: dict = field(default_factory=dict)
     fused: bool = False  # q, k unnormalised and g = gate logits (see module docstring)
+    scalar_gate: bool = False  # g is [B, T, H]: one gate per token and head
 
     def transforms(self) -> dict:
-        """Input transforms the consumer applies: none, or for ``fused``
+        """Input forms the consumer handles: the gate layout, and for ``fused``
         inputs the in-kernel L2 norm and the softplus gate with its scale."""
         if not self.fused:
-            return dict(qk_l2norm=False, gate_logits=False, gate_scale=1.0)
-        return dict(qk_l2norm=True, gate_logits=True, gate_scale=float(self.meta["gscale"]))
+            return dict(qk_l2norm=False, gate_logits=False, gate_scale=1.0, scalar_gate=self.scalar_gate)
+        return dict(qk_l2norm=True, gate_logits=True, gate_scale=float(self.meta["gscale"]),
+                    scalar_gate=self.scalar_gate)
 
     @property
     def B(self) -> int:
@@ -140,7 +145,7 @@ def make_prefill(seed: int, B: int, T: int, H: int, dk: int, dv: int,
                  h0_std: Optional[float] = None,
                  seqlens: Optional[np.ndarray] = None,
                  lengths_range: Optional[tuple] = None, n_seqs: int = 0,
-                 name: str = "", fused: bool = False) -> KdaInputs:
+                 name: str = "", fused: bool = False, scalar_gate: bool = False) -> KdaInputs:
     """Draw one prefill problem.
 
     For packed variable-length input either pass ``seqlens`` or
@@ -163,7 +168,7 @@ def make_prefill(seed: int, B: int, T: int, H: int, dk: int, dv: int,
     k = rng.standard_normal((B, T, H, dk), dtype=f32)
     v = rng.standard_normal((B, T, H, dv), dtype=f32)
     bl = rng.standard_normal((B, T, H), dtype=f32)
-    gl = rng.standard_normal((B, T, H, dk), dtype=f32)
+    gl = rng.standard_normal((B, T, H) if scalar_gate else (B, T, H, dk), dtype=f32)
     h0 = None
     if h0_std is not None:
         h0 = (h0_std * rng.standard_normal((N, H, dk, dv), dtype=f32)).astype(f32)
@@ -174,7 +179,8 @@ def make_prefill(seed: int, B: int, T: int, H: int, dk: int, dv: int,
     g = gl if fused else (-np.float32(gscale) * softplus(gl)).astype(f32)
     return KdaInputs(q=q, k=k, v=v, g=g, beta=beta, h0=h0, cu_seqlens=cu,
                      in_dtype=in_dtype, name=name,
-                     meta=dict(seed=seed, gscale=gscale, h0_std=h0_std), fused=fused)
+                     meta=dict(seed=seed, gscale=gscale, h0_std=h0_std), fused=fused,
+                     scalar_gate=scalar_gate)
 
 
 def make_decode_state(seed: int, N: int, H: int, dk: int, dv: int,
@@ -186,16 +192,17 @@ def make_decode_state(seed: int, N: int, H: int, dk: int, dv: int,
 
 
 def decode_steps(rng, steps: int, N: int, H: int, dk: int, dv: int,
-                 in_dtype: str = "bf16", gscale: float = 1.0, fused: bool = False) -> Iterator[dict]:
+                 in_dtype: str = "bf16", gscale: float = 1.0, fused: bool = False,
+                 scalar_gate: bool = False) -> Iterator[dict]:
     """Yield one token per sequence per step: q, k, g [N,H,dk]; v [N,H,dv]; beta [N,H].
-    ``fused`` as for make_prefill: q, k unnormalised and g the gate logits."""
+    ``fused`` and ``scalar_gate`` (g [N,H]) as for make_prefill."""
     f32 = np.float32
     for _ in range(steps):
         q = rng.standard_normal((N, H, dk), dtype=f32)
         k = rng.standard_normal((N, H, dk), dtype=f32)
         v = rng.standard_normal((N, H, dv), dtype=f32)
         bl = rng.standard_normal((N, H), dtype=f32)
-        gl = rng.standard_normal((N, H, dk), dtype=f32)
+        gl = rng.standard_normal((N, H) if scalar_gate else (N, H, dk), dtype=f32)
         yield dict(q=_maybe_bf16(q if fused else l2_normalise(q), in_dtype),
                    k=_maybe_bf16(k if fused else l2_normalise(k), in_dtype),
                    v=_maybe_bf16(v, in_dtype),
@@ -204,12 +211,13 @@ def decode_steps(rng, steps: int, N: int, H: int, dk: int, dv: int,
 
 
 def decode_step_pool(rng, pool: int, N: int, H: int, dk: int, dv: int,
-                     in_dtype: str = "bf16", gscale: float = 1.0, fused: bool = False) -> dict:
+                     in_dtype: str = "bf16", gscale: float = 1.0, fused: bool = False,
+                     scalar_gate: bool = False) -> dict:
     """Draw ``pool`` token batches for the decode workload, stacked on a
     leading axis: q, k, g [pool,N,H,dk]; v [pool,N,H,dv]; beta [pool,N,H].
     Step s of a long decode run uses batch s % pool (each step still reads
     its own copy at its own device offset)."""
-    steps = list(decode_steps(rng, pool, N, H, dk, dv, in_dtype, gscale, fused))
+    steps = list(decode_steps(rng, pool, N, H, dk, dv, in_dtype, gscale, fused, scalar_gate))
     return {k: np.stack([s[k] for s in steps]) for k in steps[0]}
 
 

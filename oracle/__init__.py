@@ -46,7 +46,7 @@ def _load():
             i64, ctypes.POINTER(ctypes.c_int64), i64, i64, i64,
             fp, fp, fp, fp, fp, dp, ctypes.c_double,
             ctypes.POINTER(ctypes.c_int32), i64, dp, dp, ctypes.c_int,
-            ctypes.c_int, ctypes.c_int, ctypes.c_double]
+            ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int]
         lib.kda_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -67,7 +67,7 @@ def _ptr(a, t):
 def forward(q, k, v, g, beta, h0=None, cu_seqlens=None, scale: float = 1.0,
             heads: Optional[Sequence[int]] = None, nthreads: int = 0,
             want_state: bool = True, qk_l2norm: bool = False,
-            gate_logits: bool = False, gate_scale: float = 1.0):
+            gate_logits: bool = False, gate_scale: float = 1.0, scalar_gate: bool = False):
     """fp64 token recurrence.
 
     q, k, g: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H] (any float
@@ -80,6 +80,8 @@ def forward(q, k, v, g, beta, h0=None, cu_seqlens=None, scale: float = 1.0,
     qk_l2norm: q and k are L2-normalised per token and head first
     (x / sqrt(sum x^2 + 1e-6)).  gate_logits: g holds logits z and the
     log-gate is -gate_scale * softplus(z).  Both in fp64, see kda_oracle.c.
+    scalar_gate: g is [B, T, H], one gate per token and head for all key
+    channels (Gated DeltaNet).
     """
     lib = _load()
     q, k, v, g, beta = map(_f32, (q, k, v, g, beta))
@@ -101,7 +103,7 @@ def forward(q, k, v, g, beta, h0=None, cu_seqlens=None, scale: float = 1.0,
         _ptr(g, ctypes.c_float), _ptr(beta, ctypes.c_float), _ptr(h0a, ctypes.c_double),
         float(scale), hs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), nh,
         _ptr(o, ctypes.c_double), _ptr(hT, ctypes.c_double), int(nthreads),
-        int(bool(qk_l2norm)), int(bool(gate_logits)), float(gate_scale))
+        int(bool(qk_l2norm)), int(bool(gate_logits)), float(gate_scale), int(bool(scalar_gate)))
     if rc != 0:
         raise RuntimeError(f"kda_oracle_forward failed with code {rc}")
     return o, hT

@@ -29,6 +29,9 @@
  *  - gate_logits: g holds logits z and the log-gate is
  *    g_t = -gate_scale * softplus(z_t), softplus(z) = log(1 + exp(z)), the
  *    form of the synthetic gate recipe.
+ * With scalar_gate, g holds one value per token and head ([T_total, H]) that
+ * applies to every key channel: Gated DeltaNet's scalar forget gate, which
+ * the pages name as the special case KDA generalises.
  *
  * Arithmetic is fp64 throughout; inputs arrive as float32 arrays holding the
  * exact values the GPU receives (bf16 values are exactly representable in
@@ -72,7 +75,7 @@ int kda_oracle_forward(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk,
                        const float *g, const float *beta, const double *h0,
                        double scale, const int32_t *heads, int64_t nh, double *o,
                        double *hT, int nthreads, int qk_l2norm, int gate_logits,
-                       double gate_scale)
+                       double gate_scale, int scalar_gate)
 {
     if (n_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0 || nh <= 0)
         return 1;
@@ -121,8 +124,8 @@ int kda_oracle_forward(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk,
             const double b = (double)beta[t * H + h];
             /* S~ = Diag(exp(g_t)) S_{t-1} */
             for (int64_t i = 0; i < dk; ++i) {
-                const double gi = gate_logits ? -gate_scale * softplus((double)g[base_k + i])
-                                              : (double)g[base_k + i];
+                const double graw = scalar_gate ? (double)g[t * H + h] : (double)g[base_k + i];
+                const double gi = gate_logits ? -gate_scale * softplus(graw) : graw;
                 const double a = exp(gi);
                 for (int64_t j = 0; j < dv; ++j)
                     S[i * dv + j] *= a;

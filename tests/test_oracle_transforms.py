@@ -13,7 +13,9 @@ They are pinned here against facts that hold without the oracle:
 * invariance to a positive per-token rescaling of q and of k;
 * rows that are already exactly unit-norm (Hadamard rows) pass unchanged;
 * the gate equals the log-gate formed with numpy's logaddexp (log(e^0 + e^z));
-* closed forms: z = 0 gives alpha = 2^-gate_scale, z -> -inf gives alpha = 1.
+* closed forms: z = 0 gives alpha = 2^-gate_scale, z -> -inf gives alpha = 1;
+* a scalar gate per token and head (g of shape [B, T, H]) is Gated DeltaNet:
+  the separately written numpy Gated DeltaNet gives the same result.
 
 Deliberately wrong transforms (planted on the CPU) show that each pin set
 catches the plausible mistakes.
@@ -22,6 +24,7 @@ import numpy as np
 import pytest
 
 import oracle
+from oracle import reference as ref
 from gated_delta_rule_52_amd.inputs import make_prefill
 from test_oracle import hadamard_keys, rel
 
@@ -108,8 +111,25 @@ def pin_gate_closed_forms(fwd):
             and rel(c[0], d[0]) < 1e-12 and rel(c[1], d[1]) < 1e-12)
 
 
+def pin_scalar_gate_is_gdn(fwd):
+    """One gate per token and head, for every key channel: the recurrence is
+    Gated DeltaNet, S_t = alpha_t (I - beta k k^T) S + beta k v^T (independent
+    numpy form), with alpha = exp(g), or exp(-s softplus(z)) from logits."""
+    x = make_prefill(98, 1, 13, 2, 6, 4, in_dtype="fp32", h0_std=0.5, scalar_gate=True)
+    ok = True
+    for logits, s in ((False, 1.0), (True, 0.6)):
+        g = x.g.astype(np.float64)
+        lg = -s * np.logaddexp(0.0, g) if logits else g
+        o, hT = fwd(x.q, x.k, x.v, x.g, x.beta, h0=x.h0, qk_l2norm=False, gate_logits=logits,
+                    gate_scale=s, scalar_gate=True)
+        o2, S2 = ref.gated_deltanet(x.q[0], x.k[0], x.v[0], np.exp(lg[0]), x.beta[0], x.h0[0])
+        # 1e-6: a harness that forms the log-gate itself hands it over in float32
+        ok = ok and max(rel(o[0], o2), rel(hT[0], S2)) < (1e-6 if logits else 1e-12)
+    return ok
+
+
 PINS = [pin_l2_worked_example, pin_l2_scale_invariance, pin_l2_unit_rows_unchanged,
-        pin_gate_logaddexp, pin_gate_closed_forms]
+        pin_gate_logaddexp, pin_gate_closed_forms, pin_scalar_gate_is_gdn]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -122,8 +142,13 @@ def test_oracle_transform_pin(pin):
 def make_transformed(mutation=None):
     """Apply the transforms in numpy (one planted mistake, or none), then the
     oracle with both switched off."""
-    def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, qk_l2norm=False, gate_logits=False, gate_scale=1.0):
+    def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, qk_l2norm=False, gate_logits=False, gate_scale=1.0,
+            scalar_gate=False):
         q, k, g = (np.asarray(a, np.float64) for a in (q, k, g))
+        if scalar_gate:  # one gate per token and head, for every key channel
+            g = np.repeat(g[..., None], q.shape[-1], axis=-1)
+            if mutation == "scalar_gate_first_channel":
+                g[..., 1:] = -60.0 if gate_logits else 0.0
         if qk_l2norm:
             def nrm(x):
                 if mutation == "l2_no_sqrt":
@@ -144,7 +169,7 @@ def make_transformed(mutation=None):
 
 
 MUTATIONS = ["l2_no_sqrt", "l2_l1", "l2_q_only", "l2_k_only", "gate_plus", "gate_no_scale",
-             "gate_exp", "gate_log_only", "gate_relu"]
+             "gate_exp", "gate_log_only", "gate_relu", "scalar_gate_first_channel"]
 
 
 def test_numpy_transform_passes_all_pins():
