@@ -38,11 +38,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def prefill_alg_bytes(B, T, H, dk, dv, N, in_bytes=2, out_bytes=2, h0=True, hT=True):
+def prefill_alg_bytes(B, T, H, dk, dv, N, in_bytes=2, out_bytes=2, h0=True, hT=True, gate_width=None):
     """Algorithmic HBM bytes of one prefill: every input read once, every
-    output written once, no intermediates."""
+    output written once, no intermediates.  gate_width: fp32 gate values per
+    token and head (dk, or 1 for a scalar gate)."""
     th = B * T * H
-    per_th = (2 * dk + dv + 1) * in_bytes + dk * 4 + dv * out_bytes
+    gw = dk if gate_width is None else gate_width
+    per_th = (2 * dk + dv + 1) * in_bytes + gw * 4 + dv * out_bytes
     return th * per_th + (int(h0) + int(hT)) * N * H * dk * dv * 4
 
 
@@ -294,7 +296,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode and append lines")
     ap.add_argument("--no-append", action="store_true", help="skip the append line")
-    ap.add_argument("--no-fused", action="store_true", help="skip the fused input-transform line")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the fused input-transform and scalar-gate lines")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -359,6 +362,15 @@ def main():
             "tokens_per_s": xf.B * xf.T / (msf * 1e-3),
             "roofline": {"bound": "hbm", "achieved": fach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": fach / HBM_PEAK_GBS, "alg_bytes_per_launch": fbytes},
+        }
+        xs, mss, pers, _ = time_prefill(args, "prefill_64k_scalar_gate")
+        sbytes = prefill_alg_bytes(xs.B, xs.T, xs.H, xs.dk, xs.dv, xs.N, gate_width=1)
+        sach = sbytes / (mss * 1e-3) / 1e9
+        rec["scalar_gate"] = {
+            "workload": "prefill_64k_scalar_gate", "ms_per_step": mss, "ms_median": float(np.median(pers)),
+            "tokens_per_s": xs.B * xs.T / (mss * 1e-3), "vs_channel_gate": ms / mss,
+            "roofline": {"bound": "hbm", "achieved": sach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": sach / HBM_PEAK_GBS, "alg_bytes_per_launch": sbytes},
         }
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(x)

@@ -15,6 +15,7 @@ KDA_DTYPE_BF16 = 0
 KDA_DTYPE_FP32 = 1
 KDA_FLAG_QK_L2NORM = 1
 KDA_FLAG_GATE_SOFTPLUS = 2
+KDA_FLAG_SCALAR_GATE = 4
 
 STATUS = {
     0: "KDA_OK", 1: "KDA_ERR_NULL_POINTER", 2: "KDA_ERR_BAD_SHAPE", 3: "KDA_ERR_UNSUPPORTED",

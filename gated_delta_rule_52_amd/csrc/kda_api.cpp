@@ -63,7 +63,7 @@ kda_status read_args(const Args *a, Args &out) {
         out.flags = 0;
         out.gate_scale = 1.f;
     }
-    if (out.flags & ~(KDA_FLAG_QK_L2NORM | KDA_FLAG_GATE_SOFTPLUS))
+    if (out.flags & ~(KDA_FLAG_QK_L2NORM | KDA_FLAG_GATE_SOFTPLUS | KDA_FLAG_SCALAR_GATE))
         return fail(KDA_ERR_UNSUPPORTED, "unknown flags 0x%x", out.flags);
     if ((out.flags & KDA_FLAG_GATE_SOFTPLUS) && !(std::isfinite(out.gate_scale) && out.gate_scale >= 0.f))
         return fail(KDA_ERR_BAD_SHAPE, "gate_scale must be finite and >= 0");
@@ -76,7 +76,14 @@ kda::InputXform xform_of(const Args *a) {
     x.qk_l2norm = (a->flags & KDA_FLAG_QK_L2NORM) != 0;
     x.gate_softplus = (a->flags & KDA_FLAG_GATE_SOFTPLUS) != 0;
     x.gate_scale = a->gate_scale;
+    x.scalar_gate = (a->flags & KDA_FLAG_SCALAR_GATE) != 0;
     return x;
+}
+
+// fp32 gate values per token and head: dk, or 1 with a scalar gate
+template <class Args>
+size_t gate_width(const Args *a) {
+    return (a->flags & KDA_FLAG_SCALAR_GATE) ? 1 : static_cast<size_t>(a->dk);
 }
 
 // Checks shared by kda_chunk_fwd and kda_chunk_fwd_workspace_bytes (on a struct read by read_args).
@@ -112,7 +119,7 @@ kda_status check_prefill_buffers(const kda_chunk_fwd_args *a) {
     const size_t in_sz = dsize(a->in_dtype);
     const Range ro = range_of(a->o, th * a->dv * dsize(a->out_dtype));
     const Range ins[] = {range_of(a->q, th * a->dk * in_sz), range_of(a->k, th * a->dk * in_sz),
-                         range_of(a->v, th * a->dv * in_sz), range_of(a->g, th * a->dk * 4),
+                         range_of(a->v, th * a->dv * in_sz), range_of(a->g, th * gate_width(a) * 4),
                          range_of(a->beta, th * in_sz)};
     const size_t sbytes = static_cast<size_t>(N) * a->H * a->dk * a->dv * 4;
     for (const Range &r : ins)
@@ -178,7 +185,7 @@ kda_status kda_chunk_fwd(const kda_chunk_fwd_args *user) {
     const size_t in_sz = dsize(a->in_dtype);
     const Range ro = range_of(a->o, th * a->dv * dsize(a->out_dtype));
     const Range ins[] = {range_of(a->q, th * a->dk * in_sz), range_of(a->k, th * a->dk * in_sz),
-                         range_of(a->v, th * a->dv * in_sz), range_of(a->g, th * a->dk * 4),
+                         range_of(a->v, th * a->dv * in_sz), range_of(a->g, th * gate_width(a) * 4),
                          range_of(a->beta, th * in_sz)};
     const size_t sbytes = static_cast<size_t>(N) * a->H * a->dk * a->dv * 4;
     const size_t need = kda::chunk_workspace_bytes(a->B, a->T, a->H, a->dk, a->dv, N, a->chunk_size,
@@ -264,7 +271,7 @@ kda_status kda_recurrent_step(const kda_recurrent_step_args *user) {
     const Range ro = range_of(a->o, nh * a->dv * dsize(a->out_dtype));
     const Range rf = range_of(a->final_state, sbytes);
     const Range ins[] = {range_of(a->q, nh * a->dk * in_sz), range_of(a->k, nh * a->dk * in_sz),
-                         range_of(a->v, nh * a->dv * in_sz), range_of(a->g, nh * a->dk * 4),
+                         range_of(a->v, nh * a->dv * in_sz), range_of(a->g, nh * gate_width(a) * 4),
                          range_of(a->beta, nh * in_sz)};
     for (const Range &r : ins)
         if (overlap(ro, r) || overlap(rf, r)) return fail(KDA_ERR_ALIAS, "an output overlaps an input");

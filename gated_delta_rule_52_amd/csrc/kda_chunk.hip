@@ -153,7 +153,8 @@ chunk_fp32_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
 #pragma unroll
             for (int m = 0; m < RP; ++m) {
                 const int r = part * RP + m;
-                gv[m] = r < L ? ix.log_gate(g[((c0 + r) * H + h) * DK + c]) : 0.f;
+                const int64_t gi = ix.scalar_gate ? (c0 + r) * H + h : ((c0 + r) * H + h) * DK + c;
+                gv[m] = r < L ? ix.log_gate(g[gi]) : 0.f;
             }
             float acc = 0.f;
 #pragma unroll

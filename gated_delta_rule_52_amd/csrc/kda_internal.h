@@ -15,7 +15,8 @@ struct InputXform {
     bool qk_l2norm;      // q, k divided by sqrt(sum x^2 + kL2Eps) over dk
     bool gate_softplus;  // g holds logits z; log-gate = -gate_scale softplus(z)
     float gate_scale;
-    bool any() const { return qk_l2norm || gate_softplus; }
+    bool scalar_gate;    // g is [tokens, H]: one gate per token and head for every key channel
+    bool any() const { return qk_l2norm || gate_softplus || scalar_gate; }
     // The log-gate for input value g.  softplus(z) = log(1 + e^z) is taken as
     // max(z, log(1 + e^min(z, 15))): above 15 softplus(z) - z < 3.1e-7, and
     // below it the only loss is 1 + e^z rounding, an absolute error under

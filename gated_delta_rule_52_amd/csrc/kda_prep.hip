@@ -133,7 +133,11 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
     const rsrc_t rs_k = make_rsrc(k + base, 2 * elems);
     const rsrc_t rs_q = make_rsrc(q + base, 2 * elems);
     const rsrc_t rs_v = make_rsrc(v + base, 2 * elems);
-    const rsrc_t rs_g = make_rsrc(g + base, 4 * elems);
+    // the gate: [.., dk] per channel, or one value per row at stride H with a scalar gate (XF only);
+    // the unused resource has size 0, so no load through it touches memory
+    const bool sg = XF && ix.scalar_gate;
+    const rsrc_t rs_g = make_rsrc(g + (sg ? 0 : base), sg ? 0 : 4 * elems);
+    const rsrc_t rs_gs = make_rsrc(g + (sg ? c0 * H + h : 0), sg ? 4 * static_cast<uint32_t>((L - 1) * H + 1) : 0);
     char *pack = packs + (static_cast<int64_t>(bx) * H + h) * kPkBytes;
     const rsrc_t rs_p = make_rsrc(pack, kPkBytes);
     const uint32_t key_lane = 8 * rq8 * tok_stride + 2 * cq;
@@ -153,7 +157,13 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const uint32_t e = m * tok_stride + hh * HC + key_lane;
-                const u2 gg = ld64(rs_g, 4 * e);
+                u2 gg;
+                if (sg) {
+                    const uint32_t gs = ld32(rs_gs, 4 * (8 * rq8 + m) * static_cast<uint32_t>(H));
+                    gg = u2{gs, gs};
+                } else {
+                    gg = ld64(rs_g, 4 * e);
+                }
                 rk[hh][m] = ld32(rs_k, 2 * e);
                 rq[hh][m] = ld32(rs_q, 2 * e);
                 float g0 = __uint_as_float(gg[0]), g1 = __uint_as_float(gg[1]);

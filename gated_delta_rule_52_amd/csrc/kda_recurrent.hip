@@ -82,7 +82,7 @@ recurrent_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
         for (int i = tid; i < DK; i += NT) {
             s_kqa[b][0][i] = In::load(k, tk + i);
             s_kqa[b][1][i] = In::load(q, tk + i);
-            s_kqa[b][2][i] = __expf(xf.log_gate(g[tk + i]));
+            s_kqa[b][2][i] = __expf(xf.log_gate(g[xf.scalar_gate ? t * H + h : tk + i]));
         }
         if (tid == 0) s_beta[b] = In::load(beta, t * H + h);
         const float4 vv = In::load4(v, tv + col);

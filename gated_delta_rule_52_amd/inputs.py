@@ -234,6 +234,9 @@ WORKLOADS = {
     # the same problem handed over before the L2 norm and the gate activation
     "prefill_64k_fused": dict(kind="prefill", seed=2, B=1, T=65536, H=16, dk=128, dv=128,
                               in_dtype="bf16", gscale=1.0, h0_std=0.02, fused=True),
+    # the same shapes with one gate per token and head (Gated DeltaNet's gate)
+    "prefill_64k_scalar_gate": dict(kind="prefill", seed=2, B=1, T=65536, H=16, dk=128, dv=128,
+                                    in_dtype="bf16", gscale=1.0, h0_std=0.02, scalar_gate=True),
     "decode_256x16": dict(kind="decode", seed=3, N=256, H=16, dk=128, dv=128,
                           in_dtype="bf16", gscale=1.0, steps=1024, pool=32, state_std=0.02),
     "append_256x16x64": dict(kind="prefill", seed=5, B=256, T=64, H=16, dk=128, dv=128,

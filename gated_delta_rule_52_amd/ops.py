@@ -34,8 +34,9 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _flags(qk_l2norm: bool, gate_logits: bool) -> int:
-    return (_lib.KDA_FLAG_QK_L2NORM if qk_l2norm else 0) | (_lib.KDA_FLAG_GATE_SOFTPLUS if gate_logits else 0)
+def _flags(qk_l2norm: bool, gate_logits: bool, scalar_gate: bool = False) -> int:
+    return ((_lib.KDA_FLAG_QK_L2NORM if qk_l2norm else 0) | (_lib.KDA_FLAG_GATE_SOFTPLUS if gate_logits else 0)
+            | (_lib.KDA_FLAG_SCALAR_GATE if scalar_gate else 0))
 
 
 def _fill_chunk_args(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, scale,
@@ -79,8 +80,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               chunk_size: int = 64, out_dtype: Optional[torch.dtype] = None,
               output_final_state: bool = True, final_state: Optional[torch.Tensor] = None,
               o: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-              qk_l2norm: bool = False, gate_logits: bool = False, gate_scale: float = 1.0
-              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              qk_l2norm: bool = False, gate_logits: bool = False, gate_scale: float = 1.0,
+              scalar_gate: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise KDA prefill.  Returns (o [B,T,H,dv], final_state [N,H,dk,dv] or None).
 
     q, k: [B,T,H,dk] (bf16 or fp32); v: [B,T,H,dv]; g: [B,T,H,dk] fp32 (log
@@ -92,7 +93,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     Input transforms done inside the kernels: ``qk_l2norm`` divides each
     token's q and k by its L2 norm (plus 1e-6 under the root); with
     ``gate_logits`` g holds logits z and the log-gate is
-    -gate_scale * softplus(z).
+    -gate_scale * softplus(z).  ``scalar_gate``: g is [B,T,H], one gate per token
+    and head for every key channel (Gated DeltaNet).
     """
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -102,7 +104,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     _need(q, "q", (B, T, H, dk), dt)
     _need(k, "k", (B, T, H, dk), dt)
     _need(v, "v", (B, T, H, dv), dt)
-    _need(g, "g", (B, T, H, dk), torch.float32)
+    _need(g, "g", (B, T, H) if scalar_gate else (B, T, H, dk), torch.float32)
     _need(beta, "beta", (B, T, H), dt)
     N = B
     if cu_seqlens is not None:
@@ -123,7 +125,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
     a = _fill_chunk_args(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, scale,
-                         chunk_size, workspace, ws if ws > 0 else 0, _flags(qk_l2norm, gate_logits), gate_scale)
+                         chunk_size, workspace, ws if ws > 0 else 0, _flags(qk_l2norm, gate_logits, scalar_gate),
+                         gate_scale)
     _lib.check(_lib.chunk_fwd_raw(a))
     return o, final_state
 
@@ -133,8 +136,8 @@ def recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   cu_seqlens: Optional[torch.Tensor] = None, scale: float = 1.0,
                   out_dtype: Optional[torch.dtype] = None, output_final_state: bool = True,
                   final_state: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
-                  qk_l2norm: bool = False, gate_logits: bool = False, gate_scale: float = 1.0
-                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                  qk_l2norm: bool = False, gate_logits: bool = False, gate_scale: float = 1.0,
+                  scalar_gate: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Token-by-token fused recurrent forward for short segments (at most a few
     dozen tokens per sequence): the same arguments, shapes, input transforms and
     results as ``chunk_fwd`` (no chunk size, no workspace).  Returns (o, final_state)."""
@@ -146,7 +149,7 @@ def recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     _need(q, "q", (B, T, H, dk), dt)
     _need(k, "k", (B, T, H, dk), dt)
     _need(v, "v", (B, T, H, dv), dt)
-    _need(g, "g", (B, T, H, dk), torch.float32)
+    _need(g, "g", (B, T, H) if scalar_gate else (B, T, H, dk), torch.float32)
     _need(beta, "beta", (B, T, H), dt)
     N = B
     if cu_seqlens is not None:
@@ -164,7 +167,7 @@ def recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     else:
         _need(o, "o", (B, T, H, dv), od)
     a = _fill_chunk_args(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, scale, 64,
-                         flags=_flags(qk_l2norm, gate_logits), gate_scale=gate_scale)
+                         flags=_flags(qk_l2norm, gate_logits, scalar_gate), gate_scale=gate_scale)
     _lib.check(_lib.recurrent_fwd_raw(a))
     return o, final_state
 
@@ -174,7 +177,8 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
                    final_state: Optional[torch.Tensor] = None, scale: float = 1.0,
                    out_dtype: Optional[torch.dtype] = None,
                    o: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
-                   gate_logits: bool = False, gate_scale: float = 1.0) -> torch.Tensor:
+                   gate_logits: bool = False, gate_scale: float = 1.0,
+                   scalar_gate: bool = False) -> torch.Tensor:
     """One decode step for N sequences.  q, k, g: [N,H,dk]; v: [N,H,dv];
     beta: [N,H]; state: [N,H,dk,dv] fp32 (or None for zeros).  The new state
     is written to ``final_state`` (default: ``state`` itself, in place).
@@ -187,7 +191,7 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
     _need(q, "q", (N, H, dk), dt)
     _need(k, "k", (N, H, dk), dt)
     _need(v, "v", (N, H, dv), dt)
-    _need(g, "g", (N, H, dk), torch.float32)
+    _need(g, "g", (N, H) if scalar_gate else (N, H, dk), torch.float32)
     _need(beta, "beta", (N, H), dt)
     if state is not None:
         _need(state, "state", (N, H, dk, dv), torch.float32)
@@ -207,7 +211,7 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
     a.in_dtype = _DT[dt]
     a.out_dtype = _DT[od]
     a.stream = _stream(q.device)
-    a.flags = _flags(qk_l2norm, gate_logits)
+    a.flags = _flags(qk_l2norm, gate_logits, scalar_gate)
     a.gate_scale = float(gate_scale)
     _lib.check(_lib.recurrent_step_raw(a))
     return o

@@ -58,12 +58,18 @@ extern "C" {
  * KDA_FLAG_GATE_SOFTPLUS: g holds gate logits z and the log-gate used is
  *   -gate_scale * softplus(z), softplus(z) = log(1 + exp(z)), so that
  *   alpha = (1 + e^z)^-gate_scale.  gate_scale must be finite and >= 0.
+ * KDA_FLAG_SCALAR_GATE: g holds one value per token and head, [B, T, H]
+ *   ([N, H] for a decode step), applied to every key channel: the scalar
+ *   forget gate of Gated DeltaNet, which the review notes' "Method" section
+ *   names as the case KDA refines channel by channel.  Combines with the
+ *   other flags.
  *
  * Structs of ABI version 1 (struct_size equal to the offset of `flags`) are
  * still accepted and apply no transform.
  */
 #define KDA_FLAG_QK_L2NORM 1u
 #define KDA_FLAG_GATE_SOFTPLUS 2u
+#define KDA_FLAG_SCALAR_GATE 4u
 #define KDA_L2NORM_EPS 1e-6f
 
 typedef enum {
@@ -94,7 +100,8 @@ typedef enum {
  *   q, k : [B, T, H, dk]  in_dtype
  *   v    : [B, T, H, dv]  in_dtype
  *   g    : [B, T, H, dk]  fp32, log of the per-channel forget gate (alpha = exp(g)),
- *                         or gate logits with KDA_FLAG_GATE_SOFTPLUS
+ *                         or gate logits with KDA_FLAG_GATE_SOFTPLUS; [B, T, H]
+ *                         with KDA_FLAG_SCALAR_GATE
  *   beta : [B, T, H]      in_dtype, the per-token, per-head write strength
  *   initial_state : [N, H, dk, dv] fp32, or NULL for zeros
  *   final_state   : [N, H, dk, dv] fp32, or NULL to skip; may equal initial_state
@@ -168,7 +175,8 @@ kda_status kda_recurrent_fwd(const kda_chunk_fwd_args *args);
  *
  * Shapes:
  *   q, k : [N, H, dk] in_dtype;  v : [N, H, dv] in_dtype;  g : [N, H, dk] fp32
- *          (log-gate, or gate logits with KDA_FLAG_GATE_SOFTPLUS)
+ *          (log-gate, or gate logits with KDA_FLAG_GATE_SOFTPLUS; [N, H] with
+ *          KDA_FLAG_SCALAR_GATE)
  *   beta : [N, H] in_dtype
  *   initial_state : [N, H, dk, dv] fp32, or NULL for zeros
  *   final_state   : [N, H, dk, dv] fp32, required; may equal initial_state

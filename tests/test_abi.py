@@ -63,7 +63,7 @@ def chunk_args(**kw):
     (dict(o=FAKE + 64), "KDA_ERR_ALIAS"),
     (dict(final_state=3 * FAKE + 8), "KDA_ERR_ALIAS"),
     (dict(initial_state=7 * FAKE + 4096), "KDA_ERR_ALIAS"),
-    (dict(flags=4), "KDA_ERR_UNSUPPORTED"),
+    (dict(flags=8), "KDA_ERR_UNSUPPORTED"),
     (dict(flags=_lib.KDA_FLAG_GATE_SOFTPLUS, gate_scale=-1.0), "KDA_ERR_BAD_SHAPE"),
     (dict(flags=_lib.KDA_FLAG_GATE_SOFTPLUS, gate_scale=float("nan")), "KDA_ERR_BAD_SHAPE"),
 ])
@@ -83,7 +83,7 @@ def test_chunk_fwd_rejects(kw, status):
     (dict(v=None), "KDA_ERR_NULL_POINTER"),
     (dict(o=2 * FAKE + 8), "KDA_ERR_ALIAS"),
     (dict(final_state=6 * FAKE + 8), "KDA_ERR_ALIAS"),
-    (dict(flags=8), "KDA_ERR_UNSUPPORTED"),
+    (dict(flags=16), "KDA_ERR_UNSUPPORTED"),
     (dict(flags=3, gate_scale=float("inf")), "KDA_ERR_BAD_SHAPE"),
 ])
 def test_recurrent_fwd_rejects(kw, status):
@@ -149,7 +149,7 @@ def step_args(**kw):
     (dict(o=5 * FAKE), "KDA_ERR_ALIAS"),
     (dict(final_state=FAKE), "KDA_ERR_ALIAS"),
     (dict(initial_state=7 * FAKE + 256), "KDA_ERR_ALIAS"),
-    (dict(flags=16), "KDA_ERR_UNSUPPORTED"),
+    (dict(flags=32), "KDA_ERR_UNSUPPORTED"),
     (dict(flags=_lib.KDA_FLAG_GATE_SOFTPLUS, gate_scale=-0.5), "KDA_ERR_BAD_SHAPE"),
 ])
 def test_recurrent_step_rejects(kw, status):

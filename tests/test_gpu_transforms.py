@@ -104,3 +104,46 @@ def test_decode_steps(kda, dk, dv, dt):
         worst = max(worst, eo, es)
     say(f"case decode transforms dk={dk} dv={dv} {dt}: worst rel err over {steps} steps {worst:.3e} (tol {tol:g})")
     assert worst <= tol
+
+
+# ------------------------------------------- scalar gate (Gated DeltaNet's gate)
+
+@pytest.mark.parametrize("fused", [False, True], ids=["log_gate", "logits_l2norm"])
+def test_scalar_gate_bf16(kda, fused):
+    """g of shape [B,T,H] on the matrix-core prep, alone and with both transforms."""
+    check(kda, make_prefill(116, 2, 150, 2, 128, 128, h0_std=0.3, fused=fused, scalar_gate=True,
+                            name=f"scalar_bf16_{'fused' if fused else 'plain'}"))
+
+
+def test_scalar_gate_exact_chunks(kda):
+    check(kda, make_prefill(117, 1, 130, 2, 128, 128, gscale=3.0, h0_std=0.3, scalar_gate=True,
+                            name="scalar_exact"))
+
+
+@pytest.mark.parametrize("dk,dv,dt", [(64, 64, "fp32"), (64, 128, "bf16")])
+def test_scalar_gate_fp32_path(kda, dk, dv, dt):
+    check(kda, make_prefill(118, 1, 99, 2, dk, dv, in_dtype=dt, h0_std=0.3, fused=True, scalar_gate=True,
+                            name=f"scalar_{dk}x{dv}_{dt}"))
+
+
+def test_scalar_gate_recurrent_fwd(kda):
+    check(kda, make_prefill(119, 3, 33, 2, 128, 128, h0_std=0.3, scalar_gate=True, name="scalar_rec"),
+          path="recurrent")
+
+
+def test_scalar_gate_decode_step(kda):
+    import torch
+    N, H, dk, dv = 5, 2, 128, 64
+    rng, S0 = make_decode_state(120, N, H, dk, dv, std=0.3)
+    P = decode_step_pool(rng, 1, N, H, dk, dv, in_dtype="bf16", scalar_gate=True)
+    S = dev(S0, torch.float32)
+    o = kda.recurrent_step(dev(P["q"][0], torch.bfloat16), dev(P["k"][0], torch.bfloat16),
+                           dev(P["v"][0], torch.bfloat16), dev(P["g"][0], torch.float32),
+                           dev(P["beta"][0], torch.bfloat16), S, out_dtype=torch.float32, scalar_gate=True)
+    o_ref, s_ref = oracle.decode_step(P["q"][0], P["k"][0], P["v"][0], P["g"][0], P["beta"][0],
+                                      S0.astype(np.float64), scalar_gate=True)
+    torch.cuda.synchronize()
+    eo = np.linalg.norm(o.cpu().numpy() - o_ref) / np.linalg.norm(o_ref)
+    es = np.linalg.norm(S.cpu().numpy() - s_ref) / np.linalg.norm(s_ref)
+    say(f"case scalar-gate decode: o={eo:.3e} state={es:.3e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
