@@ -31,6 +31,14 @@
 // arrive: the gate logit becomes the log-gate before the cumulative sum, and
 // each row's 1/|k| and 1/|q| (reduced over the 32 lanes that hold the row)
 // scale k and q before any product or maximum is formed.
+//
+// With one gate per token and head (SG instantiation, Gated DeltaNet's gate)
+// the decay leaves the contraction: A_kk[r,i] = beta_r e^{G_r - G_i} (k_r.k_i)
+// and A_qk[r,i] = scale e^{G_r - G_i} (q_r.k_i).  The Gram products then take
+// the raw bf16 inputs as they arrive, one product each (bf16 x bf16 products
+// are exact in the fp32 accumulator), the decay and the L2 norms scale the
+// 64 x 64 results, and e^G, e^{G_L - G} are one exponential per row.  No
+// chunk needs the exact path.
 #include "kda_internal.h"
 #include "kda_mfma.h"
 
@@ -107,12 +115,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 // exceeds exp(-kMaxChunkDecay) in some channel is not written there but
 // appended to the exact list, and EXACT = true redoes it with the pair-by-pair
 // Gram blocks.  Returns early (whole workgroup) for chunks past the segment end.
-template <bool EXACT, bool XF>
+template <bool EXACT, bool XF, bool SG>
 __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, int bx, int h,
                                            const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                            const uint16_t *__restrict__ v, const float *__restrict__ g,
                                            const uint16_t *__restrict__ beta, const SegmentView &sv, int per,
                                            int H, float scale, char *packs, const InputXform ix) {
+    static_assert(!SG || (XF && !EXACT), "the scalar gate runs in the transform instantiation, fast path only");
     const int seg = bx / per, jc = bx - seg * per;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -135,7 +144,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
     const rsrc_t rs_v = make_rsrc(v + base, 2 * elems);
     // the gate: [.., dk] per channel, or one value per row at stride H with a scalar gate (XF only);
     // the unused resource has size 0, so no load through it touches memory
-    const bool sg = XF && ix.scalar_gate;
+    const bool sg = SG || (XF && ix.scalar_gate);
     const rsrc_t rs_g = make_rsrc(g + (sg ? 0 : base), sg ? 0 : 4 * elems);
     const rsrc_t rs_gs = make_rsrc(g + (sg ? c0 * H + h : 0), sg ? 4 * static_cast<uint32_t>((L - 1) * H + 1) : 0);
     char *pack = packs + (static_cast<int64_t>(bx) * H + h) * kPkBytes;
@@ -176,17 +185,17 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
                 r1 += g1;
                 G[hh][m][0] = r0;
                 G[hh][m][1] = r1;
-                if constexpr (!XF) {
-                    mk2 = absmax2(mk2, rk[hh][m]);
-                    mq2 = absmax2(mq2, rq[hh][m]);
-                }
+                mk2 = absmax2(mk2, rk[hh][m]);
+                mq2 = absmax2(mq2, rq[hh][m]);
             }
             sm.op.part[rq8][hh * HC + 2 * cq] = r0;
             sm.op.part[rq8][hh * HC + 2 * cq + 1] = r1;
         }
         if (tid < C) sm.beta[tid] = tid < L ? bf16_to_f32(beta[(c0 + tid) * H + h]) : 0.f;
-        float mk, mq;
-        if constexpr (XF) {
+        float mk = wave_max(absmax2_value(mk2)), mq = wave_max(absmax2_value(mq2));
+#pragma unroll
+        for (int m = 0; m < 8; ++m) nk[m] = nq[m] = 1.f;
+        if (XF && ix.qk_l2norm) {
             // a row's 128 channels sit in the 32 lanes of one half-wave, four per lane
             float ak = 0.f, aq = 0.f;  // largest |k|/|k_row|, |q|/|q_row| of this thread
 #pragma unroll
@@ -201,25 +210,21 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
                     xk = fmaxf(xk, fmaxf(fabsf(k0), fabsf(k1)));
                     xq = fmaxf(xq, fmaxf(fabsf(q0), fabsf(q1)));
                 }
-                nk[m] = nq[m] = 1.f;
-                if (ix.qk_l2norm) {
-                    nk[m] = rsqrtf(half_wave_sum(sk2) + kL2Eps);
-                    nq[m] = rsqrtf(half_wave_sum(sq2) + kL2Eps);
-                }
+                nk[m] = rsqrtf(half_wave_sum(sk2) + kL2Eps);
+                nq[m] = rsqrtf(half_wave_sum(sq2) + kL2Eps);
                 ak = fmaxf(ak, xk * nk[m]);
                 aq = fmaxf(aq, xq * nq[m]);
-                if constexpr (EXACT) {
-                    if (cq == 0) {
-                        nx[8 * rq8 + m] = nk[m];
-                        nx[C + 8 * rq8 + m] = nq[m];
-                    }
-                }
             }
             mk = wave_max(ak);
             mq = wave_max(aq);
-        } else {
-            mk = wave_max(absmax2_value(mk2));
-            mq = wave_max(absmax2_value(mq2));
+        }
+        if constexpr (EXACT && XF) {  // the rows' norms (1 without the L2 norm) for the pairwise entries
+            if (cq == 0)
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    nx[8 * rq8 + m] = nk[m];
+                    nx[C + 8 * rq8 + m] = nq[m];
+                }
         }
         if (lane == 0) {
             atomicMax(&sm.imax[0], __float_as_int(mk));
@@ -237,7 +242,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
         }
         sm.op.part[0][tid] = run;
         sm.gam[tid] = __expf(run);
-        if (run < -kMaxChunkDecay) atomicOr(&sm.imax[5], 1);
+        if (!SG && run < -kMaxChunkDecay) atomicOr(&sm.imax[5], 1);
     }
     const int ek = exp_of(__int_as_float(sm.imax[0]));
     const int eq = exp_of(__int_as_float(sm.imax[1]));
@@ -267,12 +272,33 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
 #pragma unroll
     for (int u = 0; u < JPW; ++u) tacc[u] = zero4();
     uint32_t ekp[2][8];  // fp16 operand pairs of e^G k, kept for the W solve
+    // SG: per-row e^G 2^-ek, e^G 2^-eq scale, e^{G_L - G} 2^-ek, with the rows' L2 norms; and the
+    // rows' G, 1/|k| and 1/|q| in LDS for the Gram epilogue ([C] each), in the low-part area that SG
+    // leaves unused and that the later operand structures never reach
+    float sgE[8], sgQ[8], sgD[8];
+    float *const sgG = reinterpret_cast<float *>(sm.op.g.ckl), *const sgN = sgG + C;
+    static_assert(sizeof(sm.op.s) <= 5 * C * HC * sizeof(uint16_t),
+                  "the operand structures stay clear of the low-part area of the column operand");
+    if constexpr (SG) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const float e = __expf(G[0][m][0]), d = __expf(GL[0][0] - G[0][m][0]);
+            sgE[m] = e * sk * nk[m];
+            sgQ[m] = e * sq * nq[m];
+            sgD[m] = d * sk * nk[m];
+            if (cq == 0) {
+                sgG[8 * rq8 + m] = G[0][m][0];
+                sgN[8 * rq8 + m] = nk[m];
+                sgN[C + 8 * rq8 + m] = nq[m];
+            }
+        }
+    }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         // per channel: m log2(e) with m = G_L / 2, and e^m times the fp16 scales
         float mlg[2], em_sk[2], em_sq[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
+        for (int e = 0; e < 2 && !SG; ++e) {
             mlg[e] = 0.5f * kLog2e * GL[hh][e];
             const float em = __builtin_amdgcn_exp2f(mlg[e]);
             em_sk[e] = em * sk;
@@ -284,6 +310,18 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
             const int r = 8 * rq8 + m;
             float kk[2] = {lo_f(rk[hh][m]), hi_f(rk[hh][m])};
             float qq[2] = {lo_f(rq[hh][m]), hi_f(rq[hh][m])};
+            if constexpr (SG) {  // the Gram operands are the raw inputs
+                *reinterpret_cast<uint32_t *>(&sm.op.g.rkh[g_off(r, 2 * cq)]) = rk[hh][m];
+                *reinterpret_cast<uint32_t *>(&sm.op.g.rqh[g_off(r, 2 * cq)]) = rq[hh][m];
+                ekp[hh][m] = pack_h2(kk[0] * sgE[m], kk[1] * sgE[m]);
+                st32(rs_p, pack_h2(qq[0] * sgQ[m], qq[1] * sgQ[m]), kPkQ + w_col(r, hh * HC + 2 * cq));
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const uint32_t hb = hbits(static_cast<_Float16>(kk[e] * sgD[m]));
+                    kdp[e][m >> 1] = (m & 1) ? (kdp[e][m >> 1] | (hb << 16)) : hb;
+                }
+                continue;
+            }
             if constexpr (XF) {
                 kk[0] *= nk[m];
                 kk[1] *= nk[m];
@@ -353,6 +391,12 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
                 for (int s = 0; s < HC / 32; ++s) {
                     const int ra = g_off(16 * a + n16, 32 * s + 8 * g4);
                     const int cb = g_off(16 * b + n16, 32 * s + 8 * g4);
+                    if constexpr (SG) {  // raw k (columns) against raw k or q (rows): one exact product
+                        const b8 xr = *reinterpret_cast<const b8 *>(rh + ra);
+                        const b8 yc = *reinterpret_cast<const b8 *>(sm.op.g.rkh + cb);
+                        tacc[u] = mmab(yc, xr, tacc[u]);
+                        continue;
+                    }
                     const b8 xh = *reinterpret_cast<const b8 *>(rh + ra);
                     const b8 xl = *reinterpret_cast<const b8 *>(rl + ra);
                     const b8 yh = *reinterpret_cast<const b8 *>(sm.op.g.ckh + cb);
@@ -377,6 +421,15 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
             pair_ab(p, a, b);
             // this lane's entries: row 16 a + n16, columns 16 b + 4 g4 + jj
             f4 v = tacc[u];
+            if constexpr (SG) {  // the decay e^{G_r - G_i} and the rows' L2 norms
+                const int r = 16 * a + n16;
+                const float Gr = sgG[r], nr = isq ? sgN[C + r] : sgN[r];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int i = 16 * b + 4 * g4 + jj;
+                    v[jj] *= __expf(fminf(Gr - sgG[i], 0.f)) * nr * sgN[i];
+                }
+            }
             if (!isq) {  // A_kk = beta k k^T (decayed), strictly lower
                 const float br = sm.beta[16 * a + n16];
 #pragma unroll
@@ -592,16 +645,16 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
 }
 
 // fast path: one workgroup per chunk and head; grid (segments x per, heads).
-// XF: with the input transforms.
-template <bool XF>
+// XF: with the input transforms; SG: scalar gate (implies XF).
+template <bool XF, bool SG>
 __global__ void __launch_bounds__(NT, 3)
 chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                   const uint16_t *__restrict__ v, const float *__restrict__ g,
                   const uint16_t *__restrict__ beta, SegmentView sv, int per, int H, float scale,
                   char *__restrict__ packs, InputXform ix) {
     __shared__ PrepSmem sm;
-    prep_chunk<false, XF>(sm, nullptr, nullptr, blockIdx.x, blockIdx.y, q, k, v, g, beta, sv, per, H, scale, packs,
-                          ix);
+    prep_chunk<false, XF, SG>(sm, nullptr, nullptr, blockIdx.x, blockIdx.y, q, k, v, g, beta, sv, per, H, scale,
+                              packs, ix);
 }
 
 // exact path over the chunks the fast path listed (usually none)
@@ -618,7 +671,7 @@ chunk_prep_exact_kernel(const uint16_t *__restrict__ q, const uint16_t *__restri
     for (int i = blockIdx.x; i < n; i += gridDim.x) {
         const int id = sv.xlist[i];
         __syncthreads();  // the previous chunk's last LDS reads are done
-        prep_chunk<true, XF>(sm, gx, nx, id / H, id % H, q, k, v, g, beta, sv, per, H, scale, packs, ix);
+        prep_chunk<true, XF, false>(sm, gx, nx, id / H, id % H, q, k, v, g, beta, sv, per, H, scale, packs, ix);
     }
 }
 
@@ -635,13 +688,16 @@ void launch_prep(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int 
     const uint16_t *q = static_cast<const uint16_t *>(L.q), *k = static_cast<const uint16_t *>(L.k);
     const uint16_t *v = static_cast<const uint16_t *>(L.v), *b = static_cast<const uint16_t *>(L.beta);
     char *pk = static_cast<char *>(packs);
-    if (L.xf.any()) {
-        hipLaunchKernelGGL(mc::chunk_prep_kernel<true>, dim3(max_segs * per, L.H), dim3(mc::NT), 0, L.stream, q, k, v,
+    if (L.xf.scalar_gate) {  // the scalar-gate Gram is exact at any decay: no exact pass
+        hipLaunchKernelGGL((mc::chunk_prep_kernel<true, true>), dim3(max_segs * per, L.H), dim3(mc::NT), 0, L.stream,
+                           q, k, v, L.g, b, sv, per, L.H, L.scale, pk, L.xf);
+    } else if (L.xf.any()) {
+        hipLaunchKernelGGL((mc::chunk_prep_kernel<true, false>), dim3(max_segs * per, L.H), dim3(mc::NT), 0, L.stream, q, k, v,
                            L.g, b, sv, per, L.H, L.scale, pk, L.xf);
         hipLaunchKernelGGL(mc::chunk_prep_exact_kernel<true>, dim3(256), dim3(mc::NT), 0, L.stream, q, k, v, L.g, b,
                            sv, per, L.H, L.scale, pk, L.xf);
     } else {
-        hipLaunchKernelGGL(mc::chunk_prep_kernel<false>, dim3(max_segs * per, L.H), dim3(mc::NT), 0, L.stream, q, k,
+        hipLaunchKernelGGL((mc::chunk_prep_kernel<false, false>), dim3(max_segs * per, L.H), dim3(mc::NT), 0, L.stream, q, k,
                            v, L.g, b, sv, per, L.H, L.scale, pk, L.xf);
         hipLaunchKernelGGL(mc::chunk_prep_exact_kernel<false>, dim3(256), dim3(mc::NT), 0, L.stream, q, k, v, L.g, b,
                            sv, per, L.H, L.scale, pk, L.xf);
