@@ -103,6 +103,8 @@ kda_status check_chunk_sizes(const kda_chunk_fwd_args *a) {
         return fail(KDA_ERR_BAD_SHAPE, "num_seqs=%d must equal B=%d without cu_seqlens", a->num_seqs, a->B);
     }
     const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
+    if (tokens > INT32_MAX)  // the segment table holds 32-bit token offsets
+        return fail(KDA_ERR_BAD_SHAPE, "B*T=%lld tokens (at most %d)", static_cast<long long>(tokens), INT32_MAX);
     if (tokens * a->H * (a->dk > a->dv ? a->dk : a->dv) > (int64_t{1} << 40))
         return fail(KDA_ERR_BAD_SHAPE, "problem too large");
     return KDA_OK;

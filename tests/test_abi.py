@@ -58,6 +58,7 @@ def chunk_args(**kw):
     (dict(num_seqs=2), "KDA_ERR_BAD_SHAPE"),
     (dict(B=2, num_seqs=2, cu_seqlens=8 * FAKE), "KDA_ERR_BAD_SHAPE"),
     (dict(scale=float("nan")), "KDA_ERR_BAD_SHAPE"),
+    (dict(B=2, num_seqs=2, T=2 ** 30, H=1, dk=64, dv=64), "KDA_ERR_BAD_SHAPE"),  # 2^31 tokens
     (dict(q=None), "KDA_ERR_NULL_POINTER"),
     (dict(o=None), "KDA_ERR_NULL_POINTER"),
     (dict(o=FAKE + 64), "KDA_ERR_ALIAS"),

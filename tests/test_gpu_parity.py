@@ -268,3 +268,71 @@ def test_one_segment_sequences_in_place(kda, dt):
     eo, es = slice_errors(o.cpu().numpy(), S.cpu().numpy(), o_ref, h_ref, x, list(range(x.H)))
     say(f"  max slice rel err: o={eo:.3e} state={es:.3e} (tol {tol:g})")
     assert eo <= tol and es <= tol
+
+
+def forgetting_bound(g, a, b):
+    """Largest factor by which a state entering token a still reaches token b:
+    the per-channel decay over [a, b), maxed over heads and channels (the
+    delta update's (I - beta k k^T) has norm <= 1 for unit keys and beta <= 1)."""
+    return float(np.exp(np.max(np.sum(g[0, a:b].astype(np.float64), axis=0))))
+
+
+def test_one_million_tokens_windows(kda):
+    """T = 2^20 tokens, 2 heads: 256 segments per head, chained by the combine.
+    The oracle cannot replay a million tokens in a test, so windows are checked:
+    the first 4096 tokens from h0, and a window in the middle and at the end
+    (with the final state) from a zero state after a 1024-token burn-in.  The
+    burn-in's decay bounds what the true entering state can contribute; that
+    bound is computed from the data and must be below 1e-30."""
+    import torch
+    T, H, burn, win = 1 << 20, 2, 1024, 2048
+    x = make_prefill(60, 1, T, H, 128, 128, h0_std=0.02, name="1M")
+    say(f"case 1M: B=1 T={T} H={H} dk=dv=128 bf16, windows of {win} after a {burn}-token burn-in")
+    o, hT = run_prefill(kda, x)
+    heads = list(range(H))
+    worst = 0.0
+    for a in (0, T // 2 - 777, T - win - burn):
+        s0 = a if a == 0 else a + burn  # first checked token
+        if a > 0:
+            bound = forgetting_bound(x.g, a, s0)
+            assert bound < 1e-30, bound
+        h0 = x.h0.astype(np.float64) if a == 0 else None
+        sl = lambda arr: arr[:, a:s0 + win]
+        o_ref, h_ref = oracle.forward(sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta), h0=h0, heads=heads)
+        og = o[:, s0:s0 + win].cpu().numpy().astype(np.float64)
+        orf = o_ref[:, s0 - a:]
+        for j in heads:
+            e = np.linalg.norm(og[0, :, j] - orf[0, :, j]) / np.linalg.norm(orf[0, :, j])
+            worst = max(worst, e)
+        if s0 + win == T:  # the final state
+            for j in heads:
+                r = h_ref[0, j]
+                es = np.linalg.norm(hT[0, j].cpu().numpy() - r) / np.linalg.norm(r)
+                worst = max(worst, es)
+        say(f"  window from token {s0}: worst rel err so far {worst:.3e}")
+    assert worst <= TOL_BF16, worst
+
+
+def test_three_thousand_short_sequences(kda):
+    """3000 packed sequences of 1..130 tokens: the segment table over many
+    sequences, one- and two-segment sequences side by side.  Sampled
+    sequences (and the first and last) against the oracle, outputs and final
+    states."""
+    x = make_prefill(61, 1, 0, 2, 128, 128, h0_std=0.3, lengths_range=(1, 130), n_seqs=3000, name="3000seq")
+    say(f"case 3000 sequences: T={x.T} H={x.H}")
+    o, hT = run_prefill(kda, x)
+    o, hT = o.cpu().numpy(), hT.cpu().numpy()
+    rng = np.random.default_rng(62)
+    pick = sorted(set(rng.choice(3000, 40, replace=False).tolist()) | {0, 2999})
+    bounds = x.seq_bounds()
+    worst = 0.0
+    for n in pick:
+        a, b = bounds[n]
+        sl = lambda arr: arr[:, a:b]
+        o_ref, h_ref = oracle.forward(sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta),
+                                      h0=x.h0[n:n + 1].astype(np.float64))
+        for h in range(x.H):
+            worst = max(worst, np.linalg.norm(o[0, a:b, h] - o_ref[0, :, h]) / np.linalg.norm(o_ref[0, :, h]),
+                        np.linalg.norm(hT[n, h] - h_ref[0, h]) / np.linalg.norm(h_ref[0, h]))
+    say(f"  {len(pick)} sampled sequences: worst rel err {worst:.3e}")
+    assert worst <= TOL_BF16, worst
