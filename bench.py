@@ -85,7 +85,7 @@ def stored_traffic():
         return None
 
 
-def time_prefill(args, name="prefill_64k", calibrate=False):
+def time_prefill(args, name="prefill_64k", calibrate=False, sweep=None):
     """Time kda_chunk_fwd on a named workload; ``prefill_64k_fused`` is the same
     problem handed over before the L2 norm and the gate activation, which the
     kernels then apply (the input transforms)."""
@@ -132,6 +132,27 @@ def time_prefill(args, name="prefill_64k", calibrate=False):
     log(f"{'prefill' if name == 'prefill_64k' else name}: {ms:.3f} ms/step (events), median {np.median(per):.3f}, p10 {np.percentile(per, 10):.3f}, "
         f"p90 {np.percentile(per, 90):.3f}, wall {1e3 * wall / args.steps:.3f} ms/step")
     nbytes = prefill_alg_bytes(x.B, x.T, x.H, x.dk, x.dv, x.N)
+    if sweep is not None:
+        # the pages' operator sweep (batch 1, 16 heads, 2K..64K tokens): prefixes of the resident inputs
+        for T in (2048, 4096, 8192, 16384, 32768):
+            sl = lambda a: a[:, :T]
+            o_t = o[:, :T]
+            ws_t = torch.empty(kda.chunk_fwd_workspace_bytes(sl(q), v), dtype=torch.uint8, device=dev)
+            call = lambda: kda.chunk_fwd(sl(q), sl(k), sl(v), sl(g), sl(beta), initial_state=h0, final_state=hT,
+                                         o=o_t, out_dtype=bf, workspace=ws_t, **tr)
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = max(10, 2 * args.steps * 65536 // T // 4)
+            e0.record(stream)
+            for _ in range(reps):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            sweep[T] = e0.elapsed_time(e1) / reps
+            log(f"sweep T={T}: {sweep[T] * 1e3:.1f} us per call")
+        sweep[x.T] = ms
     return x, ms, per, nbytes
 
 
@@ -297,7 +318,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode and append lines")
     ap.add_argument("--no-append", action="store_true", help="skip the append line")
     ap.add_argument("--no-fused", action="store_true",
-                    help="skip the fused input-transform and scalar-gate lines")
+                    help="skip the length sweep and the fused input-transform and scalar-gate lines")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -308,7 +329,8 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    x, ms, per, nbytes = time_prefill(args, calibrate=args.calibrate_copy)
+    sweep = None if args.no_fused else {}
+    x, ms, per, nbytes = time_prefill(args, calibrate=args.calibrate_copy, sweep=sweep)
     copy_gbs = copy_ceiling()
     tok_s = x.B * x.T / (ms * 1e-3)
     ach = nbytes / (ms * 1e-3) / 1e9
@@ -352,6 +374,14 @@ def main():
             "tokens_per_s": xa.B * xa.T / (ra[best] * 1e-6),
             "roofline": {"bound": "hbm", "achieved": aach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": aach / HBM_PEAK_GBS, "alg_bytes_per_launch": abytes},
+        }
+    if sweep:
+        rec["sweep"] = {
+            "workload": "prefixes of prefill_64k (B=1, H=16, dk=dv=128, bf16, h0 and hT)",
+            "ms_per_call": {str(T): t for T, t in sorted(sweep.items())},
+            "tokens_per_s": {str(T): T / (t * 1e-3) for T, t in sorted(sweep.items())},
+            "frac_of_hbm_peak": {str(T): prefill_alg_bytes(1, T, x.H, x.dk, x.dv, 1) / (t * 1e-3) / 1e9 / HBM_PEAK_GBS
+                                 for T, t in sorted(sweep.items())},
         }
     if not args.no_fused:
         xf, msf, perf, fbytes = time_prefill(args, "prefill_64k_fused")

@@ -86,7 +86,8 @@ struct SegmentView {
     const int4 *table;      // [max_segs] {sequence, first token, end token, flags}
     const int32_t *seq_seg; // [N + 1] first segment of each sequence; [N] = count
     int N;
-    float *P;               // [max_segs, H, dk, dk]
+    float *P;               // [max_segs, H, dk, dk] fp32; on the matrix-core path two bf16 planes in the same
+                            // bytes per (segment, head): high parts [dk][dk], then low parts [dk][dk]
     float *Hs;              // [max_segs, H, dk, dv]
     float *sin;             // [max_segs, H, dk, dv] entering states (not filled for one-segment sequences)
     const float *h0;        // [N, H, dk, dv] initial states (null: zero)

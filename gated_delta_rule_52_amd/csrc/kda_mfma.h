@@ -154,6 +154,9 @@ __device__ __forceinline__ uint32_t ld16(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ u2 ld64(rsrc_t r, uint32_t off, int soff = 0) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), soff, 0);
 }
+__device__ __forceinline__ void st16(rsrc_t r, uint32_t v, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(v), r, static_cast<int>(off), 0, 0);
+}
 __device__ __forceinline__ void st32(rsrc_t r, uint32_t v, uint32_t off, int soff = 0) {
     __builtin_amdgcn_raw_buffer_store_b32(v, r, static_cast<int>(off), soff, 0);
 }

@@ -327,7 +327,26 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     } else {
         dst = (pcols ? sv.P : sv.Hs) + (static_cast<int64_t>(seg) * H + h) * DK * DV;
     }
-    if (dst) {
+    if (dst && pcols) {
+        // P as bf16 high and low planes (P = hi + lo to about 16 bits), the operands of the combine's
+        // bf16 products: element (r, c) at 2 (128 r + c) bytes, the low plane 32 KiB further
+        const rsrc_t rs = make_rsrc(dst, 4 * DK * DK);
+        constexpr uint32_t kLoPlane = 2 * DK * DK;
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int jj = 0; jj < 4; jj += 2) {
+                    uint32_t hi, lo;
+                    split2(acc[rt][ct][jj] * pow2(fr[ct]), acc[rt][ct][jj + 1] * pow2(fr[ct]), hi, lo);
+                    const uint32_t o0 = (st_lane + st_off(rt, ct, jj)) / 2, o1 = (st_lane + st_off(rt, ct, jj + 1)) / 2;
+                    st16(rs, hi, o0);
+                    st16(rs, hi >> 16, o1);
+                    st16(rs, lo, kLoPlane + o0);
+                    st16(rs, lo >> 16, kLoPlane + o1);
+                }
+    } else if (dst) {
         const rsrc_t rs = make_rsrc(dst, 4 * DK * DV);
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)

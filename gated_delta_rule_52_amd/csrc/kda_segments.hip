@@ -303,6 +303,134 @@ combine_mfma_kernel(SegmentView sv, const float *h0, float *hT, int H, int DV) {
     if (i < nsteps) step(first + i, 0, pA, hA);
 }
 
+// Combine on bf16 matrix cores for the matrix-core prefill (dk = dv = 128):
+// per (sequence, head, 16-column slice of dv) one workgroup of 8 waves walks
+// the chain entering(s+1) = P_s entering(s) + H_s on its 16 columns of the
+// state (columns evolve independently).  P_s arrives from the local pass as
+// bf16 high and low planes (P = hi + lo to about 16 significant bits); the
+// state slice is split the same way at every step.  Each product is
+// hi.hi + hi.lo + lo.hi on v_mfma_f32_16x16x32_bf16 with fp32 accumulation,
+// about 2^-16 relative error per step, well inside the bf16 path's budget.
+//
+// The chain is bound by memory latency, not arithmetic (a step is 3 x 4
+// products per wave).  Wave w owns row tile w; its P operands (rows 16 w + m,
+// k = 32 t + 8 g .. + 7 for lane (m, g): 16 contiguous bytes of a row of each
+// plane) and H addends go through a ring of four register stages, fetched
+// three steps before their step.  A head's eight slices sit on one XCD (heads
+// fastest in the grid), where P_s is read from HBM once.  The state slice
+// lives in LDS transposed ([column][row]) in hi and lo planes, double
+// buffered: the B operand of block t is 16 contiguous bytes of a column, and
+// the accumulator (rows 16 w + 4 g .. + 3 of column m) goes back as 8
+// contiguous bytes per plane.  One barrier per step.
+constexpr int kSP = 128 + 8;  // padded row stride (bf16) of the transposed state planes
+
+__global__ void __launch_bounds__(512, 1)
+combine_bf16x3_kernel(SegmentView sv, const float *h0, float *hT, int H) {
+    constexpr int DK = 128, DV = 128, NC = 16;  // columns per workgroup
+    typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+    typedef unsigned u4v __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) uint16_t sS[2][2][NC * kSP];  // [buffer][hi, lo][column * kSP + row]
+    const int h = blockIdx.x, slice = blockIdx.y, n = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, m = lane & 15;
+    const int j0 = NC * slice;
+    const int first = sv.seq_seg[n], end = sv.seq_seg[n + 1];
+    const int nsteps = end - first - 1;
+    if (nsteps == 0) return;  // one segment: nothing to carry
+    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * DV;
+
+    {   // entering state of the first segment: thread (row tid / 4, 4 columns of the slice)
+        const int r = tid >> 2, cl = 4 * (tid & 3);
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = h0 ? h0[sbase + static_cast<int64_t>(r) * DV + j0 + cl + e] : 0.f;
+        if (first == end) {  // empty sequence: the final state is the initial state
+            if (hT)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hT[sbase + static_cast<int64_t>(r) * DV + j0 + cl + e] = x[e];
+            return;
+        }
+        float *sin = sv.sin + (static_cast<int64_t>(first) * H + h) * DK * DV;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sin[static_cast<int64_t>(r) * DV + j0 + cl + e] = x[e];
+            const __bf16 hi = static_cast<__bf16>(x[e]);
+            sS[0][0][(cl + e) * kSP + r] = __builtin_bit_cast(uint16_t, hi);
+            sS[0][1][(cl + e) * kSP + r] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[e] - static_cast<float>(hi)));
+        }
+    }
+
+    const int last_seg = end - 2;
+    struct Stage {
+        u4v pa[2][4];  // P operands, [plane][block]
+        f32x4 hb;      // H addends
+    };
+    // unconditional (past the last step it repeats that step's segment), so
+    // that every path through the loop has the same memory operations
+    auto fetch = [&](int seg, Stage &st) {
+        seg = min(seg, last_seg);
+        const char *src = reinterpret_cast<const char *>(sv.P + (static_cast<int64_t>(seg) * H + h) * DK * DK);
+        const float *hs = sv.Hs + (static_cast<int64_t>(seg) * H + h) * DK * DV;
+        const int r = 16 * wave + m;
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                st.pa[pl][t] = *reinterpret_cast<const u4v *>(src + pl * 2 * DK * DK + 2 * (r * DK + 32 * t + 8 * g));
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) st.hb[jj] = hs[(16 * wave + 4 * g + jj) * DV + j0 + m];
+    };
+    auto step = [&](int seg, int b, const Stage &st) {
+        __syncthreads();  // entering(seg) complete in sS[b]; sS[b ^ 1] no longer read
+        f32x4 acc = st.hb;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int o = m * kSP + 32 * t + 8 * g;
+            const bf8 sh = __builtin_bit_cast(bf8, *reinterpret_cast<const u4v *>(&sS[b][0][o]));
+            const bf8 sl = __builtin_bit_cast(bf8, *reinterpret_cast<const u4v *>(&sS[b][1][o]));
+            const bf8 ph = __builtin_bit_cast(bf8, st.pa[0][t]), pl = __builtin_bit_cast(bf8, st.pa[1][t]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, sh, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, sl, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, sh, acc, 0, 0, 0);
+        }
+        float *sin = sv.sin + (static_cast<int64_t>(seg + 1) * H + h) * DK * DV;
+        const int r0 = 16 * wave + 4 * g;
+        unsigned hw[2], lw[2];
+#pragma unroll
+        for (int p2 = 0; p2 < 2; ++p2) {
+            const __bf16 a0 = static_cast<__bf16>(acc[2 * p2]), a1 = static_cast<__bf16>(acc[2 * p2 + 1]);
+            const __bf16 l0 = static_cast<__bf16>(acc[2 * p2] - static_cast<float>(a0));
+            const __bf16 l1 = static_cast<__bf16>(acc[2 * p2 + 1] - static_cast<float>(a1));
+            hw[p2] = __builtin_bit_cast(uint16_t, a0) | (static_cast<unsigned>(__builtin_bit_cast(uint16_t, a1)) << 16);
+            lw[p2] = __builtin_bit_cast(uint16_t, l0) | (static_cast<unsigned>(__builtin_bit_cast(uint16_t, l1)) << 16);
+        }
+        *reinterpret_cast<uint2 *>(&sS[b ^ 1][0][m * kSP + r0]) = make_uint2(hw[0], hw[1]);
+        *reinterpret_cast<uint2 *>(&sS[b ^ 1][1][m * kSP + r0]) = make_uint2(lw[0], lw[1]);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) sin[(r0 + jj) * DV + j0 + m] = acc[jj];
+    };
+    // the ring: step j uses stage j mod 4, refilled for step j + 4 right after
+    Stage s0, s1, s2, s3;
+    fetch(first, s0);
+    fetch(first + 1, s1);
+    fetch(first + 2, s2);
+    fetch(first + 3, s3);
+    int i = 0;
+    for (; i + 4 <= nsteps; i += 4) {
+        step(first + i, 0, s0);
+        fetch(first + i + 4, s0);
+        step(first + i + 1, 1, s1);
+        fetch(first + i + 5, s1);
+        step(first + i + 2, 0, s2);
+        fetch(first + i + 6, s2);
+        step(first + i + 3, 1, s3);
+        fetch(first + i + 7, s3);
+    }
+    if (i < nsteps) step(first + i, 0, s0);
+    if (i + 1 < nsteps) step(first + i + 1, 1, s1);
+    if (i + 2 < nsteps) step(first + i + 2, 0, s2);
+}
+
 }  // namespace
 
 size_t chunk_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int chunk, bool varlen, bool in_bf16) {
@@ -334,7 +462,10 @@ hipError_t launch_chunk(const ChunkLaunch &L) {
     } else {
         launch_fp32_pass<kLocal>(L, sv, p.max_segs);
     }
-    if (L.dk == 128)  // heads fastest: a head's slices share one XCD (workgroups go round-robin over XCDs)
+    if (p.packs)  // P in bf16 planes; one workgroup per (head, 16-column slice, sequence), heads fastest
+        hipLaunchKernelGGL(combine_bf16x3_kernel, dim3(L.H, L.dv / 16, L.N), dim3(512), 0, L.stream, sv, L.h0, L.hT,
+                           L.H);
+    else if (L.dk == 128)  // heads fastest: a head's slices share one XCD (workgroups go round-robin over XCDs)
         hipLaunchKernelGGL(combine_mfma_kernel, dim3(L.H, L.dv / 16, L.N), dim3(256), 0, L.stream, sv, L.h0, L.hT,
                            L.H, L.dv);
     else
