@@ -169,6 +169,153 @@ recurrent_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
     }
 }
 
+// Multi-token form: one wave per (sequence, head, 16-column slice of dv), no
+// barriers.  Lane (c = lane / 4, rg = lane % 4) holds column c of the slice
+// for rows rg R .. rg R + R - 1 (R = DK / 4) of the fp32 state.  Per token:
+// * the token's k, q and alpha (and the L2 norms) are formed once, two
+//   channels per lane, and handed to the lanes that need them through the
+//   wave's own LDS (a wave's LDS accesses are ordered, so no barrier);
+// * S~^T k and S~^T q for column c are R-term partial sums reduced over the
+//   four lanes of a quad by two DPP moves;
+// * the inputs of the next four tokens are in flight while one is processed.
+template <int Ctrl>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+    x += dpp_mov<0xB1>(x);  // quad permute [1, 0, 3, 2]
+    return x + dpp_mov<0x4E>(x);  // quad permute [2, 3, 0, 1]
+}
+
+template <int DK, bool InBf16, bool OutBf16>
+__global__ void __launch_bounds__(64)
+recurrent_seq_kernel(const void *__restrict__ q_, const void *__restrict__ k_, const void *__restrict__ v_,
+                     const float *__restrict__ g, const void *__restrict__ beta_, const float *h0, float *hT,
+                     void *__restrict__ o_, const int32_t *__restrict__ cu_seqlens, int T, int H, int DV,
+                     float scale, InputXform xf) {
+    using In = Elem<InBf16>;
+    using Out = Elem<OutBf16>;
+    const typename In::T *q = static_cast<const typename In::T *>(q_);
+    const typename In::T *k = static_cast<const typename In::T *>(k_);
+    const typename In::T *v = static_cast<const typename In::T *>(v_);
+    const typename In::T *beta = static_cast<const typename In::T *>(beta_);
+    typename Out::T *o = static_cast<typename Out::T *>(o_);
+    constexpr int R = DK / 4;         // rows per lane
+    constexpr int CPL = DK / kWave;   // channels each lane loads per token
+    static_assert(R % 4 == 0 && CPL >= 1, "tiling");
+    __shared__ __attribute__((aligned(16))) float s_in[2][3][DK];  // [buffer][k, q, alpha][channel]
+
+    const int slice = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
+    const int lane = threadIdx.x, c = lane >> 2, rg = lane & 3;
+    const int col = 16 * slice + c;
+    int64_t t0, t1;
+    if (cu_seqlens) {
+        t0 = cu_seqlens[n];
+        t1 = cu_seqlens[n + 1];
+        if (t1 < t0) t1 = t0;
+    } else {
+        t0 = static_cast<int64_t>(n) * T;
+        t1 = t0 + T;
+    }
+    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * DV;
+    float s[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) s[i] = h0 ? h0[sbase + static_cast<int64_t>(rg * R + i) * DV + col] : 0.f;
+
+    // A token's inputs, fetched four tokens ahead into a ring of registers
+    // (a token's arithmetic is far shorter than a global load's latency).
+    struct Tok {
+        float k[CPL], q[CPL], g[CPL], v, b;
+    };
+    auto fetch = [&](int64_t t, Tok &f) {
+        t = t < t1 ? t : t1 - 1;  // past the end: repeat the last token (never used)
+        const int64_t tk = (t * H + h) * DK;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            const int ch = lane * CPL + e;
+            f.k[e] = In::load(k, tk + ch);
+            f.q[e] = In::load(q, tk + ch);
+            f.g[e] = g[xf.scalar_gate ? t * H + h : tk + ch];
+        }
+        f.v = In::load(v, (t * H + h) * static_cast<int64_t>(DV) + col);
+        f.b = In::load(beta, t * H + h);
+    };
+    auto process = [&](int64_t t, const Tok &f) {
+        // the token's k, q, alpha through LDS, and its norms
+        float ik = 1.f, iq = 1.f;
+        if (xf.qk_l2norm) {
+            float kk = 0.f, qq = 0.f;
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) {
+                kk += f.k[e] * f.k[e];
+                qq += f.q[e] * f.q[e];
+            }
+            ik = rsqrtf(wave_sum(kk) + kL2Eps);
+            iq = rsqrtf(wave_sum(qq) + kL2Eps);
+        }
+        const int b = static_cast<int>(t - t0) & 1;  // alternate buffers: no write lands on a row still being read
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            const int ch = lane * CPL + e;
+            s_in[b][0][ch] = f.k[e];
+            s_in[b][1][ch] = f.q[e];
+            s_in[b][2][ch] = __expf(xf.log_gate(f.g[e]));
+        }
+        float kr[R], qr[R], ar[R];
+#pragma unroll
+        for (int i = 0; i < R; i += 4) {
+            const float4 k4 = *reinterpret_cast<const float4 *>(&s_in[b][0][rg * R + i]);
+            const float4 q4 = *reinterpret_cast<const float4 *>(&s_in[b][1][rg * R + i]);
+            const float4 a4 = *reinterpret_cast<const float4 *>(&s_in[b][2][rg * R + i]);
+            kr[i] = k4.x; kr[i + 1] = k4.y; kr[i + 2] = k4.z; kr[i + 3] = k4.w;
+            qr[i] = q4.x; qr[i + 1] = q4.y; qr[i + 2] = q4.z; qr[i + 3] = q4.w;
+            ar[i] = a4.x; ar[i + 1] = a4.y; ar[i + 2] = a4.z; ar[i + 3] = a4.w;
+        }
+        float p0 = 0.f, p1 = 0.f, r0 = 0.f, r1 = 0.f, kq0 = 0.f, kq1 = 0.f;  // two chains each
+#pragma unroll
+        for (int i = 0; i < R; i += 2) {
+            s[i] *= ar[i];
+            s[i + 1] *= ar[i + 1];
+            p0 += s[i] * kr[i];
+            p1 += s[i + 1] * kr[i + 1];
+            r0 += s[i] * qr[i];
+            r1 += s[i + 1] * qr[i + 1];
+            kq0 += kr[i] * qr[i];
+            kq1 += kr[i + 1] * qr[i + 1];
+        }
+        const float p = quad_sum(p0 + p1) * ik;  // S~^T k, k normalised
+        const float r = quad_sum(r0 + r1) * iq;
+        const float kq = quad_sum(kq0 + kq1) * ik * iq;
+        const float d = f.v - p;
+        if (rg == 0) Out::store(o, (t * H + h) * static_cast<int64_t>(DV) + col, scale * (r + f.b * kq * d));
+        const float bkd = f.b * ik * d;
+#pragma unroll
+        for (int i = 0; i < R; ++i) s[i] += bkd * kr[i];
+    };
+
+    if (t0 < t1) {
+        Tok f0, f1, f2, f3;
+        fetch(t0, f0);
+        fetch(t0 + 1, f1);
+        fetch(t0 + 2, f2);
+        fetch(t0 + 3, f3);
+        for (int64_t t = t0; t < t1; t += 4) {
+            process(t, f0);
+            fetch(t + 4, f0);
+            if (t + 1 < t1) process(t + 1, f1);
+            fetch(t + 5, f1);
+            if (t + 2 < t1) process(t + 2, f2);
+            fetch(t + 6, f2);
+            if (t + 3 < t1) process(t + 3, f3);
+            fetch(t + 7, f3);
+        }
+    }
+    if (hT) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) hT[sbase + static_cast<int64_t>(rg * R + i) * DV + col] = s[i];
+    }
+}
+
 template <int DK, int BV>
 static hipError_t launch_rec_dk(const RecurrentLaunch &L) {
     dim3 grid(L.dv / BV, L.H, L.N), block(256);
@@ -183,12 +330,28 @@ static hipError_t launch_rec_dk(const RecurrentLaunch &L) {
     return hipGetLastError();
 }
 
+template <int DK>
+static hipError_t launch_rec_seq(const RecurrentLaunch &L) {
+    dim3 grid(L.dv / 16, L.H, L.N), block(64);
+#define KDA_REC(IB, OB)                                                                                  \
+    hipLaunchKernelGGL((recurrent_seq_kernel<DK, IB, OB>), grid, block, 0, L.stream, L.q, L.k, L.v, L.g, \
+                       L.beta, L.h0, L.hT, L.o, L.cu_seqlens, L.T, L.H, L.dv, L.scale, L.xf)
+    if (L.in_bf16 && L.out_bf16) KDA_REC(true, true);
+    else if (L.in_bf16) KDA_REC(true, false);
+    else if (L.out_bf16) KDA_REC(false, true);
+    else KDA_REC(false, false);
+#undef KDA_REC
+    return hipGetLastError();
+}
+
 hipError_t launch_recurrent(const RecurrentLaunch &L) {
-    // One slice per head for a single token (enough workgroups already);
-    // 32-column slices when tokens are looped, to spread the serial work.
-    const bool narrow = L.multi_token;
-    if (L.dk == 128) return narrow ? launch_rec_dk<128, 32>(L) : (L.dv == 128 ? launch_rec_dk<128, 128>(L) : launch_rec_dk<128, 64>(L));
-    return narrow ? launch_rec_dk<64, 32>(L) : (L.dv == 128 ? launch_rec_dk<64, 128>(L) : launch_rec_dk<64, 64>(L));
+    // A decode step: one workgroup per head's whole state (or half), whose
+    // wide row loads stream the state at the copy rate.  Several tokens: one
+    // wave per 16-column slice, which runs the serial token loop without
+    // barriers.
+    if (L.multi_token) return L.dk == 128 ? launch_rec_seq<128>(L) : launch_rec_seq<64>(L);
+    if (L.dk == 128) return L.dv == 128 ? launch_rec_dk<128, 128>(L) : launch_rec_dk<128, 64>(L);
+    return L.dv == 128 ? launch_rec_dk<64, 128>(L) : launch_rec_dk<64, 64>(L);
 }
 
 }  // namespace kda
