@@ -271,6 +271,44 @@ def time_append(args):
     return x, res, append_alg_bytes(x.B, x.T, x.H, x.dk, x.dv)
 
 
+def time_append_grid():
+    """Which path serves a short append faster: sequences x new tokens (16
+    heads, d = 128, bf16, cached fp32 states), us per call of each."""
+    import torch
+    import gated_delta_rule_52_amd as kda
+    from gated_delta_rule_52_amd.inputs import make_prefill
+    bf, f32 = torch.bfloat16, torch.float32
+    t = lambda a, dt: torch.from_numpy(a).to("cuda:0").to(dt)
+    stream = torch.cuda.current_stream()
+    grid = {}
+    for N in (1, 16, 256):
+        for T in (1, 16, 64):
+            x = make_prefill(7, N, T, 16, 128, 128, h0_std=0.02)
+            q, k, v, beta = t(x.q, bf), t(x.k, bf), t(x.v, bf), t(x.beta, bf)
+            g, h0 = t(x.g, f32), t(x.h0, f32)
+            hT = torch.empty_like(h0)
+            o = torch.empty((N, T, 16, 128), dtype=bf, device="cuda:0")
+            ws = torch.empty(kda.chunk_fwd_workspace_bytes(q, v), dtype=torch.uint8, device="cuda:0")
+            row = {}
+            for name, fn in (("chunk_fwd", lambda: kda.chunk_fwd(q, k, v, g, beta, initial_state=h0, final_state=hT,
+                                                                  o=o, out_dtype=bf, workspace=ws)),
+                             ("recurrent_fwd", lambda: kda.recurrent_fwd(q, k, v, g, beta, initial_state=h0,
+                                                                          final_state=hT, o=o, out_dtype=bf))):
+                for _ in range(3):
+                    fn()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(20):
+                    fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                row[name] = 1e3 * e0.elapsed_time(e1) / 20
+            grid[f"{N}x{T}"] = row
+            log(f"append grid N={N} T={T}: chunk_fwd {row['chunk_fwd']:.1f} us, recurrent_fwd {row['recurrent_fwd']:.1f} us")
+    return grid
+
+
 def copy_ceiling():
     """HBM bandwidth a plain elementwise kernel reaches on this GPU: 1 GiB read
     and 1 GiB written per launch (torch's neg kernel), best of 10 launches."""
@@ -401,6 +439,11 @@ def main():
             "tokens_per_s": xs.B * xs.T / (mss * 1e-3), "vs_channel_gate": ms / mss,
             "roofline": {"bound": "hbm", "achieved": sach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": sach / HBM_PEAK_GBS, "alg_bytes_per_launch": sbytes},
+        }
+    if not (args.no_decode or args.no_append):
+        rec["append_grid"] = {
+            "workload": "N sequences x T new tokens, 16 heads, dk=dv=128, bf16, cached states (key 'NxT')",
+            "us_per_call": time_append_grid(),
         }
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(x)
