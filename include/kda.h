@@ -155,10 +155,11 @@ kda_status kda_chunk_fwd(const kda_chunk_fwd_args *args);
  * decode steps, go to the fused recurrent kernel, which keeps the recurrent
  * state in registers for the whole segment).  The same recurrence as
  * kda_chunk_fwd, computed token by token in order: per (sequence, head,
- * 32-column slice of dv) one workgroup reads its state slice once, applies
- * every token of the sequence, and writes the slice once.  Meant for short
- * appends (speculative decoding, chunked prompt appends); kda_chunk_fwd is the
- * faster choice once sequences are long.
+ * 16-column slice of dv) one wave reads its state slice once, applies every
+ * token of the sequence, and writes the slice once.  Meant for short appends
+ * (speculative decoding, a few tokens per sequence): on MI355X it is the
+ * faster path up to about 16 new tokens per sequence, and kda_chunk_fwd from
+ * about 64 on.
  *
  * Arguments, shapes, dtypes, aliasing rules and errors are those of
  * kda_chunk_fwd; chunk_size, workspace and workspace_bytes are ignored (no
