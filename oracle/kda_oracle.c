@@ -170,3 +170,157 @@ int kda_oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * Gradients of the recurrence above (no input transforms) by reverse-mode
+ * differentiation, step by step backwards through each token:
+ *
+ *   forward:  S~ = Diag(alpha) S_{t-1};  p = S~^T k;  u = v - p;
+ *             S_t = S~ + beta k u^T;  o_t = scale S_t^T q
+ *   backward, with dS the gradient of the loss with respect to S_t
+ *   (dS = d final_state at t = T, 0 if absent):
+ *             dS  += scale q do^T;       dq = scale S_t do
+ *             du   = beta dS^T k;        dk = beta dS u;   dbeta = k^T dS u
+ *             dv   = du;                 dp = -du
+ *             dS~  = dS + k dp^T;        dk += S~ dp
+ *             dg   = rowsum(S~ . dS~)    (d alpha_i times alpha_i)
+ *             dS   = Diag(alpha) dS~     (the gradient for S_{t-1})
+ *   and d initial_state = dS after the first token.
+ *
+ * Every state S_0 .. S_T of a (sequence, head) is kept, so memory is
+ * (T_n + 1) dk dv doubles per pair in flight.  Outputs are double arrays with
+ * the inputs' layouts: dq, dk, dg [T_total, H, dk], dv [T_total, H, dv],
+ * dbeta [T_total, H], dh0 [N, H, dk, dv].  All heads are computed.
+ */
+int kda_oracle_backward(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk,
+                        int64_t dv, const float *q, const float *k, const float *v,
+                        const float *g, const float *beta, const double *h0,
+                        double scale, const float *d_o, const double *dhT,
+                        double *dq, double *dkk, double *dvv, double *dg,
+                        double *dbeta, double *dh0, int nthreads)
+{
+    if (n_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return 1;
+    for (int64_t n = 0; n < n_seqs; ++n)
+        if (cu[n + 1] < cu[n])
+            return 2;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    const int64_t units = n_seqs * H, sz = dk * dv;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t uix = 0; uix < units; ++uix) {
+        const int64_t n = uix / H, h = uix % H, T0 = cu[n], Tn = cu[n + 1] - cu[n];
+        double *S = (double *)malloc(sizeof(double) * (size_t)((Tn + 1) * sz));
+        double *w = (double *)malloc(sizeof(double) * (size_t)(3 * sz + 4 * dk + 4 * dv));
+        if (!S || !w) {
+            free(S);
+            free(w);
+#pragma omp atomic write
+            err = 4;
+            continue;
+        }
+        double *dS = w, *St = w + sz, *dSt = w + 2 * sz;
+        double *kt = w + 3 * sz, *qt = kt + dk, *al = qt + dk, *tmp = al + dk;
+        double *vt = tmp + dk, *u = vt + dv, *dov = u + dv, *du = dov + dv;
+        /* forward, keeping every state */
+        for (int64_t i = 0; i < sz; ++i)
+            S[i] = h0 ? h0[(n * H + h) * sz + i] : 0.0;
+        for (int64_t t = 0; t < Tn; ++t) {
+            const int64_t bk = ((T0 + t) * H + h) * dk, bv = ((T0 + t) * H + h) * dv;
+            const double *Sp = S + t * sz;
+            double *Sn = S + (t + 1) * sz;
+            const double b = (double)beta[(T0 + t) * H + h];
+            for (int64_t j = 0; j < dv; ++j)
+                u[j] = (double)v[bv + j];
+            for (int64_t i = 0; i < dk; ++i) {
+                const double a = exp((double)g[bk + i]);
+                for (int64_t j = 0; j < dv; ++j) {
+                    Sn[i * dv + j] = a * Sp[i * dv + j];
+                    u[j] -= Sn[i * dv + j] * (double)k[bk + i];
+                }
+            }
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j)
+                    Sn[i * dv + j] += b * (double)k[bk + i] * u[j];
+        }
+        /* backward */
+        for (int64_t i = 0; i < sz; ++i)
+            dS[i] = dhT ? dhT[(n * H + h) * sz + i] : 0.0;
+        for (int64_t t = Tn - 1; t >= 0; --t) {
+            const int64_t tt = T0 + t, bk = (tt * H + h) * dk, bv = (tt * H + h) * dv;
+            const double *Sp = S + t * sz, *Sn = S + (t + 1) * sz;
+            const double b = (double)beta[tt * H + h];
+            for (int64_t i = 0; i < dk; ++i) {
+                kt[i] = (double)k[bk + i];
+                qt[i] = (double)q[bk + i];
+                al[i] = exp((double)g[bk + i]);
+            }
+            for (int64_t j = 0; j < dv; ++j) {
+                vt[j] = (double)v[bv + j];
+                dov[j] = (double)d_o[bv + j];
+            }
+            /* S~ = Diag(alpha) S_{t-1} and u = v - S~^T k, recomputed */
+            for (int64_t j = 0; j < dv; ++j)
+                u[j] = vt[j];
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) {
+                    St[i * dv + j] = al[i] * Sp[i * dv + j];
+                    u[j] -= St[i * dv + j] * kt[i];
+                }
+            /* o_t = scale S_t^T q */
+            for (int64_t i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < dv; ++j) {
+                    dS[i * dv + j] += scale * qt[i] * dov[j];
+                    acc += Sn[i * dv + j] * dov[j];
+                }
+                dq[bk + i] = scale * acc;
+            }
+            /* S_t = S~ + beta k u^T */
+            double db = 0.0;
+            for (int64_t j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < dk; ++i)
+                    acc += kt[i] * dS[i * dv + j];
+                du[j] = b * acc;
+                db += acc * u[j];
+            }
+            dbeta[tt * H + h] = db;
+            for (int64_t i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < dv; ++j)
+                    acc += dS[i * dv + j] * u[j];
+                tmp[i] = b * acc;
+            }
+            /* u = v - p, p = S~^T k */
+            for (int64_t j = 0; j < dv; ++j)
+                dvv[bv + j] = du[j];
+            for (int64_t i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < dv; ++j) {
+                    dSt[i * dv + j] = dS[i * dv + j] - kt[i] * du[j];
+                    acc -= St[i * dv + j] * du[j];
+                }
+                dkk[bk + i] = tmp[i] + acc;
+            }
+            /* S~ = Diag(alpha) S_{t-1} */
+            for (int64_t i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < dv; ++j) {
+                    acc += St[i * dv + j] * dSt[i * dv + j];
+                    dS[i * dv + j] = al[i] * dSt[i * dv + j];
+                }
+                dg[bk + i] = acc;
+            }
+        }
+        memcpy(dh0 + (n * H + h) * sz, dS, sizeof(double) * (size_t)sz);
+        free(S);
+        free(w);
+    }
+    return err;
+}
