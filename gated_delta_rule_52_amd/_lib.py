@@ -25,6 +25,7 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 # Every function declared in include/kda.h.
 EXPORTS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_fwd", "kda_recurrent_step",
+           "kda_recurrent_bwd_workspace_bytes", "kda_recurrent_bwd",
            "kda_status_string", "kda_last_error", "kda_abi_version")
 
 vp = ctypes.c_void_p
@@ -59,6 +60,22 @@ class RecurrentStepArgs(ctypes.Structure):
     ]
 
 
+class RecurrentBwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("q", vp), ("k", vp), ("v", vp), ("g", vp), ("beta", vp),
+        ("initial_state", vp), ("grad_o", vp), ("grad_final_state", vp),
+        ("grad_q", vp), ("grad_k", vp), ("grad_v", vp), ("grad_g", vp), ("grad_beta", vp),
+        ("grad_initial_state", vp), ("cu_seqlens", vp),
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("in_dtype", ctypes.c_int),
+        ("workspace", vp), ("workspace_bytes", ctypes.c_size_t),
+        ("stream", vp),
+    ]
+
+
 class KdaError(RuntimeError):
     def __init__(self, status: int, message: str):
         self.status = status
@@ -85,6 +102,10 @@ def load():
         lib.kda_recurrent_fwd.argtypes = [ctypes.POINTER(ChunkFwdArgs)]
         lib.kda_recurrent_step.restype = ctypes.c_int
         lib.kda_recurrent_step.argtypes = [ctypes.POINTER(RecurrentStepArgs)]
+        lib.kda_recurrent_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.kda_recurrent_bwd_workspace_bytes.argtypes = [ctypes.POINTER(RecurrentBwdArgs)]
+        lib.kda_recurrent_bwd.restype = ctypes.c_int
+        lib.kda_recurrent_bwd.argtypes = [ctypes.POINTER(RecurrentBwdArgs)]
         lib.kda_status_string.restype = ctypes.c_char_p
         lib.kda_status_string.argtypes = [ctypes.c_int]
         lib.kda_last_error.restype = ctypes.c_char_p
@@ -118,3 +139,13 @@ def recurrent_fwd_raw(args: ChunkFwdArgs) -> int:
 def recurrent_step_raw(args: RecurrentStepArgs) -> int:
     args.struct_size = ctypes.sizeof(RecurrentStepArgs)
     return load().kda_recurrent_step(ctypes.byref(args))
+
+
+def recurrent_bwd_raw(args: RecurrentBwdArgs) -> int:
+    args.struct_size = ctypes.sizeof(RecurrentBwdArgs)
+    return load().kda_recurrent_bwd(ctypes.byref(args))
+
+
+def recurrent_bwd_workspace_raw(args: RecurrentBwdArgs) -> int:
+    args.struct_size = ctypes.sizeof(RecurrentBwdArgs)
+    return load().kda_recurrent_bwd_workspace_bytes(ctypes.byref(args))

@@ -139,6 +139,36 @@ kda_status check_prefill_buffers(const kda_chunk_fwd_args *a) {
     return KDA_OK;
 }
 
+// Size checks of kda_recurrent_bwd, shared with its workspace query.
+kda_status check_bwd_sizes(const kda_recurrent_bwd_args *a) {
+    if (a->B < 0 || a->T < 0 || a->H <= 0 || a->num_seqs < 0)
+        return fail(KDA_ERR_BAD_SHAPE, "B=%d T=%d H=%d num_seqs=%d", a->B, a->T, a->H, a->num_seqs);
+    if (!valid_dim(a->dk) || !valid_dim(a->dv))
+        return fail(KDA_ERR_UNSUPPORTED, "dk=%d dv=%d (supported: 64, 128)", a->dk, a->dv);
+    if (!valid_dtype(a->in_dtype)) return fail(KDA_ERR_UNSUPPORTED, "in_dtype=%d", a->in_dtype);
+    if (!std::isfinite(a->scale)) return fail(KDA_ERR_BAD_SHAPE, "scale is not finite");
+    if (a->cu_seqlens ? a->B != 1 : a->num_seqs != a->B)
+        return fail(KDA_ERR_BAD_SHAPE, "num_seqs=%d with B=%d (%s)", a->num_seqs, a->B,
+                    a->cu_seqlens ? "packed input needs B = 1" : "num_seqs must equal B");
+    const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
+    if (tokens > INT32_MAX)
+        return fail(KDA_ERR_BAD_SHAPE, "B*T=%lld tokens (at most %d)", static_cast<long long>(tokens), INT32_MAX);
+    if (tokens * a->H * (a->dk > a->dv ? a->dk : a->dv) > (int64_t{1} << 40))
+        return fail(KDA_ERR_BAD_SHAPE, "problem too large");
+    if (a->num_seqs > 65535 || a->H > 65535)
+        return fail(KDA_ERR_UNSUPPORTED, "N=%d H=%d (at most 65535 each)", a->num_seqs, a->H);
+    return KDA_OK;
+}
+
+kda_status read_bwd_args(const kda_recurrent_bwd_args *a, kda_recurrent_bwd_args &out) {
+    if (!a) return fail(KDA_ERR_NULL_POINTER, "args is NULL");
+    if (a->struct_size != sizeof(kda_recurrent_bwd_args))
+        return fail(KDA_ERR_BAD_STRUCT, "struct_size %u (expected %zu)", a->struct_size,
+                    sizeof(kda_recurrent_bwd_args));
+    out = *a;
+    return check_bwd_sizes(&out);
+}
+
 }  // namespace
 
 extern "C" {
@@ -293,6 +323,73 @@ kda_status kda_recurrent_step(const kda_recurrent_step_args *user) {
     L.xf = xform_of(a);
     L.stream = static_cast<hipStream_t>(a->stream);
     return hip_status(kda::launch_recurrent(L), "kda_recurrent_step launch");
+}
+
+size_t kda_recurrent_bwd_workspace_bytes(const kda_recurrent_bwd_args *user) {
+    kda_recurrent_bwd_args a;
+    if (read_bwd_args(user, a) != KDA_OK) return static_cast<size_t>(-1);
+    return kda::backward_workspace_bytes(static_cast<int64_t>(a.B) * a.T, a.num_seqs, a.H, a.dk, a.dv);
+}
+
+kda_status kda_recurrent_bwd(const kda_recurrent_bwd_args *user) {
+    g_last_error.clear();
+    kda_recurrent_bwd_args args;
+    const kda_status st = read_bwd_args(user, args);
+    if (st != KDA_OK) return st;
+    const kda_recurrent_bwd_args *a = &args;
+    const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
+    const int N = a->num_seqs;
+    if (N == 0 || (tokens == 0 && !a->grad_initial_state)) return KDA_OK;
+    if (tokens > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->grad_o || !a->grad_q || !a->grad_k ||
+                       !a->grad_v || !a->grad_g || !a->grad_beta))
+        return fail(KDA_ERR_NULL_POINTER, "q, k, v, g, beta, grad_o and every token gradient are required");
+    const size_t th = static_cast<size_t>(tokens) * a->H, in_sz = dsize(a->in_dtype);
+    const size_t sbytes = static_cast<size_t>(N) * a->H * a->dk * a->dv * 4;
+    const size_t need = kda::backward_workspace_bytes(tokens, N, a->H, a->dk, a->dv);
+    if (a->workspace_bytes < need || (need > 0 && !a->workspace))
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", a->workspace_bytes, need);
+    const Range ins[] = {range_of(a->q, th * a->dk * in_sz), range_of(a->k, th * a->dk * in_sz),
+                         range_of(a->v, th * a->dv * in_sz), range_of(a->g, th * a->dk * 4),
+                         range_of(a->beta, th * in_sz), range_of(a->grad_o, th * a->dv * in_sz),
+                         range_of(a->cu_seqlens, a->cu_seqlens ? (static_cast<size_t>(N) + 1) * 4 : 0)};
+    const Range outs[] = {range_of(a->grad_q, th * a->dk * 4), range_of(a->grad_k, th * a->dk * 4),
+                          range_of(a->grad_v, th * a->dv * 4), range_of(a->grad_g, th * a->dk * 4),
+                          range_of(a->grad_beta, th * 4), range_of(a->workspace, need)};
+    const Range rh0 = range_of(a->initial_state, a->initial_state ? sbytes : 0);
+    const Range rdhT = range_of(a->grad_final_state, a->grad_final_state ? sbytes : 0);
+    const size_t n_outs = sizeof outs / sizeof outs[0];
+    for (size_t i = 0; i < n_outs; ++i) {
+        for (const Range &r : ins)
+            if (overlap(outs[i], r)) return fail(KDA_ERR_ALIAS, "a gradient or the workspace overlaps an input");
+        if (overlap(outs[i], rh0) || overlap(outs[i], rdhT))
+            return fail(KDA_ERR_ALIAS, "a gradient or the workspace overlaps a state input");
+        for (size_t j = i + 1; j < n_outs; ++j)
+            if (overlap(outs[i], outs[j])) return fail(KDA_ERR_ALIAS, "two gradients (or the workspace) overlap");
+    }
+    if (a->grad_initial_state) {
+        const Range rd = range_of(a->grad_initial_state, sbytes);
+        for (const Range &r : ins)
+            if (overlap(rd, r)) return fail(KDA_ERR_ALIAS, "grad_initial_state overlaps an input");
+        for (const Range &r : outs)
+            if (overlap(rd, r)) return fail(KDA_ERR_ALIAS, "grad_initial_state overlaps another gradient");
+        if (a->grad_initial_state != a->initial_state && overlap(rd, rh0))
+            return fail(KDA_ERR_ALIAS, "grad_initial_state partially overlaps initial_state");
+        if (a->grad_initial_state != a->grad_final_state && overlap(rd, rdhT))
+            return fail(KDA_ERR_ALIAS, "grad_initial_state partially overlaps grad_final_state");
+    }
+
+    kda::BackwardLaunch L{};
+    L.q = a->q; L.k = a->k; L.v = a->v; L.g = a->g; L.beta = a->beta; L.d_o = a->grad_o;
+    L.h0 = a->initial_state; L.dhT = a->grad_final_state;
+    L.dq = a->grad_q; L.dk = a->grad_k; L.dv = a->grad_v; L.dg = a->grad_g; L.dbeta = a->grad_beta;
+    L.dh0 = a->grad_initial_state;
+    L.cu_seqlens = a->cu_seqlens;
+    L.N = N; L.T = a->T; L.H = a->H; L.dk_dim = a->dk; L.dv_dim = a->dv;
+    L.scale = a->scale;
+    L.in_bf16 = a->in_dtype == KDA_DTYPE_BF16;
+    L.ckpt = static_cast<float *>(a->workspace);
+    L.stream = static_cast<hipStream_t>(a->stream);
+    return hip_status(kda::launch_backward(L), "kda_recurrent_bwd launch");
 }
 
 }  // extern "C"

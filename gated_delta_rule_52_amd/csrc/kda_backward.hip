@@ -1,0 +1,342 @@
+// kda_backward.hip - gradients of the KDA recurrence for gfx950, token by token.
+//
+// Reverse-mode differentiation of the recurrence of the Kimi Linear review
+// notes (section "Method", the KDA recurrence in read-then-write form):
+// S~ = Diag(alpha) S_{t-1}, u = v - S~^T k, S_t = S~ + beta k u^T,
+// o_t = scale S_t^T q.  Walking the tokens backwards with dS, the gradient of
+// the state that leaves token t (the final-state gradient before the last
+// token):
+//
+//     dS += scale q do^T              dq = scale S_t do
+//     w   = dS^T k,  du = beta w      dv = du,  dbeta = w . u
+//     dk  = beta dS u - S~ du
+//     dS~ = dS - k du^T               dg = rowsum(S~ .* dS~)   (alpha = exp(g))
+//     dS  = Diag(alpha) dS~           the gradient entering token t
+//
+// and the initial-state gradient is the dS left after the first token.
+//
+// Each step needs S_{t-1}.  The forward states are not kept: a forward sweep
+// stores every kBlock-th state in the workspace, and the backward sweep
+// rebuilds the states of each block of kBlock tokens from its stored state,
+// kSub at a time held in registers (the later sub-block first).
+//
+// One workgroup per (sequence, head), one wave per 16-column slice of dv.
+// The columns of S, and of dS, evolve independently, so each wave runs both
+// sweeps on its slice alone and only meets the others at block boundaries.
+// dq, dk, dg and dbeta are sums over all dv columns: each wave folds its 16
+// columns with cross-lane swaps, and the workgroup adds the slices through LDS
+// in a fixed order, so results are deterministic.
+//
+// Lane (c = lane / 4, rg = lane % 4) of a wave holds column c of its slice,
+// rows rg R .. rg R + R - 1 (R = dk / 4) of the state and of its gradient.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kBlock = 8;  // tokens per stored state
+constexpr int kSub = 3;    // states held in registers at once
+
+// Pair sums over lanes (l, l ^ 32) for two values at once: one lane of each
+// pair receives lo + lo', the other hi + hi'.  Which one gets which follows
+// the swap instruction and is read at run time (fold32(0, 1) > 1 in the lanes
+// left holding hi).
+__device__ __forceinline__ float fold32(float lo, float hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// The same over lanes (l, l ^ 16).
+__device__ __forceinline__ float fold16(float lo, float hi) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Over lanes (l, l ^ 8): lanes with bit 3 clear keep lo.
+__device__ __forceinline__ float fold8(float lo, float hi, bool b3) {
+    const float send = b3 ? lo : hi, keep = b3 ? hi : lo;
+    return keep + dpp_mov<0x128>(send);  // row_ror:8, i.e. lane ^ 8 within a row of 16
+}
+// Over lanes (l, l ^ 4): lanes with bit 2 clear keep lo.
+__device__ __forceinline__ float fold4(float lo, float hi, bool b2) {
+    const float send = b2 ? lo : hi, keep = b2 ? hi : lo;
+    // swizzle bitmask mode: and 0x1f, or 0, xor 4
+    return keep + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(send), 0x101F));
+}
+// Sum over the 16 columns of a slice (lane bits 2..5), left in every lane.
+__device__ __forceinline__ float column_total(float x) {
+    x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));
+    x += dpp_mov<0x128>(x);
+    x = fold16(x, x);
+    return fold32(x, x);
+}
+
+__device__ __forceinline__ float4 lds4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+
+}  // namespace
+
+template <int DK, int DV, bool InBf16>
+__global__ void __launch_bounds__(DV / 16 * kWave)
+recurrent_bwd_kernel(BackwardLaunch L) {
+    using In = Elem<InBf16>;
+    using IT = typename In::T;
+    constexpr int NS = DV / 16;   // waves, one per 16-column slice
+    constexpr int NT = NS * kWave;
+    constexpr int R = DK / 4;     // state rows per lane
+    constexpr int KEEP = R / 16;  // rows of each row sum a lane holds after folding its slice
+    static_assert(R % 16 == 0, "dk must be a multiple of 64");
+    const IT *q = static_cast<const IT *>(L.q), *k = static_cast<const IT *>(L.k);
+    const IT *v = static_cast<const IT *>(L.v), *beta = static_cast<const IT *>(L.beta);
+    const IT *d_o = static_cast<const IT *>(L.d_o);
+    const float *g = L.g;
+    const int h = blockIdx.x, n = blockIdx.y, H = L.H;
+    const int tid = threadIdx.x, lane = tid % kWave, slice = tid / kWave;
+    const int c = lane >> 2, rg = lane & 3, col = 16 * slice + c;
+    int64_t t0, t1;
+    if (L.cu_seqlens) {
+        t0 = L.cu_seqlens[n];
+        t1 = L.cu_seqlens[n + 1];
+        if (t1 < t0) t1 = t0;
+    } else {
+        t0 = static_cast<int64_t>(n) * L.T;
+        t1 = t0 + L.T;
+    }
+    const int nb = static_cast<int>((t1 - t0 + kBlock - 1) / kBlock);
+    // stored states: sequence n's block b sits in slot t0 / kBlock + n + b (slots of different
+    // sequences never meet); inside a slot, each wave's slice is lane-contiguous
+    const int64_t slot0 = t0 / kBlock + n;
+    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * DV;
+    auto stored = [&](int b) { return L.ckpt + (((slot0 + b) * H + h) * NS + slice) * (R * kWave) + lane; };
+
+    // which half each lane keeps in the first two folds, and the first row of its folded sums
+    const bool hi32 = fold32(0.f, 1.f) > 1.f, hi16 = fold16(0.f, 1.f) > 1.f;
+    const bool b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1;
+    const int row_kept = rg * R + (hi32 ? R / 2 : 0) + (hi16 ? R / 4 : 0) + (b3 ? R / 8 : 0) + (b2 ? R / 16 : 0);
+
+    __shared__ __attribute__((aligned(16))) float s_k[kBlock][DK];
+    __shared__ __attribute__((aligned(16))) float s_q[kBlock][DK];
+    __shared__ __attribute__((aligned(16))) float s_a[kBlock][DK];
+    __shared__ float s_v[kBlock][DV], s_do[kBlock][DV], s_b[kBlock];
+    __shared__ __attribute__((aligned(16))) float s_part[kBlock][NS][3][DK];  // dq, dk, dg per slice
+    __shared__ float s_pb[kBlock][NS];                                        // dbeta per slice
+
+    // this lane's part of a [dk, dv] state of (n, h); null reads as zero
+    auto load_slice = [&](float (&s)[R], const float *src) {
+        if (src) {
+            const float *p = src + sbase + static_cast<int64_t>(rg * R) * DV + col;
+#pragma unroll
+            for (int i = 0; i < R; ++i) s[i] = p[i * DV];
+        } else {
+#pragma unroll
+            for (int i = 0; i < R; ++i) s[i] = 0.f;
+        }
+    };
+
+    // tokens [tb, tb + m) of the sequence into LDS, all threads
+    auto stage = [&](int64_t tb, int m, bool backward) {
+        for (int e = tid; e < m * DK; e += NT) {
+            const int x = e / DK, i = e % DK;
+            const int64_t idx = ((tb + x) * H + h) * DK + i;
+            s_k[x][i] = In::load(k, idx);
+            s_a[x][i] = __expf(g[idx]);
+            if (backward) s_q[x][i] = In::load(q, idx);
+        }
+        for (int e = tid; e < m * DV; e += NT) {
+            const int x = e / DV, j = e % DV;
+            const int64_t idx = ((tb + x) * H + h) * static_cast<int64_t>(DV) + j;
+            s_v[x][j] = In::load(v, idx);
+            if (backward) s_do[x][j] = In::load(d_o, idx);
+        }
+        if (tid < m) s_b[tid] = In::load(beta, (tb + tid) * H + h);
+    };
+
+    // s = S_{t-1} -> S_t for staged token x
+    auto advance = [&](float (&s)[R], int x) {
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < R; i += 4) {
+            const float4 k4 = lds4(&s_k[x][rg * R + i]), a4 = lds4(&s_a[x][rg * R + i]);
+            s[i] *= a4.x; s[i + 1] *= a4.y; s[i + 2] *= a4.z; s[i + 3] *= a4.w;
+            p0 += s[i] * k4.x;
+            p1 += s[i + 1] * k4.y;
+            p0 += s[i + 2] * k4.z;
+            p1 += s[i + 3] * k4.w;
+        }
+        const float bd = s_b[x] * (s_v[x][col] - quad_sum(p0 + p1));
+#pragma unroll
+        for (int i = 0; i < R; i += 4) {
+            const float4 k4 = lds4(&s_k[x][rg * R + i]);  // read again rather than held: registers are scarce
+            s[i] += bd * k4.x; s[i + 1] += bd * k4.y; s[i + 2] += bd * k4.z; s[i + 3] += bd * k4.w;
+        }
+    };
+
+    float ds[R];  // gradient of the state leaving the token being processed
+
+    // one backward step for staged token x (sequence position t), sp = S_{t-1} (overwritten)
+    auto back = [&](float (&sp)[R], int x, int64_t t) {
+        const float dos = L.scale * s_do[x][col], bt = s_b[x];
+        float p0 = 0.f, p1 = 0.f, w0 = 0.f, w1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < R; i += 4) {
+            const float4 k4 = lds4(&s_k[x][rg * R + i]), q4 = lds4(&s_q[x][rg * R + i]);
+            const float4 a4 = lds4(&s_a[x][rg * R + i]);
+            const float kk[4] = {k4.x, k4.y, k4.z, k4.w}, qq[4] = {q4.x, q4.y, q4.z, q4.w};
+            const float aa[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sp[i + e] *= aa[e];  // S~
+                ds[i + e] += qq[e] * dos;  // dS of S_t, with the output's term
+                if (e & 1) {
+                    p1 += sp[i + e] * kk[e];
+                    w1 += ds[i + e] * kk[e];
+                } else {
+                    p0 += sp[i + e] * kk[e];
+                    w0 += ds[i + e] * kk[e];
+                }
+            }
+        }
+        const float u = s_v[x][col] - quad_sum(p0 + p1);
+        const float wc = quad_sum(w0 + w1);
+        const float du = bt * wc, bu = bt * u;
+        // The per-row terms of dq, dk and dg, summed over the slice's 16 columns by a tree of folds.
+        // The lane's i-th output (i < KEEP) collects rows i + KEEP (m0 + 2 m1) + (R/4) m2 and the same
+        // rows + R/2: fold32 joins the +R/2 pairs, fold16 the m2 pairs, fold8 m1, fold4 m0.  Rows are
+        // visited so that every fold runs as soon as both of its inputs exist.
+        auto row_terms = [&](int r, float (&o)[3]) {
+            const float kr = s_k[x][rg * R + r], ar = s_a[x][rg * R + r];
+            o[0] = (sp[r] + bu * kr) * dos;     // S_t do
+            o[1] = bu * ds[r] - du * sp[r];     // beta dS u - S~ du
+            const float dst = ds[r] - kr * du;  // dS~
+            o[2] = sp[r] * dst;                 // S~ .* dS~
+            ds[r] = ar * dst;
+        };
+        float e[2][2][3][KEEP];  // [m0][m1][quantity][i]
+        float hf[2][3][KEEP];    // [m0][quantity][i]
+#pragma unroll
+        for (int oi = 0; oi < 4; ++oi) {
+            const int mp = (oi >> 1) | ((oi & 1) << 1);  // m0 + 2 m1 in the order 0, 2, 1, 3
+            const int m0 = mp & 1, m1 = mp >> 1;
+#pragma unroll
+            for (int i = 0; i < KEEP; ++i) {
+                float f[2][3];
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2) {
+                    const int r = i + KEEP * mp + m2 * (R / 4);
+                    float lo[3], hi[3];
+                    row_terms(r, lo);
+                    row_terms(r + R / 2, hi);
+#pragma unroll
+                    for (int qn = 0; qn < 3; ++qn) f[m2][qn] = fold32(lo[qn], hi[qn]);
+                }
+#pragma unroll
+                for (int qn = 0; qn < 3; ++qn) e[m0][m1][qn][i] = fold16(f[0][qn], f[1][qn]);
+            }
+            if (m1 == 1) {
+#pragma unroll
+                for (int qn = 0; qn < 3; ++qn)
+#pragma unroll
+                    for (int i = 0; i < KEEP; ++i) hf[m0][qn][i] = fold8(e[m0][0][qn][i], e[m0][1][qn][i], b3);
+            }
+        }
+#pragma unroll
+        for (int qn = 0; qn < 3; ++qn)
+#pragma unroll
+            for (int i = 0; i < KEEP; ++i) s_part[x][slice][qn][row_kept + i] = fold4(hf[0][qn][i], hf[1][qn][i], b2);
+        if (rg == 0) L.dv[(t * H + h) * static_cast<int64_t>(DV) + col] = du;
+        const float db = column_total(u * wc);
+        if (lane == 0) s_pb[x][slice] = db;
+    };
+
+    // the slices' partial sums of staged tokens [0, m) -> dq, dk, dg, dbeta
+    auto reduce = [&](int64_t tb, int m) {
+        constexpr int V4 = DK / 4;
+        for (int e = tid; e < m * 3 * V4; e += NT) {
+            const int x = e / (3 * V4), r = e % (3 * V4), qty = r / V4, i = (r % V4) * 4;
+            float4 acc = lds4(&s_part[x][0][qty][i]);
+#pragma unroll
+            for (int sl = 1; sl < NS; ++sl) {
+                const float4 p = lds4(&s_part[x][sl][qty][i]);
+                acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+            }
+            float *dst = qty == 0 ? L.dq : (qty == 1 ? L.dk : L.dg);
+            *reinterpret_cast<float4 *>(dst + ((tb + x) * H + h) * DK + i) = acc;
+        }
+        if (tid < m) {
+            float acc = 0.f;
+#pragma unroll
+            for (int sl = 0; sl < NS; ++sl) acc += s_pb[tid][sl];
+            L.dbeta[(tb + tid) * H + h] = acc;
+        }
+    };
+
+    // forward sweep: the state entering every block
+    float st[kSub][R];
+    load_slice(st[0], L.h0);
+    for (int b = 0; b < nb; ++b) {
+        float *cp = stored(b);
+#pragma unroll
+        for (int i = 0; i < R; ++i) cp[i * kWave] = st[0][i];
+        if (b == nb - 1) break;
+        __syncthreads();  // the previous block's tokens have been read
+        stage(t0 + static_cast<int64_t>(b) * kBlock, kBlock, false);
+        __syncthreads();
+        for (int x = 0; x < kBlock; ++x) advance(st[0], x);
+    }
+
+    // backward sweep
+    load_slice(ds, L.dhT);
+    for (int b = nb - 1; b >= 0; --b) {
+        const int64_t tb = t0 + static_cast<int64_t>(b) * kBlock;
+        const int m = static_cast<int>(t1 - tb < kBlock ? t1 - tb : kBlock);
+        __syncthreads();  // the previous block's tokens and partial sums have been read
+        stage(tb, m, true);
+        __syncthreads();
+        const float *cp = stored(b);
+        for (int sub = (m - 1) / kSub; sub >= 0; --sub) {
+            const int xb = sub * kSub, ms = m - xb < kSub ? m - xb : kSub;
+#pragma unroll
+            for (int i = 0; i < R; ++i) st[0][i] = cp[i * kWave];
+            for (int x = 0; x < xb; ++x) advance(st[0], x);
+            // st[j] = the state entering token xb + j
+#pragma unroll
+            for (int j = 1; j < kSub; ++j) {
+                if (j < ms) {
+#pragma unroll
+                    for (int i = 0; i < R; ++i) st[j][i] = st[j - 1][i];
+                    advance(st[j], xb + j - 1);
+                }
+            }
+#pragma unroll
+            for (int j = kSub - 1; j >= 0; --j)
+                if (j < ms) back(st[j], xb + j, tb + xb + j);
+        }
+        __syncthreads();
+        reduce(tb, m);
+    }
+    if (L.dh0) {
+        float *p = L.dh0 + sbase + static_cast<int64_t>(rg * R) * DV + col;
+#pragma unroll
+        for (int i = 0; i < R; ++i) p[i * DV] = ds[i];
+    }
+}
+
+size_t backward_workspace_bytes(int64_t tokens, int N, int H, int dk, int dv) {
+    return static_cast<size_t>(tokens / kBlock + N) * H * dk * dv * sizeof(float);
+}
+
+template <int DK, int DV>
+static hipError_t launch_bwd(const BackwardLaunch &L) {
+    dim3 grid(L.H, L.N), block(DV / 16 * kWave);
+    if (L.in_bf16)
+        hipLaunchKernelGGL((recurrent_bwd_kernel<DK, DV, true>), grid, block, 0, L.stream, L);
+    else
+        hipLaunchKernelGGL((recurrent_bwd_kernel<DK, DV, false>), grid, block, 0, L.stream, L);
+    return hipGetLastError();
+}
+
+hipError_t launch_backward(const BackwardLaunch &L) {
+    if (L.dk_dim == 128) return L.dv_dim == 128 ? launch_bwd<128, 128>(L) : launch_bwd<128, 64>(L);
+    return L.dv_dim == 128 ? launch_bwd<64, 128>(L) : launch_bwd<64, 64>(L);
+}
+
+}  // namespace kda

@@ -61,6 +61,18 @@ struct Elem<false> {
     }
 };
 
+// A DPP move inside each row of 16 lanes (bound_ctrl: lanes without a
+// source read 0; every control used here has one for every lane).
+template <int Ctrl>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xf, 0xf, true));
+}
+// Sum over the four lanes of each quad, left in all four.
+__device__ __forceinline__ float quad_sum(float x) {
+    x += dpp_mov<0xB1>(x);  // quad permute [1, 0, 3, 2]
+    return x + dpp_mov<0x4E>(x);  // quad permute [2, 3, 0, 1]
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);

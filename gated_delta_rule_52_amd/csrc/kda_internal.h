@@ -46,6 +46,25 @@ struct RecurrentLaunch {
 
 hipError_t launch_recurrent(const RecurrentLaunch &L);
 
+// Gradients of the recurrence, token by token (kda_backward.hip).
+struct BackwardLaunch {
+    const void *q, *k, *v;
+    const float *g;
+    const void *beta;
+    const void *d_o;            // output gradient, dtype of q
+    const float *h0, *dhT;      // initial state and final-state gradient (null: zero)
+    float *dq, *dk, *dv, *dg, *dbeta, *dh0;  // fp32; dh0 may be null
+    const int32_t *cu_seqlens;  // device, or nullptr: N sequences of T tokens
+    int N, T, H, dk_dim, dv_dim;
+    float scale;
+    bool in_bf16;
+    float *ckpt;                // workspace: stored forward states
+    hipStream_t stream;
+};
+
+size_t backward_workspace_bytes(int64_t tokens, int N, int H, int dk, int dv);
+hipError_t launch_backward(const BackwardLaunch &L);
+
 // Chunkwise prefill.
 struct ChunkLaunch {
     const void *q, *k, *v;

@@ -178,15 +178,6 @@ recurrent_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
 // * S~^T k and S~^T q for column c are R-term partial sums reduced over the
 //   four lanes of a quad by two DPP moves;
 // * the inputs of the next four tokens are in flight while one is processed.
-template <int Ctrl>
-__device__ __forceinline__ float dpp_mov(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xf, 0xf, true));
-}
-__device__ __forceinline__ float quad_sum(float x) {
-    x += dpp_mov<0xB1>(x);  // quad permute [1, 0, 3, 2]
-    return x + dpp_mov<0x4E>(x);  // quad permute [2, 3, 0, 1]
-}
-
 template <int DK, bool InBf16, bool OutBf16>
 __global__ void __launch_bounds__(64)
 recurrent_seq_kernel(const void *__restrict__ q_, const void *__restrict__ k_, const void *__restrict__ v_,

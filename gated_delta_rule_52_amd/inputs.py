@@ -42,7 +42,7 @@ import numpy as np
 
 __all__ = [
     "KdaInputs", "bf16_round", "l2_normalise", "softplus", "sigmoid",
-    "make_prefill", "make_decode_state", "decode_steps", "decode_step_pool", "WORKLOADS",
+    "make_prefill", "make_output_grads", "make_decode_state", "decode_steps", "decode_step_pool", "WORKLOADS",
     "make_workload",
 ]
 
@@ -183,6 +183,19 @@ def make_prefill(seed: int, B: int, T: int, H: int, dk: int, dv: int,
                      scalar_gate=scalar_gate)
 
 
+def make_output_grads(x: KdaInputs, seed: int, dhT_std: Optional[float] = 0.02):
+    """Loss gradients for a backward pass over problem ``x``: grad_o ~ N(0, 1)
+    [B, T, H, dv] in x's input dtype (bf16-rounded for "bf16"), and the
+    final-state gradient ~ N(0, dhT_std^2) [N, H, dk, dv] float32 (None when
+    dhT_std is None).  Drawn from their own generator, grad_o first."""
+    rng = np.random.default_rng(seed)
+    do = _maybe_bf16(rng.standard_normal((x.B, x.T, x.H, x.dv), dtype=np.float32), x.in_dtype)
+    dhT = None
+    if dhT_std is not None:
+        dhT = (dhT_std * rng.standard_normal((x.N, x.H, x.dk, x.dv), dtype=np.float32)).astype(np.float32)
+    return do, dhT
+
+
 def make_decode_state(seed: int, N: int, H: int, dk: int, dv: int,
                       std: float = 0.02):
     """Return (rng, S0) for the decode workload; S0 is [N, H, dk, dv] float32."""
@@ -241,6 +254,10 @@ WORKLOADS = {
                           in_dtype="bf16", gscale=1.0, steps=1024, pool=32, state_std=0.02),
     "append_256x16x64": dict(kind="prefill", seed=5, B=256, T=64, H=16, dk=128, dv=128,
                              in_dtype="bf16", gscale=1.0, h0_std=0.02),
+    # a training batch for the gradients: 16 sequences of 4096 tokens (grad_o and the
+    # final-state gradient from make_output_grads with seed + 100)
+    "backward_16x4096x16": dict(kind="prefill", seed=6, B=16, T=4096, H=16, dk=128, dv=128,
+                                in_dtype="bf16", gscale=1.0, h0_std=0.02),
     "varlen_8seq": dict(kind="prefill", seed=4, B=1, T=None, H=32, dk=128, dv=128,
                         in_dtype="bf16", gscale=0.01, h0_std=0.02,
                         lengths_range=(1024, 32768), n_seqs=8),

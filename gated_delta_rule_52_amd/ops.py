@@ -215,3 +215,75 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
     a.gate_scale = float(gate_scale)
     _lib.check(_lib.recurrent_step_raw(a))
     return o
+
+
+def _bwd_args(q, v, cu_seqlens, scale):
+    B, T, H, dk = q.shape
+    a = _lib.RecurrentBwdArgs()
+    a.B, a.T, a.H, a.dk, a.dv = B, T, H, dk, v.shape[-1]
+    a.num_seqs = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.scale = float(scale)
+    a.in_dtype = _DT[q.dtype]
+    return a
+
+
+def recurrent_bwd_workspace_bytes(q, v, cu_seqlens=None) -> int:
+    n = _lib.recurrent_bwd_workspace_raw(_bwd_args(q, v, cu_seqlens, 1.0))
+    if n == 2 ** 64 - 1:
+        _lib.check(_lib.STATUS_CODE["KDA_ERR_BAD_SHAPE"])
+    return int(n)
+
+
+def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  beta: torch.Tensor, grad_o: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                  grad_final_state: Optional[torch.Tensor] = None,
+                  cu_seqlens: Optional[torch.Tensor] = None, scale: float = 1.0,
+                  output_grad_initial_state: bool = True, grad_initial_state: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None):
+    """Gradients of the recurrence (no input transforms) for the output
+    gradient ``grad_o`` [B,T,H,dv] (dtype of q) and the optional final-state
+    gradient [N,H,dk,dv] fp32.  Inputs as in ``chunk_fwd``.  Returns a dict of
+    fp32 tensors: dq, dk, dg [B,T,H,dk], dv [B,T,H,dv], dbeta [B,T,H] and dh0
+    [N,H,dk,dv] (None unless ``output_grad_initial_state`` or
+    ``grad_initial_state`` is given; the latter may be ``initial_state`` or
+    ``grad_final_state`` for an in-place result)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported input dtype {dt}")
+    _need(q, "q", (B, T, H, dk), dt)
+    _need(k, "k", (B, T, H, dk), dt)
+    _need(v, "v", (B, T, H, dv), dt)
+    _need(g, "g", (B, T, H, dk), torch.float32)
+    _need(beta, "beta", (B, T, H), dt)
+    _need(grad_o, "grad_o", (B, T, H, dv), dt)
+    N = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32)
+        N = cu_seqlens.numel() - 1
+    for name, t in (("initial_state", initial_state), ("grad_final_state", grad_final_state)):
+        if t is not None:
+            _need(t, name, (N, H, dk, dv), torch.float32)
+    if grad_initial_state is None and output_grad_initial_state:
+        grad_initial_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif grad_initial_state is not None:
+        _need(grad_initial_state, "grad_initial_state", (N, H, dk, dv), torch.float32)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    out = dict(dq=torch.empty((B, T, H, dk), **f32), dk=torch.empty((B, T, H, dk), **f32),
+               dv=torch.empty((B, T, H, dv), **f32), dg=torch.empty((B, T, H, dk), **f32),
+               dbeta=torch.empty((B, T, H), **f32), dh0=grad_initial_state)
+    ws = recurrent_bwd_workspace_bytes(q, v, cu_seqlens)
+    if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
+        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+    a = _bwd_args(q, v, cu_seqlens, scale)
+    a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+    a.initial_state, a.grad_o, a.grad_final_state = _ptr(initial_state), _ptr(grad_o), _ptr(grad_final_state)
+    a.grad_q, a.grad_k, a.grad_v = _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"])
+    a.grad_g, a.grad_beta, a.grad_initial_state = _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(grad_initial_state)
+    a.workspace = _ptr(workspace) if ws > 0 else None
+    a.workspace_bytes = ws
+    a.stream = _stream(q.device)
+    _lib.check(_lib.recurrent_bwd_raw(a))
+    return out

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 /*
  * Optional input transforms, applied inside the kernels to every token before
@@ -205,6 +205,71 @@ typedef struct {
 } kda_recurrent_step_args;
 
 kda_status kda_recurrent_step(const kda_recurrent_step_args *args);
+
+/*
+ * Gradients of the recurrence (the backward pass of kda_chunk_fwd and
+ * kda_recurrent_fwd, without input transforms): for the loss gradients
+ * grad_o = dL/do and grad_final_state = dL/dS_T, the gradients of L with
+ * respect to q, k, v, g, beta and the initial state.  Reverse-mode
+ * differentiation of the recurrence of the Kimi Linear review notes
+ * (section "Method", the KDA recurrence): going backwards through the tokens
+ * with dS = dL/dS_t,
+ *     dS += scale q do^T,  dq = scale S_t do,  u = v - S~^T k,  du = beta dS^T k,
+ *     dv = du,  dbeta = k^T dS u,  dk = beta dS u - S~ du,
+ *     dS~ = dS - k du^T,  dg = rowsum(S~ .* dS~),  dS <- Diag(exp(g)) dS~,
+ * with S~ = Diag(exp(g_t)) S_{t-1}; the initial-state gradient is the final dS.
+ *
+ * Computed token by token in fp32 (one workgroup per sequence and head, one
+ * wave per 16 columns of dv).  The forward states are recomputed, not read
+ * from the forward pass: every 8th one is stored in the workspace on a first
+ * sweep, and each group of 8 is rebuilt from it on the way back.
+ *
+ * Shapes (N = number of sequences; no KDA_FLAG_* transform is applied):
+ *   q, k, v, g, beta, initial_state, cu_seqlens, B, T, H, dk, dv, num_seqs,
+ *           scale, in_dtype : as in kda_chunk_fwd (g: [B, T, H, dk] log-gates)
+ *   grad_o : [B, T, H, dv] in_dtype
+ *   grad_final_state : [N, H, dk, dv] fp32, or NULL for zeros
+ *   grad_q, grad_k, grad_g : [B, T, H, dk] fp32
+ *   grad_v : [B, T, H, dv] fp32;  grad_beta : [B, T, H] fp32
+ *   grad_initial_state : [N, H, dk, dv] fp32, or NULL to skip; may equal
+ *           initial_state or grad_final_state (each slice is read before it
+ *           is written); must not overlap anything else.
+ *   The other gradients must not overlap any input, the workspace or each
+ *   other.  Every gradient element of every token is written.
+ *   workspace : device scratch of at least kda_recurrent_bwd_workspace_bytes()
+ *               bytes, (floor(B*T / 8) + N) * H * dk * dv * 4; contents on
+ *               entry ignored, on exit unspecified.
+ */
+typedef struct {
+    uint32_t struct_size; /* = sizeof(kda_recurrent_bwd_args) */
+    const void *q;
+    const void *k;
+    const void *v;
+    const float *g;
+    const void *beta;
+    const float *initial_state;
+    const void *grad_o;
+    const float *grad_final_state;
+    float *grad_q;
+    float *grad_k;
+    float *grad_v;
+    float *grad_g;
+    float *grad_beta;
+    float *grad_initial_state;
+    const int32_t *cu_seqlens;
+    int32_t B, T, H, dk, dv, num_seqs;
+    float scale;
+    kda_dtype in_dtype; /* dtype of q, k, v, beta and grad_o */
+    void *workspace;
+    size_t workspace_bytes;
+    void *stream; /* hipStream_t */
+} kda_recurrent_bwd_args;
+
+/* Bytes of workspace kda_recurrent_bwd needs (host-only; only the size fields
+ * are read).  Returns (size_t)-1 when the arguments are invalid. */
+size_t kda_recurrent_bwd_workspace_bytes(const kda_recurrent_bwd_args *args);
+
+kda_status kda_recurrent_bwd(const kda_recurrent_bwd_args *args);
 
 /* Static text for a status code. */
 const char *kda_status_string(kda_status s);

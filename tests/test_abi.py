@@ -26,7 +26,7 @@ def test_every_declared_function_is_exported():
     assert decl == sorted(_lib.EXPORTS)
     for name in decl:
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == 2
+    assert lib.kda_abi_version() == 3
 
 
 def test_status_strings():
@@ -163,3 +163,63 @@ def test_empty_problems_are_no_ops():
     assert _lib.recurrent_step_raw(step_args(N=0)) == 0
     assert _lib.chunk_fwd_raw(chunk_args(B=0, num_seqs=0)) == 0
     assert _lib.recurrent_fwd_raw(chunk_args(B=0, num_seqs=0)) == 0
+
+
+def bwd_args(**kw):
+    a = _lib.RecurrentBwdArgs()
+    base = dict(q=FAKE, k=2 * FAKE, v=3 * FAKE, g=4 * FAKE, beta=5 * FAKE, initial_state=6 * FAKE,
+                grad_o=7 * FAKE, grad_final_state=8 * FAKE, grad_q=9 * FAKE, grad_k=10 * FAKE,
+                grad_v=11 * FAKE, grad_g=12 * FAKE, grad_beta=13 * FAKE, grad_initial_state=14 * FAKE,
+                cu_seqlens=None, B=2, T=100, H=2, dk=128, dv=64, num_seqs=2, scale=1.0,
+                in_dtype=_lib.KDA_DTYPE_BF16, workspace=15 * FAKE, workspace_bytes=1 << 30)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_backward_workspace_size():
+    """(floor(B*T / 8) + N) * H * dk * dv * 4 bytes: one stored state per 8
+    tokens, at most one more per sequence."""
+    assert _lib.recurrent_bwd_workspace_raw(bwd_args()) == (200 // 8 + 2) * 2 * 128 * 64 * 4
+    assert _lib.recurrent_bwd_workspace_raw(bwd_args(B=1, T=1001, num_seqs=5, cu_seqlens=16 * FAKE)) == \
+        (1001 // 8 + 5) * 2 * 128 * 64 * 4
+    assert _lib.recurrent_bwd_workspace_raw(bwd_args(dk=32)) == 2 ** 64 - 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=96), "KDA_ERR_UNSUPPORTED"),
+    (dict(in_dtype=5), "KDA_ERR_UNSUPPORTED"),
+    (dict(H=0), "KDA_ERR_BAD_SHAPE"),
+    (dict(num_seqs=3), "KDA_ERR_BAD_SHAPE"),
+    (dict(cu_seqlens=16 * FAKE), "KDA_ERR_BAD_SHAPE"),  # packed input needs B = 1
+    (dict(scale=float("nan")), "KDA_ERR_BAD_SHAPE"),
+    (dict(B=2, num_seqs=2, T=2 ** 30, H=1, dk=64, dv=64), "KDA_ERR_BAD_SHAPE"),
+    (dict(grad_o=None), "KDA_ERR_NULL_POINTER"),
+    (dict(grad_beta=None), "KDA_ERR_NULL_POINTER"),
+    (dict(workspace_bytes=1000), "KDA_ERR_WORKSPACE_TOO_SMALL"),
+    (dict(workspace=None), "KDA_ERR_WORKSPACE_TOO_SMALL"),
+    (dict(grad_q=FAKE + 256), "KDA_ERR_ALIAS"),              # inside q
+    (dict(grad_k=9 * FAKE + 256), "KDA_ERR_ALIAS"),          # inside grad_q
+    (dict(grad_v=15 * FAKE + 4096), "KDA_ERR_ALIAS"),        # inside the workspace
+    (dict(grad_g=6 * FAKE + 64), "KDA_ERR_ALIAS"),           # inside initial_state
+    (dict(workspace=8 * FAKE), "KDA_ERR_ALIAS"),             # the final-state gradient
+    (dict(grad_initial_state=6 * FAKE + 64), "KDA_ERR_ALIAS"),  # partly over initial_state
+    (dict(grad_initial_state=8 * FAKE + 64), "KDA_ERR_ALIAS"),  # partly over grad_final_state
+    (dict(grad_initial_state=5 * FAKE), "KDA_ERR_ALIAS"),       # over beta
+])
+def test_backward_rejects(kw, status):
+    rc = _lib.recurrent_bwd_raw(bwd_args(**kw))
+    assert rc == S[status], (_lib.STATUS.get(rc), _lib.load().kda_last_error())
+    assert _lib.load().kda_last_error().decode() != ""
+
+
+def test_backward_struct_and_empty_calls():
+    lib = _lib.load()
+    a = bwd_args()
+    a.struct_size = ctypes.sizeof(_lib.RecurrentBwdArgs) - 8
+    assert lib.kda_recurrent_bwd(ctypes.byref(a)) == S["KDA_ERR_BAD_STRUCT"]
+    assert lib.kda_recurrent_bwd(None) == S["KDA_ERR_NULL_POINTER"]
+    # nothing to do: no sequence, or no token and no initial-state gradient (no launch)
+    assert _lib.recurrent_bwd_raw(bwd_args(B=0, num_seqs=0)) == 0
+    assert _lib.recurrent_bwd_raw(bwd_args(T=0, grad_initial_state=None, q=None, grad_q=None)) == 0

@@ -1,0 +1,168 @@
+"""GPU parity of the recurrent backward (kda_recurrent_bwd) against the fp64
+oracle's gradients (oracle.backward, itself pinned by finite differences and
+closed forms in test_oracle_backward.py).
+
+Metric: per (sequence, head) slice, ||gpu - oracle||_F / ||oracle||_F for each
+of dq, dk, dv, dg, dbeta and dh0.  The kernel computes in fp32 from inputs the
+oracle sees exactly (bf16 values held in float32) and writes fp32 gradients,
+so the bar is the fp32 tolerance, 1e-5, for both input dtypes.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gated_delta_rule_52_amd.inputs import make_output_grads, make_prefill, make_workload
+from kda_testlib import TOL_FP32, dev, in_dtype_of, say, upload
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import gated_delta_rule_52_amd as m
+    from gated_delta_rule_52_amd import _lib
+    _lib.load()
+    return m
+
+
+def flat(a):
+    """[B, T, H, ...] -> [B*T, H, ...]"""
+    return a.reshape((-1,) + a.shape[2:])
+
+
+def oracle_pair(x, do, dhT, n, h, scale):
+    """The oracle's gradients for sequence n, head h alone (heads and
+    sequences are independent)."""
+    a, b = x.seq_bounds()[n]
+
+    def sl(arr):
+        return flat(arr)[a:b, h:h + 1][None]
+    h0 = None if x.h0 is None else x.h0[n:n + 1, h:h + 1].astype(np.float64)
+    dh = None if dhT is None else dhT[n:n + 1, h:h + 1].astype(np.float64)
+    return oracle.backward(sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta), sl(do), h0=h0,
+                           d_final_state=dh, scale=scale)
+
+
+def run_gpu(kda, x, do, dhT, scale, **kw):
+    import torch
+    d = upload(x)
+    g = kda.recurrent_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], dev(do, in_dtype_of(x)),
+                          initial_state=d["h0"], grad_final_state=None if dhT is None else dev(dhT, torch.float32),
+                          cu_seqlens=d["cu"], scale=scale, **kw)
+    torch.cuda.synchronize()
+    return g
+
+
+def rel(gpu, ref):
+    gpu = np.asarray(gpu, np.float64)
+    if not np.isfinite(gpu).all():
+        return float("inf")
+    return float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-30))
+
+
+def pair_errors(g, ref, x, n, h):
+    """Relative errors of every gradient of (sequence n, head h); g holds the
+    device results."""
+    a, b = x.seq_bounds()[n]
+    L = b - a
+    err = {}
+    for name in ("dq", "dk", "dv", "dg", "dbeta"):
+        gg = flat(g[name])[a:b, h].cpu().numpy()
+        err[name] = rel(gg, ref[name].reshape(gg.shape)) if L else 0.0
+    if g["dh0"] is not None:
+        err["dh0"] = rel(g["dh0"][n, h].cpu().numpy(), ref["dh0"][0, 0])
+    return err
+
+
+def check(kda, x, do, dhT, scale=1.0, pairs=None, tol=TOL_FP32):
+    say(f"case {x.name}: B={x.B} T={x.T} H={x.H} dk={x.dk} dv={x.dv} N={x.N} dtype={x.in_dtype} "
+        f"h0={x.h0 is not None} dhT={dhT is not None} scale={scale}")
+    g = run_gpu(kda, x, do, dhT, scale)
+    pairs = pairs or [(n, h) for n in range(x.N) for h in range(x.H)]
+    worst = {k: 0.0 for k in NAMES}
+    for n, h in pairs:
+        a, b = x.seq_bounds()[n]
+        if b == a:  # an empty sequence: the initial-state gradient is the final-state gradient
+            want = np.zeros((x.dk, x.dv), np.float32) if dhT is None else dhT[n, h]
+            assert np.array_equal(g["dh0"][n, h].cpu().numpy(), want)
+            continue
+        e = pair_errors(g, oracle_pair(x, do, dhT, n, h, scale), x, n, h)
+        for k, v in e.items():
+            worst[k] = max(worst[k], v)
+    say("  max slice rel err: " + " ".join(f"{k}={v:.2e}" for k, v in worst.items()) + f" (tol {tol:g})")
+    assert all(v <= tol for v in worst.values()), worst
+    return g
+
+
+def test_bf16_several_blocks_ragged_tail(kda):
+    """dk = dv = 128, bf16, 50 tokens: six blocks of 8 stored states and a
+    tail of 2, initial state and final-state gradient, scale 0.9."""
+    x = make_prefill(140, 2, 50, 3, 128, 128, h0_std=0.3, name="bwd_bf16")
+    do, dhT = make_output_grads(x, 240, dhT_std=0.3)
+    check(kda, x, do, dhT, scale=0.9)
+
+
+@pytest.mark.parametrize("dk,dv,dt", [(64, 64, "fp32"), (128, 64, "bf16"), (64, 128, "bf16"),
+                                      (128, 128, "fp32")])
+def test_head_dims_and_dtypes(kda, dk, dv, dt):
+    x = make_prefill(141, 1, 37, 2, dk, dv, in_dtype=dt, h0_std=0.3, name=f"bwd_{dk}x{dv}_{dt}")
+    do, dhT = make_output_grads(x, 241, dhT_std=0.3)
+    check(kda, x, do, dhT)
+
+
+def test_varlen_with_empty_and_short_sequences(kda):
+    """Lengths 0, 1, 7, 8, 9, 33, 0, 64, 17 in one packed batch: every block
+    boundary case; empty sequences pass the final-state gradient through."""
+    x = make_prefill(142, 1, 0, 2, 128, 128, h0_std=0.3, seqlens=[0, 1, 7, 8, 9, 33, 0, 64, 17],
+                     name="bwd_varlen")
+    do, dhT = make_output_grads(x, 242, dhT_std=0.3)
+    check(kda, x, do, dhT)
+
+
+def test_without_initial_state_or_final_gradient(kda):
+    x = make_prefill(143, 2, 21, 2, 128, 128, name="bwd_zero_states")
+    do, _ = make_output_grads(x, 243, dhT_std=None)
+    check(kda, x, do, None)
+
+
+def test_long_sequences(kda):
+    """1500 tokens: 188 stored states per sequence, gate scale 1 (short memory)
+    and 0.01 (long memory, gradients reach far back)."""
+    for gs in (1.0, 0.01):
+        x = make_prefill(144, 1, 1500, 2, 128, 128, gscale=gs, h0_std=0.05, name=f"bwd_long_g{gs}")
+        do, dhT = make_output_grads(x, 244, dhT_std=0.05)
+        check(kda, x, do, dhT)
+
+
+def test_in_place_and_deterministic(kda):
+    """grad_initial_state may be grad_final_state (or initial_state); two runs
+    give the same bits; the gradient outputs need no prior contents."""
+    import torch
+    x = make_prefill(145, 2, 40, 2, 128, 128, h0_std=0.3, name="bwd_in_place")
+    do, dhT = make_output_grads(x, 245, dhT_std=0.3)
+    d = upload(x)
+    dod, dht = dev(do, in_dtype_of(x)), dev(dhT, torch.float32)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], dod)
+    a = kda.recurrent_bwd(*args, initial_state=d["h0"], grad_final_state=dht)
+    b = kda.recurrent_bwd(*args, initial_state=d["h0"], grad_final_state=dht)
+    buf = dht.clone()
+    c = kda.recurrent_bwd(*args, initial_state=d["h0"], grad_final_state=buf, grad_initial_state=buf)
+    h0c = d["h0"].clone()
+    e = kda.recurrent_bwd(*args, initial_state=h0c, grad_final_state=dht, grad_initial_state=h0c)
+    torch.cuda.synchronize()
+    for name in NAMES:
+        assert torch.equal(a[name], b[name]), f"{name} not deterministic"
+        assert torch.equal(a[name], c[name]), f"{name} differs in place (grad_final_state)"
+        assert torch.equal(a[name], e[name]), f"{name} differs in place (initial_state)"
+
+
+def test_full_size_workload_sampled(kda):
+    """The 16 x 4096 x 16 training batch in the launch configuration the
+    benchmark times, checked on three (sequence, head) pairs."""
+    x = make_workload("backward_16x4096x16")
+    do, dhT = make_output_grads(x, 106)
+    check(kda, x, do, dhT, pairs=[(0, 0), (7, 5), (15, 15)])
