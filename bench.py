@@ -7,8 +7,8 @@ inter-chunk state propagation, output) runs inside that call.  Inputs are
 drawn on the host, copied to HBM once, and are resident when timing starts.
 Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-append] [--no-fused] [--no-cpu]
-                    [--calibrate-copy]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-append] [--no-fused]
+                    [--no-backward] [--no-cpu] [--calibrate-copy]
 
 --calibrate-copy adds, before the timed region, one elementwise copy kernel
 of a known size (256 MiB read + 256 MiB written): its FETCH_SIZE / WRITE_SIZE
@@ -309,6 +309,77 @@ def time_append_grid():
     return grid
 
 
+FP32_VECTOR_PEAK_TFLOPS = 157.3   # MI355X fp32 vector (FMA = 2 flops)
+
+
+def backward_alg_flops(tokens, H, dk, dv):
+    """Algorithmic flops of the gradients (FMA = 2): per token and head one
+    forward step to recover the state (S~ = alpha S, S~^T k, the rank-1
+    write: 5 dk dv) and the reverse step (dS += q do^T, S_t do, dS^T k,
+    dS u, S~ du, dS - k du^T, rowsum(S~ .* dS~), alpha dS~: 15 dk dv)."""
+    return 20 * tokens * H * dk * dv
+
+
+def backward_alg_bytes(tokens, H, dk, dv, N, in_bytes=2):
+    """Inputs q, k, v, beta, grad_o (in_bytes), g (fp32), h0 and the
+    final-state gradient read once; dq, dk, dv, dg, dbeta (fp32) and dh0
+    written once."""
+    th = tokens * H
+    return th * ((2 * dk + 2 * dv + 1) * in_bytes + dk * 4 + (3 * dk + dv + 1) * 4) + 3 * N * H * dk * dv * 4
+
+
+def time_backward(args):
+    """Gradients of the 16 x 4096 x 16 training batch (kda_recurrent_bwd), us per call."""
+    import torch
+    import gated_delta_rule_52_amd as kda
+    from gated_delta_rule_52_amd.inputs import make_output_grads, make_workload
+    x = make_workload("backward_16x4096x16")
+    do, dhT = make_output_grads(x, 106)
+    dev = "cuda:0"
+    bf, f32 = torch.bfloat16, torch.float32
+    t = lambda a, dt: torch.from_numpy(a).to(dev).to(dt)
+    q, k, v, beta, d_o = t(x.q, bf), t(x.k, bf), t(x.v, bf), t(x.beta, bf), t(do, bf)
+    g, h0, dht = t(x.g, f32), t(x.h0, f32), t(dhT, f32)
+    ws = torch.empty(kda.recurrent_bwd_workspace_bytes(q, v), dtype=torch.uint8, device=dev)
+    dh0 = torch.empty_like(h0)
+    fn = lambda: kda.recurrent_bwd(q, k, v, g, beta, d_o, initial_state=h0, grad_final_state=dht,
+                                   grad_initial_state=dh0, workspace=ws)
+    for _ in range(max(args.warmup, 1)):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    n = max(3, min(args.steps, 10))
+    per = []
+    for _ in range(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1))
+    ms = float(np.mean(per))
+    log(f"backward_16x4096x16: {ms:.3f} ms per call")
+    return x, ms, per
+
+
+def cpu_backward_sample(x):
+    """The fp64 oracle's gradients on one sequence's first 1024 tokens, all
+    heads (OpenMP over heads): tokens x heads per second."""
+    import oracle
+    from gated_delta_rule_52_amd.inputs import make_output_grads
+    do, dhT = make_output_grads(x, 106)
+    L = 1024
+    sl = lambda a: np.ascontiguousarray(a[:1, :L])
+    threads = min(len(os.sched_getaffinity(0)), x.H)
+    t0 = time.perf_counter()
+    oracle.backward(sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta), sl(do), h0=x.h0[:1].astype(np.float64),
+                    d_final_state=dhT[:1].astype(np.float64), nthreads=threads)
+    dt = time.perf_counter() - t0
+    log(f"oracle backward: {dt:.2f} s on {threads} threads")
+    return dict(value=L / dt, unit="tokens/s (all 16 heads)", cores=threads, kind="oracle",
+                sample=f"sequence 0, first {L} tokens, {x.H} heads of backward_16x4096x16, {dt:.2f} s wall")
+
+
 def copy_ceiling():
     """HBM bandwidth a plain elementwise kernel reaches on this GPU: 1 GiB read
     and 1 GiB written per launch (torch's neg kernel), best of 10 launches."""
@@ -357,6 +428,7 @@ def main():
     ap.add_argument("--no-append", action="store_true", help="skip the append line")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip the length sweep and the fused input-transform and scalar-gate lines")
+    ap.add_argument("--no-backward", action="store_true", help="skip the gradients line")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -445,6 +517,25 @@ def main():
             "workload": "N sequences x T new tokens, 16 heads, dk=dv=128, bf16, cached states (key 'NxT')",
             "us_per_call": time_append_grid(),
         }
+    if not args.no_backward:
+        xb, msb, perb = time_backward(args)
+        toks = xb.B * xb.T
+        flops = backward_alg_flops(toks, xb.H, xb.dk, xb.dv)
+        bbytes = backward_alg_bytes(toks, xb.H, xb.dk, xb.dv, xb.N)
+        tf = flops / (msb * 1e-3) / 1e12
+        rec["backward"] = {
+            "workload": "backward_16x4096x16", "B": xb.B, "T": xb.T, "H": xb.H, "dk": xb.dk, "dv": xb.dv,
+            "in_dtype": "bf16", "grad_dtype": "fp32", "ms_per_call": msb, "ms_median": float(np.median(perb)),
+            "tokens_per_s": toks / (msb * 1e-3),
+            "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / FP32_VECTOR_PEAK_TFLOPS, "alg_flops_per_launch": flops,
+                         "hbm_alg_bytes_per_launch": bbytes,
+                         "hbm_frac": bbytes / (msb * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "kernel": "recurrent_bwd_kernel<128,128,bf16>, one launch per call"},
+        }
+        if not args.no_cpu:
+            rec["backward"]["cpu_baseline"] = cpu_backward_sample(xb)
+        del xb
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(x)
     print(json.dumps(rec), flush=True)

@@ -7,7 +7,7 @@
 // the state that leaves token t (the final-state gradient before the last
 // token):
 //
-//     dS += scale q do^T              dq = scale S_t do
+//     dS += scale q do^T              dq = scale S_t do = scale (S~ do + beta k (u . do))
 //     w   = dS^T k,  du = beta w      dv = du,  dbeta = w . u
 //     dk  = beta dS u - S~ du
 //     dS~ = dS - k du^T               dg = rowsum(S~ .* dS~)   (alpha = exp(g))
@@ -84,6 +84,7 @@ recurrent_bwd_kernel(BackwardLaunch L) {
     constexpr int NT = NS * kWave;
     constexpr int R = DK / 4;     // state rows per lane
     constexpr int KEEP = R / 16;  // rows of each row sum a lane holds after folding its slice
+    constexpr int RP = R + 4;     // LDS stride of a row group: the four groups a quad reads fall in distinct banks
     static_assert(R % 16 == 0, "dk must be a multiple of 64");
     const IT *q = static_cast<const IT *>(L.q), *k = static_cast<const IT *>(L.k);
     const IT *v = static_cast<const IT *>(L.v), *beta = static_cast<const IT *>(L.beta);
@@ -113,12 +114,13 @@ recurrent_bwd_kernel(BackwardLaunch L) {
     const bool b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1;
     const int row_kept = rg * R + (hi32 ? R / 2 : 0) + (hi16 ? R / 4 : 0) + (b3 ? R / 8 : 0) + (b2 ? R / 16 : 0);
 
-    __shared__ __attribute__((aligned(16))) float s_k[kBlock][DK];
-    __shared__ __attribute__((aligned(16))) float s_q[kBlock][DK];
-    __shared__ __attribute__((aligned(16))) float s_a[kBlock][DK];
+    // k, q, alpha of the staged tokens; channel rg R + r at rg RP + r
+    __shared__ __attribute__((aligned(16))) float s_k[kBlock][4 * RP];
+    __shared__ __attribute__((aligned(16))) float s_q[kBlock][4 * RP];
+    __shared__ __attribute__((aligned(16))) float s_a[kBlock][4 * RP];
     __shared__ float s_v[kBlock][DV], s_do[kBlock][DV], s_b[kBlock];
-    __shared__ __attribute__((aligned(16))) float s_part[kBlock][NS][3][DK];  // dq, dk, dg per slice
-    __shared__ float s_pb[kBlock][NS];                                        // dbeta per slice
+    __shared__ __attribute__((aligned(16))) float s_part[kBlock][NS][3][DK];  // row sums per slice
+    __shared__ float s_ps[kBlock][NS][2];  // per slice: sum_c u_c w_c (dbeta) and sum_c u_c scale do_c
 
     // this lane's part of a [dk, dv] state of (n, h); null reads as zero
     auto load_slice = [&](float (&s)[R], const float *src) {
@@ -135,11 +137,11 @@ recurrent_bwd_kernel(BackwardLaunch L) {
     // tokens [tb, tb + m) of the sequence into LDS, all threads
     auto stage = [&](int64_t tb, int m, bool backward) {
         for (int e = tid; e < m * DK; e += NT) {
-            const int x = e / DK, i = e % DK;
+            const int x = e / DK, i = e % DK, li = (i / R) * RP + i % R;
             const int64_t idx = ((tb + x) * H + h) * DK + i;
-            s_k[x][i] = In::load(k, idx);
-            s_a[x][i] = __expf(g[idx]);
-            if (backward) s_q[x][i] = In::load(q, idx);
+            s_k[x][li] = In::load(k, idx);
+            s_a[x][li] = __expf(g[idx]);
+            if (backward) s_q[x][li] = In::load(q, idx);
         }
         for (int e = tid; e < m * DV; e += NT) {
             const int x = e / DV, j = e % DV;
@@ -151,22 +153,38 @@ recurrent_bwd_kernel(BackwardLaunch L) {
     };
 
     // s = S_{t-1} -> S_t for staged token x
+    // LDS reads are software-pipelined by hand: each group of four rows issues the next group's reads
+    // before its own arithmetic, and a scheduling fence keeps the compiler from hoisting every read
+    // to the top (which would cost 3 R registers).
     auto advance = [&](float (&s)[R], int x) {
+        const float *kx = &s_k[x][rg * RP], *ax = &s_a[x][rg * RP];
         float p0 = 0.f, p1 = 0.f;
+        float4 kc = lds4(kx), ac = lds4(ax);
 #pragma unroll
         for (int i = 0; i < R; i += 4) {
-            const float4 k4 = lds4(&s_k[x][rg * R + i]), a4 = lds4(&s_a[x][rg * R + i]);
-            s[i] *= a4.x; s[i + 1] *= a4.y; s[i + 2] *= a4.z; s[i + 3] *= a4.w;
-            p0 += s[i] * k4.x;
-            p1 += s[i + 1] * k4.y;
-            p0 += s[i + 2] * k4.z;
-            p1 += s[i + 3] * k4.w;
+            __builtin_amdgcn_sched_barrier(0);
+            float4 kn = kc, an = ac;
+            if (i + 4 < R) {
+                kn = lds4(kx + i + 4);
+                an = lds4(ax + i + 4);
+            }
+            s[i] *= ac.x; s[i + 1] *= ac.y; s[i + 2] *= ac.z; s[i + 3] *= ac.w;
+            p0 += s[i] * kc.x;
+            p1 += s[i + 1] * kc.y;
+            p0 += s[i + 2] * kc.z;
+            p1 += s[i + 3] * kc.w;
+            kc = kn;
+            ac = an;
         }
+        kc = lds4(kx);  // k is read again rather than held: registers are scarce
         const float bd = s_b[x] * (s_v[x][col] - quad_sum(p0 + p1));
 #pragma unroll
         for (int i = 0; i < R; i += 4) {
-            const float4 k4 = lds4(&s_k[x][rg * R + i]);  // read again rather than held: registers are scarce
-            s[i] += bd * k4.x; s[i + 1] += bd * k4.y; s[i + 2] += bd * k4.z; s[i + 3] += bd * k4.w;
+            __builtin_amdgcn_sched_barrier(0);
+            float4 kn = kc;
+            if (i + 4 < R) kn = lds4(kx + i + 4);
+            s[i] += bd * kc.x; s[i + 1] += bd * kc.y; s[i + 2] += bd * kc.z; s[i + 3] += bd * kc.w;
+            kc = kn;
         }
     };
 
@@ -176,12 +194,22 @@ recurrent_bwd_kernel(BackwardLaunch L) {
     auto back = [&](float (&sp)[R], int x, int64_t t) {
         const float dos = L.scale * s_do[x][col], bt = s_b[x];
         float p0 = 0.f, p1 = 0.f, w0 = 0.f, w1 = 0.f;
+        const float *kx = &s_k[x][rg * RP], *qx = &s_q[x][rg * RP], *ax = &s_a[x][rg * RP];
+        float4 kc = lds4(kx), qc = lds4(qx), ac = lds4(ax);
 #pragma unroll
         for (int i = 0; i < R; i += 4) {
-            const float4 k4 = lds4(&s_k[x][rg * R + i]), q4 = lds4(&s_q[x][rg * R + i]);
-            const float4 a4 = lds4(&s_a[x][rg * R + i]);
-            const float kk[4] = {k4.x, k4.y, k4.z, k4.w}, qq[4] = {q4.x, q4.y, q4.z, q4.w};
-            const float aa[4] = {a4.x, a4.y, a4.z, a4.w};
+            __builtin_amdgcn_sched_barrier(0);
+            float4 kn = kc, qn = qc, an = ac;
+            if (i + 4 < R) {
+                kn = lds4(kx + i + 4);
+                qn = lds4(qx + i + 4);
+                an = lds4(ax + i + 4);
+            }
+            const float kk[4] = {kc.x, kc.y, kc.z, kc.w}, qq[4] = {qc.x, qc.y, qc.z, qc.w};
+            const float aa[4] = {ac.x, ac.y, ac.z, ac.w};
+            kc = kn;
+            qc = qn;
+            ac = an;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 sp[i + e] *= aa[e];  // S~
@@ -202,35 +230,73 @@ recurrent_bwd_kernel(BackwardLaunch L) {
         // The lane's i-th output (i < KEEP) collects rows i + KEEP (m0 + 2 m1) + (R/4) m2 and the same
         // rows + R/2: fold32 joins the +R/2 pairs, fold16 the m2 pairs, fold8 m1, fold4 m0.  Rows are
         // visited so that every fold runs as soon as both of its inputs exist.
-        auto row_terms = [&](int r, float (&o)[3]) {
-            const float kr = s_k[x][rg * R + r], ar = s_a[x][rg * R + r];
-            o[0] = (sp[r] + bu * kr) * dos;     // S_t do
+        auto row_terms = [&](int r, float kr, float ar, float (&o)[3]) {
+            o[0] = sp[r] * dos;                 // S~ do (beta k (u . do) is added over all slices)
             o[1] = bu * ds[r] - du * sp[r];     // beta dS u - S~ du
             const float dst = ds[r] - kr * du;  // dS~
             o[2] = sp[r] * dst;                 // S~ .* dS~
             ds[r] = ar * dst;
         };
+        auto ld_keep = [&](const float *p, float (&o)[KEEP]) {  // KEEP consecutive rows
+            if constexpr (KEEP == 2) {
+                const float2 w = *reinterpret_cast<const float2 *>(p);
+                o[0] = w.x;
+                o[1] = w.y;
+            } else {
+#pragma unroll
+                for (int i = 0; i < KEEP; ++i) o[i] = p[i];
+            }
+        };
         float e[2][2][3][KEEP];  // [m0][m1][quantity][i]
         float hf[2][3][KEEP];    // [m0][quantity][i]
+        // k and alpha of one quarter of the rows: [m2][low, high half][i]
+        auto ld_quarter = [&](int mp, float (&kq)[2][2][KEEP], float (&aq)[2][2][KEEP]) {
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int r = KEEP * mp + m2 * (R / 4) + hh * (R / 2);
+                    ld_keep(kx + r, kq[m2][hh]);
+                    ld_keep(ax + r, aq[m2][hh]);
+                }
+        };
+        float kq[2][2][KEEP], aq[2][2][KEEP];
+        ld_quarter(0, kq, aq);
 #pragma unroll
         for (int oi = 0; oi < 4; ++oi) {
+            __builtin_amdgcn_sched_barrier(0);
             const int mp = (oi >> 1) | ((oi & 1) << 1);  // m0 + 2 m1 in the order 0, 2, 1, 3
             const int m0 = mp & 1, m1 = mp >> 1;
+            float kqc[2][2][KEEP], aqc[2][2][KEEP];
 #pragma unroll
-            for (int i = 0; i < KEEP; ++i) {
-                float f[2][3];
+            for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
-                for (int m2 = 0; m2 < 2; ++m2) {
-                    const int r = i + KEEP * mp + m2 * (R / 4);
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int i = 0; i < KEEP; ++i) {
+                        kqc[m2][hh][i] = kq[m2][hh][i];
+                        aqc[m2][hh][i] = aq[m2][hh][i];
+                    }
+            if (oi < 3) ld_quarter(((oi + 1) >> 1) | (((oi + 1) & 1) << 1), kq, aq);
+            float f[2][3][KEEP];
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2) {
+                const int r = KEEP * mp + m2 * (R / 4);
+                const float (&kl)[KEEP] = kqc[m2][0], (&al)[KEEP] = aqc[m2][0];
+                const float (&kh)[KEEP] = kqc[m2][1], (&ah)[KEEP] = aqc[m2][1];
+#pragma unroll
+                for (int i = 0; i < KEEP; ++i) {
                     float lo[3], hi[3];
-                    row_terms(r, lo);
-                    row_terms(r + R / 2, hi);
+                    row_terms(r + i, kl[i], al[i], lo);
+                    row_terms(r + i + R / 2, kh[i], ah[i], hi);
 #pragma unroll
-                    for (int qn = 0; qn < 3; ++qn) f[m2][qn] = fold32(lo[qn], hi[qn]);
+                    for (int qn = 0; qn < 3; ++qn) f[m2][qn][i] = fold32(lo[qn], hi[qn]);
                 }
-#pragma unroll
-                for (int qn = 0; qn < 3; ++qn) e[m0][m1][qn][i] = fold16(f[0][qn], f[1][qn]);
             }
+#pragma unroll
+            for (int qn = 0; qn < 3; ++qn)
+#pragma unroll
+                for (int i = 0; i < KEEP; ++i) e[m0][m1][qn][i] = fold16(f[0][qn][i], f[1][qn][i]);
             if (m1 == 1) {
 #pragma unroll
                 for (int qn = 0; qn < 3; ++qn)
@@ -243,8 +309,11 @@ recurrent_bwd_kernel(BackwardLaunch L) {
 #pragma unroll
             for (int i = 0; i < KEEP; ++i) s_part[x][slice][qn][row_kept + i] = fold4(hf[0][qn][i], hf[1][qn][i], b2);
         if (rg == 0) L.dv[(t * H + h) * static_cast<int64_t>(DV) + col] = du;
-        const float db = column_total(u * wc);
-        if (lane == 0) s_pb[x][slice] = db;
+        const float db = column_total(u * wc), ud = column_total(u * dos);
+        if (lane == 0) {
+            s_ps[x][slice][0] = db;
+            s_ps[x][slice][1] = ud;
+        }
     };
 
     // the slices' partial sums of staged tokens [0, m) -> dq, dk, dg, dbeta
@@ -258,13 +327,21 @@ recurrent_bwd_kernel(BackwardLaunch L) {
                 const float4 p = lds4(&s_part[x][sl][qty][i]);
                 acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
             }
+            if (qty == 0) {  // dq = scale (S~ do + beta k (u . do))
+                float ud = 0.f;
+#pragma unroll
+                for (int sl = 0; sl < NS; ++sl) ud += s_ps[x][sl][1];
+                const float4 k4 = lds4(&s_k[x][(i / R) * RP + i % R]);
+                const float bud = s_b[x] * ud;
+                acc.x += bud * k4.x; acc.y += bud * k4.y; acc.z += bud * k4.z; acc.w += bud * k4.w;
+            }
             float *dst = qty == 0 ? L.dq : (qty == 1 ? L.dk : L.dg);
             *reinterpret_cast<float4 *>(dst + ((tb + x) * H + h) * DK + i) = acc;
         }
         if (tid < m) {
             float acc = 0.f;
 #pragma unroll
-            for (int sl = 0; sl < NS; ++sl) acc += s_pb[tid][sl];
+            for (int sl = 0; sl < NS; ++sl) acc += s_ps[tid][sl][0];
             L.dbeta[(tb + tid) * H + h] = acc;
         }
     };
