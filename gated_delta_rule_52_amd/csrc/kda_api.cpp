@@ -328,7 +328,7 @@ kda_status kda_recurrent_step(const kda_recurrent_step_args *user) {
 size_t kda_recurrent_bwd_workspace_bytes(const kda_recurrent_bwd_args *user) {
     kda_recurrent_bwd_args a;
     if (read_bwd_args(user, a) != KDA_OK) return static_cast<size_t>(-1);
-    return kda::backward_workspace_bytes(static_cast<int64_t>(a.B) * a.T, a.num_seqs, a.H, a.dk, a.dv);
+    return kda::backward_workspace_bytes(a.B, a.T, a.H, a.dk, a.dv, a.num_seqs, a.cu_seqlens != nullptr);
 }
 
 kda_status kda_recurrent_bwd(const kda_recurrent_bwd_args *user) {
@@ -345,7 +345,7 @@ kda_status kda_recurrent_bwd(const kda_recurrent_bwd_args *user) {
         return fail(KDA_ERR_NULL_POINTER, "q, k, v, g, beta, grad_o and every token gradient are required");
     const size_t th = static_cast<size_t>(tokens) * a->H, in_sz = dsize(a->in_dtype);
     const size_t sbytes = static_cast<size_t>(N) * a->H * a->dk * a->dv * 4;
-    const size_t need = kda::backward_workspace_bytes(tokens, N, a->H, a->dk, a->dv);
+    const size_t need = kda::backward_workspace_bytes(a->B, a->T, a->H, a->dk, a->dv, N, a->cu_seqlens != nullptr);
     if (a->workspace_bytes < need || (need > 0 && !a->workspace))
         return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", a->workspace_bytes, need);
     const Range ins[] = {range_of(a->q, th * a->dk * in_sz), range_of(a->k, th * a->dk * in_sz),
@@ -384,10 +384,10 @@ kda_status kda_recurrent_bwd(const kda_recurrent_bwd_args *user) {
     L.dq = a->grad_q; L.dk = a->grad_k; L.dv = a->grad_v; L.dg = a->grad_g; L.dbeta = a->grad_beta;
     L.dh0 = a->grad_initial_state;
     L.cu_seqlens = a->cu_seqlens;
-    L.N = N; L.T = a->T; L.H = a->H; L.dk_dim = a->dk; L.dv_dim = a->dv;
+    L.B = a->B; L.N = N; L.T = a->T; L.H = a->H; L.dk_dim = a->dk; L.dv_dim = a->dv;
     L.scale = a->scale;
     L.in_bf16 = a->in_dtype == KDA_DTYPE_BF16;
-    L.ckpt = static_cast<float *>(a->workspace);
+    L.workspace = a->workspace;
     L.stream = static_cast<hipStream_t>(a->stream);
     return hip_status(kda::launch_backward(L), "kda_recurrent_bwd launch");
 }

@@ -75,9 +75,12 @@ __device__ __forceinline__ float4 lds4(const float *p) { return *reinterpret_cas
 
 }  // namespace
 
+// Token-by-token gradients of one segment per workgroup (a sequence, or a piece of one): the forward
+// state entering the segment comes from the segmented forward (or is the initial state), the gradient
+// of the state leaving it from the reverse combine (or is the final-state gradient).
 template <int DK, int DV, bool InBf16>
 __global__ void __launch_bounds__(DV / 16 * kWave)
-recurrent_bwd_kernel(BackwardLaunch L) {
+recurrent_bwd_kernel(BackwardLaunch L, SegmentView sv, const float *dleave) {
     using In = Elem<InBf16>;
     using IT = typename In::T;
     constexpr int NS = DV / 16;   // waves, one per 16-column slice
@@ -90,23 +93,24 @@ recurrent_bwd_kernel(BackwardLaunch L) {
     const IT *v = static_cast<const IT *>(L.v), *beta = static_cast<const IT *>(L.beta);
     const IT *d_o = static_cast<const IT *>(L.d_o);
     const float *g = L.g;
-    const int h = blockIdx.x, n = blockIdx.y, H = L.H;
+    const int h = blockIdx.x, seg = blockIdx.y, H = L.H;
+    if (seg >= sv.count()) return;
+    const int4 sd = sv.table[seg];
+    const int n = sd.x;
+    const int64_t t0 = sd.y, t1 = sd.z;
     const int tid = threadIdx.x, lane = tid % kWave, slice = tid / kWave;
     const int c = lane >> 2, rg = lane & 3, col = 16 * slice + c;
-    int64_t t0, t1;
-    if (L.cu_seqlens) {
-        t0 = L.cu_seqlens[n];
-        t1 = L.cu_seqlens[n + 1];
-        if (t1 < t0) t1 = t0;
-    } else {
-        t0 = static_cast<int64_t>(n) * L.T;
-        t1 = t0 + L.T;
-    }
     const int nb = static_cast<int>((t1 - t0 + kBlock - 1) / kBlock);
-    // stored states: sequence n's block b sits in slot t0 / kBlock + n + b (slots of different
-    // sequences never meet); inside a slot, each wave's slice is lane-contiguous
-    const int64_t slot0 = t0 / kBlock + n;
-    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * DV;
+    // stored states: segment seg's block b sits in slot t0 / kBlock + seg + b (slots of different
+    // segments never meet); inside a slot, each wave's slice is lane-contiguous
+    const int64_t slot0 = t0 / kBlock + seg;
+    const int64_t nbase = (static_cast<int64_t>(n) * H + h) * DK * DV;
+    const bool one = (sd.w & (kSegFirst | kSegLast)) == (kSegFirst | kSegLast);
+    // A sequence of one segment reads the final-state gradient in place (this workgroup then writes the
+    // initial-state gradient, which may alias it); longer ones read the reverse combine's copy.
+    const float *dS_end = one ? (L.dhT ? L.dhT + nbase : nullptr)
+                              : dleave + (static_cast<int64_t>(seg) * H + h) * DK * DV;
+    float *dS_begin = (sd.w & kSegFirst) && L.dh0 ? L.dh0 + nbase : nullptr;
     auto stored = [&](int b) { return L.ckpt + (((slot0 + b) * H + h) * NS + slice) * (R * kWave) + lane; };
 
     // which half each lane keeps in the first two folds, and the first row of its folded sums
@@ -122,10 +126,10 @@ recurrent_bwd_kernel(BackwardLaunch L) {
     __shared__ __attribute__((aligned(16))) float s_part[kBlock][NS][3][DK];  // row sums per slice
     __shared__ float s_ps[kBlock][NS][2];  // per slice: sum_c u_c w_c (dbeta) and sum_c u_c scale do_c
 
-    // this lane's part of a [dk, dv] state of (n, h); null reads as zero
+    // this lane's part of a [dk, dv] state; null reads as zero
     auto load_slice = [&](float (&s)[R], const float *src) {
         if (src) {
-            const float *p = src + sbase + static_cast<int64_t>(rg * R) * DV + col;
+            const float *p = src + static_cast<int64_t>(rg * R) * DV + col;
 #pragma unroll
             for (int i = 0; i < R; ++i) s[i] = p[i * DV];
         } else {
@@ -348,7 +352,7 @@ recurrent_bwd_kernel(BackwardLaunch L) {
 
     // forward sweep: the state entering every block
     float st[kSub][R];
-    load_slice(st[0], L.h0);
+    load_slice(st[0], sv.entering(seg, sd, h, H, DK, DV));
     for (int b = 0; b < nb; ++b) {
         float *cp = stored(b);
 #pragma unroll
@@ -361,7 +365,7 @@ recurrent_bwd_kernel(BackwardLaunch L) {
     }
 
     // backward sweep
-    load_slice(ds, L.dhT);
+    load_slice(ds, dS_end);
     for (int b = nb - 1; b >= 0; --b) {
         const int64_t tb = t0 + static_cast<int64_t>(b) * kBlock;
         const int m = static_cast<int>(t1 - tb < kBlock ? t1 - tb : kBlock);
@@ -390,24 +394,209 @@ recurrent_bwd_kernel(BackwardLaunch L) {
         __syncthreads();
         reduce(tb, m);
     }
-    if (L.dh0) {
-        float *p = L.dh0 + sbase + static_cast<int64_t>(rg * R) * DV + col;
+    if (dS_begin) {
+        float *p = dS_begin + static_cast<int64_t>(rg * R) * DV + col;
 #pragma unroll
         for (int i = 0; i < R; ++i) p[i * DV] = ds[i];
     }
 }
 
-size_t backward_workspace_bytes(int64_t tokens, int N, int H, int dk, int dv) {
-    return static_cast<size_t>(tokens / kBlock + N) * H * dk * dv * sizeof(float);
+// The gradient of the state entering a segment, from a zero gradient at its end (the part of dS that
+// the segment's own output gradients contribute): walking its tokens backwards,
+//     dS += scale q do^T;   dS <- Diag(alpha) (I - beta k k^T) dS,
+// which needs no forward state.  Segments that are not the first of their sequence only.
+template <int DK, int DV, bool InBf16>
+__global__ void __launch_bounds__(DV / 16 * kWave)
+reverse_local_kernel(BackwardLaunch L, SegmentView sv, float *hb) {
+    using In = Elem<InBf16>;
+    using IT = typename In::T;
+    constexpr int NS = DV / 16, NT = NS * kWave, R = DK / 4, RP = R + 4;
+    const IT *q = static_cast<const IT *>(L.q), *k = static_cast<const IT *>(L.k);
+    const IT *beta = static_cast<const IT *>(L.beta), *d_o = static_cast<const IT *>(L.d_o);
+    const int h = blockIdx.x, seg = blockIdx.y, H = L.H;
+    if (seg >= sv.count()) return;
+    const int4 sd = sv.table[seg];
+    if (sd.w & kSegFirst) return;
+    const int64_t t0 = sd.y, t1 = sd.z;
+    const int tid = threadIdx.x, lane = tid % kWave, slice = tid / kWave;
+    const int rg = lane & 3, col = 16 * slice + (lane >> 2);
+    __shared__ __attribute__((aligned(16))) float s_k[kBlock][4 * RP];
+    __shared__ __attribute__((aligned(16))) float s_q[kBlock][4 * RP];
+    __shared__ __attribute__((aligned(16))) float s_a[kBlock][4 * RP];
+    __shared__ float s_do[kBlock][DV], s_b[kBlock];
+    float ds[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) ds[i] = 0.f;
+    const int nb = static_cast<int>((t1 - t0 + kBlock - 1) / kBlock);
+    for (int b = nb - 1; b >= 0; --b) {
+        const int64_t tb = t0 + static_cast<int64_t>(b) * kBlock;
+        const int m = static_cast<int>(t1 - tb < kBlock ? t1 - tb : kBlock);
+        __syncthreads();
+        for (int e = tid; e < m * DK; e += NT) {
+            const int x = e / DK, i = e % DK, li = (i / R) * RP + i % R;
+            const int64_t idx = ((tb + x) * H + h) * DK + i;
+            s_k[x][li] = In::load(k, idx);
+            s_q[x][li] = In::load(q, idx);
+            s_a[x][li] = __expf(L.g[idx]);
+        }
+        for (int e = tid; e < m * DV; e += NT) {
+            const int x = e / DV, j = e % DV;
+            s_do[x][j] = In::load(d_o, ((tb + x) * H + h) * static_cast<int64_t>(DV) + j);
+        }
+        if (tid < m) s_b[tid] = In::load(beta, (tb + tid) * H + h);
+        __syncthreads();
+        for (int x = m - 1; x >= 0; --x) {
+            const float *kx = &s_k[x][rg * RP], *qx = &s_q[x][rg * RP], *ax = &s_a[x][rg * RP];
+            const float dos = L.scale * s_do[x][col];
+            float w0 = 0.f, w1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < R; i += 4) {
+                const float4 k4 = lds4(kx + i), q4 = lds4(qx + i);
+                ds[i] += q4.x * dos; ds[i + 1] += q4.y * dos; ds[i + 2] += q4.z * dos; ds[i + 3] += q4.w * dos;
+                w0 += ds[i] * k4.x;
+                w1 += ds[i + 1] * k4.y;
+                w0 += ds[i + 2] * k4.z;
+                w1 += ds[i + 3] * k4.w;
+            }
+            const float bw = s_b[x] * quad_sum(w0 + w1);
+#pragma unroll
+            for (int i = 0; i < R; i += 4) {
+                const float4 k4 = lds4(kx + i), a4 = lds4(ax + i);
+                ds[i] = a4.x * (ds[i] - k4.x * bw);
+                ds[i + 1] = a4.y * (ds[i + 1] - k4.y * bw);
+                ds[i + 2] = a4.z * (ds[i + 2] - k4.z * bw);
+                ds[i + 3] = a4.w * (ds[i + 3] - k4.w * bw);
+            }
+        }
+    }
+    float *dst = hb + (static_cast<int64_t>(seg) * H + h) * DK * DV + static_cast<int64_t>(rg * R) * DV + col;
+#pragma unroll
+    for (int i = 0; i < R; ++i) dst[i * DV] = ds[i];
+}
+
+// Reverse combine: per (sequence, head, 16-column slice of dv), from the final-state gradient, walk the
+// segments backwards storing the gradient of each segment's leaving state and carrying
+//     dS_enter(s) = P_s^T dS_leave(s) + Hb_s,      dS_leave(s - 1) = dS_enter(s)
+// (P_s the segment's forward transition, Hb_s from the reverse local pass).  Sequences of one segment
+// are left to the token kernel; an empty one gets its initial-state gradient here (the final-state
+// gradient itself).  fp32 FMA, P_s staged in LDS.
+template <int DK>
+__global__ void __launch_bounds__(256)
+reverse_combine_kernel(SegmentView sv, const float *hb, const float *dhT, float *dleave, float *dh0, int H, int DV) {
+    constexpr int BV = 16, DKP = DK + 1, RG = 256 / BV, ROWS = DK / RG, PV4 = DK * DK / 4 / 256;
+    __shared__ float sP[DK * DKP];
+    __shared__ float sS[DK * BV];
+    const int slice = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
+    const int tid = threadIdx.x, j = tid % BV, ig = tid / BV, j0 = slice * BV;
+    const int first = sv.seq_seg[n], end = sv.seq_seg[n + 1];
+    if (end - first == 1) return;
+    const int64_t nbase = (static_cast<int64_t>(n) * H + h) * DK * DV;
+    float x[ROWS];
+#pragma unroll
+    for (int u = 0; u < ROWS; ++u)
+        x[u] = dhT ? dhT[nbase + static_cast<int64_t>(ig + RG * u) * DV + j0 + j] : 0.f;
+    if (first >= end) {
+        if (dh0)
+#pragma unroll
+            for (int u = 0; u < ROWS; ++u) dh0[nbase + static_cast<int64_t>(ig + RG * u) * DV + j0 + j] = x[u];
+        return;
+    }
+    for (int seg = end - 1;; --seg) {
+        float *dl = dleave + (static_cast<int64_t>(seg) * H + h) * DK * DV;
+#pragma unroll
+        for (int u = 0; u < ROWS; ++u) dl[static_cast<int64_t>(ig + RG * u) * DV + j0 + j] = x[u];
+        if (seg == first) break;
+        __syncthreads();  // the previous product has finished with sP and sS
+        const float4 *src = reinterpret_cast<const float4 *>(sv.P + (static_cast<int64_t>(seg) * H + h) * DK * DK);
+#pragma unroll
+        for (int mm = 0; mm < PV4; ++mm) {
+            const float4 pv = src[tid + 256 * mm];
+            const int e = 4 * (tid + 256 * mm), r = e / DK, cc = e % DK;
+            sP[r * DKP + cc] = pv.x;
+            sP[r * DKP + cc + 1] = pv.y;
+            sP[r * DKP + cc + 2] = pv.z;
+            sP[r * DKP + cc + 3] = pv.w;
+        }
+#pragma unroll
+        for (int u = 0; u < ROWS; ++u) sS[(ig + RG * u) * BV + j] = x[u];
+        __syncthreads();
+        const float *hs = hb + (static_cast<int64_t>(seg) * H + h) * DK * DV;
+#pragma unroll
+        for (int u = 0; u < ROWS; ++u) {
+            const int i = ig + RG * u;
+            float a0 = 0.f, a1 = 0.f;
+            for (int m = 0; m < DK; m += 2) {  // (P^T x)[i] = sum_m P[m][i] x[m]
+                a0 += sP[m * DKP + i] * sS[m * BV + j];
+                a1 += sP[(m + 1) * DKP + i] * sS[(m + 1) * BV + j];
+            }
+            x[u] = (a0 + a1) + hs[static_cast<int64_t>(i) * DV + j0 + j];
+        }
+    }
+}
+
+namespace {
+
+// workspace: [segmented forward (table, P, H, entering states)] [dS_leave per segment] [stored states];
+// the reverse local pass writes its Hb over the forward's H, which the forward combine has consumed
+struct BwdPlan {
+    size_t off_dl, off_ckpt, bytes;
+    int max_segs;
+};
+
+BwdPlan bwd_plan(int B, int T, int H, int dk, int dv, int N, bool varlen) {
+    BwdPlan p{};
+    auto a256 = [](size_t x) { return (x + 255) & ~size_t{255}; };
+    const size_t seg_bytes = segment_states_bytes(B, T, H, dk, dv, N, varlen);
+    // the same bound on segments as the segmented forward's plan: at most one more than tokens / 64 per
+    // sequence, and at least one
+    const int64_t tokens = varlen ? T : static_cast<int64_t>(B) * T;
+    const size_t state = static_cast<size_t>(H) * dk * dv * sizeof(float);
+    const size_t max_segs = static_cast<size_t>(tokens / 64 + N + 1);
+    p.off_dl = a256(seg_bytes);
+    p.off_ckpt = a256(p.off_dl + max_segs * state);
+    p.bytes = p.off_ckpt + static_cast<size_t>(tokens / kBlock + max_segs) * state;
+    return p;
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int N, bool varlen) {
+    return bwd_plan(B, T, H, dk, dv, N, varlen).bytes;
 }
 
 template <int DK, int DV>
 static hipError_t launch_bwd(const BackwardLaunch &L) {
-    dim3 grid(L.H, L.N), block(DV / 16 * kWave);
+    const bool varlen = L.cu_seqlens != nullptr;
+    const BwdPlan p = bwd_plan(L.B, L.T, L.H, DK, DV, L.N, varlen);
+    char *ws = static_cast<char *>(L.workspace);
+    ChunkLaunch c{};
+    c.q = L.q; c.k = L.k; c.v = L.v; c.g = L.g; c.beta = L.beta;
+    c.h0 = L.h0; c.hT = nullptr; c.o = nullptr;
+    c.cu_seqlens = L.cu_seqlens;
+    c.B = L.B; c.T = L.T; c.H = L.H; c.dk = DK; c.dv = DV; c.N = L.N;
+    c.chunk = 64; c.scale = L.scale;
+    c.in_bf16 = L.in_bf16; c.out_bf16 = false;
+    c.xf = InputXform{};
+    c.workspace = ws;
+    c.workspace_bytes = p.off_dl;
+    c.stream = L.stream;
+    const SegmentStates ss = launch_segment_states(c);
+    float *dleave = reinterpret_cast<float *>(ws + p.off_dl);
+    BackwardLaunch b = L;
+    b.ckpt = reinterpret_cast<float *>(ws + p.off_ckpt);
+    const dim3 grid(L.H, ss.max_segs), block(DV / 16 * kWave);
     if (L.in_bf16)
-        hipLaunchKernelGGL((recurrent_bwd_kernel<DK, DV, true>), grid, block, 0, L.stream, L);
+        hipLaunchKernelGGL((reverse_local_kernel<DK, DV, true>), grid, block, 0, L.stream, b, ss.sv, ss.sv.Hs);
     else
-        hipLaunchKernelGGL((recurrent_bwd_kernel<DK, DV, false>), grid, block, 0, L.stream, L);
+        hipLaunchKernelGGL((reverse_local_kernel<DK, DV, false>), grid, block, 0, L.stream, b, ss.sv, ss.sv.Hs);
+    hipLaunchKernelGGL((reverse_combine_kernel<DK>), dim3(DV / 16, L.H, L.N), dim3(256), 0, L.stream, ss.sv,
+                       static_cast<const float *>(ss.sv.Hs), L.dhT, dleave, L.dh0, L.H, DV);
+    if (L.in_bf16)
+        hipLaunchKernelGGL((recurrent_bwd_kernel<DK, DV, true>), grid, block, 0, L.stream, b, ss.sv,
+                           static_cast<const float *>(dleave));
+    else
+        hipLaunchKernelGGL((recurrent_bwd_kernel<DK, DV, false>), grid, block, 0, L.stream, b, ss.sv,
+                           static_cast<const float *>(dleave));
     return hipGetLastError();
 }
 

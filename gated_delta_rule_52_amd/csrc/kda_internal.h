@@ -54,15 +54,16 @@ struct BackwardLaunch {
     const void *d_o;            // output gradient, dtype of q
     const float *h0, *dhT;      // initial state and final-state gradient (null: zero)
     float *dq, *dk, *dv, *dg, *dbeta, *dh0;  // fp32; dh0 may be null
-    const int32_t *cu_seqlens;  // device, or nullptr: N sequences of T tokens
-    int N, T, H, dk_dim, dv_dim;
+    const int32_t *cu_seqlens;  // device, or nullptr: B sequences of T tokens
+    int B, N, T, H, dk_dim, dv_dim;
     float scale;
     bool in_bf16;
-    float *ckpt;                // workspace: stored forward states
+    void *workspace;            // backward_workspace_bytes()
+    float *ckpt;                // stored forward states (set by launch_backward inside the workspace)
     hipStream_t stream;
 };
 
-size_t backward_workspace_bytes(int64_t tokens, int N, int H, int dk, int dv);
+size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int N, bool varlen);
 hipError_t launch_backward(const BackwardLaunch &L);
 
 // Chunkwise prefill.
@@ -112,6 +113,7 @@ struct SegmentView {
     const float *h0;        // [N, H, dk, dv] initial states (null: zero)
     int *xlist;             // chunks (pack numbers) the matrix-core prep hands to its exact path
     int *xcount;            // their count (zeroed by the segment-table kernel)
+    bool last_p;            // fp32 local pass: also P of the last segment of a sequence of several (gradients)
     __device__ __forceinline__ int count() const { return seq_seg[N]; }
     // the entering state of segment seg = {sequence, first token, end token, flags} at head h, row-major
     // dk x dv; null stands for the zero state.  A sequence of one segment enters with its initial state,
@@ -127,6 +129,18 @@ struct SegmentView {
 
 template <int MODE>
 void launch_fp32_pass(const ChunkLaunch &L, const SegmentView &sv, int max_segs);
+
+// The segmented forward up to its combine, on the fp32 path (chunk 64): the
+// segment table, P and H of every segment but the last of each sequence (P
+// in fp32), and the entering state of every segment of a sequence of several
+// segments.  The gradients start from these.  L.workspace must hold
+// segment_states_bytes(); o and hT are not touched.
+struct SegmentStates {
+    SegmentView sv;
+    int max_segs;  // bound on the number of segments (grid size)
+};
+size_t segment_states_bytes(int B, int T, int H, int dk, int dv, int N, bool varlen);
+SegmentStates launch_segment_states(const ChunkLaunch &L);
 
 // fp16/bf16 matrix-core path (bf16 inputs, dk = dv = 128, chunk 64): a
 // parallel prep kernel writes one operand pack per chunk and head

@@ -219,10 +219,15 @@ kda_status kda_recurrent_step(const kda_recurrent_step_args *args);
  *     dS~ = dS - k du^T,  dg = rowsum(S~ .* dS~),  dS <- Diag(exp(g)) dS~,
  * with S~ = Diag(exp(g_t)) S_{t-1}; the initial-state gradient is the final dS.
  *
- * Computed token by token in fp32 (one workgroup per sequence and head, one
- * wave per 16 columns of dv).  The forward states are recomputed, not read
- * from the forward pass: every 8th one is stored in the workspace on a first
- * sweep, and each group of 8 is rebuilt from it on the way back.
+ * Computed in fp32.  Long sequences are cut into segments as in
+ * kda_chunk_fwd: the segmented forward (fp32 path) gives the state entering
+ * each segment, and the state-gradient recurrence, which needs no forward
+ * state, is chained backwards over the segments through the transposed
+ * segment transitions.  Every segment then runs token by token in parallel
+ * (one workgroup per segment and head, one wave per 16 columns of dv); its
+ * forward states are recomputed, not read from the forward pass: every 8th
+ * one is stored in the workspace on a first sweep, and each group of 8 is
+ * rebuilt from it on the way back.
  *
  * Shapes (N = number of sequences; no KDA_FLAG_* transform is applied):
  *   q, k, v, g, beta, initial_state, cu_seqlens, B, T, H, dk, dv, num_seqs,
@@ -237,8 +242,9 @@ kda_status kda_recurrent_step(const kda_recurrent_step_args *args);
  *   The other gradients must not overlap any input, the workspace or each
  *   other.  Every gradient element of every token is written.
  *   workspace : device scratch of at least kda_recurrent_bwd_workspace_bytes()
- *               bytes, (floor(B*T / 8) + N) * H * dk * dv * 4; contents on
- *               entry ignored, on exit unspecified.
+ *               bytes, about (B*T / 8 + 2 B*T / 64) * H * dk * dv * 4 (one
+ *               stored state per 8 tokens, plus per-segment states); contents
+ *               on entry ignored, on exit unspecified.
  */
 typedef struct {
     uint32_t struct_size; /* = sizeof(kda_recurrent_bwd_args) */

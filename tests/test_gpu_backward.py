@@ -114,6 +114,24 @@ def test_head_dims_and_dtypes(kda, dk, dv, dt):
     check(kda, x, do, dhT)
 
 
+def test_long_single_sequence_segmented(kda):
+    """One sequence of 16384 tokens, 2 heads: cut into 128 segments that run
+    in parallel, chained by the forward and reverse combines."""
+    x = make_prefill(146, 1, 16384, 2, 128, 128, h0_std=0.05, name="bwd_single_16k")
+    do, dhT = make_output_grads(x, 246, dhT_std=0.05)
+    check(kda, x, do, dhT)
+
+
+@pytest.mark.parametrize("dk,dv,dt", [(64, 64, "fp32"), (64, 128, "bf16"), (128, 64, "bf16")])
+def test_varlen_long_members_segmented(kda, dk, dv, dt):
+    """Packed sequences of 700, 0, 64, 65, 1, 300 tokens: several of several
+    segments, with every head size."""
+    x = make_prefill(147, 1, 0, 2, dk, dv, in_dtype=dt, gscale=0.1, h0_std=0.3,
+                     seqlens=[700, 0, 64, 65, 1, 300], name=f"bwd_varlen_seg_{dk}x{dv}")
+    do, dhT = make_output_grads(x, 247, dhT_std=0.3)
+    check(kda, x, do, dhT, scale=0.8)
+
+
 def test_varlen_with_empty_and_short_sequences(kda):
     """Lengths 0, 1, 7, 8, 9, 33, 0, 64, 17 in one packed batch: every block
     boundary case; empty sequences pass the final-state gradient through."""
@@ -138,11 +156,13 @@ def test_long_sequences(kda):
         check(kda, x, do, dhT)
 
 
-def test_in_place_and_deterministic(kda):
-    """grad_initial_state may be grad_final_state (or initial_state); two runs
-    give the same bits; the gradient outputs need no prior contents."""
+@pytest.mark.parametrize("T", [40, 300])
+def test_in_place_and_deterministic(kda, T):
+    """grad_initial_state may be grad_final_state (or initial_state), for
+    sequences of one segment (40 tokens) and of several (300); two runs give
+    the same bits; the gradient outputs need no prior contents."""
     import torch
-    x = make_prefill(145, 2, 40, 2, 128, 128, h0_std=0.3, name="bwd_in_place")
+    x = make_prefill(145, 2, T, 2, 128, 128, h0_std=0.3, name="bwd_in_place")
     do, dhT = make_output_grads(x, 245, dhT_std=0.3)
     d = upload(x)
     dod, dht = dev(do, in_dtype_of(x)), dev(dhT, torch.float32)
