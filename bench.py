@@ -328,12 +328,12 @@ def backward_alg_bytes(tokens, H, dk, dv, N, in_bytes=2):
     return th * ((2 * dk + 2 * dv + 1) * in_bytes + dk * 4 + (3 * dk + dv + 1) * 4) + 3 * N * H * dk * dv * 4
 
 
-def time_backward(args):
-    """Gradients of the 16 x 4096 x 16 training batch (kda_recurrent_bwd), us per call."""
+def time_backward(args, name="backward_64k"):
+    """Gradients (kda_recurrent_bwd) of a named workload, ms per call."""
     import torch
     import gated_delta_rule_52_amd as kda
     from gated_delta_rule_52_amd.inputs import make_output_grads, make_workload
-    x = make_workload("backward_16x4096x16")
+    x = make_workload(name)
     do, dhT = make_output_grads(x, 106)
     dev = "cuda:0"
     bf, f32 = torch.bfloat16, torch.float32
@@ -358,13 +358,13 @@ def time_backward(args):
         torch.cuda.synchronize()
         per.append(e0.elapsed_time(e1))
     ms = float(np.mean(per))
-    log(f"backward_16x4096x16: {ms:.3f} ms per call")
+    log(f"{name}: {ms:.3f} ms per call")
     return x, ms, per
 
 
 def cpu_backward_sample(x):
-    """The fp64 oracle's gradients on one sequence's first 1024 tokens, all
-    heads (OpenMP over heads): tokens x heads per second."""
+    """The fp64 oracle's gradients on the first 1024 tokens of sequence 0,
+    all heads (OpenMP over heads): tokens (all heads) per second."""
     import oracle
     from gated_delta_rule_52_amd.inputs import make_output_grads
     do, dhT = make_output_grads(x, 106)
@@ -377,7 +377,7 @@ def cpu_backward_sample(x):
     dt = time.perf_counter() - t0
     log(f"oracle backward: {dt:.2f} s on {threads} threads")
     return dict(value=L / dt, unit="tokens/s (all 16 heads)", cores=threads, kind="oracle",
-                sample=f"sequence 0, first {L} tokens, {x.H} heads of backward_16x4096x16, {dt:.2f} s wall")
+                sample=f"first {L} tokens of sequence 0, {x.H} heads, {dt:.2f} s wall")
 
 
 def copy_ceiling():
@@ -518,24 +518,26 @@ def main():
             "us_per_call": time_append_grid(),
         }
     if not args.no_backward:
-        xb, msb, perb = time_backward(args)
-        toks = xb.B * xb.T
-        flops = backward_alg_flops(toks, xb.H, xb.dk, xb.dv)
-        bbytes = backward_alg_bytes(toks, xb.H, xb.dk, xb.dv, xb.N)
-        tf = flops / (msb * 1e-3) / 1e12
-        rec["backward"] = {
-            "workload": "backward_16x4096x16", "B": xb.B, "T": xb.T, "H": xb.H, "dk": xb.dk, "dv": xb.dv,
-            "in_dtype": "bf16", "grad_dtype": "fp32", "ms_per_call": msb, "ms_median": float(np.median(perb)),
-            "tokens_per_s": toks / (msb * 1e-3),
-            "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tf / FP32_VECTOR_PEAK_TFLOPS, "alg_flops_per_launch": flops,
-                         "hbm_alg_bytes_per_launch": bbytes,
-                         "hbm_frac": bbytes / (msb * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                         "kernel": "recurrent_bwd_kernel<128,128,bf16>, one launch per call"},
-        }
-        if not args.no_cpu:
-            rec["backward"]["cpu_baseline"] = cpu_backward_sample(xb)
-        del xb
+        for key, wl in (("backward", "backward_64k"), ("backward_batch", "backward_16x4096x16")):
+            xb, msb, perb = time_backward(args, wl)
+            toks = xb.B * xb.T
+            flops = backward_alg_flops(toks, xb.H, xb.dk, xb.dv)
+            bbytes = backward_alg_bytes(toks, xb.H, xb.dk, xb.dv, xb.N)
+            tf = flops / (msb * 1e-3) / 1e12
+            rec[key] = {
+                "workload": wl, "B": xb.B, "T": xb.T, "H": xb.H, "dk": xb.dk, "dv": xb.dv,
+                "in_dtype": "bf16", "grad_dtype": "fp32", "ms_per_call": msb, "ms_median": float(np.median(perb)),
+                "tokens_per_s": toks / (msb * 1e-3),
+                "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": tf / FP32_VECTOR_PEAK_TFLOPS, "alg_flops_per_launch": flops,
+                             "hbm_alg_bytes_per_launch": bbytes,
+                             "hbm_frac": bbytes / (msb * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "kernel": "one kda_recurrent_bwd call: segmented fp32 forward to the combine, "
+                                       "reverse local pass, reverse combine, recurrent_bwd_kernel<128,128,bf16>"},
+            }
+            if key == "backward" and not args.no_cpu:
+                rec[key]["cpu_baseline"] = cpu_backward_sample(xb)
+            del xb
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(x)
     print(json.dumps(rec), flush=True)

@@ -73,6 +73,42 @@ __device__ __forceinline__ float column_total(float x) {
 
 __device__ __forceinline__ float4 lds4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 
+// One forward step of this lane's R rows of one state column, X -> X~ + b k (v - X~^T k), X~ = Diag(alpha) X,
+// with kx, ax the lane's rows of k and alpha in LDS.  The LDS reads are software-pipelined by hand: each
+// group of four rows issues the next group's reads before its own arithmetic, and a scheduling fence
+// keeps the compiler from hoisting every read to the top (which would cost 2 R registers).
+template <int R>
+__device__ __forceinline__ void advance_rows(float (&s)[R], const float *kx, const float *ax, float v, float b) {
+    float p0 = 0.f, p1 = 0.f;
+    float4 kc = lds4(kx), ac = lds4(ax);
+#pragma unroll
+    for (int i = 0; i < R; i += 4) {
+        __builtin_amdgcn_sched_barrier(0);
+        float4 kn = kc, an = ac;
+        if (i + 4 < R) {
+            kn = lds4(kx + i + 4);
+            an = lds4(ax + i + 4);
+        }
+        s[i] *= ac.x; s[i + 1] *= ac.y; s[i + 2] *= ac.z; s[i + 3] *= ac.w;
+        p0 += s[i] * kc.x;
+        p1 += s[i + 1] * kc.y;
+        p0 += s[i + 2] * kc.z;
+        p1 += s[i + 3] * kc.w;
+        kc = kn;
+        ac = an;
+    }
+    kc = lds4(kx);  // k is read again rather than held: registers are scarce
+    const float bd = b * (v - quad_sum(p0 + p1));
+#pragma unroll
+    for (int i = 0; i < R; i += 4) {
+        __builtin_amdgcn_sched_barrier(0);
+        float4 kn = kc;
+        if (i + 4 < R) kn = lds4(kx + i + 4);
+        s[i] += bd * kc.x; s[i + 1] += bd * kc.y; s[i + 2] += bd * kc.z; s[i + 3] += bd * kc.w;
+        kc = kn;
+    }
+}
+
 }  // namespace
 
 // Token-by-token gradients of one segment per workgroup (a sequence, or a piece of one): the forward
@@ -157,39 +193,8 @@ recurrent_bwd_kernel(BackwardLaunch L, SegmentView sv, const float *dleave) {
     };
 
     // s = S_{t-1} -> S_t for staged token x
-    // LDS reads are software-pipelined by hand: each group of four rows issues the next group's reads
-    // before its own arithmetic, and a scheduling fence keeps the compiler from hoisting every read
-    // to the top (which would cost 3 R registers).
     auto advance = [&](float (&s)[R], int x) {
-        const float *kx = &s_k[x][rg * RP], *ax = &s_a[x][rg * RP];
-        float p0 = 0.f, p1 = 0.f;
-        float4 kc = lds4(kx), ac = lds4(ax);
-#pragma unroll
-        for (int i = 0; i < R; i += 4) {
-            __builtin_amdgcn_sched_barrier(0);
-            float4 kn = kc, an = ac;
-            if (i + 4 < R) {
-                kn = lds4(kx + i + 4);
-                an = lds4(ax + i + 4);
-            }
-            s[i] *= ac.x; s[i + 1] *= ac.y; s[i + 2] *= ac.z; s[i + 3] *= ac.w;
-            p0 += s[i] * kc.x;
-            p1 += s[i + 1] * kc.y;
-            p0 += s[i + 2] * kc.z;
-            p1 += s[i + 3] * kc.w;
-            kc = kn;
-            ac = an;
-        }
-        kc = lds4(kx);  // k is read again rather than held: registers are scarce
-        const float bd = s_b[x] * (s_v[x][col] - quad_sum(p0 + p1));
-#pragma unroll
-        for (int i = 0; i < R; i += 4) {
-            __builtin_amdgcn_sched_barrier(0);
-            float4 kn = kc;
-            if (i + 4 < R) kn = lds4(kx + i + 4);
-            s[i] += bd * kc.x; s[i + 1] += bd * kc.y; s[i + 2] += bd * kc.z; s[i + 3] += bd * kc.w;
-            kc = kn;
-        }
+        advance_rows<R>(s, &s_k[x][rg * RP], &s_a[x][rg * RP], s_v[x][col], s_b[x]);
     };
 
     float ds[R];  // gradient of the state leaving the token being processed
@@ -401,6 +406,59 @@ recurrent_bwd_kernel(BackwardLaunch L, SegmentView sv, const float *dleave) {
     }
 }
 
+// The segmented forward's local pass, token by token in fp32, for every segment of a sequence of several:
+// H from a zero state with the segment's tokens, and the columns of the transition P (dk x dk) from the
+// identity with v = 0, both by one forward step per token.  One wave per 16 columns of [H | P].
+template <int DK, int DV, bool InBf16>
+__global__ void __launch_bounds__((DV + DK) / 16 * kWave)
+segment_local_kernel(BackwardLaunch L, SegmentView sv) {
+    using In = Elem<InBf16>;
+    using IT = typename In::T;
+    constexpr int NT = (DV + DK) / 16 * kWave, R = DK / 4, RP = R + 4;
+    const IT *k = static_cast<const IT *>(L.k), *v = static_cast<const IT *>(L.v);
+    const IT *beta = static_cast<const IT *>(L.beta);
+    const int h = blockIdx.x, seg = blockIdx.y, H = L.H;
+    if (seg >= sv.count()) return;
+    const int4 sd = sv.table[seg];
+    if ((sd.w & (kSegFirst | kSegLast)) == (kSegFirst | kSegLast)) return;  // one segment: nothing to chain
+    const int64_t t0 = sd.y, t1 = sd.z;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int rg = lane & 3;
+    const bool pcol = wave >= DV / 16;
+    const int col = (pcol ? wave - DV / 16 : wave) * 16 + (lane >> 2);  // column of P, or of H
+    __shared__ __attribute__((aligned(16))) float s_k[kBlock][4 * RP];
+    __shared__ __attribute__((aligned(16))) float s_a[kBlock][4 * RP];
+    __shared__ float s_v[kBlock][DV], s_b[kBlock];
+    float s[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) s[i] = pcol && rg * R + i == col ? 1.f : 0.f;
+    const int nb = static_cast<int>((t1 - t0 + kBlock - 1) / kBlock);
+    for (int b = 0; b < nb; ++b) {
+        const int64_t tb = t0 + static_cast<int64_t>(b) * kBlock;
+        const int m = static_cast<int>(t1 - tb < kBlock ? t1 - tb : kBlock);
+        __syncthreads();
+        for (int e = tid; e < m * DK; e += NT) {
+            const int x = e / DK, i = e % DK, li = (i / R) * RP + i % R;
+            const int64_t idx = ((tb + x) * H + h) * DK + i;
+            s_k[x][li] = In::load(k, idx);
+            s_a[x][li] = __expf(L.g[idx]);
+        }
+        for (int e = tid; e < m * DV; e += NT) {
+            const int x = e / DV, j = e % DV;
+            s_v[x][j] = In::load(v, ((tb + x) * H + h) * static_cast<int64_t>(DV) + j);
+        }
+        if (tid < m) s_b[tid] = In::load(beta, (tb + tid) * H + h);
+        __syncthreads();
+        for (int x = 0; x < m; ++x)
+            advance_rows<R>(s, &s_k[x][rg * RP], &s_a[x][rg * RP], pcol ? 0.f : s_v[x][col], s_b[x]);
+    }
+    float *dst = pcol ? sv.P + (static_cast<int64_t>(seg) * H + h) * DK * DK + static_cast<int64_t>(rg * R) * DK + col
+                      : sv.Hs + (static_cast<int64_t>(seg) * H + h) * DK * DV + static_cast<int64_t>(rg * R) * DV + col;
+    const int ld = pcol ? DK : DV;
+#pragma unroll
+    for (int i = 0; i < R; ++i) dst[i * ld] = s[i];
+}
+
 // The gradient of the state entering a segment, from a zero gradient at its end (the part of dS that
 // the segment's own output gradients contribute): walking its tokens backwards,
 //     dS += scale q do^T;   dS <- Diag(alpha) (I - beta k k^T) dS,
@@ -536,7 +594,7 @@ reverse_combine_kernel(SegmentView sv, const float *hb, const float *dhT, float 
 
 namespace {
 
-// workspace: [segmented forward (table, P, H, entering states)] [dS_leave per segment] [stored states];
+// workspace: [segment table, P, H, entering states] [dS_leave per segment] [stored states];
 // the reverse local pass writes its Hb over the forward's H, which the forward combine has consumed
 struct BwdPlan {
     size_t off_dl, off_ckpt, bytes;
@@ -580,11 +638,17 @@ static hipError_t launch_bwd(const BackwardLaunch &L) {
     c.workspace = ws;
     c.workspace_bytes = p.off_dl;
     c.stream = L.stream;
-    const SegmentStates ss = launch_segment_states(c);
+    const SegmentStates ss = launch_segment_table(c);
     float *dleave = reinterpret_cast<float *>(ws + p.off_dl);
     BackwardLaunch b = L;
     b.ckpt = reinterpret_cast<float *>(ws + p.off_ckpt);
     const dim3 grid(L.H, ss.max_segs), block(DV / 16 * kWave);
+    const dim3 block_local((DV + DK) / 16 * kWave);
+    if (L.in_bf16)
+        hipLaunchKernelGGL((segment_local_kernel<DK, DV, true>), grid, block_local, 0, L.stream, b, ss.sv);
+    else
+        hipLaunchKernelGGL((segment_local_kernel<DK, DV, false>), grid, block_local, 0, L.stream, b, ss.sv);
+    launch_segment_combine(c, ss);
     if (L.in_bf16)
         hipLaunchKernelGGL((reverse_local_kernel<DK, DV, true>), grid, block, 0, L.stream, b, ss.sv, ss.sv.Hs);
     else

@@ -113,12 +113,10 @@ chunk_fp32_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
     const int4 sd = sv.table[seg];
     const int n = sd.x;
     const bool last = sd.w & kSegLast;
+    if (MODE == kLocal && last) return;         // a last segment's P, H are never used
     const int64_t t0 = sd.y, t1 = sd.z;
     // kLocal: slices [0, DV/BV) are columns of H, the rest columns of P (dk x dk)
     const bool pcols = MODE == kLocal && slice >= DV / BV;
-    // The forward never uses a last segment's P or H; the gradients use the P of the last segment of a
-    // sequence of several segments.
-    if (MODE == kLocal && last && !(sv.last_p && pcols && !(sd.w & kSegFirst))) return;
     const int j0 = (pcols ? slice - DV / BV : slice) * BV;
     const int ld = pcols ? DK : DV;             // row stride of the state being built
 

@@ -113,7 +113,6 @@ struct SegmentView {
     const float *h0;        // [N, H, dk, dv] initial states (null: zero)
     int *xlist;             // chunks (pack numbers) the matrix-core prep hands to its exact path
     int *xcount;            // their count (zeroed by the segment-table kernel)
-    bool last_p;            // fp32 local pass: also P of the last segment of a sequence of several (gradients)
     __device__ __forceinline__ int count() const { return seq_seg[N]; }
     // the entering state of segment seg = {sequence, first token, end token, flags} at head h, row-major
     // dk x dv; null stands for the zero state.  A sequence of one segment enters with its initial state,
@@ -130,17 +129,18 @@ struct SegmentView {
 template <int MODE>
 void launch_fp32_pass(const ChunkLaunch &L, const SegmentView &sv, int max_segs);
 
-// The segmented forward up to its combine, on the fp32 path (chunk 64): the
-// segment table, P and H of every segment but the last of each sequence (P
-// in fp32), and the entering state of every segment of a sequence of several
-// segments.  The gradients start from these.  L.workspace must hold
-// segment_states_bytes(); o and hT are not touched.
+// Pieces of the segmented forward for the gradients: the segment table of a
+// plan without operand packs (chunk 64), and the combine that turns P and H
+// of every segment (written by the caller's own local pass into sv.P, sv.Hs)
+// into entering states.  L.workspace must hold segment_states_bytes(); o and
+// hT are not touched.
 struct SegmentStates {
     SegmentView sv;
     int max_segs;  // bound on the number of segments (grid size)
 };
 size_t segment_states_bytes(int B, int T, int H, int dk, int dv, int N, bool varlen);
-SegmentStates launch_segment_states(const ChunkLaunch &L);
+SegmentStates launch_segment_table(const ChunkLaunch &L);
+void launch_segment_combine(const ChunkLaunch &L, const SegmentStates &s);
 
 // fp16/bf16 matrix-core path (bf16 inputs, dk = dv = 128, chunk 64): a
 // parallel prep kernel writes one operand pack per chunk and head

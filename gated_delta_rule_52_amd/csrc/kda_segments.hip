@@ -451,7 +451,6 @@ hipError_t launch_chunk(const ChunkLaunch &L) {
     sv.h0 = L.h0;
     sv.xcount = p.packs ? reinterpret_cast<int *>(ws + p.off_xlist) : nullptr;
     sv.xlist = p.packs ? sv.xcount + 1 : nullptr;
-    sv.last_p = false;
 
     hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(256), 0, L.stream, L.cu_seqlens, L.T, L.N,
                        p.seg_len, reinterpret_cast<int4 *>(ws + p.off_table),
@@ -481,9 +480,9 @@ size_t segment_states_bytes(int B, int T, int H, int dk, int dv, int N, bool var
     return make_plan(B, T, H, dk, dv, N, 64, varlen, false).bytes;
 }
 
-SegmentStates launch_segment_states(const ChunkLaunch &L) {
+SegmentStates launch_segment_table(const ChunkLaunch &L) {
     const bool varlen = L.cu_seqlens != nullptr;
-    const Plan p = make_plan(L.B, L.T, L.H, L.dk, L.dv, L.N, 64, varlen, false);  // fp32 path: P exact in fp32
+    const Plan p = make_plan(L.B, L.T, L.H, L.dk, L.dv, L.N, 64, varlen, false);
     char *ws = static_cast<char *>(L.workspace);
     SegmentStates r{};
     SegmentView &sv = r.sv;
@@ -496,23 +495,20 @@ SegmentStates launch_segment_states(const ChunkLaunch &L) {
     sv.h0 = L.h0;
     sv.xcount = nullptr;
     sv.xlist = nullptr;
-    sv.last_p = true;
     r.max_segs = p.max_segs;
     hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(256), 0, L.stream, L.cu_seqlens, L.T, L.N,
                        p.seg_len, reinterpret_cast<int4 *>(ws + p.off_table),
                        reinterpret_cast<int32_t *>(ws + p.off_seq), nullptr);
-    ChunkLaunch c = L;
-    c.chunk = 64;
-    c.hT = nullptr;
-    c.o = nullptr;
-    launch_fp32_pass<kLocal>(c, sv, p.max_segs);
+    return r;
+}
+
+void launch_segment_combine(const ChunkLaunch &L, const SegmentStates &s) {
     if (L.dk == 128)
-        hipLaunchKernelGGL(combine_mfma_kernel, dim3(L.H, L.dv / 16, L.N), dim3(256), 0, L.stream, sv, L.h0,
+        hipLaunchKernelGGL(combine_mfma_kernel, dim3(L.H, L.dv / 16, L.N), dim3(256), 0, L.stream, s.sv, L.h0,
                            static_cast<float *>(nullptr), L.H, L.dv);
     else
-        hipLaunchKernelGGL(combine_kernel<64>, dim3(L.dv / 16, L.H, L.N), dim3(256), 0, L.stream, sv, L.h0,
+        hipLaunchKernelGGL(combine_kernel<64>, dim3(L.dv / 16, L.H, L.N), dim3(256), 0, L.stream, s.sv, L.h0,
                            static_cast<float *>(nullptr), L.H, L.dv);
-    return r;
 }
 
 }  // namespace kda

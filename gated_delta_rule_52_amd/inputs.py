@@ -258,6 +258,9 @@ WORKLOADS = {
     # final-state gradient from make_output_grads with seed + 100)
     "backward_16x4096x16": dict(kind="prefill", seed=6, B=16, T=4096, H=16, dk=128, dv=128,
                                 in_dtype="bf16", gscale=1.0, h0_std=0.02),
+    # the gradients of the prefill shape: one sequence of 65,536 tokens
+    "backward_64k": dict(kind="prefill", seed=2, B=1, T=65536, H=16, dk=128, dv=128,
+                         in_dtype="bf16", gscale=1.0, h0_std=0.02),
     "varlen_8seq": dict(kind="prefill", seed=4, B=1, T=None, H=32, dk=128, dv=128,
                         in_dtype="bf16", gscale=0.01, h0_std=0.02,
                         lengths_range=(1024, 32768), n_seqs=8),
