@@ -53,13 +53,17 @@ def decode_alg_bytes(N, H, dk, dv, in_bytes=2, out_bytes=2):
     return nh * (2 * dk * dv * 4 + (2 * dk + dv + 1) * in_bytes + dk * 4 + dv * out_bytes)
 
 
+# sources no kernel of kda_chunk_fwd is built from (decode and append kernels, gradients)
+NOT_PREFILL_SOURCES = ("kda_recurrent.hip", "kda_backward.hip")
+
+
 def source_digest():
-    """sha256 over the HIP/C++ sources: a stored traffic measurement is only
-    reported while the kernels it was taken on are unchanged."""
+    """sha256 over the HIP/C++ sources the prefill's kernels are built from: a
+    stored traffic measurement is only reported while they are unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_52_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".cpp", ".h")):
+        if name.endswith((".hip", ".cpp", ".h")) and name not in NOT_PREFILL_SOURCES:
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -342,8 +346,10 @@ def time_backward(args, name="backward_64k"):
     g, h0, dht = t(x.g, f32), t(x.h0, f32), t(dhT, f32)
     ws = torch.empty(kda.recurrent_bwd_workspace_bytes(q, v), dtype=torch.uint8, device=dev)
     dh0 = torch.empty_like(h0)
+    grads = {n: torch.empty(sh, dtype=f32, device=dev) for n, sh in
+             (("dq", q.shape), ("dk", q.shape), ("dv", v.shape), ("dg", q.shape), ("dbeta", beta.shape))}
     fn = lambda: kda.recurrent_bwd(q, k, v, g, beta, d_o, initial_state=h0, grad_final_state=dht,
-                                   grad_initial_state=dh0, workspace=ws)
+                                   grad_initial_state=dh0, workspace=ws, out=grads)
     for _ in range(max(args.warmup, 1)):
         fn()
     torch.cuda.synchronize()

@@ -240,14 +240,15 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   grad_final_state: Optional[torch.Tensor] = None,
                   cu_seqlens: Optional[torch.Tensor] = None, scale: float = 1.0,
                   output_grad_initial_state: bool = True, grad_initial_state: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None):
+                  workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None):
     """Gradients of the recurrence (no input transforms) for the output
     gradient ``grad_o`` [B,T,H,dv] (dtype of q) and the optional final-state
     gradient [N,H,dk,dv] fp32.  Inputs as in ``chunk_fwd``.  Returns a dict of
     fp32 tensors: dq, dk, dg [B,T,H,dk], dv [B,T,H,dv], dbeta [B,T,H] and dh0
     [N,H,dk,dv] (None unless ``output_grad_initial_state`` or
     ``grad_initial_state`` is given; the latter may be ``initial_state`` or
-    ``grad_final_state`` for an in-place result)."""
+    ``grad_final_state`` for an in-place result).  ``out`` may supply the
+    token gradients (a dict with dq, dk, dv, dg, dbeta), written in place."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
@@ -271,9 +272,14 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     elif grad_initial_state is not None:
         _need(grad_initial_state, "grad_initial_state", (N, H, dk, dv), torch.float32)
     f32 = dict(dtype=torch.float32, device=q.device)
-    out = dict(dq=torch.empty((B, T, H, dk), **f32), dk=torch.empty((B, T, H, dk), **f32),
-               dv=torch.empty((B, T, H, dv), **f32), dg=torch.empty((B, T, H, dk), **f32),
-               dbeta=torch.empty((B, T, H), **f32), dh0=grad_initial_state)
+    shapes = dict(dq=(B, T, H, dk), dk=(B, T, H, dk), dv=(B, T, H, dv), dg=(B, T, H, dk), dbeta=(B, T, H))
+    if out is None:
+        out = {n: torch.empty(sh, **f32) for n, sh in shapes.items()}
+    else:
+        out = {n: out[n] for n in shapes}
+        for n, sh in shapes.items():
+            _need(out[n], n, sh, torch.float32)
+    out["dh0"] = grad_initial_state
     ws = recurrent_bwd_workspace_bytes(q, v, cu_seqlens)
     if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)

@@ -173,8 +173,12 @@ def test_in_place_and_deterministic(kda, T):
     c = kda.recurrent_bwd(*args, initial_state=d["h0"], grad_final_state=buf, grad_initial_state=buf)
     h0c = d["h0"].clone()
     e = kda.recurrent_bwd(*args, initial_state=h0c, grad_final_state=dht, grad_initial_state=h0c)
+    # caller-supplied gradient tensors holding garbage are overwritten entirely
+    pre = {n: torch.full_like(a[n], float("nan")) for n in ("dq", "dk", "dv", "dg", "dbeta")}
+    f = kda.recurrent_bwd(*args, initial_state=d["h0"], grad_final_state=dht, out=pre)
     torch.cuda.synchronize()
     for name in NAMES:
+        assert torch.equal(a[name], f[name]), f"{name} differs with caller-supplied outputs"
         assert torch.equal(a[name], b[name]), f"{name} not deterministic"
         assert torch.equal(a[name], c[name]), f"{name} differs in place (grad_final_state)"
         assert torch.equal(a[name], e[name]), f"{name} differs in place (initial_state)"
