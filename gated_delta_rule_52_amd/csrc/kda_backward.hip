@@ -355,16 +355,54 @@ recurrent_bwd_kernel(BackwardLaunch L, SegmentView sv, const float *dleave) {
         }
     };
 
-    // forward sweep: the state entering every block
+    // forward sweep: the state entering every block.  Only whole blocks are swept (the last block, the
+    // only one that may be short, is not), and the next block's inputs are fetched into registers while
+    // the current one runs.
+    constexpr int KPT = kBlock * DK / NT, VPT = kBlock * DV / NT;  // elements per thread and block
+    static_assert(KPT * NT == kBlock * DK && VPT * NT == kBlock * DV, "staging split");
+    struct Ahead {
+        float k[KPT], g[KPT], v[VPT], b;
+    } ahead;
+    auto fetch_block = [&](int64_t tb) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int e = tid + j * NT;
+            const int64_t idx = ((tb + e / DK) * H + h) * DK + e % DK;
+            ahead.k[j] = In::load(k, idx);
+            ahead.g[j] = g[idx];
+        }
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int e = tid + j * NT;
+            ahead.v[j] = In::load(v, ((tb + e / DV) * H + h) * static_cast<int64_t>(DV) + e % DV);
+        }
+        if (tid < kBlock) ahead.b = In::load(beta, (tb + tid) * H + h);
+    };
+    auto put_block = [&]() {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int e = tid + j * NT, i = e % DK;
+            s_k[e / DK][(i / R) * RP + i % R] = ahead.k[j];
+            s_a[e / DK][(i / R) * RP + i % R] = __expf(ahead.g[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int e = tid + j * NT;
+            s_v[e / DV][e % DV] = ahead.v[j];
+        }
+        if (tid < kBlock) s_b[tid] = ahead.b;
+    };
     float st[kSub][R];
     load_slice(st[0], sv.entering(seg, sd, h, H, DK, DV));
+    if (nb > 1) fetch_block(t0);
     for (int b = 0; b < nb; ++b) {
         float *cp = stored(b);
 #pragma unroll
         for (int i = 0; i < R; ++i) cp[i * kWave] = st[0][i];
         if (b == nb - 1) break;
         __syncthreads();  // the previous block's tokens have been read
-        stage(t0 + static_cast<int64_t>(b) * kBlock, kBlock, false);
+        put_block();
+        if (b + 2 < nb) fetch_block(t0 + static_cast<int64_t>(b + 1) * kBlock);
         __syncthreads();
         for (int x = 0; x < kBlock; ++x) advance(st[0], x);
     }
