@@ -26,7 +26,10 @@ namespace kda {
 
 namespace {
 
-constexpr int kTargetUnits = 256;  // segments x heads: one long segment per compute unit and pass
+// segments x heads: one long segment per compute unit and pass; half that for short problems (at most
+// 1,024 chunk-heads, e.g. 2K tokens x 16 heads), where the combine's serial chain would cost more than
+// the extra parallelism saves (measured: 2K tokens x 16 heads 90 -> 79 us, 4K level, longer unchanged)
+constexpr int kTargetUnits = 256, kTargetUnitsShort = 128, kShortChunkHeads = 1024;
 
 struct Plan {
     int per;        // chunks per segment
@@ -43,7 +46,8 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int N, int chunk, bool varle
     const int64_t tokens = varlen ? T : static_cast<int64_t>(B) * T;
     const int64_t chunks = varlen ? (tokens + chunk - 1) / chunk + N
                                   : static_cast<int64_t>(B) * ((T + chunk - 1) / chunk);
-    int64_t per = (chunks * H + kTargetUnits - 1) / kTargetUnits;
+    const int64_t units = chunks * H <= kShortChunkHeads ? kTargetUnitsShort : kTargetUnits;
+    int64_t per = (chunks * H + units - 1) / units;
     if (per > 64) per = 64;
     // Segments never span two sequences, so a segment longer than the
     // sequences only pads the pack array (and the prep grid) with empty

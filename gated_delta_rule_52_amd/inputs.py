@@ -42,7 +42,7 @@ import numpy as np
 
 __all__ = [
     "KdaInputs", "bf16_round", "l2_normalise", "softplus", "sigmoid",
-    "make_prefill", "make_output_grads", "make_decode_state", "decode_steps", "decode_step_pool", "WORKLOADS",
+    "make_prefill", "make_output_grads", "make_dplr", "make_decode_state", "decode_steps", "decode_step_pool", "WORKLOADS",
     "make_workload",
 ]
 
@@ -181,6 +181,43 @@ def make_prefill(seed: int, B: int, T: int, H: int, dk: int, dv: int,
                      in_dtype=in_dtype, name=name,
                      meta=dict(seed=seed, gscale=gscale, h0_std=h0_std), fused=fused,
                      scalar_gate=scalar_gate)
+
+
+def make_dplr(seed: int, B: int, T: int, H: int, dk: int, dv: int, in_dtype: str = "bf16",
+              gscale: float = 1.0, h0_std: Optional[float] = None, seqlens=None) -> dict:
+    """Inputs of the general DPLR recurrence S_t = (Diag(e^g) - a b^T) S + k v^T.
+
+    Draw order: [lengths], q, k, v, beta-logits, g-logits, w, h0, where w is a
+    second unit direction per token and head.  q, k, w are L2-normalised N(0,1),
+    v ~ N(0,1), g = -gscale softplus(N(0,1)) and beta = sigmoid(N(0,1)), as in
+    make_prefill; then a = beta w and b = e^g * w, so the transition
+    Diag(e^g) - a b^T = (I - beta w w^T) Diag(e^g) contracts while a and b are
+    untied from the key k of the write (which is beta k).  Values that travel
+    in in_dtype are rounded once; b is formed from the rounded w.  Returns a dict
+    of float32 arrays q, k, v, g, a, b [B, T, H, d], h0 or None, cu_seqlens or
+    None, and in_dtype."""
+    rng = np.random.default_rng(seed)
+    cu = None
+    if seqlens is not None:
+        seqlens = np.asarray(seqlens, dtype=np.int64)
+        cu = np.zeros(len(seqlens) + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(seqlens)
+        B, T = 1, int(cu[-1])
+    N = B if cu is None else len(cu) - 1
+    f32 = np.float32
+    q = rng.standard_normal((B, T, H, dk), dtype=f32)
+    k = rng.standard_normal((B, T, H, dk), dtype=f32)
+    v = rng.standard_normal((B, T, H, dv), dtype=f32)
+    bl = rng.standard_normal((B, T, H), dtype=f32)
+    gl = rng.standard_normal((B, T, H, dk), dtype=f32)
+    w = rng.standard_normal((B, T, H, dk), dtype=f32)
+    h0 = None if h0_std is None else (h0_std * rng.standard_normal((N, H, dk, dv), dtype=f32)).astype(f32)
+    beta = sigmoid(bl)[..., None]
+    g = (-np.float32(gscale) * softplus(gl)).astype(f32)
+    wr = _maybe_bf16(l2_normalise(w), in_dtype)
+    return dict(q=_maybe_bf16(l2_normalise(q), in_dtype), k=_maybe_bf16(beta * l2_normalise(k), in_dtype),
+                v=_maybe_bf16(v, in_dtype), g=g, a=_maybe_bf16(beta * wr, in_dtype),
+                b=_maybe_bf16((np.exp(g) * wr).astype(f32), in_dtype), h0=h0, cu_seqlens=cu, in_dtype=in_dtype)
 
 
 def make_output_grads(x: KdaInputs, seed: int, dhT_std: Optional[float] = 0.02):

@@ -53,6 +53,10 @@ def _load():
             i64, ctypes.POINTER(ctypes.c_int64), i64, i64, i64,
             fp, fp, fp, fp, fp, dp, ctypes.c_double, fp, dp,
             dp, dp, dp, dp, dp, dp, ctypes.c_int]
+        lib.kda_oracle_dplr_forward.restype = ctypes.c_int
+        lib.kda_oracle_dplr_forward.argtypes = [
+            i64, ctypes.POINTER(ctypes.c_int64), i64, i64, i64,
+            fp, fp, fp, fp, fp, fp, dp, ctypes.c_double, dp, dp, ctypes.c_int]
         lib.kda_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -140,6 +144,28 @@ def backward(q, k, v, g, beta, d_o, h0=None, d_final_state=None, cu_seqlens=None
     if rc != 0:
         raise RuntimeError(f"kda_oracle_backward failed with code {rc}")
     return out
+
+
+def dplr_forward(q, k, v, g, a, b, h0=None, cu_seqlens=None, scale: float = 1.0, nthreads: int = 0):
+    """fp64 general DPLR recurrence S_t = (Diag(e^g_t) - a_t b_t^T) S_{t-1} + k_t v_t^T,
+    o_t = scale S_t^T q_t (kda_oracle.c).  q, k, g, a, b: [B, T, H, dk]; v: [B, T, H, dv];
+    h0: [N, H, dk, dv] or None.  Returns (o [B, T, H, dv], hT [N, H, dk, dv]) in float64."""
+    lib = _load()
+    q, k, v, g, a, b = map(_f32, (q, k, v, g, a, b))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    cu = np.arange(B + 1, dtype=np.int64) * T if cu_seqlens is None else np.ascontiguousarray(cu_seqlens, np.int64)
+    N = len(cu) - 1
+    o = np.zeros((B, T, H, dv), dtype=np.float64)
+    hT = np.zeros((N, H, dk, dv), dtype=np.float64)
+    h0a = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
+    rc = lib.kda_oracle_dplr_forward(
+        N, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, dk, dv,
+        *(_ptr(x, ctypes.c_float) for x in (q, k, v, g, a, b)), _ptr(h0a, ctypes.c_double), float(scale),
+        _ptr(o, ctypes.c_double), _ptr(hT, ctypes.c_double), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_dplr_forward failed with code {rc}")
+    return o, hT
 
 
 def decode_step(q, k, v, g, beta, state, scale: float = 1.0, nthreads: int = 0, **transforms):

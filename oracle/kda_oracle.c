@@ -160,7 +160,85 @@ int kda_oracle_forward(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk,
     return err;
 }
 
-int kda_oracle_version(void) { return 2; }
+/*
+ * General diagonal-plus-low-rank (DPLR) recurrence, the family KDA belongs to
+ * (Kimi Linear review notes, section "Chunkwise Algorithm": KDA is a DPLR
+ * transition with D = Diag(alpha_t), a_t = beta_t k_t, b_t = k_t .* alpha_t;
+ * the jxzklqfsx.com article's efficiency section compares the two kernels).
+ * The pages' own formula for the general form is lost in extraction; the
+ * plainest reading, which the KDA case must reproduce, is
+ *
+ *     S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1} + k_t v_t^T,
+ *     o_t = scale * S_t^T q_t,        alpha_t = exp(g_t),
+ *
+ * with a_t, b_t free vectors of dk channels.  Per token the oracle forms
+ * x = b_t^T S_{t-1} from the state before the decay, then
+ * S_t = Diag(alpha_t) S_{t-1} - a_t x + k_t v_t^T.  Layout as in
+ * kda_oracle_forward (a, b like k); all heads; fp64.
+ */
+int kda_oracle_dplr_forward(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk,
+                            int64_t dv, const float *q, const float *k, const float *v,
+                            const float *g, const float *a, const float *b, const double *h0,
+                            double scale, double *o, double *hT, int nthreads)
+{
+    if (n_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return 1;
+    for (int64_t n = 0; n < n_seqs; ++n)
+        if (cu[n + 1] < cu[n])
+            return 2;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < n_seqs * H; ++u) {
+        int64_t n = u / H, h = u % H;
+        double *S = (double *)malloc(sizeof(double) * (size_t)(dk * dv));
+        double *x = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (!S || !x) {
+            free(S);
+            free(x);
+#pragma omp atomic write
+            err = 4;
+            continue;
+        }
+        for (int64_t i = 0; i < dk * dv; ++i)
+            S[i] = h0 ? h0[(n * H + h) * dk * dv + i] : 0.0;
+        for (int64_t t = cu[n]; t < cu[n + 1]; ++t) {
+            const int64_t bk = (t * H + h) * dk, bv = (t * H + h) * dv;
+            /* x = b^T S_{t-1} */
+            for (int64_t j = 0; j < dv; ++j)
+                x[j] = 0.0;
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j)
+                    x[j] += (double)b[bk + i] * S[i * dv + j];
+            /* S_t = Diag(alpha) S_{t-1} - a x^T + k v^T */
+            for (int64_t i = 0; i < dk; ++i) {
+                const double al = exp((double)g[bk + i]), ai = (double)a[bk + i], ki = (double)k[bk + i];
+                for (int64_t j = 0; j < dv; ++j)
+                    S[i * dv + j] = al * S[i * dv + j] - ai * x[j] + ki * (double)v[bv + j];
+            }
+            /* o_t = scale S_t^T q_t */
+            double *ot = o + (t * H + h) * dv;
+            for (int64_t j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < dk; ++i)
+                    acc += S[i * dv + j] * (double)q[bk + i];
+                ot[j] = scale * acc;
+            }
+        }
+        if (hT)
+            memcpy(hT + (n * H + h) * dk * dv, S, sizeof(double) * (size_t)(dk * dv));
+        free(S);
+        free(x);
+    }
+    return err;
+}
+
+int kda_oracle_version(void) { return 3; }
 
 int kda_oracle_max_threads(void)
 {
