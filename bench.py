@@ -386,6 +386,43 @@ def cpu_backward_sample(x):
                 sample=f"first {L} tokens of sequence 0, {x.H} heads, {dt:.2f} s wall")
 
 
+def time_dplr(args):
+    """The general DPLR recurrence against KDA on the same token-level harness: 256
+    sequences x 16 heads x 64 new tokens from cached states (bf16, d = 128), us per call."""
+    import torch
+    import gated_delta_rule_52_amd as kda
+    from gated_delta_rule_52_amd.inputs import make_dplr, make_workload
+    bf, f32 = torch.bfloat16, torch.float32
+    t = lambda z, dt: torch.from_numpy(z).to("cuda:0").to(dt)
+    x = make_workload("append_256x16x64")
+    d = make_dplr(8, x.B, x.T, x.H, x.dk, x.dv, h0_std=0.02)
+    kq, kk, kv, kb, kg, kh = t(x.q, bf), t(x.k, bf), t(x.v, bf), t(x.beta, bf), t(x.g, f32), t(x.h0, f32)
+    dq, dk_, dv_, da, db = (t(d[n], bf) for n in ("q", "k", "v", "a", "b"))
+    dg, dh = t(d["g"], f32), t(d["h0"], f32)
+    hT = torch.empty_like(kh)
+    o = torch.empty((x.B, x.T, x.H, x.dv), dtype=bf, device="cuda:0")
+    paths = {
+        "kda_recurrent_fwd": lambda: kda.recurrent_fwd(kq, kk, kv, kg, kb, initial_state=kh, final_state=hT, o=o),
+        "dplr_recurrent_fwd": lambda: kda.dplr_recurrent_fwd(dq, dk_, dv_, dg, da, db, initial_state=dh,
+                                                             final_state=hT, o=o),
+    }
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fn in paths.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = 1e3 * e0.elapsed_time(e1) / 10
+        log(f"dplr comparison {name}: {res[name]:.1f} us per call")
+    return res
+
+
 def copy_ceiling():
     """HBM bandwidth a plain elementwise kernel reaches on this GPU: 1 GiB read
     and 1 GiB written per launch (torch's neg kernel), best of 10 launches."""
@@ -519,6 +556,11 @@ def main():
                          "frac": sach / HBM_PEAK_GBS, "alg_bytes_per_launch": sbytes},
         }
     if not (args.no_decode or args.no_append):
+        rd = time_dplr(args)
+        rec["dplr"] = {
+            "workload": "256 sequences x 16 heads x 64 new tokens, dk=dv=128, bf16, cached states; token by token",
+            "us_per_call": rd, "dplr_over_kda": rd["dplr_recurrent_fwd"] / rd["kda_recurrent_fwd"],
+        }
         rec["append_grid"] = {
             "workload": "N sequences x T new tokens, 16 heads, dk=dv=128, bf16, cached states (key 'NxT')",
             "us_per_call": time_append_grid(),

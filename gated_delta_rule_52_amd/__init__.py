@@ -6,7 +6,7 @@ The Python layer only marshals arguments: torch tensors supply device memory
 and the current HIP stream; every step of the operator runs in libkda.so.
 """
 __all__ = ["chunk_fwd", "recurrent_fwd", "recurrent_step", "recurrent_bwd", "KdaError", "chunk_fwd_workspace_bytes",
-           "recurrent_bwd_workspace_bytes"]
+           "recurrent_bwd_workspace_bytes", "dplr_recurrent_fwd"]
 
 
 def __getattr__(name):

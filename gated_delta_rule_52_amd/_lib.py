@@ -25,7 +25,7 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 # Every function declared in include/kda.h.
 EXPORTS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_fwd", "kda_recurrent_step",
-           "kda_recurrent_bwd_workspace_bytes", "kda_recurrent_bwd",
+           "kda_recurrent_bwd_workspace_bytes", "kda_recurrent_bwd", "kda_dplr_recurrent_fwd",
            "kda_status_string", "kda_last_error", "kda_abi_version")
 
 vp = ctypes.c_void_p
@@ -76,6 +76,19 @@ class RecurrentBwdArgs(ctypes.Structure):
     ]
 
 
+class DplrArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("q", vp), ("k", vp), ("v", vp), ("g", vp), ("a", vp), ("b", vp),
+        ("initial_state", vp), ("final_state", vp), ("o", vp), ("cu_seqlens", vp),
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+        ("stream", vp),
+    ]
+
+
 class KdaError(RuntimeError):
     def __init__(self, status: int, message: str):
         self.status = status
@@ -106,6 +119,8 @@ def load():
         lib.kda_recurrent_bwd_workspace_bytes.argtypes = [ctypes.POINTER(RecurrentBwdArgs)]
         lib.kda_recurrent_bwd.restype = ctypes.c_int
         lib.kda_recurrent_bwd.argtypes = [ctypes.POINTER(RecurrentBwdArgs)]
+        lib.kda_dplr_recurrent_fwd.restype = ctypes.c_int
+        lib.kda_dplr_recurrent_fwd.argtypes = [ctypes.POINTER(DplrArgs)]
         lib.kda_status_string.restype = ctypes.c_char_p
         lib.kda_status_string.argtypes = [ctypes.c_int]
         lib.kda_last_error.restype = ctypes.c_char_p
@@ -149,3 +164,8 @@ def recurrent_bwd_raw(args: RecurrentBwdArgs) -> int:
 def recurrent_bwd_workspace_raw(args: RecurrentBwdArgs) -> int:
     args.struct_size = ctypes.sizeof(RecurrentBwdArgs)
     return load().kda_recurrent_bwd_workspace_bytes(ctypes.byref(args))
+
+
+def dplr_fwd_raw(args: DplrArgs) -> int:
+    args.struct_size = ctypes.sizeof(DplrArgs)
+    return load().kda_dplr_recurrent_fwd(ctypes.byref(args))

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
 SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_chunk.hip", "kda_segments.hip", "kda_prep.hip",
-           "kda_scan.hip", "kda_backward.hip"]
+           "kda_scan.hip", "kda_backward.hip", "kda_dplr.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -392,4 +392,56 @@ kda_status kda_recurrent_bwd(const kda_recurrent_bwd_args *user) {
     return hip_status(kda::launch_backward(L), "kda_recurrent_bwd launch");
 }
 
+kda_status kda_dplr_recurrent_fwd(const kda_dplr_args *user) {
+    g_last_error.clear();
+    if (!user) return fail(KDA_ERR_NULL_POINTER, "args is NULL");
+    if (user->struct_size != sizeof(kda_dplr_args))
+        return fail(KDA_ERR_BAD_STRUCT, "struct_size %u (expected %zu)", user->struct_size, sizeof(kda_dplr_args));
+    const kda_dplr_args *a = user;
+    if (a->B < 0 || a->T < 0 || a->H <= 0 || a->num_seqs < 0)
+        return fail(KDA_ERR_BAD_SHAPE, "B=%d T=%d H=%d num_seqs=%d", a->B, a->T, a->H, a->num_seqs);
+    if (!valid_dim(a->dk) || !valid_dim(a->dv))
+        return fail(KDA_ERR_UNSUPPORTED, "dk=%d dv=%d (supported: 64, 128)", a->dk, a->dv);
+    if (!valid_dtype(a->in_dtype) || !valid_dtype(a->out_dtype))
+        return fail(KDA_ERR_UNSUPPORTED, "in_dtype=%d out_dtype=%d", a->in_dtype, a->out_dtype);
+    if (!std::isfinite(a->scale)) return fail(KDA_ERR_BAD_SHAPE, "scale is not finite");
+    if (a->cu_seqlens ? a->B != 1 : a->num_seqs != a->B)
+        return fail(KDA_ERR_BAD_SHAPE, "num_seqs=%d with B=%d (%s)", a->num_seqs, a->B,
+                    a->cu_seqlens ? "packed input needs B = 1" : "num_seqs must equal B");
+    const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
+    if (tokens > INT32_MAX)
+        return fail(KDA_ERR_BAD_SHAPE, "B*T=%lld tokens (at most %d)", static_cast<long long>(tokens), INT32_MAX);
+    const int N = a->num_seqs;
+    if (N > 65535 || a->H > 65535) return fail(KDA_ERR_UNSUPPORTED, "N=%d H=%d (at most 65535 each)", N, a->H);
+    if (N == 0 || (tokens == 0 && !a->final_state)) return KDA_OK;
+    if (tokens > 0 && (!a->q || !a->k || !a->v || !a->g || !a->a || !a->b || !a->o))
+        return fail(KDA_ERR_NULL_POINTER, "q, k, v, g, a, b and o are required");
+    const size_t th = static_cast<size_t>(tokens) * a->H, in_sz = dsize(a->in_dtype);
+    const size_t sbytes = static_cast<size_t>(N) * a->H * a->dk * a->dv * 4;
+    const Range ro = range_of(a->o, th * a->dv * dsize(a->out_dtype));
+    const Range ins[] = {range_of(a->q, th * a->dk * in_sz), range_of(a->k, th * a->dk * in_sz),
+                         range_of(a->v, th * a->dv * in_sz), range_of(a->g, th * a->dk * 4),
+                         range_of(a->a, th * a->dk * in_sz), range_of(a->b, th * a->dk * in_sz)};
+    for (const Range &r : ins)
+        if (overlap(ro, r)) return fail(KDA_ERR_ALIAS, "o overlaps an input");
+    if (a->final_state) {
+        const Range rf = range_of(a->final_state, sbytes);
+        for (const Range &r : ins)
+            if (overlap(rf, r)) return fail(KDA_ERR_ALIAS, "final_state overlaps an input");
+        if (overlap(rf, ro)) return fail(KDA_ERR_ALIAS, "final_state overlaps o");
+        if (a->initial_state && a->initial_state != a->final_state &&
+            overlap(rf, range_of(a->initial_state, sbytes)))
+            return fail(KDA_ERR_ALIAS, "final_state partially overlaps initial_state");
+    }
+    kda::DplrLaunch L{};
+    L.q = a->q; L.k = a->k; L.v = a->v; L.a = a->a; L.b = a->b; L.g = a->g;
+    L.h0 = a->initial_state; L.hT = a->final_state; L.o = a->o;
+    L.cu_seqlens = a->cu_seqlens;
+    L.N = N; L.T = a->T; L.H = a->H; L.dk = a->dk; L.dv = a->dv; L.scale = a->scale;
+    L.in_bf16 = a->in_dtype == KDA_DTYPE_BF16;
+    L.out_bf16 = a->out_dtype == KDA_DTYPE_BF16;
+    L.stream = static_cast<hipStream_t>(a->stream);
+    return hip_status(kda::launch_dplr(L), "kda_dplr_recurrent_fwd launch");
+}
+
 }  // extern "C"

@@ -46,6 +46,22 @@ struct RecurrentLaunch {
 
 hipError_t launch_recurrent(const RecurrentLaunch &L);
 
+// The general DPLR recurrence, token by token (kda_dplr.hip).
+struct DplrLaunch {
+    const void *q, *k, *v, *a, *b;
+    const float *g;
+    const float *h0;
+    float *hT;
+    void *o;
+    const int32_t *cu_seqlens;  // device, or nullptr: N sequences of T tokens
+    int N, T, H, dk, dv;
+    float scale;
+    bool in_bf16, out_bf16;
+    hipStream_t stream;
+};
+
+hipError_t launch_dplr(const DplrLaunch &L);
+
 // Gradients of the recurrence, token by token (kda_backward.hip).
 struct BackwardLaunch {
     const void *q, *k, *v;

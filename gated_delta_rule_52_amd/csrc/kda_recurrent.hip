@@ -175,8 +175,9 @@ recurrent_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
 // * the token's k, q and alpha (and the L2 norms) are formed once, two
 //   channels per lane, and handed to the lanes that need them through the
 //   wave's own LDS (a wave's LDS accesses are ordered, so no barrier);
-// * S~^T k and S~^T q for column c are R-term partial sums reduced over the
-//   four lanes of a quad by two DPP moves;
+// * per token two passes over the lane's rows: the decay with S~^T k, then
+//   the write with S_t^T q; each R-term partial sum is reduced over the four
+//   lanes of a quad by two DPP moves;
 // * the inputs of the next four tokens are in flight while one is processed.
 template <int DK, bool InBf16, bool OutBf16>
 __global__ void __launch_bounds__(64)
@@ -192,9 +193,10 @@ recurrent_seq_kernel(const void *__restrict__ q_, const void *__restrict__ k_, c
     const typename In::T *beta = static_cast<const typename In::T *>(beta_);
     typename Out::T *o = static_cast<typename Out::T *>(o_);
     constexpr int R = DK / 4;         // rows per lane
+    constexpr int RP = R + 4;         // padded LDS stride of a row group: a quad's four groups in distinct banks
     constexpr int CPL = DK / kWave;   // channels each lane loads per token
     static_assert(R % 4 == 0 && CPL >= 1, "tiling");
-    __shared__ __attribute__((aligned(16))) float s_in[2][3][DK];  // [buffer][k, q, alpha][channel]
+    __shared__ __attribute__((aligned(16))) float s_in[2][3][4 * RP];  // [buffer][k, q, alpha][row]
 
     const int slice = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
     const int lane = threadIdx.x, c = lane >> 2, rg = lane & 3;
@@ -247,41 +249,39 @@ recurrent_seq_kernel(const void *__restrict__ q_, const void *__restrict__ k_, c
         const int b = static_cast<int>(t - t0) & 1;  // alternate buffers: no write lands on a row still being read
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
-            const int ch = lane * CPL + e;
-            s_in[b][0][ch] = f.k[e];
-            s_in[b][1][ch] = f.q[e];
-            s_in[b][2][ch] = __expf(xf.log_gate(f.g[e]));
+            const int ch = lane * CPL + e, li = (ch / R) * RP + ch % R;
+            s_in[b][0][li] = f.k[e];
+            s_in[b][1][li] = f.q[e];
+            s_in[b][2][li] = __expf(xf.log_gate(f.g[e]));
         }
-        float kr[R], qr[R], ar[R];
+        // two passes over the rows: decay and S~^T k, then the write and the read S_t^T q
+        const float *kx = &s_in[b][0][rg * RP], *qx = &s_in[b][1][rg * RP], *ax = &s_in[b][2][rg * RP];
+        float p0 = 0.f, p1 = 0.f;
 #pragma unroll
         for (int i = 0; i < R; i += 4) {
-            const float4 k4 = *reinterpret_cast<const float4 *>(&s_in[b][0][rg * R + i]);
-            const float4 q4 = *reinterpret_cast<const float4 *>(&s_in[b][1][rg * R + i]);
-            const float4 a4 = *reinterpret_cast<const float4 *>(&s_in[b][2][rg * R + i]);
-            kr[i] = k4.x; kr[i + 1] = k4.y; kr[i + 2] = k4.z; kr[i + 3] = k4.w;
-            qr[i] = q4.x; qr[i + 1] = q4.y; qr[i + 2] = q4.z; qr[i + 3] = q4.w;
-            ar[i] = a4.x; ar[i + 1] = a4.y; ar[i + 2] = a4.z; ar[i + 3] = a4.w;
-        }
-        float p0 = 0.f, p1 = 0.f, r0 = 0.f, r1 = 0.f, kq0 = 0.f, kq1 = 0.f;  // two chains each
-#pragma unroll
-        for (int i = 0; i < R; i += 2) {
-            s[i] *= ar[i];
-            s[i + 1] *= ar[i + 1];
-            p0 += s[i] * kr[i];
-            p1 += s[i + 1] * kr[i + 1];
-            r0 += s[i] * qr[i];
-            r1 += s[i + 1] * qr[i + 1];
-            kq0 += kr[i] * qr[i];
-            kq1 += kr[i + 1] * qr[i + 1];
+            const float4 k4 = *reinterpret_cast<const float4 *>(kx + i);
+            const float4 a4 = *reinterpret_cast<const float4 *>(ax + i);
+            s[i] *= a4.x; s[i + 1] *= a4.y; s[i + 2] *= a4.z; s[i + 3] *= a4.w;
+            p0 += s[i] * k4.x;
+            p1 += s[i + 1] * k4.y;
+            p0 += s[i + 2] * k4.z;
+            p1 += s[i + 3] * k4.w;
         }
         const float p = quad_sum(p0 + p1) * ik;  // S~^T k, k normalised
-        const float r = quad_sum(r0 + r1) * iq;
-        const float kq = quad_sum(kq0 + kq1) * ik * iq;
-        const float d = f.v - p;
-        if (rg == 0) Out::store(o, (t * H + h) * static_cast<int64_t>(DV) + col, scale * (r + f.b * kq * d));
-        const float bkd = f.b * ik * d;
+        const float bkd = f.b * ik * (f.v - p);  // the write's beta k (v - p), k normalised
+        float r0 = 0.f, r1 = 0.f;
 #pragma unroll
-        for (int i = 0; i < R; ++i) s[i] += bkd * kr[i];
+        for (int i = 0; i < R; i += 4) {
+            const float4 k4 = *reinterpret_cast<const float4 *>(kx + i);
+            const float4 q4 = *reinterpret_cast<const float4 *>(qx + i);
+            s[i] += bkd * k4.x; s[i + 1] += bkd * k4.y; s[i + 2] += bkd * k4.z; s[i + 3] += bkd * k4.w;
+            r0 += s[i] * q4.x;
+            r1 += s[i + 1] * q4.y;
+            r0 += s[i + 2] * q4.z;
+            r1 += s[i + 3] * q4.w;
+        }
+        const float r = quad_sum(r0 + r1) * iq;  // S_t^T q, q normalised
+        if (rg == 0) Out::store(o, (t * H + h) * static_cast<int64_t>(DV) + col, scale * r);
     };
 
     if (t0 < t1) {

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 /*
  * Optional input transforms, applied inside the kernels to every token before
@@ -276,6 +276,50 @@ typedef struct {
 size_t kda_recurrent_bwd_workspace_bytes(const kda_recurrent_bwd_args *args);
 
 kda_status kda_recurrent_bwd(const kda_recurrent_bwd_args *args);
+
+/*
+ * The general diagonal-plus-low-rank (DPLR) recurrence, token by token.  The
+ * Kimi Linear review notes (section "Chunkwise Algorithm") give KDA's
+ * transition as a DPLR matrix with D = Diag(alpha_t), a_t = beta_t k_t and
+ * b_t = k_t .* alpha_t; this entry point runs the family's general member,
+ * with a_t and b_t free, per sequence and head:
+ *
+ *     S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1} + k_t v_t^T,
+ *     o_t = scale * S_t^T q_t,          alpha_t = exp(g_t).
+ *
+ * KDA is the case a = beta k, b = alpha .* k with write key beta k.  Computed
+ * in fp32 by one wave per (sequence, head, 16 columns of dv), which reads its
+ * state slice once and writes it once; meant, like kda_recurrent_fwd, for
+ * short segments.
+ *
+ * Shapes (N = number of sequences):
+ *   q, k, a, b : [B, T, H, dk] in_dtype;  v : [B, T, H, dv] in_dtype
+ *   g    : [B, T, H, dk] fp32 log-decay (alpha = exp(g) <= 1)
+ *   initial_state, final_state, o, cu_seqlens, B, T, H, dk, dv, num_seqs,
+ *   scale, out_dtype: as in kda_chunk_fwd (final_state may equal
+ *   initial_state; o must not overlap any input).
+ * No workspace.  No input transform.
+ */
+typedef struct {
+    uint32_t struct_size; /* = sizeof(kda_dplr_args) */
+    const void *q;
+    const void *k;
+    const void *v;
+    const float *g;
+    const void *a;
+    const void *b;
+    const float *initial_state;
+    float *final_state;
+    void *o;
+    const int32_t *cu_seqlens;
+    int32_t B, T, H, dk, dv, num_seqs;
+    float scale;
+    kda_dtype in_dtype;  /* dtype of q, k, v, a, b */
+    kda_dtype out_dtype; /* dtype of o */
+    void *stream;        /* hipStream_t */
+} kda_dplr_args;
+
+kda_status kda_dplr_recurrent_fwd(const kda_dplr_args *args);
 
 /* Static text for a status code. */
 const char *kda_status_string(kda_status s);

@@ -26,7 +26,7 @@ def test_every_declared_function_is_exported():
     assert decl == sorted(_lib.EXPORTS)
     for name in decl:
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == 3
+    assert lib.kda_abi_version() == 4
 
 
 def test_status_strings():
@@ -226,3 +226,39 @@ def test_backward_struct_and_empty_calls():
     # nothing to do: no sequence, or no token and no initial-state gradient (no launch)
     assert _lib.recurrent_bwd_raw(bwd_args(B=0, num_seqs=0)) == 0
     assert _lib.recurrent_bwd_raw(bwd_args(T=0, grad_initial_state=None, q=None, grad_q=None)) == 0
+
+
+def dplr_args(**kw):
+    a = _lib.DplrArgs()
+    base = dict(q=FAKE, k=2 * FAKE, v=3 * FAKE, g=4 * FAKE, a=5 * FAKE, b=6 * FAKE, initial_state=7 * FAKE,
+                final_state=7 * FAKE, o=8 * FAKE, cu_seqlens=None, B=2, T=64, H=2, dk=128, dv=128, num_seqs=2,
+                scale=1.0, in_dtype=_lib.KDA_DTYPE_BF16, out_dtype=_lib.KDA_DTYPE_FP32)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=32), "KDA_ERR_UNSUPPORTED"),
+    (dict(out_dtype=9), "KDA_ERR_UNSUPPORTED"),
+    (dict(H=0), "KDA_ERR_BAD_SHAPE"),
+    (dict(num_seqs=3), "KDA_ERR_BAD_SHAPE"),
+    (dict(scale=float("nan")), "KDA_ERR_BAD_SHAPE"),
+    (dict(b=None), "KDA_ERR_NULL_POINTER"),
+    (dict(o=5 * FAKE + 16), "KDA_ERR_ALIAS"),            # inside a
+    (dict(final_state=6 * FAKE + 16, initial_state=None), "KDA_ERR_ALIAS"),  # inside b
+    (dict(initial_state=7 * FAKE + 64), "KDA_ERR_ALIAS"),  # partial overlap with final_state
+])
+def test_dplr_rejects(kw, status):
+    rc = _lib.dplr_fwd_raw(dplr_args(**kw))
+    assert rc == S[status], (_lib.STATUS.get(rc), _lib.load().kda_last_error())
+    assert _lib.load().kda_last_error().decode() != ""
+
+
+def test_dplr_struct_size_and_empty_call():
+    lib = _lib.load()
+    a = dplr_args()
+    a.struct_size = ctypes.sizeof(_lib.DplrArgs) + 8
+    assert lib.kda_dplr_recurrent_fwd(ctypes.byref(a)) == S["KDA_ERR_BAD_STRUCT"]
+    assert _lib.dplr_fwd_raw(dplr_args(B=0, num_seqs=0)) == 0
