@@ -1,6 +1,6 @@
-"""Both entry points under HIP graph capture.
+"""Entry points under HIP graph capture.
 
-kda_chunk_fwd and kda_recurrent_step only launch kernels on the caller's
+kda_chunk_fwd, kda_recurrent_step, kda_recurrent_bwd and kda_dplr_recurrent_fwd only launch kernels on the caller's
 stream (no allocation, synchronisation or memset), so a captured sequence of
 calls replays to the same bits as the same calls made eagerly.  Each test
 replays several times, with eager work and synchronisations in between, and
@@ -86,3 +86,69 @@ def test_prefill_replayed_from_a_graph(kda):
         torch.cuda.synchronize()
         say(f"  replay {rep}: o equal {torch.equal(o, o_e)}, state equal {torch.equal(hT, h_e)}")
         assert torch.equal(o, o_e) and torch.equal(hT, h_e)
+
+
+def test_gradients_replayed_from_a_graph(kda):
+    """kda_recurrent_bwd (segment table, local passes, both combines, the
+    gradient kernel) captured with its outputs and workspace allocated
+    beforehand, replayed three times against eager calls."""
+    import torch
+    from gated_delta_rule_52_amd.inputs import make_output_grads
+    x = make_prefill(73, 1, 700, 2, 128, 128, h0_std=0.3)  # several segments per sequence
+    do, dhT = make_output_grads(x, 74, dhT_std=0.3)
+    say(f"case gradients graph: T={x.T} H={x.H}")
+    d = upload(x)
+    dod, dht = dev(do, torch.bfloat16), dev(dhT, torch.float32)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], dod)
+    ws = torch.empty(kda.recurrent_bwd_workspace_bytes(d["q"], d["v"]), dtype=torch.uint8, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    out = {n: torch.empty(sh, **f32) for n, sh in (("dq", d["q"].shape), ("dk", d["q"].shape), ("dv", d["v"].shape),
+                                                    ("dg", d["q"].shape), ("dbeta", d["beta"].shape))}
+    dh0 = torch.empty_like(dht)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        kda.recurrent_bwd(*args, initial_state=d["h0"], grad_final_state=dht, grad_initial_state=dh0,
+                          workspace=ws, out=out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        ref = kda.recurrent_bwd(*args, initial_state=d["h0"], grad_final_state=dht)
+        torch.cuda.synchronize()
+        for t in out.values():
+            t.fill_(float("nan"))
+        dh0.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        _ = (dht * 2).sum().item()
+        same = all(torch.equal(out[n], ref[n]) for n in out) and torch.equal(dh0, ref["dh0"])
+        say(f"  replay {rep}: gradients equal {same}")
+        assert same
+
+
+def test_dplr_replayed_from_a_graph(kda):
+    import torch
+    from gated_delta_rule_52_amd.inputs import make_dplr
+    dd = make_dplr(75, 2, 40, 2, 128, 128, h0_std=0.3)
+    say("case dplr graph: B=2 T=40 H=2")
+    t = {n: dev(dd[n], torch.bfloat16) for n in ("q", "k", "v", "a", "b")}
+    g, h0 = dev(dd["g"], torch.float32), dev(dd["h0"], torch.float32)
+    o = torch.empty((2, 40, 2, 128), dtype=torch.float32, device="cuda")
+    hT = torch.empty_like(h0)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        kda.dplr_recurrent_fwd(t["q"], t["k"], t["v"], g, t["a"], t["b"], initial_state=h0, final_state=hT, o=o,
+                               out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        o_ref, h_ref = kda.dplr_recurrent_fwd(t["q"], t["k"], t["v"], g, t["a"], t["b"], initial_state=h0,
+                                              out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        same = torch.equal(o, o_ref) and torch.equal(hT, h_ref)
+        say(f"  replay {rep}: equal {same}")
+        assert same
