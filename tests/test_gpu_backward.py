@@ -190,3 +190,14 @@ def test_full_size_workload_sampled(kda):
     x = make_workload("backward_16x4096x16")
     do, dhT = make_output_grads(x, 106)
     check(kda, x, do, dhT, pairs=[(0, 0), (7, 5), (15, 15)])
+
+
+def test_thousands_of_short_sequences(kda):
+    """3,000 packed sequences of 0 to 9 tokens, 2 heads: every block length,
+    empty sequences among them; checked on a spread of sequences."""
+    rng = np.random.default_rng(148)
+    lens = rng.integers(0, 10, size=3000)
+    x = make_prefill(148, 1, 0, 2, 64, 64, in_dtype="fp32", h0_std=0.3, seqlens=lens, name="bwd_3000")
+    do, dhT = make_output_grads(x, 248, dhT_std=0.3)
+    pairs = [(n, h) for n in list(range(0, 3000, 97)) + [2999] for h in range(2)]
+    check(kda, x, do, dhT, pairs=pairs)
