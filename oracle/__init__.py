@@ -52,7 +52,7 @@ def _load():
         lib.kda_oracle_backward.argtypes = [
             i64, ctypes.POINTER(ctypes.c_int64), i64, i64, i64,
             fp, fp, fp, fp, fp, dp, ctypes.c_double, fp, dp,
-            dp, dp, dp, dp, dp, dp, ctypes.c_int]
+            dp, dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int]
         lib.kda_oracle_dplr_forward.restype = ctypes.c_int
         lib.kda_oracle_dplr_forward.argtypes = [
             i64, ctypes.POINTER(ctypes.c_int64), i64, i64, i64,
@@ -120,11 +120,12 @@ def forward(q, k, v, g, beta, h0=None, cu_seqlens=None, scale: float = 1.0,
 
 
 def backward(q, k, v, g, beta, d_o, h0=None, d_final_state=None, cu_seqlens=None,
-             scale: float = 1.0, nthreads: int = 0):
+             scale: float = 1.0, nthreads: int = 0, scalar_gate: bool = False):
     """Gradients of the fp64 recurrence (no input transforms) for output
     gradient d_o [B, T, H, dv] and optional final-state gradient
     [N, H, dk, dv].  Returns a dict of float64 arrays: dq, dk, dg [B, T, H, dk],
-    dv [B, T, H, dv], dbeta [B, T, H], dh0 [N, H, dk, dv]."""
+    dv [B, T, H, dv], dbeta [B, T, H], dh0 [N, H, dk, dv].  With scalar_gate,
+    g and dg are [B, T, H] (Gated DeltaNet's gate)."""
     lib = _load()
     q, k, v, g, beta, d_o = map(_f32, (q, k, v, g, beta, d_o))
     B, T, H, dk = q.shape
@@ -132,7 +133,8 @@ def backward(q, k, v, g, beta, d_o, h0=None, d_final_state=None, cu_seqlens=None
     cu = np.arange(B + 1, dtype=np.int64) * T if cu_seqlens is None else np.ascontiguousarray(cu_seqlens, np.int64)
     N = len(cu) - 1
     out = dict(dq=np.zeros((B, T, H, dk)), dk=np.zeros((B, T, H, dk)), dv=np.zeros((B, T, H, dv)),
-               dg=np.zeros((B, T, H, dk)), dbeta=np.zeros((B, T, H)), dh0=np.zeros((N, H, dk, dv)))
+               dg=np.zeros((B, T, H) if scalar_gate else (B, T, H, dk)), dbeta=np.zeros((B, T, H)),
+               dh0=np.zeros((N, H, dk, dv)))
     h0a = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
     dhT = None if d_final_state is None else np.ascontiguousarray(d_final_state, dtype=np.float64)
     rc = lib.kda_oracle_backward(
@@ -140,7 +142,8 @@ def backward(q, k, v, g, beta, d_o, h0=None, d_final_state=None, cu_seqlens=None
         _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
         _ptr(g, ctypes.c_float), _ptr(beta, ctypes.c_float), _ptr(h0a, ctypes.c_double),
         float(scale), _ptr(d_o, ctypes.c_float), _ptr(dhT, ctypes.c_double),
-        *(_ptr(out[n], ctypes.c_double) for n in ("dq", "dk", "dv", "dg", "dbeta", "dh0")), int(nthreads))
+        *(_ptr(out[n], ctypes.c_double) for n in ("dq", "dk", "dv", "dg", "dbeta", "dh0")), int(nthreads),
+        int(bool(scalar_gate)))
     if rc != 0:
         raise RuntimeError(f"kda_oracle_backward failed with code {rc}")
     return out

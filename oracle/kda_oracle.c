@@ -269,13 +269,17 @@ int kda_oracle_max_threads(void)
  * (T_n + 1) dk dv doubles per pair in flight.  Outputs are double arrays with
  * the inputs' layouts: dq, dk, dg [T_total, H, dk], dv [T_total, H, dv],
  * dbeta [T_total, H], dh0 [N, H, dk, dv].  All heads are computed.
+ *
+ * With scalar_gate, g is [T_total, H] (one gate per token and head for every
+ * key channel, Gated DeltaNet's gate) and so is dg: the gate's gradient is the
+ * sum over channels of the per-channel dg above.
  */
 int kda_oracle_backward(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk,
                         int64_t dv, const float *q, const float *k, const float *v,
                         const float *g, const float *beta, const double *h0,
                         double scale, const float *d_o, const double *dhT,
                         double *dq, double *dkk, double *dvv, double *dg,
-                        double *dbeta, double *dh0, int nthreads)
+                        double *dbeta, double *dh0, int nthreads, int scalar_gate)
 {
     if (n_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0)
         return 1;
@@ -316,7 +320,7 @@ int kda_oracle_backward(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk
             for (int64_t j = 0; j < dv; ++j)
                 u[j] = (double)v[bv + j];
             for (int64_t i = 0; i < dk; ++i) {
-                const double a = exp((double)g[bk + i]);
+                const double a = exp((double)g[scalar_gate ? (T0 + t) * H + h : bk + i]);
                 for (int64_t j = 0; j < dv; ++j) {
                     Sn[i * dv + j] = a * Sp[i * dv + j];
                     u[j] -= Sn[i * dv + j] * (double)k[bk + i];
@@ -336,7 +340,7 @@ int kda_oracle_backward(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk
             for (int64_t i = 0; i < dk; ++i) {
                 kt[i] = (double)k[bk + i];
                 qt[i] = (double)q[bk + i];
-                al[i] = exp((double)g[bk + i]);
+                al[i] = exp((double)g[scalar_gate ? tt * H + h : bk + i]);
             }
             for (int64_t j = 0; j < dv; ++j) {
                 vt[j] = (double)v[bv + j];
@@ -387,14 +391,20 @@ int kda_oracle_backward(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk
                 dkk[bk + i] = tmp[i] + acc;
             }
             /* S~ = Diag(alpha) S_{t-1} */
+            double dgs = 0.0;
             for (int64_t i = 0; i < dk; ++i) {
                 double acc = 0.0;
                 for (int64_t j = 0; j < dv; ++j) {
                     acc += St[i * dv + j] * dSt[i * dv + j];
                     dS[i * dv + j] = al[i] * dSt[i * dv + j];
                 }
-                dg[bk + i] = acc;
+                if (scalar_gate)
+                    dgs += acc;
+                else
+                    dg[bk + i] = acc;
             }
+            if (scalar_gate)
+                dg[tt * H + h] = dgs;
         }
         memcpy(dh0 + (n * H + h) * sz, dS, sizeof(double) * (size_t)sz);
         free(S);

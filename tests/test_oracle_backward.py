@@ -36,23 +36,23 @@ def tiny(seed, T=4, H=1, dk=3, dv=2, N=1):
     return x, h0, W, Wh
 
 
-def loss(x, h0, W, Wh, scale):
-    o, hT = oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], h0=h0, scale=scale)
+def loss(x, h0, W, Wh, scale, scalar_gate=False):
+    o, hT = oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], h0=h0, scale=scale, scalar_gate=scalar_gate)
     return float(np.sum(o * W) + np.sum(hT * Wh))
 
 
-def fd_gradient(x, h0, W, Wh, scale, name, idx):
+def fd_gradient(x, h0, W, Wh, scale, name, idx, scalar_gate=False):
     def shifted(eps):
         if name == "h0":
             hp, hm = h0.copy(), h0.copy()
             hp[idx] += eps
             hm[idx] -= eps
-            return (loss(x, hp, W, Wh, scale) - loss(x, hm, W, Wh, scale)) / (2 * eps)
+            return (loss(x, hp, W, Wh, scale, scalar_gate) - loss(x, hm, W, Wh, scale, scalar_gate)) / (2 * eps)
         xp = {k: a.copy() for k, a in x.items()}
         xm = {k: a.copy() for k, a in x.items()}
         xp[name][idx] += np.float32(eps)
         xm[name][idx] -= np.float32(eps)
-        return (loss(xp, h0, W, Wh, scale) - loss(xm, h0, W, Wh, scale)) / (2 * eps)
+        return (loss(xp, h0, W, Wh, scale, scalar_gate) - loss(xm, h0, W, Wh, scale, scalar_gate)) / (2 * eps)
     d1, d2 = shifted(2.0 ** -7), shifted(2.0 ** -8)
     return (4 * d2 - d1) / 3
 
@@ -69,6 +69,26 @@ def test_backward_matches_finite_differences(scale):
         for idx in np.ndindex(arr.shape):
             fd[idx] = fd_gradient(x, h0, W32, Wh, scale, name, idx)
         an = r[key[name]]
+        err = np.linalg.norm(an - fd) / max(np.linalg.norm(fd), 1e-30)
+        assert err < 1e-8, (name, err)
+
+
+def test_backward_scalar_gate_matches_finite_differences():
+    """One gate per token and head (Gated DeltaNet): every element of every
+    input against Richardson-extrapolated central differences."""
+    x, h0, W, Wh = tiny(133)
+    rng = np.random.default_rng(134)
+    x["g"] = grid(rng, x["beta"].shape, -0.7, -0.05)  # [N, T, H]
+    r = oracle.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], W.astype(np.float32), h0=h0,
+                        d_final_state=Wh, scale=0.9, scalar_gate=True)
+    W32 = W.astype(np.float32).astype(np.float64)
+    key = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "beta": "dbeta", "h0": "dh0"}
+    for name, arr in list(x.items()) + [("h0", h0)]:
+        fd = np.zeros(arr.shape)
+        for idx in np.ndindex(arr.shape):
+            fd[idx] = fd_gradient(x, h0, W32, Wh, 0.9, name, idx, scalar_gate=True)
+        an = r[key[name]]
+        assert an.shape == fd.shape, (name, an.shape, fd.shape)
         err = np.linalg.norm(an - fd) / max(np.linalg.norm(fd), 1e-30)
         assert err < 1e-8, (name, err)
 
