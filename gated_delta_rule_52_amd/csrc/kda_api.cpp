@@ -166,6 +166,8 @@ kda_status read_bwd_args(const kda_recurrent_bwd_args *a, kda_recurrent_bwd_args
         return fail(KDA_ERR_BAD_STRUCT, "struct_size %u (expected %zu)", a->struct_size,
                     sizeof(kda_recurrent_bwd_args));
     out = *a;
+    if (out.flags & ~KDA_FLAG_SCALAR_GATE)
+        return fail(KDA_ERR_UNSUPPORTED, "flags 0x%x: only KDA_FLAG_SCALAR_GATE has gradients here", out.flags);
     return check_bwd_sizes(&out);
 }
 
@@ -344,16 +346,17 @@ kda_status kda_recurrent_bwd(const kda_recurrent_bwd_args *user) {
                        !a->grad_v || !a->grad_g || !a->grad_beta))
         return fail(KDA_ERR_NULL_POINTER, "q, k, v, g, beta, grad_o and every token gradient are required");
     const size_t th = static_cast<size_t>(tokens) * a->H, in_sz = dsize(a->in_dtype);
+    const size_t gw = (a->flags & KDA_FLAG_SCALAR_GATE) ? 1 : static_cast<size_t>(a->dk);
     const size_t sbytes = static_cast<size_t>(N) * a->H * a->dk * a->dv * 4;
     const size_t need = kda::backward_workspace_bytes(a->B, a->T, a->H, a->dk, a->dv, N, a->cu_seqlens != nullptr);
     if (a->workspace_bytes < need || (need > 0 && !a->workspace))
         return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", a->workspace_bytes, need);
     const Range ins[] = {range_of(a->q, th * a->dk * in_sz), range_of(a->k, th * a->dk * in_sz),
-                         range_of(a->v, th * a->dv * in_sz), range_of(a->g, th * a->dk * 4),
+                         range_of(a->v, th * a->dv * in_sz), range_of(a->g, th * gw * 4),
                          range_of(a->beta, th * in_sz), range_of(a->grad_o, th * a->dv * in_sz),
                          range_of(a->cu_seqlens, a->cu_seqlens ? (static_cast<size_t>(N) + 1) * 4 : 0)};
     const Range outs[] = {range_of(a->grad_q, th * a->dk * 4), range_of(a->grad_k, th * a->dk * 4),
-                          range_of(a->grad_v, th * a->dv * 4), range_of(a->grad_g, th * a->dk * 4),
+                          range_of(a->grad_v, th * a->dv * 4), range_of(a->grad_g, th * gw * 4),
                           range_of(a->grad_beta, th * 4), range_of(a->workspace, need)};
     const Range rh0 = range_of(a->initial_state, a->initial_state ? sbytes : 0);
     const Range rdhT = range_of(a->grad_final_state, a->grad_final_state ? sbytes : 0);
@@ -387,6 +390,7 @@ kda_status kda_recurrent_bwd(const kda_recurrent_bwd_args *user) {
     L.B = a->B; L.N = N; L.T = a->T; L.H = a->H; L.dk_dim = a->dk; L.dv_dim = a->dv;
     L.scale = a->scale;
     L.in_bf16 = a->in_dtype == KDA_DTYPE_BF16;
+    L.scalar_gate = (a->flags & KDA_FLAG_SCALAR_GATE) != 0;
     L.workspace = a->workspace;
     L.stream = static_cast<hipStream_t>(a->stream);
     return hip_status(kda::launch_backward(L), "kda_recurrent_bwd launch");

@@ -180,7 +180,7 @@ recurrent_bwd_kernel(BackwardLaunch L, SegmentView sv, const float *dleave) {
             const int x = e / DK, i = e % DK, li = (i / R) * RP + i % R;
             const int64_t idx = ((tb + x) * H + h) * DK + i;
             s_k[x][li] = In::load(k, idx);
-            s_a[x][li] = __expf(g[idx]);
+            s_a[x][li] = __expf(g[L.scalar_gate ? (tb + x) * H + h : idx]);
             if (backward) s_q[x][li] = In::load(q, idx);
         }
         for (int e = tid; e < m * DV; e += NT) {
@@ -344,6 +344,10 @@ recurrent_bwd_kernel(BackwardLaunch L, SegmentView sv, const float *dleave) {
                 const float bud = s_b[x] * ud;
                 acc.x += bud * k4.x; acc.y += bud * k4.y; acc.z += bud * k4.z; acc.w += bud * k4.w;
             }
+            if (qty == 2 && L.scalar_gate) {  // kept for the sum over rows below (this thread's own slot)
+                *reinterpret_cast<float4 *>(&s_part[x][0][2][i]) = acc;
+                continue;
+            }
             float *dst = qty == 0 ? L.dq : (qty == 1 ? L.dk : L.dg);
             *reinterpret_cast<float4 *>(dst + ((tb + x) * H + h) * DK + i) = acc;
         }
@@ -352,6 +356,14 @@ recurrent_bwd_kernel(BackwardLaunch L, SegmentView sv, const float *dleave) {
 #pragma unroll
             for (int sl = 0; sl < NS; ++sl) acc += s_ps[tid][sl][0];
             L.dbeta[(tb + tid) * H + h] = acc;
+        }
+        if (L.scalar_gate) {  // one gate per token and head: its gradient is the sum over the dk rows
+            __syncthreads();
+            if (tid < m) {
+                float acc = 0.f;
+                for (int i = 0; i < DK; ++i) acc += s_part[tid][0][2][i];
+                L.dg[(tb + tid) * H + h] = acc;
+            }
         }
     };
 
@@ -369,7 +381,7 @@ recurrent_bwd_kernel(BackwardLaunch L, SegmentView sv, const float *dleave) {
             const int e = tid + j * NT;
             const int64_t idx = ((tb + e / DK) * H + h) * DK + e % DK;
             ahead.k[j] = In::load(k, idx);
-            ahead.g[j] = g[idx];
+            ahead.g[j] = g[L.scalar_gate ? (tb + e / DK) * H + h : idx];
         }
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
@@ -479,7 +491,7 @@ segment_local_kernel(BackwardLaunch L, SegmentView sv) {
             const int x = e / DK, i = e % DK, li = (i / R) * RP + i % R;
             const int64_t idx = ((tb + x) * H + h) * DK + i;
             s_k[x][li] = In::load(k, idx);
-            s_a[x][li] = __expf(L.g[idx]);
+            s_a[x][li] = __expf(L.g[L.scalar_gate ? (tb + x) * H + h : idx]);
         }
         for (int e = tid; e < m * DV; e += NT) {
             const int x = e / DV, j = e % DV;
@@ -533,7 +545,7 @@ reverse_local_kernel(BackwardLaunch L, SegmentView sv, float *hb) {
             const int64_t idx = ((tb + x) * H + h) * DK + i;
             s_k[x][li] = In::load(k, idx);
             s_q[x][li] = In::load(q, idx);
-            s_a[x][li] = __expf(L.g[idx]);
+            s_a[x][li] = __expf(L.g[L.scalar_gate ? (tb + x) * H + h : idx]);
         }
         for (int e = tid; e < m * DV; e += NT) {
             const int x = e / DV, j = e % DV;

@@ -74,6 +74,7 @@ struct BackwardLaunch {
     int B, N, T, H, dk_dim, dv_dim;
     float scale;
     bool in_bf16;
+    bool scalar_gate;           // g and dg are [tokens, H]: one gate per token and head
     void *workspace;            // backward_workspace_bytes()
     float *ckpt;                // stored forward states (set by launch_backward inside the workspace)
     hipStream_t stream;

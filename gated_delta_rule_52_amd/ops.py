@@ -217,9 +217,10 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
     return o
 
 
-def _bwd_args(q, v, cu_seqlens, scale):
+def _bwd_args(q, v, cu_seqlens, scale, scalar_gate=False):
     B, T, H, dk = q.shape
     a = _lib.RecurrentBwdArgs()
+    a.flags = _lib.KDA_FLAG_SCALAR_GATE if scalar_gate else 0
     a.B, a.T, a.H, a.dk, a.dv = B, T, H, dk, v.shape[-1]
     a.num_seqs = B if cu_seqlens is None else cu_seqlens.numel() - 1
     a.cu_seqlens = _ptr(cu_seqlens)
@@ -240,7 +241,8 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   grad_final_state: Optional[torch.Tensor] = None,
                   cu_seqlens: Optional[torch.Tensor] = None, scale: float = 1.0,
                   output_grad_initial_state: bool = True, grad_initial_state: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None):
+                  workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None,
+                  scalar_gate: bool = False):
     """Gradients of the recurrence (no input transforms) for the output
     gradient ``grad_o`` [B,T,H,dv] (dtype of q) and the optional final-state
     gradient [N,H,dk,dv] fp32.  Inputs as in ``chunk_fwd``.  Returns a dict of
@@ -248,7 +250,8 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     [N,H,dk,dv] (None unless ``output_grad_initial_state`` or
     ``grad_initial_state`` is given; the latter may be ``initial_state`` or
     ``grad_final_state`` for an in-place result).  ``out`` may supply the
-    token gradients (a dict with dq, dk, dv, dg, dbeta), written in place."""
+    token gradients (a dict with dq, dk, dv, dg, dbeta), written in place.
+    ``scalar_gate``: g (and dg) are [B,T,H], one gate per token and head."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
@@ -257,7 +260,7 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     _need(q, "q", (B, T, H, dk), dt)
     _need(k, "k", (B, T, H, dk), dt)
     _need(v, "v", (B, T, H, dv), dt)
-    _need(g, "g", (B, T, H, dk), torch.float32)
+    _need(g, "g", (B, T, H) if scalar_gate else (B, T, H, dk), torch.float32)
     _need(beta, "beta", (B, T, H), dt)
     _need(grad_o, "grad_o", (B, T, H, dv), dt)
     N = B
@@ -272,7 +275,8 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     elif grad_initial_state is not None:
         _need(grad_initial_state, "grad_initial_state", (N, H, dk, dv), torch.float32)
     f32 = dict(dtype=torch.float32, device=q.device)
-    shapes = dict(dq=(B, T, H, dk), dk=(B, T, H, dk), dv=(B, T, H, dv), dg=(B, T, H, dk), dbeta=(B, T, H))
+    shapes = dict(dq=(B, T, H, dk), dk=(B, T, H, dk), dv=(B, T, H, dv),
+                  dg=(B, T, H) if scalar_gate else (B, T, H, dk), dbeta=(B, T, H))
     if out is None:
         out = {n: torch.empty(sh, **f32) for n, sh in shapes.items()}
     else:
@@ -283,7 +287,7 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     ws = recurrent_bwd_workspace_bytes(q, v, cu_seqlens)
     if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
-    a = _bwd_args(q, v, cu_seqlens, scale)
+    a = _bwd_args(q, v, cu_seqlens, scale, scalar_gate)
     a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
     a.initial_state, a.grad_o, a.grad_final_state = _ptr(initial_state), _ptr(grad_o), _ptr(grad_final_state)
     a.grad_q, a.grad_k, a.grad_v = _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"])

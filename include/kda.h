@@ -229,12 +229,13 @@ kda_status kda_recurrent_step(const kda_recurrent_step_args *args);
  * one is stored in the workspace on a first sweep, and each group of 8 is
  * rebuilt from it on the way back.
  *
- * Shapes (N = number of sequences; no KDA_FLAG_* transform is applied):
+ * Shapes (N = number of sequences):
  *   q, k, v, g, beta, initial_state, cu_seqlens, B, T, H, dk, dv, num_seqs,
- *           scale, in_dtype : as in kda_chunk_fwd (g: [B, T, H, dk] log-gates)
+ *           scale, in_dtype : as in kda_chunk_fwd (g: [B, T, H, dk] log-gates,
+ *           or [B, T, H] with KDA_FLAG_SCALAR_GATE)
  *   grad_o : [B, T, H, dv] in_dtype
  *   grad_final_state : [N, H, dk, dv] fp32, or NULL for zeros
- *   grad_q, grad_k, grad_g : [B, T, H, dk] fp32
+ *   grad_q, grad_k : [B, T, H, dk] fp32;  grad_g : the shape of g, fp32
  *   grad_v : [B, T, H, dv] fp32;  grad_beta : [B, T, H] fp32
  *   grad_initial_state : [N, H, dk, dv] fp32, or NULL to skip; may equal
  *           initial_state or grad_final_state (each slice is read before it
@@ -245,6 +246,9 @@ kda_status kda_recurrent_step(const kda_recurrent_step_args *args);
  *               bytes, about (B*T / 8 + 2 B*T / 64) * H * dk * dv * 4 (one
  *               stored state per 8 tokens, plus per-segment states); contents
  *               on entry ignored, on exit unspecified.
+ *   flags : 0 or KDA_FLAG_SCALAR_GATE (one gate per token and head, Gated
+ *           DeltaNet; its gradient is the sum over key channels).  The other
+ *           transforms are not differentiated here: KDA_ERR_UNSUPPORTED.
  */
 typedef struct {
     uint32_t struct_size; /* = sizeof(kda_recurrent_bwd_args) */
@@ -269,6 +273,7 @@ typedef struct {
     void *workspace;
     size_t workspace_bytes;
     void *stream; /* hipStream_t */
+    uint32_t flags;
 } kda_recurrent_bwd_args;
 
 /* Bytes of workspace kda_recurrent_bwd needs (host-only; only the size fields

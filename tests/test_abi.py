@@ -210,6 +210,8 @@ def test_backward_workspace_size():
     (dict(grad_initial_state=6 * FAKE + 64), "KDA_ERR_ALIAS"),  # partly over initial_state
     (dict(grad_initial_state=8 * FAKE + 64), "KDA_ERR_ALIAS"),  # partly over grad_final_state
     (dict(grad_initial_state=5 * FAKE), "KDA_ERR_ALIAS"),       # over beta
+    (dict(flags=_lib.KDA_FLAG_QK_L2NORM), "KDA_ERR_UNSUPPORTED"),
+    (dict(flags=8), "KDA_ERR_UNSUPPORTED"),
 ])
 def test_backward_rejects(kw, status):
     rc = _lib.recurrent_bwd_raw(bwd_args(**kw))

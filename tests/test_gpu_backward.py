@@ -44,7 +44,7 @@ def oracle_pair(x, do, dhT, n, h, scale):
     h0 = None if x.h0 is None else x.h0[n:n + 1, h:h + 1].astype(np.float64)
     dh = None if dhT is None else dhT[n:n + 1, h:h + 1].astype(np.float64)
     return oracle.backward(sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta), sl(do), h0=h0,
-                           d_final_state=dh, scale=scale)
+                           d_final_state=dh, scale=scale, scalar_gate=x.scalar_gate)
 
 
 def run_gpu(kda, x, do, dhT, scale, **kw):
@@ -52,7 +52,7 @@ def run_gpu(kda, x, do, dhT, scale, **kw):
     d = upload(x)
     g = kda.recurrent_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], dev(do, in_dtype_of(x)),
                           initial_state=d["h0"], grad_final_state=None if dhT is None else dev(dhT, torch.float32),
-                          cu_seqlens=d["cu"], scale=scale, **kw)
+                          cu_seqlens=d["cu"], scale=scale, scalar_gate=x.scalar_gate, **kw)
     torch.cuda.synchronize()
     return g
 
@@ -201,3 +201,12 @@ def test_thousands_of_short_sequences(kda):
     do, dhT = make_output_grads(x, 248, dhT_std=0.3)
     pairs = [(n, h) for n in list(range(0, 3000, 97)) + [2999] for h in range(2)]
     check(kda, x, do, dhT, pairs=pairs)
+
+
+@pytest.mark.parametrize("dk,dv,dt", [(128, 128, "bf16"), (64, 64, "fp32")])
+def test_scalar_gate(kda, dk, dv, dt):
+    """One gate per token and head (Gated DeltaNet): dg is [B, T, H], the sum
+    over key channels; 300 tokens so that sequences have several segments."""
+    x = make_prefill(149, 2, 300, 2, dk, dv, in_dtype=dt, h0_std=0.3, scalar_gate=True, name=f"bwd_scalar_{dt}")
+    do, dhT = make_output_grads(x, 249, dhT_std=0.3)
+    check(kda, x, do, dhT, scale=0.9)
