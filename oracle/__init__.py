@@ -52,7 +52,7 @@ def _load():
         lib.kda_oracle_backward.argtypes = [
             i64, ctypes.POINTER(ctypes.c_int64), i64, i64, i64,
             fp, fp, fp, fp, fp, dp, ctypes.c_double, fp, dp,
-            dp, dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int]
+            dp, dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double]
         lib.kda_oracle_dplr_forward.restype = ctypes.c_int
         lib.kda_oracle_dplr_forward.argtypes = [
             i64, ctypes.POINTER(ctypes.c_int64), i64, i64, i64,
@@ -120,12 +120,15 @@ def forward(q, k, v, g, beta, h0=None, cu_seqlens=None, scale: float = 1.0,
 
 
 def backward(q, k, v, g, beta, d_o, h0=None, d_final_state=None, cu_seqlens=None,
-             scale: float = 1.0, nthreads: int = 0, scalar_gate: bool = False):
+             scale: float = 1.0, nthreads: int = 0, scalar_gate: bool = False, qk_l2norm: bool = False,
+             gate_logits: bool = False, gate_scale: float = 1.0):
     """Gradients of the fp64 recurrence (no input transforms) for output
     gradient d_o [B, T, H, dv] and optional final-state gradient
     [N, H, dk, dv].  Returns a dict of float64 arrays: dq, dk, dg [B, T, H, dk],
     dv [B, T, H, dv], dbeta [B, T, H], dh0 [N, H, dk, dv].  With scalar_gate,
-    g and dg are [B, T, H] (Gated DeltaNet's gate)."""
+    g and dg are [B, T, H] (Gated DeltaNet's gate).  With the input transforms
+    of ``forward`` the gradients are those of the raw q, k and gate logits
+    (chain rule through the L2 norm and the softplus gate, kda_oracle.c)."""
     lib = _load()
     q, k, v, g, beta, d_o = map(_f32, (q, k, v, g, beta, d_o))
     B, T, H, dk = q.shape
@@ -143,7 +146,7 @@ def backward(q, k, v, g, beta, d_o, h0=None, d_final_state=None, cu_seqlens=None
         _ptr(g, ctypes.c_float), _ptr(beta, ctypes.c_float), _ptr(h0a, ctypes.c_double),
         float(scale), _ptr(d_o, ctypes.c_float), _ptr(dhT, ctypes.c_double),
         *(_ptr(out[n], ctypes.c_double) for n in ("dq", "dk", "dv", "dg", "dbeta", "dh0")), int(nthreads),
-        int(bool(scalar_gate)))
+        int(bool(scalar_gate)), int(bool(qk_l2norm)), int(bool(gate_logits)), float(gate_scale))
     if rc != 0:
         raise RuntimeError(f"kda_oracle_backward failed with code {rc}")
     return out

@@ -273,13 +273,22 @@ int kda_oracle_max_threads(void)
  * With scalar_gate, g is [T_total, H] (one gate per token and head for every
  * key channel, Gated DeltaNet's gate) and so is dg: the gate's gradient is the
  * sum over channels of the per-channel dg above.
+ *
+ * With the input transforms of kda_oracle_forward (qk_l2norm: x^ = x / r,
+ * r = sqrt(sum x^2 + eps); gate_logits: log-gate = -gate_scale softplus(z))
+ * the recurrence runs on the transformed values and the gradients are carried
+ * back through the transforms by the chain rule:
+ *   dx = (dx^ - x^ (x^ . dx^)) / r           for q and k,
+ *   dz = dloggate * (-gate_scale * sigmoid(z)),
+ * so dq, dk and dg are gradients with respect to the raw q, k and g.
  */
 int kda_oracle_backward(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk,
                         int64_t dv, const float *q, const float *k, const float *v,
                         const float *g, const float *beta, const double *h0,
                         double scale, const float *d_o, const double *dhT,
                         double *dq, double *dkk, double *dvv, double *dg,
-                        double *dbeta, double *dh0, int nthreads, int scalar_gate)
+                        double *dbeta, double *dh0, int nthreads, int scalar_gate,
+                        int qk_l2norm, int gate_logits, double gate_scale)
 {
     if (n_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0)
         return 1;
@@ -319,16 +328,21 @@ int kda_oracle_backward(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk
             const double b = (double)beta[(T0 + t) * H + h];
             for (int64_t j = 0; j < dv; ++j)
                 u[j] = (double)v[bv + j];
+            for (int64_t i = 0; i < dk; ++i)
+                kt[i] = (double)k[bk + i];
+            if (qk_l2norm)
+                l2_normalise(kt, dk);
             for (int64_t i = 0; i < dk; ++i) {
-                const double a = exp((double)g[scalar_gate ? (T0 + t) * H + h : bk + i]);
+                const double graw = (double)g[scalar_gate ? (T0 + t) * H + h : bk + i];
+                const double a = exp(gate_logits ? -gate_scale * softplus(graw) : graw);
                 for (int64_t j = 0; j < dv; ++j) {
                     Sn[i * dv + j] = a * Sp[i * dv + j];
-                    u[j] -= Sn[i * dv + j] * (double)k[bk + i];
+                    u[j] -= Sn[i * dv + j] * kt[i];
                 }
             }
             for (int64_t i = 0; i < dk; ++i)
                 for (int64_t j = 0; j < dv; ++j)
-                    Sn[i * dv + j] += b * (double)k[bk + i] * u[j];
+                    Sn[i * dv + j] += b * kt[i] * u[j];
         }
         /* backward */
         for (int64_t i = 0; i < sz; ++i)
@@ -337,10 +351,25 @@ int kda_oracle_backward(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk
             const int64_t tt = T0 + t, bk = (tt * H + h) * dk, bv = (tt * H + h) * dv;
             const double *Sp = S + t * sz, *Sn = S + (t + 1) * sz;
             const double b = (double)beta[tt * H + h];
+            double rk = 1.0, rq = 1.0;  /* the norms' r, for the chain rule */
             for (int64_t i = 0; i < dk; ++i) {
                 kt[i] = (double)k[bk + i];
                 qt[i] = (double)q[bk + i];
-                al[i] = exp((double)g[scalar_gate ? tt * H + h : bk + i]);
+                const double graw = (double)g[scalar_gate ? tt * H + h : bk + i];
+                al[i] = exp(gate_logits ? -gate_scale * softplus(graw) : graw);
+            }
+            if (qk_l2norm) {
+                double sk = 0.0, sq = 0.0;
+                for (int64_t i = 0; i < dk; ++i) {
+                    sk += kt[i] * kt[i];
+                    sq += qt[i] * qt[i];
+                }
+                rk = sqrt(sk + 1e-6);
+                rq = sqrt(sq + 1e-6);
+                for (int64_t i = 0; i < dk; ++i) {
+                    kt[i] /= rk;
+                    qt[i] /= rq;
+                }
             }
             for (int64_t j = 0; j < dv; ++j) {
                 vt[j] = (double)v[bv + j];
@@ -398,6 +427,10 @@ int kda_oracle_backward(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk
                     acc += St[i * dv + j] * dSt[i * dv + j];
                     dS[i * dv + j] = al[i] * dSt[i * dv + j];
                 }
+                if (gate_logits) {  /* d/dz of -gate_scale softplus(z) is -gate_scale sigmoid(z) */
+                    const double z = (double)g[scalar_gate ? tt * H + h : bk + i];
+                    acc *= -gate_scale / (1.0 + exp(-z));
+                }
                 if (scalar_gate)
                     dgs += acc;
                 else
@@ -405,6 +438,17 @@ int kda_oracle_backward(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk
             }
             if (scalar_gate)
                 dg[tt * H + h] = dgs;
+            if (qk_l2norm) {  /* dx = (dx^ - x^ (x^ . dx^)) / r */
+                double pq = 0.0, pk = 0.0;
+                for (int64_t i = 0; i < dk; ++i) {
+                    pq += qt[i] * dq[bk + i];
+                    pk += kt[i] * dkk[bk + i];
+                }
+                for (int64_t i = 0; i < dk; ++i) {
+                    dq[bk + i] = (dq[bk + i] - qt[i] * pq) / rq;
+                    dkk[bk + i] = (dkk[bk + i] - kt[i] * pk) / rk;
+                }
+            }
         }
         memcpy(dh0 + (n * H + h) * sz, dS, sizeof(double) * (size_t)sz);
         free(S);

@@ -36,23 +36,24 @@ def tiny(seed, T=4, H=1, dk=3, dv=2, N=1):
     return x, h0, W, Wh
 
 
-def loss(x, h0, W, Wh, scale, scalar_gate=False):
-    o, hT = oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], h0=h0, scale=scale, scalar_gate=scalar_gate)
+def loss(x, h0, W, Wh, scale, scalar_gate=False, **tr):
+    o, hT = oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], h0=h0, scale=scale, scalar_gate=scalar_gate,
+                           **tr)
     return float(np.sum(o * W) + np.sum(hT * Wh))
 
 
-def fd_gradient(x, h0, W, Wh, scale, name, idx, scalar_gate=False):
+def fd_gradient(x, h0, W, Wh, scale, name, idx, scalar_gate=False, **tr):
     def shifted(eps):
         if name == "h0":
             hp, hm = h0.copy(), h0.copy()
             hp[idx] += eps
             hm[idx] -= eps
-            return (loss(x, hp, W, Wh, scale, scalar_gate) - loss(x, hm, W, Wh, scale, scalar_gate)) / (2 * eps)
+            return (loss(x, hp, W, Wh, scale, scalar_gate, **tr) - loss(x, hm, W, Wh, scale, scalar_gate, **tr)) / (2 * eps)
         xp = {k: a.copy() for k, a in x.items()}
         xm = {k: a.copy() for k, a in x.items()}
         xp[name][idx] += np.float32(eps)
         xm[name][idx] -= np.float32(eps)
-        return (loss(xp, h0, W, Wh, scale, scalar_gate) - loss(xm, h0, W, Wh, scale, scalar_gate)) / (2 * eps)
+        return (loss(xp, h0, W, Wh, scale, scalar_gate, **tr) - loss(xm, h0, W, Wh, scale, scalar_gate, **tr)) / (2 * eps)
     d1, d2 = shifted(2.0 ** -7), shifted(2.0 ** -8)
     return (4 * d2 - d1) / 3
 
@@ -91,6 +92,29 @@ def test_backward_scalar_gate_matches_finite_differences():
         assert an.shape == fd.shape, (name, an.shape, fd.shape)
         err = np.linalg.norm(an - fd) / max(np.linalg.norm(fd), 1e-30)
         assert err < 1e-8, (name, err)
+
+
+@pytest.mark.parametrize("scalar_gate", [False, True], ids=["channel_gate", "scalar_gate"])
+def test_backward_with_transforms_matches_finite_differences(scalar_gate):
+    """The L2 norm of q and k and the softplus gate from logits (gate scale
+    0.8): gradients of the raw inputs against central differences of the
+    forward with the same transforms."""
+    x, h0, W, Wh = tiny(135)
+    rng = np.random.default_rng(136)
+    x["q"] = grid(rng, x["q"].shape, -2, 2)
+    x["k"] = grid(rng, x["k"].shape, -2, 2)
+    x["g"] = grid(rng, x["beta"].shape if scalar_gate else x["g"].shape, -2, 2)  # logits
+    tr = dict(qk_l2norm=True, gate_logits=True, gate_scale=0.8)
+    r = oracle.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], W.astype(np.float32), h0=h0,
+                        d_final_state=Wh, scale=1.1, scalar_gate=scalar_gate, **tr)
+    W32 = W.astype(np.float32).astype(np.float64)
+    key = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "beta": "dbeta", "h0": "dh0"}
+    for name, arr in list(x.items()) + [("h0", h0)]:
+        fd = np.zeros(arr.shape)
+        for idx in np.ndindex(arr.shape):
+            fd[idx] = fd_gradient(x, h0, W32, Wh, 1.1, name, idx, scalar_gate=scalar_gate, **tr)
+        err = np.linalg.norm(r[key[name]] - fd) / max(np.linalg.norm(fd), 1e-30)
+        assert err < 1e-7, (name, err)
 
 
 def test_backward_frozen_state_closed_form():
