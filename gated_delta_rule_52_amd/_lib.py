@@ -73,7 +73,7 @@ class RecurrentBwdArgs(ctypes.Structure):
         ("in_dtype", ctypes.c_int),
         ("workspace", vp), ("workspace_bytes", ctypes.c_size_t),
         ("stream", vp),
-        ("flags", ctypes.c_uint32),
+        ("flags", ctypes.c_uint32), ("gate_scale", ctypes.c_float),
     ]
 
 

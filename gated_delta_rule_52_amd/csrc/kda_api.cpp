@@ -166,8 +166,10 @@ kda_status read_bwd_args(const kda_recurrent_bwd_args *a, kda_recurrent_bwd_args
         return fail(KDA_ERR_BAD_STRUCT, "struct_size %u (expected %zu)", a->struct_size,
                     sizeof(kda_recurrent_bwd_args));
     out = *a;
-    if (out.flags & ~KDA_FLAG_SCALAR_GATE)
-        return fail(KDA_ERR_UNSUPPORTED, "flags 0x%x: only KDA_FLAG_SCALAR_GATE has gradients here", out.flags);
+    if (out.flags & ~(KDA_FLAG_QK_L2NORM | KDA_FLAG_GATE_SOFTPLUS | KDA_FLAG_SCALAR_GATE))
+        return fail(KDA_ERR_UNSUPPORTED, "unknown flags 0x%x", out.flags);
+    if ((out.flags & KDA_FLAG_GATE_SOFTPLUS) && !(std::isfinite(out.gate_scale) && out.gate_scale >= 0.f))
+        return fail(KDA_ERR_BAD_SHAPE, "gate_scale must be finite and >= 0");
     return check_bwd_sizes(&out);
 }
 
@@ -330,7 +332,9 @@ kda_status kda_recurrent_step(const kda_recurrent_step_args *user) {
 size_t kda_recurrent_bwd_workspace_bytes(const kda_recurrent_bwd_args *user) {
     kda_recurrent_bwd_args a;
     if (read_bwd_args(user, a) != KDA_OK) return static_cast<size_t>(-1);
-    return kda::backward_workspace_bytes(a.B, a.T, a.H, a.dk, a.dv, a.num_seqs, a.cu_seqlens != nullptr);
+    return kda::backward_workspace_bytes(a.B, a.T, a.H, a.dk, a.dv, a.num_seqs, a.cu_seqlens != nullptr,
+                                         (a.flags & (KDA_FLAG_QK_L2NORM | KDA_FLAG_GATE_SOFTPLUS)) != 0,
+                                         (a.flags & KDA_FLAG_SCALAR_GATE) != 0);
 }
 
 kda_status kda_recurrent_bwd(const kda_recurrent_bwd_args *user) {
@@ -348,7 +352,9 @@ kda_status kda_recurrent_bwd(const kda_recurrent_bwd_args *user) {
     const size_t th = static_cast<size_t>(tokens) * a->H, in_sz = dsize(a->in_dtype);
     const size_t gw = (a->flags & KDA_FLAG_SCALAR_GATE) ? 1 : static_cast<size_t>(a->dk);
     const size_t sbytes = static_cast<size_t>(N) * a->H * a->dk * a->dv * 4;
-    const size_t need = kda::backward_workspace_bytes(a->B, a->T, a->H, a->dk, a->dv, N, a->cu_seqlens != nullptr);
+    const size_t need = kda::backward_workspace_bytes(a->B, a->T, a->H, a->dk, a->dv, N, a->cu_seqlens != nullptr,
+                                                      (a->flags & (KDA_FLAG_QK_L2NORM | KDA_FLAG_GATE_SOFTPLUS)) != 0,
+                                                      (a->flags & KDA_FLAG_SCALAR_GATE) != 0);
     if (a->workspace_bytes < need || (need > 0 && !a->workspace))
         return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", a->workspace_bytes, need);
     const Range ins[] = {range_of(a->q, th * a->dk * in_sz), range_of(a->k, th * a->dk * in_sz),
@@ -391,6 +397,7 @@ kda_status kda_recurrent_bwd(const kda_recurrent_bwd_args *user) {
     L.scale = a->scale;
     L.in_bf16 = a->in_dtype == KDA_DTYPE_BF16;
     L.scalar_gate = (a->flags & KDA_FLAG_SCALAR_GATE) != 0;
+    L.xf = xform_of(a);
     L.workspace = a->workspace;
     L.stream = static_cast<hipStream_t>(a->stream);
     return hip_status(kda::launch_backward(L), "kda_recurrent_bwd launch");

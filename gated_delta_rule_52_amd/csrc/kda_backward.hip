@@ -642,16 +642,110 @@ reverse_combine_kernel(SegmentView sv, const float *hb, const float *dhT, float 
     }
 }
 
+// With the input transforms the gradients run on transformed copies of the inputs: a prepare pass writes,
+// per (token, head), the L2-normalised q and k and their inverse norms, the log-gates, and fp32 copies of v,
+// beta and grad_o; the passes above then run unchanged in fp32; a finish pass carries dq, dk and dg back to
+// the raw inputs by the chain rule (dx = (dx^ - x^ (x^ . dx^)) / r for q and k, dz = dloggate * (-s sigmoid(z))
+// for the gate logits z), in place.
+struct XformBufs {
+    float *q, *k, *g, *v, *b, *d, *iq, *ik;
+};
+
+// one wave per (token, head) u = t H + h, four per workgroup
+template <int DK, int DV, bool InBf16>
+__global__ void __launch_bounds__(256)
+bwd_prepare_kernel(BackwardLaunch L, XformBufs X, int64_t units) {
+    using In = Elem<InBf16>;
+    using IT = typename In::T;
+    constexpr int CPL = DK / kWave;
+    const int64_t u = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+    if (u >= units) return;
+    const int lane = threadIdx.x % kWave;
+    const IT *q = static_cast<const IT *>(L.q), *k = static_cast<const IT *>(L.k);
+    float qv[CPL], kv[CPL], qq = 0.f, kk = 0.f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+        const int64_t i = u * DK + lane * CPL + e;
+        qv[e] = In::load(q, i);
+        kv[e] = In::load(k, i);
+        qq += qv[e] * qv[e];
+        kk += kv[e] * kv[e];
+    }
+    float iq = 1.f, ik = 1.f;
+    if (L.xf.qk_l2norm) {  // the forward kernels' normalisation: x rsqrt(sum x^2 + eps)
+        iq = rsqrtf(wave_sum(qq) + kL2Eps);
+        ik = rsqrtf(wave_sum(kk) + kL2Eps);
+    }
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+        const int64_t i = u * DK + lane * CPL + e;
+        X.q[i] = qv[e] * iq;
+        X.k[i] = kv[e] * ik;
+        if (!L.scalar_gate) X.g[i] = L.xf.log_gate(L.g[i]);
+    }
+    if (lane == 0) {
+        X.iq[u] = iq;
+        X.ik[u] = ik;
+        if (L.scalar_gate) X.g[u] = L.xf.log_gate(L.g[u]);
+        X.b[u] = In::load(static_cast<const IT *>(L.beta), u);
+    }
+    for (int j = lane; j < DV; j += kWave) {
+        X.v[u * DV + j] = In::load(static_cast<const IT *>(L.v), u * DV + j);
+        X.d[u * DV + j] = In::load(static_cast<const IT *>(L.d_o), u * DV + j);
+    }
+}
+
+template <int DK>
+__global__ void __launch_bounds__(256)
+bwd_finish_kernel(BackwardLaunch L, XformBufs X, int64_t units) {
+    constexpr int CPL = DK / kWave;
+    const int64_t u = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+    if (u >= units) return;
+    const int lane = threadIdx.x % kWave;
+    if (L.xf.qk_l2norm) {
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {  // dq, then dk
+            float *dx = w == 0 ? L.dq : L.dk;
+            const float *xh = w == 0 ? X.q : X.k;
+            const float ir = w == 0 ? X.iq[u] : X.ik[u];
+            float d[CPL], xv[CPL], p = 0.f;
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) {
+                const int64_t i = u * DK + lane * CPL + e;
+                d[e] = dx[i];
+                xv[e] = xh[i];
+                p += d[e] * xv[e];
+            }
+            p = wave_sum(p);
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) dx[u * DK + lane * CPL + e] = (d[e] - xv[e] * p) * ir;
+        }
+    }
+    if (L.xf.gate_softplus) {  // d/dz of -s softplus(z) = -s sigmoid(z)
+        const float s = L.xf.gate_scale;
+        if (L.scalar_gate) {
+            if (lane == 0) L.dg[u] *= -s / (1.f + __expf(-L.g[u]));
+        } else {
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) {
+                const int64_t i = u * DK + lane * CPL + e;
+                L.dg[i] *= -s / (1.f + __expf(-L.g[i]));
+            }
+        }
+    }
+}
+
 namespace {
 
-// workspace: [segment table, P, H, entering states] [dS_leave per segment] [stored states];
+// workspace: [segment table, P, H, entering states] [dS_leave per segment] [stored states]
+// [with input transforms: q^, k^, log-gates, v, beta, grad_o in fp32, inverse norms];
 // the reverse local pass writes its Hb over the forward's H, which the forward combine has consumed
 struct BwdPlan {
-    size_t off_dl, off_ckpt, bytes;
+    size_t off_dl, off_ckpt, off_x, bytes;
     int max_segs;
 };
 
-BwdPlan bwd_plan(int B, int T, int H, int dk, int dv, int N, bool varlen) {
+BwdPlan bwd_plan(int B, int T, int H, int dk, int dv, int N, bool varlen, bool transforms, bool scalar_gate) {
     BwdPlan p{};
     auto a256 = [](size_t x) { return (x + 255) & ~size_t{255}; };
     const size_t seg_bytes = segment_states_bytes(B, T, H, dk, dv, N, varlen);
@@ -662,21 +756,55 @@ BwdPlan bwd_plan(int B, int T, int H, int dk, int dv, int N, bool varlen) {
     const size_t max_segs = static_cast<size_t>(tokens / 64 + N + 1);
     p.off_dl = a256(seg_bytes);
     p.off_ckpt = a256(p.off_dl + max_segs * state);
-    p.bytes = p.off_ckpt + static_cast<size_t>(tokens / kBlock + max_segs) * state;
+    p.off_x = a256(p.off_ckpt + static_cast<size_t>(tokens / kBlock + max_segs) * state);
+    const size_t th = static_cast<size_t>(tokens) * H;
+    p.bytes = p.off_x + (transforms ? th * (2 * dk + (scalar_gate ? 1 : dk) + 2 * dv + 3) * sizeof(float) : 0);
     return p;
+}
+
+XformBufs xform_bufs(char *base, size_t th, int dk, int dv, bool scalar_gate) {
+    XformBufs X;
+    float *f = reinterpret_cast<float *>(base);
+    X.q = f; f += th * dk;
+    X.k = f; f += th * dk;
+    X.g = f; f += th * (scalar_gate ? 1 : dk);
+    X.v = f; f += th * dv;
+    X.d = f; f += th * dv;
+    X.b = f; f += th;
+    X.iq = f; f += th;
+    X.ik = f;
+    return X;
 }
 
 }  // namespace
 
-size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int N, bool varlen) {
-    return bwd_plan(B, T, H, dk, dv, N, varlen).bytes;
+size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int N, bool varlen, bool transforms,
+                                bool scalar_gate) {
+    return bwd_plan(B, T, H, dk, dv, N, varlen, transforms, scalar_gate).bytes;
 }
 
 template <int DK, int DV>
-static hipError_t launch_bwd(const BackwardLaunch &L) {
-    const bool varlen = L.cu_seqlens != nullptr;
-    const BwdPlan p = bwd_plan(L.B, L.T, L.H, DK, DV, L.N, varlen);
-    char *ws = static_cast<char *>(L.workspace);
+static hipError_t launch_bwd(const BackwardLaunch &Lin) {
+    const bool varlen = Lin.cu_seqlens != nullptr;
+    const bool transforms = Lin.xf.qk_l2norm || Lin.xf.gate_softplus;
+    const BwdPlan p = bwd_plan(Lin.B, Lin.T, Lin.H, DK, DV, Lin.N, varlen, transforms, Lin.scalar_gate);
+    char *ws = static_cast<char *>(Lin.workspace);
+    const int64_t units = (varlen ? static_cast<int64_t>(Lin.T) : static_cast<int64_t>(Lin.B) * Lin.T) * Lin.H;
+    BackwardLaunch L = Lin;
+    XformBufs X{};
+    if (transforms) {  // run the passes on transformed fp32 copies
+        X = xform_bufs(ws + p.off_x, static_cast<size_t>(units), DK, DV, Lin.scalar_gate);
+        if (units > 0) {
+            const dim3 grid(static_cast<unsigned>((units + 3) / 4));
+            if (Lin.in_bf16)
+                hipLaunchKernelGGL((bwd_prepare_kernel<DK, DV, true>), grid, dim3(256), 0, Lin.stream, Lin, X, units);
+            else
+                hipLaunchKernelGGL((bwd_prepare_kernel<DK, DV, false>), grid, dim3(256), 0, Lin.stream, Lin, X, units);
+        }
+        L.q = X.q; L.k = X.k; L.g = X.g; L.v = X.v; L.beta = X.b; L.d_o = X.d;
+        L.in_bf16 = false;
+        L.xf = InputXform{};
+    }
     ChunkLaunch c{};
     c.q = L.q; c.k = L.k; c.v = L.v; c.g = L.g; c.beta = L.beta;
     c.h0 = L.h0; c.hT = nullptr; c.o = nullptr;
@@ -711,6 +839,9 @@ static hipError_t launch_bwd(const BackwardLaunch &L) {
     else
         hipLaunchKernelGGL((recurrent_bwd_kernel<DK, DV, false>), grid, block, 0, L.stream, b, ss.sv,
                            static_cast<const float *>(dleave));
+    if (transforms && units > 0)
+        hipLaunchKernelGGL((bwd_finish_kernel<DK>), dim3(static_cast<unsigned>((units + 3) / 4)), dim3(256), 0,
+                           Lin.stream, Lin, X, units);
     return hipGetLastError();
 }
 

@@ -75,12 +75,14 @@ struct BackwardLaunch {
     float scale;
     bool in_bf16;
     bool scalar_gate;           // g and dg are [tokens, H]: one gate per token and head
+    InputXform xf;              // Q/K L2 norm and softplus gate: gradients of the raw inputs
     void *workspace;            // backward_workspace_bytes()
     float *ckpt;                // stored forward states (set by launch_backward inside the workspace)
     hipStream_t stream;
 };
 
-size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int N, bool varlen);
+size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int N, bool varlen, bool transforms,
+                                bool scalar_gate);
 hipError_t launch_backward(const BackwardLaunch &L);
 
 // Chunkwise prefill.

@@ -217,10 +217,11 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
     return o
 
 
-def _bwd_args(q, v, cu_seqlens, scale, scalar_gate=False):
+def _bwd_args(q, v, cu_seqlens, scale, scalar_gate=False, qk_l2norm=False, gate_logits=False, gate_scale=1.0):
     B, T, H, dk = q.shape
     a = _lib.RecurrentBwdArgs()
-    a.flags = _lib.KDA_FLAG_SCALAR_GATE if scalar_gate else 0
+    a.flags = _flags(qk_l2norm, gate_logits, scalar_gate)
+    a.gate_scale = float(gate_scale)
     a.B, a.T, a.H, a.dk, a.dv = B, T, H, dk, v.shape[-1]
     a.num_seqs = B if cu_seqlens is None else cu_seqlens.numel() - 1
     a.cu_seqlens = _ptr(cu_seqlens)
@@ -229,8 +230,9 @@ def _bwd_args(q, v, cu_seqlens, scale, scalar_gate=False):
     return a
 
 
-def recurrent_bwd_workspace_bytes(q, v, cu_seqlens=None) -> int:
-    n = _lib.recurrent_bwd_workspace_raw(_bwd_args(q, v, cu_seqlens, 1.0))
+def recurrent_bwd_workspace_bytes(q, v, cu_seqlens=None, scalar_gate=False, qk_l2norm=False,
+                                  gate_logits=False) -> int:
+    n = _lib.recurrent_bwd_workspace_raw(_bwd_args(q, v, cu_seqlens, 1.0, scalar_gate, qk_l2norm, gate_logits))
     if n == 2 ** 64 - 1:
         _lib.check(_lib.STATUS_CODE["KDA_ERR_BAD_SHAPE"])
     return int(n)
@@ -242,7 +244,8 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   cu_seqlens: Optional[torch.Tensor] = None, scale: float = 1.0,
                   output_grad_initial_state: bool = True, grad_initial_state: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None,
-                  scalar_gate: bool = False):
+                  scalar_gate: bool = False, qk_l2norm: bool = False, gate_logits: bool = False,
+                  gate_scale: float = 1.0):
     """Gradients of the recurrence (no input transforms) for the output
     gradient ``grad_o`` [B,T,H,dv] (dtype of q) and the optional final-state
     gradient [N,H,dk,dv] fp32.  Inputs as in ``chunk_fwd``.  Returns a dict of
@@ -251,7 +254,9 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     ``grad_initial_state`` is given; the latter may be ``initial_state`` or
     ``grad_final_state`` for an in-place result).  ``out`` may supply the
     token gradients (a dict with dq, dk, dv, dg, dbeta), written in place.
-    ``scalar_gate``: g (and dg) are [B,T,H], one gate per token and head."""
+    ``scalar_gate``: g (and dg) are [B,T,H], one gate per token and head.
+    ``qk_l2norm``, ``gate_logits``, ``gate_scale``: the forward's input
+    transforms; dq, dk and dg are then gradients of the raw q, k and logits."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
@@ -284,10 +289,10 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         for n, sh in shapes.items():
             _need(out[n], n, sh, torch.float32)
     out["dh0"] = grad_initial_state
-    ws = recurrent_bwd_workspace_bytes(q, v, cu_seqlens)
+    ws = recurrent_bwd_workspace_bytes(q, v, cu_seqlens, scalar_gate, qk_l2norm, gate_logits)
     if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
-    a = _bwd_args(q, v, cu_seqlens, scale, scalar_gate)
+    a = _bwd_args(q, v, cu_seqlens, scale, scalar_gate, qk_l2norm, gate_logits, gate_scale)
     a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
     a.initial_state, a.grad_o, a.grad_final_state = _ptr(initial_state), _ptr(grad_o), _ptr(grad_final_state)
     a.grad_q, a.grad_k, a.grad_v = _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"])

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 /*
  * Optional input transforms, applied inside the kernels to every token before
@@ -246,9 +246,14 @@ kda_status kda_recurrent_step(const kda_recurrent_step_args *args);
  *               bytes, about (B*T / 8 + 2 B*T / 64) * H * dk * dv * 4 (one
  *               stored state per 8 tokens, plus per-segment states); contents
  *               on entry ignored, on exit unspecified.
- *   flags : 0 or KDA_FLAG_SCALAR_GATE (one gate per token and head, Gated
- *           DeltaNet; its gradient is the sum over key channels).  The other
- *           transforms are not differentiated here: KDA_ERR_UNSUPPORTED.
+ *   flags, gate_scale : the KDA_FLAG_* input transforms of the forward call.
+ *           KDA_FLAG_SCALAR_GATE: g and grad_g are [B, T, H] (the scalar gate's
+ *           gradient is the sum over key channels).  KDA_FLAG_QK_L2NORM and
+ *           KDA_FLAG_GATE_SOFTPLUS: grad_q, grad_k and grad_g are gradients of
+ *           the raw q, k and gate logits, carried back through the L2 norm
+ *           (dx = (dx^ - x^ (x^ . dx^)) / r) and through -gate_scale softplus
+ *           (dz = dloggate * (-gate_scale sigmoid(z))); the workspace then also
+ *           holds fp32 copies of the transformed inputs.
  */
 typedef struct {
     uint32_t struct_size; /* = sizeof(kda_recurrent_bwd_args) */
@@ -274,6 +279,7 @@ typedef struct {
     size_t workspace_bytes;
     void *stream; /* hipStream_t */
     uint32_t flags;
+    float gate_scale; /* used with KDA_FLAG_GATE_SOFTPLUS */
 } kda_recurrent_bwd_args;
 
 /* Bytes of workspace kda_recurrent_bwd needs (host-only; only the size fields

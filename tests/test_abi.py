@@ -26,7 +26,7 @@ def test_every_declared_function_is_exported():
     assert decl == sorted(_lib.EXPORTS)
     for name in decl:
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == 4
+    assert lib.kda_abi_version() == 5
 
 
 def test_status_strings():
@@ -188,6 +188,9 @@ def test_backward_workspace_size():
     assert n1 >= (200 // 8) * state and n2 >= (2000 // 8) * state and n2 > n1
     assert nv >= (1001 // 8) * state
     assert _lib.recurrent_bwd_workspace_raw(bwd_args(dk=32)) == 2 ** 64 - 1
+    # the input transforms add fp32 copies of the transformed inputs
+    nx = _lib.recurrent_bwd_workspace_raw(bwd_args(flags=_lib.KDA_FLAG_QK_L2NORM))
+    assert nx >= n1 + 200 * 2 * (2 * 128 + 128 + 2 * 64 + 3) * 4
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -210,8 +213,8 @@ def test_backward_workspace_size():
     (dict(grad_initial_state=6 * FAKE + 64), "KDA_ERR_ALIAS"),  # partly over initial_state
     (dict(grad_initial_state=8 * FAKE + 64), "KDA_ERR_ALIAS"),  # partly over grad_final_state
     (dict(grad_initial_state=5 * FAKE), "KDA_ERR_ALIAS"),       # over beta
-    (dict(flags=_lib.KDA_FLAG_QK_L2NORM), "KDA_ERR_UNSUPPORTED"),
     (dict(flags=8), "KDA_ERR_UNSUPPORTED"),
+    (dict(flags=_lib.KDA_FLAG_GATE_SOFTPLUS, gate_scale=-1.0), "KDA_ERR_BAD_SHAPE"),
 ])
 def test_backward_rejects(kw, status):
     rc = _lib.recurrent_bwd_raw(bwd_args(**kw))

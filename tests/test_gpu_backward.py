@@ -44,7 +44,7 @@ def oracle_pair(x, do, dhT, n, h, scale):
     h0 = None if x.h0 is None else x.h0[n:n + 1, h:h + 1].astype(np.float64)
     dh = None if dhT is None else dhT[n:n + 1, h:h + 1].astype(np.float64)
     return oracle.backward(sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta), sl(do), h0=h0,
-                           d_final_state=dh, scale=scale, scalar_gate=x.scalar_gate)
+                           d_final_state=dh, scale=scale, **x.transforms())
 
 
 def run_gpu(kda, x, do, dhT, scale, **kw):
@@ -52,7 +52,7 @@ def run_gpu(kda, x, do, dhT, scale, **kw):
     d = upload(x)
     g = kda.recurrent_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], dev(do, in_dtype_of(x)),
                           initial_state=d["h0"], grad_final_state=None if dhT is None else dev(dhT, torch.float32),
-                          cu_seqlens=d["cu"], scale=scale, scalar_gate=x.scalar_gate, **kw)
+                          cu_seqlens=d["cu"], scale=scale, **x.transforms(), **kw)
     torch.cuda.synchronize()
     return g
 
@@ -209,4 +209,15 @@ def test_scalar_gate(kda, dk, dv, dt):
     over key channels; 300 tokens so that sequences have several segments."""
     x = make_prefill(149, 2, 300, 2, dk, dv, in_dtype=dt, h0_std=0.3, scalar_gate=True, name=f"bwd_scalar_{dt}")
     do, dhT = make_output_grads(x, 249, dhT_std=0.3)
+    check(kda, x, do, dhT, scale=0.9)
+
+
+@pytest.mark.parametrize("scalar_gate,dt", [(False, "bf16"), (True, "bf16"), (False, "fp32")])
+def test_input_transforms(kda, scalar_gate, dt):
+    """Raw q, k and gate logits (the forward's in-kernel L2 norm and softplus
+    gate): dq, dk and dg are gradients of the raw inputs, carried back through
+    both transforms; several segments per sequence."""
+    x = make_prefill(152, 2, 300, 2, 128, 128, in_dtype=dt, h0_std=0.3, fused=True, scalar_gate=scalar_gate,
+                     name=f"bwd_transforms_{'scalar' if scalar_gate else 'channel'}_{dt}")
+    do, dhT = make_output_grads(x, 252, dhT_std=0.3)
     check(kda, x, do, dhT, scale=0.9)
