@@ -580,8 +580,8 @@ def main():
                              "frac": tf / FP32_VECTOR_PEAK_TFLOPS, "alg_flops_per_launch": flops,
                              "hbm_alg_bytes_per_launch": bbytes,
                              "hbm_frac": bbytes / (msb * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                             "kernel": "one kda_recurrent_bwd call: segmented fp32 forward to the combine, "
-                                       "reverse local pass, reverse combine, recurrent_bwd_kernel<128,128,bf16>"},
+                             "kernel": "one kda_recurrent_bwd call: both segment-local passes in one launch, forward "
+                                       "combine, reverse combine, recurrent_bwd_kernel<128,128,bf16>"},
             }
             if key == "backward" and not args.no_cpu:
                 rec[key]["cpu_baseline"] = cpu_backward_sample(xb)

@@ -459,12 +459,12 @@ recurrent_bwd_kernel(BackwardLaunch L, SegmentView sv, const float *dleave) {
 // The segmented forward's local pass, token by token in fp32, for every segment of a sequence of several:
 // H from a zero state with the segment's tokens, and the columns of the transition P (dk x dk) from the
 // identity with v = 0, both by one forward step per token.  One wave per 16 columns of [H | P].
-template <int DK, int DV, bool InBf16>
-__global__ void __launch_bounds__((DV + DK) / 16 * kWave)
-segment_local_kernel(BackwardLaunch L, SegmentView sv) {
+template <int DK, int DV, bool InBf16, int NT>
+__device__ __forceinline__ void segment_local_body(const BackwardLaunch &L, const SegmentView &sv) {
     using In = Elem<InBf16>;
     using IT = typename In::T;
-    constexpr int NT = (DV + DK) / 16 * kWave, R = DK / 4, RP = R + 4;
+    constexpr int R = DK / 4, RP = R + 4;
+    static_assert(NT == (DV + DK) / 16 * kWave, "one wave per 16 columns of [H | P]");
     const IT *k = static_cast<const IT *>(L.k), *v = static_cast<const IT *>(L.v);
     const IT *beta = static_cast<const IT *>(L.beta);
     const int h = blockIdx.x, seg = blockIdx.y, H = L.H;
@@ -512,13 +512,14 @@ segment_local_kernel(BackwardLaunch L, SegmentView sv) {
 // The gradient of the state entering a segment, from a zero gradient at its end (the part of dS that
 // the segment's own output gradients contribute): walking its tokens backwards,
 //     dS += scale q do^T;   dS <- Diag(alpha) (I - beta k k^T) dS,
-// which needs no forward state.  Segments that are not the first of their sequence only.
-template <int DK, int DV, bool InBf16>
-__global__ void __launch_bounds__(DV / 16 * kWave)
-reverse_local_kernel(BackwardLaunch L, SegmentView sv, float *hb) {
+// which needs no forward state.  Segments that are not the first of their sequence only.  The first
+// dv / 16 waves of the NT threads each carry 16 columns; all NT threads stage the tokens.
+template <int DK, int DV, bool InBf16, int NT>
+__device__ __forceinline__ void reverse_local_body(const BackwardLaunch &L, const SegmentView &sv, float *hb) {
     using In = Elem<InBf16>;
     using IT = typename In::T;
-    constexpr int NS = DV / 16, NT = NS * kWave, R = DK / 4, RP = R + 4;
+    constexpr int NS = DV / 16, R = DK / 4, RP = R + 4;
+    static_assert(NT >= NS * kWave, "a wave per 16 columns of dv");
     const IT *q = static_cast<const IT *>(L.q), *k = static_cast<const IT *>(L.k);
     const IT *beta = static_cast<const IT *>(L.beta), *d_o = static_cast<const IT *>(L.d_o);
     const int h = blockIdx.x, seg = blockIdx.y, H = L.H;
@@ -553,6 +554,7 @@ reverse_local_kernel(BackwardLaunch L, SegmentView sv, float *hb) {
         }
         if (tid < m) s_b[tid] = In::load(beta, (tb + tid) * H + h);
         __syncthreads();
+        if (slice >= NS) continue;  // staging only
         for (int x = m - 1; x >= 0; --x) {
             const float *kx = &s_k[x][rg * RP], *qx = &s_q[x][rg * RP], *ax = &s_a[x][rg * RP];
             const float dos = L.scale * s_do[x][col];
@@ -577,9 +579,22 @@ reverse_local_kernel(BackwardLaunch L, SegmentView sv, float *hb) {
             }
         }
     }
+    if (slice >= NS) return;
     float *dst = hb + (static_cast<int64_t>(seg) * H + h) * DK * DV + static_cast<int64_t>(rg * R) * DV + col;
 #pragma unroll
     for (int i = 0; i < R; ++i) dst[i * DV] = ds[i];
+}
+
+// Both local passes in one launch (blockIdx.z: 0 the forward one, 1 the reverse one): the reverse
+// workgroups fill the CUs the forward ones leave and the tail of one pass overlaps the other.  At
+// dk = dv = 128 a workgroup holds a CU alone (111 VGPRs for 16 waves); capping the registers so that two
+// fit spills, and is slower.
+template <int DK, int DV, bool InBf16>
+__global__ void __launch_bounds__((DV + DK) / 16 * kWave)
+local_passes_kernel(BackwardLaunch L, SegmentView sv, float *hb) {
+    constexpr int NT = (DV + DK) / 16 * kWave;
+    if (blockIdx.z == 0) segment_local_body<DK, DV, InBf16, NT>(L, sv);
+    else reverse_local_body<DK, DV, InBf16, NT>(L, sv, hb);
 }
 
 // Reverse combine: per (sequence, head, 16-column slice of dv), from the final-state gradient, walk the
@@ -737,11 +752,11 @@ bwd_finish_kernel(BackwardLaunch L, XformBufs X, int64_t units) {
 
 namespace {
 
-// workspace: [segment table, P, H, entering states] [dS_leave per segment] [stored states]
+// workspace: [segment table, P, H, entering states] [dS_leave per segment] [Hb per segment] [stored states]
 // [with input transforms: q^, k^, log-gates, v, beta, grad_o in fp32, inverse norms];
-// the reverse local pass writes its Hb over the forward's H, which the forward combine has consumed
+// (the reverse local pass writes Hb beside the forward's H: the two local passes run in one launch)
 struct BwdPlan {
-    size_t off_dl, off_ckpt, off_x, bytes;
+    size_t off_dl, off_hb, off_ckpt, off_x, bytes;
     int max_segs;
 };
 
@@ -755,7 +770,8 @@ BwdPlan bwd_plan(int B, int T, int H, int dk, int dv, int N, bool varlen, bool t
     const size_t state = static_cast<size_t>(H) * dk * dv * sizeof(float);
     const size_t max_segs = static_cast<size_t>(tokens / 64 + N + 1);
     p.off_dl = a256(seg_bytes);
-    p.off_ckpt = a256(p.off_dl + max_segs * state);
+    p.off_hb = a256(p.off_dl + max_segs * state);
+    p.off_ckpt = a256(p.off_hb + max_segs * state);
     p.off_x = a256(p.off_ckpt + static_cast<size_t>(tokens / kBlock + max_segs) * state);
     const size_t th = static_cast<size_t>(tokens) * H;
     p.bytes = p.off_x + (transforms ? th * (2 * dk + (scalar_gate ? 1 : dk) + 2 * dv + 3) * sizeof(float) : 0);
@@ -820,19 +836,16 @@ static hipError_t launch_bwd(const BackwardLaunch &Lin) {
     float *dleave = reinterpret_cast<float *>(ws + p.off_dl);
     BackwardLaunch b = L;
     b.ckpt = reinterpret_cast<float *>(ws + p.off_ckpt);
+    float *hb = reinterpret_cast<float *>(ws + p.off_hb);
     const dim3 grid(L.H, ss.max_segs), block(DV / 16 * kWave);
-    const dim3 block_local((DV + DK) / 16 * kWave);
+    const dim3 grid_local(L.H, ss.max_segs, 2), block_local((DV + DK) / 16 * kWave);
     if (L.in_bf16)
-        hipLaunchKernelGGL((segment_local_kernel<DK, DV, true>), grid, block_local, 0, L.stream, b, ss.sv);
+        hipLaunchKernelGGL((local_passes_kernel<DK, DV, true>), grid_local, block_local, 0, L.stream, b, ss.sv, hb);
     else
-        hipLaunchKernelGGL((segment_local_kernel<DK, DV, false>), grid, block_local, 0, L.stream, b, ss.sv);
+        hipLaunchKernelGGL((local_passes_kernel<DK, DV, false>), grid_local, block_local, 0, L.stream, b, ss.sv, hb);
     launch_segment_combine(c, ss);
-    if (L.in_bf16)
-        hipLaunchKernelGGL((reverse_local_kernel<DK, DV, true>), grid, block, 0, L.stream, b, ss.sv, ss.sv.Hs);
-    else
-        hipLaunchKernelGGL((reverse_local_kernel<DK, DV, false>), grid, block, 0, L.stream, b, ss.sv, ss.sv.Hs);
     hipLaunchKernelGGL((reverse_combine_kernel<DK>), dim3(DV / 16, L.H, L.N), dim3(256), 0, L.stream, ss.sv,
-                       static_cast<const float *>(ss.sv.Hs), L.dhT, dleave, L.dh0, L.H, DV);
+                       static_cast<const float *>(hb), L.dhT, dleave, L.dh0, L.H, DV);
     if (L.in_bf16)
         hipLaunchKernelGGL((recurrent_bwd_kernel<DK, DV, true>), grid, block, 0, L.stream, b, ss.sv,
                            static_cast<const float *>(dleave));
