@@ -53,8 +53,8 @@ def decode_alg_bytes(N, H, dk, dv, in_bytes=2, out_bytes=2):
     return nh * (2 * dk * dv * 4 + (2 * dk + dv + 1) * in_bytes + dk * 4 + dv * out_bytes)
 
 
-# sources no kernel of kda_chunk_fwd is built from (decode and append kernels, gradients)
-NOT_PREFILL_SOURCES = ("kda_recurrent.hip", "kda_backward.hip")
+# sources no kernel of kda_chunk_fwd is built from (decode and append kernels, gradients, DPLR)
+NOT_PREFILL_SOURCES = ("kda_recurrent.hip", "kda_backward.hip", "kda_dplr.hip")
 
 
 def source_digest():
