@@ -460,21 +460,26 @@ hipError_t launch_chunk(const ChunkLaunch &L) {
                        p.seg_len, reinterpret_cast<int4 *>(ws + p.off_table),
                        reinterpret_cast<int32_t *>(ws + p.off_seq), sv.xcount);
     void *packs = ws + p.off_pack;
+    // fixed-length sequences no longer than a segment are one segment each: the local pass and the
+    // combine would only return (their launches alone cost tens of microseconds on many short sequences)
+    const bool chained = varlen || L.T == 0 || L.T > p.seg_len;
     if (p.packs) {
         launch_prep(L, sv, p.max_segs, p.per, packs);
-        launch_scan<kLocal>(L, sv, p.max_segs, p.per, packs);
-    } else {
+        if (chained) launch_scan<kLocal>(L, sv, p.max_segs, p.per, packs);
+    } else if (chained) {
         launch_fp32_pass<kLocal>(L, sv, p.max_segs);
     }
-    if (p.packs)  // P in bf16 planes; one workgroup per (head, 16-column slice, sequence), heads fastest
-        hipLaunchKernelGGL(combine_bf16x3_kernel, dim3(L.H, L.dv / 16, L.N), dim3(512), 0, L.stream, sv, L.h0, L.hT,
-                           L.H);
-    else if (L.dk == 128)  // heads fastest: a head's slices share one XCD (workgroups go round-robin over XCDs)
-        hipLaunchKernelGGL(combine_mfma_kernel, dim3(L.H, L.dv / 16, L.N), dim3(256), 0, L.stream, sv, L.h0, L.hT,
-                           L.H, L.dv);
-    else
-        hipLaunchKernelGGL(combine_kernel<64>, dim3(L.dv / 16, L.H, L.N), dim3(256), 0, L.stream, sv, L.h0, L.hT,
-                           L.H, L.dv);
+    if (chained) {
+        if (p.packs)  // P in bf16 planes; one workgroup per (head, 16-column slice, sequence), heads fastest
+            hipLaunchKernelGGL(combine_bf16x3_kernel, dim3(L.H, L.dv / 16, L.N), dim3(512), 0, L.stream, sv, L.h0,
+                               L.hT, L.H);
+        else if (L.dk == 128)  // heads fastest: a head's slices share one XCD (workgroups go round-robin over XCDs)
+            hipLaunchKernelGGL(combine_mfma_kernel, dim3(L.H, L.dv / 16, L.N), dim3(256), 0, L.stream, sv, L.h0,
+                               L.hT, L.H, L.dv);
+        else
+            hipLaunchKernelGGL(combine_kernel<64>, dim3(L.dv / 16, L.H, L.N), dim3(256), 0, L.stream, sv, L.h0,
+                               L.hT, L.H, L.dv);
+    }
     if (p.packs) launch_scan<kOut>(L, sv, p.max_segs, p.per, packs);
     else launch_fp32_pass<kOut>(L, sv, p.max_segs);
     return hipGetLastError();
