@@ -609,7 +609,8 @@ reverse_combine_kernel(SegmentView sv, const float *hb, const float *dhT, float 
     constexpr int BV = 16, DKP = DK + 1, RG = 256 / BV, ROWS = DK / RG, PV4 = DK * DK / 4 / 256;
     __shared__ float sP[DK * DKP];
     __shared__ float sS[DK * BV];
-    const int slice = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
+    int slice, h, n;
+    slice_head_seq(slice, h, n);
     const int tid = threadIdx.x, j = tid % BV, ig = tid / BV, j0 = slice * BV;
     const int first = sv.seq_seg[n], end = sv.seq_seg[n + 1];
     if (end - first == 1) return;

@@ -73,6 +73,27 @@ __device__ __forceinline__ float quad_sum(float x) {
     return x + dpp_mov<0x4E>(x);  // quad permute [2, 3, 0, 1]
 }
 
+// The (slice, head, sequence) a workgroup of a grid (slices, H, N) works on.  Workgroups go round-robin
+// over the GPU's 8 XCDs, each with its own L2, in order of their linear index.  The slices of one
+// (sequence, head) read the same token inputs and share the cache lines of every state row, so their
+// indexes are made congruent mod 8: they run on one XCD and its L2 fetches each line once.  When N H is
+// not a multiple of 8 the slices stay consecutive.
+__device__ __forceinline__ void slice_head_seq(int &slice, int &h, int &n) {
+    const int64_t nsl = gridDim.x, groups = static_cast<int64_t>(gridDim.y) * gridDim.z;
+    const int64_t id = blockIdx.x + nsl * (blockIdx.y + static_cast<int64_t>(gridDim.y) * blockIdx.z);
+    int64_t gi;
+    if (groups % 8 == 0) {
+        const int64_t kq = id >> 3;
+        gi = (id & 7) + 8 * (kq / nsl);
+        slice = static_cast<int>(kq % nsl);
+    } else {
+        gi = id / nsl;
+        slice = static_cast<int>(id % nsl);
+    }
+    h = static_cast<int>(gi % gridDim.y);
+    n = static_cast<int>(gi / gridDim.y);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);

@@ -35,7 +35,9 @@ dplr_seq_kernel(DplrLaunch L) {
     static_assert(R % 4 == 0 && CPL >= 1, "tiling");
     __shared__ __attribute__((aligned(16))) float s_in[2][5][4 * RP];  // [buffer][k, q, a, b, alpha][row]
 
-    const int slice = blockIdx.x, h = blockIdx.y, n = blockIdx.z, H = L.H, DV = L.dv;
+    const int H = L.H, DV = L.dv;
+    int slice, h, n;
+    slice_head_seq(slice, h, n);
     const int lane = threadIdx.x, c = lane >> 2, rg = lane & 3;
     const int col = 16 * slice + c;
     int64_t t0, t1;

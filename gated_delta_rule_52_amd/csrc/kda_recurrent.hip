@@ -198,7 +198,8 @@ recurrent_seq_kernel(const void *__restrict__ q_, const void *__restrict__ k_, c
     static_assert(R % 4 == 0 && CPL >= 1, "tiling");
     __shared__ __attribute__((aligned(16))) float s_in[2][3][4 * RP];  // [buffer][k, q, alpha][row]
 
-    const int slice = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
+    int slice, h, n;
+    slice_head_seq(slice, h, n);
     const int lane = threadIdx.x, c = lane >> 2, rg = lane & 3;
     const int col = 16 * slice + c;
     int64_t t0, t1;
