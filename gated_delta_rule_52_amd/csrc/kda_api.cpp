@@ -281,7 +281,9 @@ kda_status kda_recurrent_fwd(const kda_chunk_fwd_args *user) {
     L.N = a->num_seqs; L.T = a->T; L.H = a->H; L.dk = a->dk; L.dv = a->dv; L.scale = a->scale;
     L.in_bf16 = a->in_dtype == KDA_DTYPE_BF16;
     L.out_bf16 = a->out_dtype == KDA_DTYPE_BF16;
-    L.multi_token = true;
+    // one token per sequence is a decode step: the decode kernel's wide rows stream the state at the copy
+    // rate, where the multi-token kernel's 16-column slices reach about half of it
+    L.multi_token = a->cu_seqlens != nullptr || a->T != 1;
     L.xf = xform_of(a);
     L.stream = static_cast<hipStream_t>(a->stream);
     return hip_status(kda::launch_recurrent(L), "kda_recurrent_fwd launch");

@@ -80,3 +80,48 @@ def test_in_place_state_and_bf16_output(kda):
     assert torch.equal(o32a, o32b) and torch.equal(ha, hb), "not deterministic"
     assert torch.equal(S, ha), "in-place final state differs"
     assert np.array_equal(bf16_round(o32a.cpu().numpy()), o16.float().cpu().numpy())
+
+
+@pytest.mark.parametrize("dk,dv,dt", [(128, 128, "bf16"), (64, 128, "fp32"), (128, 64, "bf16"), (64, 64, "fp32")])
+def test_one_token_per_sequence_runs_as_a_decode_step(kda, dk, dv, dt):
+    """Fixed-length input of one token per sequence takes the decode kernel:
+    parity against the oracle from an initial state, the in-place form (final
+    state aliasing the initial state) bit-equal to separate buffers, and the
+    same bits as kda_recurrent_step on the same token."""
+    import torch
+    x = make_prefill(86, 5, 1, 3, dk, dv, in_dtype=dt, h0_std=0.3, name=f"one_token_{dk}x{dv}_{dt}")
+    check(kda, x, scale=0.8)
+    d = upload(x)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    o1, h1 = kda.recurrent_fwd(*args, initial_state=d["h0"], scale=0.8, out_dtype=torch.float32)
+    S = d["h0"].clone()
+    o2, _ = kda.recurrent_fwd(*args, initial_state=S, final_state=S, scale=0.8, out_dtype=torch.float32)
+    step_in = [a[:, 0].contiguous() for a in args]  # [N, H, ...]: one token per sequence
+    o3 = kda.recurrent_step(*step_in, d["h0"].clone(), scale=0.8, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, S), "in-place run differs"
+    assert torch.equal(o1[:, 0], o3), "differs from the decode step"
+
+
+@pytest.mark.parametrize("scalar_gate", [False, True], ids=["channel_gate", "scalar_gate"])
+def test_one_token_per_sequence_with_transforms(kda, scalar_gate):
+    """Raw q, k and gate logits, one token per sequence: the in-kernel L2 norm
+    and softplus gate give the same bits as the decode step on the same raw
+    token, and the state update matches the oracle's."""
+    import torch
+    import oracle
+    x = make_prefill(87, 4, 1, 2, 128, 128, h0_std=0.3, fused=True, scalar_gate=scalar_gate,
+                     name=f"one_token_fused_{'scalar' if scalar_gate else 'channel'}")
+    d = upload(x)
+    tr = x.transforms()
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    o1, h1 = kda.recurrent_fwd(*args, initial_state=d["h0"], out_dtype=torch.float32, **tr)
+    state = d["h0"].clone()
+    o3 = kda.recurrent_step(*[a[:, 0].contiguous() for a in args], state, out_dtype=torch.float32, **tr)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, 0], o3) and torch.equal(h1, state), "differs from the decode step"
+    heads = list(range(x.H))
+    o_ref, h_ref = oracle.forward(x.q, x.k, x.v, x.g, x.beta, h0=x.h0.astype(np.float64), heads=heads, **tr)
+    eo, es = slice_errors(o1.cpu().numpy(), h1.cpu().numpy(), o_ref, h_ref, x, heads)
+    say(f"  one token with transforms: o={eo:.3e} state={es:.3e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
