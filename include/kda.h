@@ -156,7 +156,9 @@ kda_status kda_chunk_fwd(const kda_chunk_fwd_args *args);
  * state in registers for the whole segment).  The same recurrence as
  * kda_chunk_fwd, computed token by token in order: per (sequence, head,
  * 16-column slice of dv) one wave reads its state slice once, applies every
- * token of the sequence, and writes the slice once.  Meant for short appends
+ * token of the sequence, and writes the slice once.  Fixed-length input of one
+ * token per sequence runs as a decode step, with the same result bit for bit
+ * as kda_recurrent_step.  Meant for short appends
  * (speculative decoding, a few tokens per sequence): on MI355X it is the
  * faster path up to about 16 new tokens per sequence, and kda_chunk_fwd from
  * about 64 on.
@@ -208,7 +210,7 @@ kda_status kda_recurrent_step(const kda_recurrent_step_args *args);
 
 /*
  * Gradients of the recurrence (the backward pass of kda_chunk_fwd and
- * kda_recurrent_fwd, without input transforms): for the loss gradients
+ * kda_recurrent_fwd, with the same input transforms): for the loss gradients
  * grad_o = dL/do and grad_final_state = dL/dS_T, the gradients of L with
  * respect to q, k, v, g, beta and the initial state.  Reverse-mode
  * differentiation of the recurrence of the Kimi Linear review notes
@@ -220,10 +222,11 @@ kda_status kda_recurrent_step(const kda_recurrent_step_args *args);
  * with S~ = Diag(exp(g_t)) S_{t-1}; the initial-state gradient is the final dS.
  *
  * Computed in fp32.  Long sequences are cut into segments as in
- * kda_chunk_fwd: the segmented forward (fp32 path) gives the state entering
- * each segment, and the state-gradient recurrence, which needs no forward
- * state, is chained backwards over the segments through the transposed
- * segment transitions.  Every segment then runs token by token in parallel
+ * kda_chunk_fwd: a token-by-token fp32 pass gives each segment's transition
+ * and local state, which kda_chunk_fwd's combine chains into the state
+ * entering each segment, and the state-gradient recurrence, which needs no
+ * forward state, is chained backwards over the segments through the
+ * transposed segment transitions.  Every segment then runs token by token in parallel
  * (one workgroup per segment and head, one wave per 16 columns of dv); its
  * forward states are recomputed, not read from the forward pass: every 8th
  * one is stored in the workspace on a first sweep, and each group of 8 is
@@ -243,9 +246,10 @@ kda_status kda_recurrent_step(const kda_recurrent_step_args *args);
  *   The other gradients must not overlap any input, the workspace or each
  *   other.  Every gradient element of every token is written.
  *   workspace : device scratch of at least kda_recurrent_bwd_workspace_bytes()
- *               bytes, about (B*T / 8 + 2 B*T / 64) * H * dk * dv * 4 (one
- *               stored state per 8 tokens, plus per-segment states); contents
- *               on entry ignored, on exit unspecified.
+ *               bytes, about (B*T / 8 + 3 B*T / 64) * H * dk * dv * 4 (one
+ *               stored state per 8 tokens, plus state-sized buffers for the
+ *               segment chain); contents on entry ignored, on exit
+ *               unspecified.
  *   flags, gate_scale : the KDA_FLAG_* input transforms of the forward call.
  *           KDA_FLAG_SCALAR_GATE: g and grad_g are [B, T, H] (the scalar gate's
  *           gradient is the sum over key channels).  KDA_FLAG_QK_L2NORM and
