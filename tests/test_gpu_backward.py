@@ -221,3 +221,13 @@ def test_input_transforms(kda, scalar_gate, dt):
                      name=f"bwd_transforms_{'scalar' if scalar_gate else 'channel'}_{dt}")
     do, dhT = make_output_grads(x, 252, dhT_std=0.3)
     check(kda, x, do, dhT, scale=0.9)
+
+
+@pytest.mark.parametrize("dk,dv,dt", [(64, 64, "fp32"), (128, 128, "bf16")])
+def test_segmented_with_heads_grouped_per_xcd(kda, dk, dv, dt):
+    """2 sequences of 1,024 tokens x 8 heads (16 sequence-heads, a multiple of
+    8): several segments per sequence, so the reverse combine chains them with
+    a head's dv slices mapped to one XCD, over two groups of 8."""
+    x = make_prefill(153, 2, 1024, 8, dk, dv, in_dtype=dt, h0_std=0.1, name=f"bwd_grouped_{dk}x{dv}")
+    do, dhT = make_output_grads(x, 253, dhT_std=0.1)
+    check(kda, x, do, dhT, scale=0.9)

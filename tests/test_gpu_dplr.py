@@ -83,3 +83,10 @@ def test_dplr_kda_case_matches_kda_kernel(kda):
     eo, es = rel(od.cpu().numpy(), ok.cpu().numpy()), rel(hd.cpu().numpy(), hk.cpu().numpy())
     say(f"case dplr_kda_case: o={eo:.2e} state={es:.2e}")
     assert eo <= TOL_FP32 and es <= TOL_FP32
+
+
+def test_dplr_heads_grouped_per_xcd(kda):
+    """4 sequences x 8 heads (32 = 4 x 8 sequence-heads): the kernel maps
+    workgroups so that a head's dv slices share one XCD, over several groups
+    of 8; parity is unchanged."""
+    check(kda, make_dplr(163, 4, 20, 8, 128, 128, h0_std=0.3), "dplr_grouped", scale=0.9)

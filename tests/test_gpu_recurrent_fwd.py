@@ -125,3 +125,11 @@ def test_one_token_per_sequence_with_transforms(kda, scalar_gate):
     eo, es = slice_errors(o1.cpu().numpy(), h1.cpu().numpy(), o_ref, h_ref, x, heads)
     say(f"  one token with transforms: o={eo:.3e} state={es:.3e}")
     assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
+
+
+@pytest.mark.parametrize("dk,dv,dt", [(128, 128, "bf16"), (64, 64, "fp32")])
+def test_heads_grouped_per_xcd(kda, dk, dv, dt):
+    """4 sequences x 8 heads (32 sequence-heads, a multiple of 8): workgroups
+    are mapped so that a head's dv slices share one XCD, over several groups
+    of 8; parity is unchanged."""
+    check(kda, make_prefill(88, 4, 20, 8, dk, dv, in_dtype=dt, h0_std=0.3, name=f"grouped_{dk}x{dv}"), scale=0.9)
