@@ -26,7 +26,7 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 # Every function declared in include/kda.h.
 EXPORTS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_fwd", "kda_recurrent_step",
            "kda_recurrent_bwd_workspace_bytes", "kda_recurrent_bwd", "kda_dplr_recurrent_fwd",
-           "kda_status_string", "kda_last_error", "kda_abi_version")
+           "kda_status_string", "kda_last_error", "kda_last_hip_error", "kda_abi_version", "kda_version")
 
 vp = ctypes.c_void_p
 
@@ -126,8 +126,12 @@ def load():
         lib.kda_status_string.argtypes = [ctypes.c_int]
         lib.kda_last_error.restype = ctypes.c_char_p
         lib.kda_last_error.argtypes = []
+        lib.kda_last_hip_error.restype = ctypes.c_char_p
+        lib.kda_last_hip_error.argtypes = []
         lib.kda_abi_version.restype = ctypes.c_int
         lib.kda_abi_version.argtypes = []
+        lib.kda_version.restype = ctypes.c_int
+        lib.kda_version.argtypes = []
         _lib = lib
     return _lib
 

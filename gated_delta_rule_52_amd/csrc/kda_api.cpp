@@ -124,15 +124,20 @@ kda_status check_prefill_buffers(const kda_chunk_fwd_args *a) {
                          range_of(a->v, th * a->dv * in_sz), range_of(a->g, th * gate_width(a) * 4),
                          range_of(a->beta, th * in_sz)};
     const size_t sbytes = static_cast<size_t>(N) * a->H * a->dk * a->dv * 4;
+    const Range rh0 = range_of(a->initial_state, a->initial_state ? sbytes : 0);
+    const Range rcu = range_of(a->cu_seqlens, a->cu_seqlens ? (static_cast<size_t>(N) + 1) * 4 : 0);
     for (const Range &r : ins)
         if (overlap(ro, r)) return fail(KDA_ERR_ALIAS, "o overlaps an input");
+    // o is written while other workgroups still read the initial state and the sequence offsets
+    if (overlap(ro, rh0)) return fail(KDA_ERR_ALIAS, "o overlaps initial_state");
+    if (overlap(ro, rcu)) return fail(KDA_ERR_ALIAS, "o overlaps cu_seqlens");
     if (a->final_state) {
         const Range rf = range_of(a->final_state, sbytes);
         for (const Range &r : ins)
             if (overlap(rf, r)) return fail(KDA_ERR_ALIAS, "final_state overlaps an input");
         if (overlap(rf, ro)) return fail(KDA_ERR_ALIAS, "final_state overlaps o");
-        if (a->initial_state && a->initial_state != a->final_state &&
-            overlap(rf, range_of(a->initial_state, sbytes)))
+        if (overlap(rf, rcu)) return fail(KDA_ERR_ALIAS, "final_state overlaps cu_seqlens");
+        if (a->initial_state && a->initial_state != a->final_state && overlap(rf, rh0))
             return fail(KDA_ERR_ALIAS, "final_state partially overlaps initial_state");
     }
     if (N > 65535 || a->H > 65535) return fail(KDA_ERR_UNSUPPORTED, "N=%d H=%d (at most 65535 each)", N, a->H);
@@ -193,7 +198,11 @@ const char *kda_status_string(kda_status s) {
 
 const char *kda_last_error(void) { return g_last_error.c_str(); }
 
+const char *kda_last_hip_error(void) { return g_last_error.c_str(); }
+
 int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+int kda_version(void) { return KDA_ABI_VERSION; }
 
 size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_fwd_args *user) {
     kda_chunk_fwd_args args;
@@ -237,6 +246,8 @@ kda_status kda_chunk_fwd(const kda_chunk_fwd_args *user) {
             return fail(KDA_ERR_ALIAS, "workspace overlaps final_state");
         if (a->initial_state && overlap(rw, range_of(a->initial_state, sbytes)))
             return fail(KDA_ERR_ALIAS, "workspace overlaps initial_state");
+        if (a->cu_seqlens && overlap(rw, range_of(a->cu_seqlens, (static_cast<size_t>(N) + 1) * 4)))
+            return fail(KDA_ERR_ALIAS, "workspace overlaps cu_seqlens");
     }
 
     kda::ChunkLaunch L{};
@@ -314,6 +325,8 @@ kda_status kda_recurrent_step(const kda_recurrent_step_args *user) {
     for (const Range &r : ins)
         if (overlap(ro, r) || overlap(rf, r)) return fail(KDA_ERR_ALIAS, "an output overlaps an input");
     if (overlap(ro, rf)) return fail(KDA_ERR_ALIAS, "o overlaps final_state");
+    if (a->initial_state && overlap(ro, range_of(a->initial_state, sbytes)))
+        return fail(KDA_ERR_ALIAS, "o overlaps initial_state");
     if (a->initial_state && a->initial_state != a->final_state &&
         overlap(rf, range_of(a->initial_state, sbytes)))
         return fail(KDA_ERR_ALIAS, "final_state partially overlaps initial_state");

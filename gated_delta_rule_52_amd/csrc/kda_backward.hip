@@ -129,7 +129,8 @@ recurrent_bwd_kernel(BackwardLaunch L, SegmentView sv, const float *dleave) {
     const IT *v = static_cast<const IT *>(L.v), *beta = static_cast<const IT *>(L.beta);
     const IT *d_o = static_cast<const IT *>(L.d_o);
     const float *g = L.g;
-    const int h = blockIdx.x, seg = blockIdx.y, H = L.H;
+    // grid.x = segment * H + head: a packed batch may hold more than grid.y's 65,535 segments
+    const int H = L.H, h = static_cast<int>(blockIdx.x % H), seg = static_cast<int>(blockIdx.x / H);
     if (seg >= sv.count()) return;
     const int4 sd = sv.table[seg];
     const int n = sd.x;
@@ -467,7 +468,8 @@ __device__ __forceinline__ void segment_local_body(const BackwardLaunch &L, cons
     static_assert(NT == (DV + DK) / 16 * kWave, "one wave per 16 columns of [H | P]");
     const IT *k = static_cast<const IT *>(L.k), *v = static_cast<const IT *>(L.v);
     const IT *beta = static_cast<const IT *>(L.beta);
-    const int h = blockIdx.x, seg = blockIdx.y, H = L.H;
+    // grid.x = segment * H + head: a packed batch may hold more than grid.y's 65,535 segments
+    const int H = L.H, h = static_cast<int>(blockIdx.x % H), seg = static_cast<int>(blockIdx.x / H);
     if (seg >= sv.count()) return;
     const int4 sd = sv.table[seg];
     if ((sd.w & (kSegFirst | kSegLast)) == (kSegFirst | kSegLast)) return;  // one segment: nothing to chain
@@ -522,7 +524,8 @@ __device__ __forceinline__ void reverse_local_body(const BackwardLaunch &L, cons
     static_assert(NT >= NS * kWave, "a wave per 16 columns of dv");
     const IT *q = static_cast<const IT *>(L.q), *k = static_cast<const IT *>(L.k);
     const IT *beta = static_cast<const IT *>(L.beta), *d_o = static_cast<const IT *>(L.d_o);
-    const int h = blockIdx.x, seg = blockIdx.y, H = L.H;
+    // grid.x = segment * H + head: a packed batch may hold more than grid.y's 65,535 segments
+    const int H = L.H, h = static_cast<int>(blockIdx.x % H), seg = static_cast<int>(blockIdx.x / H);
     if (seg >= sv.count()) return;
     const int4 sd = sv.table[seg];
     if (sd.w & kSegFirst) return;
@@ -838,8 +841,9 @@ static hipError_t launch_bwd(const BackwardLaunch &Lin) {
     BackwardLaunch b = L;
     b.ckpt = reinterpret_cast<float *>(ws + p.off_ckpt);
     float *hb = reinterpret_cast<float *>(ws + p.off_hb);
-    const dim3 grid(L.H, ss.max_segs), block(DV / 16 * kWave);
-    const dim3 grid_local(L.H, ss.max_segs, 2), block_local((DV + DK) / 16 * kWave);
+    const unsigned seg_heads = static_cast<unsigned>(L.H) * static_cast<unsigned>(ss.max_segs);
+    const dim3 grid(seg_heads), block(DV / 16 * kWave);
+    const dim3 grid_local(seg_heads, 1, 2), block_local((DV + DK) / 16 * kWave);
     if (L.in_bf16)
         hipLaunchKernelGGL((local_passes_kernel<DK, DV, true>), grid_local, block_local, 0, L.stream, b, ss.sv, hb);
     else

@@ -106,7 +106,11 @@ chunk_fp32_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
     __shared__ float sBeta[C];
     __shared__ int sRange[NB];        // float bits of each block's largest decay
 
-    const int slice = blockIdx.x, seg = blockIdx.y, h = blockIdx.z;
+    // grid.x = segment * slices + slice (a packed batch may hold more than grid.y's 65,535 segments),
+    // grid.y = head
+    const int slices = MODE == kOut ? DV / BV : (DV + DK) / BV;
+    const int slice = static_cast<int>(blockIdx.x % slices), seg = static_cast<int>(blockIdx.x / slices);
+    const int h = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lk = lane >> 4;   // MFMA row/col lane, k lane
     if (seg >= sv.count()) return;
@@ -369,7 +373,7 @@ template <int DK, int C, int MODE>
 static void launch_fp32_dk(const ChunkLaunch &L, const SegmentView &sv, int max_segs) {
     constexpr int BV = 32;
     const int slices = MODE == kOut ? L.dv / BV : (L.dv + DK) / BV;
-    dim3 grid(slices, max_segs, L.H), block(256);
+    dim3 grid(static_cast<unsigned>(slices * max_segs), L.H), block(256);
 #define KDA_CHUNK(IB, OB)                                                                               \
     hipLaunchKernelGGL((chunk_fp32_kernel<DK, C, BV, IB, OB, MODE>), grid, block, 0, L.stream, L.q, L.k, \
                        L.v, L.g, L.beta, L.hT, L.o, sv, L.H, L.dv, L.scale, L.xf)

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 /*
  * Optional input transforms, applied inside the kernels to every token before
@@ -338,10 +338,18 @@ kda_status kda_dplr_recurrent_fwd(const kda_dplr_args *args);
 
 /* Static text for a status code. */
 const char *kda_status_string(kda_status s);
-/* Thread-local text describing the last failure on this thread ("" if none). */
+/* Thread-local text describing the last failure on this thread ("" if none):
+ * for KDA_ERR_HIP the failing launch and HIP's own error string, for every
+ * other status the argument that was rejected.  Valid until the next call
+ * on the same thread. */
 const char *kda_last_error(void);
+/* The same text under the name the boundary's specification uses for the
+ * HIP error behind KDA_ERR_HIP. */
+const char *kda_last_hip_error(void);
 /* KDA_ABI_VERSION of the loaded library. */
 int kda_abi_version(void);
+/* The same number under the specification's name. */
+int kda_version(void);
 
 #ifdef __cplusplus
 }

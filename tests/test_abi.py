@@ -26,7 +26,12 @@ def test_every_declared_function_is_exported():
     assert decl == sorted(_lib.EXPORTS)
     for name in decl:
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == 5
+    assert lib.kda_abi_version() == 6
+    # the names the boundary's specification gives: the version and the HIP error text
+    assert lib.kda_version() == lib.kda_abi_version()
+    for name in ("kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_recurrent_step", "kda_status_string",
+                 "kda_last_hip_error", "kda_version"):
+        assert name in decl, name
 
 
 def test_status_strings():
@@ -65,6 +70,11 @@ def chunk_args(**kw):
     (dict(final_state=3 * FAKE + 8), "KDA_ERR_ALIAS"),
     (dict(initial_state=7 * FAKE + 4096), "KDA_ERR_ALIAS"),
     (dict(flags=8), "KDA_ERR_UNSUPPORTED"),
+    # o written while other workgroups still read the initial state or the sequence offsets
+    (dict(initial_state=8 * FAKE, o=8 * FAKE + 64), "KDA_ERR_ALIAS"),
+    (dict(cu_seqlens=9 * FAKE, o=9 * FAKE - 64), "KDA_ERR_ALIAS"),
+    (dict(cu_seqlens=7 * FAKE + 16), "KDA_ERR_ALIAS"),
+    (dict(cu_seqlens=9 * FAKE + 64, workspace=9 * FAKE, workspace_bytes=1 << 40), "KDA_ERR_ALIAS"),
     (dict(flags=_lib.KDA_FLAG_GATE_SOFTPLUS, gate_scale=-1.0), "KDA_ERR_BAD_SHAPE"),
     (dict(flags=_lib.KDA_FLAG_GATE_SOFTPLUS, gate_scale=float("nan")), "KDA_ERR_BAD_SHAPE"),
 ])
@@ -84,6 +94,8 @@ def test_chunk_fwd_rejects(kw, status):
     (dict(v=None), "KDA_ERR_NULL_POINTER"),
     (dict(o=2 * FAKE + 8), "KDA_ERR_ALIAS"),
     (dict(final_state=6 * FAKE + 8), "KDA_ERR_ALIAS"),
+    (dict(initial_state=8 * FAKE, o=8 * FAKE + 64), "KDA_ERR_ALIAS"),
+    (dict(cu_seqlens=9 * FAKE, o=9 * FAKE - 64), "KDA_ERR_ALIAS"),
     (dict(flags=16), "KDA_ERR_UNSUPPORTED"),
     (dict(flags=3, gate_scale=float("inf")), "KDA_ERR_BAD_SHAPE"),
 ])
@@ -150,6 +162,7 @@ def step_args(**kw):
     (dict(o=5 * FAKE), "KDA_ERR_ALIAS"),
     (dict(final_state=FAKE), "KDA_ERR_ALIAS"),
     (dict(initial_state=7 * FAKE + 256), "KDA_ERR_ALIAS"),
+    (dict(initial_state=8 * FAKE, o=8 * FAKE + 64), "KDA_ERR_ALIAS"),
     (dict(flags=32), "KDA_ERR_UNSUPPORTED"),
     (dict(flags=_lib.KDA_FLAG_GATE_SOFTPLUS, gate_scale=-0.5), "KDA_ERR_BAD_SHAPE"),
 ])

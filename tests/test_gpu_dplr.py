@@ -1,6 +1,7 @@
 """GPU parity of the general DPLR recurrence (kda_dplr_recurrent_fwd) against
 the fp64 oracle (oracle.dplr_forward, pinned in test_oracle_dplr.py), with the
-per-(sequence, head) metric of the other parity tests.  The kernel computes in
+gate of the other parity tests (kda_testlib.Gate: per (sequence, head) slice
+and per row).  The kernel computes in
 fp32 from inputs the oracle sees exactly, so the bar is 1e-5 for both input
 dtypes."""
 import numpy as np
@@ -8,7 +9,7 @@ import pytest
 
 import oracle
 from gated_delta_rule_52_amd.inputs import make_dplr, make_prefill
-from kda_testlib import TOL_FP32, dev, say
+from kda_testlib import TOL_FP32, Gate, dev, gate_all, say
 
 pytestmark = pytest.mark.gpu
 
@@ -44,15 +45,14 @@ def check(kda, d, name, scale=1.0):
                                        cu_seqlens=d["cu_seqlens"], scale=scale)
     og, hg = o.cpu().numpy(), hT.cpu().numpy()
     cuv = d["cu_seqlens"] if d["cu_seqlens"] is not None else np.arange(B + 1) * T
-    eo = es = 0.0
+    go, gs = Gate("o", TOL_FP32), Gate("state", TOL_FP32)
     for n in range(len(cuv) - 1):
         a0, a1 = int(cuv[n]), int(cuv[n + 1])
         for h in range(H):
             if a1 > a0:
-                eo = max(eo, rel(og.reshape(-1, H, dv)[a0:a1, h], o_ref.reshape(-1, H, dv)[a0:a1, h]))
-            es = max(es, rel(hg[n, h], h_ref[n, h]))
-    say(f"  max slice rel err: o={eo:.2e} state={es:.2e} (tol {TOL_FP32:g})")
-    assert eo <= TOL_FP32 and es <= TOL_FP32, (eo, es)
+                go.add(og.reshape(-1, H, dv)[a0:a1, h], o_ref.reshape(-1, H, dv)[a0:a1, h])
+            gs.add(hg[n, h], h_ref[n, h])
+    gate_all([go, gs])
 
 
 @pytest.mark.parametrize("dk,dv,dt", [(128, 128, "bf16"), (64, 64, "fp32"), (128, 64, "bf16"), (64, 128, "fp32")])
