@@ -26,7 +26,8 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 # Every function declared in include/kda.h.
 EXPORTS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_fwd", "kda_recurrent_step",
            "kda_recurrent_bwd_workspace_bytes", "kda_recurrent_bwd", "kda_dplr_recurrent_fwd",
-           "kda_status_string", "kda_last_error", "kda_last_hip_error", "kda_abi_version", "kda_version")
+           "kda_status_string", "kda_last_error", "kda_last_hip_error", "kda_abi_version", "kda_version",
+           "kda_chunk_fwd_noalloc", "kda_chunk_fwd_noalloc_max_workspace_bytes")
 
 vp = ctypes.c_void_p
 
@@ -132,6 +133,10 @@ def load():
         lib.kda_abi_version.argtypes = []
         lib.kda_version.restype = ctypes.c_int
         lib.kda_version.argtypes = []
+        lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
+        lib.kda_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(ChunkFwdArgs)]
+        lib.kda_chunk_fwd_noalloc_max_workspace_bytes.restype = ctypes.c_size_t
+        lib.kda_chunk_fwd_noalloc_max_workspace_bytes.argtypes = []
         _lib = lib
     return _lib
 
@@ -144,6 +149,11 @@ def check(status: int):
 def chunk_fwd_raw(args: ChunkFwdArgs) -> int:
     args.struct_size = ctypes.sizeof(ChunkFwdArgs)
     return load().kda_chunk_fwd(ctypes.byref(args))
+
+
+def chunk_fwd_noalloc_raw(args: ChunkFwdArgs) -> int:
+    args.struct_size = ctypes.sizeof(ChunkFwdArgs)
+    return load().kda_chunk_fwd_noalloc(ctypes.byref(args))
 
 
 def chunk_workspace_raw(args: ChunkFwdArgs) -> int:

@@ -180,6 +180,8 @@ kda_status read_bwd_args(const kda_recurrent_bwd_args *a, kda_recurrent_bwd_args
 
 }  // namespace
 
+void kda::set_last_error(const char *text) { g_last_error = text; }
+
 extern "C" {
 
 const char *kda_status_string(kda_status s) {

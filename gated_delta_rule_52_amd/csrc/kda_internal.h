@@ -170,4 +170,7 @@ void launch_prep(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int 
 template <int MODE>
 void launch_scan(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, const void *packs);
 
+// Sets the thread-local text that kda_last_error() returns (kda_api.cpp).
+void set_last_error(const char *text);
+
 }  // namespace kda

@@ -131,6 +131,44 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     return o, final_state
 
 
+def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                      beta: torch.Tensor, o: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                      final_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
+                      scale: float = 1.0, chunk_size: int = 64, qk_l2norm: bool = False,
+                      gate_logits: bool = False, gate_scale: float = 1.0,
+                      scalar_gate: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``chunk_fwd`` through kda_chunk_fwd_noalloc: the caller passes every
+    output (o, and final_state when wanted), and the library's built-in
+    scratch replaces the workspace, so nothing is allocated on this path.
+    Problems whose workspace exceeds the built-in scratch raise KdaError
+    (KDA_ERR_WORKSPACE_TOO_SMALL).  Returns (o, final_state)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported input dtype {dt}")
+    _need(q, "q", (B, T, H, dk), dt)
+    _need(k, "k", (B, T, H, dk), dt)
+    _need(v, "v", (B, T, H, dv), dt)
+    _need(g, "g", (B, T, H) if scalar_gate else (B, T, H, dk), torch.float32)
+    _need(beta, "beta", (B, T, H), dt)
+    N = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32)
+        N = cu_seqlens.numel() - 1
+    if initial_state is not None:
+        _need(initial_state, "initial_state", (N, H, dk, dv), torch.float32)
+    if final_state is not None:
+        _need(final_state, "final_state", (N, H, dk, dv), torch.float32)
+    if o.dtype not in _DT:
+        raise ValueError(f"unsupported output dtype {o.dtype}")
+    _need(o, "o", (B, T, H, dv), o.dtype)
+    a = _fill_chunk_args(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, scale,
+                         chunk_size, None, 0, _flags(qk_l2norm, gate_logits, scalar_gate), gate_scale)
+    _lib.check(_lib.chunk_fwd_noalloc_raw(a))
+    return o, final_state
+
+
 def recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                   beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
                   cu_seqlens: Optional[torch.Tensor] = None, scale: float = 1.0,

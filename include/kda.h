@@ -336,6 +336,31 @@ typedef struct {
 
 kda_status kda_dplr_recurrent_fwd(const kda_dplr_args *args);
 
+/*
+ * kda_chunk_fwd without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results, aliasing
+ * rules and errors as kda_chunk_fwd, except that `workspace` and
+ * `workspace_bytes` are ignored: the scratch lives in a device array of
+ * KDA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends.  Nothing is allocated, freed or synchronised.
+ *
+ * Limit: problems whose kda_chunk_fwd_workspace_bytes() exceeds
+ * KDA_NOALLOC_SCRATCH_BYTES are rejected with KDA_ERR_WORKSPACE_TOO_SMALL
+ * before any launch.  With bf16 inputs and dk = dv = 128 the operand packs
+ * bound it: 2,048 tokens x 16 heads fit, 2,560 do not.  The fp32 path keeps
+ * only segment states there: 65,536 tokens x 16 heads at dk = dv = 128 fit.
+ *
+ * Every call on one GPU uses that GPU's array: calls that overlap in time on
+ * the same GPU (different streams or host threads) race and must be
+ * serialised by the caller.  The array keeps the last call's contents; none
+ * of it needs to start at zero.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kda_status kda_chunk_fwd_noalloc(const kda_chunk_fwd_args *args);
+/* KDA_NOALLOC_SCRATCH_BYTES of the loaded library. */
+size_t kda_chunk_fwd_noalloc_max_workspace_bytes(void);
+
 /* Static text for a status code. */
 const char *kda_status_string(kda_status s);
 /* Thread-local text describing the last failure on this thread ("" if none):

@@ -89,7 +89,7 @@ def test_decode_steps(kda, dk, dv, dt):
     tol = TOL_FP32 if dt == "fp32" else TOL_BF16
     S = dev(S0, torch.float32)
     ref = S0.astype(np.float64)
-    go, gs = Gate("o", tol), Gate("state", tol)
+    g_o, g_s = Gate("o", tol), Gate("state", tol)
     for t in range(steps):
         o = kda.recurrent_step(dev(P["q"][t], tdt), dev(P["k"][t], tdt), dev(P["v"][t], tdt),
                                dev(P["g"][t], torch.float32), dev(P["beta"][t], tdt), S,
@@ -100,10 +100,10 @@ def test_decode_steps(kda, dk, dv, dt):
         og, sg = o.cpu().numpy(), S.cpu().numpy()
         for n in range(N):
             for h in range(H):
-                go.add(og[n, h][None], o_ref[n, h][None])
-                gs.add(sg[n, h], ref[n, h])
+                g_o.add(og[n, h][None], o_ref[n, h][None])
+                g_s.add(sg[n, h], ref[n, h])
     say(f"case decode transforms dk={dk} dv={dv} {dt}, {steps} steps")
-    gate_all([go, gs])
+    gate_all([g_o, g_s])
 
 
 # ------------------------------------------- scalar gate (Gated DeltaNet's gate)
