@@ -10,9 +10,10 @@ Prints ONE JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-append] [--no-fused]
                     [--no-backward] [--no-cpu] [--calibrate-copy]
 
---calibrate-copy adds, before the timed region, one elementwise copy kernel
-of a known size (256 MiB read + 256 MiB written): its FETCH_SIZE / WRITE_SIZE
-counters give the scale for the operator's measured HBM traffic.
+--calibrate-copy adds, before the timed region, one launch of the streaming
+copy kernel (libkda_ceilings.so) of a known size (256 MiB read + 256 MiB
+written): its FETCH_SIZE / WRITE_SIZE counters give the scale for the
+operator's measured HBM traffic.
 """
 from __future__ import annotations
 
@@ -30,6 +31,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, vendor figure
+# forward flops per token and head from the Kimi Linear review notes' complexity section,
+# 6 d^2 + 3 C d + C^2 at d = 128, C = 64
+PAGES_FLOPS_PER_TOKEN_HEAD = 6 * 128 * 128 + 3 * 64 * 128 + 64 * 64
 METRIC = "KDA prefill tokens/s (H=16,d=128,T=64K) + decode step us/token, % roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fwd_prefill_64k_traffic.md")
 
@@ -110,13 +115,18 @@ def time_prefill(args, name="prefill_64k", calibrate=False, sweep=None):
     step = lambda: kda.chunk_fwd(q, k, v, g, beta, initial_state=h0, final_state=hT, o=o,
                                  out_dtype=bf, workspace=ws, **tr)
     if calibrate:
-        # an elementwise kernel (not a runtime blit) so the counters see it
+        # the streaming copy kernel of libkda_ceilings.so (not a runtime blit), so the counters see it
+        lib = ctypes.CDLL(os.path.join(ROOT, "gated_delta_rule_52_amd", "libkda_ceilings.so"))
+        lib.kda_ceiling_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                         ctypes.c_void_p]
         a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
         torch.cuda.synchronize()
-        torch.neg(a, out=b)
+        assert lib.kda_ceiling_copy(a.data_ptr(), b.data_ptr(), 256 << 20, 0,
+                                    torch.cuda.current_stream().cuda_stream) == 0
         torch.cuda.synchronize()
-        log("calibration copy (neg kernel): 268435456 B read, 268435456 B written")
+        del a, b
+        log("calibration copy (copy_kernel<false>): 268435456 B read, 268435456 B written")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -161,6 +171,10 @@ def time_prefill(args, name="prefill_64k", calibrate=False, sweep=None):
 
 
 def time_decode(args):
+    """The decode workload, 1024 consecutive steps, two ways: in place (one
+    state buffer of 256 MiB, as a serving cache updates it) and ping-pong
+    (step s reads buffer s % 2 and writes the other: 512 MiB of state, twice
+    the 256 MiB Infinity Cache, so the state streams from HBM)."""
     import torch
     from gated_delta_rule_52_amd import _lib
     from gated_delta_rule_52_amd.inputs import WORKLOADS, make_decode_state, decode_step_pool
@@ -177,19 +191,22 @@ def time_decode(args):
     v = torch.from_numpy(P["v"]).to(dev).to(bf)[idx].contiguous()
     g = torch.from_numpy(P["g"]).to(dev)[idx].contiguous()
     beta = torch.from_numpy(P["beta"]).to(dev).to(bf)[idx].contiguous()
-    S = torch.from_numpy(S0).to(dev)
+    S = [torch.from_numpy(S0).to(dev), torch.from_numpy(S0).to(dev)]
     o = torch.empty((steps, N, H, dv), dtype=bf, device=dev)
     lib = _lib.load()
     stream = torch.cuda.current_stream()
 
-    def make_args(strm):
+    def make_args(strm, ping_pong):
         keep = []
         for s in range(steps):
             a = _lib.RecurrentStepArgs()
             a.struct_size = ctypes.sizeof(_lib.RecurrentStepArgs)
             a.q, a.k, a.v = q[s].data_ptr(), k[s].data_ptr(), v[s].data_ptr()
             a.g, a.beta = g[s].data_ptr(), beta[s].data_ptr()
-            a.initial_state = a.final_state = S.data_ptr()
+            if ping_pong:
+                a.initial_state, a.final_state = S[s % 2].data_ptr(), S[(s + 1) % 2].data_ptr()
+            else:
+                a.initial_state = a.final_state = S[0].data_ptr()
             a.o = o[s].data_ptr()
             a.N, a.H, a.dk, a.dv, a.scale = N, H, dk, dv, 1.0
             a.in_dtype = a.out_dtype = _lib.KDA_DTYPE_BF16
@@ -197,29 +214,30 @@ def time_decode(args):
             keep.append(a)
         return keep
 
-    refs = make_args(stream)
-
-    def run_all(args=refs):
+    def run_all(args):
         for a in args:
             rc = lib.kda_recurrent_step(ctypes.byref(a))
             if rc:
                 _lib.check(rc)
 
-    run_all()  # warm-up pass (advances the state; timing does not depend on values)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    run_all()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = 1e3 * e0.elapsed_time(e1) / steps
-    log(f"decode: {us:.2f} us/step over {steps} steps")
-    # the same steps captured once into a HIP graph and replayed
+    res = {}
+    for mode in ("ping_pong", "in_place"):
+        refs = make_args(stream, mode == "ping_pong")
+        run_all(refs)  # warm-up pass (advances the state; timing does not depend on values)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run_all(refs)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[mode] = 1e3 * e0.elapsed_time(e1) / steps
+        log(f"decode ({mode}): {res[mode]:.2f} us/step over {steps} steps")
+    # the in-place steps captured once into a HIP graph and replayed
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(stream)
     with torch.cuda.graph(graph, stream=side):
-        run_all(make_args(torch.cuda.current_stream()))
+        run_all(make_args(torch.cuda.current_stream(), False))
     graph.replay()
     torch.cuda.synchronize()
     e0.record(stream)
@@ -227,9 +245,56 @@ def time_decode(args):
     e1.record(stream)
     torch.cuda.synchronize()
     us_graph = 1e3 * e0.elapsed_time(e1) / steps
-    log(f"decode under a graph: {us_graph:.2f} us/step")
-    return dict(N=N, H=H, dk=dk, dv=dv, steps=steps, us=us, us_graph=us_graph,
-                nbytes=decode_alg_bytes(N, H, dk, dv))
+    log(f"decode (in place) under a graph: {us_graph:.2f} us/step")
+    return dict(N=N, H=H, dk=dk, dv=dv, steps=steps, us=res["ping_pong"], us_in_place=res["in_place"],
+                us_graph=us_graph, nbytes=decode_alg_bytes(N, H, dk, dv))
+
+
+def time_prefill_own(args, name, cold_flush_bytes=512 << 20):
+    """kda_chunk_fwd on a named workload with its own recipe (its seed, its
+    initial state or none, final states written, bf16 o), ms per call: warm
+    (calls back to back) and cold (each call after writing a 512 MiB buffer,
+    which evicts the inputs from the 256 MiB Infinity Cache)."""
+    import torch
+    import gated_delta_rule_52_amd as kda
+    from gated_delta_rule_52_amd.inputs import make_workload
+    x = make_workload(name)
+    dev = "cuda:0"
+    bf, f32 = torch.bfloat16, torch.float32
+    t = lambda a, dt: torch.from_numpy(a).to(dev).to(dt)
+    q, k, v, beta, g = t(x.q, bf), t(x.k, bf), t(x.v, bf), t(x.beta, bf), t(x.g, f32)
+    h0 = None if x.h0 is None else t(x.h0, f32)
+    cu = None if x.cu_seqlens is None else t(x.cu_seqlens, torch.int32)
+    hT = torch.empty((x.N, x.H, x.dk, x.dv), dtype=f32, device=dev)
+    o = torch.empty((x.B, x.T, x.H, x.dv), dtype=bf, device=dev)
+    ws = torch.empty(kda.chunk_fwd_workspace_bytes(q, v, cu), dtype=torch.uint8, device=dev)
+    call = lambda: kda.chunk_fwd(q, k, v, g, beta, initial_state=h0, final_state=hT, o=o, cu_seqlens=cu,
+                                 out_dtype=bf, workspace=ws)
+    stream = torch.cuda.current_stream()
+    for _ in range(max(args.warmup, 3)):
+        call()
+    torch.cuda.synchronize()
+    reps = max(args.steps, 10)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm = e0.elapsed_time(e1) / reps
+    flush = torch.empty(cold_flush_bytes // 4, dtype=f32, device=dev)
+    cold = []
+    for _ in range(reps):
+        flush.fill_(1.0)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+    nbytes = prefill_alg_bytes(1, x.B * x.T, x.H, x.dk, x.dv, x.N, h0=h0 is not None, hT=True)
+    log(f"{name}: {x.B * x.T} tokens, warm {warm * 1e3:.1f} us, cold median {np.median(cold) * 1e3:.1f} us")
+    return x, warm, float(np.median(cold)), nbytes
 
 
 def append_alg_bytes(N, T, H, dk, dv, in_bytes=2, out_bytes=2):
@@ -423,26 +488,95 @@ def time_dplr(args):
     return res
 
 
-def copy_ceiling():
-    """HBM bandwidth a plain elementwise kernel reaches on this GPU: 1 GiB read
-    and 1 GiB written per launch (torch's neg kernel), best of 10 launches."""
+def time_dplr_chunk(args, x):
+    """KDA against the general DPLR recurrence, both in chunkwise form on the same fp32 matrix-core harness
+    (chunks of 32, same segment plan and combine) over the 64K prefill: B=1, T=65536, H=16, d=128, bf16
+    inputs.  The DPLR call gets a = beta k and b = exp(g) * k (KDA's member of the family; the kernel does
+    not know they are tied).  ms per call of each, and the ratio."""
     import torch
-    a = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
-    b = torch.empty_like(a)
-    for _ in range(2):
-        torch.neg(a, out=b)
-    best = float("inf")
-    for _ in range(10):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        torch.neg(a, out=b)
-        e1.record()
+    import gated_delta_rule_52_amd as kda
+    dev = "cuda:0"
+    bf, f32 = torch.bfloat16, torch.float32
+    t = lambda a, dt: torch.from_numpy(a).to(dev).to(dt)
+    q, k, v, beta, g, h0 = t(x.q, bf), t(x.k, bf), t(x.v, bf), t(x.beta, bf), t(x.g, f32), t(x.h0, f32)
+    a = (beta.float()[..., None] * k.float()).to(bf)
+    b = (torch.exp(g) * k.float()).to(bf)
+    hT = torch.empty_like(h0)
+    o = torch.empty((x.B, x.T, x.H, x.dv), dtype=bf, device=dev)
+    ws_k = torch.empty(kda.chunk_fwd_workspace_bytes(q, v, chunk_size=32), dtype=torch.uint8, device=dev)
+    paths = {
+        "kda_chunk_fwd_c32_fp32_path": lambda: kda.chunk_fwd(q, k, v, g, beta, initial_state=h0, final_state=hT,
+                                                             o=o, out_dtype=bf, workspace=ws_k, chunk_size=32),
+        "dplr_chunk_fwd_c32": lambda: kda.dplr_chunk_fwd(q, a, v, g, a, b, initial_state=h0, final_state=hT, o=o,
+                                                         out_dtype=bf),
+    }
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fn in paths.items():
+        fn()
         torch.cuda.synchronize()
-        best = min(best, e0.elapsed_time(e1))
-    gbs = 2 * a.numel() * 4 / (best * 1e-3) / 1e9
-    log(f"copy ceiling: {gbs:.0f} GB/s")
+        reps = 3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / reps
+        log(f"chunk harness {name}: {res[name]:.3f} ms per call")
+    return res
+
+
+def ceilings():
+    """Measured ceilings from this build's own kernels (libkda_ceilings.so):
+    a streaming copy of 1 GiB read + 1 GiB written per launch (plain and
+    non-temporal loads/stores, best launch of either), and a bf16 matrix-core
+    loop (8 independent 16x16x32 products per wave, 2,048 workgroups of 4
+    waves, no memory traffic).  Returns (copy GB/s, MFMA TFLOP/s, details)."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "gated_delta_rule_52_amd", "libkda_ceilings.so"))
+    lib.kda_ceiling_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    lib.kda_ceiling_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.kda_ceiling_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.kda_ceiling_mfma_flops.restype = ctypes.c_double
+    stream = torch.cuda.current_stream()
+    nbytes = 1 << 30
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    best = {}
+    for nt in (0, 1):
+        for _ in range(2):
+            assert lib.kda_ceiling_copy(a.data_ptr(), b.data_ptr(), nbytes, nt, stream.cuda_stream) == 0
+        t = float("inf")
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            lib.kda_ceiling_copy(a.data_ptr(), b.data_ptr(), nbytes, nt, stream.cuda_stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = min(t, e0.elapsed_time(e1))
+        best["nontemporal" if nt else "plain"] = 2 * nbytes / (t * 1e-3) / 1e9
+    torch.cuda.synchronize()
+    assert bool(torch.equal(a[:1024], b[:1024])), "copy ceiling kernel did not copy"
     del a, b
-    return gbs
+    blocks, iters = 2048, 4000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    lib.kda_ceiling_mfma(out.data_ptr(), blocks, 100, stream.cuda_stream)
+    tm = float("inf")
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        assert lib.kda_ceiling_mfma(out.data_ptr(), blocks, iters, stream.cuda_stream) == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        tm = min(tm, e0.elapsed_time(e1))
+    tflops = lib.kda_ceiling_mfma_flops(blocks, iters) / (tm * 1e-3) / 1e12
+    del out
+    copy_gbs = max(best.values())
+    log(f"ceilings: copy {best} GB/s, bf16 MFMA loop {tflops:.0f} TFLOP/s")
+    return copy_gbs, tflops, dict(copy_gbs=best, copy_bytes_each_way=nbytes, mfma_tflops=tflops,
+                                  mfma="v_mfma_f32_16x16x32_bf16, 8 independent chains per wave, "
+                                       f"{blocks} workgroups x 4 waves x {iters} iterations")
 
 
 def cpu_baseline(x):
@@ -484,7 +618,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     sweep = None if args.no_fused else {}
     x, ms, per, nbytes = time_prefill(args, calibrate=args.calibrate_copy, sweep=sweep)
-    copy_gbs = copy_ceiling()
+    copy_gbs, mfma_tflops, ceil = ceilings()
     tok_s = x.B * x.T / (ms * 1e-3)
     ach = nbytes / (ms * 1e-3) / 1e9
     traffic = stored_traffic()
@@ -502,21 +636,45 @@ def main():
                      "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
                      "measured_copy_gbs": copy_gbs, "frac_of_measured_copy": ach / copy_gbs,
                      "alg_bytes_per_launch": nbytes,
+                     "pages_flops_per_launch": PAGES_FLOPS_PER_TOKEN_HEAD * x.B * x.T * x.H,
+                     "mfma_frac_of_bf16_peak": PAGES_FLOPS_PER_TOKEN_HEAD * x.B * x.T * x.H / (ms * 1e-3) / 1e12
+                                               / BF16_MFMA_PEAK_TFLOPS,
                      "kernel": "kda_chunk_fwd: one call = segment table, prep, local scan, "
                                "combine, output scan (timed together on the library's stream)"},
     }
+    rec["ceilings"] = ceil
     if not args.no_decode:
         d = time_decode(args)
         dach = d["nbytes"] / (d["us"] * 1e-6) / 1e9
+        dach_ip = d["nbytes"] / (d["us_in_place"] * 1e-6) / 1e9
         rec["decode"] = {
-            "workload": "decode_256x16", "us_per_step": d["us"], "us_per_step_graph": d["us_graph"],
-            "us_per_token_step": d["us"], "us_per_token_amortized": d["us"] / d["N"],
-            "tokens_per_s": d["N"] / (d["us"] * 1e-6),
-            "steps": d["steps"],
+            "workload": "decode_256x16", "state_buffers": "ping-pong: step s reads buffer s%2, writes the other "
+                                                          "(512 MiB of state, beyond the 256 MiB Infinity Cache)",
+            "us_per_step": d["us"], "us_per_token_step": d["us"], "us_per_token_amortized": d["us"] / d["N"],
+            "tokens_per_s": d["N"] / (d["us"] * 1e-6), "steps": d["steps"],
             "roofline": {"bound": "hbm", "achieved": dach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": dach / HBM_PEAK_GBS, "alg_bytes_per_launch": d["nbytes"],
                          "measured_copy_gbs": copy_gbs, "frac_of_measured_copy": dach / copy_gbs},
+            "in_place": {"us_per_step": d["us_in_place"], "us_per_step_graph": d["us_graph"],
+                         "note": "one 256 MiB state buffer updated in place: the Infinity Cache can serve part of it",
+                         "achieved_gbs": dach_ip, "frac": dach_ip / HBM_PEAK_GBS},
         }
+    for key, wl in (("prefill_4k", "prefill_4k"), ("varlen", "varlen_8seq")):
+        xo, warm, cold, obytes = time_prefill_own(args, wl)
+        toks = xo.B * xo.T
+        rec[key] = {
+            "workload": wl, "tokens": toks, "H": xo.H, "N": xo.N, "initial_state": xo.h0 is not None,
+            "ms_per_call_warm": warm, "ms_per_call_cold": cold,
+            "tokens_per_s_warm": toks / (warm * 1e-3), "tokens_per_s_cold": toks / (cold * 1e-3),
+            "roofline": {"bound": "hbm", "alg_bytes_per_launch": obytes, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "achieved_cold": obytes / (cold * 1e-3) / 1e9,
+                         "frac_cold": obytes / (cold * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "achieved_warm": obytes / (warm * 1e-3) / 1e9,
+                         "frac_warm": obytes / (warm * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        }
+        if xo.cu_seqlens is not None:
+            rec[key]["seqlens"] = np.diff(xo.cu_seqlens).tolist()
+        del xo
     if not (args.no_decode or args.no_append):
         xa, ra, abytes = time_append(args)
         best = min(ra, key=ra.get)
@@ -560,6 +718,13 @@ def main():
         rec["dplr"] = {
             "workload": "256 sequences x 16 heads x 64 new tokens, dk=dv=128, bf16, cached states; token by token",
             "us_per_call": rd, "dplr_over_kda": rd["dplr_recurrent_fwd"] / rd["kda_recurrent_fwd"],
+        }
+        rc = time_dplr_chunk(args, x)
+        rec["dplr_chunk"] = {
+            "workload": "prefill_64k inputs (B=1, T=65536, H=16, dk=dv=128, bf16, h0), chunkwise, fp32 matrix-core "
+                        "harness with chunks of 32; DPLR gets a = beta k, b = exp(g) k",
+            "ms_per_call": rc, "dplr_over_kda": rc["dplr_chunk_fwd_c32"] / rc["kda_chunk_fwd_c32_fp32_path"],
+            "pages_ratio": 59.22 / 29.83,
         }
         rec["append_grid"] = {
             "workload": "N sequences x T new tokens, 16 heads, dk=dv=128, bf16, cached states (key 'NxT')",

@@ -27,7 +27,8 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 EXPORTS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_fwd", "kda_recurrent_step",
            "kda_recurrent_bwd_workspace_bytes", "kda_recurrent_bwd", "kda_dplr_recurrent_fwd",
            "kda_status_string", "kda_last_error", "kda_last_hip_error", "kda_abi_version", "kda_version",
-           "kda_chunk_fwd_noalloc", "kda_chunk_fwd_noalloc_max_workspace_bytes")
+           "kda_chunk_fwd_noalloc", "kda_chunk_fwd_noalloc_max_workspace_bytes", "kda_dplr_chunk_fwd",
+           "kda_dplr_chunk_fwd_workspace_bytes")
 
 vp = ctypes.c_void_p
 
@@ -91,6 +92,20 @@ class DplrArgs(ctypes.Structure):
     ]
 
 
+class DplrChunkArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("q", vp), ("k", vp), ("v", vp), ("g", vp), ("a", vp), ("b", vp),
+        ("initial_state", vp), ("final_state", vp), ("o", vp), ("cu_seqlens", vp),
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+        ("workspace", vp), ("workspace_bytes", ctypes.c_size_t),
+        ("stream", vp),
+    ]
+
+
 class KdaError(RuntimeError):
     def __init__(self, status: int, message: str):
         self.status = status
@@ -137,6 +152,10 @@ def load():
         lib.kda_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(ChunkFwdArgs)]
         lib.kda_chunk_fwd_noalloc_max_workspace_bytes.restype = ctypes.c_size_t
         lib.kda_chunk_fwd_noalloc_max_workspace_bytes.argtypes = []
+        lib.kda_dplr_chunk_fwd.restype = ctypes.c_int
+        lib.kda_dplr_chunk_fwd.argtypes = [ctypes.POINTER(DplrChunkArgs)]
+        lib.kda_dplr_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.kda_dplr_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(DplrChunkArgs)]
         _lib = lib
     return _lib
 
@@ -149,6 +168,16 @@ def check(status: int):
 def chunk_fwd_raw(args: ChunkFwdArgs) -> int:
     args.struct_size = ctypes.sizeof(ChunkFwdArgs)
     return load().kda_chunk_fwd(ctypes.byref(args))
+
+
+def dplr_chunk_fwd_raw(args: DplrChunkArgs) -> int:
+    args.struct_size = ctypes.sizeof(DplrChunkArgs)
+    return load().kda_dplr_chunk_fwd(ctypes.byref(args))
+
+
+def dplr_chunk_workspace_raw(args: DplrChunkArgs) -> int:
+    args.struct_size = ctypes.sizeof(DplrChunkArgs)
+    return load().kda_dplr_chunk_fwd_workspace_bytes(ctypes.byref(args))
 
 
 def chunk_fwd_noalloc_raw(args: ChunkFwdArgs) -> int:

@@ -18,13 +18,20 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
 SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_chunk.hip", "kda_segments.hip", "kda_prep.hip",
-           "kda_scan.hip", "kda_backward.hip", "kda_dplr.hip", "kda_noalloc.hip"]
+           "kda_scan.hip", "kda_backward.hip", "kda_dplr.hip", "kda_dplr_chunk.hip", "kda_noalloc.hip"]
+# measured ceilings (streaming copy, matrix-core loop) for the benchmark's roofline figures: a library of
+# their own, outside the operator's ABI
+CEIL_LIB = os.path.join(HERE, "libkda_ceilings.so")
+CEIL_SOURCES = ["kda_ceilings.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wno-unused-function",
     # no packed-fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: without it the register allocator keeps them in AGPRs
+    # and copies them back and forth around loops (a bf16 MFMA loop ran at half rate)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 
@@ -36,8 +43,9 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, jobs: int = 0) -> str:
-    """Compile every HIP source into libkda.so (always recompiles)."""
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1, 16)
+    """Compile every HIP source into libkda.so and libkda_ceilings.so (always
+    recompiles); returns the path of libkda.so."""
+    jobs = jobs or min(len(SOURCES) + len(CEIL_SOURCES), os.cpu_count() or 1, 16)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     with tempfile.TemporaryDirectory(prefix="kda_build_") as tmpdir:
         def compile_one(src):
@@ -49,7 +57,7 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
             return src, obj, r.returncode, r.stdout
 
         with ThreadPoolExecutor(max_workers=jobs) as ex:
-            results = list(ex.map(compile_one, SOURCES))
+            results = list(ex.map(compile_one, SOURCES + CEIL_SOURCES))
         failed = False
         for src, _, rc, out in results:
             # hipcc's host pass does not know the packed-fp32 feature and says so: harmless
@@ -59,12 +67,14 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
             failed |= rc != 0
         if failed:
             raise subprocess.CalledProcessError(1, "hipcc -c")
-        tmp = LIB + ".tmp"
-        cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[o for _, o, _, _ in results]]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+        objs = {src: o for src, o, _, _ in results}
+        for lib, srcs in ((LIB, SOURCES), (CEIL_LIB, CEIL_SOURCES)):
+            tmp = lib + ".tmp"
+            cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[objs[s] for s in srcs]]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.check_call(cmd)
+            os.replace(tmp, lib)
     return LIB
 
 

@@ -420,12 +420,14 @@ kda_status kda_recurrent_bwd(const kda_recurrent_bwd_args *user) {
     return hip_status(kda::launch_backward(L), "kda_recurrent_bwd launch");
 }
 
-kda_status kda_dplr_recurrent_fwd(const kda_dplr_args *user) {
-    g_last_error.clear();
-    if (!user) return fail(KDA_ERR_NULL_POINTER, "args is NULL");
-    if (user->struct_size != sizeof(kda_dplr_args))
-        return fail(KDA_ERR_BAD_STRUCT, "struct_size %u (expected %zu)", user->struct_size, sizeof(kda_dplr_args));
-    const kda_dplr_args *a = user;
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the token-level and chunkwise DPLR entry points (same field names).
+template <class A>
+kda_status check_dplr(const A *a, bool *nothing_to_do) {
+    *nothing_to_do = false;
     if (a->B < 0 || a->T < 0 || a->H <= 0 || a->num_seqs < 0)
         return fail(KDA_ERR_BAD_SHAPE, "B=%d T=%d H=%d num_seqs=%d", a->B, a->T, a->H, a->num_seqs);
     if (!valid_dim(a->dk) || !valid_dim(a->dv))
@@ -439,9 +441,14 @@ kda_status kda_dplr_recurrent_fwd(const kda_dplr_args *user) {
     const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
     if (tokens > INT32_MAX)
         return fail(KDA_ERR_BAD_SHAPE, "B*T=%lld tokens (at most %d)", static_cast<long long>(tokens), INT32_MAX);
+    if (tokens * a->H * (a->dk > a->dv ? a->dk : a->dv) > (int64_t{1} << 40))
+        return fail(KDA_ERR_BAD_SHAPE, "problem too large");
     const int N = a->num_seqs;
     if (N > 65535 || a->H > 65535) return fail(KDA_ERR_UNSUPPORTED, "N=%d H=%d (at most 65535 each)", N, a->H);
-    if (N == 0 || (tokens == 0 && !a->final_state)) return KDA_OK;
+    if (N == 0 || (tokens == 0 && !a->final_state)) {
+        *nothing_to_do = true;
+        return KDA_OK;
+    }
     if (tokens > 0 && (!a->q || !a->k || !a->v || !a->g || !a->a || !a->b || !a->o))
         return fail(KDA_ERR_NULL_POINTER, "q, k, v, g, a, b and o are required");
     const size_t th = static_cast<size_t>(tokens) * a->H, in_sz = dsize(a->in_dtype);
@@ -450,26 +457,95 @@ kda_status kda_dplr_recurrent_fwd(const kda_dplr_args *user) {
     const Range ins[] = {range_of(a->q, th * a->dk * in_sz), range_of(a->k, th * a->dk * in_sz),
                          range_of(a->v, th * a->dv * in_sz), range_of(a->g, th * a->dk * 4),
                          range_of(a->a, th * a->dk * in_sz), range_of(a->b, th * a->dk * in_sz)};
+    const Range rh0 = range_of(a->initial_state, a->initial_state ? sbytes : 0);
+    const Range rcu = range_of(a->cu_seqlens, a->cu_seqlens ? (static_cast<size_t>(N) + 1) * 4 : 0);
     for (const Range &r : ins)
         if (overlap(ro, r)) return fail(KDA_ERR_ALIAS, "o overlaps an input");
+    if (overlap(ro, rh0)) return fail(KDA_ERR_ALIAS, "o overlaps initial_state");
+    if (overlap(ro, rcu)) return fail(KDA_ERR_ALIAS, "o overlaps cu_seqlens");
     if (a->final_state) {
         const Range rf = range_of(a->final_state, sbytes);
         for (const Range &r : ins)
             if (overlap(rf, r)) return fail(KDA_ERR_ALIAS, "final_state overlaps an input");
         if (overlap(rf, ro)) return fail(KDA_ERR_ALIAS, "final_state overlaps o");
-        if (a->initial_state && a->initial_state != a->final_state &&
-            overlap(rf, range_of(a->initial_state, sbytes)))
+        if (overlap(rf, rcu)) return fail(KDA_ERR_ALIAS, "final_state overlaps cu_seqlens");
+        if (a->initial_state && a->initial_state != a->final_state && overlap(rf, rh0))
             return fail(KDA_ERR_ALIAS, "final_state partially overlaps initial_state");
     }
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_dplr_recurrent_fwd(const kda_dplr_args *user) {
+    g_last_error.clear();
+    if (!user) return fail(KDA_ERR_NULL_POINTER, "args is NULL");
+    if (user->struct_size != sizeof(kda_dplr_args))
+        return fail(KDA_ERR_BAD_STRUCT, "struct_size %u (expected %zu)", user->struct_size, sizeof(kda_dplr_args));
+    const kda_dplr_args *a = user;
+    bool none = false;
+    const kda_status st = check_dplr(a, &none);
+    if (st != KDA_OK || none) return st;
     kda::DplrLaunch L{};
     L.q = a->q; L.k = a->k; L.v = a->v; L.a = a->a; L.b = a->b; L.g = a->g;
     L.h0 = a->initial_state; L.hT = a->final_state; L.o = a->o;
     L.cu_seqlens = a->cu_seqlens;
-    L.N = N; L.T = a->T; L.H = a->H; L.dk = a->dk; L.dv = a->dv; L.scale = a->scale;
+    L.N = a->num_seqs; L.T = a->T; L.H = a->H; L.dk = a->dk; L.dv = a->dv; L.scale = a->scale;
     L.in_bf16 = a->in_dtype == KDA_DTYPE_BF16;
     L.out_bf16 = a->out_dtype == KDA_DTYPE_BF16;
     L.stream = static_cast<hipStream_t>(a->stream);
     return hip_status(kda::launch_dplr(L), "kda_dplr_recurrent_fwd launch");
+}
+
+size_t kda_dplr_chunk_fwd_workspace_bytes(const kda_dplr_chunk_args *a) {
+    if (!a || a->struct_size != sizeof(kda_dplr_chunk_args)) return static_cast<size_t>(-1);
+    if (a->B < 0 || a->T < 0 || a->H <= 0 || a->num_seqs < 0 || !valid_dim(a->dk) || !valid_dim(a->dv))
+        return static_cast<size_t>(-1);
+    if (a->cu_seqlens ? a->B != 1 : a->num_seqs != a->B) return static_cast<size_t>(-1);
+    return kda::dplr_chunk_workspace_bytes(a->B, a->T, a->H, a->dk, a->dv, a->num_seqs, a->cu_seqlens != nullptr);
+}
+
+kda_status kda_dplr_chunk_fwd(const kda_dplr_chunk_args *user) {
+    g_last_error.clear();
+    if (!user) return fail(KDA_ERR_NULL_POINTER, "args is NULL");
+    if (user->struct_size != sizeof(kda_dplr_chunk_args))
+        return fail(KDA_ERR_BAD_STRUCT, "struct_size %u (expected %zu)", user->struct_size,
+                    sizeof(kda_dplr_chunk_args));
+    const kda_dplr_chunk_args *a = user;
+    bool none = false;
+    kda_status st = check_dplr(a, &none);
+    if (st != KDA_OK || none) return st;
+    const int N = a->num_seqs;
+    const size_t need = kda::dplr_chunk_workspace_bytes(a->B, a->T, a->H, a->dk, a->dv, N, a->cu_seqlens != nullptr);
+    if (a->workspace_bytes < need || (need > 0 && !a->workspace))
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", a->workspace_bytes, need);
+    {   // the workspace must not overlap any input or output
+        const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
+        const size_t th = static_cast<size_t>(tokens) * a->H, in_sz = dsize(a->in_dtype);
+        const size_t sbytes = static_cast<size_t>(N) * a->H * a->dk * a->dv * 4;
+        const Range rw = range_of(a->workspace, need);
+        const Range others[] = {range_of(a->q, th * a->dk * in_sz), range_of(a->k, th * a->dk * in_sz),
+                                range_of(a->v, th * a->dv * in_sz), range_of(a->g, th * a->dk * 4),
+                                range_of(a->a, th * a->dk * in_sz), range_of(a->b, th * a->dk * in_sz),
+                                range_of(a->o, th * a->dv * dsize(a->out_dtype)),
+                                range_of(a->initial_state, a->initial_state ? sbytes : 0),
+                                range_of(a->final_state, a->final_state ? sbytes : 0),
+                                range_of(a->cu_seqlens, a->cu_seqlens ? (static_cast<size_t>(N) + 1) * 4 : 0)};
+        for (const Range &r : others)
+            if (overlap(rw, r)) return fail(KDA_ERR_ALIAS, "workspace overlaps an input or output");
+    }
+    kda::DplrChunkLaunch L{};
+    L.q = a->q; L.k = a->k; L.v = a->v; L.a = a->a; L.b = a->b; L.g = a->g;
+    L.h0 = a->initial_state; L.hT = a->final_state; L.o = a->o;
+    L.cu_seqlens = a->cu_seqlens;
+    L.B = a->B; L.T = a->T; L.H = a->H; L.dk = a->dk; L.dv = a->dv; L.N = N; L.scale = a->scale;
+    L.in_bf16 = a->in_dtype == KDA_DTYPE_BF16;
+    L.out_bf16 = a->out_dtype == KDA_DTYPE_BF16;
+    L.workspace = a->workspace;
+    L.stream = static_cast<hipStream_t>(a->stream);
+    return hip_status(kda::launch_dplr_chunk(L), "kda_dplr_chunk_fwd launch");
 }
 
 }  // extern "C"

@@ -767,7 +767,7 @@ struct BwdPlan {
 BwdPlan bwd_plan(int B, int T, int H, int dk, int dv, int N, bool varlen, bool transforms, bool scalar_gate) {
     BwdPlan p{};
     auto a256 = [](size_t x) { return (x + 255) & ~size_t{255}; };
-    const size_t seg_bytes = segment_states_bytes(B, T, H, dk, dv, N, varlen);
+    const size_t seg_bytes = segment_states_bytes(B, T, H, dk, dv, N, varlen, 64);
     // the same bound on segments as the segmented forward's plan: at most one more than tokens / 64 per
     // sequence, and at least one
     const int64_t tokens = varlen ? T : static_cast<int64_t>(B) * T;

@@ -94,6 +94,18 @@ __device__ __forceinline__ void slice_head_seq(int &slice, int &h, int &n) {
     n = static_cast<int>(gi / gridDim.y);
 }
 
+// Non-temporal 16-byte load and store, for data a kernel streams exactly once
+// each way (a decode step's state): the hint keeps it from displacing lines
+// that are reused, such as the token inputs every workgroup of a head reads.
+typedef float nt_f4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream(const float *p) {
+    const nt_f4 x = __builtin_nontemporal_load(reinterpret_cast<const nt_f4 *>(p));
+    return make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void store_stream(float *p, float4 v) {
+    __builtin_nontemporal_store(nt_f4{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_f4 *>(p));
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);

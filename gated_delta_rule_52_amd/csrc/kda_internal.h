@@ -156,9 +156,12 @@ void launch_fp32_pass(const ChunkLaunch &L, const SegmentView &sv, int max_segs)
 struct SegmentStates {
     SegmentView sv;
     int max_segs;  // bound on the number of segments (grid size)
+    int seg_len;   // tokens per segment
 };
-size_t segment_states_bytes(int B, int T, int H, int dk, int dv, int N, bool varlen);
+size_t segment_states_bytes(int B, int T, int H, int dk, int dv, int N, bool varlen, int chunk);
+// the segment table of a plan at chunk size L.chunk, without operand packs
 SegmentStates launch_segment_table(const ChunkLaunch &L);
+// the combine into entering states; sequences without tokens get final = initial in L.hT (when given)
 void launch_segment_combine(const ChunkLaunch &L, const SegmentStates &s);
 
 // fp16/bf16 matrix-core path (bf16 inputs, dk = dv = 128, chunk 64): a
@@ -169,6 +172,24 @@ size_t pack_bytes();  // bytes of one operand pack
 void launch_prep(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, void *packs);
 template <int MODE>
 void launch_scan(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, const void *packs);
+
+// The general DPLR recurrence in chunkwise form (kda_dplr_chunk.hip), on the segment machinery above.
+struct DplrChunkLaunch {
+    const void *q, *k, *v, *a, *b;
+    const float *g;
+    const float *h0;
+    float *hT;
+    void *o;
+    const int32_t *cu_seqlens;  // device, or nullptr: B sequences of T tokens
+    int B, T, H, dk, dv, N;
+    float scale;
+    bool in_bf16, out_bf16;
+    void *workspace;            // dplr_chunk_workspace_bytes()
+    hipStream_t stream;
+};
+int dplr_chunk_size();
+size_t dplr_chunk_workspace_bytes(int B, int T, int H, int dk, int dv, int N, bool varlen);
+hipError_t launch_dplr_chunk(const DplrChunkLaunch &L);
 
 // Sets the thread-local text that kda_last_error() returns (kda_api.cpp).
 void set_last_error(const char *text);

@@ -485,13 +485,13 @@ hipError_t launch_chunk(const ChunkLaunch &L) {
     return hipGetLastError();
 }
 
-size_t segment_states_bytes(int B, int T, int H, int dk, int dv, int N, bool varlen) {
-    return make_plan(B, T, H, dk, dv, N, 64, varlen, false).bytes;
+size_t segment_states_bytes(int B, int T, int H, int dk, int dv, int N, bool varlen, int chunk) {
+    return make_plan(B, T, H, dk, dv, N, chunk, varlen, false).bytes;
 }
 
 SegmentStates launch_segment_table(const ChunkLaunch &L) {
     const bool varlen = L.cu_seqlens != nullptr;
-    const Plan p = make_plan(L.B, L.T, L.H, L.dk, L.dv, L.N, 64, varlen, false);
+    const Plan p = make_plan(L.B, L.T, L.H, L.dk, L.dv, L.N, L.chunk, varlen, false);
     char *ws = static_cast<char *>(L.workspace);
     SegmentStates r{};
     SegmentView &sv = r.sv;
@@ -505,6 +505,7 @@ SegmentStates launch_segment_table(const ChunkLaunch &L) {
     sv.xcount = nullptr;
     sv.xlist = nullptr;
     r.max_segs = p.max_segs;
+    r.seg_len = p.seg_len;
     hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(256), 0, L.stream, L.cu_seqlens, L.T, L.N,
                        p.seg_len, reinterpret_cast<int4 *>(ws + p.off_table),
                        reinterpret_cast<int32_t *>(ws + p.off_seq), nullptr);
@@ -514,10 +515,10 @@ SegmentStates launch_segment_table(const ChunkLaunch &L) {
 void launch_segment_combine(const ChunkLaunch &L, const SegmentStates &s) {
     if (L.dk == 128)
         hipLaunchKernelGGL(combine_mfma_kernel, dim3(L.H, L.dv / 16, L.N), dim3(256), 0, L.stream, s.sv, L.h0,
-                           static_cast<float *>(nullptr), L.H, L.dv);
+                           L.hT, L.H, L.dv);
     else
         hipLaunchKernelGGL(combine_kernel<64>, dim3(L.dv / 16, L.H, L.N), dim3(256), 0, L.stream, s.sv, L.h0,
-                           static_cast<float *>(nullptr), L.H, L.dv);
+                           L.hT, L.H, L.dv);
 }
 
 }  // namespace kda

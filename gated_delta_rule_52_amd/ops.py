@@ -384,3 +384,54 @@ def dplr_recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: tor
     x.stream = _stream(q.device)
     _lib.check(_lib.dplr_fwd_raw(x))
     return o, final_state
+
+
+def dplr_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                   a: torch.Tensor, b: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                   cu_seqlens: Optional[torch.Tensor] = None, scale: float = 1.0,
+                   out_dtype: Optional[torch.dtype] = None, output_final_state: bool = True,
+                   final_state: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None):
+    """The general DPLR recurrence of ``dplr_recurrent_fwd`` in chunkwise form (kda_dplr_chunk_fwd):
+    same arguments and results, plus an optional caller workspace.  Returns (o, final_state)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported input dtype {dt}")
+    for name, t in (("q", q), ("k", k), ("a", a), ("b", b)):
+        _need(t, name, (B, T, H, dk), dt)
+    _need(v, "v", (B, T, H, dv), dt)
+    _need(g, "g", (B, T, H, dk), torch.float32)
+    N = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32)
+        N = cu_seqlens.numel() - 1
+    if initial_state is not None:
+        _need(initial_state, "initial_state", (N, H, dk, dv), torch.float32)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif final_state is not None:
+        _need(final_state, "final_state", (N, H, dk, dv), torch.float32)
+    od = out_dtype or dt
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=od, device=q.device)
+    else:
+        _need(o, "o", (B, T, H, dv), od)
+    x = _lib.DplrChunkArgs()
+    x.q, x.k, x.v, x.g, x.a, x.b = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(a), _ptr(b)
+    x.initial_state, x.final_state, x.o = _ptr(initial_state), _ptr(final_state), _ptr(o)
+    x.cu_seqlens = _ptr(cu_seqlens)
+    x.B, x.T, x.H, x.dk, x.dv, x.num_seqs = B, T, H, dk, dv, N
+    x.scale = float(scale)
+    x.in_dtype, x.out_dtype = _DT[dt], _DT[od]
+    ws = _lib.dplr_chunk_workspace_raw(x)
+    if ws == 2 ** 64 - 1:
+        _lib.check(_lib.STATUS_CODE["KDA_ERR_BAD_SHAPE"])
+    if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
+        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+    x.workspace = _ptr(workspace) if ws > 0 else None
+    x.workspace_bytes = int(ws)
+    x.stream = _stream(q.device)
+    _lib.check(_lib.dplr_chunk_fwd_raw(x))
+    return o, final_state

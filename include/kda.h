@@ -337,6 +337,59 @@ typedef struct {
 kda_status kda_dplr_recurrent_fwd(const kda_dplr_args *args);
 
 /*
+ * The same general DPLR recurrence in chunkwise-parallel form, on fp32
+ * matrix cores, in the harness of kda_chunk_fwd's fp32 path (same segment
+ * table, local and output passes, combine).  The Kimi Linear review notes
+ * (section "Chunkwise Algorithm") time KDA's chunk operator against general
+ * DPLR's at about half the time; the jxzklqfsx.com article's efficiency
+ * section puts the difference in the chunk algorithm: four secondary-chunk
+ * products for the general form against two for KDA, and three more matrix
+ * products.  Here, per chunk of C rows with cumulative log decay G
+ * (G_{-1} = 0) and entering state S:
+ *
+ *   B_k[r,i] = b_r.(k_i e^{G_{r-1}-G_i}), B_a[r,i] = b_r.(a_i e^{G_{r-1}-G_i})   (i <  r)
+ *   A_qk[r,i]= q_r.(k_i e^{G_r-G_i}),     A_qa[r,i]= q_r.(a_i e^{G_r-G_i})       (i <= r)
+ *   X = (I + B_a)^{-1} ((b e^{G_{r-1}}) S + B_k V)       (the rows x_r = S_{r-1}^T b_r)
+ *   O = scale ((q e^G) S + A_qk V - A_qa X)
+ *   S <- e^{G_L} S + (e^{G_L - G} k)^T V - (e^{G_L - G} a)^T X
+ *
+ * Chunks of 32 tokens: five [C][dk] fp32 operands sit in LDS at once, which
+ * at dk = 128 fits only C = 32.  Results equal kda_dplr_recurrent_fwd's up
+ * to rounding.
+ *
+ * Arguments as kda_dplr_args, plus a workspace of at least
+ * kda_dplr_chunk_fwd_workspace_bytes() bytes (contents on entry ignored, on
+ * exit unspecified; must not overlap any input or output).  final_state may
+ * equal initial_state.
+ */
+typedef struct {
+    uint32_t struct_size; /* = sizeof(kda_dplr_chunk_args) */
+    const void *q;
+    const void *k;
+    const void *v;
+    const float *g;
+    const void *a;
+    const void *b;
+    const float *initial_state;
+    float *final_state;
+    void *o;
+    const int32_t *cu_seqlens;
+    int32_t B, T, H, dk, dv, num_seqs;
+    float scale;
+    kda_dtype in_dtype;  /* dtype of q, k, v, a, b */
+    kda_dtype out_dtype; /* dtype of o */
+    void *workspace;
+    size_t workspace_bytes;
+    void *stream; /* hipStream_t */
+} kda_dplr_chunk_args;
+
+/* Bytes of workspace kda_dplr_chunk_fwd needs (host-only; only the size
+ * fields are read).  Returns (size_t)-1 when the arguments are invalid. */
+size_t kda_dplr_chunk_fwd_workspace_bytes(const kda_dplr_chunk_args *args);
+
+kda_status kda_dplr_chunk_fwd(const kda_dplr_chunk_args *args);
+
+/*
  * kda_chunk_fwd without a caller workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, results, aliasing

@@ -280,3 +280,46 @@ def test_dplr_struct_size_and_empty_call():
     a.struct_size = ctypes.sizeof(_lib.DplrArgs) + 8
     assert lib.kda_dplr_recurrent_fwd(ctypes.byref(a)) == S["KDA_ERR_BAD_STRUCT"]
     assert _lib.dplr_fwd_raw(dplr_args(B=0, num_seqs=0)) == 0
+
+
+def dplr_chunk_args(**kw):
+    a = _lib.DplrChunkArgs()
+    base = dict(q=FAKE, k=2 * FAKE, v=3 * FAKE, g=4 * FAKE, a=5 * FAKE, b=6 * FAKE, initial_state=7 * FAKE,
+                final_state=7 * FAKE, o=8 * FAKE, cu_seqlens=None, B=2, T=64, H=2, dk=128, dv=128, num_seqs=2,
+                scale=1.0, in_dtype=_lib.KDA_DTYPE_BF16, out_dtype=_lib.KDA_DTYPE_FP32,
+                workspace=9 * FAKE, workspace_bytes=1 << 30)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=32), "KDA_ERR_UNSUPPORTED"),
+    (dict(in_dtype=4), "KDA_ERR_UNSUPPORTED"),
+    (dict(H=0), "KDA_ERR_BAD_SHAPE"),
+    (dict(num_seqs=3), "KDA_ERR_BAD_SHAPE"),
+    (dict(a=None), "KDA_ERR_NULL_POINTER"),
+    (dict(o=5 * FAKE + 16), "KDA_ERR_ALIAS"),                 # inside a
+    (dict(initial_state=7 * FAKE + 64), "KDA_ERR_ALIAS"),     # partial overlap with final_state
+    (dict(workspace_bytes=1000), "KDA_ERR_WORKSPACE_TOO_SMALL"),
+    (dict(workspace=None), "KDA_ERR_WORKSPACE_TOO_SMALL"),
+    (dict(workspace=8 * FAKE + 4096), "KDA_ERR_ALIAS"),       # inside o
+    (dict(workspace=7 * FAKE), "KDA_ERR_ALIAS"),              # the states
+])
+def test_dplr_chunk_rejects(kw, status):
+    rc = _lib.dplr_chunk_fwd_raw(dplr_chunk_args(**kw))
+    assert rc == S[status], (_lib.STATUS.get(rc), _lib.load().kda_last_error())
+    assert _lib.load().kda_last_error().decode() != ""
+
+
+def test_dplr_chunk_workspace_and_struct():
+    lib = _lib.load()
+    n1 = _lib.dplr_chunk_workspace_raw(dplr_chunk_args(T=1000))
+    n2 = _lib.dplr_chunk_workspace_raw(dplr_chunk_args(T=100000))
+    assert 0 < n1 < n2 < 2 ** 64 - 1
+    assert _lib.dplr_chunk_workspace_raw(dplr_chunk_args(dk=32)) == 2 ** 64 - 1
+    a = dplr_chunk_args()
+    a.struct_size = ctypes.sizeof(_lib.DplrChunkArgs) - 8
+    assert lib.kda_dplr_chunk_fwd(ctypes.byref(a)) == S["KDA_ERR_BAD_STRUCT"]
+    assert _lib.dplr_chunk_fwd_raw(dplr_chunk_args(B=0, num_seqs=0)) == 0
