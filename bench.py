@@ -320,6 +320,8 @@ def time_append(args):
     paths = {
         "recurrent_fwd": lambda: kda.recurrent_fwd(q, k, v, g, beta, initial_state=h0, final_state=hT, o=o,
                                                    out_dtype=bf),
+        "recurrent_fwd_token_by_token": lambda: kda.recurrent_fwd(q, k, v, g, beta, initial_state=h0, final_state=hT,
+                                                                  o=o, out_dtype=bf, token_by_token=True),
         "chunk_fwd": lambda: kda.chunk_fwd(q, k, v, g, beta, initial_state=h0, final_state=hT, o=o,
                                            out_dtype=bf, workspace=ws),
     }
@@ -362,7 +364,10 @@ def time_append_grid():
             for name, fn in (("chunk_fwd", lambda: kda.chunk_fwd(q, k, v, g, beta, initial_state=h0, final_state=hT,
                                                                   o=o, out_dtype=bf, workspace=ws)),
                              ("recurrent_fwd", lambda: kda.recurrent_fwd(q, k, v, g, beta, initial_state=h0,
-                                                                          final_state=hT, o=o, out_dtype=bf))):
+                                                                          final_state=hT, o=o, out_dtype=bf)),
+                             ("token_by_token", lambda: kda.recurrent_fwd(q, k, v, g, beta, initial_state=h0,
+                                                                           final_state=hT, o=o, out_dtype=bf,
+                                                                           token_by_token=True))):
                 for _ in range(3):
                     fn()
                 torch.cuda.synchronize()
@@ -374,7 +379,8 @@ def time_append_grid():
                 torch.cuda.synchronize()
                 row[name] = 1e3 * e0.elapsed_time(e1) / 20
             grid[f"{N}x{T}"] = row
-            log(f"append grid N={N} T={T}: chunk_fwd {row['chunk_fwd']:.1f} us, recurrent_fwd {row['recurrent_fwd']:.1f} us")
+            log(f"append grid N={N} T={T}: chunk_fwd {row['chunk_fwd']:.1f} us, recurrent_fwd {row['recurrent_fwd']:.1f} us "
+                f"(token by token {row['token_by_token']:.1f} us)")
     return grid
 
 
@@ -467,7 +473,8 @@ def time_dplr(args):
     hT = torch.empty_like(kh)
     o = torch.empty((x.B, x.T, x.H, x.dv), dtype=bf, device="cuda:0")
     paths = {
-        "kda_recurrent_fwd": lambda: kda.recurrent_fwd(kq, kk, kv, kg, kb, initial_state=kh, final_state=hT, o=o),
+        "kda_recurrent_fwd": lambda: kda.recurrent_fwd(kq, kk, kv, kg, kb, initial_state=kh, final_state=hT, o=o,
+                                                       token_by_token=True),
         "dplr_recurrent_fwd": lambda: kda.dplr_recurrent_fwd(dq, dk_, dv_, dg, da, db, initial_state=dh,
                                                              final_state=hT, o=o),
     }

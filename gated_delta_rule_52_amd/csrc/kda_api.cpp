@@ -286,6 +286,17 @@ kda_status kda_recurrent_fwd(const kda_chunk_fwd_args *user) {
     if (st != KDA_OK) return st;
     const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
     if (a->num_seqs == 0 || (tokens == 0 && !a->final_state)) return KDA_OK;
+    // Appends of more than kRouteTokens tokens per sequence (on average) run faster chunkwise (measured on
+    // MI355X, 16 heads, d = 128: the token kernel wins up to about 16 new tokens per sequence, the chunk path
+    // from 64 on).  With a caller workspace big enough for kda_chunk_fwd (chunk 64) such a call goes there;
+    // without one it stays token by token, so no workspace is ever required.
+    constexpr int64_t kRouteTokens = 16;
+    if (a->workspace && tokens > kRouteTokens * a->num_seqs) {
+        kda_chunk_fwd_args c = *a;
+        c.chunk_size = 64;
+        const size_t need = kda_chunk_fwd_workspace_bytes(&c);
+        if (need != static_cast<size_t>(-1) && a->workspace_bytes >= need) return kda_chunk_fwd(&c);
+    }
 
     kda::RecurrentLaunch L{};
     L.q = a->q; L.k = a->k; L.v = a->v; L.g = a->g; L.beta = a->beta;

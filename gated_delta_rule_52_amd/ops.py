@@ -175,10 +175,14 @@ def recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   out_dtype: Optional[torch.dtype] = None, output_final_state: bool = True,
                   final_state: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
                   qk_l2norm: bool = False, gate_logits: bool = False, gate_scale: float = 1.0,
-                  scalar_gate: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Token-by-token fused recurrent forward for short segments (at most a few
-    dozen tokens per sequence): the same arguments, shapes, input transforms and
-    results as ``chunk_fwd`` (no chunk size, no workspace).  Returns (o, final_state)."""
+                  scalar_gate: bool = False, token_by_token: bool = False,
+                  workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Fused recurrent forward for short segments: the same arguments, shapes,
+    input transforms and results as ``chunk_fwd`` (no chunk size).  Calls with
+    more than 16 tokens per sequence on average are handed a chunk workspace,
+    with which kda_recurrent_fwd runs the faster chunkwise path; with
+    ``token_by_token`` no workspace is passed and the token kernel always runs.
+    Returns (o, final_state)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
@@ -204,7 +208,13 @@ def recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         o = torch.empty((B, T, H, dv), dtype=od, device=q.device)
     else:
         _need(o, "o", (B, T, H, dv), od)
+    ws = 0
+    if not token_by_token and B * T > 16 * N:
+        ws = chunk_fwd_workspace_bytes(q, v, cu_seqlens, 64)
+        if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
+            workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
     a = _fill_chunk_args(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, scale, 64,
+                         workspace if ws > 0 else None, ws,
                          flags=_flags(qk_l2norm, gate_logits, scalar_gate), gate_scale=gate_scale)
     _lib.check(_lib.recurrent_fwd_raw(a))
     return o, final_state

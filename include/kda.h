@@ -164,8 +164,12 @@ kda_status kda_chunk_fwd(const kda_chunk_fwd_args *args);
  * about 64 on.
  *
  * Arguments, shapes, dtypes, aliasing rules and errors are those of
- * kda_chunk_fwd; chunk_size, workspace and workspace_bytes are ignored (no
- * workspace is used).
+ * kda_chunk_fwd; chunk_size is ignored.  The workspace is optional: when
+ * workspace is given with at least kda_chunk_fwd_workspace_bytes() bytes for
+ * chunk size 64 and the call carries more than 16 tokens per sequence on
+ * average, it runs kda_chunk_fwd (chunk 64) instead, the faster path there;
+ * its results then carry kda_chunk_fwd's rounding.  Without a workspace (or
+ * a large enough one) the call always runs token by token.
  */
 kda_status kda_recurrent_fwd(const kda_chunk_fwd_args *args);
 

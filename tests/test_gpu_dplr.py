@@ -78,7 +78,7 @@ def test_dplr_kda_case_matches_kda_kernel(kda):
     b = (np.exp(x.g) * x.k).astype(np.float32)
     f = lambda z: dev(z, torch.float32)
     od, hd = kda.dplr_recurrent_fwd(f(x.q), f(a), f(x.v), f(x.g), f(a), f(b), initial_state=f(x.h0))
-    ok, hk = kda.recurrent_fwd(f(x.q), f(x.k), f(x.v), f(x.g), f(x.beta), initial_state=f(x.h0))
+    ok, hk = kda.recurrent_fwd(f(x.q), f(x.k), f(x.v), f(x.g), f(x.beta), initial_state=f(x.h0), token_by_token=True)
     torch.cuda.synchronize()
     eo, es = rel(od.cpu().numpy(), ok.cpu().numpy()), rel(hd.cpu().numpy(), hk.cpu().numpy())
     say(f"case dplr_kda_case: o={eo:.2e} state={es:.2e}")

@@ -22,21 +22,22 @@ def kda():
     return m
 
 
-def run(kda, x, scale=1.0, out_dtype=None, initial=True):
+def run(kda, x, scale=1.0, out_dtype=None, initial=True, token_by_token=True):
     import torch
     d = upload(x)
     o, hT = kda.recurrent_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"],
                               initial_state=d["h0"] if initial else None, cu_seqlens=d["cu"],
-                              scale=scale, out_dtype=out_dtype or torch.float32)
+                              scale=scale, out_dtype=out_dtype or torch.float32, token_by_token=token_by_token)
     torch.cuda.synchronize()
     return o, hT
 
 
-def check(kda, x, scale=1.0):
+def check(kda, x, scale=1.0, token_by_token=True):
     tol = TOL_FP32 if x.in_dtype == "fp32" else TOL_BF16
     heads = list(range(x.H))
-    say(f"case {x.name}: B={x.B} T={x.T} H={x.H} dk={x.dk} dv={x.dv} N={x.N} dtype={x.in_dtype}")
-    o, hT = run(kda, x, scale=scale)
+    say(f"case {x.name}: B={x.B} T={x.T} H={x.H} dk={x.dk} dv={x.dv} N={x.N} dtype={x.in_dtype} "
+        f"token_by_token={token_by_token}")
+    o, hT = run(kda, x, scale=scale, token_by_token=token_by_token)
     o_ref, h_ref = oracle_forward(x, heads, scale=scale)
     check_prefill_outputs(o.cpu().numpy(), hT.cpu().numpy(), o_ref, h_ref, x, heads, tol)
 
@@ -70,10 +71,10 @@ def test_in_place_state_and_bf16_output(kda):
     x = make_prefill(85, 2, 48, 2, 128, 128, h0_std=0.3, name="in_place")
     d = upload(x)
     args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
-    o32a, ha = kda.recurrent_fwd(*args, initial_state=d["h0"], out_dtype=torch.float32)
-    o32b, hb = kda.recurrent_fwd(*args, initial_state=d["h0"], out_dtype=torch.float32)
+    o32a, ha = kda.recurrent_fwd(*args, initial_state=d["h0"], out_dtype=torch.float32, token_by_token=True)
+    o32b, hb = kda.recurrent_fwd(*args, initial_state=d["h0"], out_dtype=torch.float32, token_by_token=True)
     S = d["h0"].clone()
-    o16, _ = kda.recurrent_fwd(*args, initial_state=S, final_state=S, out_dtype=torch.bfloat16)
+    o16, _ = kda.recurrent_fwd(*args, initial_state=S, final_state=S, out_dtype=torch.bfloat16, token_by_token=True)
     torch.cuda.synchronize()
     assert torch.equal(o32a, o32b) and torch.equal(ha, hb), "not deterministic"
     assert torch.equal(S, ha), "in-place final state differs"
@@ -130,3 +131,21 @@ def test_heads_grouped_per_xcd(kda, dk, dv, dt):
     are mapped so that a head's dv slices share one XCD, over several groups
     of 8; parity is unchanged."""
     check(kda, make_prefill(88, 4, 20, 8, dk, dv, in_dtype=dt, h0_std=0.3, name=f"grouped_{dk}x{dv}"), scale=0.9)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_long_appends_take_the_chunk_path(kda, dt):
+    """More than 16 tokens per sequence with a chunk workspace: kda_recurrent_fwd
+    runs kda_chunk_fwd, with the same bits as calling it directly, and the
+    result passes the oracle's gate; without a workspace the token kernel runs
+    (and passes too)."""
+    import torch
+    x = make_prefill(89, 4, 48, 2, 128, 128, in_dtype=dt, h0_std=0.3, name=f"routed_{dt}")
+    check(kda, x, scale=0.9, token_by_token=False)
+    check(kda, x, scale=0.9, token_by_token=True)
+    d = upload(x)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    o_r, h_r = kda.recurrent_fwd(*args, initial_state=d["h0"], scale=0.9, out_dtype=torch.float32)
+    o_c, h_c = kda.chunk_fwd(*args, initial_state=d["h0"], scale=0.9, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o_r, o_c) and torch.equal(h_r, h_c), "routed call differs from kda_chunk_fwd"

@@ -39,9 +39,10 @@ def check(kda, x, path="chunk"):
     say(f"case {x.name} ({path}): B={x.B} T={x.T} H={x.H} dk={x.dk} dv={x.dv} N={x.N} "
         f"dtype={x.in_dtype} transforms={x.transforms()}")
     d = upload(x)
+    extra = {} if path == "chunk" else dict(token_by_token=True)
     fn = kda.chunk_fwd if path == "chunk" else kda.recurrent_fwd
     o, hT = fn(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["h0"], cu_seqlens=d["cu"],
-               out_dtype=torch.float32, **x.transforms())
+               out_dtype=torch.float32, **x.transforms(), **extra)
     torch.cuda.synchronize()
     o_ref, h_ref = oracle_fused(x, heads)
     check_prefill_outputs(o.cpu().numpy(), hT.cpu().numpy(), o_ref, h_ref, x, heads, tol)
