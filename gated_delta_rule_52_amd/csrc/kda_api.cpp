@@ -239,6 +239,9 @@ kda_status kda_chunk_fwd(const kda_chunk_fwd_args *user) {
                                                    a->cu_seqlens != nullptr, a->in_dtype == KDA_DTYPE_BF16);
     if (a->workspace_bytes < need || (need > 0 && !a->workspace))
         return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", a->workspace_bytes, need);
+    if (!kda::chunk_grids_fit(a->B, a->T, a->H, a->dk, a->dv, N, a->chunk_size, a->cu_seqlens != nullptr,
+                              a->in_dtype == KDA_DTYPE_BF16))
+        return fail(KDA_ERR_UNSUPPORTED, "problem too large for one launch (more than 2^32 threads in a grid)");
     if (a->workspace) {
         const Range rw = range_of(a->workspace, need);
         for (const Range &r : ins)

@@ -105,6 +105,8 @@ struct ChunkLaunch {
 };
 
 size_t chunk_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int chunk, bool varlen, bool in_bf16);
+// false when one of the prefill's launches would exceed a grid dimension's 32-bit thread count
+bool chunk_grids_fit(int B, int T, int H, int dk, int dv, int N, int chunk, bool varlen, bool in_bf16);
 hipError_t launch_chunk(const ChunkLaunch &L);
 
 // ---- segmented prefill (kda_segments.hip)

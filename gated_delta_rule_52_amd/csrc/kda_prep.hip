@@ -644,7 +644,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
     }
 }
 
-// fast path: one workgroup per chunk and head; grid (segments x per, heads).
+// fast path: one workgroup per chunk and head; grid.x = (segment * per + chunk) * H + head.
 // XF: with the input transforms; SG: scalar gate (implies XF).
 template <bool XF, bool SG>
 __global__ void __launch_bounds__(NT, 3)
@@ -653,8 +653,12 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                   const uint16_t *__restrict__ beta, SegmentView sv, int per, int H, float scale,
                   char *__restrict__ packs, InputXform ix) {
     __shared__ PrepSmem sm;
-    prep_chunk<false, XF, SG>(sm, nullptr, nullptr, blockIdx.x, blockIdx.y, q, k, v, g, beta, sv, per, H, scale,
-                              packs, ix);
+    // heads fastest: the workgroups in flight at once cover whole token rows ([T, H, d]: a chunk's H heads
+    // read adjacent 256-byte pieces of the same rows) and write consecutive packs (measured at 64K x 16 heads:
+    // 1.028 -> 0.984 ms per call against chunks fastest)
+    const int h = static_cast<int>(blockIdx.x % static_cast<unsigned>(H));
+    const int bx = static_cast<int>(blockIdx.x / static_cast<unsigned>(H));
+    prep_chunk<false, XF, SG>(sm, nullptr, nullptr, bx, h, q, k, v, g, beta, sv, per, H, scale, packs, ix);
 }
 
 // exact path over the chunks the fast path listed (usually none)
@@ -689,15 +693,15 @@ void launch_prep(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int 
     const uint16_t *v = static_cast<const uint16_t *>(L.v), *b = static_cast<const uint16_t *>(L.beta);
     char *pk = static_cast<char *>(packs);
     if (L.xf.scalar_gate) {  // the scalar-gate Gram is exact at any decay: no exact pass
-        hipLaunchKernelGGL((mc::chunk_prep_kernel<true, true>), dim3(max_segs * per, L.H), dim3(mc::NT), 0, L.stream,
+        hipLaunchKernelGGL((mc::chunk_prep_kernel<true, true>), dim3(static_cast<unsigned>(max_segs) * static_cast<unsigned>(per) * L.H), dim3(mc::NT), 0, L.stream,
                            q, k, v, L.g, b, sv, per, L.H, L.scale, pk, L.xf);
     } else if (L.xf.any()) {
-        hipLaunchKernelGGL((mc::chunk_prep_kernel<true, false>), dim3(max_segs * per, L.H), dim3(mc::NT), 0, L.stream, q, k, v,
+        hipLaunchKernelGGL((mc::chunk_prep_kernel<true, false>), dim3(static_cast<unsigned>(max_segs) * static_cast<unsigned>(per) * L.H), dim3(mc::NT), 0, L.stream, q, k, v,
                            L.g, b, sv, per, L.H, L.scale, pk, L.xf);
         hipLaunchKernelGGL(mc::chunk_prep_exact_kernel<true>, dim3(256), dim3(mc::NT), 0, L.stream, q, k, v, L.g, b,
                            sv, per, L.H, L.scale, pk, L.xf);
     } else {
-        hipLaunchKernelGGL((mc::chunk_prep_kernel<false, false>), dim3(max_segs * per, L.H), dim3(mc::NT), 0, L.stream, q, k,
+        hipLaunchKernelGGL((mc::chunk_prep_kernel<false, false>), dim3(static_cast<unsigned>(max_segs) * static_cast<unsigned>(per) * L.H), dim3(mc::NT), 0, L.stream, q, k,
                            v, L.g, b, sv, per, L.H, L.scale, pk, L.xf);
         hipLaunchKernelGGL(mc::chunk_prep_exact_kernel<false>, dim3(256), dim3(mc::NT), 0, L.stream, q, k, v, L.g, b,
                            sv, per, L.H, L.scale, pk, L.xf);

@@ -441,6 +441,15 @@ size_t chunk_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int chu
     return make_plan(B, T, H, dk, dv, N, chunk, varlen, in_bf16).bytes;
 }
 
+bool chunk_grids_fit(int B, int T, int H, int dk, int dv, int N, int chunk, bool varlen, bool in_bf16) {
+    const Plan p = make_plan(B, T, H, dk, dv, N, chunk, varlen, in_bf16);
+    // a dispatch's grid size is a 32-bit count of threads per dimension; the largest 1-D grids are the
+    // prep's (chunk slots x heads workgroups of 256) and the fp32 local pass's (slices x segments of 256)
+    const uint64_t prep = static_cast<uint64_t>(p.max_segs) * p.per * H * 256;
+    const uint64_t fp32 = static_cast<uint64_t>(p.max_segs) * ((dv + dk) / 32) * 256;
+    return prep < (uint64_t{1} << 32) && fp32 < (uint64_t{1} << 32);
+}
+
 hipError_t launch_chunk(const ChunkLaunch &L) {
     const bool varlen = L.cu_seqlens != nullptr;
     const Plan p = make_plan(L.B, L.T, L.H, L.dk, L.dv, L.N, L.chunk, varlen, L.in_bf16);
