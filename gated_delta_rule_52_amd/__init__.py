@@ -7,7 +7,7 @@ and the current HIP stream; every step of the operator runs in libkda.so.
 """
 __all__ = ["chunk_fwd", "recurrent_fwd", "recurrent_step", "recurrent_bwd", "KdaError", "chunk_fwd_workspace_bytes",
            "recurrent_bwd_workspace_bytes", "dplr_recurrent_fwd", "chunk_fwd_noalloc",
-           "dplr_chunk_fwd"]
+           "dplr_chunk_fwd", "chunk_bwd", "chunk_bwd_workspace_bytes"]
 
 
 def __getattr__(name):

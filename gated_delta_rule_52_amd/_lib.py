@@ -25,7 +25,8 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 # Every function declared in include/kda.h.
 EXPORTS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_fwd", "kda_recurrent_step",
-           "kda_recurrent_bwd_workspace_bytes", "kda_recurrent_bwd", "kda_dplr_recurrent_fwd",
+           "kda_recurrent_bwd_workspace_bytes", "kda_recurrent_bwd", "kda_chunk_bwd_workspace_bytes",
+           "kda_chunk_bwd", "kda_dplr_recurrent_fwd",
            "kda_status_string", "kda_last_error", "kda_last_hip_error", "kda_abi_version", "kda_version",
            "kda_chunk_fwd_noalloc", "kda_chunk_fwd_noalloc_max_workspace_bytes", "kda_dplr_chunk_fwd",
            "kda_dplr_chunk_fwd_workspace_bytes")
@@ -136,6 +137,10 @@ def load():
         lib.kda_recurrent_bwd_workspace_bytes.argtypes = [ctypes.POINTER(RecurrentBwdArgs)]
         lib.kda_recurrent_bwd.restype = ctypes.c_int
         lib.kda_recurrent_bwd.argtypes = [ctypes.POINTER(RecurrentBwdArgs)]
+        lib.kda_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.kda_chunk_bwd_workspace_bytes.argtypes = [ctypes.POINTER(RecurrentBwdArgs)]
+        lib.kda_chunk_bwd.restype = ctypes.c_int
+        lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(RecurrentBwdArgs)]
         lib.kda_dplr_recurrent_fwd.restype = ctypes.c_int
         lib.kda_dplr_recurrent_fwd.argtypes = [ctypes.POINTER(DplrArgs)]
         lib.kda_status_string.restype = ctypes.c_char_p
@@ -208,6 +213,16 @@ def recurrent_bwd_raw(args: RecurrentBwdArgs) -> int:
 def recurrent_bwd_workspace_raw(args: RecurrentBwdArgs) -> int:
     args.struct_size = ctypes.sizeof(RecurrentBwdArgs)
     return load().kda_recurrent_bwd_workspace_bytes(ctypes.byref(args))
+
+
+def chunk_bwd_raw(args: RecurrentBwdArgs) -> int:
+    args.struct_size = ctypes.sizeof(RecurrentBwdArgs)
+    return load().kda_chunk_bwd(ctypes.byref(args))
+
+
+def chunk_bwd_workspace_raw(args: RecurrentBwdArgs) -> int:
+    args.struct_size = ctypes.sizeof(RecurrentBwdArgs)
+    return load().kda_chunk_bwd_workspace_bytes(ctypes.byref(args))
 
 
 def dplr_fwd_raw(args: DplrArgs) -> int:

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
 SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_chunk.hip", "kda_segments.hip", "kda_prep.hip",
-           "kda_scan.hip", "kda_backward.hip", "kda_dplr.hip", "kda_dplr_chunk.hip", "kda_noalloc.hip"]
+           "kda_scan.hip", "kda_backward.hip", "kda_dplr.hip", "kda_dplr_chunk.hip", "kda_noalloc.hip",
+           "kda_chunk_bwd.hip"]
 # measured ceilings (streaming copy, matrix-core loop) for the benchmark's roofline figures: a library of
 # their own, outside the operator's ABI
 CEIL_LIB = os.path.join(HERE, "libkda_ceilings.so")

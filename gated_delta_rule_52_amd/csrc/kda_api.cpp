@@ -178,6 +178,51 @@ kda_status read_bwd_args(const kda_recurrent_bwd_args *a, kda_recurrent_bwd_args
     return check_bwd_sizes(&out);
 }
 
+// Buffer checks of the gradient entry points (null pointers, workspace size, overlaps); tokens > 0 or a
+// requested initial-state gradient.
+kda_status check_bwd_buffers(const kda_recurrent_bwd_args *a, size_t need) {
+    const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
+    const int N = a->num_seqs;
+    if (tokens > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->grad_o || !a->grad_q || !a->grad_k ||
+                       !a->grad_v || !a->grad_g || !a->grad_beta))
+        return fail(KDA_ERR_NULL_POINTER, "q, k, v, g, beta, grad_o and every token gradient are required");
+    const size_t th = static_cast<size_t>(tokens) * a->H, in_sz = dsize(a->in_dtype);
+    const size_t gw = (a->flags & KDA_FLAG_SCALAR_GATE) ? 1 : static_cast<size_t>(a->dk);
+    const size_t sbytes = static_cast<size_t>(N) * a->H * a->dk * a->dv * 4;
+    if (a->workspace_bytes < need || (need > 0 && !a->workspace))
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", a->workspace_bytes, need);
+    const Range ins[] = {range_of(a->q, th * a->dk * in_sz), range_of(a->k, th * a->dk * in_sz),
+                         range_of(a->v, th * a->dv * in_sz), range_of(a->g, th * gw * 4),
+                         range_of(a->beta, th * in_sz), range_of(a->grad_o, th * a->dv * in_sz),
+                         range_of(a->cu_seqlens, a->cu_seqlens ? (static_cast<size_t>(N) + 1) * 4 : 0)};
+    const Range outs[] = {range_of(a->grad_q, th * a->dk * 4), range_of(a->grad_k, th * a->dk * 4),
+                          range_of(a->grad_v, th * a->dv * 4), range_of(a->grad_g, th * gw * 4),
+                          range_of(a->grad_beta, th * 4), range_of(a->workspace, need)};
+    const Range rh0 = range_of(a->initial_state, a->initial_state ? sbytes : 0);
+    const Range rdhT = range_of(a->grad_final_state, a->grad_final_state ? sbytes : 0);
+    const size_t n_outs = sizeof outs / sizeof outs[0];
+    for (size_t i = 0; i < n_outs; ++i) {
+        for (const Range &r : ins)
+            if (overlap(outs[i], r)) return fail(KDA_ERR_ALIAS, "a gradient or the workspace overlaps an input");
+        if (overlap(outs[i], rh0) || overlap(outs[i], rdhT))
+            return fail(KDA_ERR_ALIAS, "a gradient or the workspace overlaps a state input");
+        for (size_t j = i + 1; j < n_outs; ++j)
+            if (overlap(outs[i], outs[j])) return fail(KDA_ERR_ALIAS, "two gradients (or the workspace) overlap");
+    }
+    if (a->grad_initial_state) {
+        const Range rd = range_of(a->grad_initial_state, sbytes);
+        for (const Range &r : ins)
+            if (overlap(rd, r)) return fail(KDA_ERR_ALIAS, "grad_initial_state overlaps an input");
+        for (const Range &r : outs)
+            if (overlap(rd, r)) return fail(KDA_ERR_ALIAS, "grad_initial_state overlaps another gradient");
+        if (a->grad_initial_state != a->initial_state && overlap(rd, rh0))
+            return fail(KDA_ERR_ALIAS, "grad_initial_state partially overlaps initial_state");
+        if (a->grad_initial_state != a->grad_final_state && overlap(rd, rdhT))
+            return fail(KDA_ERR_ALIAS, "grad_initial_state partially overlaps grad_final_state");
+    }
+    return KDA_OK;
+}
+
 }  // namespace
 
 void kda::set_last_error(const char *text) { g_last_error = text; }
@@ -377,46 +422,11 @@ kda_status kda_recurrent_bwd(const kda_recurrent_bwd_args *user) {
     const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
     const int N = a->num_seqs;
     if (N == 0 || (tokens == 0 && !a->grad_initial_state)) return KDA_OK;
-    if (tokens > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->grad_o || !a->grad_q || !a->grad_k ||
-                       !a->grad_v || !a->grad_g || !a->grad_beta))
-        return fail(KDA_ERR_NULL_POINTER, "q, k, v, g, beta, grad_o and every token gradient are required");
-    const size_t th = static_cast<size_t>(tokens) * a->H, in_sz = dsize(a->in_dtype);
-    const size_t gw = (a->flags & KDA_FLAG_SCALAR_GATE) ? 1 : static_cast<size_t>(a->dk);
-    const size_t sbytes = static_cast<size_t>(N) * a->H * a->dk * a->dv * 4;
     const size_t need = kda::backward_workspace_bytes(a->B, a->T, a->H, a->dk, a->dv, N, a->cu_seqlens != nullptr,
                                                       (a->flags & (KDA_FLAG_QK_L2NORM | KDA_FLAG_GATE_SOFTPLUS)) != 0,
                                                       (a->flags & KDA_FLAG_SCALAR_GATE) != 0);
-    if (a->workspace_bytes < need || (need > 0 && !a->workspace))
-        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", a->workspace_bytes, need);
-    const Range ins[] = {range_of(a->q, th * a->dk * in_sz), range_of(a->k, th * a->dk * in_sz),
-                         range_of(a->v, th * a->dv * in_sz), range_of(a->g, th * gw * 4),
-                         range_of(a->beta, th * in_sz), range_of(a->grad_o, th * a->dv * in_sz),
-                         range_of(a->cu_seqlens, a->cu_seqlens ? (static_cast<size_t>(N) + 1) * 4 : 0)};
-    const Range outs[] = {range_of(a->grad_q, th * a->dk * 4), range_of(a->grad_k, th * a->dk * 4),
-                          range_of(a->grad_v, th * a->dv * 4), range_of(a->grad_g, th * gw * 4),
-                          range_of(a->grad_beta, th * 4), range_of(a->workspace, need)};
-    const Range rh0 = range_of(a->initial_state, a->initial_state ? sbytes : 0);
-    const Range rdhT = range_of(a->grad_final_state, a->grad_final_state ? sbytes : 0);
-    const size_t n_outs = sizeof outs / sizeof outs[0];
-    for (size_t i = 0; i < n_outs; ++i) {
-        for (const Range &r : ins)
-            if (overlap(outs[i], r)) return fail(KDA_ERR_ALIAS, "a gradient or the workspace overlaps an input");
-        if (overlap(outs[i], rh0) || overlap(outs[i], rdhT))
-            return fail(KDA_ERR_ALIAS, "a gradient or the workspace overlaps a state input");
-        for (size_t j = i + 1; j < n_outs; ++j)
-            if (overlap(outs[i], outs[j])) return fail(KDA_ERR_ALIAS, "two gradients (or the workspace) overlap");
-    }
-    if (a->grad_initial_state) {
-        const Range rd = range_of(a->grad_initial_state, sbytes);
-        for (const Range &r : ins)
-            if (overlap(rd, r)) return fail(KDA_ERR_ALIAS, "grad_initial_state overlaps an input");
-        for (const Range &r : outs)
-            if (overlap(rd, r)) return fail(KDA_ERR_ALIAS, "grad_initial_state overlaps another gradient");
-        if (a->grad_initial_state != a->initial_state && overlap(rd, rh0))
-            return fail(KDA_ERR_ALIAS, "grad_initial_state partially overlaps initial_state");
-        if (a->grad_initial_state != a->grad_final_state && overlap(rd, rdhT))
-            return fail(KDA_ERR_ALIAS, "grad_initial_state partially overlaps grad_final_state");
-    }
+    const kda_status sb = check_bwd_buffers(a, need);
+    if (sb != KDA_OK) return sb;
 
     kda::BackwardLaunch L{};
     L.q = a->q; L.k = a->k; L.v = a->v; L.g = a->g; L.beta = a->beta; L.d_o = a->grad_o;
@@ -432,6 +442,50 @@ kda_status kda_recurrent_bwd(const kda_recurrent_bwd_args *user) {
     L.workspace = a->workspace;
     L.stream = static_cast<hipStream_t>(a->stream);
     return hip_status(kda::launch_backward(L), "kda_recurrent_bwd launch");
+}
+
+size_t kda_chunk_bwd_workspace_bytes(const kda_recurrent_bwd_args *user) {
+    kda_recurrent_bwd_args a;
+    if (read_bwd_args(user, a) != KDA_OK || a.flags != 0 ||
+        !kda::chunk_bwd_supported(a.in_dtype == KDA_DTYPE_BF16, a.dk, a.dv))
+        return static_cast<size_t>(-1);
+    return kda::chunk_bwd_workspace_bytes(a.B, a.T, a.H, a.num_seqs, a.cu_seqlens != nullptr);
+}
+
+kda_status kda_chunk_bwd(const kda_recurrent_bwd_args *user) {
+    g_last_error.clear();
+    kda_recurrent_bwd_args args;
+    const kda_status st = read_bwd_args(user, args);
+    if (st != KDA_OK) return st;
+    const kda_recurrent_bwd_args *a = &args;
+    if (a->flags != 0)
+        return fail(KDA_ERR_UNSUPPORTED, "flags 0x%x: the chunkwise gradients take no input transforms "
+                    "(kda_recurrent_bwd does)", a->flags);
+    if (!kda::chunk_bwd_supported(a->in_dtype == KDA_DTYPE_BF16, a->dk, a->dv))
+        return fail(KDA_ERR_UNSUPPORTED, "the chunkwise gradients need bf16 inputs and dk = dv = 128 "
+                    "(kda_recurrent_bwd takes the rest)");
+    const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
+    const int N = a->num_seqs;
+    if (N == 0 || (tokens == 0 && !a->grad_initial_state)) return KDA_OK;
+    const bool varlen = a->cu_seqlens != nullptr;
+    const size_t need = kda::chunk_bwd_workspace_bytes(a->B, a->T, a->H, N, varlen);
+    const kda_status sb = check_bwd_buffers(a, need);
+    if (sb != KDA_OK) return sb;
+    if (!kda::chunk_bwd_grids_fit(a->B, a->T, a->H, N, varlen))
+        return fail(KDA_ERR_UNSUPPORTED, "problem too large for one launch of the chunkwise gradients");
+
+    kda::BackwardLaunch L{};
+    L.q = a->q; L.k = a->k; L.v = a->v; L.g = a->g; L.beta = a->beta; L.d_o = a->grad_o;
+    L.h0 = a->initial_state; L.dhT = a->grad_final_state;
+    L.dq = a->grad_q; L.dk = a->grad_k; L.dv = a->grad_v; L.dg = a->grad_g; L.dbeta = a->grad_beta;
+    L.dh0 = a->grad_initial_state;
+    L.cu_seqlens = a->cu_seqlens;
+    L.B = a->B; L.N = N; L.T = a->T; L.H = a->H; L.dk_dim = a->dk; L.dv_dim = a->dv;
+    L.scale = a->scale;
+    L.in_bf16 = true;
+    L.workspace = a->workspace;
+    L.stream = static_cast<hipStream_t>(a->stream);
+    return hip_status(kda::launch_chunk_bwd(L), "kda_chunk_bwd launch");
 }
 
 }  // extern "C"

@@ -120,6 +120,11 @@ hipError_t launch_chunk(const ChunkLaunch &L);
 // last segment, the final state).
 constexpr int kLocal = 0;
 constexpr int kOut = 1;
+// passes of the chunkwise gradients on the matrix-core path (kda_scan.hip): a forward replay that keeps
+// every chunk's entering state and V_new, and the two reverse walks that carry the state gradient
+constexpr int kStates = 2;
+constexpr int kRevLocal = 3;
+constexpr int kRevOut = 4;
 constexpr int kSegLast = 1;
 constexpr int kSegFirst = 2;
 
@@ -174,6 +179,50 @@ size_t pack_bytes();  // bytes of one operand pack
 void launch_prep(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, void *packs);
 template <int MODE>
 void launch_scan(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, const void *packs);
+
+// Buffers of the gradient passes of the scan.  Per chunk (pack slot s = segment * per + chunk, head h,
+// index s * H + h) the states and V_new are kept in accumulator order: 16-byte unit (w * R + t) * 64 + l
+// holds rows 16 t + 4 (l / 16) .. + 3 of column 16 w + l % 16, R = 8 row tiles for a state (dk x dv),
+// R = 4 for V_new (C x dv).
+struct ScanGrad {
+    float *st;            // kStates: the state entering each chunk
+    float *vn;            // kStates: V_new of each chunk; kRevOut: dV_new of each chunk
+    float *dst;           // kRevOut: the gradient of the state each chunk leaves
+    const float *dleave;  // kRevOut: [segment * H + h] gradient of the state each segment leaves (row-major)
+    const float *dhT;     // kRevOut: [sequence * H + h] final-state gradient (null: zero)
+    float *dh0;           // kRevOut: [sequence * H + h] initial-state gradient (null: not written)
+    float *hb;            // kRevLocal: [segment * H + h] state gradient at the segment start from zero at its end
+    bool keep_last;       // kLocal: P and H of every segment but a one-segment sequence's (the reverse combine
+                          // needs P of last segments)
+};
+template <int MODE>
+void launch_scan_grad(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, const void *packs,
+                      const ScanGrad &gr);
+
+// The chunkwise gradients (kda_chunk_bwd.hip) on the matrix-core path: the forward part of the segmented
+// prefill (segment table, prep, local pass keeping last segments, combine, kStates replay) in the layout
+// of the forward plan, then the reverse passes.
+struct ChunkGradLayout {
+    size_t bytes;  // workspace of the forward part (segment table, states, packs)
+    int per;       // chunks per segment
+    int max_segs;  // bound on the number of segments
+    bool packs;    // the matrix-core path applies
+};
+ChunkGradLayout chunk_grad_layout(int B, int T, int H, int N, bool varlen);
+// Runs the forward part into L.workspace (chunk_grad_layout().bytes) and the kStates replay into gr.st and
+// gr.vn; *chained tells whether any sequence has more than one segment (else the local pass, the combines
+// and kRevLocal have nothing to do), *packs where the operand packs are.
+SegmentView launch_chunk_grad_forward(const ChunkLaunch &L, const ScanGrad &gr, bool *chained, void **packs);
+// The reverse combine of the segment gradients (kda_backward.hip): P from sv.P as fp32 or, with planes,
+// as the matrix-core path's bf16 high and low planes; dk = 128.
+void launch_reverse_combine(const SegmentView &sv, const float *hb, const float *dhT, float *dleave, float *dh0,
+                            int H, int N, bool planes, hipStream_t stream);
+bool chunk_bwd_supported(bool in_bf16, int dk, int dv);
+size_t chunk_bwd_workspace_bytes(int B, int T, int H, int N, bool varlen);
+// false when a launch would exceed a grid dimension's 32-bit thread count or the matrix-core path's
+// 32-bit offsets
+bool chunk_bwd_grids_fit(int B, int T, int H, int N, bool varlen);
+hipError_t launch_chunk_bwd(const BackwardLaunch &L);
 
 // The general DPLR recurrence in chunkwise form (kda_dplr_chunk.hip), on the segment machinery above.
 struct DplrChunkLaunch {

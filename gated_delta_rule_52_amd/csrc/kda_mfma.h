@@ -194,7 +194,24 @@ constexpr int kPkBytes = kPkU + C * DV * 2;
 constexpr int kPkLocal = kPkQ;   // bytes the local pass copies to LDS
 constexpr int kPkOut = kPkU;     // bytes the output pass copies to LDS
 static_assert(kPkLocal % 1024 == 0 && kPkOut % 1024 == 0, "whole 1 KiB wave copies");
-enum { kHdrW = 0, kHdrQ = 1, kHdrK = 2, kHdrU = 3, kHdrA = 4 };
+enum { kHdrW = 0, kHdrQ = 1, kHdrK = 2, kHdrU = 3, kHdrA = 4, kHdrDO = 5 };
+
+// ---- reverse pack (gradients), one per chunk and head, same slots: the walk
+// over the chunks in reverse order carries dS (the gradient of the state a
+// chunk leaves) as the forward walk carries S, since
+//     dV_new = A_qk^T dO + Kd dS,   dS_enter = gamma * dS + Q^T dO - W^T dV_new
+// (Kd = e^{G_last - G} k).  With U <- A_qk^T dO, W <- -Kd, KT <- -W^T it is the
+// forward step plus one more product Q^T dO:
+//   W   slot  -Kd          [64][128]  w_col,  exponent hdr[kHdrW]
+//   KT  slot  -W^T         [128][64]  kt_col, exponent hdr[kHdrK]
+//   Q   slot  Q^T          [128][64]  kt_col, exponent hdr[kHdrQ]  (Q = scale e^G q)
+//   U   slot  A_qk^T dO    accumulator order, exponent hdr[kHdrU]
+//   DO        dO           accumulator order (as U), exponent hdr[kHdrDO]
+//   gamma as in the forward pack; the A slot is unused.
+constexpr int kRvDO = kPkBytes;
+constexpr int kRvBytes = kPkBytes + C * DV * 2;
+constexpr int kRvStage = kPkA;  // bytes the reverse passes copy to LDS (gamma, header, W, KT, Q)
+static_assert(kRvStage % 1024 == 0, "whole 1 KiB wave copies");
 
 // W, Q ([64][128] fp16) and KT ([128][64] fp16) are read as A operands of
 // 16x16x32 products whose contraction index is permuted: in step p, lane

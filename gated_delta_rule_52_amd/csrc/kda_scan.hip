@@ -24,6 +24,16 @@
 // and waves 8-15 build P (the dk x dk transition: identity start, v = 0), so
 // that leaving = P entering + H; kOut, 8 waves: replay from the entering
 // state, write o and, for a sequence's last segment, the final state.
+//
+// The gradients use three more (8 waves each).  kStates replays like kOut but
+// keeps every chunk's entering state and V_new instead of writing o.  The
+// reverse modes walk a segment's chunks last to first over the reverse pack
+// (kda_mfma.h) with the state gradient dS in the accumulators: the step is
+// the forward one with U <- A_qk^T dO, W <- -Kd, KT <- -W^T and one more
+// product Q^T dO in the update.  kRevLocal starts from zero at the segment end
+// and leaves Hb (dS_enter = P^T dS_leave + Hb); kRevOut starts from the
+// segment's true leaving gradient, keeps each chunk's dS and dV_new, and
+// writes the initial-state gradient at a sequence's first segment.
 #include "kda_internal.h"
 #include "kda_mfma.h"
 
@@ -36,20 +46,26 @@ typedef void __attribute__((address_space(3))) *lptr_t;
 
 template <int MODE>
 struct ScanCfg {
+    static constexpr bool kRev = MODE == kRevLocal || MODE == kRevOut;
     static constexpr int NCT = 1;                    // 16-column state tiles per wave
     static constexpr int NWH = 8 / NCT;              // waves per 128 columns
-    static constexpr int NW = MODE == kOut ? NWH : 2 * NWH;
+    static constexpr int NW = MODE == kLocal ? 2 * NWH : NWH;
     static constexpr int NT = NW * kWave;
-    static constexpr int kBytes = MODE == kOut ? kPkOut : kPkLocal;  // pack bytes staged in LDS
+    // pack bytes staged in LDS, and the stride of the packs
+    static constexpr int kBytes = MODE == kOut ? kPkOut : (kRev ? kRvStage : kPkLocal);
+    static constexpr int kStride = kRev ? kRvBytes : kPkBytes;
 };
 
 template <int MODE, bool OutBf16>
 __global__ void __launch_bounds__(ScanCfg<MODE>::NT, 1)
 chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__restrict__ o_, SegmentView sv,
-                  int H) {
+                  int H, ScanGrad gr) {
     constexpr bool kOutPass = MODE == kOut;
+    constexpr bool kRev = ScanCfg<MODE>::kRev;
+    constexpr bool kReplay = MODE == kOut || MODE == kStates || MODE == kRevOut;  // from a true boundary state
+    constexpr bool kKeep = MODE == kStates || MODE == kRevOut;                     // per-chunk states kept
     constexpr int NW = ScanCfg<MODE>::NW, NWH = ScanCfg<MODE>::NWH, NCT = ScanCfg<MODE>::NCT;
-    constexpr int kBytes = ScanCfg<MODE>::kBytes;
+    constexpr int kBytes = ScanCfg<MODE>::kBytes, kStride = ScanCfg<MODE>::kStride;
     // two pack buffers as separate objects, so that the compiler can tell a
     // copy into one from reads of the other and does not wait for the copy
     __shared__ __attribute__((aligned(16))) char lds0[kBytes];
@@ -66,11 +82,13 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     if (seg >= sv.count()) return;
     const int4 sd = sv.table[seg];
     const int nseq = sd.x;
-    const bool last = sd.w & kSegLast;
-    if (!kOutPass && last) return;
+    const bool last = sd.w & kSegLast, first = sd.w & kSegFirst;
+    // a last segment's P and H serve only the reverse combine; a one-segment sequence needs neither
+    if (MODE == kLocal && last && (first || !gr.keep_last)) return;
+    if (MODE == kRevLocal && first) return;  // Hb of a first segment is never used
     const int64_t t0 = sd.y, t1 = sd.z;
     const int nch = static_cast<int>((t1 - t0 + C - 1) / C);
-    const bool pcols = !kOutPass && wave >= NWH;  // this wave builds P
+    const bool pcols = MODE == kLocal && wave >= NWH;  // this wave builds P
     const int ctile0 = NCT * (wave % NWH);         // this wave's first 16-column tile
     const int col0 = 16 * ctile0;
 
@@ -79,9 +97,15 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     const uint32_t st_lane = 4 * (4 * g4 * 128 + col0 + n16);
     auto st_off = [](int rt, int ct, int jj) { return 4 * ((16 * rt + jj) * 128 + 16 * ct); };
     f4 acc[8][NCT];
-    if (kOutPass) {
-        // a zero-sized resource reads zeros: the zero initial state
-        const float *src = sv.entering(seg, sd, h, H, DK, DV);
+    if (kReplay) {
+        // a zero-sized resource reads zeros: the zero initial state (or final-state gradient)
+        const float *src;
+        if constexpr (MODE == kRevOut) {
+            if (first && last) src = gr.dhT ? gr.dhT + (static_cast<int64_t>(nseq) * H + h) * DK * DV : nullptr;
+            else src = gr.dleave + (static_cast<int64_t>(seg) * H + h) * DK * DV;
+        } else {
+            src = sv.entering(seg, sd, h, H, DK, DV);
+        }
         const rsrc_t rs = make_rsrc(src, src ? 4 * DK * DV : 0);
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
@@ -129,33 +153,53 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     constexpr int ob = OutBf16 ? 2 : 4;
     const rsrc_t rs_o = make_rsrc(static_cast<char *>(o_) + seg_base * ob, kOutPass ? ob * seg_elems : 0);
 
-    // chunk j's pack -> dst and its U -> registers
-    auto fetch = [&](int j, char *dst, u4 (&ur)[NCT][2]) {
-        const char *pack = packs + (static_cast<int64_t>(seg * per + j) * H + h) * kPkBytes;
+    // chunk j's pack -> dst and its U (and, reversed, dO) -> registers
+    auto fetch = [&](int j, char *dst, u4 (&ur)[NCT][2], u4 (&dr)[NCT][2]) {
+        const char *pack = packs + (static_cast<int64_t>(seg * per + j) * H + h) * kStride;
         for (int u = wave; u < kBytes / 1024; u += NW)
             __builtin_amdgcn_global_load_lds((gptr_t)(pack + 1024 * u + 16 * lane), (lptr_t)(dst + 1024 * u), 16, 0, 0);
         if (!pcols) {
-            const rsrc_t rs_p = make_rsrc(pack, kPkBytes);
+            const rsrc_t rs_p = make_rsrc(pack, kStride);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int pr = 0; pr < 2; ++pr)
+                for (int pr = 0; pr < 2; ++pr) {
                     ur[ct][pr] = __builtin_amdgcn_raw_buffer_load_b128(rs_p, kPkU + 16 * lane,
                                                                        u_off(ctile0 + ct, 2 * pr, 0), 0);
+                    if (kRev)
+                        dr[ct][pr] = __builtin_amdgcn_raw_buffer_load_b128(rs_p, kRvDO + 16 * lane,
+                                                                           u_off(ctile0 + ct, 2 * pr, 0), 0);
+                }
         }
     };
-    u4 urA[NCT][2] = {}, urB[NCT][2] = {};  // U of the chunk in use / of the next one (zero for P)
-    fetch(0, lds0, urA);
+    // the i-th chunk walked: first to last, or last to first in the reverse modes
+    auto chunk_of = [&](int i) { return kRev ? nch - 1 - i : i; };
+    // U (and dO) of the chunk in use / of the next one (zero for P)
+    u4 urA[NCT][2] = {}, urB[NCT][2] = {}, drA[NCT][2] = {}, drB[NCT][2] = {};
+    fetch(chunk_of(0), lds0, urA, drA);
 
     // one chunk: its pack is in L, the next one's goes to Lnext
-    auto step = [&](int j, const char *L, char *Lnext, const u4 (&ur_cur)[NCT][2], u4 (&ur_nxt)[NCT][2]) {
+    auto step = [&](int i, const char *L, char *Lnext, const u4 (&ur_cur)[NCT][2], u4 (&ur_nxt)[NCT][2],
+                    const u4 (&dr_cur)[NCT][2], u4 (&dr_nxt)[NCT][2]) {
+        const int j = chunk_of(i);
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // chunk j in L; every wave is done with chunk j - 1
-        if (j + 1 < nch) fetch(j + 1, Lnext, ur_nxt);
+        __syncthreads();  // chunk j in L; every wave is done with the previous chunk
+        if (i + 1 < nch) fetch(chunk_of(i + 1), Lnext, ur_nxt, dr_nxt);
 
         const int *hdr = reinterpret_cast<const int *>(L + kPkHdr);
         const int ew = hdr[kHdrW], ek = hdr[kHdrK];
         const float *gam = reinterpret_cast<const float *>(L + kPkGamma);
+        const int64_t slot = (static_cast<int64_t>(seg) * per + j) * H + h;
+        if constexpr (kKeep) {  // the state entering chunk j (forward) or the gradient of the one leaving it
+            float *sd_ = (MODE == kStates ? gr.st : gr.dst) + slot * (DK * DV);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const float sc = pow2(fr[ct]);
+#pragma unroll
+                for (int rt = 0; rt < 8; ++rt)
+                    *reinterpret_cast<f4 *>(sd_ + 4 * (((ctile0 + ct) * 8 + rt) * 64 + lane)) = acc[rt][ct] * sc;
+            }
+        }
         // The accumulator layout of two 16-row state tiles is the B operand
         // layout of a 16x16x32 product with a permuted contraction index (see
         // w_col), and |acc| < 96: the state feeds products as is, in fp16.
@@ -224,13 +268,35 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
                         }
                     }
                 }
-                const int eu = ek + exp_of(wave_max(mv));  // |V_new| 2^ek < 2^eu
+                int eu = ek + exp_of(wave_max(mv));  // |V_new| 2^ek < 2^eu
+                // reversed: the frame also holds Q^T dO (Q^T stored < 1, dO < 2^(e_dO + e_q) in the frame's units)
+                if (kRev) eu = max(eu, hdr[kHdrQ] + hdr[kHdrDO]);
                 const float sm = smax[ct];
                 const bool keep = eu <= fr[ct] && fr[ct] <= eu + 10 && sm <= 32.f && sm >= 0.015625f;
                 frn[ct] = keep ? fr[ct] : max(eu, sm > 0.f ? fr[ct] + exp_of(sm) : eu);
                 const float svn = pow2(ek - frn[ct]);  // V_h = V_new 2^(ek - frn)
 #pragma unroll
                 for (int a = 0; a < 4; ++a) Vh[ct][a] = to_h4(Vn[ct][a], svn);
+                if constexpr (kKeep) {  // V_new (forward) or dV_new (reversed), true scale
+                    float *vd = gr.vn + slot * (C * DV);
+#pragma unroll
+                    for (int a = 0; a < 4; ++a)
+                        *reinterpret_cast<f4 *>(vd + 4 * (((ctile0 + ct) * 4 + a) * 64 + lane)) = Vn[ct][a];
+                }
+            }
+        }
+        // reversed: dO in the new frame, dO 2^(e_q - frn), as the B operand of the extra product
+        h8 db[NCT][2];
+        if constexpr (kRev) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const float sdo = pow2(hdr[kHdrDO] + hdr[kHdrQ] - frn[ct]);
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    const h8 d = __builtin_bit_cast(h8, dr_cur[ct][pr]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) db[ct][pr][e] = static_cast<_Float16>(static_cast<float>(d[e]) * sdo);
+                }
             }
         }
         // a6: o = Q S + A_qk V_new, staged per wave in LDS, then 16-byte stores
@@ -306,6 +372,11 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
                 const h8 kt = *reinterpret_cast<const h8 *>(L + kPkKT + kt_unit(16 * rt + n16, p, g4));
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = mma32(kt, vb[ct][p], acc[rt][ct]);
+                if constexpr (kRev) {
+                    const h8 qt = *reinterpret_cast<const h8 *>(L + kPkQ + kt_unit(16 * rt + n16, p, g4));
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = mma32(qt, db[ct][p], acc[rt][ct]);
+                }
             }
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
@@ -315,17 +386,21 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) smax[ct] = wave_max(mx[ct]);
     };
-    for (int j = 0; j < nch; j += 2) {
-        step(j, lds0, lds1, urA, urB);
-        if (j + 1 < nch) step(j + 1, lds1, lds0, urB, urA);
+    for (int i = 0; i < nch; i += 2) {
+        step(i, lds0, lds1, urA, urB, drA, drB);
+        if (i + 1 < nch) step(i + 1, lds1, lds0, urB, urA, drB, drA);
     }
 
-    // ---- leaving state (DK = DV: H and P are both 128 x 128)
+    // ---- leaving state (DK = DV: H and P are both 128 x 128), or the gradient at the segment start
     float *dst = nullptr;
     if (kOutPass) {
         if (last && hT) dst = hT + (static_cast<int64_t>(nseq) * H + h) * DK * DV;
-    } else {
+    } else if (MODE == kLocal) {
         dst = (pcols ? sv.P : sv.Hs) + (static_cast<int64_t>(seg) * H + h) * DK * DV;
+    } else if (MODE == kRevLocal) {
+        dst = gr.hb + (static_cast<int64_t>(seg) * H + h) * DK * DV;
+    } else if (MODE == kRevOut) {
+        if (first && gr.dh0) dst = gr.dh0 + (static_cast<int64_t>(nseq) * H + h) * DK * DV;
     }
     if (dst && pcols) {
         // P as bf16 high and low planes (P = hi + lo to about 16 bits), the operands of the combine's
@@ -362,16 +437,32 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
 }  // namespace mc
 
 template <int MODE>
-void launch_scan(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, const void *packs) {
+void launch_scan_grad(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, const void *packs,
+                      const ScanGrad &gr) {
     dim3 grid(max_segs, L.H), block(mc::ScanCfg<MODE>::NT);
     const char *pk = static_cast<const char *>(packs);
-    if (L.out_bf16)
-        hipLaunchKernelGGL((mc::chunk_scan_kernel<MODE, true>), grid, block, 0, L.stream, pk, per, L.hT, L.o, sv, L.H);
+    if (MODE == kOut && L.out_bf16)
+        hipLaunchKernelGGL((mc::chunk_scan_kernel<MODE, true>), grid, block, 0, L.stream, pk, per, L.hT, L.o, sv, L.H,
+                           gr);
     else
-        hipLaunchKernelGGL((mc::chunk_scan_kernel<MODE, false>), grid, block, 0, L.stream, pk, per, L.hT, L.o, sv, L.H);
+        hipLaunchKernelGGL((mc::chunk_scan_kernel<MODE, false>), grid, block, 0, L.stream, pk, per, L.hT, L.o, sv,
+                           L.H, gr);
+}
+
+template <int MODE>
+void launch_scan(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, const void *packs) {
+    launch_scan_grad<MODE>(L, sv, max_segs, per, packs, ScanGrad{});
 }
 
 template void launch_scan<kLocal>(const ChunkLaunch &, const SegmentView &, int, int, const void *);
 template void launch_scan<kOut>(const ChunkLaunch &, const SegmentView &, int, int, const void *);
+template void launch_scan_grad<kLocal>(const ChunkLaunch &, const SegmentView &, int, int, const void *,
+                                       const ScanGrad &);
+template void launch_scan_grad<kStates>(const ChunkLaunch &, const SegmentView &, int, int, const void *,
+                                        const ScanGrad &);
+template void launch_scan_grad<kRevLocal>(const ChunkLaunch &, const SegmentView &, int, int, const void *,
+                                          const ScanGrad &);
+template void launch_scan_grad<kRevOut>(const ChunkLaunch &, const SegmentView &, int, int, const void *,
+                                        const ScanGrad &);
 
 }  // namespace kda

@@ -494,6 +494,40 @@ hipError_t launch_chunk(const ChunkLaunch &L) {
     return hipGetLastError();
 }
 
+ChunkGradLayout chunk_grad_layout(int B, int T, int H, int N, bool varlen) {
+    const Plan p = make_plan(B, T, H, 128, 128, N, 64, varlen, true);
+    return ChunkGradLayout{p.bytes, p.per, p.max_segs, p.packs};
+}
+
+SegmentView launch_chunk_grad_forward(const ChunkLaunch &L, const ScanGrad &gr, bool *chained, void **packs) {
+    const bool varlen = L.cu_seqlens != nullptr;
+    const Plan p = make_plan(L.B, L.T, L.H, L.dk, L.dv, L.N, L.chunk, varlen, L.in_bf16);
+    char *ws = static_cast<char *>(L.workspace);
+    SegmentView sv;
+    sv.table = reinterpret_cast<const int4 *>(ws + p.off_table);
+    sv.seq_seg = reinterpret_cast<const int32_t *>(ws + p.off_seq);
+    sv.N = L.N;
+    sv.P = reinterpret_cast<float *>(ws + p.off_P);
+    sv.Hs = reinterpret_cast<float *>(ws + p.off_H);
+    sv.sin = reinterpret_cast<float *>(ws + p.off_S);
+    sv.h0 = L.h0;
+    sv.xcount = reinterpret_cast<int *>(ws + p.off_xlist);
+    sv.xlist = sv.xcount + 1;
+    hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(256), 0, L.stream, L.cu_seqlens, L.T, L.N,
+                       p.seg_len, reinterpret_cast<int4 *>(ws + p.off_table),
+                       reinterpret_cast<int32_t *>(ws + p.off_seq), sv.xcount);
+    *packs = ws + p.off_pack;
+    *chained = varlen || L.T == 0 || L.T > p.seg_len;
+    launch_prep(L, sv, p.max_segs, p.per, *packs);
+    if (*chained) {
+        launch_scan_grad<kLocal>(L, sv, p.max_segs, p.per, *packs, gr);
+        hipLaunchKernelGGL(combine_bf16x3_kernel, dim3(L.H, L.dv / 16, L.N), dim3(512), 0, L.stream, sv, L.h0,
+                           static_cast<float *>(nullptr), L.H);
+    }
+    launch_scan_grad<kStates>(L, sv, p.max_segs, p.per, *packs, gr);
+    return sv;
+}
+
 size_t segment_states_bytes(int B, int T, int H, int dk, int dv, int N, bool varlen, int chunk) {
     return make_plan(B, T, H, dk, dv, N, chunk, varlen, false).bytes;
 }

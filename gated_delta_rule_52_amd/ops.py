@@ -286,6 +286,26 @@ def recurrent_bwd_workspace_bytes(q, v, cu_seqlens=None, scalar_gate=False, qk_l
     return int(n)
 
 
+def chunk_bwd_workspace_bytes(q, v, cu_seqlens=None) -> int:
+    n = _lib.chunk_bwd_workspace_raw(_bwd_args(q, v, cu_seqlens, 1.0, False, False, False))
+    if n == 2 ** 64 - 1:
+        _lib.check(_lib.STATUS_CODE["KDA_ERR_UNSUPPORTED"])
+    return int(n)
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+              beta: torch.Tensor, grad_o: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+              grad_final_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, scale: float = 1.0,
+              output_grad_initial_state: bool = True, grad_initial_state: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None):
+    """The gradients of ``recurrent_bwd`` by the chunk path (bf16 inputs,
+    dk = dv = 128, no input transforms); same arguments and result."""
+    return _backward(q, k, v, g, beta, grad_o, initial_state, grad_final_state, cu_seqlens, scale,
+                     output_grad_initial_state, grad_initial_state, workspace, out, False, False, False, 1.0,
+                     chunk=True)
+
+
 def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                   beta: torch.Tensor, grad_o: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
                   grad_final_state: Optional[torch.Tensor] = None,
@@ -294,7 +314,7 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None,
                   scalar_gate: bool = False, qk_l2norm: bool = False, gate_logits: bool = False,
                   gate_scale: float = 1.0):
-    """Gradients of the recurrence (no input transforms) for the output
+    """Gradients of the recurrence for the output
     gradient ``grad_o`` [B,T,H,dv] (dtype of q) and the optional final-state
     gradient [N,H,dk,dv] fp32.  Inputs as in ``chunk_fwd``.  Returns a dict of
     fp32 tensors: dq, dk, dg [B,T,H,dk], dv [B,T,H,dv], dbeta [B,T,H] and dh0
@@ -305,6 +325,14 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     ``scalar_gate``: g (and dg) are [B,T,H], one gate per token and head.
     ``qk_l2norm``, ``gate_logits``, ``gate_scale``: the forward's input
     transforms; dq, dk and dg are then gradients of the raw q, k and logits."""
+    return _backward(q, k, v, g, beta, grad_o, initial_state, grad_final_state, cu_seqlens, scale,
+                     output_grad_initial_state, grad_initial_state, workspace, out, scalar_gate, qk_l2norm,
+                     gate_logits, gate_scale, chunk=False)
+
+
+def _backward(q, k, v, g, beta, grad_o, initial_state, grad_final_state, cu_seqlens, scale,
+              output_grad_initial_state, grad_initial_state, workspace, out, scalar_gate, qk_l2norm,
+              gate_logits, gate_scale, chunk):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
@@ -337,7 +365,8 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         for n, sh in shapes.items():
             _need(out[n], n, sh, torch.float32)
     out["dh0"] = grad_initial_state
-    ws = recurrent_bwd_workspace_bytes(q, v, cu_seqlens, scalar_gate, qk_l2norm, gate_logits)
+    ws = (chunk_bwd_workspace_bytes(q, v, cu_seqlens) if chunk else
+          recurrent_bwd_workspace_bytes(q, v, cu_seqlens, scalar_gate, qk_l2norm, gate_logits))
     if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
     a = _bwd_args(q, v, cu_seqlens, scale, scalar_gate, qk_l2norm, gate_logits, gate_scale)
@@ -348,7 +377,7 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     a.workspace = _ptr(workspace) if ws > 0 else None
     a.workspace_bytes = ws
     a.stream = _stream(q.device)
-    _lib.check(_lib.recurrent_bwd_raw(a))
+    _lib.check(_lib.chunk_bwd_raw(a) if chunk else _lib.recurrent_bwd_raw(a))
     return out
 
 

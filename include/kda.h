@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 6
+#define KDA_ABI_VERSION 7
 
 /*
  * Optional input transforms, applied inside the kernels to every token before
@@ -295,6 +295,41 @@ typedef struct {
 size_t kda_recurrent_bwd_workspace_bytes(const kda_recurrent_bwd_args *args);
 
 kda_status kda_recurrent_bwd(const kda_recurrent_bwd_args *args);
+
+/*
+ * The same gradients by the chunk path (Kimi Linear review notes, section
+ * "Training and Inference": training always runs the chunkwise kernels; the
+ * gradients are those of the recurrence above), recomputing the forward
+ * chunk by chunk on matrix cores.  Per chunk of 64 tokens with entering
+ * state S, leaving-state gradient dS' and output gradient dO, the chunk form
+ * of kda_chunk_fwd differentiates to
+ *     dV_new = A_qk^T dO + Kd dS',   dS = gamma * dS' + Q^T dO - W^T dV_new,
+ * (Q = scale exp(G) q, Kd = exp(G_last - G) k, W and A_qk as in the forward
+ * chunk form) and the remaining gradients are products local to the chunk:
+ * through V_new = U - W S, the WY factors [W | U] = T beta [exp(G) k | v],
+ * T = (I + A_kk)^{-1}, and the decayed Gram products A_kk, A_qk, with a
+ * reverse cumulative sum inside the chunk for dg.
+ *
+ * Passes: kda_chunk_fwd's operand packs, local pass and combine; a forward
+ * replay keeping every chunk's entering state and V_new; the state-gradient
+ * recurrence walked backwards over the chunks with its own segmented scan
+ * (the transposed segment transitions carry it across segments); then one
+ * workgroup per chunk and head for everything local to the chunk.  The
+ * state recurrences run on fp16 operands with fp32 accumulation like
+ * kda_chunk_fwd; the chunk-local products in fp32.
+ *
+ * Arguments: as kda_recurrent_bwd, with in_dtype = KDA_DTYPE_BF16,
+ * dk = dv = 128 and flags = 0 (no input transforms); anything else returns
+ * KDA_ERR_UNSUPPORTED (kda_recurrent_bwd covers it).  grad_initial_state may
+ * equal initial_state or grad_final_state.  workspace : at least
+ * kda_chunk_bwd_workspace_bytes() bytes, about 3.2 KiB per token and head
+ * (the operand packs, and per chunk the state, V_new, the state gradient and
+ * dV_new in fp32); contents on entry ignored, on exit unspecified.  Every
+ * gradient element of every token is written.
+ */
+size_t kda_chunk_bwd_workspace_bytes(const kda_recurrent_bwd_args *args);
+
+kda_status kda_chunk_bwd(const kda_recurrent_bwd_args *args);
 
 /*
  * The general diagonal-plus-low-rank (DPLR) recurrence, token by token.  The

@@ -26,7 +26,7 @@ def test_every_declared_function_is_exported():
     assert decl == sorted(_lib.EXPORTS)
     for name in decl:
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == 6
+    assert lib.kda_abi_version() == 7
     # the names the boundary's specification gives: the version and the HIP error text
     assert lib.kda_version() == lib.kda_abi_version()
     for name in ("kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_recurrent_step", "kda_status_string",
@@ -244,6 +244,52 @@ def test_backward_struct_and_empty_calls():
     # nothing to do: no sequence, or no token and no initial-state gradient (no launch)
     assert _lib.recurrent_bwd_raw(bwd_args(B=0, num_seqs=0)) == 0
     assert _lib.recurrent_bwd_raw(bwd_args(T=0, grad_initial_state=None, q=None, grad_q=None)) == 0
+
+
+def test_chunk_backward_workspace_size():
+    """Per chunk of 64 tokens and head: a reverse pack plus the state, V_new,
+    the state gradient and dV_new in fp32 (at least 3.2 KiB per token and
+    head); other dtypes, head sizes or flags give (size_t)-1."""
+    n1 = _lib.chunk_bwd_workspace_raw(bwd_args(dv=128))
+    n2 = _lib.chunk_bwd_workspace_raw(bwd_args(dv=128, T=1000))
+    assert n1 >= 2 * 128 * 2 * 3200 and n2 >= 2 * 1024 * 2 * 3200 and n2 > n1
+    for kw in (dict(), dict(dv=128, in_dtype=_lib.KDA_DTYPE_FP32), dict(dv=128, dk=64),
+               dict(dv=128, flags=_lib.KDA_FLAG_QK_L2NORM)):
+        assert _lib.chunk_bwd_workspace_raw(bwd_args(**kw)) == 2 ** 64 - 1, kw
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dv=64), "KDA_ERR_UNSUPPORTED"),
+    (dict(dk=64), "KDA_ERR_UNSUPPORTED"),
+    (dict(in_dtype=_lib.KDA_DTYPE_FP32), "KDA_ERR_UNSUPPORTED"),
+    (dict(flags=_lib.KDA_FLAG_SCALAR_GATE), "KDA_ERR_UNSUPPORTED"),
+    (dict(flags=_lib.KDA_FLAG_QK_L2NORM), "KDA_ERR_UNSUPPORTED"),
+    (dict(H=0), "KDA_ERR_BAD_SHAPE"),
+    (dict(num_seqs=3), "KDA_ERR_BAD_SHAPE"),
+    (dict(grad_o=None), "KDA_ERR_NULL_POINTER"),
+    (dict(workspace_bytes=1000), "KDA_ERR_WORKSPACE_TOO_SMALL"),
+    (dict(workspace=None), "KDA_ERR_WORKSPACE_TOO_SMALL"),
+    (dict(grad_q=FAKE + 256), "KDA_ERR_ALIAS"),              # inside q
+    (dict(grad_v=15 * FAKE + 4096), "KDA_ERR_ALIAS"),        # inside the workspace
+    (dict(grad_initial_state=6 * FAKE + 64), "KDA_ERR_ALIAS"),  # partly over initial_state
+    (dict(grad_initial_state=5 * FAKE), "KDA_ERR_ALIAS"),       # over beta
+])
+def test_chunk_backward_rejects(kw, status):
+    args = dict(dv=128)
+    args.update(kw)
+    rc = _lib.chunk_bwd_raw(bwd_args(**args))
+    assert rc == S[status], (_lib.STATUS.get(rc), _lib.load().kda_last_error())
+    assert _lib.load().kda_last_error().decode() != ""
+
+
+def test_chunk_backward_struct_and_empty_calls():
+    lib = _lib.load()
+    a = bwd_args(dv=128)
+    a.struct_size = ctypes.sizeof(_lib.RecurrentBwdArgs) - 8
+    assert lib.kda_chunk_bwd(ctypes.byref(a)) == S["KDA_ERR_BAD_STRUCT"]
+    assert lib.kda_chunk_bwd(None) == S["KDA_ERR_NULL_POINTER"]
+    assert _lib.chunk_bwd_raw(bwd_args(dv=128, B=0, num_seqs=0)) == 0
+    assert _lib.chunk_bwd_raw(bwd_args(dv=128, T=0, grad_initial_state=None, q=None, grad_q=None)) == 0
 
 
 def dplr_args(**kw):
