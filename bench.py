@@ -403,8 +403,9 @@ def backward_alg_bytes(tokens, H, dk, dv, N, in_bytes=2):
     return th * ((2 * dk + 2 * dv + 1) * in_bytes + dk * 4 + (3 * dk + dv + 1) * 4) + 3 * N * H * dk * dv * 4
 
 
-def time_backward(args, name="backward_64k"):
-    """Gradients (kda_recurrent_bwd) of a named workload, ms per call."""
+def time_backward(args, name="backward_64k", chunk=True):
+    """Gradients of a named workload, ms per call: kda_chunk_bwd (the chunk
+    path) or kda_recurrent_bwd (token by token)."""
     import torch
     import gated_delta_rule_52_amd as kda
     from gated_delta_rule_52_amd.inputs import make_output_grads, make_workload
@@ -415,12 +416,14 @@ def time_backward(args, name="backward_64k"):
     t = lambda a, dt: torch.from_numpy(a).to(dev).to(dt)
     q, k, v, beta, d_o = t(x.q, bf), t(x.k, bf), t(x.v, bf), t(x.beta, bf), t(do, bf)
     g, h0, dht = t(x.g, f32), t(x.h0, f32), t(dhT, f32)
-    ws = torch.empty(kda.recurrent_bwd_workspace_bytes(q, v), dtype=torch.uint8, device=dev)
+    wsb = kda.chunk_bwd_workspace_bytes(q, v) if chunk else kda.recurrent_bwd_workspace_bytes(q, v)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     dh0 = torch.empty_like(h0)
     grads = {n: torch.empty(sh, dtype=f32, device=dev) for n, sh in
              (("dq", q.shape), ("dk", q.shape), ("dv", v.shape), ("dg", q.shape), ("dbeta", beta.shape))}
-    fn = lambda: kda.recurrent_bwd(q, k, v, g, beta, d_o, initial_state=h0, grad_final_state=dht,
-                                   grad_initial_state=dh0, workspace=ws, out=grads)
+    bwd = kda.chunk_bwd if chunk else kda.recurrent_bwd
+    fn = lambda: bwd(q, k, v, g, beta, d_o, initial_state=h0, grad_final_state=dht,
+                     grad_initial_state=dh0, workspace=ws, out=grads)
     for _ in range(max(args.warmup, 1)):
         fn()
     torch.cuda.synchronize()
@@ -435,7 +438,8 @@ def time_backward(args, name="backward_64k"):
         torch.cuda.synchronize()
         per.append(e0.elapsed_time(e1))
     ms = float(np.mean(per))
-    log(f"{name}: {ms:.3f} ms per call")
+    log(f"{name} ({'chunk' if chunk else 'token'} path): {ms:.3f} ms per call")
+    del ws, grads
     return x, ms, per
 
 
@@ -739,21 +743,28 @@ def main():
         }
     if not args.no_backward:
         for key, wl in (("backward", "backward_64k"), ("backward_batch", "backward_16x4096x16")):
-            xb, msb, perb = time_backward(args, wl)
+            xb, msb, perb = time_backward(args, wl, chunk=True)
+            _, mst, pert = time_backward(args, wl, chunk=False)
             toks = xb.B * xb.T
             flops = backward_alg_flops(toks, xb.H, xb.dk, xb.dv)
             bbytes = backward_alg_bytes(toks, xb.H, xb.dk, xb.dv, xb.N)
             tf = flops / (msb * 1e-3) / 1e12
             rec[key] = {
                 "workload": wl, "B": xb.B, "T": xb.T, "H": xb.H, "dk": xb.dk, "dv": xb.dv,
-                "in_dtype": "bf16", "grad_dtype": "fp32", "ms_per_call": msb, "ms_median": float(np.median(perb)),
+                "in_dtype": "bf16", "grad_dtype": "fp32", "path": "kda_chunk_bwd",
+                "ms_per_call": msb, "ms_median": float(np.median(perb)),
                 "tokens_per_s": toks / (msb * 1e-3),
-                "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "token_path": {"entry": "kda_recurrent_bwd", "ms_per_call": mst, "ms_median": float(np.median(pert)),
+                               "tokens_per_s": toks / (mst * 1e-3), "chunk_speedup": mst / msb},
+                "roofline": {"bound": "mfma", "achieved": tf, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": tf / FP32_VECTOR_PEAK_TFLOPS, "alg_flops_per_launch": flops,
+                             "flops_basis": "the token recurrence's gradient flops (20 dk dv per token and head); "
+                                            "peak: fp32 matrix cores, on which the chunk-local kernel runs",
                              "hbm_alg_bytes_per_launch": bbytes,
                              "hbm_frac": bbytes / (msb * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                             "kernel": "one kda_recurrent_bwd call: both segment-local passes in one launch, forward "
-                                       "combine, reverse combine, recurrent_bwd_kernel<128,128,bf16>"},
+                             "kernel": "one kda_chunk_bwd call: segment table, prep, local pass, combine, forward "
+                                       "replay, reverse packs, reverse local pass, reverse combine, reverse replay, "
+                                       "chunk gradients"},
             }
             if key == "backward" and not args.no_cpu:
                 rec[key]["cpu_baseline"] = cpu_backward_sample(xb)

@@ -189,11 +189,15 @@ constexpr int LH = DK + 8;  // bf16 row stride
 constexpr int LA = C + 4;   // fp32 row stride of [64][64]
 constexpr int LT = 20;      // fp32 row stride of 16 x 16 tiles
 constexpr float kMaxChunkDecayG = 80.0f;
-// LDS: phases 1-2 (state products) and phase 3 (chunk-local work) share the bytes
-constexpr int kSS = 0;                           // S, then dS'   [128][LF] fp32
-constexpr int kSO = kSS + DK * LF * 4;           // dO            [64][LF]
-constexpr int kSX = kSO + C * LF * 4;            // dV_new, then V_new [64][LF]
-constexpr int kP12 = kSX + C * LF * 4;
+// LDS: phases 1-2 (state products) and phase 3 (chunk-local work) share the bytes.  The state products
+// run on bf16 matrix cores from bf16 high and low planes (x = hi + lo to about 16 bits; dO is bf16 already):
+// hi*hi + hi*lo + lo*hi per product
+constexpr int kSSh = 0;                          // S, then dS': high plane [128][LH] bf16
+constexpr int kSSl = kSSh + DK * LH * 2;         // low plane
+constexpr int kSO = kSSl + DK * LH * 2;          // dO [64][LH] bf16
+constexpr int kSXh = kSO + C * LH * 2;           // dV_new, then V_new: high plane [64][LH]
+constexpr int kSXl = kSXh + C * LH * 2;          // low plane
+constexpr int kP12 = kSXl + C * LH * 2;
 constexpr int kK = 0;                            // k             [64][LH] bf16
 constexpr int kQ = kK + C * LH * 2;              // q
 constexpr int kRf = kQ + C * LH * 2;             // e^{G - m}, or G itself in an exact chunk   [64][LF]
@@ -211,6 +215,17 @@ static_assert(8 * 4 * 16 * LT * 4 <= kRBytes, "the dY solve tiles fit the scratc
 static_assert(kLds <= 160 * 1024, "one workgroup per compute unit");
 
 __device__ __forceinline__ f4 mf(float a, float b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
+
+// x -> bf16 high part (round to nearest even) and low part (the rest, rounded)
+__device__ __forceinline__ void split_hl(float x, uint16_t &hi, uint16_t &lo) {
+    const __bf16 h = static_cast<__bf16>(x);
+    hi = __builtin_bit_cast(uint16_t, h);
+    lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x - static_cast<float>(h)));
+}
+// 8 consecutive bf16 of row `row` from column k0 of a [rows][LH] plane
+__device__ __forceinline__ b8 rd8(const uint16_t *plane, int row, int k0) {
+    return *reinterpret_cast<const b8 *>(plane + row * LH + k0);
+}
 
 // pair index t -> block (a, b), b <= a, in the order (0,0),(1,0),(1,1),(2,0)...
 __device__ __forceinline__ void tri_ab(int t, int &a, int &b) {
@@ -260,49 +275,51 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
     };
 
     // ================= phase 1: dQ = dO S^T, dWn = dV_new S^T =================
-    float *sS = reinterpret_cast<float *>(smem + kSS), *sO = reinterpret_cast<float *>(smem + kSO);
-    float *sX = reinterpret_cast<float *>(smem + kSX);
+    uint16_t *sSh = reinterpret_cast<uint16_t *>(smem + kSSh), *sSl = reinterpret_cast<uint16_t *>(smem + kSSl);
+    uint16_t *sO = reinterpret_cast<uint16_t *>(smem + kSO);
+    uint16_t *sXh = reinterpret_cast<uint16_t *>(smem + kSXh), *sXl = reinterpret_cast<uint16_t *>(smem + kSXl);
+    // an accumulator-order unit of R row tiles into the planes
+    auto put_unit = [&](uint16_t *ph, uint16_t *pl, int u, int R, const f4 &x) {
+        int row, col;
+        unit_rc(u, R, row, col);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_hl(x[e], ph[(row + e) * LH + col], pl[(row + e) * LH + col]);
+    };
     if (tid == 0) *sFlag = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int u = tid + kGT * i;
-        const f4 x = *reinterpret_cast<const f4 *>(St + 4 * u);
-        int row, col;
-        unit_rc(u, 8, row, col);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sS[(row + e) * LF + col] = x[e];
+        put_unit(sSh, sSl, u, 8, *reinterpret_cast<const f4 *>(St + 4 * u));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int u = tid + kGT * i;
-        const f4 x = *reinterpret_cast<const f4 *>(dVt + 4 * u);
-        int row, col;
-        unit_rc(u, 4, row, col);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sX[(row + e) * LF + col] = x[e];
+        put_unit(sXh, sXl, u, 4, *reinterpret_cast<const f4 *>(dVt + 4 * u));
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int u = tid + kGT * i, r = u >> 4, cu = u & 15;
         u4 w = {0u, 0u, 0u, 0u};
         if (r < L) w = *reinterpret_cast<const u4 *>(A.d_o + trow(r) + 8 * cu);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sO[r * LF + 8 * cu + 2 * e] = lo_f(w[e]);
-            sO[r * LF + 8 * cu + 2 * e + 1] = hi_f(w[e]);
-        }
+        *reinterpret_cast<u4 *>(sO + r * LH + 8 * cu) = w;
     }
     __syncthreads();
     f4 dQh[4], dWn[4];
 #pragma unroll
     for (int a = 0; a < 4; ++a) dQh[a] = dWn[a] = zero4();
-    for (int s = 0; s < DV / 4; ++s) {
-        const int kk = 4 * s + g4;
-        const float b = sS[cw * LF + kk];  // B[j][c] = S[c][j]
+#pragma unroll
+    for (int s = 0; s < DV / 32; ++s) {
+        const int k0 = 32 * s + 8 * g4;
+        const b8 bh = rd8(sSh, cw, k0), bl = rd8(sSl, cw, k0);  // B[j][c] = S[c][j]
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            dQh[a] = mf(sO[(16 * a + n16) * LF + kk], b, dQh[a]);
-            dWn[a] = mf(sX[(16 * a + n16) * LF + kk], b, dWn[a]);
+            const b8 ao = rd8(sO, 16 * a + n16, k0);
+            dQh[a] = mmab(ao, bh, dQh[a]);
+            dQh[a] = mmab(ao, bl, dQh[a]);
+            const b8 xh = rd8(sXh, 16 * a + n16, k0), xl = rd8(sXl, 16 * a + n16, k0);
+            dWn[a] = mmab(xh, bh, dWn[a]);
+            dWn[a] = mmab(xh, bl, dWn[a]);
+            dWn[a] = mmab(xl, bh, dWn[a]);
         }
     }
     __syncthreads();
@@ -315,13 +332,9 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
             const int u = tid + kGT * i;
             const f4 x = *reinterpret_cast<const f4 *>(dSt + 4 * u);
             const f4 s = *reinterpret_cast<const f4 *>(St + 4 * u);
-            int row, col;
-            unit_rc(u, 8, row, col);
+            put_unit(sSh, sSl, u, 8, x);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sS[(row + e) * LF + col] = x[e];
-                dgp[e] += x[e] * s[e];
-            }
+            for (int e = 0; e < 4; ++e) dgp[e] += x[e] * s[e];
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -333,21 +346,23 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int u = tid + kGT * i;
-        const f4 x = *reinterpret_cast<const f4 *>(Vt + 4 * u);
-        int row, col;
-        unit_rc(u, 4, row, col);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sX[(row + e) * LF + col] = x[e];
+        put_unit(sXh, sXl, u, 4, *reinterpret_cast<const f4 *>(Vt + 4 * u));
     }
     __syncthreads();
     f4 dKd[4];
 #pragma unroll
     for (int a = 0; a < 4; ++a) dKd[a] = zero4();
-    for (int s = 0; s < DV / 4; ++s) {
-        const int kk = 4 * s + g4;
-        const float b = sS[cw * LF + kk];  // B[j][c] = dS'[c][j]
 #pragma unroll
-        for (int a = 0; a < 4; ++a) dKd[a] = mf(sX[(16 * a + n16) * LF + kk], b, dKd[a]);
+    for (int s = 0; s < DV / 32; ++s) {
+        const int k0 = 32 * s + 8 * g4;
+        const b8 bh = rd8(sSh, cw, k0), bl = rd8(sSl, cw, k0);  // B[j][c] = dS'[c][j]
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const b8 xh = rd8(sXh, 16 * a + n16, k0), xl = rd8(sXl, 16 * a + n16, k0);
+            dKd[a] = mmab(xh, bh, dKd[a]);
+            dKd[a] = mmab(xh, bl, dKd[a]);
+            dKd[a] = mmab(xl, bh, dKd[a]);
+        }
     }
     // dA_qk blocks (a, b), b <= a: wave w takes block w, waves 0 and 1 also blocks 8 and 9
     f4 dAq[2] = {zero4(), zero4()};
@@ -356,9 +371,12 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
         int a, b;
         tri_ab(wave + 8 * t, a, b);
         f4 acc = zero4();
-        for (int s = 0; s < DV / 4; ++s) {
-            const int kk = 4 * s + g4;
-            acc = mf(sO[(16 * a + n16) * LF + kk], sX[(16 * b + n16) * LF + kk], acc);
+#pragma unroll
+        for (int s = 0; s < DV / 32; ++s) {
+            const int k0 = 32 * s + 8 * g4;
+            const b8 ao = rd8(sO, 16 * a + n16, k0);
+            acc = mmab(ao, rd8(sXh, 16 * b + n16, k0), acc);
+            acc = mmab(ao, rd8(sXl, 16 * b + n16, k0), acc);
         }
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)  // entry (16 a + 4 g4 + jj, 16 b + n16): lower incl. the diagonal
@@ -537,12 +555,22 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
     // ---- M = dY Y^T (64 x 64), Y = beta [E | V]: the E half, then the V half, staged through LDS
     float *sY = reinterpret_cast<float *>(R), *sM = reinterpret_cast<float *>(R + C * LF * 4);
     f4 mt[2] = {zero4(), zero4()};
+    uint16_t *sV = reinterpret_cast<uint16_t *>(sM);  // v [64][LH] bf16 while the V half runs
+    static_assert(C * LH * 2 <= C * LA * 4, "v fits where M goes");
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) sY[(16 * a + 4 * g4 + jj) * LF + cw] = half == 0 ? dYE[a][jj] : dYV[a][jj];
+        if (half == 1)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int u = tid + kGT * i, r = u >> 4, cu = u & 15;
+                u4 w = {0u, 0u, 0u, 0u};
+                if (r < L) w = *reinterpret_cast<const u4 *>(A.v + trow(r) + 8 * cu);
+                *reinterpret_cast<u4 *>(sV + r * LH + 8 * cu) = w;
+            }
         __syncthreads();
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -552,7 +580,7 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
                 const int kk = 4 * s + g4, ri = 16 * b + n16;
                 float y;
                 if (half == 0) y = kv(ri, kk) * eG(ri, kk);
-                else y = ri < L ? bf16_to_f32(A.v[trow(ri) + kk]) : 0.f;
+                else y = bf16_to_f32(sV[ri * LH + kk]);
                 acc = mf(sY[(16 * a + n16) * LF + kk], y, acc);
             }
             mt[t] = acc;
