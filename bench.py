@@ -59,7 +59,9 @@ def decode_alg_bytes(N, H, dk, dv, in_bytes=2, out_bytes=2):
 
 
 # sources no kernel of kda_chunk_fwd is built from (decode and append kernels, gradients, DPLR)
-NOT_PREFILL_SOURCES = ("kda_recurrent.hip", "kda_backward.hip", "kda_dplr.hip")
+# the sources kda_chunk_fwd's kernels (segment table, prep, scans, combine) are built from
+PREFILL_SOURCES = ("kda_prep.hip", "kda_scan.hip", "kda_segments.hip", "kda_mfma.h", "kda_device.h",
+                   "kda_internal.h")
 
 
 def source_digest():
@@ -68,7 +70,7 @@ def source_digest():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_52_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".cpp", ".h")) and name not in NOT_PREFILL_SOURCES:
+        if name in PREFILL_SOURCES:
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
