@@ -304,6 +304,17 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
         *reinterpret_cast<u4 *>(sO + r * LH + 8 * cu) = w;
     }
     __syncthreads();
+    // phase 2's inputs, fetched while phase 1 computes
+    f4 pdS[8], pS[8], pVn[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int u = tid + kGT * i;
+        pdS[i] = *reinterpret_cast<const f4 *>(dSt + 4 * u);
+        pS[i] = *reinterpret_cast<const f4 *>(St + 4 * u);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pVn[i] = *reinterpret_cast<const f4 *>(Vt + 4 * (tid + kGT * i));
+    __builtin_amdgcn_sched_barrier(0);
     f4 dQh[4], dWn[4];
 #pragma unroll
     for (int a = 0; a < 4; ++a) dQh[a] = dWn[a] = zero4();
@@ -329,12 +340,9 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
         float dgp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {  // units (column tile i, row tile `wave`, lane): rows 16 wave + 4 g4 + e
-            const int u = tid + kGT * i;
-            const f4 x = *reinterpret_cast<const f4 *>(dSt + 4 * u);
-            const f4 s = *reinterpret_cast<const f4 *>(St + 4 * u);
-            put_unit(sSh, sSl, u, 8, x);
+            put_unit(sSh, sSl, tid + kGT * i, 8, pdS[i]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dgp[e] += x[e] * s[e];
+            for (int e = 0; e < 4; ++e) dgp[e] += pdS[i][e] * pS[i][e];
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -344,11 +352,29 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
         }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int u = tid + kGT * i;
-        put_unit(sXh, sXl, u, 4, *reinterpret_cast<const f4 *>(Vt + 4 * u));
-    }
+    for (int i = 0; i < 4; ++i) put_unit(sXh, sXl, tid + kGT * i, 4, pVn[i]);
     __syncthreads();
+    // phase 3's inputs (k, q, v rows, the gate column pieces, beta), fetched while phase 2 computes
+    const int gc = tid & (DK - 1), qq = tid >> 7;
+    u4 pk[2], pq[2], pv[2];
+    float pg[16], pbeta = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = tid + kGT * i, r = u >> 4, cu = u & 15;
+        pk[i] = pq[i] = pv[i] = u4{0u, 0u, 0u, 0u};
+        if (r < L) {
+            pk[i] = *reinterpret_cast<const u4 *>(A.k + trow(r) + 8 * cu);
+            pq[i] = *reinterpret_cast<const u4 *>(A.q + trow(r) + 8 * cu);
+            pv[i] = *reinterpret_cast<const u4 *>(A.v + trow(r) + 8 * cu);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = 16 * qq + i;
+        pg[i] = r < L ? A.g[trow(r) + gc] : 0.f;
+    }
+    if (tid < L) pbeta = bf16_to_f32(A.beta[rowb + static_cast<int64_t>(tid) * H]);
+    __builtin_amdgcn_sched_barrier(0);
     f4 dKd[4];
 #pragma unroll
     for (int a = 0; a < 4; ++a) dKd[a] = zero4();
@@ -394,24 +420,17 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int u = tid + kGT * i, r = u >> 4, cu = u & 15;
-        u4 wk = {0u, 0u, 0u, 0u}, wq = {0u, 0u, 0u, 0u};
-        if (r < L) {
-            wk = *reinterpret_cast<const u4 *>(A.k + trow(r) + 8 * cu);
-            wq = *reinterpret_cast<const u4 *>(A.q + trow(r) + 8 * cu);
-        }
-        *reinterpret_cast<u4 *>(sK + r * LH + 8 * cu) = wk;
-        *reinterpret_cast<u4 *>(sQ + r * LH + 8 * cu) = wq;
+        *reinterpret_cast<u4 *>(sK + r * LH + 8 * cu) = pk[i];
+        *reinterpret_cast<u4 *>(sQ + r * LH + 8 * cu) = pq[i];
     }
-    if (tid < C) sBeta[tid] = tid < L ? bf16_to_f32(A.beta[rowb + static_cast<int64_t>(tid) * H]) : 0.f;
+    if (tid < C) sBeta[tid] = pbeta;
     // G: channel c = tid % 128, rows 16 qq .. 16 qq + 15 (rows past L add nothing)
-    const int gc = tid & (DK - 1), qq = tid >> 7;
     float gv[16];
     {
         float run = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int r = 16 * qq + i;
-            run += r < L ? A.g[trow(r) + gc] : 0.f;
+            run += pg[i];
             gv[i] = run;
         }
         reinterpret_cast<float *>(R)[qq * DK + gc] = run;
@@ -530,77 +549,77 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
         for (int a = 0; a < 4; ++a) x[a] = *reinterpret_cast<const f4 *>(dVt + 4 * ((wave * 4 + a) * 64 + lane));
         solve_t(x, dYV);
     }
-    // dv = beta dY_V; dbeta's Y terms (row partials over this lane's column, then over the 16 columns)
-    float vv[4][4];
+    __syncthreads();  // solve tiles free
+
+    // ---- M = dY Y^T, Y = beta [E | V].  dA_kk = -(M T^T) is needed strictly below the diagonal only, which
+    // reads M[r][l] for l < r alone (T^T is upper triangular): the lower blocks of M, from dY staged in LDS
+    // half by half (the E columns, then the V columns), with v in the bytes M takes afterwards
+    float *sY = reinterpret_cast<float *>(R), *sM = reinterpret_cast<float *>(R + C * LF * 4);
+    uint16_t *sV = reinterpret_cast<uint16_t *>(sM);  // v [64][LH] bf16 until M is written
+    static_assert(C * LH * 2 <= C * LA * 4, "v fits where M goes");
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = tid + kGT * i, r = u >> 4, cu = u & 15;
+        *reinterpret_cast<u4 *>(sV + r * LH + 8 * cu) = pv[i];
+    }
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int r = 16 * a + 4 * g4 + jj;
-            vv[a][jj] = r < L ? bf16_to_f32(A.v[trow(r) + cw]) : 0.f;
-        }
+        for (int jj = 0; jj < 4; ++jj) sY[(16 * a + 4 * g4 + jj) * LF + cw] = dYE[a][jj];
+    __syncthreads();
+    // dv = beta dY_V; dbeta's Y terms (row partials over this lane's column, then over the 16 columns)
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const int r = 16 * a + 4 * g4 + jj;
             if (r < L) A.dv[trow(r) + cw] = sBeta[r] * dYV[a][jj];
-            float pb = dYE[a][jj] * kv(r, cw) * eG(r, cw) + dYV[a][jj] * vv[a][jj];
+            float pb = dYE[a][jj] * kv(r, cw) * eG(r, cw) + dYV[a][jj] * bf16_to_f32(sV[r * LH + cw]);
 #pragma unroll
             for (int m = 1; m < 16; m <<= 1) pb += __shfl_xor(pb, m, 16);
             if (n16 == 0) sDb[wave * C + r] = pb;
         }
-    __syncthreads();  // solve tiles free
-
-    // ---- M = dY Y^T (64 x 64), Y = beta [E | V]: the E half, then the V half, staged through LDS
-    float *sY = reinterpret_cast<float *>(R), *sM = reinterpret_cast<float *>(R + C * LF * 4);
     f4 mt[2] = {zero4(), zero4()};
-    uint16_t *sV = reinterpret_cast<uint16_t *>(sM);  // v [64][LH] bf16 while the V half runs
-    static_assert(C * LH * 2 <= C * LA * 4, "v fits where M goes");
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
+        if (half == 1) {
+            __syncthreads();  // the E half read
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) sY[(16 * a + 4 * g4 + jj) * LF + cw] = half == 0 ? dYE[a][jj] : dYV[a][jj];
-        if (half == 1)
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int u = tid + kGT * i, r = u >> 4, cu = u & 15;
-                u4 w = {0u, 0u, 0u, 0u};
-                if (r < L) w = *reinterpret_cast<const u4 *>(A.v + trow(r) + 8 * cu);
-                *reinterpret_cast<u4 *>(sV + r * LH + 8 * cu) = w;
-            }
-        __syncthreads();
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int tt = 2 * wave + t, a = tt >> 2, b = tt & 3;
+                for (int jj = 0; jj < 4; ++jj) sY[(16 * a + 4 * g4 + jj) * LF + cw] = dYV[a][jj];
+            __syncthreads();
+        }
+        for (int t = 0; t < nq; ++t) {  // blocks (a, b), b <= a, as for At
+            int a, b;
+            tri_ab(wave + 8 * t, a, b);
             f4 acc = mt[t];
             for (int s = 0; s < DK / 4; ++s) {
                 const int kk = 4 * s + g4, ri = 16 * b + n16;
-                float y;
-                if (half == 0) y = kv(ri, kk) * eG(ri, kk);
-                else y = bf16_to_f32(sV[ri * LH + kk]);
+                const float y = half == 0 ? kv(ri, kk) * eG(ri, kk) : bf16_to_f32(sV[ri * LH + kk]);
                 acc = mf(sY[(16 * a + n16) * LF + kk], y, acc);
             }
             mt[t] = acc;
         }
-        __syncthreads();
     }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int tt = 2 * wave + t, a = tt >> 2, b = tt & 3;
+    __syncthreads();  // M's operands read; its bytes are free
+    for (int t = 0; t < nq; ++t) {
+        int a, b;
+        tri_ab(wave + 8 * t, a, b);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) sM[(16 * a + 4 * g4 + jj) * LA + 16 * b + n16] = mt[t][jj] * sBeta[16 * b + n16];
     }
     __syncthreads();
     // ---- Z^T = T M^T by blocks from the first (waves 0-3, one column tile each); dA_kk = -Z (strictly lower)
-    f4 zt[4];
+    // (rows a > ct of the solve give Z above the diagonal, which is not needed, and are skipped; M's upper
+    // blocks are never read)
+    f4 zt[4] = {zero4(), zero4(), zero4(), zero4()};
     if (wave < 4) {
         const int ct = wave;
         float *zc = reinterpret_cast<float *>(R) + wave * (4 * 16 * LT);
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
+            if (a > ct) break;
             f4 acc = zero4();
 #pragma unroll
             for (int b = 0; b < a; ++b)
