@@ -24,7 +24,8 @@
 //   kStates    replays each segment and keeps every chunk's S and V_new;
 //   rev_pack   turns each forward pack into the reverse one (kda_mfma.h) with
 //              A_qk^T dO on fp16 matrix cores;
-//   kRevLocal, the reverse combine, kRevOut walk the chunks last to first with
+//   kRevLocal, the reverse combine (bf16 matrix cores over P^T planes the local
+//              pass writes), kRevOut walk the chunks last to first with
 //              dS in the accumulators and keep every chunk's dS' and dV_new;
 //   grad       one workgroup per chunk and head: everything above that is
 //              local to the chunk, on fp32 matrix cores (16x16x4).
@@ -805,7 +806,7 @@ namespace {
 
 struct BwdChunkPlan {
     ChunkGradLayout fwd;
-    size_t off_rp, off_st, off_vn, off_dst, off_dvn, off_hb, off_dl, bytes;
+    size_t off_rp, off_st, off_vn, off_dst, off_dvn, off_hb, off_dl, off_pt, bytes;
 };
 
 BwdChunkPlan bwd_chunk_plan(int B, int T, int H, int N, bool varlen) {
@@ -822,6 +823,7 @@ BwdChunkPlan bwd_chunk_plan(int B, int T, int H, int N, bool varlen) {
     p.off_dvn = o; o = a256(o + sh * mc::C * mc::DV * sizeof(float));
     p.off_hb = o;  o = a256(o + seg_state);
     p.off_dl = o;  o = a256(o + seg_state);
+    p.off_pt = o;  o = a256(o + seg_state);  // P^T planes: the same bytes as a fp32 state
     p.bytes = o;
     return p;
 }
@@ -859,6 +861,7 @@ hipError_t launch_chunk_bwd(const BackwardLaunch &L) {
     gf.st = reinterpret_cast<float *>(ws + p.off_st);
     gf.vn = reinterpret_cast<float *>(ws + p.off_vn);
     gf.keep_last = true;
+    gf.pt = ws + p.off_pt;
     bool chained = false;
     void *packs = nullptr;
     const SegmentView sv = launch_chunk_grad_forward(c, gf, &chained, &packs);
@@ -876,8 +879,8 @@ hipError_t launch_chunk_bwd(const BackwardLaunch &L) {
     gr.hb = reinterpret_cast<float *>(ws + p.off_hb);
     if (chained) {
         launch_scan_grad<kRevLocal>(c, sv, max_segs, per, rp, gr);
-        launch_reverse_combine(sv, gr.hb, L.dhT, reinterpret_cast<float *>(ws + p.off_dl), L.dh0, L.H, L.N,
-                               /*planes=*/true, L.stream);
+        launch_reverse_combine_bf16(sv, gf.pt, gr.hb, L.dhT, reinterpret_cast<float *>(ws + p.off_dl), L.dh0, L.H,
+                                    L.N, L.stream);
     }
     launch_scan_grad<kRevOut>(c, sv, max_segs, per, rp, gr);
     mc::GradArgs A{};

@@ -194,6 +194,7 @@ struct ScanGrad {
     float *hb;            // kRevLocal: [segment * H + h] state gradient at the segment start from zero at its end
     bool keep_last;       // kLocal: P and H of every segment but a one-segment sequence's (the reverse combine
                           // needs P of last segments)
+    char *pt;             // kLocal: also P^T as bf16 high and low planes, [segment * H + h] 64 KiB each
 };
 template <int MODE>
 void launch_scan_grad(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, const void *packs,
@@ -217,6 +218,9 @@ SegmentView launch_chunk_grad_forward(const ChunkLaunch &L, const ScanGrad &gr, 
 // as the matrix-core path's bf16 high and low planes; dk = 128.
 void launch_reverse_combine(const SegmentView &sv, const float *hb, const float *dhT, float *dleave, float *dh0,
                             int H, int N, bool planes, hipStream_t stream);
+// The same on bf16 matrix cores for the matrix-core path (dk = dv = 128): P^T planes in pt (ScanGrad::pt).
+void launch_reverse_combine_bf16(const SegmentView &sv, const char *pt, const float *hb, const float *dhT, float *dl,
+                                 float *dh0, int H, int N, hipStream_t stream);
 bool chunk_bwd_supported(bool in_bf16, int dk, int dv);
 size_t chunk_bwd_workspace_bytes(int B, int T, int H, int N, bool varlen);
 // false when a launch would exceed a grid dimension's 32-bit thread count or the matrix-core path's

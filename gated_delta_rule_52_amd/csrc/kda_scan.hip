@@ -402,6 +402,24 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     } else if (MODE == kRevOut) {
         if (first && gr.dh0) dst = gr.dh0 + (static_cast<int64_t>(nseq) * H + h) * DK * DV;
     }
+    if (MODE == kLocal && pcols && gr.pt) {
+        // P^T planes for the gradients' reverse combine: element (c, r) of P^T at 2 (128 c + r) bytes, so the
+        // four rows 16 rt + 4 g4 .. + 3 of this lane's column are 8 contiguous bytes of each plane
+        char *ptd = gr.pt + (static_cast<int64_t>(seg) * H + h) * DK * DK * 4;
+        const rsrc_t rs = make_rsrc(ptd, 4 * DK * DK);
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                uint32_t hi0, lo0, hi1, lo1;
+                const float sc = pow2(fr[ct]);
+                split2(acc[rt][ct][0] * sc, acc[rt][ct][1] * sc, hi0, lo0);
+                split2(acc[rt][ct][2] * sc, acc[rt][ct][3] * sc, hi1, lo1);
+                const uint32_t off = 2 * ((col0 + 16 * ct + n16) * DK + 16 * rt + 4 * g4);
+                st64(rs, u2{hi0, hi1}, off);
+                st64(rs, u2{lo0, lo1}, 2 * DK * DK + off);
+            }
+    }
     if (dst && pcols) {
         // P as bf16 high and low planes (P = hi + lo to about 16 bits), the operands of the combine's
         // bf16 products: element (r, c) at 2 (128 r + c) bytes, the low plane 32 KiB further

@@ -326,10 +326,17 @@ combine_mfma_kernel(SegmentView sv, const float *h0, float *hT, int H, int DV) {
 // buffered: the B operand of block t is 16 contiguous bytes of a column, and
 // the accumulator (rows 16 w + 4 g .. + 3 of column m) goes back as 8
 // contiguous bytes per plane.  One barrier per step.
+//
+// REV runs the gradients' reverse chain the same way: from the final-state
+// gradient (h0 here), dleave(s - 1) = P_s^T dleave(s) + Hb_s from the last
+// segment down to the first, over P^T planes (pt, written by the local pass
+// beside P) and Hb (hb), storing every segment's leaving gradient in dl; an
+// empty sequence's initial-state gradient (hT here) is the final-state one.
 constexpr int kSP = 128 + 8;  // padded row stride (bf16) of the transposed state planes
 
+template <bool REV>
 __global__ void __launch_bounds__(512, 1)
-combine_bf16x3_kernel(SegmentView sv, const float *h0, float *hT, int H) {
+combine_bf16x3_kernel(SegmentView sv, const float *h0, float *hT, int H, const char *pt, const float *hb, float *dl) {
     constexpr int DK = 128, DV = 128, NC = 16;  // columns per workgroup
     typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
     typedef unsigned u4v __attribute__((ext_vector_type(4)));
@@ -354,7 +361,8 @@ combine_bf16x3_kernel(SegmentView sv, const float *h0, float *hT, int H) {
                 for (int e = 0; e < 4; ++e) hT[sbase + static_cast<int64_t>(r) * DV + j0 + cl + e] = x[e];
             return;
         }
-        float *sin = sv.sin + (static_cast<int64_t>(first) * H + h) * DK * DV;
+        float *sin = REV ? dl + (static_cast<int64_t>(end - 1) * H + h) * DK * DV
+                         : sv.sin + (static_cast<int64_t>(first) * H + h) * DK * DV;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             sin[static_cast<int64_t>(r) * DV + j0 + cl + e] = x[e];
@@ -364,17 +372,19 @@ combine_bf16x3_kernel(SegmentView sv, const float *h0, float *hT, int H) {
         }
     }
 
-    const int last_seg = end - 2;
+    // segments the chain reads: first .. end - 2 forward, end - 1 .. first + 1 reversed
+    auto seg_of = [&](int i) { return REV ? end - 1 - i : first + i; };
     struct Stage {
         u4v pa[2][4];  // P operands, [plane][block]
         f32x4 hb;      // H addends
     };
     // unconditional (past the last step it repeats that step's segment), so
     // that every path through the loop has the same memory operations
-    auto fetch = [&](int seg, Stage &st) {
-        seg = min(seg, last_seg);
-        const char *src = reinterpret_cast<const char *>(sv.P + (static_cast<int64_t>(seg) * H + h) * DK * DK);
-        const float *hs = sv.Hs + (static_cast<int64_t>(seg) * H + h) * DK * DV;
+    auto fetch = [&](int i, Stage &st) {
+        const int seg = seg_of(min(i, nsteps - 1));
+        const char *src = REV ? pt + (static_cast<int64_t>(seg) * H + h) * DK * DK * 4
+                              : reinterpret_cast<const char *>(sv.P + (static_cast<int64_t>(seg) * H + h) * DK * DK);
+        const float *hs = (REV ? hb : sv.Hs) + (static_cast<int64_t>(seg) * H + h) * DK * DV;
         const int r = 16 * wave + m;
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl)
@@ -384,7 +394,8 @@ combine_bf16x3_kernel(SegmentView sv, const float *h0, float *hT, int H) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) st.hb[jj] = hs[(16 * wave + 4 * g + jj) * DV + j0 + m];
     };
-    auto step = [&](int seg, int b, const Stage &st) {
+    auto step = [&](int i, int b, const Stage &st) {
+        const int seg = seg_of(i);
         __syncthreads();  // entering(seg) complete in sS[b]; sS[b ^ 1] no longer read
         f32x4 acc = st.hb;
 #pragma unroll
@@ -397,7 +408,8 @@ combine_bf16x3_kernel(SegmentView sv, const float *h0, float *hT, int H) {
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, sl, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, sh, acc, 0, 0, 0);
         }
-        float *sin = sv.sin + (static_cast<int64_t>(seg + 1) * H + h) * DK * DV;
+        float *sin = REV ? dl + (static_cast<int64_t>(seg - 1) * H + h) * DK * DV
+                         : sv.sin + (static_cast<int64_t>(seg + 1) * H + h) * DK * DV;
         const int r0 = 16 * wave + 4 * g;
         unsigned hw[2], lw[2];
 #pragma unroll
@@ -415,24 +427,24 @@ combine_bf16x3_kernel(SegmentView sv, const float *h0, float *hT, int H) {
     };
     // the ring: step j uses stage j mod 4, refilled for step j + 4 right after
     Stage s0, s1, s2, s3;
-    fetch(first, s0);
-    fetch(first + 1, s1);
-    fetch(first + 2, s2);
-    fetch(first + 3, s3);
+    fetch(0, s0);
+    fetch(1, s1);
+    fetch(2, s2);
+    fetch(3, s3);
     int i = 0;
     for (; i + 4 <= nsteps; i += 4) {
-        step(first + i, 0, s0);
-        fetch(first + i + 4, s0);
-        step(first + i + 1, 1, s1);
-        fetch(first + i + 5, s1);
-        step(first + i + 2, 0, s2);
-        fetch(first + i + 6, s2);
-        step(first + i + 3, 1, s3);
-        fetch(first + i + 7, s3);
+        step(i, 0, s0);
+        fetch(i + 4, s0);
+        step(i + 1, 1, s1);
+        fetch(i + 5, s1);
+        step(i + 2, 0, s2);
+        fetch(i + 6, s2);
+        step(i + 3, 1, s3);
+        fetch(i + 7, s3);
     }
-    if (i < nsteps) step(first + i, 0, s0);
-    if (i + 1 < nsteps) step(first + i + 1, 1, s1);
-    if (i + 2 < nsteps) step(first + i + 2, 0, s2);
+    if (i < nsteps) step(i, 0, s0);
+    if (i + 1 < nsteps) step(i + 1, 1, s1);
+    if (i + 2 < nsteps) step(i + 2, 0, s2);
 }
 
 }  // namespace
@@ -480,8 +492,9 @@ hipError_t launch_chunk(const ChunkLaunch &L) {
     }
     if (chained) {
         if (p.packs)  // P in bf16 planes; one workgroup per (head, 16-column slice, sequence), heads fastest
-            hipLaunchKernelGGL(combine_bf16x3_kernel, dim3(L.H, L.dv / 16, L.N), dim3(512), 0, L.stream, sv, L.h0,
-                               L.hT, L.H);
+            hipLaunchKernelGGL(combine_bf16x3_kernel<false>, dim3(L.H, L.dv / 16, L.N), dim3(512), 0, L.stream, sv,
+                               L.h0, L.hT, L.H, static_cast<const char *>(nullptr), static_cast<const float *>(nullptr),
+                               static_cast<float *>(nullptr));
         else if (L.dk == 128)  // heads fastest: a head's slices share one XCD (workgroups go round-robin over XCDs)
             hipLaunchKernelGGL(combine_mfma_kernel, dim3(L.H, L.dv / 16, L.N), dim3(256), 0, L.stream, sv, L.h0,
                                L.hT, L.H, L.dv);
@@ -521,11 +534,18 @@ SegmentView launch_chunk_grad_forward(const ChunkLaunch &L, const ScanGrad &gr, 
     launch_prep(L, sv, p.max_segs, p.per, *packs);
     if (*chained) {
         launch_scan_grad<kLocal>(L, sv, p.max_segs, p.per, *packs, gr);
-        hipLaunchKernelGGL(combine_bf16x3_kernel, dim3(L.H, L.dv / 16, L.N), dim3(512), 0, L.stream, sv, L.h0,
-                           static_cast<float *>(nullptr), L.H);
+        hipLaunchKernelGGL(combine_bf16x3_kernel<false>, dim3(L.H, L.dv / 16, L.N), dim3(512), 0, L.stream, sv,
+                           L.h0, static_cast<float *>(nullptr), L.H, static_cast<const char *>(nullptr),
+                           static_cast<const float *>(nullptr), static_cast<float *>(nullptr));
     }
     launch_scan_grad<kStates>(L, sv, p.max_segs, p.per, *packs, gr);
     return sv;
+}
+
+void launch_reverse_combine_bf16(const SegmentView &sv, const char *pt, const float *hb, const float *dhT, float *dl,
+                                 float *dh0, int H, int N, hipStream_t stream) {
+    hipLaunchKernelGGL(combine_bf16x3_kernel<true>, dim3(H, 128 / 16, N), dim3(512), 0, stream, sv, dhT, dh0, H, pt, hb,
+                       dl);
 }
 
 size_t segment_states_bytes(int B, int T, int H, int dk, int dv, int N, bool varlen, int chunk) {
