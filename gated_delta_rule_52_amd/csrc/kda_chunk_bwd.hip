@@ -164,11 +164,18 @@ rev_pack_kernel(const char *__restrict__ packs, char *__restrict__ rpacks, const
     __syncthreads();
     const int ed0 = exp_of(__int_as_float(sMax[1]));
     const float sd0 = pow2(-ed0);
+    // U = fp16(A_qk^T dO 2^-ed0), and the remainder 2^11 times larger in the UL slot
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-            *reinterpret_cast<h4 *>(rp + kPkU + u_off(2 * wave + t, a, lane)) = to_h4(d0[t][a], sd0);
+        for (int a = 0; a < 4; ++a) {
+            const h4 hi = to_h4(d0[t][a], sd0);
+            f4 rest;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) rest[jj] = (d0[t][a][jj] * sd0 - static_cast<float>(hi[jj])) * 2048.f;
+            *reinterpret_cast<h4 *>(rp + kPkU + u_off(2 * wave + t, a, lane)) = hi;
+            *reinterpret_cast<h4 *>(rp + kRvUL + u_off(2 * wave + t, a, lane)) = to_h4(rest, 1.f);
+        }
     if (tid < 32)  // gamma passes through
         *reinterpret_cast<u4 *>(rp + kPkGamma + 16 * tid) = *reinterpret_cast<const u4 *>(fp + kPkGamma + 16 * tid);
     if (tid == 32) {
@@ -178,6 +185,7 @@ rev_pack_kernel(const char *__restrict__ packs, char *__restrict__ rpacks, const
         hd[kHdrK] = fh[kHdrW];  // -W^T carries W's
         hd[kHdrU] = ed0;
         hd[kHdrDO] = edo;
+        hd[kHdrUL] = ed0 - 11;
         *reinterpret_cast<u4 *>(rp + kPkHdr) = u4{uint32_t(hd[0]), uint32_t(hd[1]), uint32_t(hd[2]), uint32_t(hd[3])};
         *reinterpret_cast<u4 *>(rp + kPkHdr + 16) = u4{uint32_t(hd[4]), uint32_t(hd[5]), uint32_t(hd[6]), uint32_t(hd[7])};
     }

@@ -194,7 +194,7 @@ constexpr int kPkBytes = kPkU + C * DV * 2;
 constexpr int kPkLocal = kPkQ;   // bytes the local pass copies to LDS
 constexpr int kPkOut = kPkU;     // bytes the output pass copies to LDS
 static_assert(kPkLocal % 1024 == 0 && kPkOut % 1024 == 0, "whole 1 KiB wave copies");
-enum { kHdrW = 0, kHdrQ = 1, kHdrK = 2, kHdrU = 3, kHdrA = 4, kHdrDO = 5 };
+enum { kHdrW = 0, kHdrQ = 1, kHdrK = 2, kHdrU = 3, kHdrA = 4, kHdrDO = 5, kHdrUL = 6 };
 
 // ---- reverse pack (gradients), one per chunk and head, same slots: the walk
 // over the chunks in reverse order carries dS (the gradient of the state a
@@ -207,9 +207,12 @@ enum { kHdrW = 0, kHdrQ = 1, kHdrK = 2, kHdrU = 3, kHdrA = 4, kHdrDO = 5 };
 //   Q   slot  Q^T          [128][64]  kt_col, exponent hdr[kHdrQ]  (Q = scale e^G q)
 //   U   slot  A_qk^T dO    accumulator order, exponent hdr[kHdrU]
 //   DO        dO           accumulator order (as U), exponent hdr[kHdrDO]
+//   UL        the rest of A_qk^T dO after U's fp16 rounding, accumulator
+//             order, exponent hdr[kHdrUL] (U + UL to about 22 bits)
 //   gamma as in the forward pack; the A slot is unused.
 constexpr int kRvDO = kPkBytes;
-constexpr int kRvBytes = kPkBytes + C * DV * 2;
+constexpr int kRvUL = kRvDO + C * DV * 2;
+constexpr int kRvBytes = kRvUL + C * DV * 2;
 constexpr int kRvStage = kPkA;  // bytes the reverse passes copy to LDS (gamma, header, W, KT, Q)
 static_assert(kRvStage % 1024 == 0, "whole 1 KiB wave copies");
 

@@ -154,7 +154,7 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     const rsrc_t rs_o = make_rsrc(static_cast<char *>(o_) + seg_base * ob, kOutPass ? ob * seg_elems : 0);
 
     // chunk j's pack -> dst and its U (and, reversed, dO) -> registers
-    auto fetch = [&](int j, char *dst, u4 (&ur)[NCT][2], u4 (&dr)[NCT][2]) {
+    auto fetch = [&](int j, char *dst, u4 (&ur)[NCT][2], u4 (&dr)[NCT][2], u4 (&ul)[NCT][2]) {
         const char *pack = packs + (static_cast<int64_t>(seg * per + j) * H + h) * kStride;
         for (int u = wave; u < kBytes / 1024; u += NW)
             __builtin_amdgcn_global_load_lds((gptr_t)(pack + 1024 * u + 16 * lane), (lptr_t)(dst + 1024 * u), 16, 0, 0);
@@ -166,25 +166,29 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
                 for (int pr = 0; pr < 2; ++pr) {
                     ur[ct][pr] = __builtin_amdgcn_raw_buffer_load_b128(rs_p, kPkU + 16 * lane,
                                                                        u_off(ctile0 + ct, 2 * pr, 0), 0);
-                    if (kRev)
+                    if (kRev) {
                         dr[ct][pr] = __builtin_amdgcn_raw_buffer_load_b128(rs_p, kRvDO + 16 * lane,
                                                                            u_off(ctile0 + ct, 2 * pr, 0), 0);
+                        ul[ct][pr] = __builtin_amdgcn_raw_buffer_load_b128(rs_p, kRvUL + 16 * lane,
+                                                                           u_off(ctile0 + ct, 2 * pr, 0), 0);
+                    }
                 }
         }
     };
     // the i-th chunk walked: first to last, or last to first in the reverse modes
     auto chunk_of = [&](int i) { return kRev ? nch - 1 - i : i; };
     // U (and dO) of the chunk in use / of the next one (zero for P)
-    u4 urA[NCT][2] = {}, urB[NCT][2] = {}, drA[NCT][2] = {}, drB[NCT][2] = {};
-    fetch(chunk_of(0), lds0, urA, drA);
+    u4 urA[NCT][2] = {}, urB[NCT][2] = {}, drA[NCT][2] = {}, drB[NCT][2] = {}, ulA[NCT][2] = {}, ulB[NCT][2] = {};
+    fetch(chunk_of(0), lds0, urA, drA, ulA);
 
     // one chunk: its pack is in L, the next one's goes to Lnext
     auto step = [&](int i, const char *L, char *Lnext, const u4 (&ur_cur)[NCT][2], u4 (&ur_nxt)[NCT][2],
-                    const u4 (&dr_cur)[NCT][2], u4 (&dr_nxt)[NCT][2]) {
+                    const u4 (&dr_cur)[NCT][2], u4 (&dr_nxt)[NCT][2], const u4 (&ul_cur)[NCT][2],
+                    u4 (&ul_nxt)[NCT][2]) {
         const int j = chunk_of(i);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // chunk j in L; every wave is done with the previous chunk
-        if (i + 1 < nch) fetch(chunk_of(i + 1), Lnext, ur_nxt, dr_nxt);
+        if (i + 1 < nch) fetch(chunk_of(i + 1), Lnext, ur_nxt, dr_nxt, ul_nxt);
 
         const int *hdr = reinterpret_cast<const int *>(L + kPkHdr);
         const int ew = hdr[kHdrW], ek = hdr[kHdrK];
@@ -257,13 +261,18 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
                             mv = fmaxf(mv, fabsf(Vn[ct][a][jj]));
                         }
                 } else {
+                    const float unl = kRev ? pow2(hdr[kHdrUL]) : 0.f;
 #pragma unroll
                     for (int a = 0; a < 4; ++a) {
                         const u4 w = ur_cur[ct][a >> 1];
                         const h4 uh = __builtin_bit_cast(h4, (a & 1) ? u2{w[2], w[3]} : u2{w[0], w[1]});
+                        const u4 wl = ul_cur[ct][a >> 1];
+                        const h4 ulh = __builtin_bit_cast(h4, (a & 1) ? u2{wl[2], wl[3]} : u2{wl[0], wl[1]});
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj) {
-                            Vn[ct][a][jj] = static_cast<float>(uh[jj]) * unu - X[ct][a][jj] * unx;
+                            float u = static_cast<float>(uh[jj]) * unu;
+                            if (kRev) u += static_cast<float>(ulh[jj]) * unl;  // A_qk^T dO to about 22 bits
+                            Vn[ct][a][jj] = u - X[ct][a][jj] * unx;
                             mv = fmaxf(mv, fabsf(Vn[ct][a][jj]));
                         }
                     }
@@ -387,8 +396,8 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
         for (int ct = 0; ct < NCT; ++ct) smax[ct] = wave_max(mx[ct]);
     };
     for (int i = 0; i < nch; i += 2) {
-        step(i, lds0, lds1, urA, urB, drA, drB);
-        if (i + 1 < nch) step(i + 1, lds1, lds0, urB, urA, drB, drA);
+        step(i, lds0, lds1, urA, urB, drA, drB, ulA, ulB);
+        if (i + 1 < nch) step(i + 1, lds1, lds0, urB, urA, drB, drA, ulB, ulA);
     }
 
     // ---- leaving state (DK = DV: H and P are both 128 x 128), or the gradient at the segment start

@@ -88,19 +88,24 @@ def test_prefill_replayed_from_a_graph(kda):
         assert torch.equal(o, o_e) and torch.equal(hT, h_e)
 
 
-def test_gradients_replayed_from_a_graph(kda):
+@pytest.mark.parametrize("path", ["token", "chunk"])
+def test_gradients_replayed_from_a_graph(kda, path):
     """kda_recurrent_bwd (segment table, local passes, both combines, the
-    gradient kernel) captured with its outputs and workspace allocated
-    beforehand, replayed three times against eager calls."""
+    gradient kernel) and kda_chunk_bwd (prep, local pass, combines, replays,
+    reverse packs, reverse passes, chunk gradients) captured with their
+    outputs and workspace allocated beforehand, replayed three times against
+    eager calls."""
     import torch
     from gated_delta_rule_52_amd.inputs import make_output_grads
     x = make_prefill(73, 1, 700, 2, 128, 128, h0_std=0.3)  # several segments per sequence
     do, dhT = make_output_grads(x, 74, dhT_std=0.3)
-    say(f"case gradients graph: T={x.T} H={x.H}")
+    say(f"case gradients graph ({path} path): T={x.T} H={x.H}")
     d = upload(x)
     dod, dht = dev(do, torch.bfloat16), dev(dhT, torch.float32)
     args = (d["q"], d["k"], d["v"], d["g"], d["beta"], dod)
-    ws = torch.empty(kda.recurrent_bwd_workspace_bytes(d["q"], d["v"]), dtype=torch.uint8, device="cuda")
+    bwd = kda.chunk_bwd if path == "chunk" else kda.recurrent_bwd
+    wsb = (kda.chunk_bwd_workspace_bytes if path == "chunk" else kda.recurrent_bwd_workspace_bytes)(d["q"], d["v"])
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     f32 = dict(dtype=torch.float32, device="cuda")
     out = {n: torch.empty(sh, **f32) for n, sh in (("dq", d["q"].shape), ("dk", d["q"].shape), ("dv", d["v"].shape),
                                                     ("dg", d["q"].shape), ("dbeta", d["beta"].shape))}
@@ -109,11 +114,10 @@ def test_gradients_replayed_from_a_graph(kda):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.graph(graph, stream=side):
-        kda.recurrent_bwd(*args, initial_state=d["h0"], grad_final_state=dht, grad_initial_state=dh0,
-                          workspace=ws, out=out)
+        bwd(*args, initial_state=d["h0"], grad_final_state=dht, grad_initial_state=dh0, workspace=ws, out=out)
     torch.cuda.synchronize()
     for rep in range(3):
-        ref = kda.recurrent_bwd(*args, initial_state=d["h0"], grad_final_state=dht)
+        ref = bwd(*args, initial_state=d["h0"], grad_final_state=dht)
         torch.cuda.synchronize()
         for t in out.values():
             t.fill_(float("nan"))
