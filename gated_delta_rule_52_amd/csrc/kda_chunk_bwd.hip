@@ -22,8 +22,8 @@
 //
 // Passes: the forward segmented prefill's prep, local pass and combine, then
 //   kStates    replays each segment and keeps every chunk's S and V_new;
-//   rev_pack   turns each forward pack into the reverse one (kda_mfma.h) with
-//              A_qk^T dO on fp16 matrix cores;
+//   rev_pack   completes each reverse pack (kda_mfma.h; the prep wrote its
+//              transposed slots) with A_qk^T dO on fp16 matrix cores;
 //   kRevLocal, the reverse combine (bf16 matrix cores over P^T planes the local
 //              pass writes), kRevOut walk the chunks last to first with
 //              dS in the accumulators and keep every chunk's dS' and dV_new;
@@ -40,11 +40,13 @@ namespace {
 constexpr int kRpThreads = 256;
 constexpr int kDOP = DV + 8;  // row stride (halves) of the staged dO
 
+// The reverse pack's -Kd, -W^T and Q^T slots come from the prep (its RV instantiation, from the same fp16
+// values as the forward pack); this kernel adds A_qk^T dO (with its remainder plane), dO, gamma and the header.
 __global__ void __launch_bounds__(kRpThreads)
 rev_pack_kernel(const char *__restrict__ packs, char *__restrict__ rpacks, const uint16_t *__restrict__ d_o,
                 SegmentView sv, int per, int H) {
-    constexpr int kFwd = kPkU - kPkW;  // the W, KT, Q and A slots of the forward pack
-    __shared__ __attribute__((aligned(16))) char sF[kFwd];
+    constexpr int kA = kPkU - kPkA;  // the A_qk blocks of the forward pack
+    __shared__ __attribute__((aligned(16))) char sF[kA];
     __shared__ __attribute__((aligned(16))) uint16_t sDO[C * kDOP];
     __shared__ int sMax[2];
     const int h = static_cast<int>(blockIdx.x % static_cast<unsigned>(H));  // heads fastest
@@ -60,8 +62,8 @@ rev_pack_kernel(const char *__restrict__ packs, char *__restrict__ rpacks, const
     const char *fp = packs + (static_cast<int64_t>(slot) * H + h) * kPkBytes;
     char *rp = rpacks + (static_cast<int64_t>(slot) * H + h) * kRvBytes;
     if (tid < 2) sMax[tid] = 0;
-    for (int u = tid; u < kFwd / 16; u += kRpThreads)
-        *reinterpret_cast<u4 *>(sF + 16 * u) = *reinterpret_cast<const u4 *>(fp + kPkW + 16 * u);
+    for (int u = tid; u < kA / 16; u += kRpThreads)
+        *reinterpret_cast<u4 *>(sF + 16 * u) = *reinterpret_cast<const u4 *>(fp + kPkA + 16 * u);
     uint32_t mx = 0u;
     for (int u = tid; u < C * (DV / 8); u += kRpThreads) {  // dO rows, 16 bytes at a time; rows past L are 0
         const int r = u / (DV / 8), cu = u % (DV / 8);
@@ -79,37 +81,6 @@ rev_pack_kernel(const char *__restrict__ packs, char *__restrict__ rpacks, const
     const float sdo = pow2(-edo);
     const int *fh = reinterpret_cast<const int *>(fp + kPkHdr);
 
-    // -Kd in the W slot (w_col): unit u of row r holds columns 32p + 4g .. +3 and 32p + 16 + 4g .. +3
-    for (int idx = tid; idx < C * 16; idx += kRpThreads) {
-        const int r = idx >> 4, u = idx & 15, p = u >> 2, g = u & 3;
-        uint16_t e[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            e[i] = *reinterpret_cast<const uint16_t *>(sF + (kPkKT - kPkW) + kt_col(32 * p + 4 * g + i, r)) ^ 0x8000u;
-            e[4 + i] =
-                *reinterpret_cast<const uint16_t *>(sF + (kPkKT - kPkW) + kt_col(32 * p + 16 + 4 * g + i, r)) ^ 0x8000u;
-        }
-        const u4 w = {e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16), e[4] | (uint32_t(e[5]) << 16),
-                      e[6] | (uint32_t(e[7]) << 16)};
-        *reinterpret_cast<u4 *>(rp + kPkW + r * 256 + ((u ^ (r & 15)) << 4)) = w;
-    }
-    // -W^T in the KT slot and Q^T in the Q slot (kt_col): unit u of channel row c holds chunk rows
-    // 32p + 4g .. +3 and 32p + 16 + 4g .. +3
-    for (int idx = tid; idx < 2 * DK * 8; idx += kRpThreads) {
-        const int which = idx / (DK * 8), rem = idx % (DK * 8);  // 0: -W^T, 1: Q^T
-        const int c = rem >> 3, u = rem & 7, p = u >> 2, g = u & 3;
-        const int src = which == 0 ? 0 : (kPkQ - kPkW);
-        const uint32_t neg = which == 0 ? 0x8000u : 0u;
-        uint16_t e[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            e[i] = *reinterpret_cast<const uint16_t *>(sF + src + w_col(32 * p + 4 * g + i, c)) ^ neg;
-            e[4 + i] = *reinterpret_cast<const uint16_t *>(sF + src + w_col(32 * p + 16 + 4 * g + i, c)) ^ neg;
-        }
-        const u4 w = {e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16), e[4] | (uint32_t(e[5]) << 16),
-                      e[6] | (uint32_t(e[7]) << 16)};
-        *reinterpret_cast<u4 *>(rp + (which == 0 ? kPkKT : kPkQ) + c * 128 + ((u ^ ((c >> 1) & 7)) << 4)) = w;
-    }
     // dO in accumulator order (as U), x 2^-edo
     for (int idx = tid; idx < 8 * 2 * 64; idx += kRpThreads) {
         const int ct = idx >> 7, pr = (idx >> 6) & 1, ln = idx & 63;
@@ -145,7 +116,7 @@ rev_pack_kernel(const char *__restrict__ packs, char *__restrict__ rpacks, const
 #pragma unroll
             for (int b = a; b < 4; ++b) {
                 const int p = b * (b + 1) / 2 + a;
-                const _Float16 *blk = reinterpret_cast<const _Float16 *>(sF + (kPkA - kPkW) + 512 * p);
+                const _Float16 *blk = reinterpret_cast<const _Float16 *>(sF + 512 * p);
                 h4 av;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) av[i] = blk[4 * (16 * (n16 >> 2) + 4 * g4 + i) + (n16 & 3)];
@@ -872,10 +843,10 @@ hipError_t launch_chunk_bwd(const BackwardLaunch &L) {
     gf.pt = ws + p.off_pt;
     bool chained = false;
     void *packs = nullptr;
-    const SegmentView sv = launch_chunk_grad_forward(c, gf, &chained, &packs);
+    char *rp = ws + p.off_rp;
+    const SegmentView sv = launch_chunk_grad_forward(c, gf, rp, &chained, &packs);
     const int per = p.fwd.per, max_segs = p.fwd.max_segs;
     const unsigned blocks = static_cast<unsigned>(max_segs) * static_cast<unsigned>(per) * L.H;
-    char *rp = ws + p.off_rp;
     hipLaunchKernelGGL(mc::rev_pack_kernel, dim3(blocks), dim3(mc::kRpThreads), 0, L.stream,
                        static_cast<const char *>(packs), rp, static_cast<const uint16_t *>(L.d_o), sv, per, L.H);
     ScanGrad gr{};

@@ -176,7 +176,9 @@ void launch_segment_combine(const ChunkLaunch &L, const SegmentStates &s);
 // (kda_prep.hip); the local and output passes stream them (kda_scan.hip).
 bool f16_path_supported(bool in_bf16, int dk, int dv, int chunk);
 size_t pack_bytes();  // bytes of one operand pack
-void launch_prep(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, void *packs);
+// rpacks (the gradients only): also the reverse packs' -Kd, -W^T and Q^T slots (kda_mfma.h)
+void launch_prep(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, void *packs,
+                 void *rpacks = nullptr);
 template <int MODE>
 void launch_scan(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, const void *packs);
 
@@ -210,10 +212,11 @@ struct ChunkGradLayout {
     bool packs;    // the matrix-core path applies
 };
 ChunkGradLayout chunk_grad_layout(int B, int T, int H, int N, bool varlen);
-// Runs the forward part into L.workspace (chunk_grad_layout().bytes) and the kStates replay into gr.st and
-// gr.vn; *chained tells whether any sequence has more than one segment (else the local pass, the combines
+// Runs the forward part into L.workspace (chunk_grad_layout().bytes), the reverse packs' transposed slots
+// into rpacks, and the kStates replay into gr.st and gr.vn; *chained tells whether any sequence has more than one segment (else the local pass, the combines
 // and kRevLocal have nothing to do), *packs where the operand packs are.
-SegmentView launch_chunk_grad_forward(const ChunkLaunch &L, const ScanGrad &gr, bool *chained, void **packs);
+SegmentView launch_chunk_grad_forward(const ChunkLaunch &L, const ScanGrad &gr, void *rpacks, bool *chained,
+                                      void **packs);
 // The reverse combine of the segment gradients (kda_backward.hip): P from sv.P as fp32 or, with planes,
 // as the matrix-core path's bf16 high and low planes; dk = 128.
 void launch_reverse_combine(const SegmentView &sv, const float *hb, const float *dhT, float *dleave, float *dh0,

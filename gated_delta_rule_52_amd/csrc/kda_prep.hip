@@ -111,17 +111,19 @@ __device__ __forceinline__ int offdiag_index(int a, int b) {  // b < a
 constexpr float kLog2e = 1.4426950408889634f;
 
 // One chunk: chunk bx % per of segment bx / per, head h, into pack number
-// bx * H + h.  EXACT = false is the matrix-core path; a chunk whose decay
+// bx * H + h.  RV (for the gradients) also writes the reverse pack's -Kd,
+// -W^T and Q^T slots (kda_mfma.h) from the same fp16 values, into rpacks.  EXACT = false is the matrix-core path; a chunk whose decay
 // exceeds exp(-kMaxChunkDecay) in some channel is not written there but
 // appended to the exact list, and EXACT = true redoes it with the pair-by-pair
 // Gram blocks.  Returns early (whole workgroup) for chunks past the segment end.
-template <bool EXACT, bool XF, bool SG>
+template <bool EXACT, bool XF, bool SG, bool RV>
 __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, int bx, int h,
                                            const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                            const uint16_t *__restrict__ v, const float *__restrict__ g,
                                            const uint16_t *__restrict__ beta, const SegmentView &sv, int per,
-                                           int H, float scale, char *packs, const InputXform ix) {
+                                           int H, float scale, char *packs, const InputXform ix, char *rpacks) {
     static_assert(!SG || (XF && !EXACT), "the scalar gate runs in the transform instantiation, fast path only");
+    static_assert(!RV || (!XF && !SG), "the reverse pack serves the gradients, which take no input transform");
     const int seg = bx / per, jc = bx - seg * per;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -149,6 +151,8 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
     const rsrc_t rs_gs = make_rsrc(g + (sg ? c0 * H + h : 0), sg ? 4 * static_cast<uint32_t>((L - 1) * H + 1) : 0);
     char *pack = packs + (static_cast<int64_t>(bx) * H + h) * kPkBytes;
     const rsrc_t rs_p = make_rsrc(pack, kPkBytes);
+    const rsrc_t rs_r = make_rsrc(RV ? rpacks + (static_cast<int64_t>(bx) * H + h) * kRvBytes : nullptr,
+                                  RV ? kRvBytes : 0);
     const uint32_t key_lane = 8 * rq8 * tok_stride + 2 * cq;
 
     if (tid < 8) sm.imax[tid] = 0;
@@ -305,6 +309,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
             em_sq[e] = em * sq;
         }
         uint32_t kdp[2][4];  // rows of e^{G_L - G} k, two per 32 bits, per channel
+        uint32_t qdp[2][4];  // RV: the same for the rows of Q
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const int r = 8 * rq8 + m;
@@ -353,11 +358,19 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
             ekp[hh][m] = pack_h2(ekv[0], ekv[1]);
             // Q: the channel pair (hh HC + 2cq, +1) of row r is 4 bytes of a 16-byte unit
             st32(rs_p, pack_h2(qsv[0], qsv[1]), kPkQ + w_col(r, hh * HC + 2 * cq));
+            uint32_t kdw = 0u;
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const uint32_t hb = hbits(static_cast<_Float16>(kdv[e]));
                 kdp[e][m >> 1] = (m & 1) ? (kdp[e][m >> 1] | (hb << 16)) : hb;
+                kdw |= hb << (16 * e);
+                if constexpr (RV) {
+                    const uint32_t qb = hbits(static_cast<_Float16>(qsv[e]));
+                    qdp[e][m >> 1] = (m & 1) ? (qdp[e][m >> 1] | (qb << 16)) : qb;
+                }
             }
+            if constexpr (RV)  // -Kd, row-major like W (the sign bits flipped)
+                st32(rs_r, kdw ^ 0x80008000u, kPkW + w_col(r, hh * HC + 2 * cq));
             if constexpr (!EXACT) {
                 uint32_t hi, lo;
                 split2(ra[0], ra[1], hi, lo);
@@ -376,7 +389,11 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
         for (int e = 0; e < 2; ++e)
 #pragma unroll
             for (int t = 0; t < 2; ++t)
+            {
                 st64(rs_p, u2{kdp[e][2 * t], kdp[e][2 * t + 1]}, kPkKT + kt_col(hh * HC + 2 * cq + e, 8 * rq8 + 4 * t));
+                if constexpr (RV)  // Q^T, laid out like KT
+                    st64(rs_r, u2{qdp[e][2 * t], qdp[e][2 * t + 1]}, kPkQ + kt_col(hh * HC + 2 * cq + e, 8 * rq8 + 4 * t));
+            }
         if constexpr (!EXACT) {
             __syncthreads();  // (3a) this half's operands in LDS
 #pragma unroll
@@ -616,6 +633,10 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
                 // U straight to the pack, in accumulator order
                 const h4 uh = to_h4(Ur[t][a], suv);
                 st64(rs_p, __builtin_bit_cast(u2, uh), kPkU + u_off(ct, a, lane));
+                if constexpr (RV) {  // -W^T, laid out like KT: rows 16 a + 4 g4 .. + 3 of column col are 8 bytes
+                    const u2 wh = __builtin_bit_cast(u2, to_h4(Wr[t][a], swv));
+                    st64(rs_r, u2{wh[0] ^ 0x80008000u, wh[1] ^ 0x80008000u}, kPkKT + kt_col(col, 16 * a + 4 * g4));
+                }
             }
         }
     }
@@ -646,28 +667,28 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
 
 // fast path: one workgroup per chunk and head; grid.x = (segment * per + chunk) * H + head.
 // XF: with the input transforms; SG: scalar gate (implies XF).
-template <bool XF, bool SG>
+template <bool XF, bool SG, bool RV>
 __global__ void __launch_bounds__(NT, 3)
 chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                   const uint16_t *__restrict__ v, const float *__restrict__ g,
                   const uint16_t *__restrict__ beta, SegmentView sv, int per, int H, float scale,
-                  char *__restrict__ packs, InputXform ix) {
+                  char *__restrict__ packs, InputXform ix, char *__restrict__ rpacks) {
     __shared__ PrepSmem sm;
     // heads fastest: the workgroups in flight at once cover whole token rows ([T, H, d]: a chunk's H heads
     // read adjacent 256-byte pieces of the same rows) and write consecutive packs (measured at 64K x 16 heads:
     // 1.028 -> 0.984 ms per call against chunks fastest)
     const int h = static_cast<int>(blockIdx.x % static_cast<unsigned>(H));
     const int bx = static_cast<int>(blockIdx.x / static_cast<unsigned>(H));
-    prep_chunk<false, XF, SG>(sm, nullptr, nullptr, bx, h, q, k, v, g, beta, sv, per, H, scale, packs, ix);
+    prep_chunk<false, XF, SG, RV>(sm, nullptr, nullptr, bx, h, q, k, v, g, beta, sv, per, H, scale, packs, ix, rpacks);
 }
 
 // exact path over the chunks the fast path listed (usually none)
-template <bool XF>
+template <bool XF, bool RV>
 __global__ void __launch_bounds__(NT, 1)
 chunk_prep_exact_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                         const uint16_t *__restrict__ v, const float *__restrict__ g,
                         const uint16_t *__restrict__ beta, SegmentView sv, int per, int H, float scale,
-                        char *__restrict__ packs, InputXform ix) {
+                        char *__restrict__ packs, InputXform ix, char *__restrict__ rpacks) {
     __shared__ PrepSmem sm;
     __shared__ float gx[C * GP];  // G of the chunk, for the pair-by-pair Gram entries
     __shared__ float nx[2 * C];   // XF: 1/|k| and 1/|q| of each row
@@ -675,7 +696,8 @@ chunk_prep_exact_kernel(const uint16_t *__restrict__ q, const uint16_t *__restri
     for (int i = blockIdx.x; i < n; i += gridDim.x) {
         const int id = sv.xlist[i];
         __syncthreads();  // the previous chunk's last LDS reads are done
-        prep_chunk<true, XF, false>(sm, gx, nx, id / H, id % H, q, k, v, g, beta, sv, per, H, scale, packs, ix);
+        prep_chunk<true, XF, false, RV>(sm, gx, nx, id / H, id % H, q, k, v, g, beta, sv, per, H, scale, packs, ix,
+                                        rpacks);
     }
 }
 
@@ -688,23 +710,29 @@ bool f16_path_supported(bool in_bf16, int dk, int dv, int chunk) {
 
 size_t pack_bytes() { return mc::kPkBytes; }
 
-void launch_prep(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, void *packs) {
+void launch_prep(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, void *packs, void *rpacks) {
     const uint16_t *q = static_cast<const uint16_t *>(L.q), *k = static_cast<const uint16_t *>(L.k);
     const uint16_t *v = static_cast<const uint16_t *>(L.v), *b = static_cast<const uint16_t *>(L.beta);
-    char *pk = static_cast<char *>(packs);
-    if (L.xf.scalar_gate) {  // the scalar-gate Gram is exact at any decay: no exact pass
-        hipLaunchKernelGGL((mc::chunk_prep_kernel<true, true>), dim3(static_cast<unsigned>(max_segs) * static_cast<unsigned>(per) * L.H), dim3(mc::NT), 0, L.stream,
-                           q, k, v, L.g, b, sv, per, L.H, L.scale, pk, L.xf);
+    char *pk = static_cast<char *>(packs), *rp = static_cast<char *>(rpacks);
+    const dim3 grid(static_cast<unsigned>(max_segs) * static_cast<unsigned>(per) * L.H), block(mc::NT);
+    if (rp) {  // the gradients: no input transform, and the reverse pack's slots besides
+        hipLaunchKernelGGL((mc::chunk_prep_kernel<false, false, true>), grid, block, 0, L.stream, q, k, v, L.g, b, sv,
+                           per, L.H, L.scale, pk, L.xf, rp);
+        hipLaunchKernelGGL((mc::chunk_prep_exact_kernel<false, true>), dim3(256), block, 0, L.stream, q, k, v, L.g, b,
+                           sv, per, L.H, L.scale, pk, L.xf, rp);
+    } else if (L.xf.scalar_gate) {  // the scalar-gate Gram is exact at any decay: no exact pass
+        hipLaunchKernelGGL((mc::chunk_prep_kernel<true, true, false>), grid, block, 0, L.stream, q, k, v, L.g, b, sv,
+                           per, L.H, L.scale, pk, L.xf, rp);
     } else if (L.xf.any()) {
-        hipLaunchKernelGGL((mc::chunk_prep_kernel<true, false>), dim3(static_cast<unsigned>(max_segs) * static_cast<unsigned>(per) * L.H), dim3(mc::NT), 0, L.stream, q, k, v,
-                           L.g, b, sv, per, L.H, L.scale, pk, L.xf);
-        hipLaunchKernelGGL(mc::chunk_prep_exact_kernel<true>, dim3(256), dim3(mc::NT), 0, L.stream, q, k, v, L.g, b,
-                           sv, per, L.H, L.scale, pk, L.xf);
+        hipLaunchKernelGGL((mc::chunk_prep_kernel<true, false, false>), grid, block, 0, L.stream, q, k, v, L.g, b, sv,
+                           per, L.H, L.scale, pk, L.xf, rp);
+        hipLaunchKernelGGL((mc::chunk_prep_exact_kernel<true, false>), dim3(256), block, 0, L.stream, q, k, v, L.g, b,
+                           sv, per, L.H, L.scale, pk, L.xf, rp);
     } else {
-        hipLaunchKernelGGL((mc::chunk_prep_kernel<false, false>), dim3(static_cast<unsigned>(max_segs) * static_cast<unsigned>(per) * L.H), dim3(mc::NT), 0, L.stream, q, k,
-                           v, L.g, b, sv, per, L.H, L.scale, pk, L.xf);
-        hipLaunchKernelGGL(mc::chunk_prep_exact_kernel<false>, dim3(256), dim3(mc::NT), 0, L.stream, q, k, v, L.g, b,
-                           sv, per, L.H, L.scale, pk, L.xf);
+        hipLaunchKernelGGL((mc::chunk_prep_kernel<false, false, false>), grid, block, 0, L.stream, q, k, v, L.g, b, sv,
+                           per, L.H, L.scale, pk, L.xf, rp);
+        hipLaunchKernelGGL((mc::chunk_prep_exact_kernel<false, false>), dim3(256), block, 0, L.stream, q, k, v, L.g, b,
+                           sv, per, L.H, L.scale, pk, L.xf, rp);
     }
 }
 

@@ -512,7 +512,8 @@ ChunkGradLayout chunk_grad_layout(int B, int T, int H, int N, bool varlen) {
     return ChunkGradLayout{p.bytes, p.per, p.max_segs, p.packs};
 }
 
-SegmentView launch_chunk_grad_forward(const ChunkLaunch &L, const ScanGrad &gr, bool *chained, void **packs) {
+SegmentView launch_chunk_grad_forward(const ChunkLaunch &L, const ScanGrad &gr, void *rpacks, bool *chained,
+                                      void **packs) {
     const bool varlen = L.cu_seqlens != nullptr;
     const Plan p = make_plan(L.B, L.T, L.H, L.dk, L.dv, L.N, L.chunk, varlen, L.in_bf16);
     char *ws = static_cast<char *>(L.workspace);
@@ -531,7 +532,7 @@ SegmentView launch_chunk_grad_forward(const ChunkLaunch &L, const ScanGrad &gr, 
                        reinterpret_cast<int32_t *>(ws + p.off_seq), sv.xcount);
     *packs = ws + p.off_pack;
     *chained = varlen || L.T == 0 || L.T > p.seg_len;
-    launch_prep(L, sv, p.max_segs, p.per, *packs);
+    launch_prep(L, sv, p.max_segs, p.per, *packs, rpacks);
     if (*chained) {
         launch_scan_grad<kLocal>(L, sv, p.max_segs, p.per, *packs, gr);
         hipLaunchKernelGGL(combine_bf16x3_kernel<false>, dim3(L.H, L.dv / 16, L.N), dim3(512), 0, L.stream, sv,
