@@ -266,10 +266,12 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
         for (int e = 0; e < 4; ++e) split_hl(x[e], ph[(row + e) * LH + col], pl[(row + e) * LH + col]);
     };
     if (tid == 0) *sFlag = 0;
+    f4 pS[8];  // this thread's S units, kept for dgamma in phase 2
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int u = tid + kGT * i;
-        put_unit(sSh, sSl, u, 8, *reinterpret_cast<const f4 *>(St + 4 * u));
+        pS[i] = *reinterpret_cast<const f4 *>(St + 4 * u);
+        put_unit(sSh, sSl, u, 8, pS[i]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -284,14 +286,10 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
         *reinterpret_cast<u4 *>(sO + r * LH + 8 * cu) = w;
     }
     __syncthreads();
-    // phase 2's inputs, fetched while phase 1 computes
-    f4 pdS[8], pS[8], pVn[4];
+    // phase 2's inputs, fetched while phase 1 computes (dS' units match the S units above)
+    f4 pdS[8], pVn[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int u = tid + kGT * i;
-        pdS[i] = *reinterpret_cast<const f4 *>(dSt + 4 * u);
-        pS[i] = *reinterpret_cast<const f4 *>(St + 4 * u);
-    }
+    for (int i = 0; i < 8; ++i) pdS[i] = *reinterpret_cast<const f4 *>(dSt + 4 * (tid + kGT * i));
 #pragma unroll
     for (int i = 0; i < 4; ++i) pVn[i] = *reinterpret_cast<const f4 *>(Vt + 4 * (tid + kGT * i));
     __builtin_amdgcn_sched_barrier(0);
