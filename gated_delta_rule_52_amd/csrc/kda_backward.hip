@@ -606,8 +606,7 @@ local_passes_kernel(BackwardLaunch L, SegmentView sv, float *hb) {
 // (P_s the segment's forward transition, Hb_s from the reverse local pass).  Sequences of one segment
 // are left to the token kernel; an empty one gets its initial-state gradient here (the final-state
 // gradient itself).  fp32 FMA, P_s staged in LDS.
-// With Planes, P_s is read as the matrix-core path's bf16 high and low planes (P = hi + lo).
-template <int DK, bool Planes = false>
+template <int DK>
 __global__ void __launch_bounds__(256)
 reverse_combine_kernel(SegmentView sv, const float *hb, const float *dhT, float *dleave, float *dh0, int H, int DV) {
     constexpr int BV = 16, DKP = DK + 1, RG = 256 / BV, ROWS = DK / RG, PV4 = DK * DK / 4 / 256;
@@ -636,27 +635,14 @@ reverse_combine_kernel(SegmentView sv, const float *hb, const float *dhT, float 
         if (seg == first) break;
         __syncthreads();  // the previous product has finished with sP and sS
         const float4 *src = reinterpret_cast<const float4 *>(sv.P + (static_cast<int64_t>(seg) * H + h) * DK * DK);
-        if constexpr (Planes) {
-            const uint2 *hi = reinterpret_cast<const uint2 *>(src), *lo = hi + DK * DK / 4;
 #pragma unroll
-            for (int mm = 0; mm < PV4; ++mm) {
-                const uint2 ph = hi[tid + 256 * mm], pl = lo[tid + 256 * mm];
-                const int e = 4 * (tid + 256 * mm), r = e / DK, cc = e % DK;
-                sP[r * DKP + cc] = bf16_to_f32(ph.x & 0xffffu) + bf16_to_f32(pl.x & 0xffffu);
-                sP[r * DKP + cc + 1] = bf16_to_f32(ph.x >> 16) + bf16_to_f32(pl.x >> 16);
-                sP[r * DKP + cc + 2] = bf16_to_f32(ph.y & 0xffffu) + bf16_to_f32(pl.y & 0xffffu);
-                sP[r * DKP + cc + 3] = bf16_to_f32(ph.y >> 16) + bf16_to_f32(pl.y >> 16);
-            }
-        } else {
-#pragma unroll
-            for (int mm = 0; mm < PV4; ++mm) {
-                const float4 pv = src[tid + 256 * mm];
-                const int e = 4 * (tid + 256 * mm), r = e / DK, cc = e % DK;
-                sP[r * DKP + cc] = pv.x;
-                sP[r * DKP + cc + 1] = pv.y;
-                sP[r * DKP + cc + 2] = pv.z;
-                sP[r * DKP + cc + 3] = pv.w;
-            }
+        for (int mm = 0; mm < PV4; ++mm) {
+            const float4 pv = src[tid + 256 * mm];
+            const int e = 4 * (tid + 256 * mm), r = e / DK, cc = e % DK;
+            sP[r * DKP + cc] = pv.x;
+            sP[r * DKP + cc + 1] = pv.y;
+            sP[r * DKP + cc + 2] = pv.z;
+            sP[r * DKP + cc + 3] = pv.w;
         }
 #pragma unroll
         for (int u = 0; u < ROWS; ++u) sS[(ig + RG * u) * BV + j] = x[u];
@@ -875,17 +861,6 @@ static hipError_t launch_bwd(const BackwardLaunch &Lin) {
         hipLaunchKernelGGL((bwd_finish_kernel<DK>), dim3(static_cast<unsigned>((units + 3) / 4)), dim3(256), 0,
                            Lin.stream, Lin, X, units);
     return hipGetLastError();
-}
-
-void launch_reverse_combine(const SegmentView &sv, const float *hb, const float *dhT, float *dleave, float *dh0,
-                            int H, int N, bool planes, hipStream_t stream) {
-    constexpr int DK = 128, DV = 128;
-    if (planes)
-        hipLaunchKernelGGL((reverse_combine_kernel<DK, true>), dim3(DV / 16, H, N), dim3(256), 0, stream, sv, hb, dhT,
-                           dleave, dh0, H, DV);
-    else
-        hipLaunchKernelGGL((reverse_combine_kernel<DK, false>), dim3(DV / 16, H, N), dim3(256), 0, stream, sv, hb,
-                           dhT, dleave, dh0, H, DV);
 }
 
 hipError_t launch_backward(const BackwardLaunch &L) {

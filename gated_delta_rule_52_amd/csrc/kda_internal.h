@@ -217,11 +217,8 @@ ChunkGradLayout chunk_grad_layout(int B, int T, int H, int N, bool varlen);
 // and kRevLocal have nothing to do), *packs where the operand packs are.
 SegmentView launch_chunk_grad_forward(const ChunkLaunch &L, const ScanGrad &gr, void *rpacks, bool *chained,
                                       void **packs);
-// The reverse combine of the segment gradients (kda_backward.hip): P from sv.P as fp32 or, with planes,
-// as the matrix-core path's bf16 high and low planes; dk = 128.
-void launch_reverse_combine(const SegmentView &sv, const float *hb, const float *dhT, float *dleave, float *dh0,
-                            int H, int N, bool planes, hipStream_t stream);
-// The same on bf16 matrix cores for the matrix-core path (dk = dv = 128): P^T planes in pt (ScanGrad::pt).
+// The gradients' reverse combine on bf16 matrix cores for the matrix-core path (dk = dv = 128, kda_segments.hip):
+// dleave(s - 1) = P_s^T dleave(s) + Hb_s over the P^T planes in pt (ScanGrad::pt).
 void launch_reverse_combine_bf16(const SegmentView &sv, const char *pt, const float *hb, const float *dhT, float *dl,
                                  float *dh0, int H, int N, hipStream_t stream);
 bool chunk_bwd_supported(bool in_bf16, int dk, int dv);
