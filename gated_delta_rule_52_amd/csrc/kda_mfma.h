@@ -136,6 +136,15 @@ __device__ __forceinline__ float half_wave_sum(float x) {
     return x + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
 }
 
+// Sum over each row of 16 lanes, the result in every lane of the row: the
+// first four butterflies of half_wave_sum.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_move<0xB1>(x);
+    x += dpp_move<0x4E>(x);
+    x += dpp_move<0x141>(x);
+    return x + dpp_move<0x140>(x);
+}
+
 // Buffer resource over [base, base + bytes): raw buffer accesses at or past
 // the end read as zero and their stores are dropped.  Offsets are 32-bit
 // bytes from a wave-uniform base, so ragged tails need no masking and no

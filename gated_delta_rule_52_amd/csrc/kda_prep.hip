@@ -87,8 +87,12 @@ struct alignas(16) PrepSmem {
             alignas(16) _Float16 akk[6][64 * 4];    // off-diagonal blocks of A_kk, x 2^-2ek, in lane order
             alignas(16) _Float16 aqk[10][64 * 4];   // blocks of A_qk (incl. scale), x 2^-(eq+ek), in lane order
             alignas(16) _Float16 tinv[4][16 * BP];  // diagonal blocks of T, x 2^-et
+            // v of the chunk (bf16), written after the Gram products: rows of 256 bytes whose 16-byte units
+            // are XOR-swizzled by 2 ((row / 4) mod 4), so that the solve's reads in accumulator layout (four
+            // rows four apart, 32 bytes of each) fall on distinct banks
+            alignas(16) uint16_t v[C * DV];
         } s;
-        float part[8][DK];  // column sums of g per group of eight rows (dead before the Gram operands)
+        float part[C / 4][DK];  // column sums of g per group of four rows (dead before the Gram operands)
     } op;
     float beta[C];
     alignas(16) float gam[DK];             // exp(G_last) per channel
@@ -128,9 +132,10 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
-    // key-side ownership: channels {2cq, 2cq + 1} and {HC + 2cq, HC + 2cq + 1}
-    // of rows 8 rq8 .. 8 rq8 + 7
-    const int cq = tid & 31, rq8 = tid >> 5;
+    // key-side ownership: channels hh HC + 4 cq .. + 3 of both halves hh of dk, of rows 4 rq .. 4 rq + 3.
+    // The 16 lanes of one DPP row hold a whole token row, and every load moves 8 bytes of a bf16 input or
+    // 16 bytes of the gate.
+    const int cq = tid & 15, rq = tid >> 4;
     if (seg >= sv.count()) return;
     const int4 sd = sv.table[seg];
     const int64_t c0 = sd.y + static_cast<int64_t>(C) * jc, t1 = sd.z;
@@ -153,69 +158,83 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
     const rsrc_t rs_p = make_rsrc(pack, kPkBytes);
     const rsrc_t rs_r = make_rsrc(RV ? rpacks + (static_cast<int64_t>(bx) * H + h) * kRvBytes : nullptr,
                                   RV ? kRvBytes : 0);
-    const uint32_t key_lane = 8 * rq8 * tok_stride + 2 * cq;
+    const uint32_t key_lane = 4 * rq * tok_stride + 4 * cq;
 
     if (tid < 8) sm.imax[tid] = 0;
+    // v in 16-byte units (unit tid + NT i: row / 16, 8 channels), consumed by the solve (a4) after a trip
+    // through LDS.  Without the input transforms the loads are issued first, so that they are long done
+    // when the units are staged after the Gram products; the transforms' extra registers leave no room to
+    // hold them that long, and there they are issued once the Gram operands are dead.
+    u4 vraw[C * DV / 8 / NT];
+    auto load_v = [&]() {
+#pragma unroll
+        for (int i = 0; i < C * DV / 8 / NT; ++i) {
+            const int u = tid + NT * i;
+            vraw[i] = __builtin_amdgcn_raw_buffer_load_b128(rs_v, 2 * ((u >> 4) * tok_stride + 8 * (u & 15)), 0, 0);
+        }
+    };
+    if constexpr (!XF) load_v();
     __syncthreads();
 
     // ============ a1: raw inputs to registers, maxima, chunk-local cumulative decay ============
-    float G[2][8][2];  // [half][row][channel]
-    uint32_t rk[2][8], rq[2][8];
-    float nk[8], nq[8];  // XF: 1/|k| and 1/|q| of each of this thread's rows (1 without the L2 norm)
+    float G[2][4][4];  // [half][row][channel]
+    u2 rk[2][4], rqv[2][4];  // four bf16 channels of k and q per [half][row]
+    float nk[4], nq[4];  // XF: 1/|k| and 1/|q| of each of this thread's rows (1 without the L2 norm)
     {
         uint32_t mk2 = 0u, mq2 = 0u;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            float r0 = 0.f, r1 = 0.f;
+            float run[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
+            for (int m = 0; m < 4; ++m) {
                 const uint32_t e = m * tok_stride + hh * HC + key_lane;
-                u2 gg;
+                float gv[4];
                 if (sg) {
-                    const uint32_t gs = ld32(rs_gs, 4 * (8 * rq8 + m) * static_cast<uint32_t>(H));
-                    gg = u2{gs, gs};
+                    const float gs = __uint_as_float(ld32(rs_gs, 4 * (4 * rq + m) * static_cast<uint32_t>(H)));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) gv[i] = gs;
                 } else {
-                    gg = ld64(rs_g, 4 * e);
+                    const u4 gg = __builtin_amdgcn_raw_buffer_load_b128(rs_g, 4 * e, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) gv[i] = __uint_as_float(gg[i]);
                 }
-                rk[hh][m] = ld32(rs_k, 2 * e);
-                rq[hh][m] = ld32(rs_q, 2 * e);
-                float g0 = __uint_as_float(gg[0]), g1 = __uint_as_float(gg[1]);
-                if constexpr (XF) {  // rows past the chunk end stay 0: they must not decay G_last
-                    const bool real = 8 * rq8 + m < L;
-                    g0 = real ? ix.log_gate(g0) : 0.f;
-                    g1 = real ? ix.log_gate(g1) : 0.f;
+                rk[hh][m] = ld64(rs_k, 2 * e);
+                rqv[hh][m] = ld64(rs_q, 2 * e);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if constexpr (XF)  // rows past the chunk end stay 0: they must not decay G_last
+                        gv[i] = 4 * rq + m < L ? ix.log_gate(gv[i]) : 0.f;
+                    run[i] += gv[i];
+                    G[hh][m][i] = run[i];
                 }
-                r0 += g0;
-                r1 += g1;
-                G[hh][m][0] = r0;
-                G[hh][m][1] = r1;
-                mk2 = absmax2(mk2, rk[hh][m]);
-                mq2 = absmax2(mq2, rq[hh][m]);
+                mk2 = absmax2(absmax2(mk2, rk[hh][m][0]), rk[hh][m][1]);
+                mq2 = absmax2(absmax2(mq2, rqv[hh][m][0]), rqv[hh][m][1]);
             }
-            sm.op.part[rq8][hh * HC + 2 * cq] = r0;
-            sm.op.part[rq8][hh * HC + 2 * cq + 1] = r1;
+            *reinterpret_cast<f4 *>(&sm.op.part[rq][hh * HC + 4 * cq]) = f4{run[0], run[1], run[2], run[3]};
         }
         if (tid < C) sm.beta[tid] = tid < L ? bf16_to_f32(beta[(c0 + tid) * H + h]) : 0.f;
         float mk = wave_max(absmax2_value(mk2)), mq = wave_max(absmax2_value(mq2));
 #pragma unroll
-        for (int m = 0; m < 8; ++m) nk[m] = nq[m] = 1.f;
+        for (int m = 0; m < 4; ++m) nk[m] = nq[m] = 1.f;
         if (XF && ix.qk_l2norm) {
-            // a row's 128 channels sit in the 32 lanes of one half-wave, four per lane
+            // a row's 128 channels sit in the 16 lanes of one DPP row, eight per lane
             float ak = 0.f, aq = 0.f;  // largest |k|/|k_row|, |q|/|q_row| of this thread
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
+            for (int m = 0; m < 4; ++m) {
                 float sk2 = 0.f, sq2 = 0.f, xk = 0.f, xq = 0.f;
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const float k0 = lo_f(rk[hh][m]), k1 = hi_f(rk[hh][m]);
-                    const float q0 = lo_f(rq[hh][m]), q1 = hi_f(rq[hh][m]);
-                    sk2 += k0 * k0 + k1 * k1;
-                    sq2 += q0 * q0 + q1 * q1;
-                    xk = fmaxf(xk, fmaxf(fabsf(k0), fabsf(k1)));
-                    xq = fmaxf(xq, fmaxf(fabsf(q0), fabsf(q1)));
-                }
-                nk[m] = rsqrtf(half_wave_sum(sk2) + kL2Eps);
-                nq[m] = rsqrtf(half_wave_sum(sq2) + kL2Eps);
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int w = 0; w < 2; ++w) {
+                        const float k0 = lo_f(rk[hh][m][w]), k1 = hi_f(rk[hh][m][w]);
+                        const float q0 = lo_f(rqv[hh][m][w]), q1 = hi_f(rqv[hh][m][w]);
+                        sk2 += k0 * k0 + k1 * k1;
+                        sq2 += q0 * q0 + q1 * q1;
+                        xk = fmaxf(xk, fmaxf(fabsf(k0), fabsf(k1)));
+                        xq = fmaxf(xq, fmaxf(fabsf(q0), fabsf(q1)));
+                    }
+                nk[m] = rsqrtf(row16_sum(sk2) + kL2Eps);
+                nq[m] = rsqrtf(row16_sum(sq2) + kL2Eps);
                 ak = fmaxf(ak, xk * nk[m]);
                 aq = fmaxf(aq, xq * nq[m]);
             }
@@ -225,9 +244,9 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
         if constexpr (EXACT && XF) {  // the rows' norms (1 without the L2 norm) for the pairwise entries
             if (cq == 0)
 #pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    nx[8 * rq8 + m] = nk[m];
-                    nx[C + 8 * rq8 + m] = nq[m];
+                for (int m = 0; m < 4; ++m) {
+                    nx[4 * rq + m] = nk[m];
+                    nx[C + 4 * rq + m] = nq[m];
                 }
         }
         if (lane == 0) {
@@ -239,7 +258,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
     if (tid < DK) {  // channel tid: exclusive prefix over the row groups; part[0] takes the total
         float run = 0.f;
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
+        for (int p = 0; p < C / 4; ++p) {
             const float x = sm.op.part[p][tid];
             if (p > 0) sm.op.part[p][tid] = run;
             run += x;
@@ -252,15 +271,15 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
     const int eq = exp_of(__int_as_float(sm.imax[1]));
     const float sk = pow2(-ek), sq = pow2(-eq) * scale;
     __syncthreads();  // (2) prefixes and flag settled
-    float GL[2][2];
+    float GL[2][4];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int c = hh * HC + 2 * cq + e;
-            const float off = rq8 == 0 ? 0.f : sm.op.part[rq8][c];
+        for (int e = 0; e < 4; ++e) {
+            const int c = hh * HC + 4 * cq + e;
+            const float off = rq == 0 ? 0.f : sm.op.part[rq][c];
 #pragma unroll
-            for (int m = 0; m < 8; ++m) G[hh][m][e] += off;
+            for (int m = 0; m < 4; ++m) G[hh][m][e] += off;
             GL[hh][e] = sm.op.part[0][c];
         }
     __syncthreads();  // (2b) the sums are read before the operand area takes the Gram operands
@@ -275,67 +294,70 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
     f4 tacc[JPW];
 #pragma unroll
     for (int u = 0; u < JPW; ++u) tacc[u] = zero4();
-    uint32_t ekp[2][8];  // fp16 operand pairs of e^G k, kept for the W solve
+    u2 ekp[2][4];  // four fp16 channels of e^G k per [half][row], kept for the W solve
     // SG: per-row e^G 2^-ek, e^G 2^-eq scale, e^{G_L - G} 2^-ek, with the rows' L2 norms; and the
     // rows' G, 1/|k| and 1/|q| in LDS for the Gram epilogue ([C] each), in the low-part area that SG
     // leaves unused and that the later operand structures never reach
-    float sgE[8], sgQ[8], sgD[8];
+    float sgE[4], sgQ[4], sgD[4];
     float *const sgG = reinterpret_cast<float *>(sm.op.g.ckl), *const sgN = sgG + C;
-    static_assert(sizeof(sm.op.s) <= 5 * C * HC * sizeof(uint16_t),
-                  "the operand structures stay clear of the low-part area of the column operand");
+    static_assert(offsetof(decltype(sm.op.s), v) <= 5 * C * HC * sizeof(uint16_t),
+                  "the structures written before the Gram epilogue ends stay clear of the low-part area of the "
+                  "column operand");
     if constexpr (SG) {
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
+        for (int m = 0; m < 4; ++m) {
             const float e = __expf(G[0][m][0]), d = __expf(GL[0][0] - G[0][m][0]);
             sgE[m] = e * sk * nk[m];
             sgQ[m] = e * sq * nq[m];
             sgD[m] = d * sk * nk[m];
             if (cq == 0) {
-                sgG[8 * rq8 + m] = G[0][m][0];
-                sgN[8 * rq8 + m] = nk[m];
-                sgN[C + 8 * rq8 + m] = nq[m];
+                sgG[4 * rq + m] = G[0][m][0];
+                sgN[4 * rq + m] = nk[m];
+                sgN[C + 4 * rq + m] = nq[m];
             }
         }
     }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         // per channel: m log2(e) with m = G_L / 2, and e^m times the fp16 scales
-        float mlg[2], em_sk[2], em_sq[2];
+        float mlg[4], em_sk[4], em_sq[4];
 #pragma unroll
-        for (int e = 0; e < 2 && !SG; ++e) {
+        for (int e = 0; e < 4 && !SG; ++e) {
             mlg[e] = 0.5f * kLog2e * GL[hh][e];
             const float em = __builtin_amdgcn_exp2f(mlg[e]);
             em_sk[e] = em * sk;
             em_sq[e] = em * sq;
         }
-        uint32_t kdp[2][4];  // rows of e^{G_L - G} k, two per 32 bits, per channel
-        uint32_t qdp[2][4];  // RV: the same for the rows of Q
+        u2 kdp[4];  // per channel: e^{G_L - G} k of the four rows, fp16
+        u2 qdp[4];  // RV: the same for the rows of Q
+        auto put_half = [](u2 &w, int m, uint32_t hb) {
+            w[m >> 1] = (m & 1) ? (w[m >> 1] | (hb << 16)) : hb;
+        };
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int r = 8 * rq8 + m;
-            float kk[2] = {lo_f(rk[hh][m]), hi_f(rk[hh][m])};
-            float qq[2] = {lo_f(rq[hh][m]), hi_f(rq[hh][m])};
+        for (int m = 0; m < 4; ++m) {
+            const int r = 4 * rq + m;
+            float kk[4] = {lo_f(rk[hh][m][0]), hi_f(rk[hh][m][0]), lo_f(rk[hh][m][1]), hi_f(rk[hh][m][1])};
+            float qq[4] = {lo_f(rqv[hh][m][0]), hi_f(rqv[hh][m][0]), lo_f(rqv[hh][m][1]), hi_f(rqv[hh][m][1])};
             if constexpr (SG) {  // the Gram operands are the raw inputs
-                *reinterpret_cast<uint32_t *>(&sm.op.g.rkh[g_off(r, 2 * cq)]) = rk[hh][m];
-                *reinterpret_cast<uint32_t *>(&sm.op.g.rqh[g_off(r, 2 * cq)]) = rq[hh][m];
-                ekp[hh][m] = pack_h2(kk[0] * sgE[m], kk[1] * sgE[m]);
-                st32(rs_p, pack_h2(qq[0] * sgQ[m], qq[1] * sgQ[m]), kPkQ + w_col(r, hh * HC + 2 * cq));
+                *reinterpret_cast<u2 *>(&sm.op.g.rkh[g_off(r, 4 * cq)]) = rk[hh][m];
+                *reinterpret_cast<u2 *>(&sm.op.g.rqh[g_off(r, 4 * cq)]) = rqv[hh][m];
+                ekp[hh][m] = u2{pack_h2(kk[0] * sgE[m], kk[1] * sgE[m]), pack_h2(kk[2] * sgE[m], kk[3] * sgE[m])};
+                st64(rs_p, u2{pack_h2(qq[0] * sgQ[m], qq[1] * sgQ[m]), pack_h2(qq[2] * sgQ[m], qq[3] * sgQ[m])},
+                     kPkQ + w_col(r, hh * HC + 4 * cq));
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const uint32_t hb = hbits(static_cast<_Float16>(kk[e] * sgD[m]));
-                    kdp[e][m >> 1] = (m & 1) ? (kdp[e][m >> 1] | (hb << 16)) : hb;
-                }
+                for (int e = 0; e < 4; ++e) put_half(kdp[e], m, hbits(static_cast<_Float16>(kk[e] * sgD[m])));
                 continue;
             }
             if constexpr (XF) {
-                kk[0] *= nk[m];
-                kk[1] *= nk[m];
-                qq[0] *= nq[m];
-                qq[1] *= nq[m];
-            }
-            float ekv[2], qsv[2], kdv[2], ra[2], rb[2], rc[2];
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
+                for (int e = 0; e < 4; ++e) {
+                    kk[e] *= nk[m];
+                    qq[e] *= nq[m];
+                }
+            }
+            float ekv[4], qsv[4], kdv[4], ra[4], rb[4], rc[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
                 const float Gm = G[hh][m][e];
                 if constexpr (!EXACT) {
                     // row factor e^{G - m}, column factor e^{m - G}, both within e^{+-40}
@@ -355,45 +377,40 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
                     ra[e] = rb[e] = rc[e] = 0.f;
                 }
             }
-            ekp[hh][m] = pack_h2(ekv[0], ekv[1]);
-            // Q: the channel pair (hh HC + 2cq, +1) of row r is 4 bytes of a 16-byte unit
-            st32(rs_p, pack_h2(qsv[0], qsv[1]), kPkQ + w_col(r, hh * HC + 2 * cq));
-            uint32_t kdw = 0u;
+            ekp[hh][m] = u2{pack_h2(ekv[0], ekv[1]), pack_h2(ekv[2], ekv[3])};
+            // Q: the four channels hh HC + 4cq .. + 3 of row r are 8 contiguous bytes of a 16-byte unit
+            st64(rs_p, u2{pack_h2(qsv[0], qsv[1]), pack_h2(qsv[2], qsv[3])}, kPkQ + w_col(r, hh * HC + 4 * cq));
+            u2 kdw = {0u, 0u};
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
+            for (int e = 0; e < 4; ++e) {
                 const uint32_t hb = hbits(static_cast<_Float16>(kdv[e]));
-                kdp[e][m >> 1] = (m & 1) ? (kdp[e][m >> 1] | (hb << 16)) : hb;
-                kdw |= hb << (16 * e);
-                if constexpr (RV) {
-                    const uint32_t qb = hbits(static_cast<_Float16>(qsv[e]));
-                    qdp[e][m >> 1] = (m & 1) ? (qdp[e][m >> 1] | (qb << 16)) : qb;
-                }
+                put_half(kdp[e], m, hb);
+                put_half(kdw, e, hb);
+                if constexpr (RV) put_half(qdp[e], m, hbits(static_cast<_Float16>(qsv[e])));
             }
             if constexpr (RV)  // -Kd, row-major like W (the sign bits flipped)
-                st32(rs_r, kdw ^ 0x80008000u, kPkW + w_col(r, hh * HC + 2 * cq));
+                st64(rs_r, u2{kdw[0] ^ 0x80008000u, kdw[1] ^ 0x80008000u}, kPkW + w_col(r, hh * HC + 4 * cq));
             if constexpr (!EXACT) {
-                uint32_t hi, lo;
-                split2(ra[0], ra[1], hi, lo);
-                *reinterpret_cast<uint32_t *>(&sm.op.g.rkh[g_off(r, 2 * cq)]) = hi;
-                *reinterpret_cast<uint32_t *>(&sm.op.g.rkl[g_off(r, 2 * cq)]) = lo;
-                split2(rc[0], rc[1], hi, lo);
-                *reinterpret_cast<uint32_t *>(&sm.op.g.ckh[g_off(r, 2 * cq)]) = hi;
-                *reinterpret_cast<uint32_t *>(&sm.op.g.ckl[g_off(r, 2 * cq)]) = lo;
-                split2(rb[0], rb[1], hi, lo);
-                *reinterpret_cast<uint32_t *>(&sm.op.g.rqh[g_off(r, 2 * cq)]) = hi;
-                *reinterpret_cast<uint32_t *>(&sm.op.g.rql[g_off(r, 2 * cq)]) = lo;
+                // high and low bf16 parts of four channels, 8 bytes each
+                auto put_split = [&](const float (&x)[4], uint16_t *dh, uint16_t *dl) {
+                    uint32_t h0, l0, h1, l1;
+                    split2(x[0], x[1], h0, l0);
+                    split2(x[2], x[3], h1, l1);
+                    *reinterpret_cast<u2 *>(&dh[g_off(r, 4 * cq)]) = u2{h0, h1};
+                    *reinterpret_cast<u2 *>(&dl[g_off(r, 4 * cq)]) = u2{l0, l1};
+                };
+                put_split(ra, sm.op.g.rkh, sm.op.g.rkl);
+                put_split(rc, sm.op.g.ckh, sm.op.g.ckl);
+                put_split(rb, sm.op.g.rqh, sm.op.g.rql);
             }
         }
-        // KT: four consecutive rows of one channel are 8 contiguous bytes
+        // KT: the four rows 4rq .. 4rq + 3 of one channel are 8 contiguous bytes
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-            {
-                st64(rs_p, u2{kdp[e][2 * t], kdp[e][2 * t + 1]}, kPkKT + kt_col(hh * HC + 2 * cq + e, 8 * rq8 + 4 * t));
-                if constexpr (RV)  // Q^T, laid out like KT
-                    st64(rs_r, u2{qdp[e][2 * t], qdp[e][2 * t + 1]}, kPkQ + kt_col(hh * HC + 2 * cq + e, 8 * rq8 + 4 * t));
-            }
+        for (int e = 0; e < 4; ++e) {
+            st64(rs_p, kdp[e], kPkKT + kt_col(hh * HC + 4 * cq + e, 4 * rq));
+            if constexpr (RV)  // Q^T, laid out like KT
+                st64(rs_r, qdp[e], kPkQ + kt_col(hh * HC + 4 * cq + e, 4 * rq));
+        }
         if constexpr (!EXACT) {
             __syncthreads();  // (3a) this half's operands in LDS
 #pragma unroll
@@ -427,6 +444,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
             __syncthreads();  // (3b) this half's operands consumed
         }
     }
+    if constexpr (XF) load_v();
     if constexpr (!EXACT) {
         const float skk = sk * sk, sqk = sq * sk;  // stored A_kk x 2^-2ek, A_qk x 2^-(eq + ek)
 #pragma unroll
@@ -464,9 +482,9 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                gx[(8 * rq8 + m) * GP + hh * HC + 2 * cq] = G[hh][m][0];
-                gx[(8 * rq8 + m) * GP + hh * HC + 2 * cq + 1] = G[hh][m][1];
+            for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gx[(4 * rq + m) * GP + hh * HC + 4 * cq + e] = G[hh][m][e];
             }
         __syncthreads();
         for (int pr = tid; pr < C * C; pr += NT) {
@@ -503,15 +521,13 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
     __syncthreads();  // (4) Gram results in LDS; operand area free
 
     // ============ a3: diagonal blocks of T; e^G k to LDS, Q and KT to the pack ============
-    // the solve's v values, in accumulator layout, fetched ahead
-    uint32_t vpre[2][4][4];
+    // v staged in LDS (swizzled units, see PrepSmem)
+    auto v_at = [](int r, int c) { return r * DV + ((((c >> 3) ^ (2 * ((r >> 2) & 3)))) << 3) + (c & 7); };
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                vpre[t][a][jj] = ld16(rs_v, 2 * ((16 * a + 4 * g4 + jj) * tok_stride + 16 * (2 * wave + t) + n16));
+    for (int i = 0; i < C * DV / 8 / NT; ++i) {
+        const int u = tid + NT * i;
+        *reinterpret_cast<u4 *>(&sm.op.s.v[v_at(u >> 4, 8 * (u & 15))]) = vraw[i];
+    }
     float tcol[16];
     if (wave == 0) {  // lane 16a + j owns column j of T_aa = (I + A_aa)^{-1}
         const int a = g4, j = n16;
@@ -535,20 +551,27 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
-            *reinterpret_cast<uint32_t *>(&sm.op.s.ek[(8 * rq8 + m) * KP + hh * HC + 2 * cq]) = ekp[hh][m];
-    {   // |v| maximum, from the prefetched values (bf16 magnitudes order as integers)
+        for (int m = 0; m < 4; ++m)
+            *reinterpret_cast<u2 *>(&sm.op.s.ek[(4 * rq + m) * KP + hh * HC + 4 * cq]) = ekp[hh][m];
+    {   // |v| maximum, from the raw units (bf16 magnitudes order as integers)
         uint32_t mv = 0u;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int i = 0; i < C * DV / 8 / NT; ++i)
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) mv = max(mv, vpre[t][a][jj] & 0x7fffu);
-        const float mvf = wave_max(__uint_as_float(mv << 16));
+            for (int w = 0; w < 4; ++w) mv = absmax2(mv, vraw[i][w]);
+        const float mvf = wave_max(absmax2_value(mv));
         if (lane == 0) atomicMax(&sm.imax[2], __float_as_int(mvf));
     }
     __syncthreads();  // (5)
+    // the solve's v values in accumulator layout: rows 16 a + 4 g4 + jj of column 16 (2 wave + t) + n16
+    uint32_t vpre[2][4][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                vpre[t][a][jj] = sm.op.s.v[v_at(16 * a + 4 * g4 + jj, 16 * (2 * wave + t) + n16)];
     const int et = exp_of(__int_as_float(sm.imax[4]));
     const int ev = exp_of(__int_as_float(sm.imax[2])) - 5;  // U's solve runs below 2^5
     const float svs = pow2(-ev);
@@ -630,9 +653,12 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
                     *reinterpret_cast<_Float16 *>(wst + w_col(rr, col)) =
                         static_cast<_Float16>(Wr[t][a][jj] * swv);
                 }
-                // U straight to the pack, in accumulator order
-                const h4 uh = to_h4(Ur[t][a], suv);
-                st64(rs_p, __builtin_bit_cast(u2, uh), kPkU + u_off(ct, a, lane));
+                // U straight to the pack, in accumulator order: row blocks a - 1 and a are one 16-byte unit
+                if (a & 1) {
+                    const u2 ul = __builtin_bit_cast(u2, to_h4(Ur[t][a - 1], suv));
+                    const u2 uh = __builtin_bit_cast(u2, to_h4(Ur[t][a], suv));
+                    st128(rs_p, u4{ul[0], ul[1], uh[0], uh[1]}, kPkU + u_off(ct, a - 1, lane));
+                }
                 if constexpr (RV) {  // -W^T, laid out like KT: rows 16 a + 4 g4 .. + 3 of column col are 8 bytes
                     const u2 wh = __builtin_bit_cast(u2, to_h4(Wr[t][a], swv));
                     st64(rs_r, u2{wh[0] ^ 0x80008000u, wh[1] ^ 0x80008000u}, kPkKT + kt_col(col, 16 * a + 4 * g4));

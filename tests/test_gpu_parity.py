@@ -191,6 +191,19 @@ def test_slow_decay_packed_varlen_fp32(kda):
     check_prefill(kda, x)
 
 
+def test_magnitude_jumps_between_chunks(kda):
+    """Values whose size jumps by 10^4 from one chunk to the next, up and down, from a zero initial
+    state: the serial walk's fp16 operand frames, taken from the previous chunk's maxima, must be
+    redone whenever the new values leave their range."""
+    x = make_prefill(54, 1, 1400, 3, 128, 128, gscale=0.3, h0_std=None, name="magnitude_jumps")
+    x.v[0, 192:384] *= 1e4     # chunks 3-5 ten thousand times larger
+    x.v[0, 512:704] *= 1e-4    # chunks 8-10 ten thousand times smaller
+    x.v[0, 1000:1010] *= 3e3   # a few tokens inside a chunk
+    x.k[0, 1200:1264, 1] *= 0.0  # a chunk of head 1 that writes nothing
+    x.v = bf16_round(x.v)        # the values the device receives
+    check_prefill(kda, x)
+
+
 def test_extreme_gates(kda):
     """Blocks that decay by far more than exp(-80), next to blocks with no decay."""
     x = make_prefill(53, 1, 256, 2, 128, 128, h0_std=0.3, name="extreme_gates")
