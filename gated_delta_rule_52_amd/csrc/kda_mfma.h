@@ -175,6 +175,11 @@ __device__ __forceinline__ void st64(rsrc_t r, u2 v, uint32_t off, int soff = 0)
 __device__ __forceinline__ void st128(rsrc_t r, u4 v, uint32_t off, int soff = 0) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(off), soff, 0);
 }
+// the same with the non-temporal hint (cache policy bit 1, "nt" on gfx950), for output that is written
+// once in whole 128-byte lines and not read back soon; partial lines written this way cost far more
+__device__ __forceinline__ void st128_nt(rsrc_t r, u4 v, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(off), 0, 2);
+}
 
 // ---- per-chunk operand pack (one per chunk and head, written by the prep
 // kernel, streamed by the scan kernels).  Every fp16 matrix carries a

@@ -17,8 +17,11 @@
 // V_new feed the 16x16x32 products straight from the accumulator layout
 // (permuted contraction index, see w_col).  They are
 // rounded to fp16 with power-of-two scales of the wave's own (from its
-// maxima), so waves share nothing but the pack.  o is staged in LDS per wave
-// and written with 16-byte stores.
+// maxima), so waves share nothing but the pack.  A bf16 o is staged in LDS
+// for the whole workgroup and stored one chunk later, after the next
+// barrier, as whole 256-byte rows with the non-temporal hint (each wave
+// holds only 32 bytes of a row, and partial-line writes from several waves
+// cost HBM time); an fp32 o is staged per wave and stored at once.
 //
 // Modes: kLocal, 16 waves: waves 0-7 build H (the dv columns, zero start)
 // and waves 8-15 build P (the dk x dk transition: identity start, v = 0), so
@@ -72,8 +75,12 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     __shared__ __attribute__((aligned(16))) char lds1[kBytes];
     // o of a chunk, per wave: 64 rows x its columns, rows padded by 16 bytes
     // (the four row groups of an accumulator tile land on different banks)
+    constexpr bool kRowsOut = kOutPass && OutBf16;  // bf16 o: whole-workgroup rows, two chunks in turn
     constexpr int kStageRow = 16 * NCT * (OutBf16 ? 2 : 4) + 16;
-    __shared__ __attribute__((aligned(16))) char ostage[kOutPass ? NW : 1][kOutPass ? 64 * kStageRow : 16];
+    constexpr int kRowBytes = 2 * DV + 16;
+    __shared__ __attribute__((aligned(16))) char ostage[kOutPass && !kRowsOut ? NW : 1]
+                                                       [kOutPass && !kRowsOut ? 64 * kStageRow : 16];
+    __shared__ __attribute__((aligned(16))) char orows[kRowsOut ? 2 : 1][kRowsOut ? 64 * kRowBytes : 16];
 
     const int seg = blockIdx.x, h = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -177,6 +184,16 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     };
     // the i-th chunk walked: first to last, or last to first in the reverse modes
     auto chunk_of = [&](int i) { return kRev ? nch - 1 - i : i; };
+    // bf16 o of chunk j from orows[j & 1]: 16 lanes per 256-byte row
+    auto store_rows = [&](int j) {
+        const char *src = orows[j & 1];
+#pragma unroll
+        for (int k = 0; k < 64 * 16 / ScanCfg<MODE>::NT; ++k) {
+            const int u = tid + ScanCfg<MODE>::NT * k, rr = u >> 4, cu = u & 15;
+            const u4 w = *reinterpret_cast<const u4 *>(src + rr * kRowBytes + 16 * cu);
+            st128_nt(rs_o, w, 2 * (static_cast<uint32_t>(C * j + rr) * tok_stride) + 16 * cu);
+        }
+    };
     // U (and dO) of the chunk in use / of the next one (zero for P)
     u4 urA[NCT][2] = {}, urB[NCT][2] = {}, drA[NCT][2] = {}, drB[NCT][2] = {}, ulA[NCT][2] = {}, ulB[NCT][2] = {};
     fetch(chunk_of(0), lds0, urA, drA, ulA);
@@ -189,6 +206,8 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // chunk j in L; every wave is done with the previous chunk
         if (i + 1 < nch) fetch(chunk_of(i + 1), Lnext, ur_nxt, dr_nxt, ul_nxt);
+        if constexpr (kRowsOut)  // every wave's part of the previous chunk's o is in orows now
+            if (i > 0) store_rows(j - 1);
 
         const int *hdr = reinterpret_cast<const int *>(L + kPkHdr);
         const int ew = hdr[kHdrW], ek = hdr[kHdrK];
@@ -308,9 +327,9 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
                 }
             }
         }
-        // a6: o = Q S + A_qk V_new, staged per wave in LDS, then 16-byte stores
+        // a6: o = Q S + A_qk V_new, staged in LDS, then 16-byte stores
         if (kOutPass) {
-            char *st = ostage[wave];
+            char *st = kRowsOut ? orows[j & 1] : ostage[wave];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 const float unq = pow2(hdr[kHdrQ] + fr[ct]), una = pow2(hdr[kHdrA] + frn[ct] - ek);
@@ -326,21 +345,25 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
                     for (int jj = 0; jj < 4; ++jj) {
                         const int rr = 16 * a + 4 * g4 + jj, cc = 16 * ct + n16;
                         const float val = Y[ct][a][jj] * unq + oi[jj] * una;
-                        if constexpr (OutBf16)
+                        if constexpr (kRowsOut)
+                            *reinterpret_cast<__bf16 *>(st + rr * kRowBytes + 2 * (col0 + cc)) = static_cast<__bf16>(val);
+                        else if constexpr (OutBf16)
                             *reinterpret_cast<__bf16 *>(st + rr * kStageRow + 2 * cc) = static_cast<__bf16>(val);
                         else
                             *reinterpret_cast<float *>(st + rr * kStageRow + 4 * cc) = val;
                     }
                 }
             }
-            // 64 rows x this wave's columns: 16-byte units, rows past the
-            // segment end dropped by the buffer range
-            constexpr int kUnitsPerRow = 16 * NCT * ob / 16;
+            if constexpr (!kRowsOut) {
+                // 64 rows x this wave's columns: 16-byte units, rows past the
+                // segment end dropped by the buffer range
+                constexpr int kUnitsPerRow = 16 * NCT * ob / 16;
 #pragma unroll
-            for (int k = 0; k < 64 * kUnitsPerRow / kWave; ++k) {
-                const int i = lane + kWave * k, rr = i / kUnitsPerRow, un = i % kUnitsPerRow;
-                const u4 w = *reinterpret_cast<const u4 *>(st + rr * kStageRow + 16 * un);
-                st128(rs_o, w, ob * ((static_cast<uint32_t>(C * j + rr)) * tok_stride + col0) + 16 * un);
+                for (int k = 0; k < 64 * kUnitsPerRow / kWave; ++k) {
+                    const int i = lane + kWave * k, rr = i / kUnitsPerRow, un = i % kUnitsPerRow;
+                    const u4 w = *reinterpret_cast<const u4 *>(st + rr * kStageRow + 16 * un);
+                    st128(rs_o, w, ob * ((static_cast<uint32_t>(C * j + rr)) * tok_stride + col0) + 16 * un);
+                }
             }
         }
         // a5: S <- gamma S + KT V_new in the frame frn, where the product
@@ -398,6 +421,12 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     for (int i = 0; i < nch; i += 2) {
         step(i, lds0, lds1, urA, urB, drA, drB, ulA, ulB);
         if (i + 1 < nch) step(i + 1, lds1, lds0, urB, urA, drB, drA, ulB, ulA);
+    }
+    if constexpr (kRowsOut) {
+        if (nch > 0) {
+            __syncthreads();  // the last chunk's o is staged by every wave
+            store_rows(nch - 1);
+        }
     }
 
     // ---- leaving state (DK = DV: H and P are both 128 x 128), or the gradient at the segment start
