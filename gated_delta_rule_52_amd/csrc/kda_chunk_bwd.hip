@@ -267,16 +267,17 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
     };
     if (tid == 0) *sFlag = 0;
     f4 pS[8];  // this thread's S units, kept for dgamma in phase 2
+    // the kept states and V_new are read once, with the non-temporal hint
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int u = tid + kGT * i;
-        pS[i] = *reinterpret_cast<const f4 *>(St + 4 * u);
+        pS[i] = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(St + 4 * u));
         put_unit(sSh, sSl, u, 8, pS[i]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int u = tid + kGT * i;
-        put_unit(sXh, sXl, u, 4, *reinterpret_cast<const f4 *>(dVt + 4 * u));
+        put_unit(sXh, sXl, u, 4, __builtin_nontemporal_load(reinterpret_cast<const f4 *>(dVt + 4 * u)));
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -289,9 +290,11 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
     // phase 2's inputs, fetched while phase 1 computes (dS' units match the S units above)
     f4 pdS[8], pVn[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pdS[i] = *reinterpret_cast<const f4 *>(dSt + 4 * (tid + kGT * i));
+    for (int i = 0; i < 8; ++i)
+        pdS[i] = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(dSt + 4 * (tid + kGT * i)));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pVn[i] = *reinterpret_cast<const f4 *>(Vt + 4 * (tid + kGT * i));
+    for (int i = 0; i < 4; ++i)
+        pVn[i] = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(Vt + 4 * (tid + kGT * i)));
     __builtin_amdgcn_sched_barrier(0);
     f4 dQh[4], dWn[4];
 #pragma unroll

@@ -219,8 +219,10 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
             for (int ct = 0; ct < NCT; ++ct) {
                 const float sc = pow2(fr[ct]);
 #pragma unroll
-                for (int rt = 0; rt < 8; ++rt)
-                    *reinterpret_cast<f4 *>(sd_ + 4 * (((ctile0 + ct) * 8 + rt) * 64 + lane)) = acc[rt][ct] * sc;
+                for (int rt = 0; rt < 8; ++rt) {  // whole 1 KiB units, read once much later: non-temporal
+                    f4 *dst4 = reinterpret_cast<f4 *>(sd_ + 4 * (((ctile0 + ct) * 8 + rt) * 64 + lane));
+                    __builtin_nontemporal_store(acc[rt][ct] * sc, dst4);
+                }
             }
         }
         // The accumulator layout of two 16-row state tiles is the B operand
@@ -308,8 +310,10 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
                 if constexpr (kKeep) {  // V_new (forward) or dV_new (reversed), true scale
                     float *vd = gr.vn + slot * (C * DV);
 #pragma unroll
-                    for (int a = 0; a < 4; ++a)
-                        *reinterpret_cast<f4 *>(vd + 4 * (((ctile0 + ct) * 4 + a) * 64 + lane)) = Vn[ct][a];
+                    for (int a = 0; a < 4; ++a) {
+                        f4 *dst4 = reinterpret_cast<f4 *>(vd + 4 * (((ctile0 + ct) * 4 + a) * 64 + lane));
+                        __builtin_nontemporal_store(Vn[ct][a], dst4);
+                    }
                 }
             }
         }
@@ -346,7 +350,8 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
                         const int rr = 16 * a + 4 * g4 + jj, cc = 16 * ct + n16;
                         const float val = Y[ct][a][jj] * unq + oi[jj] * una;
                         if constexpr (kRowsOut)
-                            *reinterpret_cast<__bf16 *>(st + rr * kRowBytes + 2 * (col0 + cc)) = static_cast<__bf16>(val);
+                            *reinterpret_cast<__bf16 *>(st + rr * kRowBytes + 2 * (col0 + cc)) =
+                                static_cast<__bf16>(val);
                         else if constexpr (OutBf16)
                             *reinterpret_cast<__bf16 *>(st + rr * kStageRow + 2 * cc) = static_cast<__bf16>(val);
                         else
