@@ -29,7 +29,7 @@
 //
 // The optional input transforms (XF instantiation) act on the values as they
 // arrive: the gate logit becomes the log-gate before the cumulative sum, and
-// each row's 1/|k| and 1/|q| (reduced over the 32 lanes that hold the row)
+// each row's 1/|k| and 1/|q| (reduced over the 16 lanes that hold the row)
 // scale k and q before any product or maximum is formed.
 //
 // With one gate per token and head (SG instantiation, Gated DeltaNet's gate)
