@@ -287,6 +287,31 @@ def test_bf16_output_is_rounded_fp32_output_and_deterministic(kda):
     assert np.array_equal(want, got), "bf16 output differs from RNE(fp32 output)"
 
 
+@pytest.mark.parametrize("case", ["varlen", "batch"])
+def test_bf16_output_rows_stay_in_their_sequence(kda, case):
+    """The bf16 output is staged per chunk for the whole workgroup and stored
+    as whole rows one chunk later: packed sequences with ragged ends (several
+    segments, one token, empty) and a batch of ragged equal lengths must still
+    give RNE(fp32 o) on every token, so no row spills into a neighbour's."""
+    import torch
+    if case == "varlen":
+        x = make_prefill(59, 1, 0, 4, 128, 128, h0_std=0.3, seqlens=[700, 1, 0, 333, 64, 2100, 5, 130],
+                         name="bf16_rows_varlen")
+    else:
+        x = make_prefill(61, 3, 300, 4, 128, 128, h0_std=0.3, name="bf16_rows_batch")
+    o32, h32 = run_prefill(kda, x, out_dtype=torch.float32)
+    d = upload(x)
+    o16 = torch.full_like(o32, float("nan"), dtype=torch.bfloat16)  # tokens left unwritten stay NaN
+    _, h16 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["h0"], cu_seqlens=d["cu"],
+                           o=o16, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    want = bf16_round(o32.cpu().numpy())
+    got = o16.float().cpu().numpy()
+    assert np.array_equal(want, got), "bf16 output differs from RNE(fp32 output)"
+    assert torch.equal(h16, h32), "final state depends on the output dtype"
+    say(f"  case {x.name}: bf16 o == RNE(fp32 o) on {x.T * x.B} tokens x {x.H} heads")
+
+
 @pytest.mark.parametrize("dt", ["bf16", "fp32"])
 def test_one_segment_sequences_in_place(kda, dt):
     """A sequence that fits one segment reads its initial state where it lies
