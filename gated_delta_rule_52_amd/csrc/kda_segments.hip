@@ -79,12 +79,13 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int N, int chunk, bool varle
 }
 
 // a7: the segment table.  Each thread owns a contiguous range of sequences;
-// one block-wide exclusive scan of the per-thread segment counts gives every
-// sequence its first segment.
+// one block-wide exclusive scan of the per-thread segment counts (shuffles
+// within each wave, then the four wave totals) gives every sequence its first
+// segment.
 __global__ void __launch_bounds__(256)
 build_segments_kernel(const int32_t *__restrict__ cu_seqlens, int T, int N, int seg_len,
                       int4 *__restrict__ table, int32_t *__restrict__ seq_seg, int *xcount) {
-    __shared__ int s_cnt[256];
+    __shared__ int s_cnt[4];
     const int tid = threadIdx.x;
     if (tid == 0 && xcount) *xcount = 0;
     const int per = (N + 255) / 256;
@@ -105,19 +106,19 @@ build_segments_kernel(const int32_t *__restrict__ cu_seqlens, int T, int N, int 
         bounds(n, a, b);
         cnt += static_cast<int>((b - a + seg_len - 1) / seg_len);
     }
-    s_cnt[tid] = cnt;
-    __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int i = 0; i < 256; ++i) {
-            const int c = s_cnt[i];
-            s_cnt[i] = run;
-            run += c;
-        }
-        seq_seg[N] = run;
+    // exclusive scan of the counts: inclusive within each wave by shuffles, then the wave totals
+    const int lane = tid & 63, wave = tid >> 6;
+    int inc = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += y;
     }
+    if (lane == 63) s_cnt[wave] = inc;
     __syncthreads();
-    int idx = s_cnt[tid];
+    int idx = inc - cnt;
+    for (int w = 0; w < wave; ++w) idx += s_cnt[w];
+    if (tid == 255) seq_seg[N] = idx + cnt;
     for (int n = n0; n < n1; ++n) {
         int64_t a, b;
         bounds(n, a, b);
