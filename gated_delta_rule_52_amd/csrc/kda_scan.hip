@@ -437,7 +437,31 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     // ---- leaving state (DK = DV: H and P are both 128 x 128), or the gradient at the segment start
     float *dst = nullptr;
     if (kOutPass) {
-        if (last && hT) dst = hT + (static_cast<int64_t>(nseq) * H + h) * DK * DV;
+        if (last && hT) {
+            // the final state through the free pack buffers (rows 0-63 in one, 64-127 in the other, 528-byte
+            // rows) and out as whole 512-byte rows with the non-temporal hint: a wave holds 16 columns only
+            constexpr int kSR = DV + 4;
+            static_assert(64 * kSR * 4 <= kBytes, "half the state fits one pack buffer");
+            __syncthreads();  // every wave is done with the pack buffers
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        float *half = reinterpret_cast<float *>(rt < 4 ? lds0 : lds1);
+                        half[((16 * rt + 4 * g4 + jj) & 63) * kSR + col0 + 16 * ct + n16] =
+                            acc[rt][ct][jj] * pow2(fr[ct]);
+                    }
+            __syncthreads();
+            const rsrc_t rs = make_rsrc(hT + (static_cast<int64_t>(nseq) * H + h) * DK * DV, 4 * DK * DV);
+#pragma unroll
+            for (int i = 0; i < DK * DV / 4 / ScanCfg<MODE>::NT; ++i) {
+                const int u = tid + ScanCfg<MODE>::NT * i, r = u >> 5, cu = u & 31;
+                const float *half = reinterpret_cast<const float *>(r < 64 ? lds0 : lds1);
+                st128_nt(rs, *reinterpret_cast<const u4 *>(half + (r & 63) * kSR + 4 * cu), 4 * (r * DV + 4 * cu));
+            }
+        }
     } else if (MODE == kLocal) {
         dst = (pcols ? sv.P : sv.Hs) + (static_cast<int64_t>(seg) * H + h) * DK * DV;
     } else if (MODE == kRevLocal) {
