@@ -95,6 +95,7 @@ struct alignas(16) PrepSmem {
         float part[C / 4][DK];  // column sums of g per group of four rows (dead before the Gram operands)
     } op;
     float beta[C];
+    float nrm[2 * C];                      // XF with the L2 norm: 1/|k_r|, then 1/|q_r|, per row
     alignas(16) float gam[DK];             // exp(G_last) per channel
     int imax[8];                           // |k|, |scale q|, |v|, -, |T|, exact flag, |W|, |U|
 };
@@ -240,6 +241,12 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
             }
             mk = wave_max(ak);
             mq = wave_max(aq);
+            if (!SG && cq == 0)  // the Gram operands read them back in a2 (registers stay free in between)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    sm.nrm[4 * rq + m] = nk[m];
+                    sm.nrm[C + 4 * rq + m] = nq[m];
+                }
         }
         if constexpr (EXACT && XF) {  // the rows' norms (1 without the L2 norm) for the pairwise entries
             if (cq == 0)
@@ -348,11 +355,12 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
                 for (int e = 0; e < 4; ++e) put_half(kdp[e], m, hbits(static_cast<_Float16>(kk[e] * sgD[m])));
                 continue;
             }
-            if constexpr (XF) {
+            if (XF && ix.qk_l2norm) {
+                const float nkm = sm.nrm[r], nqm = sm.nrm[C + r];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    kk[e] *= nk[m];
-                    qq[e] *= nq[m];
+                    kk[e] *= nkm;
+                    qq[e] *= nqm;
                 }
             }
             float ekv[4], qsv[4], kdv[4], ra[4], rb[4], rc[4];
