@@ -139,6 +139,8 @@ struct SegmentView {
     const float *h0;        // [N, H, dk, dv] initial states (null: zero)
     int *xlist;             // chunks (pack numbers) the matrix-core prep hands to its exact path
     int *xcount;            // their count (zeroed by the segment-table kernel)
+    uint8_t *pz = nullptr;  // [max_segs, H, 8] matrix-core path: byte w is 1 when column tile w (16 columns) of
+                            // the segment's P is exactly zero; the local pass writes it for every P it builds
     __device__ __forceinline__ int count() const { return seq_seg[N]; }
     // the entering state of segment seg = {sequence, first token, end token, flags} at head h, row-major
     // dk x dv; null stands for the zero state.  A sequence of one segment enters with its initial state,

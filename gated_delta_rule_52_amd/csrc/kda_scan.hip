@@ -208,6 +208,10 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
         if (i + 1 < nch) fetch(chunk_of(i + 1), Lnext, ur_nxt, dr_nxt, ul_nxt);
         if constexpr (kRowsOut)  // every wave's part of the previous chunk's o is in orows now
             if (i > 0) store_rows(j - 1);
+        // A P tile that has decayed to exactly zero stays zero (gamma 0 + KT (0 - W 0) = 0), so its wave only
+        // takes its share of the copies from here on.  Under strong gates P underflows within a few chunks.
+        if constexpr (MODE == kLocal)
+            if (pcols && smax[0] == 0.f) return;
 
         const int *hdr = reinterpret_cast<const int *>(L + kPkHdr);
         const int ew = hdr[kHdrW], ek = hdr[kHdrK];
@@ -469,6 +473,9 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     } else if (MODE == kRevOut) {
         if (first && gr.dh0) dst = gr.dh0 + (static_cast<int64_t>(nseq) * H + h) * DK * DV;
     }
+    // the combines read P from an empty buffer range (zeros, no memory traffic) where every tile is zero
+    if (MODE == kLocal && pcols && sv.pz && lane == 0)
+        sv.pz[(static_cast<int64_t>(seg) * H + h) * 8 + (wave - NWH)] = smax[0] == 0.f;
     if (MODE == kLocal && pcols && gr.pt) {
         // P^T planes for the gradients' reverse combine: element (c, r) of P^T at 2 (128 c + r) bytes, so the
         // four rows 16 rt + 4 g4 .. + 3 of this lane's column are 8 contiguous bytes of each plane

@@ -21,6 +21,7 @@
 // All passes run on the caller's stream; nothing is allocated.
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_mfma.h"
 
 namespace kda {
 
@@ -36,7 +37,7 @@ struct Plan {
     int seg_len;    // tokens per segment (per * chunk)
     int max_segs;   // bound on the number of segments
     bool packs;     // matrix-core path: one operand pack per chunk and head
-    size_t off_table, off_seq, off_P, off_H, off_S, off_pack, off_xlist, bytes;
+    size_t off_table, off_seq, off_P, off_H, off_S, off_pack, off_xlist, off_pz, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t{255}; }
@@ -74,6 +75,7 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int N, int chunk, bool varle
     p.off_S = o;     o = align256(o + ms * H * dk * dv * sizeof(float));
     p.off_pack = o;  o = align256(o + (p.packs ? ms * p.per * H * pack_bytes() : 0));
     p.off_xlist = o; o = align256(o + (p.packs ? (ms * p.per * H + 1) * sizeof(int) : 0));
+    p.off_pz = o;    o = align256(o + (p.packs ? ms * H * 8 : 0));
     p.bytes = o;
     return p;
 }
@@ -375,6 +377,15 @@ combine_bf16x3_kernel(SegmentView sv, const float *h0, float *hT, int H, const c
 
     // segments the chain reads: first .. end - 2 forward, end - 1 .. first + 1 reversed
     auto seg_of = [&](int i) { return REV ? end - 1 - i : first + i; };
+    // steps whose P is exactly zero (all eight column tiles flagged by the local pass) reduce to
+    // entering(s + 1) = H_s: their P operands come from an empty buffer range, which reads zeros
+    // without a memory access (the same instructions run, so the step's result is the same bits)
+    constexpr int kZCap = 1024;  // steps past this many fetch P as usual
+    __shared__ uint8_t pzs[kZCap];
+    for (int i = tid; i < min(nsteps, kZCap); i += 512)
+        pzs[i] = sv.pz && *reinterpret_cast<const uint64_t *>(sv.pz + (static_cast<int64_t>(seg_of(i)) * H + h) * 8) ==
+                              0x0101010101010101ull;
+    __syncthreads();
     struct Stage {
         u4v pa[2][4];  // P operands, [plane][block]
         f32x4 hb;      // H addends
@@ -382,16 +393,19 @@ combine_bf16x3_kernel(SegmentView sv, const float *h0, float *hT, int H, const c
     // unconditional (past the last step it repeats that step's segment), so
     // that every path through the loop has the same memory operations
     auto fetch = [&](int i, Stage &st) {
-        const int seg = seg_of(min(i, nsteps - 1));
+        const int ic = min(i, nsteps - 1), seg = seg_of(ic);
         const char *src = REV ? pt + (static_cast<int64_t>(seg) * H + h) * DK * DK * 4
                               : reinterpret_cast<const char *>(sv.P + (static_cast<int64_t>(seg) * H + h) * DK * DK);
         const float *hs = (REV ? hb : sv.Hs) + (static_cast<int64_t>(seg) * H + h) * DK * DV;
         const int r = 16 * wave + m;
+        const bool pzero = ic < kZCap && __builtin_amdgcn_readfirstlane(pzs[ic]);
+        const mc::rsrc_t rp = mc::make_rsrc(src, pzero ? 0u : 4u * DK * DK);
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                st.pa[pl][t] = *reinterpret_cast<const u4v *>(src + pl * 2 * DK * DK + 2 * (r * DK + 32 * t + 8 * g));
+                st.pa[pl][t] = __builtin_amdgcn_raw_buffer_load_b128(rp, pl * 2 * DK * DK + 2 * (r * DK + 32 * t + 8 * g),
+                                                                      0, 0);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) st.hb[jj] = hs[(16 * wave + 4 * g + jj) * DV + j0 + m];
     };
@@ -477,6 +491,7 @@ hipError_t launch_chunk(const ChunkLaunch &L) {
     sv.h0 = L.h0;
     sv.xcount = p.packs ? reinterpret_cast<int *>(ws + p.off_xlist) : nullptr;
     sv.xlist = p.packs ? sv.xcount + 1 : nullptr;
+    sv.pz = p.packs ? reinterpret_cast<uint8_t *>(ws + p.off_pz) : nullptr;
 
     hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(256), 0, L.stream, L.cu_seqlens, L.T, L.N,
                        p.seg_len, reinterpret_cast<int4 *>(ws + p.off_table),
@@ -528,6 +543,7 @@ SegmentView launch_chunk_grad_forward(const ChunkLaunch &L, const ScanGrad &gr, 
     sv.h0 = L.h0;
     sv.xcount = reinterpret_cast<int *>(ws + p.off_xlist);
     sv.xlist = sv.xcount + 1;
+    sv.pz = p.packs ? reinterpret_cast<uint8_t *>(ws + p.off_pz) : nullptr;
     hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(256), 0, L.stream, L.cu_seqlens, L.T, L.N,
                        p.seg_len, reinterpret_cast<int4 *>(ws + p.off_table),
                        reinterpret_cast<int32_t *>(ws + p.off_seq), sv.xcount);

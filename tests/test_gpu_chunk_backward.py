@@ -88,6 +88,17 @@ def test_slow_decay_long_retention(kda):
     check(kda, x, do, dhT)
 
 
+def test_zero_and_carrying_transitions_in_one_chain(kda):
+    """4,096 tokens, 2 heads, one chunk per segment: long retention (gate scale 0.01) with every third
+    chunk decaying past e^-200 (scale 4), whose transition is exactly zero.  Both combines read the
+    zero transitions as zeros without fetching them and carry the others."""
+    x = make_prefill(167, 1, 4096, 2, 128, 128, gscale=0.01, h0_std=0.05, name="cbwd_mixed")
+    for c0 in range(0, 4096, 3 * 64):
+        x.g[0, c0:c0 + 64] *= 400.0
+    do, dhT = make_output_grads(x, 267, dhT_std=0.05)
+    check(kda, x, do, dhT)
+
+
 def test_fast_decay_takes_the_exact_chunk_path(kda):
     """Gate scale 4: chunks decay past e^-80, so the Gram products and their
     gradients are formed pair by pair."""

@@ -191,6 +191,17 @@ def test_slow_decay_packed_varlen_fp32(kda):
     check_prefill(kda, x)
 
 
+def test_zero_and_carrying_transitions_in_one_chain(kda):
+    """8,192 tokens, 2 heads: segments of 128 tokens, long retention (gate scale 0.01) in most of them
+    and strong gates (scale 1.5) in every third.  The strong segments' transitions P underflow to exactly
+    zero, which the local pass flags and the combine then reads as zeros without fetching; the others
+    carry the state across their boundary.  Both kinds alternate along one combine chain."""
+    x = make_prefill(55, 1, 8192, 2, 128, 128, gscale=0.01, h0_std=0.3, name="mixed_transitions")
+    for s0 in range(0, 8192, 3 * 128):
+        x.g[0, s0:s0 + 128] *= 150.0
+    check_prefill(kda, x)
+
+
 def test_magnitude_jumps_between_chunks(kda):
     """Values whose size jumps by 10^4 from one chunk to the next, up and down, from a zero initial
     state: the serial walk's fp16 operand frames, taken from the previous chunk's maxima, must be
