@@ -47,6 +47,9 @@ namespace {
 typedef const void __attribute__((address_space(1))) *gptr_t;
 typedef void __attribute__((address_space(3))) *lptr_t;
 
+// chunks at a segment's end the local pass walks first (the rest only if their transition is not zero)
+constexpr int kTail = 4;
+
 template <int MODE>
 struct ScanCfg {
     static constexpr bool kRev = MODE == kRevLocal || MODE == kRevOut;
@@ -62,7 +65,7 @@ struct ScanCfg {
 template <int MODE, bool OutBf16>
 __global__ void __launch_bounds__(ScanCfg<MODE>::NT, 1)
 chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__restrict__ o_, SegmentView sv,
-                  int H, ScanGrad gr) {
+                  int H, ScanGrad gr, int redo) {
     constexpr bool kOutPass = MODE == kOut;
     constexpr bool kRev = ScanCfg<MODE>::kRev;
     constexpr bool kReplay = MODE == kOut || MODE == kStates || MODE == kRevOut;  // from a true boundary state
@@ -95,6 +98,20 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     if (MODE == kRevLocal && first) return;  // Hb of a first segment is never used
     const int64_t t0 = sd.y, t1 = sd.z;
     const int nch = static_cast<int>((t1 - t0 + C - 1) / C);
+    // The local pass first walks only a segment's last kTail chunks (redo = 0).  If the transition over them,
+    // P_tail, is exactly zero (it underflows fp32: strong gates forget within a few chunks), then the segment's
+    // P = P_tail P_head is zero as well, and H = P_tail H_head + H_tail is H_tail, the state those chunks reach
+    // from zero: the earlier chunks' part lies below fp32's range, just as a zero P drops the entering state in
+    // the combine.  The flags in sv.pz record whether P_tail is zero; a second launch (redo = 1) walks the
+    // whole of every segment whose tail transition is not.
+    int i0 = 0;
+    if constexpr (MODE == kLocal) {
+        const bool tail = nch > kTail && sv.pz;
+        if (redo && (!tail || *reinterpret_cast<const uint64_t *>(sv.pz + (static_cast<int64_t>(seg) * H + h) * 8) ==
+                                  0x0101010101010101ull))
+            return;
+        if (!redo && tail) i0 = nch - kTail;
+    }
     const bool pcols = MODE == kLocal && wave >= NWH;  // this wave builds P
     const int ctile0 = NCT * (wave % NWH);         // this wave's first 16-column tile
     const int col0 = 16 * ctile0;
@@ -121,7 +138,7 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
                     acc[rt][ct][jj] = __uint_as_float(ld32(rs, st_lane, st_off(rt, ct, jj)));
-    } else {
+    } else {  // H from zero, P from the identity
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
@@ -196,7 +213,6 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     };
     // U (and dO) of the chunk in use / of the next one (zero for P)
     u4 urA[NCT][2] = {}, urB[NCT][2] = {}, drA[NCT][2] = {}, drB[NCT][2] = {}, ulA[NCT][2] = {}, ulB[NCT][2] = {};
-    fetch(chunk_of(0), lds0, urA, drA, ulA);
 
     // one chunk: its pack is in L, the next one's goes to Lnext
     auto step = [&](int i, const char *L, char *Lnext, const u4 (&ur_cur)[NCT][2], u4 (&ur_nxt)[NCT][2],
@@ -427,7 +443,8 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) smax[ct] = wave_max(mx[ct]);
     };
-    for (int i = 0; i < nch; i += 2) {
+    fetch(chunk_of(i0), lds0, urA, drA, ulA);
+    for (int i = i0; i < nch; i += 2) {
         step(i, lds0, lds1, urA, urB, drA, drB, ulA, ulB);
         if (i + 1 < nch) step(i + 1, lds1, lds0, urB, urA, drB, drA, ulB, ulA);
     }
@@ -535,10 +552,14 @@ void launch_scan_grad(const ChunkLaunch &L, const SegmentView &sv, int max_segs,
     const char *pk = static_cast<const char *>(packs);
     if (MODE == kOut && L.out_bf16)
         hipLaunchKernelGGL((mc::chunk_scan_kernel<MODE, true>), grid, block, 0, L.stream, pk, per, L.hT, L.o, sv, L.H,
-                           gr);
+                           gr, 0);
     else
         hipLaunchKernelGGL((mc::chunk_scan_kernel<MODE, false>), grid, block, 0, L.stream, pk, per, L.hT, L.o, sv,
-                           L.H, gr);
+                           L.H, gr, 0);
+    // the local pass walked only the segments' tails: whole walks of those whose tail transition is not zero
+    if (MODE == kLocal && per > mc::kTail && sv.pz)
+        hipLaunchKernelGGL((mc::chunk_scan_kernel<MODE, false>), grid, block, 0, L.stream, pk, per, L.hT, L.o, sv,
+                           L.H, gr, 1);
 }
 
 template <int MODE>
