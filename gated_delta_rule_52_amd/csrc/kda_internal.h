@@ -147,10 +147,18 @@ struct SegmentView {
     // read in place: the workgroup that reads it is the one that later writes the final state, which may
     // alias it.  Longer sequences read a copy, because their last segment may finish before the first
     // has read its entering state.
+    // A later segment whose predecessor's P is exactly zero enters with that predecessor's H (the combine
+    // leaves such states unwritten when a sequence has no nonzero P).
     __device__ __forceinline__ const float *entering(int seg, int4 sd, int h, int H, int DK, int DV) const {
         if ((sd.w & (kSegFirst | kSegLast)) == (kSegFirst | kSegLast))
             return h0 ? h0 + (static_cast<int64_t>(sd.x) * H + h) * DK * DV : nullptr;
+        if (!(sd.w & kSegFirst) && pz_all(seg - 1, h, H)) return Hs + (static_cast<int64_t>(seg - 1) * H + h) * DK * DV;
         return sin + (static_cast<int64_t>(seg) * H + h) * DK * DV;
+    }
+    // every column tile of segment seg's P at head h is exactly zero (false without flags)
+    __device__ __forceinline__ bool pz_all(int seg, int h, int H) const {
+        return pz && *reinterpret_cast<const uint64_t *>(pz + (static_cast<int64_t>(seg) * H + h) * 8) ==
+                         0x0101010101010101ull;
     }
 };
 

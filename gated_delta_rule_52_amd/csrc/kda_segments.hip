@@ -382,10 +382,15 @@ combine_bf16x3_kernel(SegmentView sv, const float *h0, float *hT, int H, const c
     // without a memory access (the same instructions run, so the step's result is the same bits)
     constexpr int kZCap = 1024;  // steps past this many fetch P as usual
     __shared__ uint8_t pzs[kZCap];
-    for (int i = tid; i < min(nsteps, kZCap); i += 512)
-        pzs[i] = sv.pz && *reinterpret_cast<const uint64_t *>(sv.pz + (static_cast<int64_t>(seg_of(i)) * H + h) * 8) ==
-                              0x0101010101010101ull;
-    __syncthreads();
+    bool live = nsteps > kZCap;  // some step's P is not known to be zero
+    for (int i = tid; i < min(nsteps, kZCap); i += 512) {
+        pzs[i] = sv.pz_all(seg_of(i), h, H);
+        live |= !pzs[i];
+    }
+    // A forward chain of zero transitions only: entering(s + 1) = H_s throughout, and the output pass reads
+    // those states where the local pass left them (SegmentView::entering), so only the initial state's copy
+    // (written above) is needed.
+    if (!__syncthreads_or(live) && !REV) return;
     struct Stage {
         u4v pa[2][4];  // P operands, [plane][block]
         f32x4 hb;      // H addends
