@@ -132,7 +132,7 @@ recurrent_bwd_kernel(BackwardLaunch L, SegmentView sv, const float *dleave) {
     // grid.x = segment * H + head: a packed batch may hold more than grid.y's 65,535 segments
     const int H = L.H, h = static_cast<int>(blockIdx.x % H), seg = static_cast<int>(blockIdx.x / H);
     if (seg >= sv.count()) return;
-    const int4 sd = sv.table[seg];
+    const int4 sd = sv.desc(seg);
     const int n = sd.x;
     const int64_t t0 = sd.y, t1 = sd.z;
     const int tid = threadIdx.x, lane = tid % kWave, slice = tid / kWave;
@@ -471,7 +471,7 @@ __device__ __forceinline__ void segment_local_body(const BackwardLaunch &L, cons
     // grid.x = segment * H + head: a packed batch may hold more than grid.y's 65,535 segments
     const int H = L.H, h = static_cast<int>(blockIdx.x % H), seg = static_cast<int>(blockIdx.x / H);
     if (seg >= sv.count()) return;
-    const int4 sd = sv.table[seg];
+    const int4 sd = sv.desc(seg);
     if ((sd.w & (kSegFirst | kSegLast)) == (kSegFirst | kSegLast)) return;  // one segment: nothing to chain
     const int64_t t0 = sd.y, t1 = sd.z;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -527,7 +527,7 @@ __device__ __forceinline__ void reverse_local_body(const BackwardLaunch &L, cons
     // grid.x = segment * H + head: a packed batch may hold more than grid.y's 65,535 segments
     const int H = L.H, h = static_cast<int>(blockIdx.x % H), seg = static_cast<int>(blockIdx.x / H);
     if (seg >= sv.count()) return;
-    const int4 sd = sv.table[seg];
+    const int4 sd = sv.desc(seg);
     if (sd.w & kSegFirst) return;
     const int64_t t0 = sd.y, t1 = sd.z;
     const int tid = threadIdx.x, lane = tid % kWave, slice = tid / kWave;
@@ -615,7 +615,7 @@ reverse_combine_kernel(SegmentView sv, const float *hb, const float *dhT, float 
     int slice, h, n;
     slice_head_seq(slice, h, n);
     const int tid = threadIdx.x, j = tid % BV, ig = tid / BV, j0 = slice * BV;
-    const int first = sv.seq_seg[n], end = sv.seq_seg[n + 1];
+    const int first = sv.first_seg(n), end = sv.first_seg(n + 1);
     if (end - first == 1) return;
     const int64_t nbase = (static_cast<int64_t>(n) * H + h) * DK * DV;
     float x[ROWS];

@@ -114,7 +114,7 @@ chunk_fp32_kernel(const void *__restrict__ q_, const void *__restrict__ k_,
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lk = lane >> 4;   // MFMA row/col lane, k lane
     if (seg >= sv.count()) return;
-    const int4 sd = sv.table[seg];
+    const int4 sd = sv.desc(seg);
     const int n = sd.x;
     const bool last = sd.w & kSegLast;
     if (MODE == kLocal && last) return;         // a last segment's P, H are never used

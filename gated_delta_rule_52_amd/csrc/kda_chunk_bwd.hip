@@ -55,7 +55,7 @@ rev_pack_kernel(const char *__restrict__ packs, char *__restrict__ rpacks, const
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n16 = lane & 15, g4 = lane >> 4;
     if (seg >= sv.count()) return;
-    const int4 sd = sv.table[seg];
+    const int4 sd = sv.desc(seg);
     const int64_t c0 = sd.y + static_cast<int64_t>(C) * jc, t1 = sd.z;
     if (c0 >= t1) return;
     const int L = static_cast<int>(t1 - c0 < C ? t1 - c0 : C);
@@ -233,7 +233,7 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
     if (seg >= sv.count()) return;
-    const int4 sd = sv.table[seg];
+    const int4 sd = sv.desc(seg);
     const int64_t c0 = sd.y + static_cast<int64_t>(C) * jc, t1 = sd.z;
     if (c0 >= t1) return;
     const int L = static_cast<int>(t1 - c0 < C ? t1 - c0 : C);

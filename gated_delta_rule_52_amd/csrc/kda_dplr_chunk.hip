@@ -84,7 +84,7 @@ dplr_chunk_kernel(DplrChunkLaunch Lp, SegmentView sv) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lk = lane >> 4;
     if (seg >= sv.count()) return;
-    const int4 sd = sv.table[seg];
+    const int4 sd = sv.desc(seg);
     const int n = sd.x;
     const bool last = sd.w & kSegLast;
     if (MODE == kLocal && last) return;

@@ -137,11 +137,23 @@ struct SegmentView {
     float *Hs;              // [max_segs, H, dk, dv]
     float *sin;             // [max_segs, H, dk, dv] entering states (not filled for one-segment sequences)
     const float *h0;        // [N, H, dk, dv] initial states (null: zero)
-    int *xlist;             // chunks (pack numbers) the matrix-core prep hands to its exact path
-    int *xcount;            // their count (zeroed by the segment-table kernel)
+    int fixed_T = -1;       // >= 0: fixed-length batch of N sequences of fixed_T tokens, cut into segments of
+    int seg_len = 0;        // seg_len tokens; the table is then computed where needed instead of read
     uint8_t *pz = nullptr;  // [max_segs, H, 8] matrix-core path: byte w is 1 when column tile w (16 columns) of
                             // the segment's P is exactly zero; the local pass writes it for every P it builds
-    __device__ __forceinline__ int count() const { return seq_seg[N]; }
+    // segments per sequence of a fixed-length batch
+    __device__ __forceinline__ int fixed_segs() const { return (fixed_T + seg_len - 1) / seg_len; }
+    __device__ __forceinline__ int count() const { return fixed_T >= 0 ? N * fixed_segs() : seq_seg[N]; }
+    // first segment of sequence n (n = N: the count)
+    __device__ __forceinline__ int first_seg(int n) const { return fixed_T >= 0 ? n * fixed_segs() : seq_seg[n]; }
+    // {sequence, first token, end token, flags} of segment seg
+    __device__ __forceinline__ int4 desc(int seg) const {
+        if (fixed_T < 0) return table[seg];
+        const int ns = fixed_segs(), n = seg / ns, s = seg - n * ns;
+        const int t0 = n * fixed_T + s * seg_len, end = (n + 1) * fixed_T;
+        return make_int4(n, t0, t0 + seg_len < end ? t0 + seg_len : end,
+                         (s == ns - 1 ? kSegLast : 0) | (s == 0 ? kSegFirst : 0));
+    }
     // the entering state of segment seg = {sequence, first token, end token, flags} at head h, row-major
     // dk x dv; null stands for the zero state.  A sequence of one segment enters with its initial state,
     // read in place: the workgroup that reads it is the one that later writes the final state, which may

@@ -209,6 +209,9 @@ constexpr int kPkLocal = kPkQ;   // bytes the local pass copies to LDS
 constexpr int kPkOut = kPkU;     // bytes the output pass copies to LDS
 static_assert(kPkLocal % 1024 == 0 && kPkOut % 1024 == 0, "whole 1 KiB wave copies");
 enum { kHdrW = 0, kHdrQ = 1, kHdrK = 2, kHdrU = 3, kHdrA = 4, kHdrDO = 5, kHdrUL = 6 };
+// header word 7 of a forward pack: 1 when the fast prep left the chunk to its exact path, written for every
+// slot (an empty slot's pack holds only this word); each pack's own line, so no two workgroups share it
+constexpr int kHdrX = 7;
 
 // ---- reverse pack (gradients), one per chunk and head, same slots: the walk
 // over the chunks in reverse order carries dS (the gradient of the state a

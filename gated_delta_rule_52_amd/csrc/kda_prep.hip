@@ -137,10 +137,19 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
     // The 16 lanes of one DPP row hold a whole token row, and every load moves 8 bytes of a bf16 input or
     // 16 bytes of the gate.
     const int cq = tid & 15, rq = tid >> 4;
-    if (seg >= sv.count()) return;
-    const int4 sd = sv.table[seg];
+    // the fast path records in every slot's pack whether it leaves the chunk to the exact path (empty: no)
+    char *pack = packs + (static_cast<int64_t>(bx) * H + h) * kPkBytes;
+    int *xflag = reinterpret_cast<int *>(pack + kPkHdr + 4 * kHdrX);
+    if (seg >= sv.count()) {
+        if (!EXACT && tid == 0) *xflag = 0;
+        return;
+    }
+    const int4 sd = sv.desc(seg);
     const int64_t c0 = sd.y + static_cast<int64_t>(C) * jc, t1 = sd.z;
-    if (c0 >= t1) return;
+    if (c0 >= t1) {
+        if (!EXACT && tid == 0) *xflag = 0;
+        return;
+    }
     const int L = static_cast<int>(t1 - c0 < C ? t1 - c0 : C);
 
     // the chunk's rows of head h; rows past L read as zero
@@ -155,7 +164,6 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
     const bool sg = SG || (XF && ix.scalar_gate);
     const rsrc_t rs_g = make_rsrc(g + (sg ? 0 : base), sg ? 0 : 4 * elems);
     const rsrc_t rs_gs = make_rsrc(g + (sg ? c0 * H + h : 0), sg ? 4 * static_cast<uint32_t>((L - 1) * H + 1) : 0);
-    char *pack = packs + (static_cast<int64_t>(bx) * H + h) * kPkBytes;
     const rsrc_t rs_p = make_rsrc(pack, kPkBytes);
     const rsrc_t rs_r = make_rsrc(RV ? rpacks + (static_cast<int64_t>(bx) * H + h) * kRvBytes : nullptr,
                                   RV ? kRvBytes : 0);
@@ -291,10 +299,9 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
         }
     __syncthreads();  // (2b) the sums are read before the operand area takes the Gram operands
     if constexpr (!EXACT) {
-        if (sm.imax[5] != 0) {  // beyond the factored form's range: exact kernel
-            if (tid == 0) sv.xlist[atomicAdd(sv.xcount, 1)] = bx * H + h;
-            return;
-        }
+        const bool exact = sm.imax[5] != 0;  // beyond the factored form's range: exact kernel
+        if (tid == 0) *xflag = exact;
+        if (exact) return;
     }
 
     // ============ a2: Gram tiles, one half of dk at a time ============
@@ -716,22 +723,35 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     prep_chunk<false, XF, SG, RV>(sm, nullptr, nullptr, bx, h, q, k, v, g, beta, sv, per, H, scale, packs, ix, rpacks);
 }
 
-// exact path over the chunks the fast path listed (usually none)
+// exact path over the slots the fast path flagged (usually none): each workgroup takes NT consecutive slots
+// at a time, gathers their flags by wave ballots, and runs the flagged ones
 template <bool XF, bool RV>
 __global__ void __launch_bounds__(NT, 1)
 chunk_prep_exact_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                         const uint16_t *__restrict__ v, const float *__restrict__ g,
                         const uint16_t *__restrict__ beta, SegmentView sv, int per, int H, float scale,
-                        char *__restrict__ packs, InputXform ix, char *__restrict__ rpacks) {
+                        char *__restrict__ packs, InputXform ix, char *__restrict__ rpacks, int nslots) {
     __shared__ PrepSmem sm;
     __shared__ float gx[C * GP];  // G of the chunk, for the pair-by-pair Gram entries
     __shared__ float nx[2 * C];   // XF: 1/|k| and 1/|q| of each row
-    const int n = *sv.xcount;
-    for (int i = blockIdx.x; i < n; i += gridDim.x) {
-        const int id = sv.xlist[i];
-        __syncthreads();  // the previous chunk's last LDS reads are done
-        prep_chunk<true, XF, false, RV>(sm, gx, nx, id / H, id % H, q, k, v, g, beta, sv, per, H, scale, packs, ix,
-                                        rpacks);
+    __shared__ unsigned long long s_mask[NT / 64];
+    const int tid = threadIdx.x;
+    for (int base = blockIdx.x * NT; base < nslots; base += gridDim.x * NT) {
+        const bool f = base + tid < nslots &&
+                       *reinterpret_cast<const int *>(packs + static_cast<int64_t>(base + tid) * kPkBytes + kPkHdr +
+                                                      4 * kHdrX);
+        const unsigned long long m = __ballot(f);
+        if ((tid & 63) == 0) s_mask[tid >> 6] = m;
+        __syncthreads();  // the masks are complete
+        for (int w = 0; w < NT / 64; ++w) {
+            for (unsigned long long mm = s_mask[w]; mm; mm &= mm - 1) {
+                const int id = base + 64 * w + __builtin_ctzll(mm);
+                __syncthreads();  // the previous chunk's last LDS reads are done
+                prep_chunk<true, XF, false, RV>(sm, gx, nx, id / H, id % H, q, k, v, g, beta, sv, per, H, scale,
+                                                packs, ix, rpacks);
+            }
+        }
+        __syncthreads();  // every thread has read the masks
     }
 }
 
@@ -749,11 +769,12 @@ void launch_prep(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int 
     const uint16_t *v = static_cast<const uint16_t *>(L.v), *b = static_cast<const uint16_t *>(L.beta);
     char *pk = static_cast<char *>(packs), *rp = static_cast<char *>(rpacks);
     const dim3 grid(static_cast<unsigned>(max_segs) * static_cast<unsigned>(per) * L.H), block(mc::NT);
+    const int nslots = static_cast<int>(grid.x);
     if (rp) {  // the gradients: no input transform, and the reverse pack's slots besides
         hipLaunchKernelGGL((mc::chunk_prep_kernel<false, false, true>), grid, block, 0, L.stream, q, k, v, L.g, b, sv,
                            per, L.H, L.scale, pk, L.xf, rp);
         hipLaunchKernelGGL((mc::chunk_prep_exact_kernel<false, true>), dim3(256), block, 0, L.stream, q, k, v, L.g, b,
-                           sv, per, L.H, L.scale, pk, L.xf, rp);
+                           sv, per, L.H, L.scale, pk, L.xf, rp, nslots);
     } else if (L.xf.scalar_gate) {  // the scalar-gate Gram is exact at any decay: no exact pass
         hipLaunchKernelGGL((mc::chunk_prep_kernel<true, true, false>), grid, block, 0, L.stream, q, k, v, L.g, b, sv,
                            per, L.H, L.scale, pk, L.xf, rp);
@@ -761,12 +782,12 @@ void launch_prep(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int 
         hipLaunchKernelGGL((mc::chunk_prep_kernel<true, false, false>), grid, block, 0, L.stream, q, k, v, L.g, b, sv,
                            per, L.H, L.scale, pk, L.xf, rp);
         hipLaunchKernelGGL((mc::chunk_prep_exact_kernel<true, false>), dim3(256), block, 0, L.stream, q, k, v, L.g, b,
-                           sv, per, L.H, L.scale, pk, L.xf, rp);
+                           sv, per, L.H, L.scale, pk, L.xf, rp, nslots);
     } else {
         hipLaunchKernelGGL((mc::chunk_prep_kernel<false, false, false>), grid, block, 0, L.stream, q, k, v, L.g, b, sv,
                            per, L.H, L.scale, pk, L.xf, rp);
         hipLaunchKernelGGL((mc::chunk_prep_exact_kernel<false, false>), dim3(256), block, 0, L.stream, q, k, v, L.g, b,
-                           sv, per, L.H, L.scale, pk, L.xf, rp);
+                           sv, per, L.H, L.scale, pk, L.xf, rp, nslots);
     }
 }
 

@@ -90,7 +90,7 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
     if (seg >= sv.count()) return;
-    const int4 sd = sv.table[seg];
+    const int4 sd = sv.desc(seg);
     const int nseq = sd.x;
     const bool last = sd.w & kSegLast, first = sd.w & kSegFirst;
     // a last segment's P and H serve only the reverse combine; a one-segment sequence needs neither

@@ -37,7 +37,7 @@ struct Plan {
     int seg_len;    // tokens per segment (per * chunk)
     int max_segs;   // bound on the number of segments
     bool packs;     // matrix-core path: one operand pack per chunk and head
-    size_t off_table, off_seq, off_P, off_H, off_S, off_pack, off_xlist, off_pz, bytes;
+    size_t off_table, off_seq, off_P, off_H, off_S, off_pack, off_pz, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t{255}; }
@@ -74,7 +74,6 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int N, int chunk, bool varle
     p.off_H = o;     o = align256(o + ms * H * dk * dv * sizeof(float));
     p.off_S = o;     o = align256(o + ms * H * dk * dv * sizeof(float));
     p.off_pack = o;  o = align256(o + (p.packs ? ms * p.per * H * pack_bytes() : 0));
-    p.off_xlist = o; o = align256(o + (p.packs ? (ms * p.per * H + 1) * sizeof(int) : 0));
     p.off_pz = o;    o = align256(o + (p.packs ? ms * H * 8 : 0));
     p.bytes = o;
     return p;
@@ -86,10 +85,9 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int N, int chunk, bool varle
 // segment.
 __global__ void __launch_bounds__(256)
 build_segments_kernel(const int32_t *__restrict__ cu_seqlens, int T, int N, int seg_len,
-                      int4 *__restrict__ table, int32_t *__restrict__ seq_seg, int *xcount) {
+                      int4 *__restrict__ table, int32_t *__restrict__ seq_seg) {
     __shared__ int s_cnt[4];
     const int tid = threadIdx.x;
-    if (tid == 0 && xcount) *xcount = 0;
     const int per = (N + 255) / 256;
     const int n0 = tid * per, n1 = min(N, n0 + per);
     auto bounds = [&](int n, int64_t &a, int64_t &b) {
@@ -151,7 +149,7 @@ combine_kernel(SegmentView sv, const float *h0, float *hT, int H, int DV) {
     const int slice = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
     const int tid = threadIdx.x, j = tid % BV, ig = tid / BV;
     const int j0 = slice * BV;
-    const int first = sv.seq_seg[n], end = sv.seq_seg[n + 1];
+    const int first = sv.first_seg(n), end = sv.first_seg(n + 1);
     if (end - first == 1) return;  // one segment: nothing to carry
     const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * DV;
 
@@ -231,7 +229,7 @@ combine_mfma_kernel(SegmentView sv, const float *h0, float *hT, int H, int DV) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, m = lane & 15;
     const int j0 = 16 * slice;
-    const int first = sv.seq_seg[n], end = sv.seq_seg[n + 1];
+    const int first = sv.first_seg(n), end = sv.first_seg(n + 1);
     const int nsteps = end - first - 1;  // segments whose leaving state is some segment's entering state
     if (nsteps == 0) return;             // one segment: nothing to carry
     const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * DV;
@@ -348,7 +346,7 @@ combine_bf16x3_kernel(SegmentView sv, const float *h0, float *hT, int H, const c
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, m = lane & 15;
     const int j0 = NC * slice;
-    const int first = sv.seq_seg[n], end = sv.seq_seg[n + 1];
+    const int first = sv.first_seg(n), end = sv.first_seg(n + 1);
     const int nsteps = end - first - 1;
     if (nsteps == 0) return;  // one segment: nothing to carry
     const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * DV;
@@ -482,6 +480,18 @@ bool chunk_grids_fit(int B, int T, int H, int dk, int dv, int N, int chunk, bool
     return prep < (uint64_t{1} << 32) && fp32 < (uint64_t{1} << 32);
 }
 
+// The segment table of a packed batch; a fixed-length batch's segments are computed where they are needed
+// (SegmentView::desc), which saves a launch.
+void launch_table(const ChunkLaunch &L, const Plan &p, char *ws, SegmentView &sv) {
+    if (L.cu_seqlens) {
+        hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(256), 0, L.stream, L.cu_seqlens, L.T, L.N, p.seg_len,
+                           reinterpret_cast<int4 *>(ws + p.off_table), reinterpret_cast<int32_t *>(ws + p.off_seq));
+    } else {
+        sv.fixed_T = L.T;
+        sv.seg_len = p.seg_len;
+    }
+}
+
 hipError_t launch_chunk(const ChunkLaunch &L) {
     const bool varlen = L.cu_seqlens != nullptr;
     const Plan p = make_plan(L.B, L.T, L.H, L.dk, L.dv, L.N, L.chunk, varlen, L.in_bf16);
@@ -494,13 +504,8 @@ hipError_t launch_chunk(const ChunkLaunch &L) {
     sv.Hs = reinterpret_cast<float *>(ws + p.off_H);
     sv.sin = reinterpret_cast<float *>(ws + p.off_S);
     sv.h0 = L.h0;
-    sv.xcount = p.packs ? reinterpret_cast<int *>(ws + p.off_xlist) : nullptr;
-    sv.xlist = p.packs ? sv.xcount + 1 : nullptr;
     sv.pz = p.packs ? reinterpret_cast<uint8_t *>(ws + p.off_pz) : nullptr;
-
-    hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(256), 0, L.stream, L.cu_seqlens, L.T, L.N,
-                       p.seg_len, reinterpret_cast<int4 *>(ws + p.off_table),
-                       reinterpret_cast<int32_t *>(ws + p.off_seq), sv.xcount);
+    launch_table(L, p, ws, sv);
     void *packs = ws + p.off_pack;
     // fixed-length sequences no longer than a segment are one segment each: the local pass and the
     // combine would only return (their launches alone cost tens of microseconds on many short sequences)
@@ -546,12 +551,8 @@ SegmentView launch_chunk_grad_forward(const ChunkLaunch &L, const ScanGrad &gr, 
     sv.Hs = reinterpret_cast<float *>(ws + p.off_H);
     sv.sin = reinterpret_cast<float *>(ws + p.off_S);
     sv.h0 = L.h0;
-    sv.xcount = reinterpret_cast<int *>(ws + p.off_xlist);
-    sv.xlist = sv.xcount + 1;
     sv.pz = p.packs ? reinterpret_cast<uint8_t *>(ws + p.off_pz) : nullptr;
-    hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(256), 0, L.stream, L.cu_seqlens, L.T, L.N,
-                       p.seg_len, reinterpret_cast<int4 *>(ws + p.off_table),
-                       reinterpret_cast<int32_t *>(ws + p.off_seq), sv.xcount);
+    launch_table(L, p, ws, sv);
     *packs = ws + p.off_pack;
     *chained = varlen || L.T == 0 || L.T > p.seg_len;
     launch_prep(L, sv, p.max_segs, p.per, *packs, rpacks);
@@ -588,13 +589,11 @@ SegmentStates launch_segment_table(const ChunkLaunch &L) {
     sv.Hs = reinterpret_cast<float *>(ws + p.off_H);
     sv.sin = reinterpret_cast<float *>(ws + p.off_S);
     sv.h0 = L.h0;
-    sv.xcount = nullptr;
-    sv.xlist = nullptr;
     r.max_segs = p.max_segs;
     r.seg_len = p.seg_len;
     hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(256), 0, L.stream, L.cu_seqlens, L.T, L.N,
                        p.seg_len, reinterpret_cast<int4 *>(ws + p.off_table),
-                       reinterpret_cast<int32_t *>(ws + p.off_seq), nullptr);
+                       reinterpret_cast<int32_t *>(ws + p.off_seq));
     return r;
 }
 
