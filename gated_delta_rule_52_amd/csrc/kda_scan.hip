@@ -104,6 +104,8 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     // from zero: the earlier chunks' part lies below fp32's range, just as a zero P drops the entering state in
     // the combine.  The flags in sv.pz record whether P_tail is zero; a second launch (redo = 1) walks the
     // whole of every segment whose tail transition is not.
+    __shared__ int s_live;  // kLocal: some P tile of the tail walk is not zero
+    if (MODE == kLocal && tid == 0) s_live = 0;
     int i0 = 0;
     if constexpr (MODE == kLocal) {
         const bool tail = nch > kTail && sv.pz;
@@ -452,6 +454,18 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
         if (nch > 0) {
             __syncthreads();  // the last chunk's o is staged by every wave
             store_rows(nch - 1);
+        }
+    }
+
+    if constexpr (MODE == kLocal) {
+        // a tail walk whose P is not zero stores nothing but its flags: the second launch writes H and P
+        if (i0 > 0) {
+            if (pcols && lane == 0 && smax[0] != 0.f) atomicOr(&s_live, 1);
+            __syncthreads();  // s_live complete
+            if (s_live) {
+                if (pcols && lane == 0) sv.pz[(static_cast<int64_t>(seg) * H + h) * 8 + (wave - NWH)] = smax[0] == 0.f;
+                return;
+            }
         }
     }
 
