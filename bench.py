@@ -685,8 +685,9 @@ def main():
                      "pages_flops_per_launch": PAGES_FLOPS_PER_TOKEN_HEAD * x.B * x.T * x.H,
                      "mfma_frac_of_bf16_peak": PAGES_FLOPS_PER_TOKEN_HEAD * x.B * x.T * x.H / (ms * 1e-3) / 1e12
                                                / BF16_MFMA_PEAK_TFLOPS,
-                     "kernel": "kda_chunk_fwd: one call = segment table, prep, local scan, "
-                               "combine, output scan (timed together on the library's stream)"},
+                     "kernel": "kda_chunk_fwd: one call = prep, exact-path pass, local scan (segment tails, "
+                               "then whole segments whose tail transition is not zero), combine, output scan "
+                               "(timed together on the library's stream)"},
     }
     rec["ceilings"] = ceil
     if not args.no_decode:
