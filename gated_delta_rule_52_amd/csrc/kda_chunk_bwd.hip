@@ -786,7 +786,7 @@ namespace {
 
 struct BwdChunkPlan {
     ChunkGradLayout fwd;
-    size_t off_rp, off_st, off_vn, off_dst, off_dvn, off_hb, off_dl, off_pt, bytes;
+    size_t off_rp, off_st, off_vn, off_dst, off_dvn, off_hb, off_dl, off_pt, off_pzh, bytes;
 };
 
 BwdChunkPlan bwd_chunk_plan(int B, int T, int H, int N, bool varlen) {
@@ -804,6 +804,7 @@ BwdChunkPlan bwd_chunk_plan(int B, int T, int H, int N, bool varlen) {
     p.off_hb = o;  o = a256(o + seg_state);
     p.off_dl = o;  o = a256(o + seg_state);
     p.off_pt = o;  o = a256(o + seg_state);  // P^T planes: the same bytes as a fp32 state
+    p.off_pzh = o; o = a256(o + static_cast<size_t>(p.fwd.max_segs) * H * 8);
     p.bytes = o;
     return p;
 }
@@ -842,6 +843,7 @@ hipError_t launch_chunk_bwd(const BackwardLaunch &L) {
     gf.vn = reinterpret_cast<float *>(ws + p.off_vn);
     gf.keep_last = true;
     gf.pt = ws + p.off_pt;
+    gf.pzh = reinterpret_cast<uint8_t *>(ws + p.off_pzh);
     bool chained = false;
     void *packs = nullptr;
     char *rp = ws + p.off_rp;
@@ -857,6 +859,7 @@ hipError_t launch_chunk_bwd(const BackwardLaunch &L) {
     gr.dhT = L.dhT;
     gr.dh0 = L.dh0;
     gr.hb = reinterpret_cast<float *>(ws + p.off_hb);
+    gr.pzh = gf.pzh;
     if (chained) {
         launch_scan_grad<kRevLocal>(c, sv, max_segs, per, rp, gr);
         launch_reverse_combine_bf16(sv, gf.pt, gr.hb, L.dhT, reinterpret_cast<float *>(ws + p.off_dl), L.dh0, L.H,

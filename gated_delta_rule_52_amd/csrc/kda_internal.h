@@ -219,6 +219,9 @@ struct ScanGrad {
     bool keep_last;       // kLocal: P and H of every segment but a one-segment sequence's (the reverse combine
                           // needs P of last segments)
     char *pt;             // kLocal: also P^T as bf16 high and low planes, [segment * H + h] 64 KiB each
+    uint8_t *pzh;         // kLocal writes (its second grid layer), kRevLocal reads: [segment * H + h] 8 bytes,
+                          // byte w 1 where column tile w of the transition over the segment's first 4 chunks
+                          // is exactly zero (not written for segments of at most 4 chunks)
 };
 template <int MODE>
 void launch_scan_grad(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, const void *packs,

@@ -106,13 +106,28 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
     // whole of every segment whose tail transition is not.
     __shared__ int s_live;  // kLocal: some P tile of the tail walk is not zero
     if (MODE == kLocal && tid == 0) s_live = 0;
-    int i0 = 0;
+    // The gradients' reverse local pass walks a segment last to first from zero at its end.  Where the forward
+    // transition over the segment's first kTail chunks is exactly zero, the chunks after them reach the segment's
+    // start only through that transition's transpose, so the walk takes those first chunks alone.  The forward
+    // local pass finds that transition in a second grid layer (blockIdx.z = 1, P waves only, flags in gr.pzh).
+    const bool head = MODE == kLocal && blockIdx.z == 1;
+    int i0 = 0, iend = nch;  // the walked steps
     if constexpr (MODE == kLocal) {
-        const bool tail = nch > kTail && sv.pz;
-        if (redo && (!tail || *reinterpret_cast<const uint64_t *>(sv.pz + (static_cast<int64_t>(seg) * H + h) * 8) ==
-                                  0x0101010101010101ull))
-            return;
-        if (!redo && tail) i0 = nch - kTail;
+        if (head) {
+            if (nch <= kTail || !gr.pzh) return;
+            iend = kTail;
+        } else {
+            const bool tail = nch > kTail && sv.pz;
+            if (redo && (!tail || *reinterpret_cast<const uint64_t *>(sv.pz + (static_cast<int64_t>(seg) * H + h) * 8) ==
+                                      0x0101010101010101ull))
+                return;
+            if (!redo && tail) i0 = nch - kTail;
+        }
+    }
+    if constexpr (MODE == kRevLocal) {
+        if (gr.pzh && nch > kTail &&
+            *reinterpret_cast<const uint64_t *>(gr.pzh + (static_cast<int64_t>(seg) * H + h) * 8) == 0x0101010101010101ull)
+            i0 = nch - kTail;
     }
     const bool pcols = MODE == kLocal && wave >= NWH;  // this wave builds P
     const int ctile0 = NCT * (wave % NWH);         // this wave's first 16-column tile
@@ -223,13 +238,13 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
         const int j = chunk_of(i);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // chunk j in L; every wave is done with the previous chunk
-        if (i + 1 < nch) fetch(chunk_of(i + 1), Lnext, ur_nxt, dr_nxt, ul_nxt);
+        if (i + 1 < iend) fetch(chunk_of(i + 1), Lnext, ur_nxt, dr_nxt, ul_nxt);
         if constexpr (kRowsOut)  // every wave's part of the previous chunk's o is in orows now
             if (i > 0) store_rows(j - 1);
         // A P tile that has decayed to exactly zero stays zero (gamma 0 + KT (0 - W 0) = 0), so its wave only
         // takes its share of the copies from here on.  Under strong gates P underflows within a few chunks.
         if constexpr (MODE == kLocal)
-            if (pcols && smax[0] == 0.f) return;
+            if (pcols ? smax[0] == 0.f : head) return;  // the head layer builds P only
 
         const int *hdr = reinterpret_cast<const int *>(L + kPkHdr);
         const int ew = hdr[kHdrW], ek = hdr[kHdrK];
@@ -446,9 +461,13 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
         for (int ct = 0; ct < NCT; ++ct) smax[ct] = wave_max(mx[ct]);
     };
     fetch(chunk_of(i0), lds0, urA, drA, ulA);
-    for (int i = i0; i < nch; i += 2) {
+    for (int i = i0; i < iend; i += 2) {
         step(i, lds0, lds1, urA, urB, drA, drB, ulA, ulB);
-        if (i + 1 < nch) step(i + 1, lds1, lds0, urB, urA, drB, drA, ulB, ulA);
+        if (i + 1 < iend) step(i + 1, lds1, lds0, urB, urA, drB, drA, ulB, ulA);
+    }
+    if (head) {  // the head layer leaves its flags only
+        if (pcols && lane == 0) gr.pzh[(static_cast<int64_t>(seg) * H + h) * 8 + (wave - NWH)] = smax[0] == 0.f;
+        return;
     }
     if constexpr (kRowsOut) {
         if (nch > 0) {
@@ -562,7 +581,8 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
 template <int MODE>
 void launch_scan_grad(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int per, const void *packs,
                       const ScanGrad &gr) {
-    dim3 grid(max_segs, L.H), block(mc::ScanCfg<MODE>::NT);
+    // the forward local pass of the gradients also finds the transitions over the segments' first chunks
+    dim3 grid(max_segs, L.H, MODE == kLocal && gr.pzh ? 2 : 1), block(mc::ScanCfg<MODE>::NT);
     const char *pk = static_cast<const char *>(packs);
     if (MODE == kOut && L.out_bf16)
         hipLaunchKernelGGL((mc::chunk_scan_kernel<MODE, true>), grid, block, 0, L.stream, pk, per, L.hT, L.o, sv, L.H,
@@ -572,8 +592,8 @@ void launch_scan_grad(const ChunkLaunch &L, const SegmentView &sv, int max_segs,
                            L.H, gr, 0);
     // the local pass walked only the segments' tails: whole walks of those whose tail transition is not zero
     if (MODE == kLocal && per > mc::kTail && sv.pz)
-        hipLaunchKernelGGL((mc::chunk_scan_kernel<MODE, false>), grid, block, 0, L.stream, pk, per, L.hT, L.o, sv,
-                           L.H, gr, 1);
+        hipLaunchKernelGGL((mc::chunk_scan_kernel<MODE, false>), dim3(max_segs, L.H), block, 0, L.stream, pk, per,
+                           L.hT, L.o, sv, L.H, gr, 1);
 }
 
 template <int MODE>
