@@ -99,6 +99,19 @@ def test_zero_and_carrying_transitions_in_one_chain(kda):
     check(kda, x, do, dhT)
 
 
+def test_head_and_tail_walks_that_hold_and_that_fail(kda):
+    """32,768 tokens, 2 heads: segments of 8 chunks, long retention (gate scale 0.01), with strong gates (scale 3)
+    in the last 4 chunks of every third segment (the forward tail walk holds) and in the first 4 chunks of the
+    next one (the reverse local pass walks only those: the forward transition over them is zero); the third
+    segment of each group keeps its memory end to end (both walks whole).  Two sampled pairs."""
+    x = make_prefill(168, 1, 32768, 2, 128, 128, gscale=0.01, h0_std=0.05, name="cbwd_walks")
+    for s0 in range(0, 32768, 3 * 512):
+        x.g[0, s0 + 256:s0 + 512] *= 300.0
+        x.g[0, s0 + 512:s0 + 768] *= 300.0
+    do, dhT = make_output_grads(x, 268, dhT_std=0.05)
+    check(kda, x, do, dhT, pairs=[(0, 0), (0, 1)])
+
+
 def test_fast_decay_takes_the_exact_chunk_path(kda):
     """Gate scale 4: chunks decay past e^-80, so the Gram products and their
     gradients are formed pair by pair."""

@@ -202,6 +202,18 @@ def test_zero_and_carrying_transitions_in_one_chain(kda):
     check_prefill(kda, x)
 
 
+def test_tail_walks_that_hold_and_that_fail(kda):
+    """65,536 tokens, 2 heads: segments of 8 chunks (512 tokens), so the local pass first walks each segment's
+    last 4 chunks.  Long retention (gate scale 0.01) everywhere, and strong gates (scale 3) in the last 4 chunks
+    of every third segment (their tail transition is zero: the tail walk holds) and in the first 4 chunks of the
+    next one (its tail keeps its memory: the second launch walks it whole)."""
+    x = make_prefill(56, 1, 65536, 2, 128, 128, gscale=0.01, h0_std=0.3, name="tail_walks")
+    for s0 in range(0, 65536, 3 * 512):
+        x.g[0, s0 + 256:s0 + 512] *= 300.0   # segment s: strong tail
+        x.g[0, s0 + 512:s0 + 768] *= 300.0   # segment s + 1: strong head, weak tail
+    check_prefill(kda, x)
+
+
 def test_magnitude_jumps_between_chunks(kda):
     """Values whose size jumps by 10^4 from one chunk to the next, up and down, from a zero initial
     state: the serial walk's fp16 operand frames, taken from the previous chunk's maxima, must be
