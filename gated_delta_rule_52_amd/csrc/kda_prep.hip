@@ -119,7 +119,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // bx * H + h.  RV (for the gradients) also writes the reverse pack's -Kd,
 // -W^T and Q^T slots (kda_mfma.h) from the same fp16 values, into rpacks.  EXACT = false is the matrix-core path; a chunk whose decay
 // exceeds exp(-kMaxChunkDecay) in some channel is not written there but
-// appended to the exact list, and EXACT = true redoes it with the pair-by-pair
+// flagged in its pack's header, and EXACT = true redoes it with the pair-by-pair
 // Gram blocks.  Returns early (whole workgroup) for chunks past the segment end.
 template <bool EXACT, bool XF, bool SG, bool RV>
 __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, int bx, int h,
