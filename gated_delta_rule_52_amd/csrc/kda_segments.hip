@@ -19,6 +19,8 @@
 //             state, write o and (last segment) the final state.
 //
 // All passes run on the caller's stream; nothing is allocated.
+#include <algorithm>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_mfma.h"
@@ -31,6 +33,7 @@ namespace {
 // 1,024 chunk-heads, e.g. 2K tokens x 16 heads), where the combine's serial chain would cost more than
 // the extra parallelism saves (measured: 2K tokens x 16 heads 90 -> 79 us, 4K level, longer unchanged)
 constexpr int kTargetUnits = 256, kTargetUnitsShort = 128, kShortChunkHeads = 1024;
+constexpr int kTail = 4;  // chunks the local pass walks first at a segment's end (kda_scan.hip)
 
 struct Plan {
     int per;        // chunks per segment
@@ -47,7 +50,11 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int N, int chunk, bool varle
     const int64_t tokens = varlen ? T : static_cast<int64_t>(B) * T;
     const int64_t chunks = varlen ? (tokens + chunk - 1) / chunk + N
                                   : static_cast<int64_t>(B) * ((T + chunk - 1) / chunk);
-    const int64_t units = chunks * H <= kShortChunkHeads ? kTargetUnitsShort : kTargetUnits;
+    // short problems: segments of at least kTail chunks (the local pass walks such a segment whole, and its
+    // transition is then zero under strong gates, which empties the combine), at most 256 of them
+    const int64_t units = chunks * H <= kShortChunkHeads
+                              ? std::max<int64_t>(kTargetUnitsShort, std::min<int64_t>(kTargetUnits, chunks * H / kTail))
+                              : kTargetUnits;
     int64_t per = (chunks * H + units - 1) / units;
     if (per > 64) per = 64;
     // Segments never span two sequences, so a segment longer than the
