@@ -202,6 +202,14 @@ def test_zero_and_carrying_transitions_in_one_chain(kda):
     check_prefill(kda, x)
 
 
+def test_short_plan_with_long_retention(kda):
+    """4,096 tokens, 16 heads: the short-problem plan's 16 segments of 4 chunks per head, walked whole by the
+    local pass; with long retention (gate scale 0.01) no transition is zero, so the combine carries the state
+    through its 15-step chain on every head."""
+    x = make_prefill(57, 1, 4096, 16, 128, 128, gscale=0.01, h0_std=0.3, name="short_plan_slow")
+    check_prefill(kda, x, heads=[0, 5, 15])
+
+
 def test_tail_walks_that_hold_and_that_fail(kda):
     """65,536 tokens, 2 heads: segments of 8 chunks (512 tokens), so the local pass first walks each segment's
     last 4 chunks.  Long retention (gate scale 0.01) everywhere, and strong gates (scale 3) in the last 4 chunks
