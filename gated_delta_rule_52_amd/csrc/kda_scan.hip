@@ -142,7 +142,10 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
         // a zero-sized resource reads zeros: the zero initial state (or final-state gradient)
         const float *src;
         if constexpr (MODE == kRevOut) {
+            // the gradient leaving a segment whose successor's P is exactly zero is that successor's Hb (the
+            // reverse combine leaves it unwritten when a sequence has no nonzero P)
             if (first && last) src = gr.dhT ? gr.dhT + (static_cast<int64_t>(nseq) * H + h) * DK * DV : nullptr;
+            else if (!last && sv.pz_all(seg + 1, h, H)) src = gr.hb + (static_cast<int64_t>(seg + 1) * H + h) * DK * DV;
             else src = gr.dleave + (static_cast<int64_t>(seg) * H + h) * DK * DV;
         } else {
             src = sv.entering(seg, sd, h, H, DK, DV);

@@ -393,10 +393,11 @@ combine_bf16x3_kernel(SegmentView sv, const float *h0, float *hT, int H, const c
         pzs[i] = sv.pz_all(seg_of(i), h, H);
         live |= !pzs[i];
     }
-    // A forward chain of zero transitions only: entering(s + 1) = H_s throughout, and the output pass reads
-    // those states where the local pass left them (SegmentView::entering), so only the initial state's copy
-    // (written above) is needed.
-    if (!__syncthreads_or(live) && !REV) return;
+    // A chain of zero transitions only: entering(s + 1) = H_s throughout (reversed: dleave(s - 1) = Hb_s), and
+    // the output pass (the reverse replay) reads those states where the local pass left them
+    // (SegmentView::entering, and the reverse replay's own choice), so only the first state's copy (written
+    // above) is needed.
+    if (!__syncthreads_or(live)) return;
     struct Stage {
         u4v pa[2][4];  // P operands, [plane][block]
         f32x4 hb;      // H addends
