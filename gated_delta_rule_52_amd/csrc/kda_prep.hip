@@ -393,8 +393,10 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, float *gx, float *nx, i
                 }
             }
             ekp[hh][m] = u2{pack_h2(ekv[0], ekv[1]), pack_h2(ekv[2], ekv[3])};
-            // Q: the four channels hh HC + 4cq .. + 3 of row r are 8 contiguous bytes of a 16-byte unit
-            st64(rs_p, u2{pack_h2(qsv[0], qsv[1]), pack_h2(qsv[2], qsv[3])}, kPkQ + w_col(r, hh * HC + 4 * cq));
+            // Q: the four channels hh HC + 4cq .. + 3 of row r are 8 contiguous bytes of a 16-byte unit (the
+            // gradients' passes read only the reverse pack's Q^T, so their forward pack goes without)
+            if constexpr (!RV)
+                st64(rs_p, u2{pack_h2(qsv[0], qsv[1]), pack_h2(qsv[2], qsv[3])}, kPkQ + w_col(r, hh * HC + 4 * cq));
             u2 kdw = {0u, 0u};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
