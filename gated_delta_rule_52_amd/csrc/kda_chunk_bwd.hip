@@ -216,7 +216,8 @@ __device__ __forceinline__ void tri_ab(int t, int &a, int &b) {
 struct GradArgs {
     const uint16_t *q, *k, *v, *beta, *d_o;
     const float *g;
-    const float *st, *vn, *dst, *dvn;  // per chunk: S, V_new, dS', dV_new (accumulator order)
+    const float *st, *vn, *dst, *dvn;  // per chunk: S, V_new, dS', dV_new (accumulator order; S and dS' as fp16)
+    const int *stf, *dstf;             // per chunk and 16-column tile: the exponents of S's and dS''s fp16 frames
     float *dq, *dk, *dv, *dg, *dbeta;
     int per, H;
     float scale;
@@ -238,7 +239,11 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
     if (c0 >= t1) return;
     const int L = static_cast<int>(t1 - c0 < C ? t1 - c0 : C);
     const int64_t sh = static_cast<int64_t>(slot) * H + h;
-    const float *St = A.st + sh * (DK * DV), *dSt = A.dst + sh * (DK * DV);
+    // S and dS' arrive as fp16 in power-of-two frames, one per 16-column tile (unit u = tid + kGT i: tile i)
+    const h4 *St = reinterpret_cast<const h4 *>(A.st + sh * (DK * DV)), *dSt = reinterpret_cast<const h4 *>(A.dst + sh * (DK * DV));
+    const int *Sf = A.stf + sh * 8, *dSf = A.dstf + sh * 8;
+    auto wide = [](h4 x, float s) { return f4{static_cast<float>(x[0]) * s, static_cast<float>(x[1]) * s,
+                                             static_cast<float>(x[2]) * s, static_cast<float>(x[3]) * s}; };
     const float *Vt = A.vn + sh * (C * DV), *dVt = A.dvn + sh * (C * DV);
     const int64_t rowb = c0 * H + h;  // token row c0 + r of head h is (rowb + r H) * 128
     auto trow = [&](int r) { return (rowb + static_cast<int64_t>(r) * H) * DK; };
@@ -271,7 +276,7 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int u = tid + kGT * i;
-        pS[i] = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(St + 4 * u));
+        pS[i] = wide(__builtin_nontemporal_load(St + u), pow2(Sf[i]));
         put_unit(sSh, sSl, u, 8, pS[i]);
     }
 #pragma unroll
@@ -291,7 +296,7 @@ chunk_grad_kernel(GradArgs A, SegmentView sv) {
     f4 pdS[8], pVn[4];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        pdS[i] = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(dSt + 4 * (tid + kGT * i)));
+        pdS[i] = wide(__builtin_nontemporal_load(dSt + tid + kGT * i), pow2(dSf[i]));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         pVn[i] = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(Vt + 4 * (tid + kGT * i)));
@@ -786,7 +791,7 @@ namespace {
 
 struct BwdChunkPlan {
     ChunkGradLayout fwd;
-    size_t off_rp, off_st, off_vn, off_dst, off_dvn, off_hb, off_dl, off_pt, off_pzh, bytes;
+    size_t off_rp, off_st, off_vn, off_dst, off_dvn, off_hb, off_dl, off_pt, off_pzh, off_stf, off_dstf, bytes;
 };
 
 BwdChunkPlan bwd_chunk_plan(int B, int T, int H, int N, bool varlen) {
@@ -805,6 +810,8 @@ BwdChunkPlan bwd_chunk_plan(int B, int T, int H, int N, bool varlen) {
     p.off_dl = o;  o = a256(o + seg_state);
     p.off_pt = o;  o = a256(o + seg_state);  // P^T planes: the same bytes as a fp32 state
     p.off_pzh = o; o = a256(o + static_cast<size_t>(p.fwd.max_segs) * H * 8);
+    p.off_stf = o; o = a256(o + sh * 8 * sizeof(int));
+    p.off_dstf = o; o = a256(o + sh * 8 * sizeof(int));
     p.bytes = o;
     return p;
 }
@@ -841,6 +848,7 @@ hipError_t launch_chunk_bwd(const BackwardLaunch &L) {
     ScanGrad gf{};
     gf.st = reinterpret_cast<float *>(ws + p.off_st);
     gf.vn = reinterpret_cast<float *>(ws + p.off_vn);
+    gf.stf = reinterpret_cast<int *>(ws + p.off_stf);
     gf.keep_last = true;
     gf.pt = ws + p.off_pt;
     gf.pzh = reinterpret_cast<uint8_t *>(ws + p.off_pzh);
@@ -855,6 +863,7 @@ hipError_t launch_chunk_bwd(const BackwardLaunch &L) {
     ScanGrad gr{};
     gr.vn = reinterpret_cast<float *>(ws + p.off_dvn);
     gr.dst = reinterpret_cast<float *>(ws + p.off_dst);
+    gr.dstf = reinterpret_cast<int *>(ws + p.off_dstf);
     gr.dleave = reinterpret_cast<const float *>(ws + p.off_dl);
     gr.dhT = L.dhT;
     gr.dh0 = L.dh0;
@@ -871,6 +880,7 @@ hipError_t launch_chunk_bwd(const BackwardLaunch &L) {
     A.v = static_cast<const uint16_t *>(L.v); A.beta = static_cast<const uint16_t *>(L.beta);
     A.d_o = static_cast<const uint16_t *>(L.d_o); A.g = L.g;
     A.st = gf.st; A.vn = gf.vn; A.dst = gr.dst; A.dvn = gr.vn;
+    A.stf = gf.stf; A.dstf = gr.dstf;
     A.dq = L.dq; A.dk = L.dk; A.dv = L.dv; A.dg = L.dg; A.dbeta = L.dbeta;
     A.per = per; A.H = L.H; A.scale = L.scale;
     hipLaunchKernelGGL(mc::chunk_grad_kernel, dim3(blocks), dim3(mc::kGT), 0, L.stream, A, sv);

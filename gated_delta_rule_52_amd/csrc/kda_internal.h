@@ -209,9 +209,11 @@ void launch_scan(const ChunkLaunch &L, const SegmentView &sv, int max_segs, int 
 // holds rows 16 t + 4 (l / 16) .. + 3 of column 16 w + l % 16, R = 8 row tiles for a state (dk x dv),
 // R = 4 for V_new (C x dv).
 struct ScanGrad {
-    float *st;            // kStates: the state entering each chunk
+    float *st;            // kStates: the state entering each chunk (fp16 in the walk's frame, accumulator order)
+    int *stf;             // kStates: that frame's exponent per chunk and 16-column tile ([chunk slot * H + h][8])
+    int *dstf;            // kRevOut: the same for dst
     float *vn;            // kStates: V_new of each chunk; kRevOut: dV_new of each chunk
-    float *dst;           // kRevOut: the gradient of the state each chunk leaves
+    float *dst;           // kRevOut: the gradient of the state each chunk leaves (stored as st)
     const float *dleave;  // kRevOut: [segment * H + h] gradient of the state each segment leaves (row-major)
     const float *dhT;     // kRevOut: [sequence * H + h] final-state gradient (null: zero)
     float *dh0;           // kRevOut: [sequence * H + h] initial-state gradient (null: not written)

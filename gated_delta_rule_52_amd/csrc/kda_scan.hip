@@ -253,16 +253,17 @@ chunk_scan_kernel(const char *__restrict__ packs, int per, float *hT, void *__re
         const int ew = hdr[kHdrW], ek = hdr[kHdrK];
         const float *gam = reinterpret_cast<const float *>(L + kPkGamma);
         const int64_t slot = (static_cast<int64_t>(seg) * per + j) * H + h;
-        if constexpr (kKeep) {  // the state entering chunk j (forward) or the gradient of the one leaving it
-            float *sd_ = (MODE == kStates ? gr.st : gr.dst) + slot * (DK * DV);
+        if constexpr (kKeep) {
+            // the state entering chunk j (forward) or the gradient of the one leaving it, as the fp16 operand the
+            // walk itself multiplies with (|acc| < 96 in the wave's frame) and the frame's exponent per tile
+            h4 *sd_ = reinterpret_cast<h4 *>((MODE == kStates ? gr.st : gr.dst) + slot * (DK * DV));
+            int *sf = (MODE == kStates ? gr.stf : gr.dstf) + slot * 8;
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const float sc = pow2(fr[ct]);
+                if (lane == 0) sf[ctile0 + ct] = fr[ct];
 #pragma unroll
-                for (int rt = 0; rt < 8; ++rt) {  // whole 1 KiB units, read once much later: non-temporal
-                    f4 *dst4 = reinterpret_cast<f4 *>(sd_ + 4 * (((ctile0 + ct) * 8 + rt) * 64 + lane));
-                    __builtin_nontemporal_store(acc[rt][ct] * sc, dst4);
-                }
+                for (int rt = 0; rt < 8; ++rt)  // whole 512-byte pieces, read once much later: non-temporal
+                    __builtin_nontemporal_store(to_h4(acc[rt][ct], 1.f), sd_ + ((ctile0 + ct) * 8 + rt) * 64 + lane);
             }
         }
         // The accumulator layout of two 16-row state tiles is the B operand
